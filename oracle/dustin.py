@@ -1,0 +1,329 @@
+"""Plain CPU oracle for the Dustin sparse-verification step (fp64 NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library and imports nothing from it.
+
+Sources (the three web pages about "Dustin: Draft-Augmented Sparse
+Verification for Efficient Long-Context Generation with Speculative
+Decoding", arXiv 2606.24957):
+
+* the Chinese translation of the arXiv HTML (bittide.aicompass.dev),
+  section 3.1, equations (1)-(4): ARR, windowed ARR and the SD oracle;
+  section 3.2: history attention A_{i-delta,.} with delta = 1;
+* the blog summary (liuzhao09.github.io), section 2.2 (hybrid aggregation:
+  S_Draft over H_d, L_d, Gamma; S_Target over H_t, L_t; one global index
+  set), section 2.3 (verification set: protected sink + recent window, draft
+  top-m, target fill), section 2.4 (scoring restricted to a few semantic
+  retrieval heads), Fig. 5 (Stage 2: attention over the compressed KV only).
+
+The pages print the S_Draft / S_Target and verification-set formulas only as
+prose (the formula slots of the blog are empty).  The readings taken here are
+the plainest ones the prose supports; each function states its reading.
+
+Everything is computed per sequence in float64 with no blocking, fusion or
+reordering beyond the definitions.  Inputs may be float32/bfloat16-rounded
+values; they are upcast to float64 first.
+
+Layouts (per sequence):
+  q        [w][Hq][d]            window queries q_{i+s}, s = 0..w-1
+  K, V     [n][Hkv][d]           history keys/values of one target layer
+  q_hist   [S][d]                most recent target query, one row per
+                                 scored (layer, head) pair
+  q_draft  [L_d][Gamma][H_d][d_d]
+  K_draft  [L_d][n][Hkv_d][d_d]
+Query head h reads KV head floor(h / G) with G = Hq / Hkv.
+
+Parity pins for every function live in tests/test_oracle_pins.py; no
+function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "softmax",
+    "head_probs",
+    "window_attention",
+    "dense_attention",
+    "sparse_attention",
+    "arr_step",
+    "arr_window",
+    "sd_oracle",
+    "score_target",
+    "score_draft",
+    "select_verify_set",
+    "topk_desc",
+    "protected_positions",
+    "pages_to_contiguous",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def softmax(x, axis=-1):
+    """Numerically plain softmax along ``axis`` (max-subtracted exp / sum)."""
+    x = _f64(x)
+    m = np.max(x, axis=axis, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def _kv_head_of(h, Hq, Hkv):
+    """Grouped-query mapping: query head h reads KV head floor(h / G)."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def head_probs(q, K, scale=None):
+    """Per-head attention probabilities of the window queries over history.
+
+    P[h][s][j] = softmax_j(scale * q[s][h] . K[j][g(h)]), j in [0, n).
+
+    Reading (translation section 3.1, definition of A_{i,j}): A is normalised
+    over the valid history V_i only, so the w window tokens are not part of
+    the denominator and sum_j A_{i,j} = 1 holds at every window step.
+    """
+    q = _f64(q)
+    K = _f64(K)
+    w, Hq, d = q.shape
+    n, Hkv, dk = K.shape
+    assert dk == d
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    P = np.empty((Hq, w, n))
+    for h in range(Hq):
+        g = _kv_head_of(h, Hq, Hkv)
+        logits = scale * (q[:, h, :] @ K[:, g, :].T)  # [w][n]
+        P[h] = softmax(logits, axis=-1)
+    return P
+
+
+def window_attention(q, K, scale=None):
+    """A[s][j]: full-cache attention weight of window step s on position j.
+
+    Translation section 3.1 defines a single normalised weight A_{i,j} per
+    step without saying how heads are combined; reading taken: the mean over
+    the query heads of one layer.  ARR is linear in A, so this equals the
+    mean of the per-head ARRs, and one global set serves all heads (blog
+    section 2.2).
+    """
+    return head_probs(q, K, scale).mean(axis=0)
+
+
+def dense_attention(q, K, V, scale=None):
+    """Full-cache verification attention (blog Fig. 7 "Full Cache" baseline).
+
+    O[s][h] = sum_j P[h][s][j] * V[j][g(h)].
+    """
+    P = head_probs(q, K, scale)
+    V = _f64(V)
+    w, Hq, d = np.asarray(q).shape
+    Hkv = V.shape[1]
+    O = np.empty((w, Hq, V.shape[2]))
+    for h in range(Hq):
+        O[:, h, :] = P[h] @ V[:, _kv_head_of(h, Hq, Hkv), :]
+    return O
+
+
+def sparse_attention(q, K, V, I, scale=None):
+    """Sparse verification attention over the compressed KV (blog Fig. 5,
+    Stage 2): the target attends only to the rows in the index set I.
+
+    O[s][h] = sum_{j in I} softmax_{j in I}(scale * q[s][h] . K[j][g(h)]) V[j][g(h)].
+    Also returns lse[s][h] = log sum_{j in I} exp(scale * q . k_j) (natural log).
+    Entries of I that are negative (padding) are ignored.
+    """
+    I = np.asarray(I, dtype=np.int64)
+    I = I[I >= 0]
+    q = _f64(q)
+    w, Hq, d = q.shape
+    Ks = _f64(K)[I]
+    Vs = _f64(V)[I]
+    Hkv = np.asarray(K).shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    O = np.zeros((w, Hq, np.asarray(V).shape[2]))
+    lse = np.full((w, Hq), -np.inf)
+    if I.size == 0:
+        return O, lse
+    for h in range(Hq):
+        g = _kv_head_of(h, Hq, Hkv)
+        logits = scale * (q[:, h, :] @ Ks[:, g, :].T)  # [w][|I|]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        z = e.sum(axis=1, keepdims=True)
+        O[:, h, :] = (e / z) @ Vs[:, g, :]
+        lse[:, h] = (m + np.log(z))[:, 0]
+    return O, lse
+
+
+def arr_step(A, I):
+    """Eq. (1) of translation section 3.1, one value per window step:
+    ARR_{i+s} = sum_{j in K} A_{i+s, j}.  Negative entries of I are padding."""
+    A = _f64(A)
+    I = np.asarray(I, dtype=np.int64)
+    I = I[I >= 0]
+    return A[:, I].sum(axis=1)
+
+
+def arr_window(A, I):
+    """Eq. (2): windowed ARR = (1/w) * sum_{s=0}^{w-1} ARR_{i+s}."""
+    return float(np.mean(arr_step(A, I)))
+
+
+def topk_desc(scores, k, candidates=None):
+    """TopK_k by (score descending, position ascending).
+
+    The pages do not state a tie rule; reading taken: lower position first.
+    Returns the chosen positions in selection order.
+    """
+    scores = _f64(scores)
+    if candidates is None:
+        candidates = np.arange(scores.shape[0])
+    candidates = np.asarray(candidates, dtype=np.int64)
+    if k <= 0 or candidates.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    # np.lexsort sorts by the last key first: primary -score, secondary index.
+    order = np.lexsort((candidates, -scores[candidates]))
+    return candidates[order[: min(k, candidates.size)]]
+
+
+def sd_oracle(A, k):
+    """Eq. (3)-(4): SD oracle.
+
+    Abar_j = (1/w) sum_s A_{i+s, j};  K_orc = TopK_k(Abar);
+    ARR^(w)(orc) = sum_{j in K_orc} Abar_j.
+    Returns (sorted K_orc, ARR^(w)(orc), Abar).
+    """
+    Abar = _f64(A).mean(axis=0)
+    sel = np.sort(topk_desc(Abar, k))
+    return sel, float(Abar[sel].sum()), Abar
+
+
+def score_target(q_hist, K_layers, sub_heads, Hq, scale=None):
+    """S_Target (blog section 2.2 and section 2.4).
+
+    The target's most recent attention (translation section 3.2: history
+    distance delta = 1) recomputed by QK^T on the searched subset of
+    (layer, head) pairs only.  The blog gives the aggregation only in words
+    ("aggregate into a global token-importance vector"); reading taken: the
+    plain sum of the per-head softmax probabilities,
+        S_T[j] = sum_{(l,h) in subset} softmax_j(scale * q_hist[l,h] . K_l[j][g(h)]).
+    A mean would differ by a constant factor and rank identically.
+
+    q_hist: [S][d]; K_layers: dict or list indexed by layer -> [n][Hkv][d];
+    sub_heads: S pairs (layer, head).
+    """
+    q_hist = _f64(q_hist)
+    S, d = q_hist.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    n = np.asarray(K_layers[sub_heads[0][0]]).shape[0]
+    out = np.zeros(n)
+    for r, (layer, h) in enumerate(sub_heads):
+        K = _f64(K_layers[layer])
+        g = _kv_head_of(h, Hq, K.shape[1])
+        out += softmax(scale * (K[:, g, :] @ q_hist[r]))
+    return out
+
+
+def score_draft(q_draft, K_draft, scale=None):
+    """S_Draft (blog section 2.2 and Fig. 5: the draft's attention heat maps
+    are summed along the draft steps).
+
+    Reading taken: plain sum over draft layers l, draft query heads h and
+    draft steps g of the draft's attention over the history positions,
+        S_D[j] = sum_{l,h,g} softmax_j(scale_d * q_draft[l,g,h] . K_draft[l][j][c(h)]),
+    with c(h) = floor(h / G_d) and the softmax taken over history positions
+    only (the draft's own new tokens are not history).
+
+    q_draft: [L_d][Gamma][H_d][d_d]; K_draft: [L_d][n][Hkv_d][d_d].
+    """
+    q_draft = _f64(q_draft)
+    L_d, Gamma, H_d, d_d = q_draft.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_d)
+    n = np.asarray(K_draft[0]).shape[0]
+    out = np.zeros(n)
+    for l in range(L_d):
+        K = _f64(K_draft[l])
+        Hkv_d = K.shape[1]
+        for h in range(H_d):
+            c = _kv_head_of(h, H_d, Hkv_d)
+            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)  # [Gamma][n]
+            out += softmax(logits, axis=-1).sum(axis=0)
+    return out
+
+
+def protected_positions(n, n_sink, n_window):
+    """Protected tier of the verification set (blog section 2.3): the first
+    n_sink positions (attention sinks) and the last n_window positions
+    (recent window), clipped to [0, n)."""
+    sink = np.arange(0, min(n_sink, n))
+    recent = np.arange(max(0, n - n_window), n)
+    return np.union1d(sink, recent).astype(np.int64)
+
+
+def select_verify_set(s_draft, s_target, n, k, m, n_sink, n_window):
+    """Verification set I_verify (blog section 2.3), one per sequence, shared
+    by every layer and head (blog section 2.2).
+
+    Tiers, in the order the blog gives them:
+      1. P = attention sinks [0, n_sink) and recent window [n - n_window, n);
+      2. D = the m' highest-S_Draft positions outside P;
+      3. T = the highest-S_Target positions outside P and D, filling the
+         budget k.
+    Reading of the budget: k counts the protected tokens; m' =
+    min(m, k - |P|, |V \\ P|); |I| = min(k, n).  A missing S_Draft means
+    m' = 0 (target only); a missing S_Target means the draft tier fills the
+    budget (m' = k - |P|).  Ties: higher score first, then lower position.
+
+    Returns (idx ascending int64 array, tier array aligned with idx:
+    0 protected, 1 draft, 2 target).
+    """
+    if s_draft is None and s_target is None:
+        raise ValueError("at least one score vector is required")
+    if n_sink + n_window > k:
+        raise ValueError("protected tokens exceed the budget")
+    P = protected_positions(n, n_sink, n_window)
+    rest = np.setdiff1d(np.arange(n), P)
+    budget = k - P.size
+    if s_draft is None:
+        m_eff = 0
+    elif s_target is None:
+        m_eff = budget
+    else:
+        m_eff = m
+    m_eff = max(0, min(m_eff, budget, rest.size))
+    D = topk_desc(s_draft, m_eff, rest) if m_eff > 0 else np.zeros(0, np.int64)
+    rest2 = np.setdiff1d(rest, D)
+    t_cnt = max(0, min(budget - D.size, rest2.size))
+    T = topk_desc(s_target, t_cnt, rest2) if t_cnt > 0 else np.zeros(0, np.int64)
+    idx = np.concatenate([P, D, T]).astype(np.int64)
+    tier = np.concatenate([
+        np.zeros(P.size, np.int8),
+        np.ones(D.size, np.int8),
+        np.full(T.size, 2, np.int8),
+    ])
+    order = np.argsort(idx, kind="stable")
+    return idx[order], tier[order]
+
+
+def pages_to_contiguous(pool, page_row, n, page_size):
+    """Logical history rows [0, n) of a paged cache.
+
+    pool: [num_pages][page_size][...]; page_row: physical page id of each
+    logical page of this sequence.  Logical position j lives in physical page
+    page_row[j // page_size], slot j % page_size.
+    """
+    pool = np.asarray(pool)
+    n_pages = (n + page_size - 1) // page_size
+    rows = [pool[int(page_row[p])] for p in range(n_pages)]
+    flat = np.concatenate(rows, axis=0) if rows else pool[:0].reshape((0,) + pool.shape[2:])
+    return flat[:n]

@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties an oracle function to a closed form, an invariant the pages
+state, a library routine for a special case, or brute force on tiny inputs,
+chosen so that a dropped term, a wrong sign or index, a transposed operand or
+a wrong head mapping fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _frac(s):
+    return float(Fraction(s))
+
+
+def _lnfrac(s):
+    return math.log(float(Fraction(s.split("ln", 1)[1].strip().replace(" ", ""))))
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Hand-derived worked examples (translation section 3.1, Eq. 1-4)
+# --------------------------------------------------------------------------
+
+def _worked_inputs():
+    g = _load("worked_example_arr.json")
+    K = np.array([[[math.log(j + 1), 0.0]] for j in range(4)])  # [4][1][2]
+    q = np.array(g["inputs"]["q"], dtype=np.float64)            # [w=2][Hq=2][2]
+    V = np.array(g["inputs"]["V"], dtype=np.float64)            # [4][1][2]
+    return g, q, K, V
+
+
+def test_worked_example_window_attention():
+    g, q, K, V = _worked_inputs()
+    A = oracle.window_attention(q, K, scale=1.0)
+    exp = np.array([[_frac(x) for x in row] for row in g["expected"]["A"]])
+    np.testing.assert_allclose(A, exp, rtol=0, atol=1e-14)
+
+
+def test_worked_example_arr_and_sd_oracle():
+    g, q, K, V = _worked_inputs()
+    A = oracle.window_attention(q, K, scale=1.0)
+    ex = g["expected"]
+    set_a = g["inputs"]["set_a"]
+    np.testing.assert_allclose(oracle.arr_step(A, set_a), [_frac(x) for x in ex["arr_step_set_a"]], atol=1e-14)
+    assert abs(oracle.arr_window(A, set_a) - _frac(ex["arr_window_set_a"])) < 1e-14
+    sel, arr, Abar = oracle.sd_oracle(A, g["inputs"]["k"])
+    np.testing.assert_allclose(Abar, [_frac(x) for x in ex["Abar"]], atol=1e-14)
+    assert sel.tolist() == ex["orc_set"]
+    assert abs(arr - _frac(ex["orc_arr"])) < 1e-14
+
+
+def test_worked_example_dense_and_sparse_outputs():
+    g, q, K, V = _worked_inputs()
+    ex = g["expected"]
+    O = oracle.dense_attention(q, K, V, scale=1.0)
+    exp = np.array([[[_frac(x) for x in h] for h in s] for s in ex["dense_out"]])
+    np.testing.assert_allclose(O, exp, atol=1e-14)
+    Os, lse = oracle.sparse_attention(q, K, V, g["inputs"]["set_sparse"], scale=1.0)
+    exp = np.array([[[_frac(x) for x in h] for h in s] for s in ex["sparse_out"]])
+    np.testing.assert_allclose(Os, exp, atol=1e-14)
+    exp_lse = np.array([[_lnfrac(x) for x in s] for s in ex["sparse_lse"]])
+    np.testing.assert_allclose(lse, exp_lse, atol=1e-14)
+
+
+def test_worked_example_tiers():
+    g = _load("worked_example_tiers.json")
+    for c in g["cases"]:
+        idx, tier = oracle.select_verify_set(np.array(g["s_draft"], float), np.array(g["s_target"], float),
+                                             g["n"], c["k"], c["m"], g["n_sink"], g["n_window"])
+        assert idx.tolist() == c["idx"], c["why"]
+        assert tier.tolist() == c["tier"], c["why"]
+
+
+# --------------------------------------------------------------------------
+# Library routines for special cases
+# --------------------------------------------------------------------------
+
+def test_softmax_matches_scipy():
+    rng = np.random.default_rng(0)
+    x = rng.normal(size=(3, 17)) * 5
+    np.testing.assert_allclose(oracle.softmax(x), scipy.special.softmax(x, axis=-1), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("w,Hq,Hkv,d,n", [(4, 8, 2, 16, 37), (1, 1, 1, 8, 5), (3, 6, 3, 32, 64)])
+def test_dense_attention_matches_torch_sdpa(w, Hq, Hkv, d, n):
+    rng = np.random.default_rng(w * 100 + n)
+    q = rng.normal(size=(w, Hq, d))
+    K = rng.normal(size=(n, Hkv, d)) * 2
+    V = rng.normal(size=(n, Hkv, d))
+    O = oracle.dense_attention(q, K, V)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]          # [1][Hq][w][d]
+    kt = torch.from_numpy(K).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(V).permute(1, 0, 2)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True)
+    np.testing.assert_allclose(O, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_attention_matches_masked_sdpa_and_logsumexp():
+    rng = np.random.default_rng(7)
+    w, Hq, Hkv, d, n = 4, 8, 2, 16, 50
+    q = rng.normal(size=(w, Hq, d))
+    K = rng.normal(size=(n, Hkv, d)) * 2
+    V = rng.normal(size=(n, Hkv, d))
+    I = np.sort(rng.choice(n, 13, replace=False))
+    O, lse = oracle.sparse_attention(q, K, V, np.concatenate([I, [-1, -1]]))
+    mask = torch.zeros(n, dtype=torch.bool)
+    mask[torch.from_numpy(I)] = True
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(K).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(V).permute(1, 0, 2)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None, None, :], enable_gqa=True)
+    np.testing.assert_allclose(O, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        logits = q[:, h, :] @ K[I, g, :].T / math.sqrt(d)
+        np.testing.assert_allclose(lse[:, h], scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
+
+
+def test_sparse_equals_dense_when_set_is_everything():
+    # k >= |V_i|: sparse attention over all rows equals full attention.
+    rng = np.random.default_rng(3)
+    q = rng.normal(size=(4, 8, 16))
+    K = rng.normal(size=(40, 2, 16))
+    V = rng.normal(size=(40, 2, 16))
+    O, _ = oracle.sparse_attention(q, K, V, np.arange(40))
+    np.testing.assert_allclose(O, oracle.dense_attention(q, K, V), rtol=1e-13, atol=1e-13)
+
+
+def test_single_query_two_token_closed_form():
+    # G = 1, w = 1: o = (e^a v0 + e^b v1) / (e^a + e^b) with a, b the scaled logits.
+    q = np.array([[[1.0, 2.0, 0.0, 0.0]]])
+    K = np.array([[[1.0, 0.0, 0.0, 0.0]], [[0.0, 1.0, 0.0, 0.0]]])
+    V = np.array([[[1.0, 0.0, 3.0, 0.0]], [[0.0, 1.0, 0.0, -2.0]]])
+    a, b = 1.0 / 2.0, 2.0 / 2.0       # scale 1/sqrt(4)
+    pa = math.exp(a) / (math.exp(a) + math.exp(b))
+    expect = pa * V[0, 0] + (1 - pa) * V[1, 0]
+    np.testing.assert_allclose(oracle.dense_attention(q, K, V)[0, 0], expect, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# ARR invariants the pages state
+# --------------------------------------------------------------------------
+
+def _rand_A(rng, w=4, n=30, Hq=4, Hkv=2, d=8):
+    q = rng.normal(size=(w, Hq, d)) * 1.5
+    K = rng.normal(size=(n, Hkv, d)) * 1.5
+    return oracle.window_attention(q, K)
+
+
+def test_arr_of_full_history_is_one():
+    # Translation section 3.1: sum_j A_{i,j} = 1 over V_i, so ARR(V_i) = 1.
+    A = _rand_A(np.random.default_rng(1))
+    np.testing.assert_allclose(A.sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.arr_step(A, np.arange(A.shape[1])), 1.0, rtol=1e-14)
+    assert abs(oracle.arr_window(A, np.arange(A.shape[1])) - 1.0) < 1e-14
+
+
+def test_orc_arr_is_sum_of_topk_via_partition():
+    # Eq. (4) = Eq. (2) evaluated on Eq. (3)'s set; by linearity it is the sum
+    # of the k largest entries of Abar.  np.partition is an independent route.
+    rng = np.random.default_rng(2)
+    A = _rand_A(rng, n=200)
+    Abar = A.mean(axis=0)
+    for k in (1, 5, 17, 100, 200):
+        _, arr, _ = oracle.sd_oracle(A, k)
+        top = np.partition(Abar, Abar.size - k)[Abar.size - k:]
+        assert abs(arr - top.sum()) < 1e-13
+        sel, _, _ = oracle.sd_oracle(A, k)
+        assert abs(oracle.arr_window(A, sel) - arr) < 1e-13
+
+
+def test_orc_is_upper_bound_brute_force():
+    # Translation section 3.1: the SD oracle is an upper bound of windowed ARR
+    # over every policy with budget k.  Brute force over all subsets, n = 12.
+    rng = np.random.default_rng(4)
+    A = _rand_A(rng, n=12)
+    for k in (1, 3, 6):
+        sel, arr, _ = oracle.sd_oracle(A, k)
+        best = max(oracle.arr_window(A, list(c)) for c in itertools.combinations(range(12), k))
+        assert abs(best - arr) < 1e-13
+        for _ in range(50):
+            other = rng.choice(12, k, replace=False)
+            assert oracle.arr_window(A, other) <= arr + 1e-15
+
+
+def test_arr_monotone_in_k():
+    rng = np.random.default_rng(5)
+    A = _rand_A(rng, n=300)
+    prev = -1.0
+    for k in range(1, 301, 7):
+        _, arr, _ = oracle.sd_oracle(A, k)
+        assert arr >= prev - 1e-15
+        prev = arr
+
+
+# --------------------------------------------------------------------------
+# TopK and the tier rule
+# --------------------------------------------------------------------------
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        n = int(rng.integers(1, 14))
+        s = rng.integers(0, 4, size=n).astype(float)      # many ties
+        k = int(rng.integers(0, n + 2))
+        got = oracle.topk_desc(s, k).tolist()
+        # pure-Python reference: sort positions by (-score, position)
+        ref = sorted(range(n), key=lambda j: (-s[j], j))[:k]
+        assert got == ref
+
+
+def _best_subset(scores, cands, r):
+    """Brute force: max-sum r-subset of cands, lowest positions among ties."""
+    best, best_key = None, None
+    for c in itertools.combinations(sorted(cands), r):
+        key = (-sum(scores[j] for j in c), c)
+        if best_key is None or key < best_key:
+            best, best_key = set(c), key
+    return best if best is not None else set()
+
+
+def test_tiers_brute_force():
+    rng = np.random.default_rng(8)
+    for trial in range(300):
+        n = int(rng.integers(1, 11))
+        sd = rng.integers(0, 5, size=n).astype(float)
+        st = rng.integers(0, 5, size=n).astype(float)
+        n_sink = int(rng.integers(0, 3))
+        n_window = int(rng.integers(0, 3))
+        k = int(rng.integers(n_sink + n_window, n_sink + n_window + 8))
+        if k == 0:
+            continue
+        m = int(rng.integers(0, k + 2))
+        idx, tier = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
+        P = set(range(min(n_sink, n))) | set(range(max(0, n - n_window), n))
+        rest = set(range(n)) - P
+        m_eff = max(0, min(m, k - len(P), len(rest)))
+        D = _best_subset(sd, rest, m_eff)
+        T = _best_subset(st, rest - D, max(0, min(k - len(P) - m_eff, len(rest - D))))
+        assert set(idx.tolist()) == P | D | T
+        assert idx.tolist() == sorted(idx.tolist())
+        assert len(idx) == min(k, n) == len(set(idx.tolist()))
+        lab = dict(zip(idx.tolist(), tier.tolist()))
+        assert all(lab[j] == 0 for j in P)
+        assert all(lab[j] == 1 for j in D)
+        assert all(lab[j] == 2 for j in T)
+
+
+def test_tier_special_cases():
+    rng = np.random.default_rng(9)
+    n = 64
+    sd = rng.random(n)
+    st = rng.random(n)
+    # m = 0, no protection: TopK_k of S_Target (Dustin-T in the blog's ablation)
+    idx, _ = oracle.select_verify_set(sd, st, n, 10, 0, 0, 0)
+    assert idx.tolist() == sorted(np.argsort(-st)[:10].tolist())
+    # m = k, no protection: TopK_k of S_Draft (Dustin-D)
+    idx, _ = oracle.select_verify_set(sd, st, n, 10, 10, 0, 0)
+    assert idx.tolist() == sorted(np.argsort(-sd)[:10].tolist())
+    # missing draft scores behave like m = 0; missing target scores like m = k
+    assert oracle.select_verify_set(None, st, n, 10, 5, 0, 0)[0].tolist() == sorted(np.argsort(-st)[:10].tolist())
+    assert oracle.select_verify_set(sd, None, n, 10, 5, 0, 0)[0].tolist() == sorted(np.argsort(-sd)[:10].tolist())
+    # k >= n returns all positions; protected tokens always included
+    assert oracle.select_verify_set(sd, st, n, 100, 7, 4, 8)[0].tolist() == list(range(n))
+    idx, _ = oracle.select_verify_set(sd, st, n, 20, 7, 4, 8)
+    assert set(range(4)) | set(range(56, 64)) <= set(idx.tolist())
+    # protected window larger than the sequence
+    assert oracle.protected_positions(5, 4, 8).tolist() == [0, 1, 2, 3, 4]
+    with pytest.raises(ValueError):
+        oracle.select_verify_set(sd, st, n, 5, 0, 4, 8)
+
+
+# --------------------------------------------------------------------------
+# Scoring: S_Target and S_Draft
+# --------------------------------------------------------------------------
+
+def test_scores_uniform_when_keys_identical():
+    # Identical keys give a uniform softmax: S_T = S / n, S_D = L_d H_d Gamma / n.
+    rng = np.random.default_rng(10)
+    n, Hq, Hkv, d = 33, 8, 2, 16
+    K = np.broadcast_to(rng.normal(size=(1, Hkv, d)), (n, Hkv, d))
+    sub = [(0, 0), (0, 3), (0, 5)]
+    qh = rng.normal(size=(3, d))
+    np.testing.assert_allclose(oracle.score_target(qh, {0: K}, sub, Hq), 3.0 / n, rtol=1e-13)
+    L_d, G_, H_d, Hkv_d, d_d = 2, 3, 4, 2, 8
+    Kd = np.broadcast_to(rng.normal(size=(L_d, 1, Hkv_d, d_d)), (L_d, n, Hkv_d, d_d))
+    qd = rng.normal(size=(L_d, G_, H_d, d_d))
+    np.testing.assert_allclose(oracle.score_draft(qd, Kd), L_d * H_d * G_ / n, rtol=1e-13)
+
+
+def test_score_sums_count_every_term():
+    rng = np.random.default_rng(11)
+    n, Hq, Hkv, d = 70, 8, 4, 16
+    Ks = {0: rng.normal(size=(n, Hkv, d)), 2: rng.normal(size=(n, Hkv, d))}
+    sub = [(0, 1), (2, 6), (2, 7), (0, 0)]
+    st = oracle.score_target(rng.normal(size=(4, d)) * 3, Ks, sub, Hq)
+    assert abs(st.sum() - 4.0) < 1e-12 and (st > 0).all()
+    L_d, G_, H_d, Hkv_d, d_d = 3, 4, 6, 2, 8
+    sd = oracle.score_draft(rng.normal(size=(L_d, G_, H_d, d_d)) * 3, rng.normal(size=(L_d, n, Hkv_d, d_d)))
+    assert abs(sd.sum() - L_d * H_d * G_) < 1e-11 and (sd > 0).all()
+
+
+def test_score_head_to_kv_mapping_and_scale():
+    # KV head 0 holds identical keys (uniform softmax); KV head 1 holds one key
+    # aligned with the query strongly enough that its softmax is one-hot at p.
+    n, Hq, Hkv, d, p = 16, 8, 2, 4, 11
+    K = np.zeros((n, Hkv, d))
+    K[:, 0, :] = 0.5
+    K[p, 1, 0] = 200.0
+    qh = np.array([[1.0, 0, 0, 0], [1.0, 0, 0, 0]])
+    # head 4 -> kv 1 (4 // 4); head 1 -> kv 0.  A modulo mapping would swap them.
+    st = oracle.score_target(qh, {0: K}, [(0, 4), (0, 1)], Hq)
+    expect = np.full(n, 1.0 / n)
+    expect[p] += 1.0
+    np.testing.assert_allclose(st, expect, rtol=0, atol=1e-14)
+    # scale 1/sqrt(d_d): two keys with raw logits 2 and 0 -> p0 = sigmoid(2/2)
+    qd = np.zeros((1, 1, 4, 4))
+    qd[0, 0, :, 0] = 2.0
+    Kd = np.zeros((1, 2, 2, 4))
+    Kd[0, 0, :, 0] = 1.0
+    sd = oracle.score_draft(qd, Kd)
+    p0 = 1.0 / (1.0 + math.exp(-1.0))
+    np.testing.assert_allclose(sd, [4 * p0, 4 * (1 - p0)], rtol=1e-14)
+    # draft head 1 -> draft kv 0 with G_d = 2 (a modulo mapping gives kv 1)
+    qd = np.zeros((1, 1, 4, 4))
+    qd[0, 0, 1, 0] = 1.0
+    Kd = np.zeros((1, 3, 2, 4))
+    Kd[0, 2, 0, 0] = 400.0         # kv 0: one-hot at position 2 for head 1
+    sd = oracle.score_draft(qd, Kd)
+    # heads 0, 2, 3 have zero queries -> uniform 1/3 each; head 1 -> one-hot
+    np.testing.assert_allclose(sd, np.array([1, 1, 1]) + np.array([0, 0, 1.0]), atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Paged layout
+# --------------------------------------------------------------------------
+
+def test_pages_identity_and_permuted():
+    rng = np.random.default_rng(12)
+    n, ps = 45, 16
+    logical = rng.normal(size=(48, 3, 4))
+    pool = logical.reshape(3, ps, 3, 4)
+    np.testing.assert_array_equal(oracle.pages_to_contiguous(pool, [0, 1, 2], n, ps), logical[:n])
+    perm = np.array([2, 0, 1])
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    np.testing.assert_array_equal(oracle.pages_to_contiguous(pool2, perm, n, ps), logical[:n])
