@@ -1,0 +1,238 @@
+/*
+ * dustin.h -- C ABI of the MI355X (gfx950) sparse-verification step.
+ *
+ * The step is the target-side verification of long-context, multi-batch
+ * speculative decoding described for "Dustin: Draft-Augmented Sparse
+ * Verification for Efficient Long-Context Generation with Speculative
+ * Decoding" (arXiv 2606.24957):
+ *   1. hybrid token-importance scoring   -> dustin_score
+ *   2. one global TopK index set per sequence, shared by every layer and
+ *      head (protected sink/window tokens, draft top-m, target fill)
+ *                                        -> dustin_topk
+ *   3. grouped-query attention of the w window tokens over the selected
+ *      K/V rows only                     -> dustin_sparse_verify_attn
+ *   plus the evaluator of the translation's section 3.1 (attention recovery
+ *   rate):                               -> dustin_window_attn, dustin_arr
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers unless marked "host"; all tensors are
+ *   dense row-major with the shapes given.  The caller owns every buffer,
+ *   including the workspace; the library never allocates or frees memory.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *   default stream).  Nothing synchronises; device-side faults surface at
+ *   the caller's next synchronisation.
+ * - All argument checks run on the host before any HIP call, so every
+ *   DUSTIN_ERR_INVALID_ARG / DUSTIN_ERR_UNSUPPORTED path works without a GPU.
+ *   Values that live in device memory (sequence lengths, page tables, index
+ *   lists) cannot be checked on the host; kernels clamp them: lengths to
+ *   [0, N_max], index entries outside [0, n_b) and page ids outside
+ *   [0, num_pages) are treated as absent (never dereferenced).
+ * - Workspace: pass at least the byte count the matching *_workspace_bytes()
+ *   function returns for the same shape.  dustin_sparse_verify_attn and
+ *   dustin_window_attn keep arrival counters at the start of their workspace:
+ *   it must be zero-filled before its first use, every call leaves it zero
+ *   again, and it must not be handed to another entry point in between.
+ *   The other entry points make no assumption about workspace contents.
+ *   Calls that may overlap in time must not share a workspace.
+ * - Outputs are bitwise deterministic for fixed inputs and shapes.
+ * - Functions are stateless and reentrant; dustin_last_error() is
+ *   thread-local.
+ */
+#ifndef DUSTIN_H
+#define DUSTIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUSTIN_ABI_VERSION 1
+
+typedef enum dustin_status {
+    DUSTIN_OK = 0,
+    DUSTIN_ERR_INVALID_ARG = 1, /* bad shape, null required pointer, small workspace */
+    DUSTIN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    DUSTIN_ERR_HIP = 3          /* a HIP runtime call failed; see dustin_last_error() */
+} dustin_status;
+
+typedef enum dustin_dtype {
+    DUSTIN_F32 = 0,  /* float32 storage, float32 arithmetic */
+    DUSTIN_BF16 = 1  /* bfloat16 storage, float32 accumulation */
+} dustin_dtype;
+
+/* hipStream_t without pulling in the HIP headers. */
+typedef struct ihipStream_t *dustin_stream_t;
+
+/*
+ * One layer's KV cache (the blog's Fig. 5: the full target or draft cache
+ * stays resident; a verification step only reads part of it).
+ *
+ *  page_size == 0 (contiguous):  k, v are [B][N_max][H_kv][head_dim]
+ *  page_size == 16 (paged):      k, v are [num_pages][16][H_kv][head_dim];
+ *      logical position j of sequence b lives in physical page
+ *      page_table[b * max_pages + j / 16], slot j % 16.
+ *  seq_lens [B] (device, int32): n_b = |V_i|, the valid history length of
+ *      sequence b; rows at positions >= n_b are never read.
+ *  v may be NULL where only keys are needed (scoring, dustin_window_attn).
+ *  head_dim must be 32, 64 or 128.
+ */
+typedef struct dustin_kv {
+    const void *k;
+    const void *v;
+    int32_t dtype;              /* dustin_dtype */
+    int32_t B;
+    int32_t H_kv;
+    int32_t head_dim;
+    int32_t N_max;
+    const int32_t *seq_lens;    /* device [B] */
+    int32_t page_size;          /* 0 or 16 */
+    const int32_t *page_table;  /* device [B][max_pages]; NULL when contiguous */
+    int32_t max_pages;
+    int32_t num_pages;          /* pages in the pool (bounds page ids) */
+} dustin_kv;
+
+/*
+ * dustin_score -- hybrid token-importance vectors (blog section 2.2; the
+ * scored target heads are the searched subset of section 2.4).
+ *
+ *   S_Draft[b][j]  = sum over draft layers l < L_d, draft heads h < H_d and
+ *                    draft steps g < gamma of
+ *                    softmax_{j < n_b}(scale_draft * q_draft[b][l][g][h] . Kd_l[b][j][h / G_d])
+ *                    with G_d = H_d / draft_layers[l].H_kv;
+ *   S_Target[b][j] = sum over r < S of
+ *                    softmax_{j < n_b}(scale_target * q_hist[b][r] . Kt_{L(r)}[b][j][H(r) / G])
+ *                    where (L(r), H(r)) = (sub_heads[2r], sub_heads[2r+1]) and
+ *                    G = H_t / target_layers[L(r)].H_kv.
+ * The softmax runs over the history positions only.  q_hist holds the
+ * target's most recent query (history distance 1, translation section 3.2).
+ *
+ *  draft_layers   host [L_d] descriptors (k used; same B, N_max, H_kv,
+ *                 head_dim, dtype, paging for all layers)
+ *  q_draft        [B][L_d][gamma][H_d][d_draft], draft dtype
+ *  target_layers  host [L_t] descriptors (k used; same B, N_max as draft)
+ *  q_hist         [B][S][d_target], target dtype
+ *  sub_heads      host [S][2] (layer, head) pairs, 0 <= layer < L_t,
+ *                 0 <= head < H_t
+ *  scale_*        softmax scale; 0 means 1/sqrt(head_dim)
+ *  s_draft        [B][N_max] float32 out, 0 at j >= n_b; NULL or L_d == 0
+ *                 skips the draft side
+ *  s_target       [B][N_max] float32 out; NULL or S == 0 skips it
+ * Sequence lengths come from the first descriptor used (draft layer 0, else
+ * target layer 0); every descriptor must describe the same sequences.
+ */
+dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d,
+                           const void *q_draft, int32_t H_d, int32_t gamma,
+                           const dustin_kv *target_layers, int32_t L_t,
+                           const void *q_hist, const int32_t *sub_heads,
+                           int32_t S, int32_t H_t,
+                           float scale_draft, float scale_target,
+                           float *s_draft, float *s_target,
+                           void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_score_workspace_bytes(int32_t B, int32_t N_max, int32_t L_d,
+                                    int32_t H_d, int32_t gamma, int32_t S);
+
+/*
+ * dustin_topk -- the per-sequence verification set I_verify (blog section
+ * 2.3), global across layers and heads (blog section 2.2):
+ *   P = [0, min(n_sink, n)) U [max(0, n - n_window), n)      protected
+ *   D = the m' positions outside P with the largest S_Draft   draft tier
+ *   T = the positions outside P u D with the largest S_Target filling the
+ *       budget                                                 target tier
+ * with m' = min(m, k - |P|, n - |P|), |I| = min(k, n); ties go to the lower
+ * position.  s_draft == NULL means m' = 0; s_target == NULL means the draft
+ * tier fills the budget.  The SD oracle of the translation's Eq. (3) is this
+ * call on the window-mean attention with m = n_sink = n_window = 0.
+ *
+ *  s_draft, s_target  [B][N_max] float32, non-negative (positions >= n_b
+ *                     are ignored)
+ *  seq_lens           [B] device int32
+ *  idx   out [B][k] int32: selected positions in ascending order, -1 padded
+ *  count out [B] int32 = min(k, n_b)
+ *  tier  out, nullable [B][k] int8: 0 protected, 1 draft, 2 target, -1 pad
+ * Requires 1 <= k, 0 <= m, n_sink, n_window >= 0, n_sink + n_window <= k.
+ */
+dustin_status dustin_topk(const float *s_draft, const float *s_target,
+                          const int32_t *seq_lens, int32_t B, int32_t N_max,
+                          int32_t k, int32_t m, int32_t n_sink, int32_t n_window,
+                          int32_t *idx, int32_t *count, int8_t *tier,
+                          void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_topk_workspace_bytes(int32_t B, int32_t N_max, int32_t k);
+
+/*
+ * dustin_sparse_verify_attn -- Stage 2 of the blog's Fig. 5: attention of
+ * the w window queries over the compressed KV (only the selected rows).
+ *   O[b][s][h] = sum_{j in I_b} softmax_{j in I_b}(scale * q[b][s][h] . K[b][j][h/G]) V[b][j][h/G]
+ *   lse[b][s][h] = ln sum_{j in I_b} exp(scale * q[b][s][h] . K[b][j][h/G])
+ * with G = H_q / kv->H_kv and I_b = idx[b][0 .. count[b]).
+ * idx == NULL gives dense full-cache attention over j < n_b (the blog's
+ * "Full Cache" baseline of Fig. 7); count is then ignored and k must be 0.
+ *
+ *  q     [B][w][H_q][head_dim], kv dtype
+ *  kv    k and v required
+ *  idx   [B][k] int32 positions (any order, no duplicates), or NULL
+ *  count [B] int32 (entries beyond count[b] are ignored)
+ *  scale 0 means 1/sqrt(head_dim)
+ *  out   [B][w][H_q][head_dim], kv dtype; an empty set gives 0
+ *  lse   nullable [B][w][H_q] float32; an empty set gives -inf
+ * Requires w * (H_q / H_kv) <= 64.
+ */
+dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q,
+                                        const dustin_kv *kv, const int32_t *idx,
+                                        const int32_t *count, int32_t k, float scale,
+                                        void *out, float *lse,
+                                        void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+/* k_or_n: the k passed to the call, or N_max for the dense (idx == NULL) form. */
+size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv,
+                                   int32_t head_dim, int32_t k_or_n);
+
+/*
+ * dustin_window_attn -- the full-cache attention weights A_{i+s,j} of the
+ * translation's section 3.1 for every window step s < w, as the mean over
+ * the H_q query heads of one layer of each head's softmax over the history
+ * j < n_b (so sum_j A[b][s][j] = 1).
+ *
+ *  q   [B][w][H_q][head_dim], kv dtype
+ *  A   out [B][w][N_max] float32, 0 at j >= n_b
+ */
+dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q,
+                                 const dustin_kv *kv, float scale, float *A,
+                                 void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_window_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q,
+                                          int32_t H_kv, int32_t head_dim, int32_t N_max);
+
+/*
+ * dustin_arr -- attention recovery rate of an index set (translation section
+ * 3.1): Eq. (1) arr_step[b][s] = sum_{j in I_b} A[b][s][j] and Eq. (2)
+ * arr_window[b] = (1/w) sum_s arr_step[b][s].  Entries of idx beyond
+ * count[b], negative or >= n_b are ignored; duplicates count once per entry.
+ *
+ *  A          [B][w][N_max] float32 (e.g. from dustin_window_attn)
+ *  idx, count as produced by dustin_topk
+ *  arr_step   out [B][w] float32 (nullable)
+ *  arr_window out [B] float32 (nullable)
+ */
+dustin_status dustin_arr(const float *A, const int32_t *seq_lens, int32_t B, int32_t w,
+                         int32_t N_max, const int32_t *idx, const int32_t *count, int32_t k,
+                         float *arr_step, float *arr_window, dustin_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *dustin_status_string(dustin_status status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char *dustin_last_error(void);
+
+/* DUSTIN_ABI_VERSION of the loaded library. */
+int32_t dustin_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUSTIN_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) sparse-verification step of long-context speculative
+decoding (Dustin, arXiv 2606.24957): hybrid importance scoring, a global
+TopK verification set, and attention over the selected K/V rows only.
+
+The compute lives in libdustin.so (HIP kernels behind the C ABI of
+include/dustin.h); this package only marshals torch tensors into it.
+"""
+from ._lib import (  # noqa: F401
+    KV, DustinError, DustinKV, Workspace, lib,
+    dustin_arr, dustin_score, dustin_sparse_verify_attn, dustin_topk, dustin_window_attn,
+    EXPORTS, LIB_PATH,
+)

@@ -1,0 +1,268 @@
+"""ctypes binding of libdustin.so (include/dustin.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every computation runs in the library's gfx950 kernels.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdustin.so")
+
+DUSTIN_F32 = 0
+DUSTIN_BF16 = 1
+STATUS = {0: "DUSTIN_OK", 1: "DUSTIN_ERR_INVALID_ARG", 2: "DUSTIN_ERR_UNSUPPORTED", 3: "DUSTIN_ERR_HIP"}
+
+EXPORTS = [
+    "dustin_score", "dustin_score_workspace_bytes",
+    "dustin_topk", "dustin_topk_workspace_bytes",
+    "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes",
+    "dustin_window_attn", "dustin_window_attn_workspace_bytes",
+    "dustin_arr",
+    "dustin_status_string", "dustin_last_error", "dustin_abi_version",
+]
+
+
+class DustinKV(ctypes.Structure):
+    """Mirror of struct dustin_kv."""
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("N_max", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+    ]
+
+
+class DustinError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib():
+    """Load libdustin.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python -m sparse_kv_verification_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        kvp = ctypes.POINTER(DustinKV)
+        L.dustin_score.argtypes = [kvp, i32, vp, i32, i32, kvp, i32, vp, vp, i32, i32, f32, f32, vp, vp, vp, sz, vp]
+        L.dustin_score.restype = ctypes.c_int
+        L.dustin_score_workspace_bytes.argtypes = [i32] * 6
+        L.dustin_score_workspace_bytes.restype = sz
+        L.dustin_topk.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.dustin_topk.restype = ctypes.c_int
+        L.dustin_topk_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dustin_topk_workspace_bytes.restype = sz
+        L.dustin_sparse_verify_attn.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.dustin_sparse_verify_attn.restype = ctypes.c_int
+        L.dustin_attn_workspace_bytes.argtypes = [i32] * 6
+        L.dustin_attn_workspace_bytes.restype = sz
+        L.dustin_window_attn.argtypes = [vp, i32, i32, kvp, f32, vp, vp, sz, vp]
+        L.dustin_window_attn.restype = ctypes.c_int
+        L.dustin_window_attn_workspace_bytes.argtypes = [i32] * 6
+        L.dustin_window_attn_workspace_bytes.restype = sz
+        L.dustin_arr.argtypes = [vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+        L.dustin_arr.restype = ctypes.c_int
+        L.dustin_status_string.argtypes = [ctypes.c_int]
+        L.dustin_status_string.restype = ctypes.c_char_p
+        L.dustin_last_error.argtypes = []
+        L.dustin_last_error.restype = ctypes.c_char_p
+        L.dustin_abi_version.argtypes = []
+        L.dustin_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise DustinError(status, lib().dustin_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t=None):
+    if t is not None and t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DUSTIN_F32
+    if t.dtype == torch.bfloat16:
+        return DUSTIN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class KV:
+    """One layer's cache descriptor; keeps the tensors it points to alive.
+
+    Contiguous: k, v are [B][N_max][H_kv][head_dim].
+    Paged: k, v are [num_pages][16][H_kv][head_dim] with page_table
+    [B][max_pages] (int32); N_max defaults to max_pages * 16.
+    """
+
+    def __init__(self, k, v=None, seq_lens=None, page_table=None, N_max=None, B=None):
+        self.k, self.v, self.seq_lens, self.page_table = k, v, seq_lens, page_table
+        if seq_lens is None or seq_lens.dtype != torch.int32:
+            raise TypeError("seq_lens must be an int32 tensor")
+        if page_table is None:
+            Bk, N, H, D = k.shape
+            ps, maxp, npages = 0, 0, 0
+        else:
+            npages, ps, H, D = k.shape
+            Bk, maxp = page_table.shape
+            N = N_max if N_max is not None else maxp * ps
+        self.desc = DustinKV(
+            k=k.data_ptr(), v=v.data_ptr() if v is not None else None, dtype=_dtype_code(k),
+            B=B if B is not None else Bk, H_kv=H, head_dim=D, N_max=N,
+            seq_lens=seq_lens.data_ptr(), page_size=ps,
+            page_table=page_table.data_ptr() if page_table is not None else None,
+            max_pages=maxp, num_pages=npages)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def _kv_array(kvs):
+    arr = (DustinKV * len(kvs))(*[x.desc for x in kvs])
+    return arr
+
+
+class Workspace:
+    """Zero-initialised device scratch, grown on demand.  One per entry point:
+    the attention calls rely on the arrival counters at its start being zero
+    (they leave them zero), so it must not be shared with other calls."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _ws(name, ws, nbytes, device):
+    if ws is None:
+        ws = _default_ws.setdefault((name, str(device)), Workspace())
+    return ws.get(nbytes, device)
+
+
+# --------------------------------------------------------------------------
+
+def dustin_sparse_verify_attn(q, kv: KV, idx=None, count=None, k=None, scale=0.0,
+                              out=None, lse=None, ws: Workspace | None = None):
+    """Sparse verification attention over the rows idx[b][:count[b]] (or dense
+    over j < n_b when idx is None).  q: [B][w][H_q][d]."""
+    B, w, Hq, D = q.shape
+    kk = 0 if idx is None else (k if k is not None else idx.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    d = kv.desc
+    nbytes = lib().dustin_attn_workspace_bytes(d.B, w, Hq, d.H_kv, d.head_dim, kk if idx is not None else d.N_max)
+    wsb = _ws("attn", ws, nbytes, q.device)
+    _check(lib().dustin_sparse_verify_attn(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
+                                           _ptr(out), _ptr(lse), _ptr(wsb), wsb.numel(), _stream(q)))
+    return out
+
+
+def dustin_score(draft_kvs, q_draft, target_kvs, q_hist, sub_heads, H_t, s_draft=None, s_target=None,
+                 scale_draft=0.0, scale_target=0.0, ws: Workspace | None = None, want_draft=True,
+                 want_target=True):
+    """Hybrid importance vectors S_Draft, S_Target ([B][N_max] float32 each).
+    q_draft: [B][L_d][gamma][H_d][d_d]; q_hist: [B][S][d]; sub_heads: S
+    (layer, head) pairs into target_kvs."""
+    ref = (draft_kvs or target_kvs)[0]
+    B, N = ref.desc.B, ref.desc.N_max
+    dev = (q_draft if q_draft is not None else q_hist).device
+    L_d = len(draft_kvs) if (draft_kvs and want_draft) else 0
+    H_d = gamma = 0
+    if L_d:
+        _, L_chk, gamma, H_d, _ = q_draft.shape
+        assert L_chk == L_d, "q_draft layer count differs from draft_kvs"
+        if s_draft is None:
+            s_draft = torch.empty((B, N), dtype=torch.float32, device=dev)
+    S = len(sub_heads) if (sub_heads and want_target) else 0
+    if S and s_target is None:
+        s_target = torch.empty((B, N), dtype=torch.float32, device=dev)
+    heads = (ctypes.c_int32 * (2 * max(S, 1)))(*[x for p in (sub_heads or [])[:S] for x in p])
+    darr = _kv_array(draft_kvs) if L_d else None
+    tarr = _kv_array(target_kvs) if S else None
+    nbytes = lib().dustin_score_workspace_bytes(B, N, L_d, H_d, gamma, S)
+    wsb = _ws("score", ws, nbytes, dev)
+    _check(lib().dustin_score(darr, L_d, _ptr(q_draft) if L_d else None, H_d, gamma,
+                              tarr, len(target_kvs) if S else 0, _ptr(q_hist) if S else None,
+                              heads if S else None, S, int(H_t), float(scale_draft), float(scale_target),
+                              _ptr(s_draft) if L_d else None, _ptr(s_target) if S else None,
+                              _ptr(wsb), wsb.numel(), _stream(wsb)))
+    return s_draft, s_target
+
+
+def dustin_topk(s_draft, s_target, seq_lens, k, m, n_sink, n_window, idx=None, count=None, tier=None,
+                want_tier=True, ws: Workspace | None = None):
+    """Per-sequence verification set; returns (idx [B][k] int32 ascending,
+    count [B] int32, tier [B][k] int8 or None)."""
+    ref = s_target if s_target is not None else s_draft
+    B, N = ref.shape
+    dev = ref.device
+    if idx is None:
+        idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B,), dtype=torch.int32, device=dev)
+    if tier is None and want_tier:
+        tier = torch.empty((B, k), dtype=torch.int8, device=dev)
+    nbytes = lib().dustin_topk_workspace_bytes(B, N, k)
+    wsb = _ws("topk", ws, nbytes, dev)
+    _check(lib().dustin_topk(_ptr(s_draft), _ptr(s_target), _ptr(seq_lens), B, N, k, m, n_sink, n_window,
+                             _ptr(idx), _ptr(count), _ptr(tier), _ptr(wsb), wsb.numel(), _stream(ref)))
+    return idx, count, tier
+
+
+def dustin_window_attn(q, kv: KV, scale=0.0, A=None, ws: Workspace | None = None):
+    """Head-mean full-cache attention weights A [B][w][N_max] (float32)."""
+    B, w, Hq, D = q.shape
+    d = kv.desc
+    if A is None:
+        A = torch.empty((B, w, d.N_max), dtype=torch.float32, device=q.device)
+    nbytes = lib().dustin_window_attn_workspace_bytes(d.B, w, Hq, d.H_kv, d.head_dim, d.N_max)
+    wsb = _ws("window", ws, nbytes, q.device)
+    _check(lib().dustin_window_attn(_ptr(q), w, Hq, kv.ref, float(scale), _ptr(A), _ptr(wsb), wsb.numel(),
+                                    _stream(q)))
+    return A
+
+
+def dustin_arr(A, seq_lens, idx, count, arr_step=None, arr_window=None):
+    """ARR per window step (Eq. 1) and windowed ARR (Eq. 2)."""
+    B, w, N = A.shape
+    k = idx.shape[1]
+    if arr_step is None:
+        arr_step = torch.empty((B, w), dtype=torch.float32, device=A.device)
+    if arr_window is None:
+        arr_window = torch.empty((B,), dtype=torch.float32, device=A.device)
+    _check(lib().dustin_arr(_ptr(A), _ptr(seq_lens), B, w, N, _ptr(idx), _ptr(count), k, _ptr(arr_step),
+                            _ptr(arr_window), _stream(A)))
+    return arr_step, arr_window

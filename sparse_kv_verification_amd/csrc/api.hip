@@ -1,0 +1,415 @@
+// C ABI of the sparse-verification library (declared in include/dustin.h).
+//
+// Every entry point validates its arguments on the host first and returns
+// DUSTIN_ERR_INVALID_ARG / DUSTIN_ERR_UNSUPPORTED before touching the HIP
+// runtime, then enqueues its kernels on the caller's stream.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dustin.h"
+#include "common.h"
+#include "internal.h"
+
+using namespace dustin;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dustin_status fail(dustin_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dustin_status ok() {
+    g_last_error.clear();
+    return DUSTIN_OK;
+}
+
+dustin_status hip_status(hipError_t e, const char *where) {
+    if (e == hipSuccess) return ok();
+    return fail(DUSTIN_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define CHECK(cond, st, ...)                         \
+    do {                                             \
+        if (!(cond)) return fail((st), __VA_ARGS__); \
+    } while (0)
+
+constexpr int64_t kInt32Max = 2147483647LL;
+
+dustin_status check_kv(const dustin_kv *kv, const char *what, bool need_v) {
+    CHECK(kv != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: descriptor is NULL", what);
+    CHECK(kv->k != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: k is NULL", what);
+    CHECK(!need_v || kv->v != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: v is NULL", what);
+    CHECK(kv->dtype == DUSTIN_F32 || kv->dtype == DUSTIN_BF16, DUSTIN_ERR_UNSUPPORTED,
+          "%s: dtype %d not supported", what, kv->dtype);
+    CHECK(kv->B >= 1 && kv->H_kv >= 1 && kv->N_max >= 1, DUSTIN_ERR_INVALID_ARG,
+          "%s: B, H_kv and N_max must be >= 1 (got %d, %d, %d)", what, kv->B, kv->H_kv, kv->N_max);
+    CHECK(kv->head_dim == 32 || kv->head_dim == 64 || kv->head_dim == 128, DUSTIN_ERR_UNSUPPORTED,
+          "%s: head_dim %d not supported (32, 64, 128)", what, kv->head_dim);
+    CHECK(kv->seq_lens != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: seq_lens is NULL", what);
+    if (kv->page_size == 0) {
+        CHECK((int64_t)kv->B * kv->N_max <= kInt32Max, DUSTIN_ERR_UNSUPPORTED, "%s: B * N_max too large", what);
+    } else if (kv->page_size == 16) {
+        CHECK(kv->page_table != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: paged cache without page_table", what);
+        CHECK(kv->max_pages >= (kv->N_max + 15) / 16, DUSTIN_ERR_INVALID_ARG,
+              "%s: max_pages %d < ceil(N_max / 16)", what, kv->max_pages);
+        CHECK(kv->num_pages >= 1 && (int64_t)kv->num_pages * 16 <= kInt32Max, DUSTIN_ERR_INVALID_ARG,
+              "%s: num_pages %d out of range", what, kv->num_pages);
+    } else {
+        return fail(DUSTIN_ERR_UNSUPPORTED, "%s: page_size %d not supported (0, 16)", what, kv->page_size);
+    }
+    return DUSTIN_OK;
+}
+
+KvView view_of(const dustin_kv *kv) {
+    KvView v{};
+    v.k = (const char *)kv->k;
+    v.v = (const char *)kv->v;
+    v.seq_lens = kv->seq_lens;
+    v.page_table = kv->page_size ? kv->page_table : nullptr;
+    v.B = kv->B;
+    v.Hkv = kv->H_kv;
+    v.D = kv->head_dim;
+    v.N_max = kv->N_max;
+    v.page_size = kv->page_size;
+    v.max_pages = kv->max_pages;
+    v.num_pages = kv->num_pages;
+    v.f32 = kv->dtype == DUSTIN_F32;
+    return v;
+}
+
+bool same_geometry(const dustin_kv *a, const dustin_kv *b) {
+    return a->B == b->B && a->N_max == b->N_max && a->H_kv == b->H_kv && a->head_dim == b->head_dim &&
+           a->dtype == b->dtype && a->page_size == b->page_size;
+}
+
+float resolve_scale(float scale, int d) { return scale == 0.f ? 1.f / std::sqrt((float)d) : scale; }
+
+dustin_status check_attn_shape(const dustin_kv *kv, int w, int H_q, const char *what) {
+    CHECK(w >= 1 && H_q >= 1, DUSTIN_ERR_INVALID_ARG, "%s: w and H_q must be >= 1", what);
+    CHECK(H_q % kv->H_kv == 0, DUSTIN_ERR_INVALID_ARG, "%s: H_q %d not a multiple of H_kv %d", what, H_q, kv->H_kv);
+    CHECK(w * (H_q / kv->H_kv) <= 64, DUSTIN_ERR_UNSUPPORTED, "%s: w * G = %d exceeds 64", what, w * (H_q / kv->H_kv));
+    CHECK(kv->dtype == DUSTIN_F32 || kv->head_dim >= 64, DUSTIN_ERR_UNSUPPORTED,
+          "%s: bf16 attention needs head_dim 64 or 128", what);
+    return DUSTIN_OK;
+}
+
+struct WindowLayout {
+    AttnPlan plan;
+    size_t off_out, off_lse, bytes;
+};
+
+WindowLayout window_layout(int B, int w, int H_q, int H_kv, int D, int N_max, int esz) {
+    WindowLayout L{};
+    L.plan = attn_plan(B, w, H_q, H_kv, D, N_max, false);
+    size_t off = L.plan.ws_bytes;
+    L.off_out = off;
+    off = align_up(off + (size_t)B * w * H_q * D * esz, 256);
+    L.off_lse = off;
+    off = align_up(off + (size_t)B * w * H_q * sizeof(float), 256);
+    L.bytes = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dustin_status_string(dustin_status st) {
+    switch (st) {
+        case DUSTIN_OK: return "DUSTIN_OK";
+        case DUSTIN_ERR_INVALID_ARG: return "DUSTIN_ERR_INVALID_ARG";
+        case DUSTIN_ERR_UNSUPPORTED: return "DUSTIN_ERR_UNSUPPORTED";
+        case DUSTIN_ERR_HIP: return "DUSTIN_ERR_HIP";
+    }
+    return "DUSTIN_ERR_UNKNOWN";
+}
+
+const char *dustin_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dustin_abi_version(void) { return DUSTIN_ABI_VERSION; }
+
+size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv, int32_t head_dim, int32_t k_or_n) {
+    if (B < 1 || w < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || head_dim < 1 || k_or_n < 1) return 0;
+    return attn_plan(B, w, H_q, H_kv, head_dim, k_or_n, false).ws_bytes;
+}
+
+dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                        const int32_t *idx, const int32_t *count, int32_t k, float scale,
+                                        void *out, float *lse, void *ws, size_t ws_bytes,
+                                        dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "sparse_verify_attn kv", true);
+    if (st != DUSTIN_OK) return st;
+    if ((st = check_attn_shape(kv, w, H_q, "sparse_verify_attn")) != DUSTIN_OK) return st;
+    CHECK(q != nullptr && out != nullptr, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: q and out are required");
+    if (idx) {
+        CHECK(count != nullptr, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: count is NULL");
+        CHECK(k >= 1, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: k must be >= 1 (got %d)", k);
+    } else {
+        CHECK(k == 0, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: dense form (idx NULL) needs k == 0");
+    }
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: scale is not finite");
+    const int tokens = idx ? k : kv->N_max;
+    const AttnPlan p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
+    CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "sparse_verify_attn: too many tokens");
+    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+          "sparse_verify_attn: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+    AttnArgs a{};
+    a.kv = view_of(kv);
+    a.q = q;
+    a.w = w;
+    a.Hq = H_q;
+    a.G = H_q / kv->H_kv;
+    a.R = w * a.G;
+    a.idx = idx;
+    a.count = count;
+    a.k = idx ? k : 0;
+    a.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
+    a.out = out;
+    a.lse = lse;
+    char *wsb = (char *)ws;
+    a.counters = (int32_t *)wsb;
+    a.part_m = (float *)(wsb + p.off_m);
+    a.part_l = (float *)(wsb + p.off_l);
+    a.part_o = (float *)(wsb + p.off_o);
+    a.splits = p.splits;
+    a.tps = p.tps;
+    a.rpad = p.rpad;
+    return hip_status(launch_attn(a, p, (hipStream_t)stream), "sparse_verify_attn launch");
+}
+
+size_t dustin_window_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv, int32_t head_dim,
+                                          int32_t N_max) {
+    if (B < 1 || w < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || head_dim < 1 || N_max < 1) return 0;
+    return window_layout(B, w, H_q, H_kv, head_dim, N_max, 4).bytes;
+}
+
+dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv, float scale, float *A,
+                                 void *ws, size_t ws_bytes, dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "window_attn kv", false);
+    if (st != DUSTIN_OK) return st;
+    if ((st = check_attn_shape(kv, w, H_q, "window_attn")) != DUSTIN_OK) return st;
+    CHECK(w <= 16, DUSTIN_ERR_UNSUPPORTED, "window_attn: w %d exceeds 16", w);
+    CHECK(q != nullptr && A != nullptr, DUSTIN_ERR_INVALID_ARG, "window_attn: q and A are required");
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "window_attn: scale is not finite");
+    // The dense pass needs V only for its (discarded) output; K stands in.
+    const WindowLayout L = window_layout(kv->B, w, H_q, kv->H_kv, kv->head_dim, kv->N_max, 4);
+    CHECK(ws != nullptr && ws_bytes >= L.bytes, DUSTIN_ERR_INVALID_ARG,
+          "window_attn: workspace of %zu bytes needed (got %zu)", L.bytes, ws_bytes);
+    char *wsb = (char *)ws;
+    AttnArgs a{};
+    a.kv = view_of(kv);
+    a.kv.v = a.kv.k;
+    a.q = q;
+    a.w = w;
+    a.Hq = H_q;
+    a.G = H_q / kv->H_kv;
+    a.R = w * a.G;
+    a.idx = nullptr;
+    a.count = nullptr;
+    a.k = 0;
+    const float sc = resolve_scale(scale, kv->head_dim);
+    a.scale_log2 = sc * kLog2e;
+    a.out = wsb + L.off_out;
+    a.lse = (float *)(wsb + L.off_lse);
+    a.counters = (int32_t *)wsb;
+    a.part_m = (float *)(wsb + L.plan.off_m);
+    a.part_l = (float *)(wsb + L.plan.off_l);
+    a.part_o = (float *)(wsb + L.plan.off_o);
+    a.splits = L.plan.splits;
+    a.tps = L.plan.tps;
+    a.rpad = L.plan.rpad;
+    hipError_t e = launch_attn(a, L.plan, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "window_attn dense pass");
+    WindowArgs wa{};
+    wa.kv = view_of(kv);
+    wa.q = q;
+    wa.w = w;
+    wa.Hq = H_q;
+    wa.G = a.G;
+    wa.scale_log2 = a.scale_log2;
+    wa.lse = a.lse;
+    wa.A = A;
+    return hip_status(launch_window_probs(wa, (hipStream_t)stream), "window_attn probabilities");
+}
+
+dustin_status dustin_arr(const float *A, const int32_t *seq_lens, int32_t B, int32_t w, int32_t N_max,
+                         const int32_t *idx, const int32_t *count, int32_t k, float *arr_step,
+                         float *arr_window, dustin_stream_t stream) {
+    CHECK(A && seq_lens && idx && count, DUSTIN_ERR_INVALID_ARG, "arr: A, seq_lens, idx and count are required");
+    CHECK(B >= 1 && w >= 1 && N_max >= 1 && k >= 1, DUSTIN_ERR_INVALID_ARG, "arr: B, w, N_max and k must be >= 1");
+    CHECK(w <= 64, DUSTIN_ERR_UNSUPPORTED, "arr: w %d exceeds 64", w);
+    ArrArgs a{A, seq_lens, B, w, N_max, k, idx, count, arr_step, arr_window};
+    if (!arr_step && !arr_window) return ok();
+    return hip_status(launch_arr(a, (hipStream_t)stream), "arr launch");
+}
+
+size_t dustin_topk_workspace_bytes(int32_t B, int32_t N_max, int32_t k) {
+    if (B < 1 || N_max < 1 || k < 1) return 0;
+    return topk_plan(B, N_max, k).ws_bytes;
+}
+
+dustin_status dustin_topk(const float *s_draft, const float *s_target, const int32_t *seq_lens, int32_t B,
+                          int32_t N_max, int32_t k, int32_t m, int32_t n_sink, int32_t n_window, int32_t *idx,
+                          int32_t *count, int8_t *tier, void *ws, size_t ws_bytes, dustin_stream_t stream) {
+    CHECK(s_draft || s_target, DUSTIN_ERR_INVALID_ARG, "topk: at least one score vector is required");
+    CHECK(seq_lens && idx && count, DUSTIN_ERR_INVALID_ARG, "topk: seq_lens, idx and count are required");
+    CHECK(B >= 1 && N_max >= 1, DUSTIN_ERR_INVALID_ARG, "topk: B and N_max must be >= 1");
+    CHECK(k >= 1, DUSTIN_ERR_INVALID_ARG, "topk: k must be >= 1 (got %d)", k);
+    CHECK(m >= 0 && n_sink >= 0 && n_window >= 0, DUSTIN_ERR_INVALID_ARG, "topk: m, n_sink, n_window must be >= 0");
+    CHECK((int64_t)n_sink + n_window <= k, DUSTIN_ERR_INVALID_ARG,
+          "topk: n_sink + n_window = %d exceeds k = %d", n_sink + n_window, k);
+    CHECK((int64_t)B * N_max <= kInt32Max, DUSTIN_ERR_UNSUPPORTED, "topk: B * N_max too large");
+    const TopkPlan p = topk_plan(B, N_max, k);
+    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+          "topk: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+    TopkArgs a{};
+    a.s_draft = s_draft;
+    a.s_target = s_target;
+    a.seq_lens = seq_lens;
+    a.B = B;
+    a.N_max = N_max;
+    a.k = k;
+    a.m = m;
+    a.n_sink = n_sink;
+    a.n_window = n_window;
+    a.idx = idx;
+    a.count = count;
+    a.tier = tier;
+    a.flag = (uint8_t *)ws + p.off_flag;
+    return hip_status(launch_topk(a, (hipStream_t)stream), "topk launch");
+}
+
+size_t dustin_score_workspace_bytes(int32_t B, int32_t N_max, int32_t L_d, int32_t H_d, int32_t gamma, int32_t S) {
+    if (B < 1 || N_max < 1 || L_d < 0 || H_d < 0 || gamma < 0 || S < 0) return 0;
+    return score_plan(B, N_max, L_d, H_d, gamma, S, 1).ws_bytes;
+}
+
+dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const void *q_draft, int32_t H_d,
+                           int32_t gamma, const dustin_kv *target_layers, int32_t L_t, const void *q_hist,
+                           const int32_t *sub_heads, int32_t S, int32_t H_t, float scale_draft,
+                           float scale_target, float *s_draft, float *s_target, void *ws, size_t ws_bytes,
+                           dustin_stream_t stream) {
+    const bool do_draft = s_draft != nullptr && L_d > 0;
+    const bool do_target = s_target != nullptr && S > 0;
+    CHECK(L_d >= 0 && S >= 0 && L_t >= 0, DUSTIN_ERR_INVALID_ARG, "score: negative count");
+    CHECK(std::isfinite(scale_draft) && std::isfinite(scale_target), DUSTIN_ERR_INVALID_ARG,
+          "score: scale is not finite");
+    const dustin_kv *ref = nullptr;
+    int Hkv_d = 1;
+    int G_d = 1;
+    if (do_draft) {
+        CHECK(draft_layers != nullptr, DUSTIN_ERR_INVALID_ARG, "score: draft_layers is NULL");
+        CHECK(L_d <= kMaxDraftLayers, DUSTIN_ERR_UNSUPPORTED, "score: L_d %d exceeds %d", L_d, kMaxDraftLayers);
+        for (int l = 0; l < L_d; ++l) {
+            dustin_status st = check_kv(&draft_layers[l], "score draft layer", false);
+            if (st != DUSTIN_OK) return st;
+            CHECK(same_geometry(&draft_layers[l], &draft_layers[0]), DUSTIN_ERR_INVALID_ARG,
+                  "score: draft layer %d differs in geometry from layer 0", l);
+        }
+        ref = &draft_layers[0];
+        CHECK(q_draft != nullptr, DUSTIN_ERR_INVALID_ARG, "score: q_draft is NULL");
+        CHECK(H_d >= 1 && gamma >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_d and gamma must be >= 1");
+        Hkv_d = ref->H_kv;
+        CHECK(H_d % Hkv_d == 0, DUSTIN_ERR_INVALID_ARG, "score: H_d %d not a multiple of draft H_kv %d", H_d, Hkv_d);
+        G_d = H_d / Hkv_d;
+        CHECK(gamma * G_d <= 64, DUSTIN_ERR_UNSUPPORTED, "score: gamma * G_d = %d exceeds 64", gamma * G_d);
+        if (ref->dtype == DUSTIN_F32) {
+            CHECK(L_d <= 8 && (int64_t)L_d * H_d * gamma <= kMaxScoreQoff &&
+                      (int64_t)L_d * Hkv_d * ((gamma * G_d + 7) / 8) <= kMaxScoreRows,
+                  DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than this build supports");
+        }
+    }
+    int view_of_layer[64];
+    int n_views = 0;
+    int layer_ids[8];
+    if (do_target) {
+        CHECK(target_layers != nullptr && L_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: target_layers missing");
+        CHECK(sub_heads != nullptr && q_hist != nullptr, DUSTIN_ERR_INVALID_ARG, "score: sub_heads / q_hist missing");
+        CHECK(S <= kMaxScoreRows, DUSTIN_ERR_UNSUPPORTED, "score: S %d exceeds %d", S, kMaxScoreRows);
+        CHECK(H_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_t must be >= 1");
+        CHECK(L_t <= 64, DUSTIN_ERR_UNSUPPORTED, "score: L_t %d exceeds 64", L_t);
+        for (int l = 0; l < L_t; ++l) view_of_layer[l] = -1;
+        for (int r = 0; r < S; ++r) {
+            const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
+            CHECK(l >= 0 && l < L_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] layer %d out of range", r, l);
+            CHECK(h >= 0 && h < H_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] head %d out of range", r, h);
+            if (view_of_layer[l] < 0) {
+                dustin_status st = check_kv(&target_layers[l], "score target layer", false);
+                if (st != DUSTIN_OK) return st;
+                CHECK(n_views < 8, DUSTIN_ERR_UNSUPPORTED, "score: more than 8 distinct target layers");
+                CHECK(H_t % target_layers[l].H_kv == 0, DUSTIN_ERR_INVALID_ARG,
+                      "score: H_t %d not a multiple of layer %d H_kv", H_t, l);
+                view_of_layer[l] = n_views;
+                layer_ids[n_views++] = l;
+            }
+        }
+        const dustin_kv *t0 = &target_layers[layer_ids[0]];
+        for (int i = 1; i < n_views; ++i)
+            CHECK(same_geometry(&target_layers[layer_ids[i]], t0), DUSTIN_ERR_INVALID_ARG,
+                  "score: scored target layers differ in geometry");
+        if (ref) {
+            CHECK(t0->B == ref->B && t0->N_max == ref->N_max, DUSTIN_ERR_INVALID_ARG,
+                  "score: draft and target describe different batches");
+        } else {
+            ref = t0;
+        }
+    }
+    if (!do_draft && !do_target) return ok();
+    const ScorePlan p = score_plan(ref->B, ref->N_max, do_draft ? L_d : 0, H_d, gamma, do_target ? S : 0, Hkv_d);
+    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+          "score: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+    char *wsb = (char *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    if (do_target) {
+        TargetScoreArgs a{};
+        for (int i = 0; i < n_views; ++i) a.kv[i] = view_of(&target_layers[layer_ids[i]]);
+        a.n_layers = n_views;
+        a.q_hist = q_hist;
+        a.S = S;
+        for (int r = 0; r < S; ++r) {
+            const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
+            a.row_layer[r] = view_of_layer[l];
+            a.row_kvh[r] = h / (H_t / target_layers[l].H_kv);
+        }
+        a.scale_log2 = resolve_scale(scale_target, a.kv[0].D) * kLog2e;
+        a.s_target = s_target;
+        a.logit = (float *)(wsb + p.off_tlogit);
+        a.stat = (float *)(wsb + p.off_tstat);
+        a.lse = (float *)(wsb + p.off_tlse);
+        a.nchunk = p.nchunk;
+        hipError_t e = launch_target_score(a, s);
+        if (e != hipSuccess) return hip_status(e, "score target launch");
+    }
+    if (do_draft) {
+        DraftScoreArgs a{};
+        for (int l = 0; l < L_d; ++l) a.kv[l] = view_of(&draft_layers[l]);
+        a.L_d = L_d;
+        a.H_d = H_d;
+        a.gamma = gamma;
+        a.Hkv_d = Hkv_d;
+        a.G_d = G_d;
+        a.rows = gamma * G_d;
+        a.q_draft = q_draft;
+        a.scale_log2 = resolve_scale(scale_draft, a.kv[0].D) * kLog2e;
+        a.s_draft = s_draft;
+        a.stat = (float *)(wsb + p.off_dstat);
+        a.lse = (float *)(wsb + p.off_dlse);
+        a.nchunk = p.nchunk;
+        hipError_t e = launch_draft_score(a, s);
+        if (e != hipSuccess) return hip_status(e, "score draft launch");
+    }
+    return ok();
+}
+
+}  // extern "C"

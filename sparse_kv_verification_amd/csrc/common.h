@@ -1,0 +1,140 @@
+// Device-side helpers shared by the gfx950 kernels of the sparse-verification
+// step: vector types for the MFMA operands, bf16 conversion, wave64
+// reductions and the LDS-DMA / waitcnt wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dustin {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t x = __float_as_uint(f);
+    if ((x & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((x >> 16) | 0x40u);
+    x += 0x7fffu + ((x >> 16) & 1u);
+    return static_cast<uint16_t>(x >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Reduce across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+// Reduce across the 16 lanes of one 16-lane group.
+__device__ __forceinline__ float lane16_sum(float v) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float lane16_max(float v) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS.  `lds_base` is the
+// wave-uniform destination; lane i lands at lds_base + 16 * i.
+__device__ __forceinline__ void dma16(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS byte address (the offset register value of ds_* instructions).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(lds_void_t *)p;
+}
+
+// Transposed LDS reads (ds_read_b64_tr_b16) of the V operand of the PV
+// product, issued as one block that also waits for their completion.  Within
+// each 16-lane group, lane i receives element (i mod 4) of the 8-byte rows
+// addressed by lanes 4t + i/4, t = 0..3.  addr[d] is this lane's address for
+// the first row quad of d tile d; the second quad sits OFF1 bytes further.
+// Written as inline assembly so that the compiler does not serialise these
+// reads behind the global->LDS copies still in flight to other buffers.
+template <int OFF1>
+__device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&addr)[8], s16x4 (&lo)[8], s16x4 (&hi)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %20 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %10, %21\n\t"
+        "ds_read_b64_tr_b16 %11, %21 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %12, %22\n\t"
+        "ds_read_b64_tr_b16 %13, %22 offset:%c24\n\t"
+        "ds_read_b64_tr_b16 %14, %23\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%c24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+          "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]),
+          "v"(addr[6]), "v"(addr[7]), "i"(OFF1)
+        : "memory");
+}
+
+template <int OFF1>
+__device__ __forceinline__ void ds_read_tr16_x4(const uint32_t (&addr)[4], s16x4 (&lo)[4], s16x4 (&hi)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%c12\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%c12\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%c12\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%c12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF1)
+        : "memory");
+}
+
+}  // namespace dustin

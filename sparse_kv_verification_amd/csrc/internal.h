@@ -1,0 +1,141 @@
+// Internal interfaces between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dustin {
+
+// Device-side view of one layer's KV cache (see dustin_kv in dustin.h).
+struct KvView {
+    const char *k;
+    const char *v;
+    const int32_t *seq_lens;
+    const int32_t *page_table;
+    int32_t B, Hkv, D, N_max;
+    int32_t page_size, max_pages, num_pages;
+    int32_t f32;  // 1 = float32 storage, 0 = bfloat16
+};
+
+// ---------------------------------------------------------------- attention
+constexpr int kAttnTile = 32;       // tokens per pipeline tile
+constexpr int kAttnMaxTps = 1024;   // tokens per split (row table in LDS)
+constexpr int kAttnMaxSplits = 1024;
+
+struct AttnPlan {
+    int rows;      // R = w * G query rows per (sequence, KV head)
+    int rb;        // 16-row blocks
+    int rpad;      // 16 * rb
+    int splits;    // token splits per (sequence, KV head)
+    int tps;       // tokens per split (multiple of kAttnTile)
+    size_t off_m, off_l, off_o;  // workspace byte offsets
+    size_t ws_bytes;
+};
+
+AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32);
+
+struct AttnArgs {
+    KvView kv;
+    const void *q;           // [B][w][Hq][D]
+    int32_t w, Hq, G, R;
+    const int32_t *idx;      // [B][k] or nullptr (dense)
+    const int32_t *count;    // [B]
+    int32_t k;
+    float scale_log2;        // softmax scale * log2(e)
+    void *out;               // [B][w][Hq][D]
+    float *lse;              // [B][w][Hq] or nullptr
+    float *part_m, *part_l, *part_o;
+    int32_t *counters;       // [B * Hkv]
+    int32_t splits, tps, rpad;
+};
+
+hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+
+// ---------------------------------------------------------------- scoring
+constexpr int kScoreChunk = 256;    // positions per scoring work-group
+constexpr int kMaxScoreRows = 64;   // scored target rows
+constexpr int kMaxDraftLayers = 32;
+constexpr int kMaxScoreQoff = 256;   // rows of the float32 draft path
+
+struct ScorePlan {
+    int nchunk;                     // ceil(N_max / kScoreChunk)
+    // target side
+    size_t off_tlogit, off_tstat, off_tlse;   // [B][S][N_max], [B][S][nchunk][2], [B][S]
+    // draft side
+    size_t off_dstat, off_dlse;     // [B][L_d][Hkv_d][rows][nchunk][2], [B][L_d][Hkv_d][rows]
+    size_t ws_bytes;
+};
+
+ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int Hkv_d);
+
+struct TargetScoreArgs {
+    KvView kv[8];                   // distinct target layers referenced (<= 8)
+    int32_t n_layers;
+    const void *q_hist;             // [B][S][D]
+    int32_t S;
+    int32_t row_layer[kMaxScoreRows];   // index into kv[]
+    int32_t row_kvh[kMaxScoreRows];     // KV head of each row
+    float scale_log2;
+    float *s_target;                // [B][N_max]
+    float *logit;                   // ws
+    float *stat;                    // ws
+    float *lse;                     // ws
+    int32_t nchunk;
+};
+
+hipError_t launch_target_score(const TargetScoreArgs &a, hipStream_t s);
+
+struct DraftScoreArgs {
+    KvView kv[kMaxDraftLayers];
+    int32_t L_d, H_d, gamma, Hkv_d, G_d, rows;  // rows = gamma * G_d
+    const void *q_draft;            // [B][L_d][gamma][H_d][d_d]
+    float scale_log2;
+    float *s_draft;                 // [B][N_max]
+    float *stat;                    // ws
+    float *lse;                     // ws
+    int32_t nchunk;
+};
+
+hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- select
+struct TopkPlan {
+    size_t off_flag;                // [B][N_max] uint8 tier flags
+    size_t ws_bytes;
+};
+TopkPlan topk_plan(int B, int N_max, int k);
+
+struct TopkArgs {
+    const float *s_draft, *s_target;
+    const int32_t *seq_lens;
+    int32_t B, N_max, k, m, n_sink, n_window;
+    int32_t *idx, *count;
+    int8_t *tier;
+    uint8_t *flag;
+};
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- evaluator
+struct WindowArgs {
+    KvView kv;
+    const void *q;                  // [B][w][Hq][D]
+    int32_t w, Hq, G;
+    float scale_log2;
+    const float *lse;               // [B][w][Hq] natural-log row normalisers
+    float *A;                       // [B][w][N_max]
+};
+hipError_t launch_window_probs(const WindowArgs &a, hipStream_t s);
+
+struct ArrArgs {
+    const float *A;
+    const int32_t *seq_lens;
+    int32_t B, w, N_max, k;
+    const int32_t *idx, *count;
+    float *arr_step, *arr_window;
+};
+hipError_t launch_arr(const ArrArgs &a, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace dustin

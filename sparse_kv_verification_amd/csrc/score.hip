@@ -1,0 +1,635 @@
+// Hybrid token-importance scoring (Dustin blog section 2.2; scored target
+// heads restricted to a small searched subset, section 2.4) for gfx950.
+//
+//   S_Target[b][j] = sum_r softmax_j(scale * q_hist[b][r] . K_{L(r)}[b][j][kv(r)])
+//   S_Draft[b][j]  = sum_{l,h,g} softmax_j(scale_d * q_draft[b][l][g][h] . Kd_l[b][j][h/G_d])
+//
+// Each softmax is normalised over the whole history j < n_b before the sum,
+// so every row needs its global max and sum.  Both sides therefore work in
+// two steps:
+//   1. a streaming pass over K that produces, per row and per 256-position
+//      chunk, the chunk max and sum of exp2 (log2 domain);
+//   2. a second step that turns the chunk statistics into each row's
+//      log-sum-exp and accumulates the normalised probabilities per position.
+// Target side: step 1 also keeps the (few) logits, so step 2 reads logits
+// instead of K.  Draft side: 28 rows per K row make stored logits larger than
+// K itself, so step 2 recomputes the logits from K with MFMA.
+//
+// Work-group -> data mapping: one 256-lane work-group per (sequence, unit,
+// 256-position chunk) in step 1; one per (sequence, chunk) in the draft's
+// step 2, which loops over all draft (layer, KV head) units and sums in a
+// fixed order, so S_Draft is bitwise deterministic without atomics.
+
+#include "common.h"
+#include "internal.h"
+
+namespace dustin {
+
+constexpr int CH = kScoreChunk;
+
+__device__ __forceinline__ int sl_len(const KvView &kv, int b) {
+    return min(max(kv.seq_lens[b], 0), kv.N_max);
+}
+
+// Byte pointer to the head row (b, j, h) of one layer's K, or nullptr when a
+// page id is out of range.
+__device__ __forceinline__ const char *krow(const KvView &kv, int b, int j, int h, int esz) {
+    int64_t r;
+    if (kv.page_size == 0) {
+        r = (int64_t)b * kv.N_max + j;
+    } else {
+        const int pg = kv.page_table[(int64_t)b * kv.max_pages + (j >> 4)];
+        if (pg < 0 || pg >= kv.num_pages) return nullptr;
+        r = (int64_t)pg * 16 + (j & 15);
+    }
+    return kv.k + ((r * kv.Hkv + h) * kv.D) * esz;
+}
+
+// Load the 16-byte slice `slice` of a head row as floats (8 bf16 or 4 f32).
+template <bool F32>
+__device__ __forceinline__ void load_slice(const char *row, int slice, float (&x)[8]) {
+    if (row == nullptr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+        return;
+    }
+    const u32x4 v = *(const u32x4 *)(row + slice * 16);
+    if constexpr (F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v[i]);
+#pragma unroll
+        for (int i = 4; i < 8; ++i) x[i] = 0.f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(v[i] << 16);
+            x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU statistics pass.  A "unit" is one (layer view, KV head) with up
+// to 8 query rows sharing it.  Lanes are grouped LPI per position (16 bytes
+// per lane); each group computes the dot products of one K row with the
+// unit's rows.
+
+struct UnitTable {
+    int32_t n_units;
+    int32_t view[kMaxScoreRows];     // index into the KvView array
+    int32_t kvh[kMaxScoreRows];
+    int32_t row0[kMaxScoreRows];     // first global row id of the unit
+    int32_t nrow[kMaxScoreRows];     // rows in the unit (<= 8)
+};
+
+template <bool F32, int D, int NV>
+struct ValuStatsParams {
+    KvView kv[NV];
+    UnitTable ut;
+    const char *q;                   // row r of sequence b at q + (b * q_bstride + qoff[r]) * esz
+    int64_t q_bstride;
+    int32_t qoff[kMaxScoreQoff];
+    int32_t total_rows;
+    float scale_log2;
+    float *stat;                     // [B][total_rows][nchunk][2]
+    float *logit;                    // [B][total_rows][N_max] or nullptr
+    int32_t nchunk, N_max;
+};
+
+template <bool F32, int D, int NV>
+__global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, NV> p) {
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int LPI = D * ESZ / 16;         // lanes per position
+    constexpr int EPL = 16 / ESZ;             // elements per lane
+    constexpr int IPP = 256 / LPI;            // positions per pass
+    __shared__ float qs[8][D];
+    __shared__ float lg[8][CH];
+
+    const int chunk = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const KvView &kv = p.kv[p.ut.view[u]];
+    const int kvh = p.ut.kvh[u], row0 = p.ut.row0[u], nr = p.ut.nrow[u];
+    const int nb = sl_len(kv, b);
+    const int j0 = chunk * CH;
+
+    for (int e = tid; e < nr * D; e += 256) {
+        const int r = e / D, d = e - (e / D) * D;
+        const char *qp = p.q + ((int64_t)b * p.q_bstride + p.qoff[row0 + r] + d) * ESZ;
+        qs[r][d] = F32 ? *(const float *)qp : bf16_bits_to_f32(*(const uint16_t *)qp);
+    }
+    __syncthreads();
+
+    const int grp = tid / LPI, sl = tid - (tid / LPI) * LPI;
+    for (int pos = grp; pos < CH; pos += IPP) {
+        const int j = j0 + pos;
+        float x[8];
+        const bool ok = j < nb;
+        load_slice<F32>(ok ? krow(kv, b, j, kvh, ESZ) : nullptr, sl, x);
+        for (int r = 0; r < nr; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) s += qs[r][sl * EPL + i] * x[i];
+#pragma unroll
+            for (int o = LPI / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+            if (sl == 0) lg[r][pos] = ok ? s * p.scale_log2 : kNegInf;
+        }
+    }
+    __syncthreads();
+
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int r = wave; r < nr; r += 4) {
+        float v[CH / 64];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) {
+            v[i] = lg[r][lane + 64 * i];
+            mx = fmaxf(mx, v[i]);
+        }
+        mx = wave_max(mx);
+        const float muse = (mx == kNegInf) ? 0.f : mx;
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) z += exp2f(v[i] - muse);
+        z = wave_sum(z);
+        if (lane == 0) {
+            float *st = p.stat + (((int64_t)b * p.total_rows + row0 + r) * p.nchunk + chunk) * 2;
+            st[0] = mx;
+            st[1] = z;
+        }
+        if (p.logit) {
+            float *lp = p.logit + ((int64_t)b * p.total_rows + row0 + r) * p.N_max + j0;
+#pragma unroll
+            for (int i = 0; i < CH / 64; ++i) {
+                const int pos = lane + 64 * i;
+                if (j0 + pos < p.N_max) lp[pos] = v[i];
+            }
+        }
+    }
+}
+
+// Row log-sum-exp (log2 domain) from the per-chunk statistics.
+// One wave per row.
+__global__ __launch_bounds__(256) void rows_lse(const float *stat, float *lse, int nrows_total, int nchunk) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= nrows_total) return;
+    const float *st = stat + (int64_t)row * nchunk * 2;
+    float mx = kNegInf;
+    for (int c = lane; c < nchunk; c += 64) mx = fmaxf(mx, st[2 * c]);
+    mx = wave_max(mx);
+    const float muse = (mx == kNegInf) ? 0.f : mx;
+    float z = 0.f;
+    for (int c = lane; c < nchunk; c += 64) z += st[2 * c + 1] * exp2f(st[2 * c] - muse);
+    z = wave_sum(z);
+    if (lane == 0) lse[row] = (z > 0.f) ? muse + __log2f(z) : __builtin_huge_valf();
+}
+
+// S_Target[b][j] = sum_r exp2(logit[r][j] - lse[r]).
+__global__ __launch_bounds__(256) void target_finalize(const float *logit, const float *lse, float *out,
+                                                       const int32_t *seq_lens, int S, int N_max) {
+    const int b = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= N_max) return;
+    const int nb = min(max(seq_lens[b], 0), N_max);
+    float acc = 0.f;
+    if (j < nb) {
+        for (int r = 0; r < S; ++r)
+            acc += exp2f(logit[((int64_t)b * S + r) * N_max + j] - lse[(int64_t)b * S + r]);
+    }
+    out[(int64_t)b * N_max + j] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Draft side, float32 storage: VALU accumulation pass.  One work-group per
+// (sequence, chunk); loops over every unit in order.
+template <int D, int NV>
+struct DraftValuAccParams {
+    KvView kv[NV];
+    UnitTable ut;
+    const char *q;
+    int64_t q_bstride;
+    int32_t qoff[kMaxScoreQoff];
+    int32_t total_rows;
+    float scale_log2;
+    const float *lse;                // [B][total_rows]
+    float *out;                      // [B][N_max]
+    int32_t N_max;
+};
+
+template <int D, int NV>
+__global__ __launch_bounds__(256) void draft_acc_valu(DraftValuAccParams<D, NV> p) {
+    constexpr int LPI = D * 4 / 16;
+    constexpr int IPP = 256 / LPI;
+    __shared__ float qs[8][D];
+    __shared__ float ls[8];
+    __shared__ float acc[CH];
+    const int chunk = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int j0 = chunk * CH;
+    const int grp = tid / LPI, sl = tid - (tid / LPI) * LPI;
+    for (int i = tid; i < CH; i += 256) acc[i] = 0.f;
+    for (int u = 0; u < p.ut.n_units; ++u) {
+        const KvView &kv = p.kv[p.ut.view[u]];
+        const int kvh = p.ut.kvh[u], row0 = p.ut.row0[u], nr = p.ut.nrow[u];
+        const int nb = sl_len(kv, b);
+        __syncthreads();
+        for (int e = tid; e < nr * D; e += 256) {
+            const int r = e / D, d = e - (e / D) * D;
+            qs[r][d] = *(const float *)(p.q + ((int64_t)b * p.q_bstride + p.qoff[row0 + r] + d) * 4);
+        }
+        if (tid < nr) ls[tid] = p.lse[(int64_t)b * p.total_rows + row0 + tid];
+        __syncthreads();
+        for (int pos = grp; pos < CH; pos += IPP) {
+            const int j = j0 + pos;
+            const bool ok = j < nb;
+            float x[8];
+            load_slice<true>(ok ? krow(kv, b, j, kvh, 4) : nullptr, sl, x);
+            float tot = 0.f;
+            for (int r = 0; r < nr; ++r) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s += qs[r][sl * 4 + i] * x[i];
+#pragma unroll
+                for (int o = LPI / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+                tot += exp2f(s * p.scale_log2 - ls[r]);
+            }
+            if (sl == 0 && ok) acc[pos] += tot;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < CH; i += 256) {
+        const int j = j0 + i;
+        if (j < p.N_max) p.out[(int64_t)b * p.N_max + j] = acc[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Draft side, bfloat16 storage: MFMA passes.  For unit u = (layer l, draft KV
+// head c) the R = gamma * G_d rows are (step g, head c*G_d + hh), row index
+// g * G_d + hh.  S = Q . K^T per 16-token subtile with
+// v_mfma_f32_16x16x32_bf16: lane holds token (lane & 15) and rows
+// rb*16 + (lane >> 4)*4 + i.
+
+template <int D, int RB>
+struct DraftMfma {
+    static constexpr int KK = D / 32;
+
+    // Q operand fragments of unit (l, c): row rb*16 + (lane&15), d slice kk*32 + (lane>>4)*8.
+    static __device__ __forceinline__ void load_q(const DraftScoreArgs &a, int b, int l, int c, int lane,
+                                                  bf16x8 (&qf)[RB][KK]) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = rb * 16 + (lane & 15);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                if (r < a.rows) {
+                    const int gs = r / a.G_d, hh = r - (r / a.G_d) * a.G_d;
+                    const uint16_t *qp = (const uint16_t *)a.q_draft +
+                        ((((int64_t)b * a.L_d + l) * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + kk * 32 + (lane >> 4) * 8;
+                    qf[rb][kk] = *(const bf16x8 *)qp;
+                } else {
+                    for (int i = 0; i < 8; ++i) qf[rb][kk][i] = (__bf16)0.f;
+                }
+            }
+        }
+    }
+
+    // K^T operand fragments of 4 subtiles (64 positions from j_base).
+    static __device__ __forceinline__ void load_k(const KvView &kv, int b, int c, int j_base, int nb, int lane,
+                                                  bf16x8 (&kf)[4][KK]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int j = j_base + st * 16 + (lane & 15);
+            const char *row = (j < nb) ? krow(kv, b, j, c, 2) : nullptr;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                if (row) {
+                    kf[st][kk] = *(const bf16x8 *)(row + (kk * 32 + (lane >> 4) * 8) * 2);
+                } else {
+                    for (int i = 0; i < 8; ++i) kf[st][kk][i] = (__bf16)0.f;
+                }
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void logits(const bf16x8 (&qf)[RB][KK], const bf16x8 (&kf)[4][KK],
+                                                  f32x4 (&s)[4][RB]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf[st][kk], acc, 0, 0, 0);
+                s[st][rb] = acc;
+            }
+    }
+};
+
+template <int D, int RB>
+__global__ __launch_bounds__(256) void draft_stats_mfma(DraftScoreArgs a) {
+    using M = DraftMfma<D, RB>;
+    __shared__ float red[4][RB * 16][2];
+    const int chunk = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+    const int l = u / a.Hkv_d, c = u - (u / a.Hkv_d) * a.Hkv_d;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const KvView &kv = a.kv[l];
+    const int nb = sl_len(kv, b);
+    const int jb = chunk * CH + wave * 64;
+
+    bf16x8 qf[RB][M::KK];
+    bf16x8 kf[4][M::KK];
+    M::load_q(a, b, l, c, lane, qf);
+    M::load_k(kv, b, c, jb, nb, lane, kf);
+    f32x4 s[4][RB];
+    M::logits(qf, kf, s);
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bool ok = jb + st * 16 + (lane & 15) < nb;
+                const float v = ok ? s[st][rb][i] * a.scale_log2 : kNegInf;
+                s[st][rb][i] = v;
+                mx = fmaxf(mx, v);
+            }
+            mx = lane16_max(mx);
+            const float muse = (mx == kNegInf) ? 0.f : mx;
+            float z = 0.f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) z += exp2f(s[st][rb][i] - muse);
+            z = lane16_sum(z);
+            if ((lane & 15) == 0) {
+                const int r = rb * 16 + (lane >> 4) * 4 + i;
+                red[wave][r][0] = mx;
+                red[wave][r][1] = z;
+            }
+        }
+    __syncthreads();
+    if (threadIdx.x < a.rows) {
+        const int r = threadIdx.x;
+        float mx = kNegInf;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][r][0]);
+        const float muse = (mx == kNegInf) ? 0.f : mx;
+        float z = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) z += red[w][r][1] * exp2f(red[w][r][0] - muse);
+        float *st = a.stat + ((((int64_t)b * a.L_d * a.Hkv_d + u) * a.rows + r) * a.nchunk + chunk) * 2;
+        st[0] = mx;
+        st[1] = z;
+    }
+}
+
+template <int D, int RB>
+__global__ __launch_bounds__(256) void draft_acc_mfma(DraftScoreArgs a) {
+    using M = DraftMfma<D, RB>;
+    const int chunk = blockIdx.x, b = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int jb = chunk * CH + wave * 64;
+    const int U = a.L_d * a.Hkv_d;
+    const float *lse_b = a.lse + (int64_t)b * U * a.rows;
+
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 qf[RB][M::KK], qn[RB][M::KK];
+    bf16x8 kf[4][M::KK], kn[4][M::KK];
+    float lr[RB][4], ln[RB][4];
+
+    auto load_unit = [&](int u, bf16x8 (&q)[RB][M::KK], bf16x8 (&k)[4][M::KK], float (&ls)[RB][4]) {
+        const int l = u / a.Hkv_d, c = u - (u / a.Hkv_d) * a.Hkv_d;
+        const KvView &kv = a.kv[l];
+        M::load_q(a, b, l, c, lane, q);
+        M::load_k(kv, b, c, jb, sl_len(kv, b), lane, k);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rb * 16 + (lane >> 4) * 4 + i;
+                ls[rb][i] = (r < a.rows) ? lse_b[(int64_t)u * a.rows + r] : __builtin_huge_valf();
+            }
+    };
+
+    load_unit(0, qf, kf, lr);
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) load_unit(u + 1, qn, kn, ln);
+        const int l = u / a.Hkv_d;
+        const int nb = sl_len(a.kv[l], b);
+        f32x4 s[4][RB];
+        M::logits(qf, kf, s);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            float t = 0.f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t += exp2f(s[st][rb][i] * a.scale_log2 - lr[rb][i]);
+            if (jb + st * 16 + (lane & 15) < nb) acc[st] += t;
+        }
+        if (u + 1 < U) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int kk = 0; kk < M::KK; ++kk) qf[rb][kk] = qn[rb][kk];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int kk = 0; kk < M::KK; ++kk) kf[st][kk] = kn[st][kk];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lr[rb][i] = ln[rb][i];
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const float v = group4_sum(acc[st]);
+        const int j = jb + st * 16 + (lane & 15);
+        if (lane < 16 && j < a.kv[0].N_max) a.s_draft[(int64_t)b * a.kv[0].N_max + j] = v;
+    }
+}
+
+// --------------------------------------------------------------- host side
+ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int Hkv_d) {
+    ScorePlan p{};
+    p.nchunk = (N_max + CH - 1) / CH;
+    (void)Hkv_d;
+    const size_t drows = (size_t)L_d * gamma * H_d;   // rows over all draft (layer, KV head) units
+    size_t off = 0;
+    p.off_tlogit = off;
+    off = align_up(off + (size_t)B * S * N_max * sizeof(float), 256);
+    p.off_tstat = off;
+    off = align_up(off + (size_t)B * S * p.nchunk * 2 * sizeof(float), 256);
+    p.off_tlse = off;
+    off = align_up(off + (size_t)B * S * sizeof(float), 256);
+    p.off_dstat = off;
+    off = align_up(off + (size_t)B * drows * p.nchunk * 2 * sizeof(float), 256);
+    p.off_dlse = off;
+    off = align_up(off + (size_t)B * drows * sizeof(float), 256);
+    p.ws_bytes = off;
+    return p;
+}
+
+template <bool F32, int D, int NV>
+static hipError_t run_unit_stats(const ValuStatsParams<F32, D, NV> &p, int B, hipStream_t s) {
+    dim3 grid(p.nchunk, p.ut.n_units, B);
+    hipLaunchKernelGGL((unit_stats_valu<F32, D, NV>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool F32, int D>
+static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
+    ValuStatsParams<F32, D, 8> p{};
+    for (int i = 0; i < a.n_layers; ++i) p.kv[i] = a.kv[i];
+    const KvView &k0 = a.kv[0];
+    // one unit per (layer, kv head) with at most 8 rows, rows kept in order
+    UnitTable &ut = p.ut;
+    ut.n_units = 0;
+    for (int r = 0; r < a.S;) {
+        int n = 1;
+        while (r + n < a.S && n < 8 && a.row_layer[r + n] == a.row_layer[r] && a.row_kvh[r + n] == a.row_kvh[r]) ++n;
+        ut.view[ut.n_units] = a.row_layer[r];
+        ut.kvh[ut.n_units] = a.row_kvh[r];
+        ut.row0[ut.n_units] = r;
+        ut.nrow[ut.n_units] = n;
+        ++ut.n_units;
+        r += n;
+    }
+    p.q = (const char *)a.q_hist;
+    p.q_bstride = (int64_t)a.S * D;
+    for (int r = 0; r < a.S; ++r) p.qoff[r] = r * D;
+    p.total_rows = a.S;
+    p.scale_log2 = a.scale_log2;
+    p.stat = a.stat;
+    p.logit = a.logit;
+    p.nchunk = a.nchunk;
+    p.N_max = k0.N_max;
+    hipError_t e = run_unit_stats(p, k0.B, s);
+    if (e != hipSuccess) return e;
+    float *lse = a.lse;
+    hipLaunchKernelGGL(rows_lse, dim3((k0.B * a.S + 3) / 4), dim3(256), 0, s, a.stat, lse, k0.B * a.S, a.nchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(target_finalize, dim3((k0.N_max + 255) / 256, k0.B), dim3(256), 0, s, a.logit, lse,
+                       a.s_target, k0.seq_lens, a.S, k0.N_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_target_score(const TargetScoreArgs &a, hipStream_t s) {
+    const KvView &k0 = a.kv[0];
+    if (k0.f32) {
+        switch (k0.D) {
+            case 32: return target_impl<true, 32>(a, s);
+            case 64: return target_impl<true, 64>(a, s);
+            case 128: return target_impl<true, 128>(a, s);
+        }
+    } else {
+        switch (k0.D) {
+            case 32: return target_impl<false, 32>(a, s);
+            case 64: return target_impl<false, 64>(a, s);
+            case 128: return target_impl<false, 128>(a, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
+    // float32 drafts are small (tests, tiny configs): at most 8 layers, and
+    // units of <= 8 rows.
+    const KvView &k0 = a.kv[0];
+    if (a.L_d > 8) return hipErrorInvalidValue;
+    ValuStatsParams<true, D, 8> p{};
+    for (int i = 0; i < a.L_d; ++i) p.kv[i] = a.kv[i];
+    UnitTable &ut = p.ut;
+    ut.n_units = 0;
+    int row = 0;
+    for (int l = 0; l < a.L_d; ++l)
+        for (int c = 0; c < a.Hkv_d; ++c)
+            for (int r0 = 0; r0 < a.rows; r0 += 8) {
+                if (ut.n_units >= kMaxScoreRows) return hipErrorInvalidValue;
+                const int n = (a.rows - r0 < 8) ? a.rows - r0 : 8;
+                ut.view[ut.n_units] = l;
+                ut.kvh[ut.n_units] = c;
+                ut.row0[ut.n_units] = row;
+                ut.nrow[ut.n_units] = n;
+                for (int i = 0; i < n; ++i) {
+                    const int r = r0 + i, gs = r / a.G_d, hh = r - (r / a.G_d) * a.G_d;
+                    if (row + i >= kMaxScoreQoff) return hipErrorInvalidValue;
+                    p.qoff[row + i] = ((l * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D;
+                }
+                row += n;
+                ++ut.n_units;
+            }
+    p.q = (const char *)a.q_draft;
+    p.q_bstride = (int64_t)a.L_d * a.gamma * a.H_d * D;
+    p.total_rows = row;
+    p.scale_log2 = a.scale_log2;
+    p.stat = a.stat;
+    p.logit = nullptr;
+    p.nchunk = a.nchunk;
+    p.N_max = k0.N_max;
+    hipError_t e = run_unit_stats(p, k0.B, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rows_lse, dim3((k0.B * row + 3) / 4), dim3(256), 0, s, a.stat, a.lse, k0.B * row, a.nchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    DraftValuAccParams<D, 8> q{};
+    for (int i = 0; i < a.L_d; ++i) q.kv[i] = a.kv[i];
+    q.ut = ut;
+    q.q = p.q;
+    q.q_bstride = p.q_bstride;
+    for (int i = 0; i < row; ++i) q.qoff[i] = p.qoff[i];
+    q.total_rows = row;
+    q.scale_log2 = a.scale_log2;
+    q.lse = a.lse;
+    q.out = a.s_draft;
+    q.N_max = k0.N_max;
+    hipLaunchKernelGGL((draft_acc_valu<D, 8>), dim3(a.nchunk, k0.B), dim3(256), 0, s, q);
+    return hipGetLastError();
+}
+
+template <int D, int RB>
+static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
+    const KvView &k0 = a.kv[0];
+    const int U = a.L_d * a.Hkv_d;
+    hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(a.nchunk, U, k0.B), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nrows = k0.B * U * a.rows;
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, a.stat, a.lse, nrows, a.nchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((draft_acc_mfma<D, RB>), dim3(a.nchunk, k0.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s) {
+    const KvView &k0 = a.kv[0];
+    if (k0.f32) {
+        switch (k0.D) {
+            case 32: return draft_f32_impl<32>(a, s);
+            case 64: return draft_f32_impl<64>(a, s);
+            case 128: return draft_f32_impl<128>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    const int RB = (a.rows + 15) / 16;
+#define DUSTIN_DRAFT_CASE(DD)                                  \
+    switch (RB) {                                              \
+        case 1: return draft_bf16_impl<DD, 1>(a, s);           \
+        case 2: return draft_bf16_impl<DD, 2>(a, s);           \
+        case 3: return draft_bf16_impl<DD, 3>(a, s);           \
+        case 4: return draft_bf16_impl<DD, 4>(a, s);           \
+    }                                                          \
+    return hipErrorInvalidValue;
+    switch (k0.D) {
+        case 32: DUSTIN_DRAFT_CASE(32)
+        case 64: DUSTIN_DRAFT_CASE(64)
+        case 128: DUSTIN_DRAFT_CASE(128)
+    }
+#undef DUSTIN_DRAFT_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dustin

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dustin.h declares, and rejects bad arguments on the host before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_kv_verification_amd as dk
+from sparse_kv_verification_amd._lib import DustinKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, HIPERR = 1, 2, 3
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dustin.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dustin_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return dk.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert set(names) == set(dk.EXPORTS)
+
+
+def test_version_and_strings(L):
+    assert L.dustin_abi_version() == 1
+    assert L.dustin_status_string(0) == b"DUSTIN_OK"
+    assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
+
+
+def kv(**kw):
+    d = dict(k=FAKE, v=FAKE, dtype=1, B=2, H_kv=8, head_dim=128, N_max=4096, seq_lens=FAKE,
+             page_size=0, page_table=None, max_pages=0, num_pages=0)
+    d.update(kw)
+    return DustinKV(**d)
+
+
+def attn(L, desc, q=FAKE, w=4, Hq=64, idx=FAKE, count=FAKE, k=2048, ws=FAKE, ws_bytes=1 << 40, scale=0.0, out=FAKE):
+    return L.dustin_sparse_verify_attn(q, w, Hq, ctypes.byref(desc), idx, count, k, scale, out, None, ws, ws_bytes, None)
+
+
+def test_attention_argument_errors(L):
+    assert attn(L, kv(k=None)) == INVALID
+    assert attn(L, kv(v=None)) == INVALID
+    assert attn(L, kv(), q=None) == INVALID
+    assert attn(L, kv(), out=None) == INVALID
+    assert attn(L, kv(dtype=7)) == UNSUPPORTED
+    assert attn(L, kv(head_dim=96)) == UNSUPPORTED
+    assert attn(L, kv(dtype=1, head_dim=32)) == UNSUPPORTED          # bf16 MFMA path needs 64/128
+    assert attn(L, kv(), Hq=60) == INVALID                            # not a multiple of H_kv
+    assert attn(L, kv(), w=9) == UNSUPPORTED                          # w * G = 72 > 64
+    assert attn(L, kv(), k=0) == INVALID
+    assert attn(L, kv(), count=None) == INVALID
+    assert attn(L, kv(), idx=None, k=5) == INVALID                    # dense form takes k = 0
+    assert attn(L, kv(seq_lens=None)) == INVALID
+    assert attn(L, kv(page_size=8)) == UNSUPPORTED
+    assert attn(L, kv(page_size=16, page_table=None, max_pages=256, num_pages=10)) == INVALID
+    assert attn(L, kv(page_size=16, page_table=FAKE, max_pages=10, num_pages=10)) == INVALID
+    assert attn(L, kv(), scale=float("nan")) == INVALID
+    need = L.dustin_attn_workspace_bytes(2, 4, 64, 8, 128, 2048)
+    assert need > 0
+    assert attn(L, kv(), ws_bytes=need - 1) == INVALID
+    assert attn(L, kv(), ws=None) == INVALID
+    assert b"workspace" in L.dustin_last_error()
+
+
+def test_topk_argument_errors(L):
+    f = lambda **kw: L.dustin_topk(kw.get("sd", FAKE), kw.get("st", FAKE), kw.get("lens", FAKE), kw.get("B", 2),
+                                   kw.get("N", 1000), kw.get("k", 64), kw.get("m", 10), kw.get("ns", 4),
+                                   kw.get("nw", 8), kw.get("idx", FAKE), kw.get("cnt", FAKE), None, FAKE,
+                                   kw.get("ws", 1 << 30), None)
+    assert f(sd=None, st=None) == INVALID
+    assert f(k=0) == INVALID
+    assert f(m=-1) == INVALID
+    assert f(ns=40, nw=40) == INVALID           # protected tokens exceed k
+    assert f(idx=None) == INVALID
+    assert f(lens=None) == INVALID
+    assert f(ws=L.dustin_topk_workspace_bytes(2, 1000, 64) - 1) == INVALID
+
+
+def test_score_argument_errors(L):
+    d = (DustinKV * 2)(kv(H_kv=2, head_dim=64), kv(H_kv=2, head_dim=64))
+    t = (DustinKV * 1)(kv())
+    heads = (ctypes.c_int32 * 4)(0, 0, 0, 8)
+    def f(**kw):
+        return L.dustin_score(kw.get("d", d), kw.get("L_d", 2), kw.get("qd", FAKE), kw.get("H_d", 14),
+                              kw.get("gamma", 4), kw.get("t", t), kw.get("L_t", 1), kw.get("qh", FAKE),
+                              kw.get("heads", heads), kw.get("S", 2), kw.get("H_t", 64), 0.0, 0.0,
+                              kw.get("sd", FAKE), kw.get("st", FAKE), FAKE, kw.get("ws", 1 << 40), None)
+    assert f(qd=None) == INVALID
+    assert f(H_d=13) == INVALID                                   # not a multiple of draft H_kv
+    assert f(gamma=20) == UNSUPPORTED                             # gamma * G_d = 140 > 64
+    bad = (DustinKV * 2)(kv(H_kv=2, head_dim=64), kv(H_kv=2, head_dim=128))
+    assert f(d=bad) == INVALID                                    # layers differ in geometry
+    assert f(heads=(ctypes.c_int32 * 4)(0, 0, 1, 8)) == INVALID   # layer out of range
+    assert f(heads=(ctypes.c_int32 * 4)(0, 0, 0, 64)) == INVALID  # head out of range
+    assert f(H_t=60) == INVALID                                   # H_t not a multiple of H_kv
+    assert f(qh=None) == INVALID
+    assert f(S=65, heads=(ctypes.c_int32 * 130)()) == UNSUPPORTED
+    assert f(ws=10) == INVALID
+    # nothing requested: a no-op that succeeds without touching the GPU
+    assert f(sd=None, st=None) == 0
+
+
+def test_arr_and_window_argument_errors(L):
+    assert L.dustin_arr(None, FAKE, 2, 4, 100, FAKE, FAKE, 8, FAKE, FAKE, None) == INVALID
+    assert L.dustin_arr(FAKE, FAKE, 2, 65, 100, FAKE, FAKE, 8, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.dustin_arr(FAKE, FAKE, 2, 4, 100, FAKE, FAKE, 0, FAKE, FAKE, None) == INVALID
+    desc = kv()
+    assert L.dustin_window_attn(FAKE, 17, 8, ctypes.byref(desc), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, None, FAKE, 1 << 40, None) == INVALID
+    assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, FAKE, FAKE, 16, None) == INVALID
+
+
+def test_workspace_sizes_are_shape_only(L):
+    # c4 shapes: the attention plan merges partials from several splits
+    a = L.dustin_attn_workspace_bytes(16, 4, 64, 8, 128, 2048)
+    b = L.dustin_attn_workspace_bytes(16, 4, 64, 8, 128, 32768)
+    assert 0 < a < b
+    assert L.dustin_attn_workspace_bytes(0, 4, 64, 8, 128, 2048) == 0
+    assert L.dustin_score_workspace_bytes(16, 32768, 24, 14, 4, 8) > 16 * 8 * 32768 * 4
+    assert L.dustin_topk_workspace_bytes(16, 32768, 2048) >= 16 * 32768
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_valid_call_without_device_reports_hip_error(L):
+    # Validation passes; the first HIP call then fails because there is no device.
+    desc = kv()
+    st = attn(L, desc)
+    assert st == HIPERR
+    assert L.dustin_last_error() != b""
