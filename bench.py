@@ -1,0 +1,294 @@
+"""Benchmark of the sparse-verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  dustin_score (draft + target-subset scoring)
+  -> dustin_topk (global verification set per sequence)
+  -> L x dustin_sparse_verify_attn (one call per target layer, each layer its
+     own K/V buffers, the same index set).
+Default workload: Qwen2.5-72B-shaped target (64 query / 8 KV heads, head_dim
+128, 80 layers), 0.5B-shaped draft (24 layers x 14 heads, 2 KV heads,
+head_dim 64), batch 16, context 32768, w = Gamma = 4, k = 2048, bf16.
+
+Prints ONE JSON line (rank 0).  `value` is microseconds per step (lower is
+better), timed with HIP events around K steps replayed from a HIP graph
+(eager timing reported alongside).  The dominant kernel (the gathered
+attention) is also timed per launch with HIP events on its stream, and the
+whole step is related to the 8 TB/s HBM peak through its algorithmic bytes.
+The CPU oracle is timed on a bounded sample (whole step for one sequence
+with one attention layer) and scaled to a full step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="c4")
+    p.add_argument("--k", type=int, default=None)
+    p.add_argument("--layers", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_bytes(sh, x, k_eff, counts, sub_heads):
+    """Bytes the method must move (no second passes, no partials)."""
+    import torch
+    esz = 4 if sh.dtype == "f32" else 2
+    n_tot = int(x.seq_lens.sum())
+    U = len({(l, h // sh.G) for (l, h) in sub_heads})
+    draft = sh.L_d * n_tot * sh.Hkv_d * sh.d_d * esz + x.q_draft.numel() * esz
+    target = n_tot * U * sh.d * esz + x.q_hist.numel() * esz
+    scores_out = 2 * sh.B * sh.n * 4
+    select = 2 * sh.B * sh.n * 4 + sh.B * k_eff * (4 + 1) + sh.B * 4
+    sel_rows = int(counts.sum())
+    per_layer = sel_rows * sh.Hkv * sh.d * esz * 2 + 2 * x.q.numel() * esz + sh.B * k_eff * 4 + sh.B * 4
+    return {
+        "score": draft + target + scores_out,
+        "select": select,
+        "attn_per_layer": per_layer,
+        "step": draft + target + scores_out + select + sh.layers * per_layer,
+        "dense_per_layer": n_tot * sh.Hkv * sh.d * esz * 2 + 2 * x.q.numel() * esz,
+    }
+
+
+def cpu_baseline(sh, x, k, m, n_sink, n_window):
+    """Time the oracle (as it stands) on one sequence: scoring, selection and
+    one attention layer, then scale to a full step (B sequences, all layers)."""
+    import numpy as np
+    import oracle
+    f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    b = 0
+    n = int(x.seq_lens[b])
+    K, V = f(x.logical("K", b)), f(x.logical("V", b))
+    Kd = f(x.logical("Kd", b))
+    qd, qh, q = f(x.q_draft[b]), f(x.q_hist[b]), f(x.q[b])
+    t0 = time.perf_counter()
+    sd = oracle.score_draft(qd, Kd)
+    st = oracle.score_target(qh, {0: K}, x.sub_heads, sh.Hq)
+    t1 = time.perf_counter()
+    I, _ = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
+    t2 = time.perf_counter()
+    oracle.sparse_attention(q, K, V, I)
+    t3 = time.perf_counter()
+    per_seq = (t1 - t0) + (t2 - t1) + sh.layers * (t3 - t2)
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    return {
+        "value": per_seq * sh.B * 1e6,
+        "unit": "us/step",
+        "cores": int(threads or 1),
+        "kind": "oracle",
+        "sample": (f"sequence 0 of {sh.B} (n={n}): score_draft + score_target + select + 1 of {sh.layers} "
+                   f"attention layers, fp64 NumPy; scaled x{sh.B} sequences and x{sh.layers} layers"),
+        "measured_s": {"score": t1 - t0, "select": t2 - t1, "attn_1_layer": t3 - t2},
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpu_count": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    over = {}
+    if args.k:
+        over["k"] = args.k
+    if args.layers:
+        over["layers"] = args.layers
+    sh = synth.preset(args.config).replace(**over)
+    k = sh.k
+    n_sink, n_window, m = synth.tier_defaults(k)
+    log(f"config {sh.name} B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d} w={sh.w} k={k} "
+        f"layers={sh.layers} draft {sh.L_d}x{sh.H_d} (kv {sh.Hkv_d}, d {sh.d_d}); m={m} sink={n_sink} window={n_window}")
+    t = time.time()
+    x = synth.make(sh, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated in {time.time() - t:.1f}s")
+
+    # per-layer K/V buffers: layer 0 is the generated cache, the others are
+    # copies in distinct allocations (so no layer is served from cache)
+    Ks, Vs = [x.K], [x.V]
+    for _ in range(1, sh.layers):
+        Ks.append(x.K.clone())
+        Vs.append(x.V.clone())
+    torch.cuda.synchronize()
+    log(f"{sh.layers} layers resident ({sh.layers * 2 * x.K.numel() * x.K.element_size() / 1e9:.1f} GB)")
+    kvs = [dk.KV(Ks[l], Vs[l], x.seq_lens, x.page_table) for l in range(sh.layers)]
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
+    s_d = torch.empty((sh.B, sh.n), dtype=torch.float32, device=dev)
+    s_t = torch.empty_like(s_d)
+    idx = torch.empty((sh.B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((sh.B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(x.q)
+    ws_s, ws_k, ws_a = dk.Workspace(), dk.Workspace(), dk.Workspace()
+
+    def score():
+        dk.dustin_score(dkv, x.q_draft, [kvs[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
+
+    def select():
+        dk.dustin_topk(s_d, s_t, x.seq_lens, k, m, n_sink, n_window, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+
+    def attn(l):
+        dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=out, ws=ws_a)
+
+    def step():
+        score()
+        select()
+        for l in range(sh.layers):
+            attn(l)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    bytes_ = algorithmic_bytes(sh, x, k, cnt, x.sub_heads)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3   # us
+
+    eager_us = timed(step, args.steps)
+    log(f"eager step {eager_us:.1f} us")
+
+    graph_us = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()                       # warm the capture stream's workspaces
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_us = timed(g.replay, args.steps)
+        log(f"graph step {graph_us:.1f} us")
+    step_us = graph_us if graph_us is not None else eager_us
+
+    # component timings (eager, events on the launch stream)
+    score_us = timed(score, args.steps)
+    select_us = timed(select, args.steps)
+    # dominant kernel: one event pair around every attention launch
+    durs = []
+    for _ in range(args.steps):
+        for l in range(sh.layers):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            attn(l)
+            e1.record(stream)
+            durs.append((e0, e1))
+    torch.cuda.synchronize()
+    attn_launch_us = sum(a.elapsed_time(b) for a, b in durs) / len(durs) * 1e3
+    attn_loop_us = timed(lambda: [attn(l) for l in range(sh.layers)], args.steps) / sh.layers
+    log(f"score {score_us:.1f} us, select {select_us:.1f} us, attention {attn_launch_us:.2f} us/launch "
+        f"({attn_loop_us:.2f} us/layer in a loop)")
+
+    dense = None
+    if not args.no_dense:
+        dout = torch.empty_like(x.q)
+        ws_d = dk.Workspace()
+        def dense_layers():
+            for l in range(sh.layers):
+                dk.dustin_sparse_verify_attn(x.q, kvs[l], None, None, out=dout, ws=ws_d)
+        dense_layers()
+        dense_us = timed(dense_layers, 2)
+        dense = {
+            "us_per_step_attention": dense_us,
+            "GBps": bytes_["dense_per_layer"] * sh.layers / dense_us / 1e3,
+            "speedup_sparse_step_vs_dense_attention": dense_us / step_us,
+        }
+        dense["frac"] = dense["GBps"] / HBM_PEAK_GBPS
+        log(f"dense attention {dense_us:.1f} us/step ({dense['GBps']:.0f} GB/s), "
+            f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster")
+
+    step_gbps = bytes_["step"] / step_us / 1e3
+    attn_gbps = bytes_["attn_per_layer"] / attn_launch_us / 1e3
+    res = {
+        "metric": "sparse-verify us/step + HBM GB/s (% roofline), 32k ctx, b=16, k=2048, w=4",
+        "value": round(step_us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded heavy-hitter Gaussian K/V/Q, projected draft)",
+        "config": {
+            "workload": f"{sh.name}: B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d} w={sh.w} k={k} "
+                        f"layers={sh.layers} draft={sh.L_d}x{sh.H_d}/{sh.Hkv_d}x{sh.d_d}",
+            "global_batch": sh.B, "seq_len": sh.n, "k": k, "m": m, "n_sink": n_sink, "n_window": n_window,
+            "scored_target_heads": len(x.sub_heads), "parallelism": "single-gpu",
+        },
+        "step_GBps": round(step_gbps, 1),
+        "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": bytes_["step"],
+        "eager_us_per_step": round(eager_us, 2),
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "components_us": {"score": round(score_us, 2), "select": round(select_us, 2),
+                          "attention_per_layer": round(attn_launch_us, 3),
+                          "attention_per_layer_in_loop": round(attn_loop_us, 3)},
+        "roofline": {
+            "kernel": "attn_bf16_kernel (dustin_sparse_verify_attn)",
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": bytes_["attn_per_layer"],
+        },
+        "dense_baseline": dense,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,67 +63,167 @@ __device__ __forceinline__ int seq_len(const KvView &kv, int b) {
     return min(max(kv.seq_lens[b], 0), kv.N_max);
 }
 
-// Merge the split partials of (b, g) and write the output rows.  Executed by
-// one wave (64 lanes).
-template <bool F32OUT, int D>
-__device__ void merge_splits(const AttnArgs &a, int bg, int b, int g, int lane) {
+// Merge the split partials of (b, g) and write the output rows, using NT
+// threads.  Each thread owns one (row, eighth of d) slice and folds the
+// splits in with a running maximum, so every load is independent of the
+// arithmetic and the merge costs about one memory round trip.
+template <bool F32OUT, int D, int NT>
+__device__ void merge_splits(const AttnArgs &a, int bg, int b, int g, int tid) {
+    constexpr int PART = D / 8;    // floats per (row, part) slice
+    constexpr int NC = PART / 4;   // float4 chunks per slice
+    // The partials were stored write-through (st_agent) before their
+    // writers' arrivals; read them back device-coherently.
     const size_t pb = (size_t)bg * a.splits * a.rpad;
-    for (int r = 0; r < a.R; ++r) {
-        float mx = kNegInf;
-        for (int s = lane; s < a.splits; s += 64) mx = fmaxf(mx, a.part_m[pb + (size_t)s * a.rpad + r]);
-        mx = wave_max(mx);
-        const float muse = (mx == kNegInf) ? 0.f : mx;
-        float L = 0.f;
-        for (int s = lane; s < a.splits; s += 64) {
-            const size_t o = pb + (size_t)s * a.rpad + r;
-            L += a.part_l[o] * exp2f(a.part_m[o] - muse);
+    const uint32_t nml = (uint32_t)(a.splits * a.rpad * sizeof(float));
+    const __amdgpu_buffer_rsrc_t pm = coherent_rsrc(a.part_m + pb, nml);
+    const __amdgpu_buffer_rsrc_t pl = coherent_rsrc(a.part_l + pb, nml);
+    const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, nml * D);
+    for (int e = tid; e < a.R * 8; e += NT) {
+        const int r = e >> 3, h = e & 7;
+        float M = kNegInf, L = 0.f;
+        f32x4 acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int s = 0; s < a.splits; ++s) {
+            const uint32_t o = (uint32_t)(s * a.rpad + r);
+            const float ms = ld_coherent(pm, o * 4u), ls = ld_coherent(pl, o * 4u);
+            f32x4 v[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) v[c] = ld_coherent4(po, (o * D + h * PART + 4 * c) * 4u);
+            const float Mn = fmaxf(M, ms);
+            const float mu = (Mn == kNegInf) ? 0.f : Mn;
+            const float so = exp2f(M - mu), sn = exp2f(ms - mu);
+            L = L * so + ls * sn;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] = acc[c] * so + v[c] * sn;
+            M = Mn;
         }
-        L = wave_sum(L);
         const float inv = (L > 0.f) ? 1.f / L : 0.f;
-        const int sq = r / a.G, gh = r - sq * a.G;
-        const size_t orow = (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D;
-        for (int d = lane * 2; d < D; d += 128) {
-            float acc0 = 0.f, acc1 = 0.f;
-            for (int s = 0; s < a.splits; ++s) {
-                const size_t o = pb + (size_t)s * a.rpad + r;
-                const float ws = exp2f(a.part_m[o] - muse);
-                const float *po = a.part_o + o * D + d;
-                acc0 += ws * po[0];
-                acc1 += ws * po[1];
-            }
-            acc0 *= inv;
-            acc1 *= inv;
+        const int sq = r / a.G, gh = r - (r / a.G) * a.G;
+        const size_t hrow = ((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh;
+        const size_t orow = hrow * D + h * PART;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const f32x4 v = acc[c] * inv;
             if constexpr (F32OUT) {
-                float *op = (float *)a.out + orow + d;
-                op[0] = acc0;
-                op[1] = acc1;
+                *(f32x4 *)((float *)a.out + orow + 4 * c) = v;
             } else {
-                uint32_t packed = f32_to_bf16_bits(acc0) | ((uint32_t)f32_to_bf16_bits(acc1) << 16);
-                *(uint32_t *)((uint16_t *)a.out + orow + d) = packed;
+                uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+                uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+                uint32_t *op = (uint32_t *)((uint16_t *)a.out + orow + 4 * c);
+                op[0] = lo;
+                op[1] = hi;
             }
         }
-        if (a.lse && lane == 0) {
-            a.lse[((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh] =
-                (L > 0.f) ? (mx + __log2f(L)) * kLn2 : kNegInf;
-        }
+        if (a.lse && h == 0) a.lse[hrow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
     }
 }
 
-// Arrival on the (b, g) counter after this work-group's partial is stored.
-// Returns true for the last of the a.splits arrivals.
+// Merge for the MFMA kernel, whose split partials are stored in register
+// order: per split, float4 element (rb, dt, lane) holds row rb*16 + (lane&15),
+// d = dt*16 + 4*(lane>>4) .. +3, so every publishing store is a contiguous
+// 1 KiB per wave.  Same single-pass fold as merge_splits.
+template <int D, int RB, int NT>
+__device__ void merge_splits_reg(const AttnArgs &a, int bg, int b, int g, int tid) {
+    constexpr int DT = D / 16;
+    constexpr int NE = RB * DT * 64 / NT;   // float4 elements per thread
+    static_assert(NE * NT == RB * DT * 64, "merge geometry");
+    const size_t pb = (size_t)bg * a.splits * a.rpad;
+    const uint32_t nml = (uint32_t)(a.splits * a.rpad * sizeof(float));
+    const __amdgpu_buffer_rsrc_t pm = coherent_rsrc(a.part_m + pb, nml);
+    const __amdgpu_buffer_rsrc_t pl = coherent_rsrc(a.part_l + pb, nml);
+    const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, nml * D);
+    uint16_t *__restrict__ outp = (uint16_t *)a.out;
+    float M[NE], L[NE];
+    f32x4 acc[NE];
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        M[k] = kNegInf;
+        L[k] = 0.f;
+        acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // software pipeline: split s + 1 is loaded while split s is folded in
+    float ms[2][NE], ls[2][NE];
+    f32x4 v[2][NE];
+    auto load = [&](int s, int slot) {
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int e = tid + k * NT;
+            const int r = (e / (DT * 64)) * 16 + (e & 15);
+            const uint32_t o = (uint32_t)(s * a.rpad + r) * 4u;
+            ms[slot][k] = ld_coherent(pm, o);
+            ls[slot][k] = ld_coherent(pl, o);
+            v[slot][k] = ld_coherent4(po, ((uint32_t)(s * a.rpad * D) + (uint32_t)e * 4u) * 4u);
+        }
+    };
+    auto fold = [&](int slot) {
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const float Mn = fmaxf(M[k], ms[slot][k]);
+            const float mu = (Mn == kNegInf) ? 0.f : Mn;
+            const float so = __builtin_amdgcn_exp2f(M[k] - mu), sn = __builtin_amdgcn_exp2f(ms[slot][k] - mu);
+            L[k] = L[k] * so + ls[slot][k] * sn;
+            acc[k] = acc[k] * so + v[slot][k] * sn;
+            M[k] = Mn;
+        }
+    };
+    load(0, 0);
+    int s = 0;
+    for (; s + 2 <= a.splits; s += 2) {
+        load(s + 1, 1);
+        fold(0);
+        if (s + 2 < a.splits) load(s + 2, 0);
+        fold(1);
+    }
+    if (s < a.splits) fold(0);
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int e = tid + k * NT;
+        const int i = (e / 64) % DT, ln = e & 63;
+        const int r = (e / (DT * 64)) * 16 + (ln & 15);
+        if (r >= a.R) continue;
+        const float inv = (L[k] > 0.f) ? 1.f / L[k] : 0.f;
+        const int sq = r / a.G, gh = r - (r / a.G) * a.G;
+        const size_t hrow = ((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh;
+        const f32x4 o = acc[k] * inv;
+        uint32_t lo = f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+        uint32_t hi = f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+        uint32_t *op = (uint32_t *)(outp + hrow * D + i * 16 + (ln >> 4) * 4);
+        op[0] = lo;
+        op[1] = hi;
+        if (a.lse && i == 0 && ln < 16) a.lse[hrow] = (L[k] > 0.f) ? (M[k] + __log2f(L[k])) * kLn2 : kNegInf;
+    }
+}
+
+// Split partials are exchanged through device-coherent stores and loads
+// (st_agent / ld_agent): a work-group stores its partial, waits for the
+// stores to complete, and only then bumps the (b, g) arrival counter; the
+// last of the a.splits arrivals merges.  Single-wave variant.
 __device__ __forceinline__ bool arrive_last(const AttnArgs &a, int bg, int lane) {
-    __threadfence();
+    wait_all_mem();
     int prev = 0;
-    if (lane == 0) prev = atomicAdd(&a.counters[bg], 1);
+    if (lane == 0) prev = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0, 64);
-    if (prev != a.splits - 1) return false;
-    __threadfence();
-    return true;
+    return prev == a.splits - 1;
 }
 
 // --------------------------------------------------------------- bf16 / MFMA
+// Four waves share one LDS ring of NBUF 32-token tiles.  Wave w owns row
+// block w % RB (16 query rows) and, of every tile, the 16-token subtiles
+// s = w / RB (mod NTH) with NTH = 4 / RB: each wave keeps its own running
+// softmax state over its share of the tokens, so no score or exponential is
+// computed twice; the shares of one row block are merged through LDS at the
+// end.  Each wave issues a quarter of every tile's DMA, and one barrier per
+// tile both publishes the tile and frees the buffer the next DMA overwrites.
+//
+// Per 16-token subtile and row block:
+//   S^T = K_sub . Q^T         4 (D = 128) x v_mfma_f32_16x16x32_bf16
+//   P   = exp2(S^T - m)       lane holds row (lane & 15), tokens 4*(lane>>4)+j
+//   O^T += V_sub^T . P^T      D/16 x v_mfma_f32_16x16x16_bf16; the V operand
+//                             comes from one transposed LDS read per d tile.
 template <int D, int RB, int NBUF>
-__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(AttnArgs a) {
     constexpr int T = kAttnTile;
     constexpr int ROWB = D * 2;       // bytes of one head row
     constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -132,12 +232,20 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     constexpr int TB = T * ROWB;      // bytes of one K tile
     constexpr int KK = D / 32;        // k-steps of the QK^T MFMA
     constexpr int DT = D / 16;        // 16-wide d tiles of the PV MFMA
-    static_assert(NI * 1024 == TB, "tile / DMA geometry");
+    constexpr int NW = 4;             // waves per work-group
+    constexpr int NTH = NW / RB;      // token shares per row block
+    constexpr int NIW = NI / NW;      // DMA instructions per wave per K (or V) tile
+    static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
+    static_assert(NI * 1024 == TB && NIW >= 1 && NIW * NW == NI, "tile / DMA geometry");
+    static_assert(NBUF * 2 * TB >= NW * 16 * D * 4, "LDS ring reused for the share merge");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sm[NBUF][2][TB];
-    __shared__ int rows[kAttnMaxTps];
+    __shared__ float share_ml[NW][16][2];
+    __shared__ int s_flag;
+    extern __shared__ int rows[];   // [a.tps] physical rows, sized at launch
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rbw = wave % RB, th = wave / RB;
     const int split = blockIdx.x % a.splits;
     const int bg = blockIdx.x / a.splits;
     const int b = bg / a.kv.Hkv, g = bg - (bg / a.kv.Hkv) * a.kv.Hkv;
@@ -147,39 +255,51 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     const int t0 = split * a.tps;
     const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
 
-    for (int t = lane; t < ntok; t += 64) {
-        const int j = a.idx ? a.idx[(int64_t)b * a.k + t0 + t] : t0 + t;
-        rows[t] = (j >= 0 && j < nb) ? phys_row(a.kv, b, j) : -1;
+    if (tid == 0) s_flag = 0;
+    // Q^T operand fragments of this wave's row block: lane holds row
+    // rbw*16 + (lane & 15), d slice kk*32 + (lane >> 4) * 8.  Issued first so
+    // they overlap the index loads below.
+    const int qrow = rbw * 16 + (lane & 15);
+    bf16x8 qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        if (qrow < a.R) {
+            const int sq = qrow / a.G, gh = qrow - (qrow / a.G) * a.G;
+            const uint16_t *qp = (const uint16_t *)a.q +
+                (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D + kk * 32 + (lane >> 4) * 8;
+            qf[kk] = *(const bf16x8 *)qp;
+        } else {
+            for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.f;
+        }
     }
     __syncthreads();
-
-    // Q^T operand fragments: lane holds row (lane & 15), d slice (lane >> 4) * 8.
-    bf16x8 qf[RB][KK];
+    bool any_bad = false;
+    {   // physical row of every token of the split; all loads issued first
+        constexpr int PER = kAttnMaxTps / 256;
+        int jv[PER];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r = rb * 16 + (lane & 15);
+        for (int i = 0; i < PER; ++i) {
+            const int t = tid + 256 * i;
+            jv[i] = (t < ntok) ? (a.idx ? a.idx[(int64_t)b * a.k + t0 + t] : t0 + t) : -1;
+        }
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (r < a.R) {
-                const int sq = r / a.G, gh = r - (r / a.G) * a.G;
-                const uint16_t *qp = (const uint16_t *)a.q +
-                    (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D + kk * 32 + (lane >> 4) * 8;
-                qf[rb][kk] = *(const bf16x8 *)qp;
-            } else {
-                for (int i = 0; i < 8; ++i) qf[rb][kk][i] = (__bf16)0.f;
+        for (int i = 0; i < PER; ++i) {
+            const int t = tid + 256 * i;
+            if (t < ntok) {
+                const int r = (jv[i] >= 0 && jv[i] < nb) ? phys_row(a.kv, b, jv[i]) : -1;
+                rows[t] = r;
+                any_bad |= (r < 0);
             }
         }
     }
+    if (any_bad) s_flag = 1;
+    __syncthreads();
+    const bool all_rows_valid = (s_flag == 0);
 
-    f32x4 o[RB][DT];
-    float mrow[RB], lsum[RB];
+    f32x4 o[DT];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        mrow[rb] = kNegInf;
-        lsum[rb] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrow = kNegInf, lsum = 0.f;
 
     const char *kbase = a.kv.k;
     const char *vbase = a.kv.v;
@@ -188,15 +308,21 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
 
     auto issue = [&](int tile, int buf) {
         const int tb = tile * T;
+        int r[NIW];
 #pragma unroll
-        for (int c = 0; c < NI; ++c) {
+        for (int ci = 0; ci < NIW; ++ci) {
+            const int rho = (wave * NIW + ci) * RPI + lane / CPR;
+            const int t = tb + rho;
+            r[ci] = (t < ntok) ? rows[t] : -1;
+        }
+#pragma unroll
+        for (int ci = 0; ci < NIW; ++ci) {
+            const int c = wave * NIW + ci;
             const int rho = c * RPI + lane / CPR;
             const int chunk = (lane % CPR) ^ swz<D>(rho);
-            const int t = tb + rho;
-            const int r = (t < ntok) ? rows[t] : -1;
             const char *kp, *vp;
-            if (r >= 0) {
-                const size_t off = (size_t)r * row_stride + head_off + chunk * 16;
+            if (r[ci] >= 0) {
+                const size_t off = (size_t)r[ci] * row_stride + head_off + chunk * 16;
                 kp = kbase + off;
                 vp = vbase + off;
             } else {
@@ -207,92 +333,66 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
         }
     };
 
-    auto compute = [&](int tile, int buf) {
+    // One 16-token subtile `sub` of the tile in `buf`.
+    auto compute_sub = [&](int tile, int buf, int sub) {
         const uint8_t *kt = sm[buf][0];
         const uint8_t *vt = sm[buf][1];
-        const int tb = tile * T;
-        f32x4 st[2][RB];
+        const int tb = tile * T + sub * 16;
+        const int krho = sub * 16 + (lane & 15);
+        bf16x8 kf[KK];
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) st[ts][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int rho = ts * 16 + (lane & 15);
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int chunk = kk * 4 + (lane >> 4);
-                const bf16x8 kf = *(const bf16x8 *)(kt + rho * ROWB + ((chunk ^ swz<D>(rho)) << 4));
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    st[ts][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][kk], st[ts][rb], 0, 0, 0);
-            }
+        for (int kk = 0; kk < KK; ++kk) {
+            const int chunk = kk * 4 + (lane >> 4);
+            kf[kk] = *(const bf16x8 *)(kt + krho * ROWB + ((chunk ^ swz<D>(krho)) << 4));
         }
-        // validity of the 8 tokens this lane holds: t = tb + ts*16 + (lane>>4)*4 + j
-        bool valid[2][4];
+        f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
+        for (int kk = 0; kk < KK; ++kk)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], st, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[j] *= a.scale_log2;
+        if (!(all_rows_valid && tb + 16 <= ntok)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int t = tb + ts * 16 + (lane >> 4) * 4 + j;
-                valid[ts][j] = (t < ntok) && (rows[t] >= 0);
+                const int t = tb + (lane >> 4) * 4 + j;
+                if (!(t < ntok && rows[t] >= 0)) st[j] = kNegInf;
             }
-        bf16x8 pf[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int ts = 0; ts < 2; ++ts)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float s = valid[ts][j] ? st[ts][rb][j] * a.scale_log2 : kNegInf;
-                    st[ts][rb][j] = s;
-                    mx = fmaxf(mx, s);
-                }
-            mx = group4_max(mx);
-            const float mnew = fmaxf(mrow[rb], mx);
-            const float muse = (mnew == kNegInf) ? 0.f : mnew;
-            const float alpha = exp2f(mrow[rb] - muse);
-            mrow[rb] = mnew;
-            float ps = 0.f;
-#pragma unroll
-            for (int ts = 0; ts < 2; ++ts)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p = exp2f(st[ts][rb][j] - muse);
-                    ps += p;
-                    pf[rb][ts * 4 + j] = (__bf16)p;
-                }
-            lsum[rb] = lsum[rb] * alpha + ps;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[rb][dt] *= alpha;
         }
-        // PV: V^T fragment via two transposed LDS reads per 16-wide d tile.
-        // Rows rho0 and rho0 + 16 share their swizzle, so the second read of
-        // each pair is the first address plus 16 rows.
-        const int q4 = lane >> 4, sl = lane & 15;
-        const int rho0 = 4 * q4 + (sl >> 2);
-        const uint32_t vrow = lds_addr(vt) + rho0 * ROWB;
+        float mx = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+        mx = group4_max(mx);
+        const float mnew = fmaxf(mrow, mx);
+        const float muse = (mnew == kNegInf) ? 0.f : mnew;
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(st[j] - muse);
+        if (mnew != mrow) {
+            // the running maximum moved for some row of this wave
+            const float alpha = __builtin_amdgcn_exp2f(mrow - muse);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) o[i] *= alpha;
+            mrow = mnew;
+        }
+        lsum += (p[0] + p[1]) + (p[2] + p[3]);
+        s16x4 pf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pf[j] = __builtin_bit_cast(short, (__bf16)p[j]);
+        // V^T operand: lane (q = lane>>4, i = lane&15) receives V[tb + 4q + t][d0 + i],
+        // t = 0..3, from the 8-byte rows addressed by the lanes 4t + i/4.
+        const int sl = lane & 15;
+        const int vrho = sub * 16 + 4 * (lane >> 4) + (sl >> 2);
+        const uint32_t vrow = lds_addr(vt) + vrho * ROWB;
         uint32_t vaddr[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int dcol = dt * 16 + (sl & 3) * 4;
-            vaddr[dt] = vrow + (((dcol >> 3) ^ swz<D>(rho0)) << 4) + (dcol & 7) * 2;
+        for (int i = 0; i < DT; ++i) {
+            const int dcol = i * 16 + (sl & 3) * 4;
+            vaddr[i] = vrow + (((dcol >> 3) ^ swz<D>(vrho)) << 4) + (dcol & 7) * 2;
         }
-        s16x4 vlo[DT], vhi[DT];
-        if constexpr (DT == 8) {
-            ds_read_tr16_x8<16 * ROWB>(vaddr, vlo, vhi);
-        } else {
-            ds_read_tr16_x4<16 * ROWB>(vaddr, vlo, vhi);
-        }
+        s16x4 vf[DT];
+        ds_read_tr16_n<DT>(vaddr, vf);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            s16x8 vv;
-            vv[0] = vlo[dt][0]; vv[1] = vlo[dt][1]; vv[2] = vlo[dt][2]; vv[3] = vlo[dt][3];
-            vv[4] = vhi[dt][0]; vv[5] = vhi[dt][1]; vv[6] = vhi[dt][2]; vv[7] = vhi[dt][3];
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][dt], 0, 0, 0);
-        }
+        for (int i = 0; i < DT; ++i)
+            o[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[i], pf, o[i], 0, 0, 0);
     };
 
     const int ntiles = (ntok + T - 1) / T;
@@ -300,64 +400,97 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < NBUF - 1; ++i)
         if (i < ntiles) issue(i, i);
     for (int i = 0; i < ntiles; ++i) {
-        const int nxt = i + NBUF - 1;
-        if (nxt < ntiles) issue(nxt, nxt % NBUF);
-        const int ahead = min(ntiles - 1 - i, NBUF - 1);
-        // wait until tile i's 2*NI DMA operations have landed
+        // own DMA of tile i done (tiles issued after it may stay in flight)
+        const int ahead = min(ntiles - 1 - i, NBUF - 2);
         if constexpr (NBUF >= 4) {
-            if (ahead >= 3) { wait_vmcnt<3 * 2 * NI>(); goto ready; }
+            if (ahead >= 2) { wait_vmcnt<2 * 2 * NIW>(); goto ready; }
         }
         if constexpr (NBUF >= 3) {
-            if (ahead >= 2) { wait_vmcnt<2 * 2 * NI>(); goto ready; }
+            if (ahead >= 1) { wait_vmcnt<2 * NIW>(); goto ready; }
         }
-        if (ahead >= 1) { wait_vmcnt<2 * NI>(); goto ready; }
         wait_vmcnt<0>();
     ready:
-        compute(i, i % NBUF);
+        __syncthreads();   // tile i visible to all waves; buffer (i-1) free
+        {
+            const int nxt = i + NBUF - 1;
+            if (nxt < ntiles) issue(nxt, nxt % NBUF);
+        }
+        for (int sub = th; sub < 2; sub += NTH) compute_sub(i, i % NBUF, sub);
     }
 
+    lsum = group4_sum(lsum);
+    __syncthreads();   // ring no longer read: reuse it for the share merge
+    float *shr = (float *)&sm[0][0][0];   // [NW][16 rows][D]
+    if constexpr (NTH > 1) {
+        if (th > 0) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) lsum[rb] = group4_sum(lsum[rb]);
+            for (int i = 0; i < DT; ++i)
+                *(f32x4 *)(shr + ((size_t)wave * 16 + (lane & 15)) * D + i * 16 + (lane >> 4) * 4) = o[i];
+            if (lane < 16) {
+                share_ml[wave][lane][0] = mrow;
+                share_ml[wave][lane][1] = lsum;
+            }
+        }
+        __syncthreads();
+        if (th == 0) {   // fold in the other shares of this row block
+            for (int t2 = 1; t2 < NTH; ++t2) {
+                const int w2 = t2 * RB + rbw;
+                const float m2 = share_ml[w2][lane & 15][0], l2 = share_ml[w2][lane & 15][1];
+                const float mn = fmaxf(mrow, m2);
+                const float mu = (mn == kNegInf) ? 0.f : mn;
+                const float s1 = __builtin_amdgcn_exp2f(mrow - mu), s2 = __builtin_amdgcn_exp2f(m2 - mu);
+                lsum = lsum * s1 + l2 * s2;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+                    o[i] = o[i] * s1 +
+                           *(const f32x4 *)(shr + ((size_t)w2 * 16 + (lane & 15)) * D + i * 16 + (lane >> 4) * 4) * s2;
+                mrow = mn;
+            }
+        }
+    }
 
+    // waves with th == 0 now hold the work-group's result for their rows
+    const int r = rbw * 16 + (lane & 15);
     if (a.splits == 1) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int r = rb * 16 + (lane & 15);
-            if (r >= a.R) continue;
+        if (th == 0 && r < a.R) {
             const int sq = r / a.G, gh = r - (r / a.G) * a.G;
             const size_t orow = (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D;
-            const float inv = (lsum[rb] > 0.f) ? 1.f / lsum[rb] : 0.f;
+            const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 16 + (lane >> 4) * 4;
-                uint32_t lo = f32_to_bf16_bits(o[rb][dt][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[rb][dt][1] * inv) << 16);
-                uint32_t hi = f32_to_bf16_bits(o[rb][dt][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[rb][dt][3] * inv) << 16);
+            for (int i = 0; i < DT; ++i) {
+                const int d = i * 16 + (lane >> 4) * 4;
+                uint32_t lo = f32_to_bf16_bits(o[i][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[i][1] * inv) << 16);
+                uint32_t hi = f32_to_bf16_bits(o[i][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[i][3] * inv) << 16);
                 uint32_t *op = (uint32_t *)((uint16_t *)a.out + orow + d);
                 op[0] = lo;
                 op[1] = hi;
             }
             if (a.lse && lane < 16)
                 a.lse[((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh] =
-                    (lsum[rb] > 0.f) ? (mrow[rb] + __log2f(lsum[rb])) * kLn2 : kNegInf;
+                    (lsum > 0.f) ? (mrow + __log2f(lsum)) * kLn2 : kNegInf;
         }
         return;
     }
 
-    const size_t pb = ((size_t)bg * a.splits + split) * a.rpad;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r = rb * 16 + (lane & 15);
+    // publish this split's partial; the last split of (b, g) to arrive merges
+    if (th == 0) {
+        const size_t pb = ((size_t)bg * a.splits + split) * a.rpad;
         if (lane < 16) {
-            a.part_m[pb + r] = mrow[rb];
-            a.part_l[pb + r] = lsum[rb];
+            st_agent(a.part_m + pb + r, mrow);
+            st_agent(a.part_l + pb + r, lsum);
         }
+        float *po = a.part_o + pb * D + ((size_t)rbw * DT * 64 + lane) * 4;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *(f32x4 *)(a.part_o + (pb + r) * D + dt * 16 + (lane >> 4) * 4) = o[rb][dt];
+        for (int i = 0; i < DT; ++i) st_agent_x4(po + (size_t)i * 256, o[i]);
+        wait_all_mem();
     }
-    if (!arrive_last(a, bg, lane)) return;
-    merge_splits<false, D>(a, bg, b, g, lane);
-    if (lane == 0) a.counters[bg] = 0;
+    __syncthreads();
+    if (tid == 0)
+        s_flag = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
+    __syncthreads();
+    if (!s_flag) return;
+    merge_splits_reg<D, RB, 256>(a, bg, b, g, tid);
+    if (tid == 0) a.counters[bg] = 0;
 }
 
 // --------------------------------------------------------------- float32 / VALU
@@ -481,21 +614,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
     const size_t pb = ((size_t)bg * a.splits + split) * a.rpad;
     if (tid < R) {
-        a.part_m[pb + tid] = m_s[tid];
-        a.part_l[pb + tid] = l_s[tid];
+        st_agent(a.part_m + pb + tid, m_s[tid]);
+        st_agent(a.part_l + pb + tid, l_s[tid]);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = tid + i * 256;
         if (e < R * D) {
             const int r = e / D, d = e - (e / D) * D;
-            a.part_o[(pb + r) * D + d] = acc[i];
+            st_agent(a.part_o + (pb + r) * D + d, acc[i]);
         }
     }
+    wait_all_mem();
     __syncthreads();
     if (tid >= 64) return;
     if (!arrive_last(a, bg, tid)) return;
-    merge_splits<true, D>(a, bg, b, g, tid);
+    merge_splits<true, D, 64>(a, bg, b, g, tid);
     if (tid == 0) a.counters[bg] = 0;
 }
 
@@ -505,15 +639,16 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
     const int G = Hq / Hkv;
     p.rows = w * G;
     p.rb = (p.rows + 15) / 16;
+    if (p.rb == 3) p.rb = 4;   // the bf16 kernel splits its four waves over 1, 2 or 4 row blocks
     p.rpad = p.rb * 16;
     const long groups = (long)B * Hkv;
     const int tok = tokens > 0 ? tokens : 1;
-    // Aim for ~3 co-resident 64-lane work-groups per CU on a 256-CU part,
-    // with at least one 32-token tile per split and at most kAttnMaxTps
-    // tokens per split.  The plan depends on shapes only, so workspace sizes
+    // Aim for kAttnTargetGroups work-groups (about two co-resident 256-lane
+    // groups per CU on a 256-CU part), with at least one 32-token tile per
+    // split and at most kAttnMaxTps tokens per split.  The plan depends on shapes only, so workspace sizes
     // can be queried without a device.
     (void)f32;
-    const long target = 768;
+    const long target = kAttnTargetGroups;
     long splits = (target + groups - 1) / groups;
     const long max_by_tiles = (tok + kAttnTile - 1) / kAttnTile;
     if (splits > max_by_tiles) splits = max_by_tiles;
@@ -542,7 +677,8 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
 
 template <int D, int RB>
 static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RB, 3>), grid, dim3(64), 0, s, a);
+    const size_t dyn = (size_t)a.tps * sizeof(int);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs>), grid, dim3(256), dyn, s, a);
     return hipGetLastError();
 }
 
@@ -561,14 +697,14 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
         switch (p.rb) {
             case 1: return launch_bf16<128, 1>(a, grid, s);
             case 2: return launch_bf16<128, 2>(a, grid, s);
-            case 3: return launch_bf16<128, 3>(a, grid, s);
+            case 3: return launch_bf16<128, 4>(a, grid, s);
             case 4: return launch_bf16<128, 4>(a, grid, s);
         }
     } else if (a.kv.D == 64) {
         switch (p.rb) {
             case 1: return launch_bf16<64, 1>(a, grid, s);
             case 2: return launch_bf16<64, 2>(a, grid, s);
-            case 3: return launch_bf16<64, 3>(a, grid, s);
+            case 3: return launch_bf16<64, 4>(a, grid, s);
             case 4: return launch_bf16<64, 4>(a, grid, s);
         }
     }

@@ -79,6 +79,47 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Device-coherent ("agent scope") relaxed loads and stores.  On gfx950 they
+// are issued with the sc1 cache policy: stores write through the XCD-local
+// L2 and loads do not hit stale L2 lines, so data exchanged between
+// work-groups on different XCDs needs no L2 write-back or invalidation.
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent4(float *p, f32x4 v) {
+    st_agent(p, v[0]);
+    st_agent(p + 1, v[1]);
+    st_agent(p + 2, v[2]);
+    st_agent(p + 3, v[3]);
+}
+__device__ __forceinline__ f32x4 ld_agent4(const float *p) {
+    return f32x4{ld_agent(p), ld_agent(p + 1), ld_agent(p + 2), ld_agent(p + 3)};
+}
+// 16-byte device-coherent store (global_store_dwordx4 with sc1).  Issued as
+// inline assembly, so the caller must wait_all_mem() before depending on it.
+__device__ __forceinline__ void st_agent_x4(float *p, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+// Device-coherent loads through a buffer resource: buffer_load with the sc1
+// cache policy reads the coherent copy (no stale XCD-local L2 line) while the
+// compiler schedules and overlaps them like ordinary loads.  Loads past
+// `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ f32x4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySc1));
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
 // LDS byte address (the offset register value of ds_* instructions).
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(lds_void_t *)p;
@@ -120,6 +161,30 @@ __device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&addr)[8], s16x4
 }
 
 template <int OFF1>
+__device__ __forceinline__ void ds_read_tr16_x2(const uint32_t (&addr)[2], s16x4 (&lo)[2], s16x4 (&hi)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%c6\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%c6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]), "i"(OFF1)
+        : "memory");
+}
+
+template <int OFF1>
+__device__ __forceinline__ void ds_read_tr16_x1(const uint32_t (&addr)[1], s16x4 (&lo)[1], s16x4 (&hi)[1]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:%c3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0])
+        : "v"(addr[0]), "i"(OFF1)
+        : "memory");
+}
+
+template <int OFF1>
 __device__ __forceinline__ void ds_read_tr16_x4(const uint32_t (&addr)[4], s16x4 (&lo)[4], s16x4 (&hi)[4]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
@@ -135,6 +200,50 @@ __device__ __forceinline__ void ds_read_tr16_x4(const uint32_t (&addr)[4], s16x4
           "=&v"(lo[3]), "=&v"(hi[3])
         : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF1)
         : "memory");
+}
+
+// N single transposed reads (one per d tile, 4 tokens each) plus their
+// completion wait, for the 16x16x16 PV product.
+__device__ __forceinline__ void ds_read_tr16_n8(const uint32_t (&a)[8], s16x4 (&v)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+__device__ __forceinline__ void ds_read_tr16_n4(const uint32_t (&a)[4], s16x4 (&v)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+template <int N>
+__device__ __forceinline__ void ds_read_tr16_n(const uint32_t (&a)[N], s16x4 (&v)[N]) {
+    static_assert(N == 8 || N == 4, "d tiles");
+    if constexpr (N == 8) ds_read_tr16_n8(a, v);
+    else ds_read_tr16_n4(a, v);
+}
+
+// Dispatch on the number of d tiles.
+template <int N, int OFF1>
+__device__ __forceinline__ void ds_read_tr16(const uint32_t (&addr)[N], s16x4 (&lo)[N], s16x4 (&hi)[N]) {
+    if constexpr (N == 8) ds_read_tr16_x8<OFF1>(addr, lo, hi);
+    else if constexpr (N == 4) ds_read_tr16_x4<OFF1>(addr, lo, hi);
+    else if constexpr (N == 2) ds_read_tr16_x2<OFF1>(addr, lo, hi);
+    else ds_read_tr16_x1<OFF1>(addr, lo, hi);
 }
 
 }  // namespace dustin

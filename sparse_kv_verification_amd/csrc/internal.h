@@ -20,8 +20,9 @@ struct KvView {
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnTile = 32;       // tokens per pipeline tile
-constexpr int kAttnMaxTps = 1024;   // tokens per split (row table in LDS)
-constexpr int kAttnMaxSplits = 1024;
+constexpr int kAttnMaxTps = 4096;   // tokens per split (row table in LDS)
+constexpr int kAttnBufs = 3;           // LDS ring depth (tiles)
+constexpr int kAttnTargetGroups = 512;  // work-groups the split planner aims for
 
 struct AttnPlan {
     int rows;      // R = w * G query rows per (sequence, KV head)
