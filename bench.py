@@ -190,9 +190,9 @@ def main():
     log(f"eager step {eager_us:.1f} us")
 
     graph_us = None
+    cap = torch.cuda.Stream()
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             step()                       # warm the capture stream's workspaces
@@ -210,7 +210,20 @@ def main():
     # component timings (eager, events on the launch stream)
     score_us = timed(score, args.steps)
     select_us = timed(select, args.steps)
-    # dominant kernel: one event pair around every attention launch
+    # dominant kernel: the L attention launches of a step, replayed from a
+    # HIP graph and timed with events on the launch stream; divided by L this
+    # is the average launch duration (inter-kernel gaps inside the graph
+    # included).  One event pair per eager launch is reported alongside.
+    attn_graph_us = None
+    if not args.no_graph:
+        ga = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(ga, stream=cap):
+                for l in range(sh.layers):
+                    attn(l)
+        torch.cuda.synchronize()
+        ga.replay()
+        attn_graph_us = timed(ga.replay, args.steps) / sh.layers
     durs = []
     for _ in range(args.steps):
         for l in range(sh.layers):
@@ -220,10 +233,11 @@ def main():
             e1.record(stream)
             durs.append((e0, e1))
     torch.cuda.synchronize()
-    attn_launch_us = sum(a.elapsed_time(b) for a, b in durs) / len(durs) * 1e3
+    attn_event_us = sum(a.elapsed_time(b) for a, b in durs) / len(durs) * 1e3
     attn_loop_us = timed(lambda: [attn(l) for l in range(sh.layers)], args.steps) / sh.layers
+    attn_launch_us = attn_graph_us if attn_graph_us is not None else attn_loop_us
     log(f"score {score_us:.1f} us, select {select_us:.1f} us, attention {attn_launch_us:.2f} us/launch "
-        f"({attn_loop_us:.2f} us/layer in a loop)")
+        f"(graph replay; eager loop {attn_loop_us:.2f}, single event-bracketed launch {attn_event_us:.2f})")
 
     dense = None
     if not args.no_dense:
@@ -270,10 +284,12 @@ def main():
         "eager_us_per_step": round(eager_us, 2),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
         "components_us": {"score": round(score_us, 2), "select": round(select_us, 2),
-                          "attention_per_layer": round(attn_launch_us, 3),
-                          "attention_per_layer_in_loop": round(attn_loop_us, 3)},
+                          "attention_per_launch": round(attn_launch_us, 3),
+                          "attention_per_launch_eager_loop": round(attn_loop_us, 3),
+                          "attention_single_launch_event_bracketed": round(attn_event_us, 3)},
         "roofline": {
-            "kernel": "attn_bf16_kernel (dustin_sparse_verify_attn)",
+            "kernel": "attn_bf16_kernel<128, 2, 3, false> (dustin_sparse_verify_attn)",
+            "launch_us": round(attn_launch_us, 3),
             "bound": "hbm",
             "achieved": round(attn_gbps, 1),
             "peak": HBM_PEAK_GBPS,

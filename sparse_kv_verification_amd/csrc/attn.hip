@@ -222,7 +222,7 @@ __device__ __forceinline__ bool arrive_last(const AttnArgs &a, int bg, int lane)
 //   P   = exp2(S^T - m)       lane holds row (lane & 15), tokens 4*(lane>>4)+j
 //   O^T += V_sub^T . P^T      D/16 x v_mfma_f32_16x16x16_bf16; the V operand
 //                             comes from one transposed LDS read per d tile.
-template <int D, int RB, int NBUF>
+template <int D, int RB, int NBUF, bool DENSE>
 __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(AttnArgs a) {
     constexpr int T = kAttnTile;
     constexpr int ROWB = D * 2;       // bytes of one head row
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
     const int b = bg / a.kv.Hkv, g = bg - (bg / a.kv.Hkv) * a.kv.Hkv;
 
     const int nb = seq_len(a.kv, b);
-    const int cnt = a.idx ? min(max(a.count[b], 0), a.k) : nb;
+    const int cnt = DENSE ? nb : min(max(a.count[b], 0), a.k);
     const int t0 = split * a.tps;
     const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
 
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int t = tid + 256 * i;
-            jv[i] = (t < ntok) ? (a.idx ? a.idx[(int64_t)b * a.k + t0 + t] : t0 + t) : -1;
+            jv[i] = (t < ntok) ? (DENSE ? t0 + t : a.idx[(int64_t)b * a.k + t0 + t]) : -1;
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -678,7 +678,10 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
 template <int D, int RB>
 static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
     const size_t dyn = (size_t)a.tps * sizeof(int);
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs>), grid, dim3(256), dyn, s, a);
+    if (a.idx)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs, false>), grid, dim3(256), dyn, s, a);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs, true>), grid, dim3(256), dyn, s, a);
     return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@
 namespace dustin {
 
 constexpr int CH = kScoreChunk;
+constexpr int kScoreGroups = 1024;   // persistent work-groups (four per CU)
 
 __device__ __forceinline__ int sl_len(const KvView &kv, int b) {
     return min(max(kv.seq_lens[b], 0), kv.N_max);
@@ -327,128 +328,172 @@ struct DraftMfma {
     }
 };
 
+// Statistics pass.  Persistent work-groups walk the items (b, unit u,
+// 1024-position chunk) round robin; each wave streams 256 positions in
+// groups of four 16-position subtiles, the next group's K fragments in
+// flight while the current group is reduced into per-lane running
+// (max, sum of exp2) pairs.
+constexpr int kDraftStatChunk = 1024;
+
 template <int D, int RB>
-__global__ __launch_bounds__(256) void draft_stats_mfma(DraftScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     __shared__ float red[4][RB * 16][2];
-    const int chunk = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
-    const int l = u / a.Hkv_d, c = u - (u / a.Hkv_d) * a.Hkv_d;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const KvView &kv = a.kv[l];
-    const int nb = sl_len(kv, b);
-    const int jb = chunk * CH + wave * 64;
-
-    bf16x8 qf[RB][M::KK];
-    bf16x8 kf[4][M::KK];
-    M::load_q(a, b, l, c, lane, qf);
-    M::load_k(kv, b, c, jb, nb, lane, kf);
-    f32x4 s[4][RB];
-    M::logits(qf, kf, s);
-
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const bool ok = jb + st * 16 + (lane & 15) < nb;
-                const float v = ok ? s[st][rb][i] * a.scale_log2 : kNegInf;
-                s[st][rb][i] = v;
-                mx = fmaxf(mx, v);
-            }
-            mx = lane16_max(mx);
-            const float muse = (mx == kNegInf) ? 0.f : mx;
-            float z = 0.f;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) z += exp2f(s[st][rb][i] - muse);
-            z = lane16_sum(z);
-            if ((lane & 15) == 0) {
-                const int r = rb * 16 + (lane >> 4) * 4 + i;
-                red[wave][r][0] = mx;
-                red[wave][r][1] = z;
-            }
-        }
-    __syncthreads();
-    if (threadIdx.x < a.rows) {
-        const int r = threadIdx.x;
-        float mx = kNegInf;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][r][0]);
-        const float muse = (mx == kNegInf) ? 0.f : mx;
-        float z = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) z += red[w][r][1] * exp2f(red[w][r][0] - muse);
-        float *st = a.stat + ((((int64_t)b * a.L_d * a.Hkv_d + u) * a.rows + r) * a.nchunk + chunk) * 2;
-        st[0] = mx;
-        st[1] = z;
-    }
-}
-
-template <int D, int RB>
-__global__ __launch_bounds__(256) void draft_acc_mfma(DraftScoreArgs a) {
-    using M = DraftMfma<D, RB>;
-    const int chunk = blockIdx.x, b = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int jb = chunk * CH + wave * 64;
     const int U = a.L_d * a.Hkv_d;
-    const float *lse_b = a.lse + (int64_t)b * U * a.rows;
-
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 qf[RB][M::KK], qn[RB][M::KK];
-    bf16x8 kf[4][M::KK], kn[4][M::KK];
-    float lr[RB][4], ln[RB][4];
-
-    auto load_unit = [&](int u, bf16x8 (&q)[RB][M::KK], bf16x8 (&k)[4][M::KK], float (&ls)[RB][4]) {
-        const int l = u / a.Hkv_d, c = u - (u / a.Hkv_d) * a.Hkv_d;
+    const int nch = a.nchunk;                 // kDraftStatChunk-position chunks
+    const int items = a.kv[0].B * U * nch;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int c = it % nch, u = (it / nch) % U, b = it / (nch * U);
+        const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
         const KvView &kv = a.kv[l];
-        M::load_q(a, b, l, c, lane, q);
-        M::load_k(kv, b, c, jb, sl_len(kv, b), lane, k);
+        const int nb = sl_len(kv, b);
+        const int jw = c * kDraftStatChunk + wave * (kDraftStatChunk / 4);
+        bf16x8 qf[RB][M::KK];
+        M::load_q(a, b, l, kvh, lane, qf);
+        float mrun[RB][4], zrun[RB][4];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = rb * 16 + (lane >> 4) * 4 + i;
-                ls[rb][i] = (r < a.rows) ? lse_b[(int64_t)u * a.rows + r] : __builtin_huge_valf();
+                mrun[rb][i] = kNegInf;
+                zrun[rb][i] = 0.f;
             }
-    };
+        constexpr int NG = kDraftStatChunk / 4 / 64;   // 64-position groups per wave
+        auto fold = [&](int gi, const bf16x8 (&k)[4][M::KK]) {
+            f32x4 sc[4][RB];
+            M::logits(qf, k, sc);
+            const int jg = jw + gi * 64;
+            const bool full = jg + 64 <= nb;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float mx = mrun[rb][i];
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) {
+                        float v = sc[st][rb][i] * a.scale_log2;
+                        if (!full && jg + st * 16 + (lane & 15) >= nb) v = kNegInf;
+                        sc[st][rb][i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                    const float mu = (mx == kNegInf) ? 0.f : mx;
+                    float z = zrun[rb][i] * __builtin_amdgcn_exp2f(mrun[rb][i] - mu);
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) z += __builtin_amdgcn_exp2f(sc[st][rb][i] - mu);
+                    mrun[rb][i] = mx;
+                    zrun[rb][i] = z;
+                }
+        };
+        // two named operand sets keep the double buffer in registers
+        bf16x8 kA[4][M::KK], kB[4][M::KK];
+        M::load_k(kv, b, kvh, jw, nb, lane, kA);
+#pragma unroll 1
+        for (int gi = 0; gi < NG; gi += 2) {
+            M::load_k(kv, b, kvh, jw + (gi + 1) * 64, nb, lane, kB);
+            fold(gi, kA);
+            if (gi + 2 < NG) M::load_k(kv, b, kvh, jw + (gi + 2) * 64, nb, lane, kA);
+            fold(gi + 1, kB);
+        }
+        // combine the 16 token lanes of each row, then the four waves
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mx = lane16_max(mrun[rb][i]);
+                const float mu = (mx == kNegInf) ? 0.f : mx;
+                const float z = lane16_sum(zrun[rb][i] * __builtin_amdgcn_exp2f(mrun[rb][i] - mu));
+                if ((lane & 15) == 0) {
+                    const int r = rb * 16 + (lane >> 4) * 4 + i;
+                    red[wave][r][0] = mx;
+                    red[wave][r][1] = z;
+                }
+            }
+        __syncthreads();
+        if (threadIdx.x < a.rows) {
+            const int r = threadIdx.x;
+            float mx = kNegInf;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][r][0]);
+            const float mu = (mx == kNegInf) ? 0.f : mx;
+            float z = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) z += red[w][r][1] * __builtin_amdgcn_exp2f(red[w][r][0] - mu);
+            float *st = a.stat + ((((int64_t)b * U + u) * a.rows + r) * nch + c) * 2;
+            st[0] = mx;
+            st[1] = z;
+        }
+        __syncthreads();
+    }
+}
 
-    load_unit(0, qf, kf, lr);
-    for (int u = 0; u < U; ++u) {
-        if (u + 1 < U) load_unit(u + 1, qn, kn, ln);
-        const int l = u / a.Hkv_d;
-        const int nb = sl_len(a.kv[l], b);
-        f32x4 s[4][RB];
-        M::logits(qf, kf, s);
+// Accumulation pass.  Persistent work-groups walk the items (b, 256-position
+// chunk); each wave owns 64 positions and loops over every draft unit in a
+// fixed order, the next unit's operands in flight, so S_Draft is summed in
+// registers without atomics.
+constexpr int kDraftAccChunk = 256;
+
+template <int D, int RB>
+__global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
+    using M = DraftMfma<D, RB>;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int U = a.L_d * a.Hkv_d;
+    const int N = a.kv[0].N_max;
+    const int nch = (N + kDraftAccChunk - 1) / kDraftAccChunk;
+    const int items = a.kv[0].B * nch;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int c = it % nch, b = it / nch;
+        const int jb = c * kDraftAccChunk + wave * 64;
+        const float *lse_b = a.lse + (int64_t)b * U * a.rows;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        // two operand sets, A and B, named separately so that they stay in
+        // registers (a runtime-indexed pair would live in scratch memory)
+        bf16x8 qA[RB][M::KK], qB[RB][M::KK];
+        bf16x8 kA[4][M::KK], kB[4][M::KK];
+        float lA[RB][4], lB[RB][4];
+        auto load_unit = [&](int u, bf16x8 (&q)[RB][M::KK], bf16x8 (&k)[4][M::KK], float (&ls)[RB][4]) {
+            const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
+            const KvView &kv = a.kv[l];
+            M::load_q(a, b, l, kvh, lane, q);
+            M::load_k(kv, b, kvh, jb, sl_len(kv, b), lane, k);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rb * 16 + (lane >> 4) * 4 + i;
+                    ls[rb][i] = (r < a.rows) ? lse_b[(int64_t)u * a.rows + r] : __builtin_huge_valf();
+                }
+        };
+        auto fold_unit = [&](int u, const bf16x8 (&q)[RB][M::KK], const bf16x8 (&k)[4][M::KK],
+                             const float (&ls)[RB][4]) {
+            const int nb = sl_len(a.kv[u / a.Hkv_d], b);
+            f32x4 sc[4][RB];
+            M::logits(q, k, sc);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float t = 0.f;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) t += __builtin_amdgcn_exp2f(sc[st][rb][i] * a.scale_log2 - ls[rb][i]);
+                if (jb + st * 16 + (lane & 15) < nb) acc[st] += t;
+            }
+        };
+        load_unit(0, qA, kA, lA);
+        for (int u = 0; u < U; u += 2) {
+            if (u + 1 < U) load_unit(u + 1, qB, kB, lB);
+            fold_unit(u, qA, kA, lA);
+            if (u + 1 < U) {
+                if (u + 2 < U) load_unit(u + 2, qA, kA, lA);
+                fold_unit(u + 1, qB, kB, lB);
+            }
+        }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            float t = 0.f;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) t += exp2f(s[st][rb][i] * a.scale_log2 - lr[rb][i]);
-            if (jb + st * 16 + (lane & 15) < nb) acc[st] += t;
+            const float v = group4_sum(acc[st]);
+            const int j = jb + st * 16 + (lane & 15);
+            if (lane < 16 && j < N) a.s_draft[(int64_t)b * N + j] = v;
         }
-        if (u + 1 < U) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int kk = 0; kk < M::KK; ++kk) qf[rb][kk] = qn[rb][kk];
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-#pragma unroll
-                for (int kk = 0; kk < M::KK; ++kk) kf[st][kk] = kn[st][kk];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lr[rb][i] = ln[rb][i];
-        }
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const float v = group4_sum(acc[st]);
-        const int j = jb + st * 16 + (lane & 15);
-        if (lane < 16 && j < a.kv[0].N_max) a.s_draft[(int64_t)b * a.kv[0].N_max + j] = v;
     }
 }
 
@@ -594,13 +639,19 @@ template <int D, int RB>
 static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     const int U = a.L_d * a.Hkv_d;
-    hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(a.nchunk, U, k0.B), dim3(256), 0, s, a);
+    DraftScoreArgs b = a;
+    b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
+    const int stat_items = k0.B * U * b.nchunk;
+    hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(stat_items < kScoreGroups ? stat_items : kScoreGroups),
+                       dim3(256), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrows = k0.B * U * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, a.stat, a.lse, nrows, a.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((draft_acc_mfma<D, RB>), dim3(a.nchunk, k0.B), dim3(256), 0, s, a);
+    const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
+    hipLaunchKernelGGL((draft_acc_mfma<D, RB>), dim3(acc_items < kScoreGroups ? acc_items : kScoreGroups),
+                       dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
