@@ -288,7 +288,7 @@ def main():
                           "attention_per_launch_eager_loop": round(attn_loop_us, 3),
                           "attention_single_launch_event_bracketed": round(attn_event_us, 3)},
         "roofline": {
-            "kernel": "attn_bf16_kernel<128, 2, 3, false> (dustin_sparse_verify_attn)",
+            "kernel": "attn_bf16_kernel<128, 2, 8, false> (dustin_sparse_verify_attn)",
             "launch_us": round(attn_launch_us, 3),
             "bound": "hbm",
             "achieved": round(attn_gbps, 1),

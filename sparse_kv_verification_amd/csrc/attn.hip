@@ -6,13 +6,14 @@
 // Dustin blog's Fig. 5 ("compressed KV").  Without an index list the same
 // kernel streams every row j < n_b (the "Full Cache" baseline of Fig. 7).
 //
-// Work decomposition: one 64-lane work-group per (b, g, token split).  The
-// split's K and V rows are gathered tile by tile (32 tokens) straight into
-// LDS with global->LDS DMA (16 B per lane), NBUF tiles deep, so the HBM
-// gather of later tiles overlaps the MFMA work on the current one.  Rows are
-// stored with a 16-byte-chunk XOR swizzle so that both the K operand reads
-// (ds_read_b128) and the transposed V reads (ds_read_b64_tr_b16) are free of
-// bank conflicts.
+// Work decomposition: one work-group per (b, g, token split), sized to fill
+// one CU (8 waves, about 130 KiB of LDS), with the splits planned so that
+// the grid is about one group per CU.  The split's K and V rows are gathered
+// tile by tile straight into an LDS ring with global->LDS DMA (16 B per
+// lane), several tiles deep, so the HBM gather of later tiles overlaps the
+// MFMA work on the current one.  Rows are stored with a 16-byte-chunk XOR
+// swizzle so that both the K operand reads (ds_read_b128) and the transposed
+// V reads (ds_read_b64_tr_b16) are free of bank conflicts.
 //
 //   S^T[token][row] = K_tile . Q^T      v_mfma_f32_16x16x32_bf16, fp32 acc
 //   online softmax over tokens (exp2 domain, per-row running max)
@@ -120,82 +121,6 @@ __device__ void merge_splits(const AttnArgs &a, int bg, int b, int g, int tid) {
     }
 }
 
-// Merge for the MFMA kernel, whose split partials are stored in register
-// order: per split, float4 element (rb, dt, lane) holds row rb*16 + (lane&15),
-// d = dt*16 + 4*(lane>>4) .. +3, so every publishing store is a contiguous
-// 1 KiB per wave.  Same single-pass fold as merge_splits.
-template <int D, int RB, int NT>
-__device__ void merge_splits_reg(const AttnArgs &a, int bg, int b, int g, int tid) {
-    constexpr int DT = D / 16;
-    constexpr int NE = RB * DT * 64 / NT;   // float4 elements per thread
-    static_assert(NE * NT == RB * DT * 64, "merge geometry");
-    const size_t pb = (size_t)bg * a.splits * a.rpad;
-    const uint32_t nml = (uint32_t)(a.splits * a.rpad * sizeof(float));
-    const __amdgpu_buffer_rsrc_t pm = coherent_rsrc(a.part_m + pb, nml);
-    const __amdgpu_buffer_rsrc_t pl = coherent_rsrc(a.part_l + pb, nml);
-    const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, nml * D);
-    uint16_t *__restrict__ outp = (uint16_t *)a.out;
-    float M[NE], L[NE];
-    f32x4 acc[NE];
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        M[k] = kNegInf;
-        L[k] = 0.f;
-        acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // software pipeline: split s + 1 is loaded while split s is folded in
-    float ms[2][NE], ls[2][NE];
-    f32x4 v[2][NE];
-    auto load = [&](int s, int slot) {
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const int e = tid + k * NT;
-            const int r = (e / (DT * 64)) * 16 + (e & 15);
-            const uint32_t o = (uint32_t)(s * a.rpad + r) * 4u;
-            ms[slot][k] = ld_coherent(pm, o);
-            ls[slot][k] = ld_coherent(pl, o);
-            v[slot][k] = ld_coherent4(po, ((uint32_t)(s * a.rpad * D) + (uint32_t)e * 4u) * 4u);
-        }
-    };
-    auto fold = [&](int slot) {
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const float Mn = fmaxf(M[k], ms[slot][k]);
-            const float mu = (Mn == kNegInf) ? 0.f : Mn;
-            const float so = __builtin_amdgcn_exp2f(M[k] - mu), sn = __builtin_amdgcn_exp2f(ms[slot][k] - mu);
-            L[k] = L[k] * so + ls[slot][k] * sn;
-            acc[k] = acc[k] * so + v[slot][k] * sn;
-            M[k] = Mn;
-        }
-    };
-    load(0, 0);
-    int s = 0;
-    for (; s + 2 <= a.splits; s += 2) {
-        load(s + 1, 1);
-        fold(0);
-        if (s + 2 < a.splits) load(s + 2, 0);
-        fold(1);
-    }
-    if (s < a.splits) fold(0);
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        const int e = tid + k * NT;
-        const int i = (e / 64) % DT, ln = e & 63;
-        const int r = (e / (DT * 64)) * 16 + (ln & 15);
-        if (r >= a.R) continue;
-        const float inv = (L[k] > 0.f) ? 1.f / L[k] : 0.f;
-        const int sq = r / a.G, gh = r - (r / a.G) * a.G;
-        const size_t hrow = ((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh;
-        const f32x4 o = acc[k] * inv;
-        uint32_t lo = f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
-        uint32_t hi = f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
-        uint32_t *op = (uint32_t *)(outp + hrow * D + i * 16 + (ln >> 4) * 4);
-        op[0] = lo;
-        op[1] = hi;
-        if (a.lse && i == 0 && ln < 16) a.lse[hrow] = (L[k] > 0.f) ? (M[k] + __log2f(L[k])) * kLn2 : kNegInf;
-    }
-}
-
 // Split partials are exchanged through device-coherent stores and loads
 // (st_agent / ld_agent): a work-group stores its partial, waits for the
 // stores to complete, and only then bumps the (b, g) arrival counter; the
@@ -209,22 +134,45 @@ __device__ __forceinline__ bool arrive_last(const AttnArgs &a, int bg, int lane)
 }
 
 // --------------------------------------------------------------- bf16 / MFMA
-// Four waves share one LDS ring of NBUF 32-token tiles.  Wave w owns row
+// NW waves share one LDS ring of NBUF tiles of T tokens.  Wave w owns row
 // block w % RB (16 query rows) and, of every tile, the 16-token subtiles
-// s = w / RB (mod NTH) with NTH = 4 / RB: each wave keeps its own running
+// s = w / RB (mod NTH) with NTH = NW / RB: each wave keeps its own running
 // softmax state over its share of the tokens, so no score or exponential is
-// computed twice; the shares of one row block are merged through LDS at the
-// end.  Each wave issues a quarter of every tile's DMA, and one barrier per
-// tile both publishes the tile and frees the buffer the next DMA overwrites.
+// computed twice; the shares of one row block are folded through LDS at the
+// end, every wave folding one slice of the d columns.  Each wave issues
+// 1 / NW of every tile's DMA.  One barrier per tile both publishes the tile
+// and frees the buffer the next DMA overwrites; it waits only for LDS
+// traffic (lds_barrier), so the DMA of later tiles stays in flight.
 //
 // Per 16-token subtile and row block:
 //   S^T = K_sub . Q^T         4 (D = 128) x v_mfma_f32_16x16x32_bf16
 //   P   = exp2(S^T - m)       lane holds row (lane & 15), tokens 4*(lane>>4)+j
 //   O^T += V_sub^T . P^T      D/16 x v_mfma_f32_16x16x16_bf16; the V operand
 //                             comes from one transposed LDS read per d tile.
-template <int D, int RB, int NBUF, bool DENSE>
-__global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int T = kAttnTile;
+
+// Wait until this wave's DMA for the current tile has landed while the
+// `ahead` tiles issued after it (PER instructions each) may stay in flight.
+template <int A, int PER>
+__device__ __forceinline__ void wait_tile(int ahead) {
+    if constexpr (A <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= A) wait_vmcnt<A * PER>();
+        else wait_tile<A - 1, PER>(ahead);
+    }
+}
+
+template <int D, int RB, int NW>
+struct AttnGeom {
+    static constexpr int T = (16 * NW / RB > kAttnTile) ? 16 * NW / RB : kAttnTile;   // tokens per tile
+    static constexpr int STAGE = 2 * T * D * 2;                                        // K + V bytes per tile
+    static constexpr int NBUF = (kAttnRingBytes / STAGE < 8) ? kAttnRingBytes / STAGE : 8;
+};
+
+template <int D, int RB, int NW, bool DENSE>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int T = AttnGeom<D, RB, NW>::T;
+    constexpr int NBUF = AttnGeom<D, RB, NW>::NBUF;
     constexpr int ROWB = D * 2;       // bytes of one head row
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;     // rows per DMA instruction
@@ -232,12 +180,13 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
     constexpr int TB = T * ROWB;      // bytes of one K tile
     constexpr int KK = D / 32;        // k-steps of the QK^T MFMA
     constexpr int DT = D / 16;        // 16-wide d tiles of the PV MFMA
-    constexpr int NW = 4;             // waves per work-group
+    constexpr int NT = NW * 64;       // threads per work-group
     constexpr int NTH = NW / RB;      // token shares per row block
     constexpr int NIW = NI / NW;      // DMA instructions per wave per K (or V) tile
     static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
+    static_assert(NW == 4 || NW == 8, "waves");
+    static_assert(NBUF >= 2 && T % 16 == 0 && (T / 16) % NTH == 0, "ring / subtile geometry");
     static_assert(NI * 1024 == TB && NIW >= 1 && NIW * NW == NI, "tile / DMA geometry");
-    static_assert(NBUF * 2 * TB >= NW * 16 * D * 4, "LDS ring reused for the share merge");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sm[NBUF][2][TB];
     __shared__ float share_ml[NW][16][2];
@@ -272,28 +221,43 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
             for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();   // s_flag cleared; the Q loads stay in flight
     bool any_bad = false;
     {   // physical row of every token of the split; all loads issued first
-        constexpr int PER = kAttnMaxTps / 256;
+        constexpr int PER = kAttnMaxTps / NT;
         int jv[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int t = tid + 256 * i;
+            const int t = tid + NT * i;
             jv[i] = (t < ntok) ? (DENSE ? t0 + t : a.idx[(int64_t)b * a.k + t0 + t]) : -1;
+        }
+        // paged caches: every page-table entry is requested before any is used
+        int pg[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = tid + NT * i;
+            const bool ok = t < ntok && jv[i] >= 0 && jv[i] < nb;
+            pg[i] = (ok && a.kv.page_size != 0) ? a.kv.page_table[(int64_t)b * a.kv.max_pages + (jv[i] >> 4)] : 0;
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int t = tid + 256 * i;
+            const int t = tid + NT * i;
             if (t < ntok) {
-                const int r = (jv[i] >= 0 && jv[i] < nb) ? phys_row(a.kv, b, jv[i]) : -1;
+                int r = -1;
+                if (jv[i] >= 0 && jv[i] < nb) {
+                    if (a.kv.page_size == 0) r = b * a.kv.N_max + jv[i];
+                    else if (pg[i] >= 0 && pg[i] < a.kv.num_pages) r = pg[i] * 16 + (jv[i] & 15);
+                }
                 rows[t] = r;
                 any_bad |= (r < 0);
             }
         }
     }
     if (any_bad) s_flag = 1;
-    __syncthreads();
+    // Q fragments and index loads have landed (nothing else is in flight
+    // yet), so no wait on them is left for the compiler to place in the loop.
+    wait_vmcnt<0>();
+    lds_barrier();
     const bool all_rows_valid = (s_flag == 0);
 
     f32x4 o[DT];
@@ -339,12 +303,17 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
         const uint8_t *vt = sm[buf][1];
         const int tb = tile * T + sub * 16;
         const int krho = sub * 16 + (lane & 15);
-        bf16x8 kf[KK];
+        uint32_t kaddr[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const int chunk = kk * 4 + (lane >> 4);
-            kf[kk] = *(const bf16x8 *)(kt + krho * ROWB + ((chunk ^ swz<D>(krho)) << 4));
+            kaddr[kk] = lds_addr(kt) + krho * ROWB + ((chunk ^ swz<D>(krho)) << 4);
         }
+        u32x4 kraw[KK];
+        ds_read_b128_n(kaddr, kraw);
+        bf16x8 kf[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, kraw[kk]);
         f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
@@ -401,87 +370,85 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
         if (i < ntiles) issue(i, i);
     for (int i = 0; i < ntiles; ++i) {
         // own DMA of tile i done (tiles issued after it may stay in flight)
-        const int ahead = min(ntiles - 1 - i, NBUF - 2);
-        if constexpr (NBUF >= 4) {
-            if (ahead >= 2) { wait_vmcnt<2 * 2 * NIW>(); goto ready; }
-        }
-        if constexpr (NBUF >= 3) {
-            if (ahead >= 1) { wait_vmcnt<2 * NIW>(); goto ready; }
-        }
-        wait_vmcnt<0>();
-    ready:
-        __syncthreads();   // tile i visible to all waves; buffer (i-1) free
+        wait_tile<NBUF - 2, 2 * NIW>(min(ntiles - 1 - i, NBUF - 2));
+        lds_barrier();   // tile i visible to all waves; buffer (i-1) free
         {
             const int nxt = i + NBUF - 1;
             if (nxt < ntiles) issue(nxt, nxt % NBUF);
         }
-        for (int sub = th; sub < 2; sub += NTH) compute_sub(i, i % NBUF, sub);
+        for (int sub = th; sub < T / 16; sub += NTH) compute_sub(i, i % NBUF, sub);
     }
 
     lsum = group4_sum(lsum);
-    __syncthreads();   // ring no longer read: reuse it for the share merge
-    float *shr = (float *)&sm[0][0][0];   // [NW][16 rows][D]
-    if constexpr (NTH > 1) {
-        if (th > 0) {
+    __syncthreads();   // ring no longer read: reuse it for the share fold
+
+    // Every wave leaves its share (running max, sum and unnormalised O of its
+    // rows over its tokens) in LDS.  Then wave (rbw, th) folds the NTH shares
+    // of row block rbw, in share order, for the d columns th * DS .. + DS:
+    // lane (row = lane & 15, q = lane >> 4) owns E consecutive columns.
+    constexpr int SROW = D + 4;   // padded share row (floats): rows start on different banks
+    constexpr int DS = D / NTH;
+    constexpr int E = DS / 4;
+    static_assert(E % 4 == 0, "fold slice");
+    static_assert(NW * 16 * SROW * 4 <= NBUF * 2 * TB, "LDS ring reused for the share fold");
+    float *shr = (float *)&sm[0][0][0];   // [NW][16][SROW]
+    {
+        float *my = shr + ((size_t)wave * 16 + (lane & 15)) * SROW + (lane >> 4) * 4;
 #pragma unroll
-            for (int i = 0; i < DT; ++i)
-                *(f32x4 *)(shr + ((size_t)wave * 16 + (lane & 15)) * D + i * 16 + (lane >> 4) * 4) = o[i];
-            if (lane < 16) {
-                share_ml[wave][lane][0] = mrow;
-                share_ml[wave][lane][1] = lsum;
-            }
-        }
-        __syncthreads();
-        if (th == 0) {   // fold in the other shares of this row block
-            for (int t2 = 1; t2 < NTH; ++t2) {
-                const int w2 = t2 * RB + rbw;
-                const float m2 = share_ml[w2][lane & 15][0], l2 = share_ml[w2][lane & 15][1];
-                const float mn = fmaxf(mrow, m2);
-                const float mu = (mn == kNegInf) ? 0.f : mn;
-                const float s1 = __builtin_amdgcn_exp2f(mrow - mu), s2 = __builtin_amdgcn_exp2f(m2 - mu);
-                lsum = lsum * s1 + l2 * s2;
-#pragma unroll
-                for (int i = 0; i < DT; ++i)
-                    o[i] = o[i] * s1 +
-                           *(const f32x4 *)(shr + ((size_t)w2 * 16 + (lane & 15)) * D + i * 16 + (lane >> 4) * 4) * s2;
-                mrow = mn;
-            }
+        for (int i = 0; i < DT; ++i) *(f32x4 *)(my + i * 16) = o[i];
+        if (lane < 16) {
+            share_ml[wave][lane][0] = mrow;
+            share_ml[wave][lane][1] = lsum;
         }
     }
-
-    // waves with th == 0 now hold the work-group's result for their rows
-    const int r = rbw * 16 + (lane & 15);
-    if (a.splits == 1) {
-        if (th == 0 && r < a.R) {
-            const int sq = r / a.G, gh = r - (r / a.G) * a.G;
-            const size_t orow = (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D;
-            const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+    __syncthreads();
+    const int row = lane & 15, r = rbw * 16 + row;
+    const int d0 = th * DS + (lane >> 4) * E;
+    float M = kNegInf, L = 0.f;
+    f32x4 acc[E / 4];
 #pragma unroll
-            for (int i = 0; i < DT; ++i) {
-                const int d = i * 16 + (lane >> 4) * 4;
-                uint32_t lo = f32_to_bf16_bits(o[i][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[i][1] * inv) << 16);
-                uint32_t hi = f32_to_bf16_bits(o[i][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[i][3] * inv) << 16);
-                uint32_t *op = (uint32_t *)((uint16_t *)a.out + orow + d);
-                op[0] = lo;
-                op[1] = hi;
+    for (int c = 0; c < E / 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t2 = 0; t2 < NTH; ++t2) {
+        const int w2 = t2 * RB + rbw;
+        const float m2 = share_ml[w2][row][0], l2 = share_ml[w2][row][1];
+        const float mn = fmaxf(M, m2);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        const float s1 = __builtin_amdgcn_exp2f(M - mu), s2 = __builtin_amdgcn_exp2f(m2 - mu);
+        L = L * s1 + l2 * s2;
+        const float *src = shr + ((size_t)w2 * 16 + row) * SROW + d0;
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) acc[c] = acc[c] * s1 + *(const f32x4 *)(src + 4 * c) * s2;
+        M = mn;
+    }
+
+    if (a.splits == 1) {
+        if (r < a.R) {
+            const int sq = r / a.G, gh = r - (r / a.G) * a.G;
+            const size_t hrow = ((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh;
+            const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+            for (int c = 0; c < E / 4; ++c) {
+                uint32_t *op = (uint32_t *)((uint16_t *)a.out + hrow * D + d0 + 4 * c);
+                op[0] = f32_to_bf16_bits(acc[c][0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[c][1] * inv) << 16);
+                op[1] = f32_to_bf16_bits(acc[c][2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[c][3] * inv) << 16);
             }
-            if (a.lse && lane < 16)
-                a.lse[((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh] =
-                    (lsum > 0.f) ? (mrow + __log2f(lsum)) * kLn2 : kNegInf;
+            if (a.lse && th == 0 && lane < 16) a.lse[hrow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
         }
         return;
     }
 
-    // publish this split's partial; the last split of (b, g) to arrive merges
-    if (th == 0) {
+    // publish this split's partial (row-major); the last split of (b, g) to
+    // arrive merges
+    {
         const size_t pb = ((size_t)bg * a.splits + split) * a.rpad;
-        if (lane < 16) {
-            st_agent(a.part_m + pb + r, mrow);
-            st_agent(a.part_l + pb + r, lsum);
+        if (th == 0 && lane < 16) {
+            st_agent(a.part_m + pb + r, M);
+            st_agent(a.part_l + pb + r, L);
         }
-        float *po = a.part_o + pb * D + ((size_t)rbw * DT * 64 + lane) * 4;
+        const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, (uint32_t)(a.rpad * D * sizeof(float)));
 #pragma unroll
-        for (int i = 0; i < DT; ++i) st_agent_x4(po + (size_t)i * 256, o[i]);
+        for (int c = 0; c < E / 4; ++c) st_coherent4(po, (uint32_t)((r * D + d0 + 4 * c) * 4), acc[c]);
         wait_all_mem();
     }
     __syncthreads();
@@ -489,7 +456,7 @@ __global__ __launch_bounds__(256, (NBUF <= 3 ? 3 : 2)) void attn_bf16_kernel(Att
         s_flag = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
     __syncthreads();
     if (!s_flag) return;
-    merge_splits_reg<D, RB, 256>(a, bg, b, g, tid);
+    merge_splits<false, D, NT>(a, bg, b, g, tid);
     if (tid == 0) a.counters[bg] = 0;
 }
 
@@ -639,22 +606,24 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
     const int G = Hq / Hkv;
     p.rows = w * G;
     p.rb = (p.rows + 15) / 16;
-    if (p.rb == 3) p.rb = 4;   // the bf16 kernel splits its four waves over 1, 2 or 4 row blocks
+    if (p.rb == 3) p.rb = 4;   // the bf16 kernel splits its waves over 1, 2 or 4 row blocks
     p.rpad = p.rb * 16;
     const long groups = (long)B * Hkv;
     const int tok = tokens > 0 ? tokens : 1;
-    // Aim for kAttnTargetGroups work-groups (about two co-resident 256-lane
-    // groups per CU on a 256-CU part), with at least one 32-token tile per
-    // split and at most kAttnMaxTps tokens per split.  The plan depends on shapes only, so workspace sizes
+    // Aim for kAttnTargetGroups work-groups (one 8-wave bf16 group per CU on
+    // a 256-CU part).  Every split holds whole tiles (kAttnSplitQuantum tokens
+    // covers every tile size of both kernels) and at most kAttnMaxTps tokens.
+    // The plan depends on shapes only (not on the dtype), so workspace sizes
     // can be queried without a device.
     (void)f32;
     const long target = kAttnTargetGroups;
+    const long quantum = kAttnSplitQuantum;
     long splits = (target + groups - 1) / groups;
-    const long max_by_tiles = (tok + kAttnTile - 1) / kAttnTile;
+    const long max_by_tiles = (tok + quantum - 1) / quantum;
     if (splits > max_by_tiles) splits = max_by_tiles;
     if (splits < 1) splits = 1;
     long tps = (tok + splits - 1) / splits;
-    tps = (tps + kAttnTile - 1) / kAttnTile * kAttnTile;
+    tps = (tps + quantum - 1) / quantum * quantum;
     if (tps > kAttnMaxTps) tps = kAttnMaxTps;
     splits = (tok + tps - 1) / tps;
     p.splits = (int)splits;
@@ -677,11 +646,14 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
 
 template <int D, int RB>
 static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
+    // 8 waves (two per SIMD hide the MFMA / LDS latency of the tile loop)
+    // unless a tile would then hold fewer DMA instructions than waves.
+    constexpr int NW = (D == 64 && RB == 4) ? 4 : (RB == 1 ? 4 : 8);
     const size_t dyn = (size_t)a.tps * sizeof(int);
     if (a.idx)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs, false>), grid, dim3(256), dyn, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, false>), grid, dim3(NW * 64), dyn, s, a);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, kAttnBufs, true>), grid, dim3(256), dyn, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, true>), grid, dim3(NW * 64), dyn, s, a);
     return hipGetLastError();
 }
 

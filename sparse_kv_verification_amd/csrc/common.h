@@ -45,6 +45,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Reduce across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+// (v_permlane32_swap / v_permlane16_swap would avoid the LDS round trip of
+// these shuffles, but made the attention output depend on timing in one
+// 4-wave configuration; the shuffles are deterministic.)
 __device__ __forceinline__ float group4_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
     return fmaxf(v, __shfl_xor(v, 32, 64));
@@ -79,6 +82,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Work-group barrier for hand-offs through LDS only.  __syncthreads() also
+// fences global memory, and on gfx950 that makes every wave wait for all of
+// its outstanding vector-memory operations, including global->LDS DMA issued
+// for later pipeline stages, at every barrier.  This barrier waits only for
+// the wave's own LDS accesses (lgkmcnt(0)); callers first wait, with
+// wait_vmcnt, for exactly the DMA the next stage reads.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Device-coherent ("agent scope") relaxed loads and stores.  On gfx950 they
 // are issued with the sc1 cache policy: stores write through the XCD-local
 // L2 and loads do not hit stale L2 lines, so data exchanged between
@@ -98,11 +115,6 @@ __device__ __forceinline__ void st_agent4(float *p, f32x4 v) {
 __device__ __forceinline__ f32x4 ld_agent4(const float *p) {
     return f32x4{ld_agent(p), ld_agent(p + 1), ld_agent(p + 2), ld_agent(p + 3)};
 }
-// 16-byte device-coherent store (global_store_dwordx4 with sc1).  Issued as
-// inline assembly, so the caller must wait_all_mem() before depending on it.
-__device__ __forceinline__ void st_agent_x4(float *p, f32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
-}
 // Device-coherent loads through a buffer resource: buffer_load with the sc1
 // cache policy reads the coherent copy (no stale XCD-local L2 line) while the
 // compiler schedules and overlaps them like ordinary loads.  Loads past
@@ -116,6 +128,13 @@ __device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 __device__ __forceinline__ f32x4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySc1));
+}
+// 16-byte device-coherent store: buffer_store_dwordx4 with the sc1 cache
+// policy writes through the XCD-local L2.  (A compiler builtin rather than
+// inline assembly: the compiler must see the store to keep its data
+// registers intact until the store has read them.)
+__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCachePolicySc1);
 }
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -230,6 +249,31 @@ __device__ __forceinline__ void ds_read_tr16_n4(const uint32_t (&a)[4], s16x4 (&
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 }
+// N x ds_read_b128 as inline asm.  The compiler treats any C++ read of an LDS
+// buffer that global->LDS DMA writes as possibly aliasing DMA still in
+// flight and waits for all outstanding vector-memory operations first; the
+// pipelined kernels order these reads themselves (wait_vmcnt + lds_barrier).
+__device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[4], u32x4 (&v)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+__device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[2], u32x4 (&v)[2]) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void ds_read_tr16_n(const uint32_t (&a)[N], s16x4 (&v)[N]) {
     static_assert(N == 8 || N == 4, "d tiles");

@@ -19,10 +19,11 @@ struct KvView {
 };
 
 // ---------------------------------------------------------------- attention
-constexpr int kAttnTile = 32;       // tokens per pipeline tile
-constexpr int kAttnMaxTps = 4096;   // tokens per split (row table in LDS)
-constexpr int kAttnBufs = 3;           // LDS ring depth (tiles)
-constexpr int kAttnTargetGroups = 512;  // work-groups the split planner aims for
+constexpr int kAttnTile = 32;            // tokens per tile (float32 kernel; bf16 minimum)
+constexpr int kAttnSplitQuantum = 128;   // bf16 splits hold a multiple of this many tokens
+constexpr int kAttnMaxTps = 4096;        // tokens per split (row table in LDS)
+constexpr int kAttnRingBytes = 128 * 1024;   // LDS of the bf16 kernel's K/V ring
+constexpr int kAttnTargetGroups = 256;   // bf16 work-groups the split planner aims for
 
 struct AttnPlan {
     int rows;      // R = w * G query rows per (sequence, KV head)
