@@ -329,11 +329,13 @@ struct DraftMfma {
 };
 
 // Statistics pass.  Persistent work-groups walk the items (b, unit u,
-// 1024-position chunk) round robin; each wave streams 256 positions in
+// 4096-position chunk) round robin; each wave streams 1024 positions in
 // groups of four 16-position subtiles, the next group's K fragments in
 // flight while the current group is reduced into per-lane running
-// (max, sum of exp2) pairs.
-constexpr int kDraftStatChunk = 1024;
+// (max, sum of exp2) pairs.  The first group (and the Q fragments) of the
+// work-group's next item are requested during the last group of the
+// current one, so the stream does not stall between items.
+constexpr int kDraftStatChunk = 4096;
 
 template <int D, int RB>
 __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
@@ -343,14 +345,32 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
     const int U = a.L_d * a.Hkv_d;
     const int nch = a.nchunk;                 // kDraftStatChunk-position chunks
     const int items = a.kv[0].B * U * nch;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int c = it % nch, u = (it / nch) % U, b = it / (nch * U);
-        const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
-        const KvView &kv = a.kv[l];
-        const int nb = sl_len(kv, b);
-        const int jw = c * kDraftStatChunk + wave * (kDraftStatChunk / 4);
-        bf16x8 qf[RB][M::KK];
-        M::load_q(a, b, l, kvh, lane, qf);
+    constexpr int NG = kDraftStatChunk / 4 / 64;   // 64-position groups per wave
+    static_assert(NG % 2 == 0, "groups are folded in pairs");
+    struct Item { int b, u, c, l, kvh, nb, jw; };
+    auto decode = [&](int it) {
+        Item x;
+        x.c = it % nch;
+        x.u = (it / nch) % U;
+        x.b = it / (nch * U);
+        x.l = x.u / a.Hkv_d;
+        x.kvh = x.u - x.l * a.Hkv_d;
+        x.nb = sl_len(a.kv[x.l], x.b);
+        x.jw = x.c * kDraftStatChunk + wave * (kDraftStatChunk / 4);
+        return x;
+    };
+    int it = blockIdx.x;
+    if (it >= items) return;
+    // two named operand sets keep the double buffer in registers
+    bf16x8 qf[RB][M::KK], qn[RB][M::KK];
+    bf16x8 kA[4][M::KK], kB[4][M::KK];
+    Item cur = decode(it);
+    M::load_q(a, cur.b, cur.l, cur.kvh, lane, qf);
+    M::load_k(a.kv[cur.l], cur.b, cur.kvh, cur.jw, cur.nb, lane, kA);
+    for (; it < items; it += gridDim.x) {
+        const int nxt_it = it + gridDim.x;
+        const Item nxt = decode(nxt_it < items ? nxt_it : it);
+        const KvView &kv = a.kv[cur.l];
         float mrun[RB][4], zrun[RB][4];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -359,12 +379,11 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
                 mrun[rb][i] = kNegInf;
                 zrun[rb][i] = 0.f;
             }
-        constexpr int NG = kDraftStatChunk / 4 / 64;   // 64-position groups per wave
         auto fold = [&](int gi, const bf16x8 (&k)[4][M::KK]) {
             f32x4 sc[4][RB];
             M::logits(qf, k, sc);
-            const int jg = jw + gi * 64;
-            const bool full = jg + 64 <= nb;
+            const int jg = cur.jw + gi * 64;
+            const bool full = jg + 64 <= cur.nb;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
                         float v = sc[st][rb][i] * a.scale_log2;
-                        if (!full && jg + st * 16 + (lane & 15) >= nb) v = kNegInf;
+                        if (!full && jg + st * 16 + (lane & 15) >= cur.nb) v = kNegInf;
                         sc[st][rb][i] = v;
                         mx = fmaxf(mx, v);
                     }
@@ -385,14 +404,16 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
                     zrun[rb][i] = z;
                 }
         };
-        // two named operand sets keep the double buffer in registers
-        bf16x8 kA[4][M::KK], kB[4][M::KK];
-        M::load_k(kv, b, kvh, jw, nb, lane, kA);
 #pragma unroll 1
         for (int gi = 0; gi < NG; gi += 2) {
-            M::load_k(kv, b, kvh, jw + (gi + 1) * 64, nb, lane, kB);
+            M::load_k(kv, cur.b, cur.kvh, cur.jw + (gi + 1) * 64, cur.nb, lane, kB);
             fold(gi, kA);
-            if (gi + 2 < NG) M::load_k(kv, b, kvh, jw + (gi + 2) * 64, nb, lane, kA);
+            if (gi + 2 < NG) {
+                M::load_k(kv, cur.b, cur.kvh, cur.jw + (gi + 2) * 64, cur.nb, lane, kA);
+            } else if (nxt_it < items) {   // prefetch the next item's first group
+                M::load_q(a, nxt.b, nxt.l, nxt.kvh, lane, qn);
+                M::load_k(a.kv[nxt.l], nxt.b, nxt.kvh, nxt.jw, nxt.nb, lane, kA);
+            }
             fold(gi + 1, kB);
         }
         // combine the 16 token lanes of each row, then the four waves
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
                     red[wave][r][1] = z;
                 }
             }
-        __syncthreads();
+        lds_barrier();   // the prefetch above stays in flight
         if (threadIdx.x < a.rows) {
             const int r = threadIdx.x;
             float mx = kNegInf;
@@ -419,11 +440,16 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
             float z = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) z += red[w][r][1] * __builtin_amdgcn_exp2f(red[w][r][0] - mu);
-            float *st = a.stat + ((((int64_t)b * U + u) * a.rows + r) * nch + c) * 2;
+            float *st = a.stat + ((((int64_t)cur.b * U + cur.u) * a.rows + r) * nch + cur.c) * 2;
             st[0] = mx;
             st[1] = z;
         }
-        __syncthreads();
+        lds_barrier();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kk = 0; kk < M::KK; ++kk) qf[rb][kk] = qn[rb][kk];
+        cur = nxt;
     }
 }
 
