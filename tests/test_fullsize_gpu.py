@@ -1,0 +1,110 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times: score -> select -> sparse attention (and the dense baseline) on the
+real shapes, checked against the oracle on sampled sequences (the oracle
+computes those one by one) and, for every sequence, through properties that
+hold at any size (score sums, bit-exact selection from the GPU's own scores).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_kv_verification_amd as dk
+from _util import check_set_tieband, f64, oracle_kv, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_step(sh, x, k):
+    """The bench step's calls (layer 0) with the library's own planning."""
+    n_sink, n_window, m = synth.tier_defaults(k)
+    kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
+    s_d, s_t = dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq)
+    idx, cnt, tier = dk.dustin_topk(s_d, s_t, x.seq_lens, k, m, n_sink, n_window)
+    out = dk.dustin_sparse_verify_attn(x.q, kv, idx, cnt)
+    torch.cuda.synchronize()
+    return (n_sink, n_window, m), kv, s_d, s_t, idx, cnt, tier, out
+
+
+def _check(sh, x, k, sample):
+    (n_sink, n_window, m), kv, s_d, s_t, idx, cnt, tier, out = _run_step(sh, x, k)
+    lens = x.seq_lens.cpu().numpy()
+    S, rows_d = len(x.sub_heads), sh.L_d * sh.H_d * sh.w
+    # every sequence: score sums and the selection rule on the GPU's own scores
+    sd_all, st_all = s_d.cpu().numpy(), s_t.cpu().numpy()
+    for b in range(sh.B):
+        n = int(lens[b])
+        assert abs(st_all[b, :n].astype(np.float64).sum() - S) < 1e-3 * S
+        assert abs(sd_all[b, :n].astype(np.float64).sum() - rows_d) < 1e-3 * rows_d
+        assert (st_all[b, n:] == 0).all() and (sd_all[b, n:] == 0).all()
+        I, T = oracle.select_verify_set(sd_all[b, :n], st_all[b, :n], n, k, m, n_sink, n_window)
+        c = int(cnt[b])
+        assert c == len(I) == min(k, n)
+        assert (idx[b, :c].cpu().numpy() == I).all(), f"b={b}: set differs from the rule on the GPU scores"
+        assert (tier[b, :c].cpu().numpy() == T).all()
+    # sampled sequences: scores, end-to-end set and attention against the oracle
+    for b in sample:
+        n = int(lens[b])
+        K = oracle_kv(x, "K", b)
+        st = oracle.score_target(f64(x.q_hist[b]), {0: K}, x.sub_heads, sh.Hq)
+        sd = oracle.score_draft(f64(x.q_draft[b]), oracle_kv(x, "Kd", b))
+        np.testing.assert_allclose(f64(s_t[b, :n]), st, rtol=2e-4, atol=1e-12)
+        np.testing.assert_allclose(f64(s_d[b, :n]), sd, rtol=2e-4, atol=1e-12)
+        oi, ot = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
+        c = int(cnt[b])
+        nd = check_set_tieband(idx[b, :c].cpu().numpy(), tier[b, :c].cpu().numpy(), oi, ot, sd, st)
+        I = idx[b, :c].cpu().numpy()
+        O, _ = oracle.sparse_attention(f64(x.q[b]), K, oracle_kv(x, "V", b), I)
+        err = np.abs(f64(out[b]) - O).max()
+        say(f"  b={b} n={n} k={k}: set diff {nd} (tie band), attention max|dO|={err:.2e}")
+        assert err <= 2e-2
+    return kv
+
+
+@pytest.mark.parametrize("k", [512, 1024, 2048])
+def test_c4_headline_step(k):
+    """72B-shaped headline workload (B=16, 32k, 64/8 heads) at each swept k."""
+    say("full-size c4 step, k =", k)
+    sh = synth.preset("c4").replace(k=k, layers=1)
+    x = synth.make(sh, device=DEV)
+    _check(sh, x, k, sample=[0, sh.B - 1])
+
+
+def test_c3_step_and_dense_baseline():
+    """32B-shaped workload, with the dense full-KV baseline on the same inputs."""
+    say("full-size c3 step + dense")
+    sh = synth.preset("c3")
+    x = synth.make(sh, device=DEV)
+    kv = _check(sh, x, sh.k, sample=[5])
+    lse = torch.empty((sh.B, sh.w, sh.Hq), dtype=torch.float32, device=DEV)
+    dense = dk.dustin_sparse_verify_attn(x.q, kv, None, None, lse=lse)
+    torch.cuda.synchronize()
+    for b in (0, 11):
+        n = int(x.seq_lens[b])
+        K, V = oracle_kv(x, "K", b), oracle_kv(x, "V", b)
+        O = oracle.dense_attention(f64(x.q[b]), K, V)
+        _, L = oracle.sparse_attention(f64(x.q[b]), K, V, np.arange(n))   # k = n: the dense LSE
+        err = np.abs(f64(dense[b]) - O).max()
+        lerr = np.abs(f64(lse[b]) - L).max()
+        say(f"  dense b={b}: max|dO|={err:.2e} max|dlse|={lerr:.2e}")
+        assert err <= 2e-2 and lerr <= 2e-3
+
+
+def test_c2_step():
+    """7B-shaped workload, every sequence sampled."""
+    say("full-size c2 step")
+    sh = synth.preset("c2")
+    x = synth.make(sh, device=DEV)
+    _check(sh, x, sh.k, sample=list(range(sh.B)))
+
+
+def test_c5_ragged_paged_step():
+    """Ragged paged stress (B=8, n in [8192, 131072], 16-token pages, w=8, k=4096)."""
+    say("full-size c5 step")
+    sh = synth.preset("c5")
+    x = synth.make(sh, device=DEV)
+    lens = x.seq_lens.cpu().numpy()
+    _check(sh, x, sh.k, sample=[int(np.argmin(lens)), int(np.argmax(lens))])
