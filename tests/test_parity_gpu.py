@@ -116,6 +116,7 @@ SELECT_CASES = [
     (dict(B=2, N=3000, k=700, m=700, ns=0, nw=0, ties=False), "draft-only"),
     (dict(B=4, N=1000, k=2048, m=100, ns=4, nw=32, ties=True), "k>=n"),
     (dict(B=1, N=131072, k=4096, m=2030, ns=4, nw=32, ties=False), "long"),
+    (dict(B=2, N=140000, k=1000, m=400, ns=4, nw=32, ties=True), "longer-than-registers"),
     (dict(B=2, N=2500, k=333, m=50, ns=8, nw=8, ties=True, no_draft=True), "no-draft"),
     (dict(B=2, N=2500, k=333, m=50, ns=8, nw=8, ties=True, no_target=True), "no-target"),
 ]
