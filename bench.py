@@ -47,7 +47,42 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="for counter collection: one warm step, a 1 GiB float32 copy (the calibration "
+                        "kernel of known size), then one more step; prints no JSON")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_c4_k2048_traffic.txt")
+TRAFFIC_SOURCES = ["sparse_kv_verification_amd/csrc/attn.hip", "sparse_kv_verification_amd/csrc/common.h",
+                   "sparse_kv_verification_amd/csrc/internal.h"]
+
+
+def attn_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per sparse-attention launch from the committed counter
+    summary, or None when the kernel sources changed after it was taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    a, b = line.split("=", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("source_sha256") != attn_source_digest():
+            return None
+        return {"bytes_per_launch": int(kv["hbm_bytes_per_launch"]),
+                "fetch_bytes": int(kv["fetch_bytes_per_launch"]), "write_bytes": int(kv["write_bytes_per_launch"])}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(sh, x, k_eff, counts, sub_heads):
@@ -71,26 +106,36 @@ def algorithmic_bytes(sh, x, k_eff, counts, sub_heads):
     }
 
 
-def cpu_baseline(sh, x, k, m, n_sink, n_window):
-    """Time the oracle (as it stands) on one sequence: scoring, selection and
-    one attention layer, then scale to a full step (B sequences, all layers)."""
+def cpu_baseline(sh, x, k, m, n_sink, n_window, budget_s=20.0):
+    """Time the oracle (as it stands) on whole sequences of the step: draft
+    and target scoring, selection and every attention layer of the sequence
+    (the layers hold identical copies, so one host copy serves all of them),
+    until about `budget_s` seconds of oracle time; scale to all B sequences."""
     import numpy as np
     import oracle
     f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
-    b = 0
-    n = int(x.seq_lens[b])
-    K, V = f(x.logical("K", b)), f(x.logical("V", b))
-    Kd = f(x.logical("Kd", b))
-    qd, qh, q = f(x.q_draft[b]), f(x.q_hist[b]), f(x.q[b])
-    t0 = time.perf_counter()
-    sd = oracle.score_draft(qd, Kd)
-    st = oracle.score_target(qh, {0: K}, x.sub_heads, sh.Hq)
-    t1 = time.perf_counter()
-    I, _ = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
-    t2 = time.perf_counter()
-    oracle.sparse_attention(q, K, V, I)
-    t3 = time.perf_counter()
-    per_seq = (t1 - t0) + (t2 - t1) + sh.layers * (t3 - t2)
+    done, total = 0, {"score": 0.0, "select": 0.0, "attention": 0.0}
+    for b in range(sh.B):
+        n = int(x.seq_lens[b])
+        K, V = f(x.logical("K", b)), f(x.logical("V", b))
+        Kd = f(x.logical("Kd", b))
+        qd, qh, q = f(x.q_draft[b]), f(x.q_hist[b]), f(x.q[b])
+        t0 = time.perf_counter()
+        sd = oracle.score_draft(qd, Kd)
+        st = oracle.score_target(qh, {0: K}, x.sub_heads, sh.Hq)
+        t1 = time.perf_counter()
+        I, _ = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
+        t2 = time.perf_counter()
+        for _ in range(sh.layers):
+            oracle.sparse_attention(q, K, V, I)
+        t3 = time.perf_counter()
+        total["score"] += t1 - t0
+        total["select"] += t2 - t1
+        total["attention"] += t3 - t2
+        done += 1
+        del K, V, Kd
+        if sum(total.values()) >= budget_s:
+            break
     threads = None
     try:
         import threadpoolctl
@@ -98,14 +143,15 @@ def cpu_baseline(sh, x, k, m, n_sink, n_window):
         threads = max((i.get("num_threads", 1) for i in info), default=1)
     except Exception:
         threads = os.cpu_count()
+    measured = sum(total.values())
     return {
-        "value": per_seq * sh.B * 1e6,
+        "value": measured / done * sh.B * 1e6,
         "unit": "us/step",
         "cores": int(threads or 1),
         "kind": "oracle",
-        "sample": (f"sequence 0 of {sh.B} (n={n}): score_draft + score_target + select + 1 of {sh.layers} "
-                   f"attention layers, fp64 NumPy; scaled x{sh.B} sequences and x{sh.layers} layers"),
-        "measured_s": {"score": t1 - t0, "select": t2 - t1, "attn_1_layer": t3 - t2},
+        "sample": (f"sequences 0..{done - 1} of {sh.B} (n={sh.n}), each: score_draft + score_target + select + "
+                   f"all {sh.layers} attention layers, fp64 NumPy; {measured:.1f} s measured, scaled x{sh.B / done:g}"),
+        "measured_s": {a: round(b, 3) for a, b in total.items()},
         "host_cpu": platform.processor() or platform.machine(),
         "host_cpu_count": os.cpu_count(),
     }
@@ -173,6 +219,18 @@ def main():
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
+    if args.pmc_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log("pmc probe: calibration copy of 1073741824 bytes (read + write)")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc probe: one step")
+        step()
+        torch.cuda.synchronize()
+        log("pmc probe done")
+        return
     bytes_ = algorithmic_bytes(sh, x, k, cnt, x.sub_heads)
     stream = torch.cuda.current_stream()
 
@@ -257,6 +315,7 @@ def main():
         log(f"dense attention {dense_us:.1f} us/step ({dense['GBps']:.0f} GB/s), "
             f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster")
 
+    traffic = measured_traffic()
     step_gbps = bytes_["step"] / step_us / 1e3
     attn_gbps = bytes_["attn_per_layer"] / attn_launch_us / 1e3
     res = {
@@ -295,7 +354,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes_per_launch": bytes_["attn_per_layer"],
         },
         "dense_baseline": dense,
