@@ -199,10 +199,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int bg = blockIdx.x / a.splits;
     const int b = bg / a.kv.Hkv, g = bg - (bg / a.kv.Hkv) * a.kv.Hkv;
 
-    const int nb = seq_len(a.kv, b);
-    const int cnt = DENSE ? nb : min(max(a.count[b], 0), a.k);
+    // Every load of the prologue is independent of the others, so they are
+    // all in flight together: sequence length, count, Q and the split's
+    // index entries (read up to the k bound; the count masks them after).
+    const int nb_raw = a.kv.seq_lens[b];
+    const int cnt_raw = DENSE ? 0 : a.count[b];
     const int t0 = split * a.tps;
-    const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
 
     if (tid == 0) s_flag = 0;
     // Q^T operand fragments of this wave's row block: lane holds row
@@ -221,16 +223,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.f;
         }
     }
-    lds_barrier();   // s_flag cleared; the Q loads stay in flight
-    bool any_bad = false;
-    {   // physical row of every token of the split; all loads issued first
-        constexpr int PER = kAttnMaxTps / NT;
-        int jv[PER];
+    constexpr int PER = kAttnMaxTps / NT;
+    int jv[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int t = tid + NT * i;
-            jv[i] = (t < ntok) ? (DENSE ? t0 + t : a.idx[(int64_t)b * a.k + t0 + t]) : -1;
-        }
+    for (int i = 0; i < PER; ++i) {
+        const int t = tid + NT * i;
+        jv[i] = DENSE ? t0 + t : ((t < a.tps && t0 + t < a.k) ? a.idx[(int64_t)b * a.k + t0 + t] : -1);
+    }
+    const int nb = min(max(nb_raw, 0), a.kv.N_max);
+    const int cnt = DENSE ? nb : min(max(cnt_raw, 0), a.k);
+    const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
+    lds_barrier();   // s_flag cleared; the loads stay in flight
+    bool any_bad = false;
+    {   // physical row of every token of the split
         // paged caches: every page-table entry is requested before any is used
         int pg[PER];
 #pragma unroll
