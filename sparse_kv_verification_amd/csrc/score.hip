@@ -54,7 +54,7 @@ __device__ __forceinline__ void load_slice(const char *row, int slice, float (&x
         for (int i = 0; i < 8; ++i) x[i] = 0.f;
         return;
     }
-    const u32x4 v = *(const u32x4 *)(row + slice * 16);
+    const u32x4 v = ld_stream16(row + slice * 16);
     if constexpr (F32) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v[i]);
@@ -276,28 +276,45 @@ struct DraftMfma {
     static constexpr int KK = D / 32;
 
     // Q operand fragments of unit (l, c): row rb*16 + (lane&15), d slice kk*32 + (lane>>4)*8.
+    // Branch-free: padding rows load row 0 and are zeroed by a select, so
+    // every lane issues the same loads and the compiler can count them (a
+    // load skipped on some paths makes every later wait a full drain).
     static __device__ __forceinline__ void load_q(const DraftScoreArgs &a, int b, int l, int c, int lane,
                                                   bf16x8 (&qf)[RB][KK]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int r = rb * 16 + (lane & 15);
+            const bool ok = r < a.rows;
+            const int rr = ok ? r : 0;
+            const int gs = rr / a.G_d, hh = rr - (rr / a.G_d) * a.G_d;
+            const uint16_t *qp = (const uint16_t *)a.q_draft +
+                ((((int64_t)b * a.L_d + l) * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + (lane >> 4) * 8;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                if (r < a.rows) {
-                    const int gs = r / a.G_d, hh = r - (r / a.G_d) * a.G_d;
-                    const uint16_t *qp = (const uint16_t *)a.q_draft +
-                        ((((int64_t)b * a.L_d + l) * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + kk * 32 + (lane >> 4) * 8;
-                    qf[rb][kk] = *(const bf16x8 *)qp;
-                } else {
-                    for (int i = 0; i < 8; ++i) qf[rb][kk][i] = (__bf16)0.f;
-                }
+                const u32x4 v = *(const u32x4 *)(qp + kk * 32);
+                qf[rb][kk] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{0u, 0u, 0u, 0u});
             }
         }
     }
 
-    // K^T operand fragments of 4 subtiles (64 positions from j_base).
+    // K^T operand fragments of 4 subtiles (64 positions from j_base).  For a
+    // contiguous cache the loads are branch-free (positions past n_b read a
+    // valid row and are masked by the caller); a paged cache looks the page
+    // up first.
     static __device__ __forceinline__ void load_k(const KvView &kv, int b, int c, int j_base, int nb, int lane,
                                                   bf16x8 (&kf)[4][KK]) {
+        if (kv.page_size == 0) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int j = j_base + st * 16 + (lane & 15);
+                const int jj = (j < nb) ? j : 0;
+                const char *row = kv.k + ((((int64_t)b * kv.N_max + jj) * kv.Hkv + c) * D) * 2;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    kf[st][kk] = *(const bf16x8 *)(row + (kk * 32 + (lane >> 4) * 8) * 2);
+            }
+            return;
+        }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int j = j_base + st * 16 + (lane & 15);
@@ -459,60 +476,107 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
 // registers without atomics.
 constexpr int kDraftAccChunk = 256;
 
-template <int D, int RB>
+template <int D, int RB, bool PAGED>
 __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
+    constexpr int KK = M::KK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int U = a.L_d * a.Hkv_d;
-    const int N = a.kv[0].N_max;
+    const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
+    const int N = k0.N_max;
     const int nch = (N + kDraftAccChunk - 1) / kDraftAccChunk;
-    const int items = a.kv[0].B * nch;
+    const int items = k0.B * nch;
+    // per-lane parts of the Q addresses (row rb*16 + (lane & 15)) and of the
+    // normaliser index (rows rb*16 + (lane >> 4)*4 + i); padding rows read
+    // row 0 and are masked
+    int qoff[RB];
+    bool qok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        qok[rb] = r < a.rows;
+        const int rr = qok[rb] ? r : 0;
+        qoff[rb] = ((rr / a.G_d) * a.H_d + (rr - (rr / a.G_d) * a.G_d)) * D + (lane >> 4) * 8;
+    }
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int c = it % nch, b = it / nch;
         const int jb = c * kDraftAccChunk + wave * 64;
+        const int nb = sl_len(k0, b);
         const float *lse_b = a.lse + (int64_t)b * U * a.rows;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        // two operand sets, A and B, named separately so that they stay in
-        // registers (a runtime-indexed pair would live in scratch memory)
-        bf16x8 qA[RB][M::KK], qB[RB][M::KK];
-        bf16x8 kA[4][M::KK], kB[4][M::KK];
+        // byte offset of this lane's K row in a layer, per subtile (positions
+        // past n_b read row 0 of the sequence and are masked)
+        int64_t koff[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int j = jb + st * 16 + (lane & 15);
+            koff[st] = (((int64_t)b * N + (j < nb ? j : 0)) * k0.Hkv * D + (lane >> 4) * 8) * 2;
+        }
+        // Operands in two named sets, one unit in flight while the other is
+        // folded (a third set measured no faster).  Named sets stay in
+        // registers; a runtime-indexed set would live in scratch memory.
+        // Past the last unit the loads repeat the last unit (never folded),
+        // so every load is unconditional and the compiler's waits stay exact.
+        bf16x8 qA[RB][KK], qB[RB][KK];
+        bf16x8 kA[4][KK], kB[4][KK];
         float lA[RB][4], lB[RB][4];
-        auto load_unit = [&](int u, bf16x8 (&q)[RB][M::KK], bf16x8 (&k)[4][M::KK], float (&ls)[RB][4]) {
+        auto load_k = [&](int u, bf16x8 (&k)[4][KK]) {
+            u = (u < U) ? u : U - 1;
             const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
-            const KvView &kv = a.kv[l];
-            M::load_q(a, b, l, kvh, lane, q);
-            M::load_k(kv, b, kvh, jb, sl_len(kv, b), lane, k);
+            if constexpr (PAGED) {
+                M::load_k(a.kv[l], b, kvh, jb, nb, lane, k);
+            } else {
+                const char *base = a.kv[l].k + (int64_t)kvh * D * 2;
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) k[st][kk] = *(const bf16x8 *)(base + koff[st] + kk * 64);
+            }
+        };
+        auto load_ql = [&](int u, bf16x8 (&q)[RB][KK], float (&ls)[RB][4]) {
+            u = (u < U) ? u : U - 1;
+            const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
+            const uint16_t *qb = (const uint16_t *)a.q_draft +
+                ((((int64_t)b * a.L_d + l) * a.gamma) * a.H_d + kvh * a.G_d) * D;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const u32x4 v = *(const u32x4 *)(qb + qoff[rb] + kk * 32);
+                    q[rb][kk] = __builtin_bit_cast(bf16x8, qok[rb] ? v : u32x4{0u, 0u, 0u, 0u});
+                }
+            const float *lu = lse_b + (int64_t)u * a.rows;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rb * 16 + (lane >> 4) * 4 + i;
-                    ls[rb][i] = (r < a.rows) ? lse_b[(int64_t)u * a.rows + r] : __builtin_huge_valf();
+                    const float v = lu[r < a.rows ? r : 0];
+                    ls[rb][i] = (r < a.rows) ? v : __builtin_huge_valf();
                 }
         };
-        auto fold_unit = [&](int u, const bf16x8 (&q)[RB][M::KK], const bf16x8 (&k)[4][M::KK],
-                             const float (&ls)[RB][4]) {
-            const int nb = sl_len(a.kv[u / a.Hkv_d], b);
-            f32x4 sc[4][RB];
-            M::logits(q, k, sc);
+        auto fold_unit = [&](int u, const bf16x8 (&q)[RB][KK], const bf16x8 (&k)[4][KK], const float (&ls)[RB][4]) {
+            if (u >= U) return;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int st = 0; st < 4; ++st) {   // one subtile's logits live at a time
                 float t = 0.f;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb) {
+                    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) t += __builtin_amdgcn_exp2f(sc[st][rb][i] * a.scale_log2 - ls[rb][i]);
+                    for (int kk = 0; kk < KK; ++kk)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[rb][kk], k[st][kk], sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) t += __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
+                }
                 if (jb + st * 16 + (lane & 15) < nb) acc[st] += t;
             }
         };
-        load_unit(0, qA, kA, lA);
+        load_k(0, kA);
+        load_ql(0, qA, lA);
         for (int u = 0; u < U; u += 2) {
-            if (u + 1 < U) load_unit(u + 1, qB, kB, lB);
-            fold_unit(u, qA, kA, lA);
-            if (u + 1 < U) {
-                if (u + 2 < U) load_unit(u + 2, qA, kA, lA);
-                fold_unit(u + 1, qB, kB, lB);
-            }
+            load_ql(u + 1, qB, lB); load_k(u + 1, kB); fold_unit(u + 0, qA, kA, lA);
+            load_ql(u + 2, qA, lA); load_k(u + 2, kA); fold_unit(u + 1, qB, kB, lB);
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -676,8 +740,9 @@ static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
-    hipLaunchKernelGGL((draft_acc_mfma<D, RB>), dim3(acc_items < kScoreGroups ? acc_items : kScoreGroups),
-                       dim3(256), 0, s, b);
+    const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
+    if (k0.page_size != 0) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true>), grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((draft_acc_mfma<D, RB, false>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
