@@ -16,7 +16,9 @@ Decoding", arXiv 2606.24957):
   S_Draft over H_d, L_d, Gamma; S_Target over H_t, L_t; one global index
   set), section 2.3 (verification set: protected sink + recent window, draft
   top-m, target fill), section 2.4 (scoring restricted to a few semantic
-  retrieval heads), Fig. 5 (Stage 2: attention over the compressed KV only).
+  retrieval heads), Fig. 5 (Stage 2: the target verifies the draft tokens
+  with the compressed KV; accepted tokens are written back to the target KV,
+  rejected ones are dropped).
 
 The pages print the S_Draft / S_Target and verification-set formulas only as
 prose (the formula slots of the blog are empty).  The readings taken here are
@@ -49,6 +51,9 @@ __all__ = [
     "window_attention",
     "dense_attention",
     "sparse_attention",
+    "verify_attention",
+    "append_window_kv",
+    "commit_window",
     "arr_step",
     "arr_window",
     "sd_oracle",
@@ -161,6 +166,61 @@ def sparse_attention(q, K, V, I, scale=None):
         O[:, h, :] = (e / z) @ Vs[:, g, :]
         lse[:, h] = (m + np.log(z))[:, 0]
     return O, lse
+
+
+def verify_attention(q, K, V, K_win, V_win, I, scale=None):
+    """Stage 2 of blog Fig. 5 with the draft window itself in view: the w
+    draft tokens are verified in one pass, and draft token s sees the
+    compressed history I plus the draft tokens 0..s (the usual causal order
+    inside a speculative window; the pages leave this block implicit, and
+    this is its plainest reading).
+
+    K_win, V_win [w][Hkv][d]: the window tokens' keys and values.
+    O[s][h] = softmax over (I u window[0..s]) of scale * q[s][h] . k, times v.
+    Returns O [w][Hq][d] and lse [w][Hq] (natural log).
+    """
+    I = np.asarray(I, dtype=np.int64)
+    I = I[I >= 0]
+    q = _f64(q)
+    w, Hq, d = q.shape
+    Kh, Vh = _f64(K)[I], _f64(V)[I]
+    Kw, Vw = _f64(K_win), _f64(V_win)
+    Hkv = Kw.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    O = np.zeros((w, Hq, Vw.shape[2]))
+    lse = np.zeros((w, Hq))
+    for s in range(w):
+        for h in range(Hq):
+            g = _kv_head_of(h, Hq, Hkv)
+            keys = np.concatenate([Kh[:, g, :], Kw[: s + 1, g, :]], axis=0)
+            vals = np.concatenate([Vh[:, g, :], Vw[: s + 1, g, :]], axis=0)
+            logits = scale * (keys @ q[s, h, :])
+            m = logits.max()
+            e = np.exp(logits - m)
+            z = e.sum()
+            O[s, h, :] = (e / z) @ vals
+            lse[s, h] = m + np.log(z)
+    return O, lse
+
+
+def append_window_kv(K, V, n, K_win, V_win):
+    """The draft tokens' keys and values go into the cache right after the
+    history (positions n .. n + w - 1) before they are verified; positions
+    past the cache end are dropped.  Returns new arrays (K, V of [N][Hkv][d])."""
+    K, V = np.array(K, copy=True), np.array(V, copy=True)
+    for t in range(np.asarray(K_win).shape[0]):
+        if n + t < K.shape[0]:
+            K[n + t] = K_win[t]
+            V[n + t] = V_win[t]
+    return K, V
+
+
+def commit_window(n, accepted, w):
+    """After verification the accepted draft tokens stay in the cache (blog
+    Fig. 5): the history grows by the accepted count, clamped to [0, w]; the
+    rows of rejected tokens lie past the new length and are never read."""
+    return n + min(max(int(accepted), 0), w)
 
 
 def arr_step(A, I):

@@ -363,3 +363,87 @@ def test_pages_identity_and_permuted():
     pool2 = np.empty_like(pool)
     pool2[perm] = pool
     np.testing.assert_array_equal(oracle.pages_to_contiguous(pool2, perm, n, ps), logical[:n])
+
+
+# ---------------------------------------------------------------- verification window (blog Fig. 5, Stage 2)
+def _window_case(seed, w=4, Hq=8, Hkv=2, d=16, n=30):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(w, Hq, d)), rng.normal(size=(n, Hkv, d)) * 1.5, rng.normal(size=(n, Hkv, d)),
+            rng.normal(size=(w, Hkv, d)) * 1.5, rng.normal(size=(w, Hkv, d)))
+
+
+def test_verify_attention_matches_causally_masked_sdpa():
+    # history set I plus the window: query s sees I and window tokens 0..s
+    q, K, V, Kw, Vw = _window_case(11)
+    w, n = q.shape[0], K.shape[0]
+    I = np.sort(np.random.default_rng(5).choice(n, 9, replace=False))
+    O, lse = oracle.verify_attention(q, K, V, Kw, Vw, np.concatenate([I, [-1]]))
+    Kc, Vc = np.concatenate([K, Kw]), np.concatenate([V, Vw])
+    mask = torch.zeros(w, n + w, dtype=torch.bool)
+    mask[:, torch.from_numpy(I)] = True
+    for s in range(w):
+        mask[s, n:n + s + 1] = True
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(Kc).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(Vc).permute(1, 0, 2)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None], enable_gqa=True)
+    np.testing.assert_allclose(O, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    Hq, Hkv, d = q.shape[1], K.shape[1], q.shape[2]
+    for s in range(w):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = np.concatenate([K[I, g], Kw[:s + 1, g]])
+            np.testing.assert_allclose(lse[s, h], scipy.special.logsumexp(keys @ q[s, h] / math.sqrt(d)), rtol=1e-13)
+
+
+def test_verify_attention_without_history_is_causal_self_attention():
+    q, K, V, Kw, Vw = _window_case(12)
+    O, _ = oracle.verify_attention(q, K, V, Kw, Vw, [])
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(Kw).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(Vw).permute(1, 0, 2)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(O, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_verify_attention_uniform_keys_average_the_visible_values():
+    # identical keys -> uniform softmax: step s averages |I| + s + 1 value rows
+    w, Hq, Hkv, d, n = 4, 4, 1, 8, 12
+    rng = np.random.default_rng(13)
+    key = rng.normal(size=d)
+    K = np.tile(key, (n, Hkv, 1))
+    Kw = np.tile(key, (w, Hkv, 1))
+    V = rng.normal(size=(n, Hkv, d))
+    Vw = rng.normal(size=(w, Hkv, d))
+    q = rng.normal(size=(w, Hq, d))
+    I = np.array([0, 3, 7])
+    O, lse = oracle.verify_attention(q, K, V, Kw, Vw, I)
+    for s in range(w):
+        expect = np.concatenate([V[I, 0], Vw[:s + 1, 0]]).mean(axis=0)
+        for h in range(Hq):
+            np.testing.assert_allclose(O[s, h], expect, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[s, h], key @ q[s, h] / math.sqrt(d) + math.log(len(I) + s + 1), rtol=1e-12)
+
+
+def test_single_step_window_is_sparse_attention_over_appended_row():
+    # w = 1: the draft token sees I plus itself, i.e. the set I u {n} of the
+    # cache after the window row is appended at position n
+    q, K, V, Kw, Vw = _window_case(14, w=1)
+    n = K.shape[0]
+    I = np.array([2, 5, 9, 20])
+    O, lse = oracle.verify_attention(q, K, V, Kw, Vw, I)
+    Ka, Va = oracle.append_window_kv(np.concatenate([K, np.zeros((1,) + K.shape[1:])]),
+                                     np.concatenate([V, np.zeros((1,) + V.shape[1:])]), n, Kw, Vw)
+    O2, lse2 = oracle.sparse_attention(q, Ka, Va, np.concatenate([I, [n]]))
+    np.testing.assert_allclose(O, O2, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-13)
+
+
+def test_append_and_commit_window():
+    K = np.zeros((10, 1, 2))
+    V = np.zeros((10, 1, 2))
+    Kw = np.arange(8.0).reshape(4, 1, 2)
+    Ka, Va = oracle.append_window_kv(K, V, 7, Kw, -Kw)
+    assert (Ka[:7] == 0).all() and (Ka[7:10] == Kw[:3]).all() and (Va[7:10] == -Kw[:3]).all()   # row n+3 falls off
+    assert oracle.commit_window(7, 2, 4) == 9
+    assert oracle.commit_window(7, 9, 4) == 11 and oracle.commit_window(7, -1, 4) == 7
