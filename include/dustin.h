@@ -11,6 +11,10 @@
  *                                        -> dustin_topk
  *   3. grouped-query attention of the w window tokens over the selected
  *      K/V rows only                     -> dustin_sparse_verify_attn
+ *      (history only) or dustin_verify_attn (history set plus the window's
+ *      own rows, causally), with dustin_append_window_kv writing the window
+ *      into the cache first and dustin_commit_window keeping the accepted
+ *      tokens afterwards
  *   plus the evaluator of the translation's section 3.1 (attention recovery
  *   rate):                               -> dustin_window_attn, dustin_arr
  *
@@ -29,8 +33,8 @@
  *   [0, N_max], index entries outside [0, n_b) and page ids outside
  *   [0, num_pages) are treated as absent (never dereferenced).
  * - Workspace: pass at least the byte count the matching *_workspace_bytes()
- *   function returns for the same shape.  dustin_sparse_verify_attn and
- *   dustin_window_attn keep arrival counters at the start of their workspace:
+ *   function returns for the same shape.  dustin_sparse_verify_attn,
+ *   dustin_verify_attn and dustin_window_attn keep arrival counters at the start of their workspace:
  *   it must be zero-filled before its first use, every call leaves it zero
  *   again, and it must not be handed to another entry point in between.
  *   The other entry points make no assumption about workspace contents.
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 1
+#define DUSTIN_ABI_VERSION 2
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -190,6 +194,59 @@ dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q,
 /* k_or_n: the k passed to the call, or N_max for the dense (idx == NULL) form. */
 size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv,
                                    int32_t head_dim, int32_t k_or_n);
+
+/*
+ * dustin_append_window_kv -- writes the w draft tokens' keys and values into
+ * the target cache right after each history, as Stage 2 of the blog's Fig. 5
+ * does before verifying them: row n_b + t of sequence b receives
+ * k_win[b][t] / v_win[b][t] for t < w.  seq_lens is read, not changed.
+ *
+ *  kv     k and v required; rows at positions >= N_max are not written
+ *         (the caller keeps N_max >= n_b + w), and in a paged cache a
+ *         position whose page id is outside [0, num_pages) is skipped
+ *  k_win  [B][w][H_kv][head_dim], kv dtype
+ *  v_win  [B][w][H_kv][head_dim], kv dtype
+ * kv->k, kv->v, k_win and v_win must be 16-byte aligned.
+ */
+dustin_status dustin_append_window_kv(const dustin_kv *kv, const void *k_win, const void *v_win,
+                                      int32_t w, dustin_stream_t stream);
+
+/*
+ * dustin_verify_attn -- the whole attention of one verification step (blog,
+ * Fig. 5, Stage 2): window query s of sequence b attends the selected
+ * history rows I_b and the window's own rows n_b .. n_b + s (already in the
+ * cache through dustin_append_window_kv), i.e. a causal block over the
+ * window:
+ *   J_{b,s} = I_b  U  { n_b + t : 0 <= t <= s }
+ *   O[b][s][h]   = sum_{j in J_{b,s}} softmax_j(scale * q[b][s][h] . K[b][j][h/G]) V[b][j][h/G]
+ *   lse[b][s][h] = ln sum_{j in J_{b,s}} exp(scale * q[b][s][h] . K[b][j][h/G])
+ * Arguments, layouts and errors as for dustin_sparse_verify_attn; idx ==
+ * NULL gives the dense form I_b = { j < n_b } (the "Full Cache" step).
+ * Index entries at or past n_b are ignored (the window rows are added by
+ * the call itself), and window rows at positions >= N_max are left out.
+ * Workspace: dustin_verify_attn_workspace_bytes for the same shape.
+ */
+dustin_status dustin_verify_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                 const int32_t *idx, const int32_t *count, int32_t k, float scale,
+                                 void *out, float *lse, void *ws, size_t ws_bytes,
+                                 dustin_stream_t stream);
+
+/* k_or_n: the k passed to the call, or N_max for the dense (idx == NULL) form. */
+size_t dustin_verify_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv,
+                                          int32_t head_dim, int32_t k_or_n);
+
+/*
+ * dustin_commit_window -- the end of a verification step (blog, Fig. 5,
+ * Stage 2): the accepted tokens' rows stay in the cache and the rejected
+ * ones are dropped, so seq_lens[b] += clamp(accepted[b], 0, w).  The rows of
+ * rejected tokens then lie past the new length and are overwritten by the
+ * next dustin_append_window_kv.
+ *
+ *  seq_lens  [B] int32, updated in place
+ *  accepted  [B] int32 accepted-token counts
+ */
+dustin_status dustin_commit_window(int32_t *seq_lens, const int32_t *accepted, int32_t B,
+                                   int32_t w, dustin_stream_t stream);
 
 /*
  * dustin_window_attn -- the full-cache attention weights A_{i+s,j} of the

@@ -22,6 +22,8 @@ EXPORTS = [
     "dustin_score", "dustin_score_workspace_bytes",
     "dustin_topk", "dustin_topk_workspace_bytes",
     "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes",
+    "dustin_verify_attn", "dustin_verify_attn_workspace_bytes",
+    "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
     "dustin_arr",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
@@ -73,6 +75,14 @@ def lib():
         L.dustin_sparse_verify_attn.restype = ctypes.c_int
         L.dustin_attn_workspace_bytes.argtypes = [i32] * 6
         L.dustin_attn_workspace_bytes.restype = sz
+        L.dustin_verify_attn.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.dustin_verify_attn.restype = ctypes.c_int
+        L.dustin_verify_attn_workspace_bytes.argtypes = [i32] * 6
+        L.dustin_verify_attn_workspace_bytes.restype = sz
+        L.dustin_append_window_kv.argtypes = [kvp, vp, vp, i32, vp]
+        L.dustin_append_window_kv.restype = ctypes.c_int
+        L.dustin_commit_window.argtypes = [vp, vp, i32, i32, vp]
+        L.dustin_commit_window.restype = ctypes.c_int
         L.dustin_window_attn.argtypes = [vp, i32, i32, kvp, f32, vp, vp, sz, vp]
         L.dustin_window_attn.restype = ctypes.c_int
         L.dustin_window_attn_workspace_bytes.argtypes = [i32] * 6
@@ -188,6 +198,38 @@ def dustin_sparse_verify_attn(q, kv: KV, idx=None, count=None, k=None, scale=0.0
     _check(lib().dustin_sparse_verify_attn(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
                                            _ptr(out), _ptr(lse), _ptr(wsb), wsb.numel(), _stream(q)))
     return out
+
+
+def dustin_verify_attn(q, kv: KV, idx=None, count=None, k=None, scale=0.0,
+                       out=None, lse=None, ws: Workspace | None = None):
+    """Attention of one verification step: window query s attends the
+    selected history rows idx[b][:count[b]] (all j < n_b when idx is None)
+    and the window's own cache rows n_b .. n_b + s.  q: [B][w][H_q][d]."""
+    B, w, Hq, D = q.shape
+    kk = 0 if idx is None else (k if k is not None else idx.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    d = kv.desc
+    nbytes = lib().dustin_verify_attn_workspace_bytes(d.B, w, Hq, d.H_kv, d.head_dim,
+                                                      kk if idx is not None else d.N_max)
+    wsb = _ws("verify", ws, nbytes, q.device)
+    _check(lib().dustin_verify_attn(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
+                                    _ptr(out), _ptr(lse), _ptr(wsb), wsb.numel(), _stream(q)))
+    return out
+
+
+def dustin_append_window_kv(kv: KV, k_win, v_win):
+    """Write the window's keys/values ([B][w][H_kv][d] each) into cache rows
+    n_b .. n_b + w - 1; the sequence lengths are not changed."""
+    w = k_win.shape[1]
+    _check(lib().dustin_append_window_kv(kv.ref, _ptr(k_win), _ptr(v_win), w, _stream(k_win)))
+
+
+def dustin_commit_window(seq_lens, accepted, w):
+    """seq_lens[b] += clamp(accepted[b], 0, w), in place."""
+    B = seq_lens.shape[0]
+    _check(lib().dustin_commit_window(_ptr(seq_lens), _ptr(accepted), B, int(w), _stream(seq_lens)))
+    return seq_lens
 
 
 def dustin_score(draft_kvs, q_draft, target_kvs, q_hist, sub_heads, H_t, s_draft=None, s_target=None,

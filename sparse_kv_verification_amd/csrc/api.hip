@@ -144,26 +144,32 @@ size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_
     return attn_plan(B, w, H_q, H_kv, head_dim, k_or_n, false).ws_bytes;
 }
 
-dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
-                                        const int32_t *idx, const int32_t *count, int32_t k, float scale,
-                                        void *out, float *lse, void *ws, size_t ws_bytes,
-                                        dustin_stream_t stream) {
-    dustin_status st = check_kv(kv, "sparse_verify_attn kv", true);
+}  // extern "C"
+
+namespace {
+// Shared body of dustin_sparse_verify_attn (causal = 0) and dustin_verify_attn
+// (causal = 1: the w window rows after each history are attended causally).
+dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                        const int32_t *idx, const int32_t *count, int32_t k, float scale, void *out, float *lse,
+                        void *ws, size_t ws_bytes, dustin_stream_t stream, int causal) {
+    char what[96];
+    snprintf(what, sizeof what, "%s kv", name);
+    dustin_status st = check_kv(kv, what, true);
     if (st != DUSTIN_OK) return st;
-    if ((st = check_attn_shape(kv, w, H_q, "sparse_verify_attn")) != DUSTIN_OK) return st;
-    CHECK(q != nullptr && out != nullptr, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: q and out are required");
+    if ((st = check_attn_shape(kv, w, H_q, name)) != DUSTIN_OK) return st;
+    CHECK(q != nullptr && out != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: q and out are required", name);
     if (idx) {
-        CHECK(count != nullptr, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: count is NULL");
-        CHECK(k >= 1, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: k must be >= 1 (got %d)", k);
+        CHECK(count != nullptr, DUSTIN_ERR_INVALID_ARG, "%s: count is NULL", name);
+        CHECK(k >= 1, DUSTIN_ERR_INVALID_ARG, "%s: k must be >= 1 (got %d)", name, k);
     } else {
-        CHECK(k == 0, DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: dense form (idx NULL) needs k == 0");
+        CHECK(k == 0, DUSTIN_ERR_INVALID_ARG, "%s: dense form (idx NULL) needs k == 0", name);
     }
-    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "sparse_verify_attn: scale is not finite");
-    const int tokens = idx ? k : kv->N_max;
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "%s: scale is not finite", name);
+    const int tokens = (idx ? k : kv->N_max) + (causal ? w : 0);
     const AttnPlan p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
-    CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "sparse_verify_attn: too many tokens");
+    CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "%s: too many tokens", name);
     CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
-          "sparse_verify_attn: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+          "%s: workspace of %zu bytes needed (got %zu)", name, p.ws_bytes, ws_bytes);
     AttnArgs a{};
     a.kv = view_of(kv);
     a.q = q;
@@ -185,7 +191,50 @@ dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q, c
     a.splits = p.splits;
     a.tps = p.tps;
     a.rpad = p.rpad;
-    return hip_status(launch_attn(a, p, (hipStream_t)stream), "sparse_verify_attn launch");
+    a.causal = causal;
+    snprintf(what, sizeof what, "%s launch", name);
+    return hip_status(launch_attn(a, p, (hipStream_t)stream), what);
+}
+}  // namespace
+
+extern "C" {
+
+dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                        const int32_t *idx, const int32_t *count, int32_t k, float scale,
+                                        void *out, float *lse, void *ws, size_t ws_bytes,
+                                        dustin_stream_t stream) {
+    return attn_call("sparse_verify_attn", q, w, H_q, kv, idx, count, k, scale, out, lse, ws, ws_bytes, stream, 0);
+}
+
+size_t dustin_verify_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv, int32_t head_dim,
+                                          int32_t k_or_n) {
+    if (B < 1 || w < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || head_dim < 1 || k_or_n < 1) return 0;
+    return attn_plan(B, w, H_q, H_kv, head_dim, k_or_n + w, false).ws_bytes;
+}
+
+dustin_status dustin_verify_attn(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv, const int32_t *idx,
+                                 const int32_t *count, int32_t k, float scale, void *out, float *lse, void *ws,
+                                 size_t ws_bytes, dustin_stream_t stream) {
+    return attn_call("verify_attn", q, w, H_q, kv, idx, count, k, scale, out, lse, ws, ws_bytes, stream, 1);
+}
+
+dustin_status dustin_append_window_kv(const dustin_kv *kv, const void *k_win, const void *v_win, int32_t w,
+                                      dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "append_window_kv kv", true);
+    if (st != DUSTIN_OK) return st;
+    CHECK(k_win != nullptr && v_win != nullptr, DUSTIN_ERR_INVALID_ARG, "append_window_kv: k_win and v_win are required");
+    CHECK(w >= 1, DUSTIN_ERR_INVALID_ARG, "append_window_kv: w must be >= 1 (got %d)", w);
+    CHECK(((uintptr_t)kv->k | (uintptr_t)kv->v | (uintptr_t)k_win | (uintptr_t)v_win) % 16 == 0,
+          DUSTIN_ERR_INVALID_ARG, "append_window_kv: k, v, k_win and v_win must be 16-byte aligned");
+    return hip_status(launch_append_window(view_of(kv), k_win, v_win, w, (hipStream_t)stream), "append_window_kv launch");
+}
+
+dustin_status dustin_commit_window(int32_t *seq_lens, const int32_t *accepted, int32_t B, int32_t w,
+                                   dustin_stream_t stream) {
+    CHECK(seq_lens != nullptr && accepted != nullptr, DUSTIN_ERR_INVALID_ARG,
+          "commit_window: seq_lens and accepted are required");
+    CHECK(B >= 1 && w >= 1, DUSTIN_ERR_INVALID_ARG, "commit_window: B and w must be >= 1");
+    return hip_status(launch_commit_window(seq_lens, accepted, B, w, (hipStream_t)stream), "commit_window launch");
 }
 
 size_t dustin_window_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv, int32_t head_dim,

@@ -169,7 +169,7 @@ struct AttnGeom {
     static constexpr int NBUF = (kAttnRingBytes / STAGE < 8) ? kAttnRingBytes / STAGE : 8;
 };
 
-template <int D, int RB, int NW, bool DENSE>
+template <int D, int RB, int NW, bool DENSE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     constexpr int T = AttnGeom<D, RB, NW>::T;
     constexpr int NBUF = AttnGeom<D, RB, NW>::NBUF;
@@ -231,27 +231,39 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         jv[i] = DENSE ? t0 + t : ((t < a.tps && t0 + t < a.k) ? a.idx[(int64_t)b * a.k + t0 + t] : -1);
     }
     const int nb = min(max(nb_raw, 0), a.kv.N_max);
-    const int cnt = DENSE ? nb : min(max(cnt_raw, 0), a.k);
+    // History tokens of the (b, g) token list come first; with CAUSAL the w
+    // draft-window rows (cache positions n_b .. n_b + w - 1) follow them.
+    const int hist = DENSE ? nb : min(max(cnt_raw, 0), a.k);
+    const int cnt = hist + (CAUSAL ? a.w : 0);
     const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
+    const int win_lo = hist - t0;   // local index of the first window token
     lds_barrier();   // s_flag cleared; the loads stay in flight
     bool any_bad = false;
     {   // physical row of every token of the split
-        // paged caches: every page-table entry is requested before any is used
-        int pg[PER];
+        int pos[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int t = tid + NT * i;
-            const bool ok = t < ntok && jv[i] >= 0 && jv[i] < nb;
-            pg[i] = (ok && a.kv.page_size != 0) ? a.kv.page_table[(int64_t)b * a.kv.max_pages + (jv[i] >> 4)] : 0;
+            int p = -1;
+            if (t < ntok) {
+                if (!CAUSAL || t < win_lo) p = (jv[i] >= 0 && jv[i] < nb) ? jv[i] : -1;
+                else p = (nb + t - win_lo < a.kv.N_max) ? nb + t - win_lo : -1;
+            }
+            pos[i] = p;
         }
+        // paged caches: every page-table entry is requested before any is used
+        int pg[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            pg[i] = (pos[i] >= 0 && a.kv.page_size != 0) ? a.kv.page_table[(int64_t)b * a.kv.max_pages + (pos[i] >> 4)] : 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int t = tid + NT * i;
             if (t < ntok) {
                 int r = -1;
-                if (jv[i] >= 0 && jv[i] < nb) {
-                    if (a.kv.page_size == 0) r = b * a.kv.N_max + jv[i];
-                    else if (pg[i] >= 0 && pg[i] < a.kv.num_pages) r = pg[i] * 16 + (jv[i] & 15);
+                if (pos[i] >= 0) {
+                    if (a.kv.page_size == 0) r = b * a.kv.N_max + pos[i];
+                    else if (pg[i] >= 0 && pg[i] < a.kv.num_pages) r = pg[i] * 16 + (pos[i] & 15);
                 }
                 rows[t] = r;
                 any_bad |= (r < 0);
@@ -325,11 +337,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], st, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) st[j] *= a.scale_log2;
-        if (!(all_rows_valid && tb + 16 <= ntok)) {
+        if (!(all_rows_valid && tb + 16 <= ntok && (!CAUSAL || tb + 16 <= win_lo))) {
+            // this lane's query row; window token t_w is visible to window step s iff t_w <= s
+            const int sq = (rbw * 16 + (lane & 15)) / a.G;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = tb + (lane >> 4) * 4 + j;
                 if (!(t < ntok && rows[t] >= 0)) st[j] = kNegInf;
+                if (CAUSAL && t >= win_lo && t - win_lo > sq) st[j] = kNegInf;
             }
         }
         float mx = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
@@ -483,14 +498,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int bg = blockIdx.x / a.splits;
     const int b = bg / a.kv.Hkv, g = bg - (bg / a.kv.Hkv) * a.kv.Hkv;
     const int nb = seq_len(a.kv, b);
-    const int cnt = a.idx ? min(max(a.count[b], 0), a.k) : nb;
+    // history tokens first; with a.causal the w window rows (positions
+    // n_b .. n_b + w - 1) follow, seen causally by the window steps
+    const int hist = a.idx ? min(max(a.count[b], 0), a.k) : nb;
+    const int cnt = hist + (a.causal ? a.w : 0);
     const int t0 = split * a.tps;
     const int ntok = max(0, min(cnt, t0 + a.tps) - t0);
+    const int win_lo = hist - t0;
     const int R = a.R;
 
     for (int t = tid; t < ntok; t += 256) {
-        const int j = a.idx ? a.idx[(int64_t)b * a.k + t0 + t] : t0 + t;
-        rows[t] = (j >= 0 && j < nb) ? phys_row(a.kv, b, j) : -1;
+        if (t < win_lo) {
+            const int j = a.idx ? a.idx[(int64_t)b * a.k + t0 + t] : t0 + t;
+            rows[t] = (j >= 0 && j < nb) ? phys_row(a.kv, b, j) : -1;
+        } else {
+            const int p = nb + t - win_lo;
+            rows[t] = (p < a.kv.N_max) ? phys_row(a.kv, b, p) : -1;
+        }
     }
     for (int e = tid; e < R * D; e += 256) {
         const int r = e / D, d = e - (e / D) * D;
@@ -529,7 +553,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
             const int tr = (tb + t < ntok) ? rows[tb + t] : -1;
             float s = 0.f;
             for (int d = 0; d < D; ++d) s += qs[r][d] * ks[t][d];
-            ps[r][t] = (tr >= 0) ? s * a.scale_log2 : kNegInf;
+            const bool hidden = a.causal && tb + t >= win_lo && tb + t - win_lo > r / a.G;
+            ps[r][t] = (tr >= 0 && !hidden) ? s * a.scale_log2 : kNegInf;
         }
         __syncthreads();
         if (tid < R) {
@@ -655,10 +680,17 @@ static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
     // unless a tile would then hold fewer DMA instructions than waves.
     constexpr int NW = (D == 64 && RB == 4) ? 4 : (RB == 1 ? 4 : 8);
     const size_t dyn = (size_t)a.tps * sizeof(int);
-    if (a.idx)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, false>), grid, dim3(NW * 64), dyn, s, a);
-    else
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, true>), grid, dim3(NW * 64), dyn, s, a);
+    if (a.causal) {
+        if (a.idx)
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, false, true>), grid, dim3(NW * 64), dyn, s, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, true, true>), grid, dim3(NW * 64), dyn, s, a);
+    } else {
+        if (a.idx)
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, false, false>), grid, dim3(NW * 64), dyn, s, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, NW, true, false>), grid, dim3(NW * 64), dyn, s, a);
+    }
     return hipGetLastError();
 }
 

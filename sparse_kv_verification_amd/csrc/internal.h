@@ -50,9 +50,14 @@ struct AttnArgs {
     float *part_m, *part_l, *part_o;
     int32_t *counters;       // [B * Hkv]
     int32_t splits, tps, rpad;
+    int32_t causal;          // 1: the w window rows after the history are attended causally
 };
 
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+
+// ---------------------------------------------------------------- draft window in the cache
+hipError_t launch_append_window(const KvView &kv, const void *k_win, const void *v_win, int w, hipStream_t s);
+hipError_t launch_commit_window(int32_t *seq_lens, const int32_t *accepted, int B, int w, hipStream_t s);
 
 // ---------------------------------------------------------------- scoring
 constexpr int kScoreChunk = 256;    // positions per scoring work-group

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.dustin_abi_version() == 1
+    assert L.dustin_abi_version() == 2
     assert L.dustin_status_string(0) == b"DUSTIN_OK"
     assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
 
@@ -123,6 +123,37 @@ def test_arr_and_window_argument_errors(L):
     assert L.dustin_window_attn(FAKE, 17, 8, ctypes.byref(desc), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
     assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, None, FAKE, 1 << 40, None) == INVALID
     assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, FAKE, FAKE, 16, None) == INVALID
+
+
+def test_verify_window_argument_errors(L):
+    def va(desc, **kw):
+        return L.dustin_verify_attn(kw.get("q", FAKE), kw.get("w", 4), kw.get("Hq", 64), ctypes.byref(desc),
+                                    kw.get("idx", FAKE), kw.get("count", FAKE), kw.get("k", 2048), 0.0,
+                                    kw.get("out", FAKE), None, FAKE, kw.get("ws_bytes", 1 << 40), None)
+    assert va(kv(v=None)) == INVALID
+    assert va(kv(), out=None) == INVALID
+    assert va(kv(), w=9) == UNSUPPORTED
+    assert va(kv(), idx=None, k=5) == INVALID
+    assert va(kv(), count=None) == INVALID
+    need = L.dustin_verify_attn_workspace_bytes(2, 4, 64, 8, 128, 2048)
+    assert need > 0
+    assert va(kv(), ws_bytes=need - 1) == INVALID
+    assert b"verify_attn" in L.dustin_last_error()
+    assert L.dustin_verify_attn_workspace_bytes(2, 0, 64, 8, 128, 2048) == 0
+
+    def ap(desc, kw_=FAKE, vw=FAKE, w=4):
+        return L.dustin_append_window_kv(ctypes.byref(desc), kw_, vw, w, None)
+    assert ap(kv(), kw_=None) == INVALID
+    assert ap(kv(), vw=None) == INVALID
+    assert ap(kv(v=None)) == INVALID
+    assert ap(kv(), w=0) == INVALID
+    assert ap(kv(), kw_=FAKE + 8) == INVALID                       # not 16-byte aligned
+    assert b"aligned" in L.dustin_last_error()
+    assert ap(kv(dtype=7)) == UNSUPPORTED
+    assert L.dustin_commit_window(None, FAKE, 2, 4, None) == INVALID
+    assert L.dustin_commit_window(FAKE, None, 2, 4, None) == INVALID
+    assert L.dustin_commit_window(FAKE, FAKE, 0, 4, None) == INVALID
+    assert L.dustin_commit_window(FAKE, FAKE, 2, 0, None) == INVALID
 
 
 def test_workspace_sizes_are_shape_only(L):

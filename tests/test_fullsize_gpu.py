@@ -108,3 +108,38 @@ def test_c5_ragged_paged_step():
     x = synth.make(sh, device=DEV)
     lens = x.seq_lens.cpu().numpy()
     _check(sh, x, sh.k, sample=[int(np.argmin(lens)), int(np.argmax(lens))])
+
+
+def test_c4_verify_step_with_window():
+    """The headline shape with the window in the cache: append, score,
+    select, then the causal verification attention, on histories shortened
+    by w so the window fits; sampled sequences against the oracle."""
+    say("full-size c4 verify step with the window")
+    sh = synth.preset("c4").replace(layers=1)
+    x = synth.make(sh, device=DEV)
+    x.seq_lens.sub_(sh.w)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4)
+    shp = (sh.B, sh.w, sh.Hkv, sh.d)
+    k_win = torch.randn(shp, generator=g, device=DEV).to(x.K.dtype)
+    v_win = torch.randn(shp, generator=g, device=DEV).to(x.K.dtype)
+    kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
+    sample = [3, sh.B - 2]
+    hist = {b: (oracle_kv(x, "K", b), oracle_kv(x, "V", b)) for b in sample}
+    dk.dustin_append_window_kv(kv, k_win, v_win)
+    n_sink, n_window, m = synth.tier_defaults(sh.k)
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
+    s_d, s_t = dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq)
+    idx, cnt, _ = dk.dustin_topk(s_d, s_t, x.seq_lens, sh.k, m, n_sink, n_window)
+    lse = torch.empty((sh.B, sh.w, sh.Hq), dtype=torch.float32, device=DEV)
+    out = dk.dustin_verify_attn(x.q, kv, idx, cnt, lse=lse)
+    torch.cuda.synchronize()
+    for b in sample:
+        K, V = hist[b]
+        c = int(cnt[b])
+        I = idx[b, :c].cpu().numpy()
+        assert I.max() < int(x.seq_lens[b])
+        O, L = oracle.verify_attention(f64(x.q[b]), K, V, f64(k_win[b]), f64(v_win[b]), I)
+        err, lerr = np.abs(f64(out[b]) - O).max(), np.abs(f64(lse[b]) - L).max()
+        say(f"  b={b} |I|={c} max|dO|={err:.2e} max|dlse|={lerr:.2e}")
+        assert err <= 2e-2 and lerr <= 2e-3
