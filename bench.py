@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-window", action="store_true",
+                   help="skip the verification-window step (append + causal verify attention + commit)")
     p.add_argument("--pmc-probe", action="store_true",
                    help="for counter collection: one warm step, a 1 GiB float32 copy (the calibration "
                         "kernel of known size), then one more step; prints no JSON")
@@ -347,7 +349,7 @@ def main():
                           "attention_per_launch_eager_loop": round(attn_loop_us, 3),
                           "attention_single_launch_event_bracketed": round(attn_event_us, 3)},
         "roofline": {
-            "kernel": "attn_bf16_kernel<128, 2, 8, false> (dustin_sparse_verify_attn)",
+            "kernel": "attn_bf16_kernel<128, 2, 8, false, false> (dustin_sparse_verify_attn)",
             "launch_us": round(attn_launch_us, 3),
             "bound": "hbm",
             "achieved": round(attn_gbps, 1),
@@ -362,7 +364,86 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
+    if not args.no_window:
+        # Last, because it writes the window rows into every layer's cache.
+        res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
     print(json.dumps(res), flush=True)
+
+
+def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):
+    """The step with the draft window in the cache: every layer's window
+    rows appended, score, select, L causal verification attentions over the
+    set plus the window, and the commit.  The histories are w shorter than
+    the generated ones so the window fits behind them; the commit accepts 0
+    tokens so the timed step repeats on the same lengths."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    dev = x.q.device
+    lens_w = (x.seq_lens - sh.w).clamp_min(0).to(torch.int32)
+    kvw = [dk.KV(Ks[l], Vs[l], lens_w, x.page_table) for l in range(sh.layers)]
+    dkw = [dk.KV(x.Kd[l], None, lens_w, x.page_table) for l in range(sh.L_d)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + sh.seed)
+    shp = (sh.B, sh.w, sh.Hkv, sh.d)
+    k_win = torch.randn(shp, generator=g, device=dev).to(x.K.dtype)
+    v_win = torch.randn(shp, generator=g, device=dev).to(x.K.dtype)
+    accepted = torch.zeros((sh.B,), dtype=torch.int32, device=dev)
+    s_d = torch.empty((sh.B, sh.n), dtype=torch.float32, device=dev)
+    s_t = torch.empty_like(s_d)
+    idx = torch.empty((sh.B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((sh.B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(x.q)
+    ws_s, ws_k, ws_v = dk.Workspace(), dk.Workspace(), dk.Workspace()
+
+    def append():
+        for l in range(sh.layers):
+            dk.dustin_append_window_kv(kvw[l], k_win, v_win)
+
+    def verify():
+        for l in range(sh.layers):
+            dk.dustin_verify_attn(x.q, kvw[l], idx, cnt, out=out, ws=ws_v)
+
+    def step():
+        append()
+        dk.dustin_score(dkw, x.q_draft, [kvw[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
+        dk.dustin_topk(s_d, s_t, lens_w, k, m, n_sink, n_window, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+        verify()
+        dk.dustin_commit_window(lens_w, accepted, sh.w)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    run, per_launch = step, verify
+    graphs = []
+    if not args.no_graph:
+        for fn in (step, verify):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gr, stream=cap):
+                    fn()
+            torch.cuda.synchronize()
+            gr.replay()
+            graphs.append(gr)
+        run, per_launch = graphs[0].replay, graphs[1].replay
+    step_us = timed(run, args.steps)
+    verify_us = timed(per_launch, args.steps) / sh.layers
+    append_us = timed(append, args.steps) / sh.layers
+    commit_us = timed(lambda: dk.dustin_commit_window(lens_w, accepted, sh.w), args.steps)
+    esz = x.K.element_size()
+    rows = int(cnt.sum()) + sh.B * sh.w
+    per_layer = rows * sh.Hkv * sh.d * esz * 2 + 2 * x.q.numel() * esz + sh.B * k * 4 + sh.B * 4
+    log(f"window step {step_us:.1f} us; verify attention {verify_us:.2f} us/launch "
+        f"({per_layer / verify_us / 1e3:.0f} GB/s), append {append_us:.2f} us/layer, commit {commit_us:.2f} us")
+    return {
+        "step_us": round(step_us, 2),
+        "verify_attn_per_launch_us": round(verify_us, 3),
+        "verify_attn_GBps": round(per_layer / verify_us / 1e3, 1),
+        "verify_attn_algorithmic_bytes_per_launch": per_layer,
+        "append_per_layer_us_eager": round(append_us, 3),
+        "commit_us_eager": round(commit_us, 3),
+        "timing": "graph replay" if graphs else "eager",
+        "histories": "generated lengths minus w (room for the window)",
+    }
 
 
 if __name__ == "__main__":
