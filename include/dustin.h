@@ -34,10 +34,13 @@
  *   [0, num_pages) are treated as absent (never dereferenced).
  * - Workspace: pass at least the byte count the matching *_workspace_bytes()
  *   function returns for the same shape.  dustin_sparse_verify_attn,
- *   dustin_verify_attn and dustin_window_attn keep arrival counters at the start of their workspace:
- *   it must be zero-filled before its first use, every call leaves it zero
- *   again, and it must not be handed to another entry point in between.
- *   The other entry points make no assumption about workspace contents.
+ *   dustin_verify_attn and dustin_window_attn keep arrival counters in the
+ *   first 64 KiB of their workspace (one slot per (sequence, KV head), so
+ *   B * H_kv <= 16384): that region must be zero-filled before its first
+ *   use and every call leaves it zero again, so one workspace may serve
+ *   successive calls of these three entry points of any shapes, but it must
+ *   not be handed to another entry point in between.  The other entry
+ *   points make no assumption about workspace contents.
  *   Calls that may overlap in time must not share a workspace.
  * - Outputs are bitwise deterministic for fixed inputs and shapes.
  * - Functions are stateless and reentrant; dustin_last_error() is

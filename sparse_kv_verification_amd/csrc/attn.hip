@@ -19,10 +19,11 @@
 //   online softmax over tokens (exp2 domain, per-row running max)
 //   O^T[d][row]    += V_tile^T . P^T    P rounded to bf16 for the MFMA
 //
-// Splits of one (b, g) are merged by the last work-group to finish (an
-// atomic arrival counter in the workspace, reset to zero afterwards), so the
-// whole call is one kernel launch.  The merge order is fixed, which keeps the
-// output bitwise deterministic.
+// Splits of one (b, g) are merged inside the same launch through an arrival
+// counter in the workspace (reset to zero afterwards): a split that finds all
+// the others already published merges at once, otherwise the last one to
+// arrive does.  The merge order is fixed, which keeps the output bitwise
+// deterministic.
 //
 // A float32 variant (plain VALU arithmetic, 256 lanes per work-group) serves
 // float32 caches with the same split/merge scheme.
@@ -400,7 +401,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     }
 
     lsum = group4_sum(lsum);
-    __syncthreads();   // ring no longer read: reuse it for the share fold
+    // Ring no longer read (every tile's DMA has been waited for): reuse it for
+    // the share fold.  LDS-only barriers from here on, so the split
+    // handshake's counter load below overlaps the fold.
+    lds_barrier();
+    int seen = 0;
+    if (a.splits > 1 && tid == 0)
+        seen = __hip_atomic_load(&a.counters[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Every wave leaves its share (running max, sum and unnormalised O of its
     // rows over its tokens) in LDS.  Then wave (rbw, th) folds the NTH shares
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             share_ml[wave][lane][1] = lsum;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int row = lane & 15, r = rbw * 16 + row;
     const int d0 = th * DS + (lane >> 4) * E;
     float M = kNegInf, L = 0.f;
@@ -458,10 +465,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         return;
     }
 
-    // publish this split's partial (row-major); the last split of (b, g) to
-    // arrive merges
+    // Split partials (row-major m, l, O per split).  A split that, when its
+    // token loop ended, found every other split of (b, g) already published merges
+    // at once: its own partial comes from registers, so it neither waits for
+    // its stores nor arrives.  Otherwise it publishes, waits for its stores,
+    // and arrives; the last split to arrive merges.  Exactly one split
+    // merges, always in split order, so the output does not depend on which.
+    const size_t pb0 = (size_t)bg * a.splits * a.rpad;   // partial rows of split 0 of (b, g)
     {
-        const size_t pb = ((size_t)bg * a.splits + split) * a.rpad;
+        const size_t pb = pb0 + (size_t)split * a.rpad;
         if (th == 0 && lane < 16) {
             st_agent(a.part_m + pb + r, M);
             st_agent(a.part_l + pb + r, L);
@@ -469,14 +481,60 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, (uint32_t)(a.rpad * D * sizeof(float)));
 #pragma unroll
         for (int c = 0; c < E / 4; ++c) st_coherent4(po, (uint32_t)((r * D + d0 + 4 * c) * 4), acc[c]);
-        wait_all_mem();
     }
-    __syncthreads();
-    if (tid == 0)
-        s_flag = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
-    __syncthreads();
-    if (!s_flag) return;
-    merge_splits<false, D, NT>(a, bg, b, g, tid);
+    if (tid == 0) s_flag = (seen == a.splits - 1);
+    lds_barrier();   // the partial stores stay in flight
+    if (!s_flag) {
+        wait_all_mem();
+        __syncthreads();
+        if (tid == 0)
+            s_flag = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
+        __syncthreads();
+        if (!s_flag) return;
+    }
+    // merge: each lane folds its (row, E columns) slice over the splits
+    {
+        const uint32_t nml = (uint32_t)(a.splits * a.rpad * sizeof(float));
+        const __amdgpu_buffer_rsrc_t pm = coherent_rsrc(a.part_m + pb0, nml);
+        const __amdgpu_buffer_rsrc_t pl = coherent_rsrc(a.part_l + pb0, nml);
+        const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb0 * D, nml * D);
+        float Mt = kNegInf, Lt = 0.f;
+        f32x4 at[E / 4];
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) at[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < a.splits; ++s2) {
+            float ms = M, ls = L;
+            f32x4 v[E / 4];
+#pragma unroll
+            for (int c = 0; c < E / 4; ++c) v[c] = acc[c];
+            if (s2 != split) {
+                const uint32_t o = (uint32_t)(s2 * a.rpad + r);
+                ms = ld_coherent(pm, o * 4u);
+                ls = ld_coherent(pl, o * 4u);
+#pragma unroll
+                for (int c = 0; c < E / 4; ++c) v[c] = ld_coherent4(po, (o * D + d0 + 4 * c) * 4u);
+            }
+            const float Mn = fmaxf(Mt, ms);
+            const float mu = (Mn == kNegInf) ? 0.f : Mn;
+            const float so = exp2f(Mt - mu), sn = exp2f(ms - mu);
+            Lt = Lt * so + ls * sn;
+#pragma unroll
+            for (int c = 0; c < E / 4; ++c) at[c] = at[c] * so + v[c] * sn;
+            Mt = Mn;
+        }
+        if (r < a.R) {
+            const int sq = r / a.G, gh = r - (r / a.G) * a.G;
+            const size_t hrow = ((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh;
+            const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
+#pragma unroll
+            for (int c = 0; c < E / 4; ++c) {
+                uint32_t *op = (uint32_t *)((uint16_t *)a.out + hrow * D + d0 + 4 * c);
+                op[0] = f32_to_bf16_bits(at[c][0] * inv) | ((uint32_t)f32_to_bf16_bits(at[c][1] * inv) << 16);
+                op[1] = f32_to_bf16_bits(at[c][2] * inv) | ((uint32_t)f32_to_bf16_bits(at[c][3] * inv) << 16);
+            }
+            if (a.lse && th == 0 && lane < 16) a.lse[hrow] = (Lt > 0.f) ? (Mt + __log2f(Lt)) * kLn2 : kNegInf;
+        }
+    }
     if (tid == 0) a.counters[bg] = 0;
 }
 
@@ -658,7 +716,7 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
     splits = (tok + tps - 1) / tps;
     p.splits = (int)splits;
     p.tps = (int)tps;
-    size_t off = align_up((size_t)groups * sizeof(int32_t), 256);
+    size_t off = align_up((size_t)kAttnCounterSlots * sizeof(int32_t), 256);
     if (p.splits > 1) {
         const size_t nrow = (size_t)groups * p.splits * p.rpad;
         p.off_m = off;

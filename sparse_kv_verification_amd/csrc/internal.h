@@ -24,6 +24,11 @@ constexpr int kAttnSplitQuantum = 128;   // bf16 splits hold a multiple of this 
 constexpr int kAttnMaxTps = 4096;        // tokens per split (row table in LDS)
 constexpr int kAttnRingBytes = 128 * 1024;   // LDS of the bf16 kernel's K/V ring
 constexpr int kAttnTargetGroups = 256;   // bf16 work-groups the split planner aims for
+// Arrival counters occupy a fixed region at the start of every attention
+// workspace, one slot per (sequence, KV head), whatever the call's shape: a
+// workspace reused by calls of different shapes then never finds a counter
+// on top of another call's stored partials.
+constexpr int kAttnCounterSlots = 16384;
 
 struct AttnPlan {
     int rows;      // R = w * G query rows per (sequence, KV head)

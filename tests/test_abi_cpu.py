@@ -70,6 +70,7 @@ def test_attention_argument_errors(L):
     assert attn(L, kv(page_size=16, page_table=None, max_pages=256, num_pages=10)) == INVALID
     assert attn(L, kv(page_size=16, page_table=FAKE, max_pages=10, num_pages=10)) == INVALID
     assert attn(L, kv(), scale=float("nan")) == INVALID
+    assert attn(L, kv(B=4096, H_kv=8)) == UNSUPPORTED                 # more groups than counter slots
     need = L.dustin_attn_workspace_bytes(2, 4, 64, 8, 128, 2048)
     assert need > 0
     assert attn(L, kv(), ws_bytes=need - 1) == INVALID

@@ -110,6 +110,33 @@ def test_attention_edge_cases():
         assert np.abs(f64(lse[b]) - L).max() <= 2e-3
 
 
+def test_attention_workspace_reused_across_shapes():
+    """One workspace serves a dense call with few (b, KV head) groups and many
+    splits, then a sparse call with 128 groups: the second call's arrival
+    counters must not land on the partials the first one stored."""
+    say("attention workspace reused across shapes")
+    ws = dk.Workspace()
+    x1 = _make("ws-dense", dict(B=2, n=8000, Hq=64, Hkv=8, L_d=1))
+    kv1 = dk.KV(x1.K, x1.V, x1.seq_lens, x1.page_table)
+    d1 = kv1.desc
+    n1 = dk.lib().dustin_attn_workspace_bytes(d1.B, 4, 64, 8, 128, d1.N_max)
+    dk.dustin_sparse_verify_attn(x1.q, kv1, ws=ws)
+    x2 = _make("ws-sparse", dict(B=16, n=1000, Hq=64, Hkv=8, k=256, L_d=1))
+    kv2 = dk.KV(x2.K, x2.V, x2.seq_lens, x2.page_table)
+    n2 = dk.lib().dustin_attn_workspace_bytes(16, 4, 64, 8, 128, 256)
+    assert n2 <= n1, "the second call must reuse the first call's workspace"
+    idx, cnt = make_idx(x2.seq_lens, 256, seed=11, device=DEV)
+    out = dk.dustin_sparse_verify_attn(x2.q, kv2, idx, cnt, ws=ws)
+    torch.cuda.synchronize()
+    for b in (0, 9, 15):
+        n = int(x2.seq_lens[b])
+        I = valid_set(idx[b].cpu().numpy(), int(cnt[b]), n)
+        O, _ = oracle.sparse_attention(f64(x2.q[b]), oracle_kv(x2, "K", b), oracle_kv(x2, "V", b), I)
+        err = np.abs(f64(out[b]) - O).max()
+        say(f"  b={b} max|dO|={err:.2e}")
+        assert err <= 2e-2
+
+
 SELECT_CASES = [
     (dict(B=3, N=5000, k=512, m=200, ns=4, nw=32, ties=True), "ties"),
     (dict(B=2, N=3000, k=700, m=0, ns=0, nw=0, ties=False), "target-only"),
