@@ -57,16 +57,24 @@ __device__ __forceinline__ float group4_sum(float v) {
     return v + __shfl_xor(v, 32, 64);
 }
 
-// Reduce across the 16 lanes of one 16-lane group.
+// Reduce across the 16 lanes of one 16-lane group (a DPP row): rotations
+// by 8, 4, 2 and 1 within the row leave the full result in every lane,
+// with register-only DPP moves rather than LDS shuffles.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float lane16_sum(float v) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    return v + row_ror<1>(v);
 }
 __device__ __forceinline__ float lane16_max(float v) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    return fmaxf(v, row_ror<1>(v));
 }
 
 // 16-byte streaming load (nontemporal: the data is read once per pass and

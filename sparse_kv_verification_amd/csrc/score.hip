@@ -587,6 +587,371 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Draft side, streaming form for contiguous bfloat16 drafts with two 64-wide
+// KV heads, where a draft layer's position row is 256 bytes ([2][64] bf16).
+// Every wave streams its own positions through a private two-stage LDS ring:
+// a stage is 32 positions of one layer (8 KiB) fetched with the nontemporal
+// global->LDS DMA (each row is read once per pass), while the wave computes
+// on the other stage.  The sixteen 16-byte chunks of a position row are
+// stored XOR-swizzled by the position's low four bits, so a K-operand read
+// (16 positions, one chunk each) touches 16 distinct bank groups.  Register
+// loads on the way (Q fragments, row normalisers, lengths) complete in order
+// with the DMA, and every stage starts with a full vmcnt wait, so a stage
+// never reads LDS before its own bytes have landed.
+constexpr int kStreamPos = 32;                    // positions per stage
+constexpr int kStreamStage = kStreamPos * 256;    // bytes per stage
+constexpr int kStreamGroups = 512;                // two 4-wave groups per CU
+
+// DMA of positions j0 .. j0 + 31 of one layer into `stage`; `seq` is the
+// layer's k pointer advanced to the sequence.  Positions past the cache end
+// read the last row (the caller masks them).
+__device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast, int lane, uint8_t *stage) {
+#pragma unroll
+    for (int i = 0; i < kStreamStage / 1024; ++i) {
+        const int rho = i * 4 + (lane >> 4);
+        const int chunk = (lane & 15) ^ (rho & 15);
+        const uint32_t j = (uint32_t)min(j0 + rho, jlast);
+        dma16_stream(seq + (j * 256u + (uint32_t)chunk * 16u), stage + i * 1024);
+    }
+}
+
+// Buffer resource over `bytes` bytes at `base` (loads past the end read 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-lane byte offsets of the Q fragments of a (sequence, draft layer)
+// block [gamma][H_d][64]: row rb*16 + (lane & 15) of KV head 0 (head h adds
+// h * G_d rows of 128 bytes), d slice (lane >> 4) * 8.  Padding rows read
+// row 0: their logits are never used (the statistics pass does not store
+// them; the accumulation pass gives them an infinite normaliser).
+template <int RB>
+__device__ __forceinline__ void stream_qoff(const DraftScoreArgs &a, int lane, uint32_t (&qo)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        const int rr = r < a.rows ? r : 0;
+        qo[rb] = (uint32_t)(((rr / a.G_d) * a.H_d + (rr - (rr / a.G_d) * a.G_d)) * 128 + (lane >> 4) * 16);
+    }
+}
+
+template <int RB>
+__device__ __forceinline__ void stream_load_q(const DraftScoreArgs &a, int b, int l, const uint32_t (&qo)[RB],
+                                              bf16x8 (&q)[2][RB][2]) {
+    const uint32_t blk = (uint32_t)(a.gamma * a.H_d * 128);
+    const __amdgpu_buffer_rsrc_t r = stream_rsrc((const char *)a.q_draft + ((int64_t)b * a.L_d + l) * blk, blk);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                q[h][rb][kk] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, qo[rb] + kk * 64, h * a.G_d * 128, 0));
+}
+
+// K operand (head h, both k-steps) of 16-position subtile `st` of a stage:
+// lane holds position st * 16 + (lane & 15), d slice kk * 32 + (lane >> 4) * 8.
+__device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int lane, bf16x8 (&k)[2]) {
+    const int rho = st * 16 + (lane & 15);
+    uint32_t ad[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int chunk = h * 8 + kk * 4 + (lane >> 4);
+        ad[kk] = base + rho * 256 + ((chunk ^ (rho & 15)) << 4);
+    }
+    u32x4 raw[2];
+    ds_read_b128_n(ad, raw);
+    k[0] = __builtin_bit_cast(bf16x8, raw[0]);
+    k[1] = __builtin_bit_cast(bf16x8, raw[1]);
+}
+
+// Statistics pass, streaming form.  Items (b, layer, 4096-position chunk)
+// walk round robin over the persistent groups; wave w streams positions
+// w * 1024 .. + 1023 of the chunk (stages past n_b are skipped) keeping
+// per-lane running (max, sum of exp2) pairs for both KV heads.  An item's
+// first stage requests the next item's Q fragments and its last stage the
+// next item's first DMA; items alternate between two named Q sets, so no
+// register copy waits for a pending load.  The cross-wave combine
+// alternates between two LDS buffers, so one barrier per item suffices.
+template <int RB>
+__global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
+    constexpr int KK = 2;
+    constexpr int PER_WAVE = kDraftStatChunk / 4;
+    constexpr int NSTAGE = PER_WAVE / kStreamPos;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][kStreamStage];
+    __shared__ float red[2][4][2][RB * 16][2];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int U = a.L_d * 2;
+    const int nch = a.nchunk;
+    const int items = a.kv[0].B * a.L_d * nch;
+    struct Item { int b, l, c, nb, jw, nst; const char *seq; int jlast; };
+    auto decode = [&](int it) {
+        Item x;
+        x.c = it % nch;
+        x.l = (it / nch) % a.L_d;
+        x.b = it / (nch * a.L_d);
+        x.nb = sl_len(a.kv[x.l], x.b);
+        x.jw = x.c * kDraftStatChunk + wave * PER_WAVE;
+        const int left = x.nb - x.jw;
+        x.nst = left <= 0 ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
+        x.seq = a.kv[x.l].k + (int64_t)x.b * a.kv[x.l].N_max * 256;
+        x.jlast = a.kv[x.l].N_max - 1;
+        return x;
+    };
+    uint32_t qo[RB];
+    stream_qoff<RB>(a, lane, qo);
+    int slot = 0, par = 0;
+    // One item on Q set q; requests the next item's Q into qn and, when the
+    // next item has stages, its first DMA.
+    auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[2][RB][KK],
+                    bf16x8 (&qn)[2][RB][KK]) {
+        float mrun[2][RB][4], zrun[2][RB][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mrun[h][rb][i] = kNegInf;
+                    zrun[h][rb][i] = 0.f;
+                }
+        auto next_dma = [&](int s) {   // the DMA after stage s
+            if (s + 1 < cur.nst) stream_issue(cur.seq, cur.jw + (s + 1) * kStreamPos, cur.jlast, lane, ring[wave][slot ^ 1]);
+            else if (has_next && nxt.nst > 0) stream_issue(nxt.seq, nxt.jw, nxt.jlast, lane, ring[wave][slot ^ 1]);
+        };
+        auto stage = [&](int s) {
+            const uint32_t base = lds_addr(ring[wave][slot]);
+            const int j0 = cur.jw + s * kStreamPos;
+            const bool full = j0 + kStreamPos <= cur.nb;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 sc[2][RB];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    bf16x8 k[2];
+                    stream_kfrag(base, st, h, lane, k);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < KK; ++kk)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[h][rb][kk], k[kk], acc, 0, 0, 0);
+                        sc[st][rb] = acc;
+                    }
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v0 = sc[0][rb][i] * a.scale_log2, v1 = sc[1][rb][i] * a.scale_log2;
+                        if (!full) {
+                            if (j0 + (lane & 15) >= cur.nb) v0 = kNegInf;
+                            if (j0 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
+                        }
+                        const float mx = fmaxf(mrun[h][rb][i], fmaxf(v0, v1));
+                        const float mu = (mx == kNegInf) ? 0.f : mx;
+                        zrun[h][rb][i] = zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu) +
+                                         __builtin_amdgcn_exp2f(v0 - mu) + __builtin_amdgcn_exp2f(v1 - mu);
+                        mrun[h][rb][i] = mx;
+                    }
+            }
+            slot ^= 1;
+        };
+        if (cur.nst == 0) {
+            stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
+            if (has_next && nxt.nst > 0) stream_issue(nxt.seq, nxt.jw, nxt.jlast, lane, ring[wave][slot]);
+        } else {
+            wait_vmcnt<0>();
+            stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
+            next_dma(0);
+            stage(0);
+            for (int s = 1; s < cur.nst; ++s) {
+                wait_vmcnt<0>();
+                next_dma(s);
+                stage(s);
+            }
+        }
+        // combine the 16 token lanes of each row, then the four waves
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float mx = lane16_max(mrun[h][rb][i]);
+                    const float mu = (mx == kNegInf) ? 0.f : mx;
+                    const float z = lane16_sum(zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu));
+                    if ((lane & 15) == 0) {
+                        const int r = rb * 16 + (lane >> 4) * 4 + i;
+                        red[par][wave][h][r][0] = mx;
+                        red[par][wave][h][r][1] = z;
+                    }
+                }
+        lds_barrier();   // the next item's requests stay in flight
+        if (threadIdx.x < 2 * a.rows) {
+            const int h = threadIdx.x / a.rows, r = threadIdx.x - h * a.rows;
+            float mx = kNegInf;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[par][w][h][r][0]);
+            const float mu = (mx == kNegInf) ? 0.f : mx;
+            float z = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) z += red[par][w][h][r][1] * __builtin_amdgcn_exp2f(red[par][w][h][r][0] - mu);
+            float *st = a.stat + ((((int64_t)cur.b * U + cur.l * 2 + h) * a.rows + r) * nch + cur.c) * 2;
+            st[0] = mx;
+            st[1] = z;
+        }
+        par ^= 1;
+    };
+    int it = blockIdx.x;
+    if (it >= items) return;
+    bf16x8 qA[2][RB][KK], qB[2][RB][KK];
+    Item cur = decode(it);
+    stream_load_q<RB>(a, cur.b, cur.l, qo, qA);
+    if (cur.nst > 0) stream_issue(cur.seq, cur.jw, cur.jlast, lane, ring[wave][slot]);
+    for (;;) {
+        int nit = it + gridDim.x;
+        Item nxt = decode(nit < items ? nit : it);
+        item(cur, nxt, nit < items, qA, qB);
+        if (nit >= items) break;
+        it = nit;
+        cur = nxt;
+        nit = it + gridDim.x;
+        nxt = decode(nit < items ? nit : it);
+        item(cur, nxt, nit < items, qB, qA);
+        if (nit >= items) break;
+        it = nit;
+        cur = nxt;
+    }
+}
+
+// Accumulation pass, streaming form.  Items (b, 1024-position chunk) walk
+// round robin over the persistent groups (chunks wholly past n_b only write
+// zeros); wave w owns positions w * 256 .. + 255 of the chunk and streams
+// them layer after layer, 8 stages per layer (stages past n_b are skipped).
+// A layer's Q fragments and row normalisers are requested by the previous
+// layer's first stage, unconditionally and into the other of two named
+// register sets, so no register copy waits for a pending load.  Each stage
+// adds sum_{head, row} exp2(logit - lse) for its 32 positions to a
+// wave-private LDS accumulator, in layer order, so S_Draft needs no atomics.
+template <int RB>
+__global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
+    constexpr int KK = 2;
+    constexpr int CHUNK = 1024;
+    constexpr int PER_WAVE = CHUNK / 4;
+    constexpr int NSTAGE = PER_WAVE / kStreamPos;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][kStreamStage];
+    __shared__ float accs[4][PER_WAVE];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
+    const int N = k0.N_max;
+    const int nch = (N + CHUNK - 1) / CHUNK;
+    const int items = k0.B * nch;
+    const int L = a.L_d;
+    const int U = L * 2;
+    // per-lane Q offsets, and normaliser offsets: rows rb*16 + (lane >> 4)*4
+    // .. + 3 in one 16-byte load (the row count is a multiple of 4); rows past
+    // the count read row 0's normalisers and are dropped where the terms are
+    // summed (a select there, not on the loaded values, so no wait follows
+    // the loads)
+    uint32_t qo[RB], lo[RB];
+    bool lok[RB];
+    stream_qoff<RB>(a, lane, qo);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r4 = rb * 16 + (lane >> 4) * 4;
+        lok[rb] = r4 < a.rows;
+        lo[rb] = (uint32_t)(lok[rb] ? r4 : 0) * 4u;
+    }
+    auto load_lse = [&](int b, int l, f32x4 (&ls)[2][RB]) {
+        const __amdgpu_buffer_rsrc_t lr =
+            stream_rsrc(a.lse + ((int64_t)b * U + l * 2) * a.rows, (uint32_t)(2 * a.rows * sizeof(float)));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                ls[h][rb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, lo[rb], h * a.rows * 4, 0));
+    };
+    float *acc = accs[wave];
+    int slot = 0;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int b = it / nch, c = it - (it / nch) * nch;
+        const int nb = sl_len(k0, b);
+        const int jw = c * CHUNK + wave * PER_WAVE;
+        const int left = nb - jw;
+        const int nst = left <= 0 ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE / 64; ++i) acc[lane + 64 * i] = 0.f;
+        if (nst > 0) {
+            const int64_t seq0 = (int64_t)b * N * 256;
+            bf16x8 qA[2][RB][KK], qB[2][RB][KK];
+            f32x4 lA[2][RB], lB[2][RB];
+            stream_load_q<RB>(a, b, 0, qo, qA);
+            load_lse(b, 0, lA);
+            stream_issue(a.kv[0].k + seq0, jw, N - 1, lane, ring[wave][slot]);
+            auto stage = [&](int s, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB]) {
+                const uint32_t base = lds_addr(ring[wave][slot]);
+#pragma unroll
+                for (int s16 = 0; s16 < 2; ++s16) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        bf16x8 k[2];
+                        stream_kfrag(base, s16, h, lane, k);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kk = 0; kk < KK; ++kk)
+                                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[h][rb][kk], k[kk], sc, 0, 0, 0);
+                            float e = 0.f;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[h][rb][i]);
+                            t += lok[rb] ? e : 0.f;
+                        }
+                    }
+                    t = group4_sum(t);
+                    if (lane < 16) acc[s * kStreamPos + s16 * 16 + lane] += t;
+                }
+                slot ^= 1;
+            };
+            auto layer = [&](int l, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB], bf16x8 (&qn)[2][RB][KK],
+                             f32x4 (&lsn)[2][RB]) {
+                // both layers' cache pointers from uniform indices (scalar
+                // loads, outside the vector-load order)
+                const int ln = (l + 1 < L) ? l + 1 : l;
+                const char *kl = a.kv[l].k + seq0;
+                const char *kn = a.kv[ln].k + seq0;
+                auto next_dma = [&](int s) {   // the DMA after stage s of this layer
+                    if (s + 1 < nst) stream_issue(kl, jw + (s + 1) * kStreamPos, N - 1, lane, ring[wave][slot ^ 1]);
+                    else if (l + 1 < L) stream_issue(kn, jw, N - 1, lane, ring[wave][slot ^ 1]);
+                };
+                wait_vmcnt<0>();
+                stream_load_q<RB>(a, b, ln, qo, qn);
+                load_lse(b, ln, lsn);
+                next_dma(0);
+                stage(0, q, ls);
+                for (int s = 1; s < nst; ++s) {
+                    wait_vmcnt<0>();
+                    next_dma(s);
+                    stage(s, q, ls);
+                }
+            };
+            for (int l = 0; l < L; l += 2) {
+                layer(l, qA, lA, qB, lB);
+                layer(l + 1, qB, lB, qA, lA);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PER_WAVE / 64; ++i) {
+            const int j = jw + lane + 64 * i;
+            if (j < N) a.s_draft[(int64_t)b * N + j] = (j < nb) ? acc[lane + 64 * i] : 0.f;
+        }
+    }
+}
+
 // --------------------------------------------------------------- host side
 ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int Hkv_d) {
     ScorePlan p{};
@@ -725,9 +1090,33 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Streaming passes: contiguous cache, two 64-wide draft KV heads, an even
+// number of draft layers and a row count that is a multiple of four.
+template <int RB>
+static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
+    const KvView &k0 = a.kv[0];
+    DraftScoreArgs b = a;
+    b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
+    const int stat_items = k0.B * a.L_d * b.nchunk;
+    hipLaunchKernelGGL((draft_stats_stream<RB>), dim3(stat_items < kStreamGroups ? stat_items : kStreamGroups),
+                       dim3(256), 0, s, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nrows = k0.B * a.L_d * 2 * a.rows;
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int acc_items = k0.B * ((k0.N_max + 1023) / 1024);
+    hipLaunchKernelGGL((draft_acc_stream<RB>), dim3(acc_items < kStreamGroups ? acc_items : kStreamGroups),
+                       dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
 template <int D, int RB>
 static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
+    if constexpr (D == 64 && RB <= 2) {
+        if (a.Hkv_d == 2 && k0.page_size == 0 && a.L_d % 2 == 0 && a.rows % 4 == 0) return draft_stream_impl<RB>(a, s);
+    }
     const int U = a.L_d * a.Hkv_d;
     DraftScoreArgs b = a;
     b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
