@@ -11,7 +11,9 @@ Decoding", arXiv 2606.24957):
 
 * the Chinese translation of the arXiv HTML (bittide.aicompass.dev),
   section 3.1, equations (1)-(4): ARR, windowed ARR and the SD oracle;
-  section 3.2: history attention A_{i-delta,.} with delta = 1;
+  section 3.2: history attention A_{i-delta,.} (delta = 1 for S_Target; the
+  history-policy comparison of Fig. 2 over several delta);
+  section 3.3 (Fig. 3): the draft lookahead compared with the oracle;
 * the blog summary (liuzhao09.github.io), section 2.2 (hybrid aggregation:
   S_Draft over H_d, L_d, Gamma; S_Target over H_t, L_t; one global index
   set), section 2.3 (verification set: protected sink + recent window, draft
@@ -60,6 +62,8 @@ __all__ = [
     "score_target",
     "score_draft",
     "select_verify_set",
+    "history_policy",
+    "policy_sweep",
     "topk_desc",
     "protected_positions",
     "pages_to_contiguous",
@@ -373,6 +377,52 @@ def select_verify_set(s_draft, s_target, n, k, m, n_sink, n_window):
     ])
     order = np.argsort(idx, kind="stable")
     return idx[order], tier[order]
+
+
+def history_policy(A_past, k):
+    """Translation section 3.2 (Fig. 2): rank the history positions by the
+    head-mean full-cache attention A_{i-delta,.} of the query delta steps
+    back and keep the top k (ties: lower position first).  Returns the
+    positions ascending."""
+    return np.sort(topk_desc(A_past, k))
+
+
+def policy_sweep(q_window, q_past, K, s_draft, s_target, ks, m_hybrid, n_sink, n_window, scale=None):
+    """Windowed ARR (Eq. 2) of the selection policies the pages compare, at
+    every budget k in ks, for one sequence:
+
+      row 0             the SD oracle (Eq. 3-4), the upper bound;
+      rows 1 .. P       the history policy of each past query (translation
+                        section 3.2, Fig. 2), P = len(q_past);
+      row P + 1         the draft lookahead alone, TopK_k of S_Draft
+                        (translation section 3.3, Fig. 3);
+      rows P + 2 .. + 4 the verification set of blog section 2.3 with
+                        m = 0 (target history only, Dustin-T), m = k - |P|
+                        (draft lookahead only after the protected tokens,
+                        Dustin-D) and m = m_hybrid[k] (Dustin-H), the three
+                        variants of blog Table 3.
+
+    A is the head-mean full-cache attention of the window queries (Eq. 1);
+    the past queries' A_{i-delta,.} comes from the same definition with a
+    one-step window.  q_window [w][Hq][d]; q_past [P][Hq][d]; K [n][Hkv][d];
+    s_draft, s_target [n].  Returns [P + 5][len(ks)].
+    """
+    A = window_attention(q_window, K, scale)
+    n = A.shape[1]
+    q_past = _f64(q_past)
+    A_past = [window_attention(q_past[p][None], K, scale)[0] for p in range(q_past.shape[0])]
+    P = len(A_past)
+    out = np.zeros((P + 5, len(ks)))
+    for ki, k in enumerate(ks):
+        out[0, ki] = arr_window(A, sd_oracle(A, k)[0])
+        for p in range(P):
+            out[1 + p, ki] = arr_window(A, history_policy(A_past[p], k))
+        out[P + 1, ki] = arr_window(A, np.sort(topk_desc(s_draft, k)))
+        ms = (0, k - n_sink - n_window, m_hybrid[ki])
+        for r, m in enumerate(ms):
+            I, _ = select_verify_set(s_draft, s_target, n, k, m, n_sink, n_window)
+            out[P + 2 + r, ki] = arr_window(A, I)
+    return out
 
 
 def pages_to_contiguous(pool, page_row, n, page_size):

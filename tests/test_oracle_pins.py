@@ -447,3 +447,79 @@ def test_append_and_commit_window():
     assert (Ka[:7] == 0).all() and (Ka[7:10] == Kw[:3]).all() and (Va[7:10] == -Kw[:3]).all()   # row n+3 falls off
     assert oracle.commit_window(7, 2, 4) == 9
     assert oracle.commit_window(7, 9, 4) == 11 and oracle.commit_window(7, -1, 4) == 7
+
+
+# --------------------------------------------------------------------------
+# Policy sweep (translation sections 3.2-3.3, Figs. 2-3; blog Table 3)
+# --------------------------------------------------------------------------
+def _sweep_case(seed, w=4, P=3, Hq=8, Hkv=2, d=16, n=40):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((n, Hkv, d))
+    K[rng.choice(n, 4, replace=False)] += 2.0          # a few salient keys
+    q_window = rng.standard_normal((w, Hq, d))
+    q_past = q_window[0] + 0.5 * rng.standard_normal((P, Hq, d)).cumsum(axis=0)
+    s_draft = rng.random(n)
+    s_target = rng.random(n)
+    return q_window, q_past, K, s_draft, s_target
+
+
+def test_sweep_oracle_row_bounds_every_policy_and_nested_rows_grow():
+    """Eq. (4): the SD oracle maximises the windowed ARR over all k-subsets,
+    so it bounds every policy row; TopK sets are nested in k, so the history,
+    draft, Dustin-T and Dustin-D rows are non-decreasing in k."""
+    qw, qp, K, sd, st = _sweep_case(1)
+    ks = [4, 6, 8, 12, 20, 39]
+    out = oracle.policy_sweep(qw, qp, K, sd, st, ks, [max(0, (k - 4) // 2) for k in ks], 2, 2)
+    assert out.shape == (3 + 5, len(ks))
+    assert (out[0][None, :] >= out - 1e-12).all()
+    for row in range(0, out.shape[0] - 1):                # Dustin-H's m changes with k
+        assert (np.diff(out[row]) >= -1e-12).all(), row
+    # brute force: the oracle row is the best k-subset at a small k
+    A = oracle.window_attention(qw, K)
+    best = max(oracle.arr_window(A, list(c)) for c in itertools.combinations(range(K.shape[0]), 2))
+    assert abs(oracle.policy_sweep(qw, qp, K, sd, st, [2], [0], 0, 0)[0, 0] - best) < 1e-12
+
+
+def test_sweep_full_budget_recovers_everything():
+    """ARR = 1 when the set covers V_i (translation section 3.1), for every policy."""
+    qw, qp, K, sd, st = _sweep_case(2, n=25)
+    out = oracle.policy_sweep(qw, qp, K, sd, st, [25, 40], [10, 10], 3, 5)
+    np.testing.assert_allclose(out, 1.0, atol=1e-12)
+
+
+def test_sweep_policies_reduce_to_the_oracle():
+    """Special cases that turn each policy into the SD oracle: a past query
+    equal to the (single) window query, draft scores equal to the window
+    mean Abar, and Dustin-T without protected tokens on S_Target = Abar."""
+    qw, qp, K, sd, st = _sweep_case(3, w=1, P=2)
+    qp = np.stack([qw[0], qp[1]])
+    Abar = oracle.window_attention(qw, K).mean(axis=0)
+    anti = 1.0 - Abar                                            # ranks the least attended first
+    ks = [3, 7, 15]
+    # draft scores = Abar, target scores anti-correlated
+    out = oracle.policy_sweep(qw, qp, K, Abar, anti, ks, [0, 0, 0], 0, 0)
+    np.testing.assert_allclose(out[1], out[0], atol=1e-15)     # history with delta = 0
+    np.testing.assert_allclose(out[3], out[0], atol=1e-15)     # draft lookahead = Abar
+    np.testing.assert_allclose(out[5], out[0], atol=1e-15)     # Dustin-D: all budget to the draft
+    assert (out[4] < out[0] - 1e-6).all()                       # Dustin-T ranks by the anti scores
+    assert not np.allclose(out[2], out[0])                      # the drifted query is worse
+    # the roles swapped
+    out = oracle.policy_sweep(qw, qp, K, anti, Abar, ks, [0, 0, 0], 0, 0)
+    np.testing.assert_allclose(out[4], out[0], atol=1e-15)     # Dustin-T on S_T = Abar
+    assert (out[3] < out[0] - 1e-6).all() and (out[5] < out[0] - 1e-6).all()
+
+
+def test_sweep_history_rows_use_the_past_query_attention():
+    """The history row ranks by A_{i-delta,.} (Eq. 1 with the past query), not
+    by the window: checked against a direct TopK of the past query's head
+    mean attention computed with scipy."""
+    qw, qp, K, sd, st = _sweep_case(4, P=1, Hq=4, Hkv=1)
+    d = K.shape[2]
+    logits = np.einsum("hd,nd->hn", qp[0], K[:, 0, :]) / np.sqrt(d)
+    Ap = scipy.special.softmax(logits, axis=1).mean(axis=0)
+    order = np.lexsort((np.arange(Ap.size), -Ap))
+    A = oracle.window_attention(qw, K)
+    for k in (3, 9):
+        want = A[:, np.sort(order[:k])].sum(axis=1).mean()
+        got = oracle.policy_sweep(qw, qp, K, sd, st, [k], [0], 0, 0)[1, 0]
+        assert abs(got - want) < 1e-12

@@ -184,6 +184,7 @@ SCORE_CASES = [
     ("qwen7b-ragged", dict(base="c2", B=3, n=2100, L_d=3, n_lo=900)),
     ("paged-drift", dict(base="c5", B=2, n=3000, n_lo=1200, L_d=2)),
     ("qwen72b-packed", dict(base="c4", B=2, n=1700, L_d=2, S=8)),
+    ("stream-ragged", dict(base="c2", B=3, n=5000, L_d=4, n_lo=700)),
     ("tiny-f32", dict(base="c1")),
 ]
 
