@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-window", action="store_true",
                    help="skip the verification-window step (append + causal verify attention + commit)")
+    p.add_argument("--no-sweep", action="store_true", help="skip the policy sweep (ARR of the compared policies)")
     p.add_argument("--pmc-probe", action="store_true",
                    help="for counter collection: one warm step, a 1 GiB float32 copy (the calibration "
                         "kernel of known size), then one more step; prints no JSON")
@@ -364,10 +365,52 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
+    if not args.no_sweep:
+        res["policy_sweep"] = policy_sweep(args, sh, x, kvs[0], s_d, s_t, n_sink, n_window, timed)
     if not args.no_window:
         # Last, because it writes the window rows into every layer's cache.
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
     print(json.dumps(res), flush=True)
+
+
+SWEEP_DELTAS = (1, 4, 16, 64)
+SWEEP_KS = (128, 256, 512, 1024, 2048)
+
+
+def policy_sweep(args, sh, x, kv, s_d, s_t, n_sink, n_window, timed):
+    """Windowed ARR (Eq. 2) of the compared selection policies on the step's
+    own scores and window queries, at several budgets: the SD oracle, the
+    history policy at look-back distances 1/4/16/64, the draft lookahead and
+    Dustin-T/D/H (mean over the batch), with the sweep's time and the
+    oracle's time for the same sweep of one sequence."""
+    import numpy as np
+    import synth
+    import sparse_kv_verification_amd as dk
+    qpast = synth.history_trajectory(x, SWEEP_DELTAS)
+    ks = [kk for kk in SWEEP_KS if kk >= n_sink + n_window]
+    ms = [synth.tier_defaults(kk)[2] for kk in ks]
+    ws = dk.Workspace()
+    arr = dk.dustin_policy_sweep(x.q, qpast, kv, s_d, s_t, ks, ms, n_sink, n_window, ws=ws)
+    us = timed(lambda: dk.dustin_policy_sweep(x.q, qpast, kv, s_d, s_t, ks, ms, n_sink, n_window, arr=arr, ws=ws),
+               max(2, args.steps // 4))
+    mean = arr.mean(dim=2).cpu().numpy()          # [policies][ks]
+    names = ["oracle"] + [f"history_delta{dd}" for dd in SWEEP_DELTAS] + ["draft", "dustin_T", "dustin_D", "dustin_H"]
+    table = {nm: {str(kk): round(float(mean[r, i]), 4) for i, kk in enumerate(ks)} for r, nm in enumerate(names)}
+    log(f"policy sweep {us:.0f} us ({len(names)} policies x {len(ks)} budgets); windowed ARR at k={ks[-1]}: " +
+        ", ".join(f"{nm} {mean[r, -1]:.3f}" for r, nm in enumerate(names)))
+    out = {"us_per_sweep": round(us, 1), "deltas": list(SWEEP_DELTAS), "ks": ks, "m_hybrid": ms,
+           "mean_windowed_arr": table}
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+        n = int(x.seq_lens[0])
+        K = f(x.logical("K", 0))
+        t0 = time.perf_counter()
+        oracle.policy_sweep(f(x.q[0]), f(qpast[:, 0]), K, f(s_d[0, :n]), f(s_t[0, :n]), ks, ms, n_sink, n_window)
+        dt = time.perf_counter() - t0
+        out["cpu_oracle_one_sequence_s"] = round(dt, 2)
+        out["cpu_oracle_scaled_us"] = round(dt * sh.B * 1e6, 0)
+    return out
 
 
 def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):

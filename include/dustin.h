@@ -16,7 +16,9 @@
  *      into the cache first and dustin_commit_window keeping the accepted
  *      tokens afterwards
  *   plus the evaluator of the translation's section 3.1 (attention recovery
- *   rate):                               -> dustin_window_attn, dustin_arr
+ *   rate):                               -> dustin_window_attn, dustin_arr,
+ *   and the policy comparison of its sections 3.2-3.3
+ *                                        -> dustin_window_mean, dustin_policy_sweep
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -34,11 +36,12 @@
  *   [0, num_pages) are treated as absent (never dereferenced).
  * - Workspace: pass at least the byte count the matching *_workspace_bytes()
  *   function returns for the same shape.  dustin_sparse_verify_attn,
- *   dustin_verify_attn and dustin_window_attn keep arrival counters in the
- *   first 64 KiB of their workspace (one slot per (sequence, KV head), so
- *   B * H_kv <= 16384): that region must be zero-filled before its first
+ *   dustin_verify_attn, dustin_window_attn and dustin_policy_sweep keep
+ *   arrival counters in the first 64 KiB of their workspace (one slot per
+ *   (sequence, KV head), so B * H_kv <= 16384): that region must be
+ *   zero-filled before its first
  *   use and every call leaves it zero again, so one workspace may serve
- *   successive calls of these three entry points of any shapes, but it must
+ *   successive calls of these entry points of any shapes, but it must
  *   not be handed to another entry point in between.  The other entry
  *   points make no assumption about workspace contents.
  *   Calls that may overlap in time must not share a workspace.
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 2
+#define DUSTIN_ABI_VERSION 3
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -281,6 +284,53 @@ size_t dustin_window_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q,
 dustin_status dustin_arr(const float *A, const int32_t *seq_lens, int32_t B, int32_t w,
                          int32_t N_max, const int32_t *idx, const int32_t *count, int32_t k,
                          float *arr_step, float *arr_window, dustin_stream_t stream);
+
+/*
+ * dustin_window_mean -- the averaged future attention of Eq. (3) in the
+ * translation's section 3.1: Abar[b][j] = (1/w) sum_{s < w} A[b][s][j]
+ * (TopK_k of Abar is the SD oracle's set, Eq. (4)).
+ *
+ *  A     [B][w][N_max] float32 (e.g. from dustin_window_attn)
+ *  Abar  out [B][N_max] float32
+ */
+dustin_status dustin_window_mean(const float *A, int32_t B, int32_t w, int32_t N_max, float *Abar,
+                                 dustin_stream_t stream);
+
+/*
+ * dustin_policy_sweep -- windowed ARR (Eq. 2) of the selection policies the
+ * pages compare, at every budget ks[i] (translation sections 3.2-3.3,
+ * Figs. 2-3, and the variants of the blog's Table 3), per sequence.  The
+ * ground truth is A of the w window queries (Eq. 1, head mean over one
+ * target layer).  Output rows:
+ *   row 0                   SD oracle: TopK_k of Abar (Eq. 3-4)
+ *   rows 1 .. n_past        history: TopK_k of A_{i-delta,.}, the head-mean
+ *                           full-cache attention of past query p (Fig. 2)
+ *   row n_past + 1          draft lookahead alone: TopK_k of S_Draft (Fig. 3)
+ *   rows n_past + 2 .. + 4  the dustin_topk verification set with m = 0
+ *                           (Dustin-T), m = k - n_sink - n_window (Dustin-D)
+ *                           and m = m_hybrid[i] (Dustin-H)
+ * Ties in every TopK: higher score first, then lower position.
+ *
+ *  q_window  [B][w][H_q][head_dim], kv dtype (w <= 16)
+ *  q_past    [n_past][B][H_q][head_dim], kv dtype; NULL when n_past == 0
+ *            (n_past <= 64)
+ *  kv        one target layer (k used)
+ *  s_draft, s_target  [B][N_max] float32 (e.g. from dustin_score)
+ *  ks, m_hybrid  host [nk]; every k >= n_sink + n_window, 0 <= m_hybrid <= k
+ *  arr       out [n_past + 5][nk][B] float32
+ *  ws        dustin_policy_sweep_workspace_bytes(..., max k) bytes; its first
+ *            64 KiB are arrival counters under the same rules as the
+ *            attention workspaces (zero-filled before first use, left zero)
+ * The calls run in order on `stream`.
+ */
+dustin_status dustin_policy_sweep(const void *q_window, int32_t w, const void *q_past, int32_t n_past,
+                                  int32_t H_q, const dustin_kv *kv, const float *s_draft,
+                                  const float *s_target, const int32_t *ks, const int32_t *m_hybrid,
+                                  int32_t nk, int32_t n_sink, int32_t n_window, float scale, float *arr,
+                                  void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_policy_sweep_workspace_bytes(int32_t B, int32_t w, int32_t n_past, int32_t H_q,
+                                           int32_t H_kv, int32_t head_dim, int32_t N_max, int32_t k_max);
 
 /* Human-readable name of a status code (static storage). */
 const char *dustin_status_string(dustin_status status);

@@ -25,7 +25,7 @@ EXPORTS = [
     "dustin_verify_attn", "dustin_verify_attn_workspace_bytes",
     "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
-    "dustin_arr",
+    "dustin_arr", "dustin_window_mean", "dustin_policy_sweep", "dustin_policy_sweep_workspace_bytes",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
 ]
 
@@ -89,6 +89,13 @@ def lib():
         L.dustin_window_attn_workspace_bytes.restype = sz
         L.dustin_arr.argtypes = [vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, vp]
         L.dustin_arr.restype = ctypes.c_int
+        L.dustin_window_mean.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.dustin_window_mean.restype = ctypes.c_int
+        L.dustin_policy_sweep.argtypes = [vp, i32, vp, i32, i32, kvp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, sz,
+                                          vp]
+        L.dustin_policy_sweep.restype = ctypes.c_int
+        L.dustin_policy_sweep_workspace_bytes.argtypes = [i32] * 8
+        L.dustin_policy_sweep_workspace_bytes.restype = sz
         L.dustin_status_string.argtypes = [ctypes.c_int]
         L.dustin_status_string.restype = ctypes.c_char_p
         L.dustin_last_error.argtypes = []
@@ -308,3 +315,42 @@ def dustin_arr(A, seq_lens, idx, count, arr_step=None, arr_window=None):
     _check(lib().dustin_arr(_ptr(A), _ptr(seq_lens), B, w, N, _ptr(idx), _ptr(count), k, _ptr(arr_step),
                             _ptr(arr_window), _stream(A)))
     return arr_step, arr_window
+
+
+def dustin_window_mean(A, Abar=None):
+    """Eq. (3)'s averaged future attention Abar [B][N_max] of A [B][w][N_max]."""
+    B, w, N = A.shape
+    if Abar is None:
+        Abar = torch.empty((B, N), dtype=torch.float32, device=A.device)
+    _check(lib().dustin_window_mean(_ptr(A), B, w, N, _ptr(Abar), _stream(A)))
+    return Abar
+
+
+POLICY_NAMES = ("oracle", "history", "draft", "dustin_T", "dustin_D", "dustin_H")
+
+
+def dustin_policy_sweep(q_window, q_past, kv: KV, s_draft, s_target, ks, m_hybrid, n_sink, n_window, scale=0.0,
+                        arr=None, ws: Workspace | None = None):
+    """Windowed ARR of the compared selection policies at each budget:
+    arr [n_past + 5][len(ks)][B]; rows: SD oracle, one history row per past
+    query, draft lookahead, Dustin-T, Dustin-D, Dustin-H.
+    q_window [B][w][H_q][d]; q_past [n_past][B][H_q][d] or None."""
+    B, w, Hq, D = q_window.shape
+    n_past = 0 if q_past is None else q_past.shape[0]
+    nk = len(ks)
+    d = kv.desc
+    for t in (s_draft, s_target):
+        if tuple(t.shape) != (d.B, d.N_max) or not t.is_contiguous():
+            raise ValueError(f"score vectors must be contiguous [B][N_max] = [{d.B}][{d.N_max}], got {tuple(t.shape)}")
+    if q_past is not None and tuple(q_past.shape[1:]) != (B, Hq, D):
+        raise ValueError(f"q_past must be [n_past][B][H_q][d], got {tuple(q_past.shape)}")
+    if arr is None:
+        arr = torch.empty((n_past + 5, nk, B), dtype=torch.float32, device=q_window.device)
+    kbuf = (ctypes.c_int32 * nk)(*[int(k) for k in ks])
+    mbuf = (ctypes.c_int32 * nk)(*[int(m) for m in m_hybrid])
+    nbytes = lib().dustin_policy_sweep_workspace_bytes(d.B, w, n_past, Hq, d.H_kv, d.head_dim, d.N_max, max(ks))
+    wsb = _ws("sweep", ws, nbytes, q_window.device)
+    _check(lib().dustin_policy_sweep(_ptr(q_window), w, _ptr(q_past), n_past, Hq, kv.ref, _ptr(s_draft),
+                                     _ptr(s_target), kbuf, mbuf, nk, n_sink, n_window, float(scale), _ptr(arr),
+                                     _ptr(wsb), wsb.numel(), _stream(q_window)))
+    return arr

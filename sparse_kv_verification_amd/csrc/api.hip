@@ -464,3 +464,123 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
 }
 
 }  // extern "C"
+
+namespace {
+// Sweep workspace: the window-attention workspace first (its arrival
+// counters at offset 0), then A of the window [B][w][N], Abar [B][N], the
+// past queries' A [P][B][N], one index set [B][k_max] with its counts, and
+// the select workspace.
+struct SweepLayout {
+    size_t attn_bytes, off_awin, off_abar, off_apast, off_idx, off_cnt, off_topk, bytes;
+};
+
+SweepLayout sweep_layout(int B, int w, int P, int H_q, int H_kv, int D, int N, int k_max) {
+    SweepLayout L{};
+    const size_t a1 = window_layout(B, w, H_q, H_kv, D, N, 4).bytes;
+    const size_t a2 = window_layout(B, 1, H_q, H_kv, D, N, 4).bytes;
+    L.attn_bytes = a1 > a2 ? a1 : a2;
+    size_t off = align_up(L.attn_bytes, 256);
+    L.off_awin = off;
+    off = align_up(off + (size_t)B * w * N * sizeof(float), 256);
+    L.off_abar = off;
+    off = align_up(off + (size_t)B * N * sizeof(float), 256);
+    L.off_apast = off;
+    off = align_up(off + (size_t)P * B * N * sizeof(float), 256);
+    L.off_idx = off;
+    off = align_up(off + (size_t)B * k_max * sizeof(int32_t), 256);
+    L.off_cnt = off;
+    off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+    L.off_topk = off;
+    off = align_up(off + topk_plan(B, N, k_max).ws_bytes, 256);
+    L.bytes = off;
+    return L;
+}
+}  // namespace
+
+extern "C" {
+
+dustin_status dustin_window_mean(const float *A, int32_t B, int32_t w, int32_t N_max, float *Abar,
+                                 dustin_stream_t stream) {
+    CHECK(A != nullptr && Abar != nullptr, DUSTIN_ERR_INVALID_ARG, "window_mean: A and Abar are required");
+    CHECK(B >= 1 && w >= 1 && N_max >= 1, DUSTIN_ERR_INVALID_ARG, "window_mean: B, w and N_max must be >= 1");
+    return hip_status(launch_window_mean(A, B, w, N_max, Abar, (hipStream_t)stream), "window_mean launch");
+}
+
+size_t dustin_policy_sweep_workspace_bytes(int32_t B, int32_t w, int32_t n_past, int32_t H_q, int32_t H_kv,
+                                           int32_t head_dim, int32_t N_max, int32_t k_max) {
+    if (B < 1 || w < 1 || n_past < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv || head_dim < 1 || N_max < 1 || k_max < 1)
+        return 0;
+    return sweep_layout(B, w, n_past, H_q, H_kv, head_dim, N_max, k_max).bytes;
+}
+
+dustin_status dustin_policy_sweep(const void *q_window, int32_t w, const void *q_past, int32_t n_past, int32_t H_q,
+                                  const dustin_kv *kv, const float *s_draft, const float *s_target,
+                                  const int32_t *ks, const int32_t *m_hybrid, int32_t nk, int32_t n_sink,
+                                  int32_t n_window, float scale, float *arr, void *ws, size_t ws_bytes,
+                                  dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "policy_sweep kv", false);
+    if (st != DUSTIN_OK) return st;
+    if ((st = check_attn_shape(kv, w, H_q, "policy_sweep")) != DUSTIN_OK) return st;
+    CHECK(w <= 16, DUSTIN_ERR_UNSUPPORTED, "policy_sweep: w %d exceeds 16", w);
+    CHECK(n_past >= 0 && n_past <= 64, DUSTIN_ERR_UNSUPPORTED, "policy_sweep: n_past %d outside [0, 64]", n_past);
+    CHECK(q_window != nullptr && (n_past == 0 || q_past != nullptr), DUSTIN_ERR_INVALID_ARG,
+          "policy_sweep: q_window (and q_past when n_past > 0) are required");
+    CHECK(s_draft != nullptr && s_target != nullptr && arr != nullptr, DUSTIN_ERR_INVALID_ARG,
+          "policy_sweep: s_draft, s_target and arr are required");
+    CHECK(ks != nullptr && m_hybrid != nullptr && nk >= 1, DUSTIN_ERR_INVALID_ARG,
+          "policy_sweep: ks, m_hybrid (host arrays) and nk >= 1 are required");
+    CHECK(n_sink >= 0 && n_window >= 0, DUSTIN_ERR_INVALID_ARG, "policy_sweep: n_sink and n_window must be >= 0");
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "policy_sweep: scale is not finite");
+    int k_max = 1;
+    for (int i = 0; i < nk; ++i) {
+        CHECK(ks[i] >= 1 && (int64_t)n_sink + n_window <= ks[i], DUSTIN_ERR_INVALID_ARG,
+              "policy_sweep: ks[%d] = %d must be >= 1 and >= n_sink + n_window", i, ks[i]);
+        CHECK(m_hybrid[i] >= 0 && m_hybrid[i] <= ks[i], DUSTIN_ERR_INVALID_ARG,
+              "policy_sweep: m_hybrid[%d] = %d outside [0, k]", i, m_hybrid[i]);
+        if (ks[i] > k_max) k_max = ks[i];
+    }
+    const int B = kv->B, N = kv->N_max;
+    const SweepLayout L = sweep_layout(B, w, n_past, H_q, kv->H_kv, kv->head_dim, N, k_max);
+    CHECK(ws != nullptr && ws_bytes >= L.bytes, DUSTIN_ERR_INVALID_ARG,
+          "policy_sweep: workspace of %zu bytes needed (got %zu)", L.bytes, ws_bytes);
+    char *wsb = (char *)ws;
+    float *Awin = (float *)(wsb + L.off_awin);
+    float *Abar = (float *)(wsb + L.off_abar);
+    float *Apast = (float *)(wsb + L.off_apast);
+    int32_t *idx = (int32_t *)(wsb + L.off_idx);
+    int32_t *cnt = (int32_t *)(wsb + L.off_cnt);
+    void *tws = wsb + L.off_topk;
+    const size_t tbytes = L.bytes - L.off_topk;
+    // ground truth: A of the window (Eq. 1) and its mean (Eq. 3)
+    if ((st = dustin_window_attn(q_window, w, H_q, kv, scale, Awin, wsb, L.attn_bytes, stream)) != DUSTIN_OK)
+        return st;
+    {
+        const hipError_t e = launch_window_mean(Awin, B, w, N, Abar, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e, "policy_sweep window mean");
+    }
+    // A_{i-delta,.} of each past query (a one-step window each)
+    const size_t esz = kv->dtype == DUSTIN_F32 ? 4 : 2;
+    const size_t qstride = (size_t)B * H_q * kv->head_dim * esz;
+    for (int p = 0; p < n_past; ++p)
+        if ((st = dustin_window_attn((const char *)q_past + p * qstride, 1, H_q, kv, scale, Apast + (size_t)p * B * N,
+                                     wsb, L.attn_bytes, stream)) != DUSTIN_OK)
+            return st;
+    auto eval = [&](const float *sd, const float *stg, int k, int m, int ns, int nw, int row, int ki) {
+        dustin_status e = dustin_topk(sd, stg, kv->seq_lens, B, N, k, m, ns, nw, idx, cnt, nullptr, tws, tbytes, stream);
+        if (e != DUSTIN_OK) return e;
+        return dustin_arr(Awin, kv->seq_lens, B, w, N, idx, cnt, k, nullptr, arr + ((size_t)row * nk + ki) * B, stream);
+    };
+    for (int ki = 0; ki < nk; ++ki) {
+        const int k = ks[ki];
+        if ((st = eval(nullptr, Abar, k, 0, 0, 0, 0, ki)) != DUSTIN_OK) return st;
+        for (int p = 0; p < n_past; ++p)
+            if ((st = eval(nullptr, Apast + (size_t)p * B * N, k, 0, 0, 0, 1 + p, ki)) != DUSTIN_OK) return st;
+        if ((st = eval(s_draft, nullptr, k, k, 0, 0, n_past + 1, ki)) != DUSTIN_OK) return st;
+        const int ms[3] = {0, k - n_sink - n_window, m_hybrid[ki]};
+        for (int r = 0; r < 3; ++r)
+            if ((st = eval(s_draft, s_target, k, ms[r], n_sink, n_window, n_past + 2 + r, ki)) != DUSTIN_OK) return st;
+    }
+    return ok();
+}
+
+}  // extern "C"

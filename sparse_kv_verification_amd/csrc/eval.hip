@@ -149,4 +149,22 @@ hipError_t launch_arr(const ArrArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Eq. (3)'s averaged future attention: Abar[b][j] = (1/w) sum_s A[b][s][j],
+// summed in window order.
+__global__ __launch_bounds__(256) void window_mean_kernel(const float *A, int B, int w, int N, float *Abar) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)B * N) return;
+    const int64_t b = e / N, j = e - (e / N) * N;
+    const float *a = A + b * w * N + j;
+    float t = 0.f;
+    for (int s = 0; s < w; ++s) t += a[(int64_t)s * N];
+    Abar[e] = t / (float)w;
+}
+
+hipError_t launch_window_mean(const float *A, int B, int w, int N, float *Abar, hipStream_t s) {
+    const int64_t n = (int64_t)B * N;
+    hipLaunchKernelGGL(window_mean_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, A, B, w, N, Abar);
+    return hipGetLastError();
+}
+
 }  // namespace dustin

@@ -147,6 +147,7 @@ struct ArrArgs {
     float *arr_step, *arr_window;
 };
 hipError_t launch_arr(const ArrArgs &a, hipStream_t s);
+hipError_t launch_window_mean(const float *A, int B, int w, int N, float *Abar, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

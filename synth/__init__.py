@@ -39,7 +39,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Shape", "PRESETS", "preset", "make", "tier_defaults", "spread_heads"]
+__all__ = ["Shape", "PRESETS", "preset", "make", "tier_defaults", "spread_heads", "history_trajectory"]
 
 
 @dataclass(frozen=True)
@@ -117,7 +117,7 @@ def spread_heads(shape):
 
 
 _STREAMS = ["K", "V", "heavy", "dirs", "salience", "q", "drift_q", "proj",
-            "draft_k_noise", "draft_q_noise", "lens", "pages"]
+            "draft_k_noise", "draft_q_noise", "lens", "pages", "trajectory"]
 
 
 def _gen(master, stream, device):
@@ -245,6 +245,7 @@ def make(shape: Shape, seed=None, device="cpu"):
         else:
             steps.append(base + 0.2 * _randn((B, Hq, d), gdq, dev))
     q_all = torch.stack(steps, dim=1)           # [B][w+1][Hq][d], index 0 = history
+    q_prev = q_all[:, 0].clone()                 # q_{i-1}, every head (float32)
     q = q_all[:, 1:]
     sub_heads = spread_heads(shape)
     q_hist = torch.stack([q_all[:, 0, h] for (_, h) in sub_heads], dim=1)   # [B][S][d]
@@ -320,4 +321,27 @@ def make(shape: Shape, seed=None, device="cpu"):
 
     return Inputs(shape=shape, seq_lens=lens.to(torch.int32).to(dev), q=q, q_hist=q_hist,
                   sub_heads=sub_heads, q_draft=q_draft, K=K.contiguous(), V=V.contiguous(),
-                  Kd=Kd.contiguous(), page_table=page_table)
+                  Kd=Kd.contiguous(), page_table=page_table, extra={"q_prev": q_prev, "master": master})
+
+
+def history_trajectory(x: Inputs, deltas):
+    """Past target queries q_{i-delta} for each delta in ``deltas`` (all >= 1),
+    [len(deltas)][B][Hq][d] in the storage dtype: q_{i-1} is the generator's
+    history query, and each earlier step adds an independent N(0, 0.2^2)
+    drift, q_{i-t} = q_{i-t+1} + 0.2 * z_t (the same per-step drift the
+    window queries carry), so a query further back has drifted further."""
+    deltas = [int(t) for t in deltas]
+    assert deltas and min(deltas) >= 1
+    shape = x.shape
+    dev = x.q.device
+    g = _gen(x.extra["master"], "trajectory", dev)
+    cur = x.extra["q_prev"].clone()
+    want = {t: i for i, t in enumerate(deltas)}
+    out = [None] * len(deltas)
+    for t in range(1, max(deltas) + 1):
+        if t > 1:
+            cur = cur + 0.2 * _randn(tuple(cur.shape), g, dev)
+        if t in want:
+            out[want[t]] = cur.clone()
+    store = x.q.dtype
+    return torch.stack(out).to(store).contiguous()

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.dustin_abi_version() == 2
+    assert L.dustin_abi_version() == 3
     assert L.dustin_status_string(0) == b"DUSTIN_OK"
     assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
 
@@ -155,6 +155,32 @@ def test_verify_window_argument_errors(L):
     assert L.dustin_commit_window(FAKE, None, 2, 4, None) == INVALID
     assert L.dustin_commit_window(FAKE, FAKE, 0, 4, None) == INVALID
     assert L.dustin_commit_window(FAKE, FAKE, 2, 0, None) == INVALID
+
+
+def test_sweep_argument_errors(L):
+    desc = kv()
+    ks = (ctypes.c_int32 * 3)(128, 512, 2048)
+    ms = (ctypes.c_int32 * 3)(46, 238, 1006)
+    def f(**kw):
+        return L.dustin_policy_sweep(kw.get("qw", FAKE), kw.get("w", 4), kw.get("qp", FAKE), kw.get("P", 4),
+                                     kw.get("Hq", 64), ctypes.byref(kw.get("desc", desc)), kw.get("sd", FAKE),
+                                     kw.get("st", FAKE), kw.get("ks", ks), kw.get("ms", ms), kw.get("nk", 3),
+                                     kw.get("ns", 4), kw.get("nw", 32), 0.0, kw.get("arr", FAKE), FAKE,
+                                     kw.get("ws", 1 << 40), None)
+    assert f(qw=None) == INVALID
+    assert f(qp=None) == INVALID                          # n_past > 0 needs q_past
+    assert f(sd=None) == INVALID and f(st=None) == INVALID and f(arr=None) == INVALID
+    assert f(ks=None) == INVALID and f(nk=0) == INVALID
+    assert f(w=17) == UNSUPPORTED
+    assert f(P=65) == UNSUPPORTED
+    assert f(ks=(ctypes.c_int32 * 3)(16, 512, 2048)) == INVALID              # k < n_sink + n_window
+    assert f(ms=(ctypes.c_int32 * 3)(200, 238, 1006)) == INVALID             # m_hybrid > k
+    need = L.dustin_policy_sweep_workspace_bytes(2, 4, 4, 64, 8, 128, 4096, 2048)
+    assert need > L.dustin_window_attn_workspace_bytes(2, 4, 64, 8, 128, 4096)
+    assert f(ws=need - 1) == INVALID
+    assert b"workspace" in L.dustin_last_error()
+    assert L.dustin_window_mean(None, 2, 4, 10, FAKE, None) == INVALID
+    assert L.dustin_window_mean(FAKE, 2, 0, 10, FAKE, None) == INVALID
 
 
 def test_workspace_sizes_are_shape_only(L):

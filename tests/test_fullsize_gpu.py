@@ -143,3 +143,35 @@ def test_c4_verify_step_with_window():
         err, lerr = np.abs(f64(out[b]) - O).max(), np.abs(f64(lse[b]) - L).max()
         say(f"  b={b} |I|={c} max|dO|={err:.2e} max|dlse|={lerr:.2e}")
         assert err <= 2e-2 and lerr <= 2e-3
+
+
+def test_c4_policy_sweep():
+    """The policy sweep on the 72B-shaped workload (B=16, 32k) with the
+    look-back distances of Fig. 2 and the budgets of the k sweep; two sampled
+    sequences against the oracle.  Scores: seeded synthetic [B][N_max]."""
+    say("full-size c4 policy sweep")
+    sh = synth.preset("c4").replace(layers=1, L_d=1)
+    x = synth.make(sh, device=DEV)
+    deltas, ks = [1, 4, 16, 64], [128, 512, 2048]
+    qpast = synth.history_trajectory(x, deltas)
+    kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    sd = (torch.rand((sh.B, sh.n), generator=g, device=DEV) ** 4).contiguous()
+    st = (torch.rand((sh.B, sh.n), generator=g, device=DEV) ** 4).contiguous()
+    ms = [synth.tier_defaults(k)[2] for k in ks]
+    arr = dk.dustin_policy_sweep(x.q, qpast, kv, sd, st, ks, ms, 4, 32).cpu().numpy()
+    P = len(deltas)
+    for b in (2, sh.B - 1):
+        K = oracle_kv(x, "K", b)
+        want = oracle.policy_sweep(f64(x.q[b]), f64(qpast[:, b]), K, f64(sd[b]), f64(st[b]), ks, ms, 4, 32)
+        A = oracle.window_attention(f64(x.q[b]), K)
+        rank = [A.mean(axis=0)] + [oracle.window_attention(f64(qpast[p, b])[None], K)[0] for p in range(P)]
+        for row in range(P + 5):
+            for ki, k in enumerate(ks):
+                s = np.sort(rank[row])[::-1] if row <= P else None
+                if s is not None and (s[k - 1] - s[k]) / s[k - 1] < 2e-4:
+                    assert arr[row, ki, b] <= want[0, ki] + 1e-4
+                    continue
+                assert abs(arr[row, ki, b] - want[row, ki]) <= 1e-4, (b, row, k)
+        say(f"  b={b} k=2048: oracle {want[0, -1]:.4f} history {np.round(want[1:P + 1, -1], 4)}")
