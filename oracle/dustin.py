@@ -14,6 +14,8 @@ Decoding", arXiv 2606.24957):
   section 3.2: history attention A_{i-delta,.} (delta = 1 for S_Target; the
   history-policy comparison of Fig. 2 over several delta);
   section 3.3 (Fig. 3): the draft lookahead compared with the oracle;
+  related work: Quest's page scoring from min/max key statistics (the
+  page-level estimator of section 5.4.1);
 * the blog summary (liuzhao09.github.io), section 2.2 (hybrid aggregation:
   S_Draft over H_d, L_d, Gamma; S_Target over H_t, L_t; one global index
   set), section 2.3 (verification set: protected sink + recent window, draft
@@ -64,6 +66,8 @@ __all__ = [
     "select_verify_set",
     "history_policy",
     "policy_sweep",
+    "page_key_bounds",
+    "page_scores",
     "topk_desc",
     "protected_positions",
     "pages_to_contiguous",
@@ -422,6 +426,46 @@ def policy_sweep(q_window, q_past, K, s_draft, s_target, ks, m_hybrid, n_sink, n
         for r, m in enumerate(ms):
             I, _ = select_verify_set(s_draft, s_target, n, k, m, n_sink, n_window)
             out[P + 2 + r, ki] = arr_window(A, I)
+    return out
+
+
+def page_key_bounds(K, n, page=16):
+    """Page statistics of the page-level estimator the pages compare with
+    (Quest, in the translation's related work: the full cache stays and
+    pages are scored with cheap min/max key statistics instead of exact
+    QK^T; Quest-16 in the blog's Fig. 8): for each page of `page`
+    consecutive history positions and each KV head, the elementwise minimum
+    and maximum of the keys over the page's positions below n.
+    K [>= n][Hkv][d] -> (kmin, kmax), each [ceil(n / page)][Hkv][d]."""
+    K = _f64(K)[:n]
+    npg = -(-n // page)
+    kmin = np.empty((npg,) + K.shape[1:])
+    kmax = np.empty((npg,) + K.shape[1:])
+    for p in range(npg):
+        blk = K[p * page:min(n, (p + 1) * page)]
+        kmin[p] = blk.min(axis=0)
+        kmax[p] = blk.max(axis=0)
+    return kmin, kmax
+
+
+def page_scores(q, kmin, kmax, scale=None):
+    """Page criticality from the bounds alone: for window step s and query
+    head h (KV head g(h)), the largest value scale * q . k can take over any
+    key inside the page's box, scale * sum_d max(q_d kmin_d, q_d kmax_d).
+    Reading taken for one global page set: these bounds summed over the
+    window steps and query heads (as S_Target sums its heads).
+    q [w][Hq][d]; kmin, kmax [npages][Hkv][d] -> [npages]."""
+    q = _f64(q)
+    w, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kmin, kmax = _f64(kmin), _f64(kmax)
+    out = np.zeros(kmin.shape[0])
+    for h in range(Hq):
+        g = _kv_head_of(h, Hq, kmin.shape[1])
+        for s in range(w):
+            qq = q[s, h]
+            out += scale * np.maximum(kmin[:, g, :] * qq, kmax[:, g, :] * qq).sum(axis=1)
     return out
 
 

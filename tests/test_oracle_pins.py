@@ -523,3 +523,59 @@ def test_sweep_history_rows_use_the_past_query_attention():
         want = A[:, np.sort(order[:k])].sum(axis=1).mean()
         got = oracle.policy_sweep(qw, qp, K, sd, st, [k], [0], 0, 0)[1, 0]
         assert abs(got - want) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Page-level estimator (Quest-16 of the blog's Fig. 8)
+# --------------------------------------------------------------------------
+def test_page_bounds_enclose_and_touch_the_keys():
+    """Every key of a page lies inside its box, each face is reached by some
+    key of the page, single-token pages collapse to the key, and the ragged
+    last page covers only the positions below n."""
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((50, 3, 8))
+    kmin, kmax = oracle.page_key_bounds(K, 37, page=16)
+    assert kmin.shape == (3, 3, 8)
+    for p in range(3):
+        blk = K[p * 16:min(37, p * 16 + 16)]
+        assert (blk >= kmin[p] - 0).all() and (blk <= kmax[p]).all()
+        assert (np.isclose(blk, kmin[p]).any(axis=0)).all() and (np.isclose(blk, kmax[p]).any(axis=0)).all()
+    assert not np.allclose(kmax[2], K[32:48].max(axis=0))          # positions 37.. excluded
+    k1, x1 = oracle.page_key_bounds(K, 7, page=1)
+    assert np.array_equal(k1, K[:7]) and np.array_equal(x1, K[:7])
+
+
+def test_page_scores_bound_the_logits_and_match_the_box_corners():
+    """The score bounds the page's summed logits from above, is exact for
+    single-token pages, and equals brute force over the 2^d corners of the
+    box (per head and step); a one-hot key pins the head -> KV head map."""
+    rng = np.random.default_rng(6)
+    w, Hq, Hkv, d, n = 2, 4, 2, 3, 40
+    q = rng.standard_normal((w, Hq, d))
+    K = rng.standard_normal((n, Hkv, d))
+    kmin, kmax = oracle.page_key_bounds(K, n, 8)
+    sc = oracle.page_scores(q, kmin, kmax)
+    G = Hq // Hkv
+    s = 1 / np.sqrt(d)
+    for p in range(5):
+        blk = K[p * 8:(p + 1) * 8]
+        exact = max(sum(s * q[t, h] @ blk[j, h // G] for t in range(w) for h in range(Hq)) for j in range(8))
+        assert sc[p] >= exact - 1e-12
+        corners = 0.0
+        for t in range(w):
+            for h in range(Hq):
+                g = h // G
+                corners += s * max(q[t, h] @ np.where(c, kmax[p, g], kmin[p, g])
+                                   for c in itertools.product([False, True], repeat=d))
+        assert abs(sc[p] - corners) < 1e-12
+    k1, x1 = oracle.page_key_bounds(K, n, 1)
+    exact1 = np.array([sum(s * q[t, h] @ K[j, h // G] for t in range(w) for h in range(Hq)) for j in range(n)])
+    np.testing.assert_allclose(oracle.page_scores(q, k1, x1), exact1, atol=1e-12)
+    # one-hot: only KV head 1 holds a key, so only heads G.. 2G-1 see it
+    K2 = np.zeros((1, Hkv, d))
+    K2[0, 1, 0] = 1.0
+    q2 = np.zeros((1, Hq, d))
+    q2[0, G, 0] = 2.0                 # a head of group 1
+    q2[0, 0, 0] = 5.0                 # a head of group 0 (sees a zero key)
+    b0, b1 = oracle.page_key_bounds(K2, 1, 1)
+    assert abs(oracle.page_scores(q2, b0, b1)[0] - 2.0 / np.sqrt(d)) < 1e-15
