@@ -19,6 +19,8 @@
  *   rate):                               -> dustin_window_attn, dustin_arr,
  *   and the policy comparison of its sections 3.2-3.3
  *                                        -> dustin_window_mean, dustin_policy_sweep
+ *   and the page-level estimator the pages compare scoring costs with
+ *                                        -> dustin_page_bounds, dustin_page_scores
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 3
+#define DUSTIN_ABI_VERSION 4
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -331,6 +333,39 @@ dustin_status dustin_policy_sweep(const void *q_window, int32_t w, const void *q
 
 size_t dustin_policy_sweep_workspace_bytes(int32_t B, int32_t w, int32_t n_past, int32_t H_q,
                                            int32_t H_kv, int32_t head_dim, int32_t N_max, int32_t k_max);
+
+/*
+ * dustin_page_bounds -- page statistics of the page-level estimator the
+ * pages compare Dustin's scoring with (Quest in the translation's related
+ * work: pages scored from cheap min/max key statistics; Quest-16 in the
+ * blog's Fig. 8): for every 16-position page p and KV head g,
+ *   kmin[b][p][g][d] = min_{j in page p, j < n_b} K[b][j][g][d], kmax likewise.
+ * Pages with no position below n_b are written as 0.
+ *
+ *  kv          k used (contiguous, or paged with its own 16-position pages)
+ *  kmin, kmax  out [B][ceil(N_max / 16)][H_kv][head_dim], kv dtype (exact:
+ *              the bounds are stored values); 16-byte aligned
+ */
+dustin_status dustin_page_bounds(const dustin_kv *kv, void *kmin, void *kmax, dustin_stream_t stream);
+
+/*
+ * dustin_page_scores -- page criticality from the bounds alone (no QK^T):
+ *   scores[b][p] = scale * sum_{s < w} sum_{h < H_q} sum_d
+ *                  max(q[b][s][h][d] * kmin[b][p][g(h)][d], q[b][s][h][d] * kmax[b][p][g(h)][d])
+ * (the per-head bound of scale * q . k over the page's box, summed over the
+ * window steps and heads for one global page set); 0 for pages with no
+ * position below n_b.
+ *
+ *  q       [B][w][H_q][head_dim], kv dtype; 16-byte aligned
+ *  kmin, kmax  from dustin_page_bounds
+ *  scale   0 means 1/sqrt(head_dim)
+ *  scores  out [B][ceil(N_max / 16)] float32
+ *
+ * Both calls need H_kv * head_dim <= 8192 (else DUSTIN_ERR_UNSUPPORTED).
+ */
+dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                 const void *kmin, const void *kmax, float scale, float *scores,
+                                 dustin_stream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *dustin_status_string(dustin_status status);

@@ -26,6 +26,7 @@ EXPORTS = [
     "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
     "dustin_arr", "dustin_window_mean", "dustin_policy_sweep", "dustin_policy_sweep_workspace_bytes",
+    "dustin_page_bounds", "dustin_page_scores",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
 ]
 
@@ -96,6 +97,10 @@ def lib():
         L.dustin_policy_sweep.restype = ctypes.c_int
         L.dustin_policy_sweep_workspace_bytes.argtypes = [i32] * 8
         L.dustin_policy_sweep_workspace_bytes.restype = sz
+        L.dustin_page_bounds.argtypes = [kvp, vp, vp, vp]
+        L.dustin_page_bounds.restype = ctypes.c_int
+        L.dustin_page_scores.argtypes = [vp, i32, i32, kvp, vp, vp, f32, vp, vp]
+        L.dustin_page_scores.restype = ctypes.c_int
         L.dustin_status_string.argtypes = [ctypes.c_int]
         L.dustin_status_string.restype = ctypes.c_char_p
         L.dustin_last_error.argtypes = []
@@ -354,3 +359,26 @@ def dustin_policy_sweep(q_window, q_past, kv: KV, s_draft, s_target, ks, m_hybri
                                      _ptr(s_target), kbuf, mbuf, nk, n_sink, n_window, float(scale), _ptr(arr),
                                      _ptr(wsb), wsb.numel(), _stream(q_window)))
     return arr
+
+
+def dustin_page_bounds(kv: KV, kmin=None, kmax=None):
+    """Page min/max key bounds [B][ceil(N_max/16)][H_kv][d] (kv dtype)."""
+    d = kv.desc
+    shape = (d.B, (d.N_max + 15) // 16, d.H_kv, d.head_dim)
+    if kmin is None:
+        kmin = torch.empty(shape, dtype=kv.k.dtype, device=kv.k.device)
+    if kmax is None:
+        kmax = torch.empty(shape, dtype=kv.k.dtype, device=kv.k.device)
+    _check(lib().dustin_page_bounds(kv.ref, _ptr(kmin), _ptr(kmax), _stream(kv.k)))
+    return kmin, kmax
+
+
+def dustin_page_scores(q, kv: KV, kmin, kmax, scale=0.0, scores=None):
+    """Page scores [B][ceil(N_max/16)] float32 from the bounds."""
+    B, w, Hq, D = q.shape
+    d = kv.desc
+    if scores is None:
+        scores = torch.empty((d.B, (d.N_max + 15) // 16), dtype=torch.float32, device=q.device)
+    _check(lib().dustin_page_scores(_ptr(q), w, Hq, kv.ref, _ptr(kmin), _ptr(kmax), float(scale), _ptr(scores),
+                                    _stream(q)))
+    return scores

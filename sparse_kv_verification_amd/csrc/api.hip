@@ -584,3 +584,49 @@ dustin_status dustin_policy_sweep(const void *q_window, int32_t w, const void *q
 }
 
 }  // extern "C"
+
+extern "C" {
+
+dustin_status dustin_page_bounds(const dustin_kv *kv, void *kmin, void *kmax, dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "page_bounds kv", false);
+    if (st != DUSTIN_OK) return st;
+    CHECK(kmin != nullptr && kmax != nullptr, DUSTIN_ERR_INVALID_ARG, "page_bounds: kmin and kmax are required");
+    CHECK(kv->H_kv * kv->head_dim <= kPageMaxRow, DUSTIN_ERR_UNSUPPORTED,
+          "page_bounds: H_kv * head_dim = %d exceeds %d", kv->H_kv * kv->head_dim, kPageMaxRow);
+    CHECK(((uintptr_t)kmin | (uintptr_t)kmax | (uintptr_t)kv->k) % 16 == 0, DUSTIN_ERR_INVALID_ARG,
+          "page_bounds: k, kmin and kmax must be 16-byte aligned");
+    PageArgs a{};
+    a.kv = view_of(kv);
+    a.kmin = kmin;
+    a.kmax = kmax;
+    a.npages = (kv->N_max + 15) / 16;
+    return hip_status(launch_page_bounds(a, (hipStream_t)stream), "page_bounds launch");
+}
+
+dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv, const void *kmin,
+                                 const void *kmax, float scale, float *scores, dustin_stream_t stream) {
+    dustin_status st = check_kv(kv, "page_scores kv", false);
+    if (st != DUSTIN_OK) return st;
+    CHECK(q != nullptr && kmin != nullptr && kmax != nullptr && scores != nullptr, DUSTIN_ERR_INVALID_ARG,
+          "page_scores: q, kmin, kmax and scores are required");
+    CHECK(w >= 1 && H_q >= 1 && H_q % kv->H_kv == 0, DUSTIN_ERR_INVALID_ARG,
+          "page_scores: w >= 1 and H_q a multiple of H_kv are required");
+    CHECK(kv->H_kv * kv->head_dim <= kPageMaxRow, DUSTIN_ERR_UNSUPPORTED,
+          "page_scores: H_kv * head_dim = %d exceeds %d", kv->H_kv * kv->head_dim, kPageMaxRow);
+    CHECK(((uintptr_t)q | (uintptr_t)kmin | (uintptr_t)kmax) % 16 == 0, DUSTIN_ERR_INVALID_ARG,
+          "page_scores: q, kmin and kmax must be 16-byte aligned");
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "page_scores: scale is not finite");
+    PageArgs a{};
+    a.kv = view_of(kv);
+    a.q = q;
+    a.w = w;
+    a.Hq = H_q;
+    a.kmin = const_cast<void *>(kmin);
+    a.kmax = const_cast<void *>(kmax);
+    a.npages = (kv->N_max + 15) / 16;
+    a.scale = resolve_scale(scale, kv->head_dim);
+    a.scores = scores;
+    return hip_status(launch_page_scores(a, (hipStream_t)stream), "page_scores launch");
+}
+
+}  // extern "C"

@@ -149,6 +149,21 @@ struct ArrArgs {
 hipError_t launch_arr(const ArrArgs &a, hipStream_t s);
 hipError_t launch_window_mean(const float *A, int B, int w, int N, float *Abar, hipStream_t s);
 
+// ---------------------------------------------------------------- page-level estimator
+struct PageArgs {
+    KvView kv;
+    const void *q;            // [B][w][Hq][D]
+    int32_t w, Hq;
+    void *kmin, *kmax;        // [B][npages][Hkv][D], kv dtype
+    int32_t npages;           // ceil(N_max / 16)
+    float scale;
+    float *scores;            // [B][npages]
+};
+hipError_t launch_page_bounds(const PageArgs &a, hipStream_t s);
+hipError_t launch_page_scores(const PageArgs &a, hipStream_t s);
+size_t page_scores_lds_bytes(int Hkv, int D, int w, int Hq, bool f32);
+constexpr int kPageMaxRow = 8192;   // H_kv * head_dim limit of the page estimator
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace dustin
