@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 4
+#define DUSTIN_ABI_VERSION 5
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -360,12 +360,16 @@ dustin_status dustin_page_bounds(const dustin_kv *kv, void *kmin, void *kmax, du
  *  kmin, kmax  from dustin_page_bounds
  *  scale   0 means 1/sqrt(head_dim)
  *  scores  out [B][ceil(N_max / 16)] float32
+ *  ws      device scratch, >= dustin_page_scores_workspace_bytes(B, H_kv,
+ *          head_dim), 16-byte aligned; its contents need no initialisation
  *
- * Both calls need H_kv * head_dim <= 8192 (else DUSTIN_ERR_UNSUPPORTED).
+ * Both calls need H_kv * head_dim <= 4096 (else DUSTIN_ERR_UNSUPPORTED).
  */
 dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
                                  const void *kmin, const void *kmax, float scale, float *scores,
-                                 dustin_stream_t stream);
+                                 void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_page_scores_workspace_bytes(int32_t B, int32_t H_kv, int32_t head_dim);
 
 /* Human-readable name of a status code (static storage). */
 const char *dustin_status_string(dustin_status status);

@@ -26,7 +26,7 @@ EXPORTS = [
     "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
     "dustin_arr", "dustin_window_mean", "dustin_policy_sweep", "dustin_policy_sweep_workspace_bytes",
-    "dustin_page_bounds", "dustin_page_scores",
+    "dustin_page_bounds", "dustin_page_scores", "dustin_page_scores_workspace_bytes",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
 ]
 
@@ -99,7 +99,9 @@ def lib():
         L.dustin_policy_sweep_workspace_bytes.restype = sz
         L.dustin_page_bounds.argtypes = [kvp, vp, vp, vp]
         L.dustin_page_bounds.restype = ctypes.c_int
-        L.dustin_page_scores.argtypes = [vp, i32, i32, kvp, vp, vp, f32, vp, vp]
+        L.dustin_page_scores.argtypes = [vp, i32, i32, kvp, vp, vp, f32, vp, vp, sz, vp]
+        L.dustin_page_scores_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dustin_page_scores_workspace_bytes.restype = sz
         L.dustin_page_scores.restype = ctypes.c_int
         L.dustin_status_string.argtypes = [ctypes.c_int]
         L.dustin_status_string.restype = ctypes.c_char_p
@@ -373,12 +375,13 @@ def dustin_page_bounds(kv: KV, kmin=None, kmax=None):
     return kmin, kmax
 
 
-def dustin_page_scores(q, kv: KV, kmin, kmax, scale=0.0, scores=None):
+def dustin_page_scores(q, kv: KV, kmin, kmax, scale=0.0, scores=None, ws: Workspace | None = None):
     """Page scores [B][ceil(N_max/16)] float32 from the bounds."""
     B, w, Hq, D = q.shape
     d = kv.desc
     if scores is None:
         scores = torch.empty((d.B, (d.N_max + 15) // 16), dtype=torch.float32, device=q.device)
+    wsb = _ws("pages", ws, lib().dustin_page_scores_workspace_bytes(d.B, d.H_kv, d.head_dim), q.device)
     _check(lib().dustin_page_scores(_ptr(q), w, Hq, kv.ref, _ptr(kmin), _ptr(kmax), float(scale), _ptr(scores),
-                                    _stream(q)))
+                                    _ptr(wsb), wsb.numel(), _stream(q)))
     return scores

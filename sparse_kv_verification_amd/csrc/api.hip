@@ -603,8 +603,14 @@ dustin_status dustin_page_bounds(const dustin_kv *kv, void *kmin, void *kmax, du
     return hip_status(launch_page_bounds(a, (hipStream_t)stream), "page_bounds launch");
 }
 
+size_t dustin_page_scores_workspace_bytes(int32_t B, int32_t H_kv, int32_t head_dim) {
+    if (B < 1 || H_kv < 1 || head_dim < 1) return 0;
+    return align_up((size_t)B * 2 * H_kv * head_dim * sizeof(float), 256);
+}
+
 dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv, const void *kmin,
-                                 const void *kmax, float scale, float *scores, dustin_stream_t stream) {
+                                 const void *kmax, float scale, float *scores, void *ws, size_t ws_bytes,
+                                 dustin_stream_t stream) {
     dustin_status st = check_kv(kv, "page_scores kv", false);
     if (st != DUSTIN_OK) return st;
     CHECK(q != nullptr && kmin != nullptr && kmax != nullptr && scores != nullptr, DUSTIN_ERR_INVALID_ARG,
@@ -616,7 +622,13 @@ dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const du
     CHECK(((uintptr_t)q | (uintptr_t)kmin | (uintptr_t)kmax) % 16 == 0, DUSTIN_ERR_INVALID_ARG,
           "page_scores: q, kmin and kmax must be 16-byte aligned");
     CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "page_scores: scale is not finite");
+    CHECK((int64_t)((kv->N_max + 15) / 16) * kv->H_kv * kv->head_dim * (kv->dtype == DUSTIN_F32 ? 4 : 2) <= kInt32Max,
+          DUSTIN_ERR_UNSUPPORTED, "page_scores: one sequence's bounds exceed 2 GiB");
+    const size_t need = dustin_page_scores_workspace_bytes(kv->B, kv->H_kv, kv->head_dim);
+    CHECK(ws != nullptr && ws_bytes >= need && (uintptr_t)ws % 16 == 0, DUSTIN_ERR_INVALID_ARG,
+          "page_scores: 16-byte aligned workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     PageArgs a{};
+    a.pm = (float *)ws;
     a.kv = view_of(kv);
     a.q = q;
     a.w = w;

@@ -158,11 +158,11 @@ struct PageArgs {
     int32_t npages;           // ceil(N_max / 16)
     float scale;
     float *scores;            // [B][npages]
+    float *pm;                // [B][2][Hkv * D] scratch: sums of max(q, 0), min(q, 0)
 };
 hipError_t launch_page_bounds(const PageArgs &a, hipStream_t s);
 hipError_t launch_page_scores(const PageArgs &a, hipStream_t s);
-size_t page_scores_lds_bytes(int Hkv, int D, int w, int Hq, bool f32);
-constexpr int kPageMaxRow = 8192;   // H_kv * head_dim limit of the page estimator
+constexpr int kPageMaxRow = 4096;   // H_kv * head_dim limit of the page estimator
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

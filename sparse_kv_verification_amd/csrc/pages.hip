@@ -89,70 +89,119 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(PageArgs a) {
 }
 
 // Page scores.  Each term splits exactly as
-//   max(q lo, q hi) = q (lo + hi) / 2 + |q| (hi - lo) / 2      (hi >= lo),
+//   max(q lo, q hi) = max(q, 0) hi + min(q, 0) lo                (hi >= lo),
 // so, summed over the window steps and the query heads of KV head g,
-//   score[p] = scale * sum_{g, d} (c1[g][d] (lo + hi) + c2[g][d] (hi - lo))
-// with c1 = sum q / 2 and c2 = sum |q| / 2 over those (step, head) pairs: a
-// dot product of the page's bounds with two per-sequence vectors, so the
-// kernel streams the bounds once at the HBM rate.
-//
-// Work-group (chunk set, sequence): first c1 / c2 into LDS (16-byte query
-// pieces, the (step, head) rows split over replicas of the piece grid and
-// added up afterwards), then each wave takes chunks of 8 pages; lane l takes
-// the row's 16-byte pieces l, l + 64, ... of all 8 pages (16 loads in flight
-// per piece), and each page's sum is reduced across the wave.
+//   score[p] = scale * sum_{g, d} (P[g][d] hi[p][g][d] + M[g][d] lo[p][g][d])
+// with P = sum max(q, 0) and M = sum min(q, 0) over those (step, head)
+// pairs: a dot product of the page's bounds with two per-sequence vectors.
+// A small kernel forms P and M once per call; the scoring kernel streams the
+// bounds once at the HBM rate.
+
+// P / M: work-group (sequence, KV head); thread t takes the 16-byte query
+// piece t % (D / EPV) of rows t / (D / EPV), t / (D / EPV) + replicas, ...;
+// the replicas are added in LDS.
 template <bool F32>
+__global__ __launch_bounds__(256) void page_query_split_kernel(PageArgs a) {
+    using T = typename std::conditional<F32, float, uint16_t>::type;
+    constexpr int EPV = 16 / sizeof(T);
+    __shared__ float red[2][256 * EPV];         // [replica][D] partial sums, D / EPV * replicas = 256
+    const int b = blockIdx.x, g = blockIdx.y;
+    const int D = a.kv.D, G = a.Hq / a.kv.Hkv, nq = a.w * G;
+    const int dp = D / EPV, reps = blockDim.x / dp;   // dp divides 256
+    const int piece = threadIdx.x % dp, r = threadIdx.x / dp;
+    float sp[EPV], sm[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) sp[k] = sm[k] = 0.f;
+    constexpr int U = 4;                        // rows loaded together (one round of independent loads)
+    for (int i0 = r; i0 < nq; i0 += U * reps) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = min(i0 + u * reps, nq - 1);
+            const int s = i / G, h = g * G + (i - s * G);
+            v[u] = *(const u32x4 *)((const T *)a.q + (((int64_t)b * a.w + s) * a.Hq + h) * D + piece * EPV);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u * reps >= nq) break;
+            const T *x = (const T *)&v[u];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                float qv;
+                if constexpr (F32) qv = x[k];
+                else qv = __builtin_bit_cast(float, (uint32_t)x[k] << 16);
+                sp[k] += fmaxf(qv, 0.f);
+                sm[k] += fminf(qv, 0.f);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) {
+        red[0][r * D + piece * EPV + k] = sp[k];
+        red[1][r * D + piece * EPV + k] = sm[k];
+    }
+    __syncthreads();
+    const int rowe = a.kv.Hkv * D;
+    for (int e = threadIdx.x; e < D; e += blockDim.x) {
+        float p = 0.f, m = 0.f;
+        for (int q = 0; q < reps; ++q) {
+            p += red[0][q * D + e];
+            m += red[1][q * D + e];
+        }
+        a.pm[((int64_t)b * 2) * rowe + g * D + e] = p;
+        a.pm[((int64_t)b * 2 + 1) * rowe + g * D + e] = m;
+    }
+}
+
+// Scoring: each wave holds P / M for its own row pieces in registers (lane l
+// owns the 16-byte pieces l, l + 64, ..., PPL of them) and takes chunks of PC
+// pages (PC * PPL = 8: one round of 16 loads per lane per chunk, few enough
+// registers for four waves per SIMD to overlap loads with arithmetic); each
+// page's sum is reduced across the wave.
+#ifndef DUSTIN_PAGE_AUX
+#define DUSTIN_PAGE_AUX 2
+#endif
+constexpr int kPageAux = DUSTIN_PAGE_AUX;   // cache policy of the bounds loads (2: non-temporal, read once)
+
+template <bool F32, int PPL>
 __global__ __launch_bounds__(256) void page_scores_kernel(PageArgs a) {
     using T = typename std::conditional<F32, float, uint16_t>::type;
     constexpr int EPV = 16 / sizeof(T);
-    constexpr int PC = 8;                       // pages per chunk
-    extern __shared__ float lds[];              // part [R][2][rowe], then c [2][rowe]
+    constexpr int PC = PPL >= 8 ? 1 : 8 / PPL;  // pages per chunk
     const int b = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const KvView &kv = a.kv;
-    const int D = kv.D, rowe = kv.Hkv * D, npc = rowe / EPV;
-    const int G = a.Hq / kv.Hkv, nq = a.w * G;  // (step, head) rows per KV head
-    const int R = max(1, min(nq, (int)blockDim.x / npc));
-    float *part = lds, *cc = lds + (size_t)R * 2 * rowe;
+    const int rowe = kv.Hkv * kv.D, npc = rowe / EPV;
     auto f = [](T x) -> float {
         if constexpr (F32) return x;
         else return __builtin_bit_cast(float, (uint32_t)x << 16);
     };
-    for (int t = threadIdx.x; t < npc * R; t += blockDim.x) {
-        const int pc = t % npc, r = t / npc;
-        const int e = pc * EPV, g = e / D, d = e - g * D;   // a piece stays inside one head (D % EPV == 0)
-        float s1[EPV], s2[EPV];
+    // buffer resources over the sequence's bounds (reads past them return 0);
+    // the page offset is wave-uniform, lanes add one 32-bit piece offset
+    const uint32_t seq_bytes = (uint32_t)((size_t)a.npages * rowe * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rmin = __builtin_amdgcn_make_buffer_rsrc(
+        (char *)a.kmin + (int64_t)b * seq_bytes, (short)0, (int)seq_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rmax = __builtin_amdgcn_make_buffer_rsrc(
+        (char *)a.kmax + (int64_t)b * seq_bytes, (short)0, (int)seq_bytes, 0x00020000);
+    uint32_t loff[PPL];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) s1[k] = s2[k] = 0.f;
-        for (int i = r; i < nq; i += R) {
-            const int s = i / G, h = g * G + (i - s * G);
-            const u32x4 v = *(const u32x4 *)((const T *)a.q + (((int64_t)b * a.w + s) * a.Hq + h) * D + d);
-            const T *x = (const T *)&v;
+    for (int j = 0; j < PPL; ++j) loff[j] = (uint32_t)min(lane + 64 * j, npc - 1) * 16u;
+    float pv[PPL][EPV], mv[PPL][EPV];
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                const float qv = f(x[k]);
-                s1[k] += qv;
-                s2[k] += fabsf(qv);
+    for (int j = 0; j < PPL; ++j) {
+        const int pc = lane + 64 * j;
+        const bool ok = pc < npc;
+        const float *src = a.pm + (int64_t)b * 2 * rowe + (ok ? pc : 0) * EPV;
+#pragma unroll
+        for (int k = 0; k < EPV; k += 4) {
+            const f32x4 x = *(const f32x4 *)(src + k), y = *(const f32x4 *)(src + rowe + k);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pv[j][k + u] = ok ? x[u] : 0.f;
+                mv[j][k + u] = ok ? y[u] : 0.f;
             }
         }
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-            part[((size_t)r * 2) * rowe + e + k] = s1[k];
-            part[((size_t)r * 2 + 1) * rowe + e + k] = s2[k];
-        }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < rowe; e += blockDim.x) {
-        float s1 = 0.f, s2 = 0.f;
-        for (int r = 0; r < R; ++r) {
-            s1 += part[((size_t)r * 2) * rowe + e];
-            s2 += part[((size_t)r * 2 + 1) * rowe + e];
-        }
-        cc[e] = 0.5f * s1;
-        cc[rowe + e] = 0.5f * s2;
-    }
-    __syncthreads();
-
     const int nb = min(max(kv.seq_lens[b], 0), kv.N_max);
     const int used = (nb + 15) / 16;            // pages with positions below n_b
     const int nchunk = (a.npages + PC - 1) / PC;
@@ -163,34 +212,25 @@ __global__ __launch_bounds__(256) void page_scores_kernel(PageArgs a) {
             if (lane < PC && p0 + lane < a.npages) out[p0 + lane] = 0.f;
             continue;
         }
+        u32x4 vlo[PC][PPL], vhi[PC][PPL];
+#pragma unroll
+        for (int i = 0; i < PC; ++i) {
+            const int pb = min(p0 + i, a.npages - 1) * rowe * (int)sizeof(T);
+#pragma unroll
+            for (int j = 0; j < PPL; ++j) {
+                vlo[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rmin, loff[j], pb, kPageAux));
+                vhi[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rmax, loff[j], pb, kPageAux));
+            }
+        }
         float acc[PC];
 #pragma unroll
-        for (int i = 0; i < PC; ++i) acc[i] = 0.f;
-        for (int pc = lane; pc < npc; pc += 64) {
-            const int e = pc * EPV;
-            u32x4 vlo[PC], vhi[PC];
+        for (int i = 0; i < PC; ++i) {
+            acc[i] = 0.f;
 #pragma unroll
-            for (int i = 0; i < PC; ++i) {
-                const int p = min(p0 + i, a.npages - 1);
-                const int64_t off = ((int64_t)b * a.npages + p) * rowe + e;
-                vlo[i] = *(const u32x4 *)((const T *)a.kmin + off);
-                vhi[i] = *(const u32x4 *)((const T *)a.kmax + off);
-            }
-            float c1[EPV], c2[EPV];
+            for (int j = 0; j < PPL; ++j) {
+                const T *lo = (const T *)&vlo[i][j], *hi = (const T *)&vhi[i][j];
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                c1[k] = cc[e + k];
-                c2[k] = cc[rowe + e + k];
-            }
-#pragma unroll
-            for (int i = 0; i < PC; ++i) {
-                const T *lo = (const T *)&vlo[i], *hi = (const T *)&vhi[i];
-#pragma unroll
-                for (int k = 0; k < EPV; ++k) {
-                    const float l = f(lo[k]), h = f(hi[k]);
-                    acc[i] = fmaf(c1[k], l + h, acc[i]);
-                    acc[i] = fmaf(c2[k], h - l, acc[i]);
-                }
+                for (int k = 0; k < EPV; ++k) acc[i] = fmaf(pv[j][k], f(hi[k]), fmaf(mv[j][k], f(lo[k]), acc[i]));
             }
         }
 #pragma unroll
@@ -202,10 +242,11 @@ __global__ __launch_bounds__(256) void page_scores_kernel(PageArgs a) {
     }
 }
 
-size_t page_scores_lds_bytes(int Hkv, int D, int w, int Hq, bool f32) {
-    const int epv = f32 ? 4 : 8, rowe = Hkv * D, npc = rowe / epv;
-    const int R = std::max(1, std::min(w * (Hq / Hkv), 256 / npc));
-    return ((size_t)R * 2 + 2) * rowe * sizeof(float);
+int page_pieces_per_lane(int Hkv, int D, bool f32) {
+    const int npc = Hkv * D / (f32 ? 4 : 8);
+    int ppl = 1;
+    while (ppl * 64 < npc) ppl *= 2;
+    return ppl;
 }
 
 hipError_t launch_page_bounds(const PageArgs &a, hipStream_t s) {
@@ -216,16 +257,33 @@ hipError_t launch_page_bounds(const PageArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_page_scores(const PageArgs &a, hipStream_t s) {
-    const size_t lds = page_scores_lds_bytes(a.kv.Hkv, a.kv.D, a.w, a.Hq, a.kv.f32);
-    const int nchunk = (a.npages + 7) / 8;
-    // about 512 work-groups in all, each wave holding at least one chunk
-    const int gx = std::max(1, std::min((512 + a.kv.B - 1) / a.kv.B, (nchunk + 3) / 4));
-    const dim3 grid(gx, a.kv.B);
-    const void *fn = a.kv.f32 ? (const void *)page_scores_kernel<true> : (const void *)page_scores_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (a.kv.f32) hipLaunchKernelGGL(page_query_split_kernel<true>, dim3(a.kv.B, a.kv.Hkv), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(page_query_split_kernel<false>, dim3(a.kv.B, a.kv.Hkv), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.kv.f32) hipLaunchKernelGGL(page_scores_kernel<true>, grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL(page_scores_kernel<false>, grid, dim3(256), lds, s, a);
+    const int ppl = page_pieces_per_lane(a.kv.Hkv, a.kv.D, a.kv.f32);
+    const int pc = ppl >= 8 ? 1 : 8 / ppl;
+    const int nchunk = (a.npages + pc - 1) / pc;
+    // about 1024 work-groups in all (four waves per SIMD), each wave holding at least one chunk
+    const int gx = std::max(1, std::min((1024 + a.kv.B - 1) / a.kv.B, (nchunk + 3) / 4));
+    const dim3 grid(gx, a.kv.B);
+    // H_kv * head_dim <= 4096: up to 16 pieces per lane in float32, 8 in bfloat16
+#define DUSTIN_PAGE_CASE(F, P) \
+    case P: hipLaunchKernelGGL((page_scores_kernel<F, P>), grid, dim3(256), 0, s, a); break;
+    if (a.kv.f32) {
+        switch (ppl) {
+            DUSTIN_PAGE_CASE(true, 1) DUSTIN_PAGE_CASE(true, 2) DUSTIN_PAGE_CASE(true, 4)
+            DUSTIN_PAGE_CASE(true, 8) DUSTIN_PAGE_CASE(true, 16)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (ppl) {
+            DUSTIN_PAGE_CASE(false, 1) DUSTIN_PAGE_CASE(false, 2) DUSTIN_PAGE_CASE(false, 4)
+            DUSTIN_PAGE_CASE(false, 8)
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef DUSTIN_PAGE_CASE
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.dustin_abi_version() == 4
+    assert L.dustin_abi_version() == 5
     assert L.dustin_status_string(0) == b"DUSTIN_OK"
     assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
 
@@ -188,13 +188,17 @@ def test_page_estimator_argument_errors(L):
     assert L.dustin_page_bounds(ctypes.byref(desc), None, FAKE, None) == INVALID
     assert L.dustin_page_bounds(ctypes.byref(desc), FAKE + 4, FAKE, None) == INVALID     # misaligned
     assert L.dustin_page_bounds(ctypes.byref(kv(k=None)), FAKE, FAKE, None) == INVALID
+    need = L.dustin_page_scores_workspace_bytes(2, 8, 128)
+    assert need == 2 * 2 * 8 * 128 * 4
     f = lambda **k: L.dustin_page_scores(k.get("q", FAKE), k.get("w", 4), k.get("Hq", 64), ctypes.byref(desc),
-                                         FAKE, FAKE, k.get("scale", 0.0), k.get("out", FAKE), None)
+                                         FAKE, FAKE, k.get("scale", 0.0), k.get("out", FAKE), k.get("ws", FAKE),
+                                         k.get("ws_bytes", need), None)
     assert f(q=None) == INVALID and f(out=None) == INVALID
     assert f(Hq=60) == INVALID
     assert f(q=FAKE + 2) == INVALID                      # misaligned
-    assert L.dustin_page_scores(FAKE, 4, 512, ctypes.byref(kv(H_kv=128)), FAKE, FAKE, 0.0, FAKE, None) \
-        == UNSUPPORTED                                   # H_kv * head_dim beyond 8192
+    assert f(ws=None) == INVALID and f(ws_bytes=need - 1) == INVALID
+    assert L.dustin_page_scores(FAKE, 4, 512, ctypes.byref(kv(H_kv=64)), FAKE, FAKE, 0.0, FAKE, FAKE, 1 << 30,
+                                None) == UNSUPPORTED     # H_kv * head_dim beyond 4096
     assert f(scale=float("inf")) == INVALID
 
 
