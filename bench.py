@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-window", action="store_true",
                    help="skip the verification-window step (append + causal verify attention + commit)")
     p.add_argument("--no-sweep", action="store_true", help="skip the policy sweep (ARR of the compared policies)")
+    p.add_argument("--no-curve", action="store_true",
+                   help="skip the estimator-overhead curve (dense, naive, Quest-16, Dustin-T/D/H over context length)")
     p.add_argument("--pmc-probe", action="store_true",
                    help="for counter collection: one warm step, a 1 GiB float32 copy (the calibration "
                         "kernel of known size), then one more step; prints no JSON")
@@ -367,6 +369,8 @@ def main():
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
     if not args.no_sweep:
         res["policy_sweep"] = policy_sweep(args, sh, x, kvs[0], s_d, s_t, n_sink, n_window, timed)
+    if not args.no_curve:
+        res["estimator_curve"] = estimator_curve(args, sh, x, cap, timed)
     if not args.no_window:
         # Last, because it writes the window rows into every layer's cache.
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
@@ -411,6 +415,139 @@ def policy_sweep(args, sh, x, kv, s_d, s_t, n_sink, n_window, timed):
         out["cpu_oracle_one_sequence_s"] = round(dt, 2)
         out["cpu_oracle_scaled_us"] = round(dt * sh.B * 1e6, 0)
     return out
+
+
+CURVE_NS = (4096, 8192, 16384, 32768)
+CURVE_DISTINCT_LAYERS = 8
+
+
+def estimator_curve(args, sh, x, cap, timed):
+    """Criticality-estimation cost against context length, normalised by
+    full-cache attention (the comparison of the blog's Fig. 8), per
+    verification step of the whole target model (sh.layers layers):
+      dense     full-cache attention of the w window queries, every layer
+      naive     every head of every layer scored: the draft side over all
+                draft layers and heads plus all H_q target heads of every
+                target layer (S_Target materialised per layer)
+      quest16   page scores of every layer from 16-position min/max key
+                bounds (bounds built outside the timed region: they are kept
+                up to date as pages fill)
+      dustin_T  the scored target-head subset (S heads of one layer)
+      dustin_D  the draft side as configured
+      dustin_H  both sides (the step's score call)
+    normalized_byte_floor is the same ratio for the bytes each estimator has
+    to read (K of the scored layers, draft K, page bounds), which a faster
+    kernel cannot go below.
+    The n-position inputs are the first n positions of the generated cache.
+    Per-layer work cycles over 8 distinct layer buffers, each far larger
+    than the last-level cache, so no launch is served from cache.  Every
+    estimator is replayed from a HIP graph and timed with events."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    if x.page_table is not None:
+        return None
+    dev = x.q.device
+    NL = CURVE_DISTINCT_LAYERS
+    reps = max(2, args.steps // 4)
+    all_heads = [(0, h) for h in range(sh.Hq)]
+    q_all = x.q[:, -1].contiguous()                     # [B][H_q][d]: one target query per head
+    rows = []
+
+    def graph_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        if args.no_graph:
+            return timed(fn, reps)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr, stream=cap):
+                fn()
+        torch.cuda.synchronize()
+        gr.replay()
+        return timed(gr.replay, reps)
+
+    for n in CURVE_NS:
+        if n > sh.n:
+            continue
+        lens = torch.full((sh.B,), n, dtype=torch.int32, device=dev)
+        Kn = [x.K[:, :n].clone() for _ in range(NL)]
+        Vn = [x.V[:, :n].clone() for _ in range(NL)]
+        kv = [dk.KV(Kn[i], Vn[i], lens, None) for i in range(NL)]
+        Kd = [x.Kd[l][:, :n].contiguous() for l in range(sh.L_d)]
+        dkv = [dk.KV(Kd[l], None, lens, None) for l in range(sh.L_d)]
+        s_d = torch.empty((sh.B, n), dtype=torch.float32, device=dev)
+        s_t = torch.empty_like(s_d)
+        out = torch.empty_like(x.q)
+        ws = {nm: dk.Workspace() for nm in ("dense", "naive_t", "naive_d", "t", "d", "h")}
+        bounds = [dk.dustin_page_bounds(kv[i]) for i in range(NL)]
+        pscores = torch.empty((sh.B, (n + 15) // 16), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def dense():
+            for l in range(sh.layers):
+                dk.dustin_sparse_verify_attn(x.q, kv[l % NL], None, None, out=out, ws=ws["dense"])
+
+        def naive():
+            dk.dustin_score(dkv, x.q_draft, [kv[0]], None, None, sh.Hq, s_draft=s_d, ws=ws["naive_d"],
+                            want_target=False)
+            for l in range(sh.layers):
+                dk.dustin_score([], None, [kv[l % NL]], q_all, all_heads, sh.Hq, s_target=s_t, ws=ws["naive_t"],
+                                want_draft=False)
+
+        def quest():
+            for l in range(sh.layers):
+                dk.dustin_page_scores(x.q, kv[l % NL], bounds[l % NL][0], bounds[l % NL][1], scores=pscores)
+
+        def quest_bounds():
+            for i in range(NL):
+                dk.dustin_page_bounds(kv[i], bounds[i][0], bounds[i][1])
+
+        def dustin_t():
+            dk.dustin_score([], None, [kv[0]], x.q_hist, x.sub_heads, sh.Hq, s_target=s_t, ws=ws["t"],
+                            want_draft=False)
+
+        def dustin_d():
+            dk.dustin_score(dkv, x.q_draft, [kv[0]], None, None, sh.Hq, s_draft=s_d, ws=ws["d"], want_target=False)
+
+        def dustin_h():
+            dk.dustin_score(dkv, x.q_draft, [kv[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t,
+                            ws=ws["h"])
+
+        us = {nm: graph_us(fn) for nm, fn in (("dense", dense), ("naive", naive), ("quest16", quest),
+                                               ("dustin_T", dustin_t), ("dustin_D", dustin_d),
+                                               ("dustin_H", dustin_h))}
+        bounds_us = timed(quest_bounds, reps) / NL
+        # page scores per launch against the HBM peak: both bounds tensors, q and the scores
+        eb = x.K.element_size()
+        pbytes = (2 * sh.B * ((n + 15) // 16) * sh.Hkv * sh.d * eb + sh.B * sh.w * sh.Hq * sh.d * eb
+                  + sh.B * ((n + 15) // 16) * 4)
+        p_us = us["quest16"] / sh.layers
+        # bytes every estimator must read at least, against dense attention's K + V of every layer
+        kbytes = sh.B * n * sh.Hkv * sh.d * eb
+        dbytes = sh.L_d * sh.B * n * sh.Hkv_d * sh.d_d * x.Kd[0].element_size()
+        floors = {"naive": (kbytes * sh.layers + dbytes) / (2 * kbytes * sh.layers),
+                  "quest16": (2 * kbytes / 16 * sh.layers) / (2 * kbytes * sh.layers),
+                  "dustin_T": kbytes / (2 * kbytes * sh.layers),
+                  "dustin_D": dbytes / (2 * kbytes * sh.layers),
+                  "dustin_H": (kbytes + dbytes) / (2 * kbytes * sh.layers)}
+        row = {"n": n, "us": {k_: round(v, 1) for k_, v in us.items()},
+               "normalized": {k_: round(v / us["dense"], 5) for k_, v in us.items() if k_ != "dense"},
+               "normalized_byte_floor": {k_: round(v, 5) for k_, v in floors.items()},
+               "quest16_page_scores_per_launch_us": round(p_us, 2),
+               "quest16_page_scores_GBps": round(pbytes / p_us / 1e3, 1),
+               "quest16_page_scores_frac": round(pbytes / p_us / 1e3 / HBM_PEAK_GBPS, 4),
+               "quest16_page_bounds_per_layer_us": round(bounds_us, 1)}
+        log(f"estimator curve n={n}: dense {us['dense']:.0f} us; normalized " +
+            ", ".join(f"{k_} {v:.4f} (1/{1 / v:.0f})" for k_, v in row["normalized"].items()) +
+            f"; page scores {p_us:.2f} us/launch ({row['quest16_page_scores_GBps']:.0f} GB/s)")
+        rows.append(row)
+        del Kn, Vn, kv, Kd, dkv, bounds, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return {"layers": sh.layers, "distinct_layer_buffers": NL, "draft_layers": sh.L_d, "draft_heads": sh.H_d,
+            "target_heads_scored": len(x.sub_heads), "rows": rows}
 
 
 def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):
