@@ -16,6 +16,11 @@ Decoding", arXiv 2606.24957):
   section 3.3 (Fig. 3): the draft lookahead compared with the oracle;
   related work: Quest's page scoring from min/max key statistics (the
   page-level estimator of section 5.4.1);
+* the blog summary, section 2.4 and Fig. 6: the semantic-retrieval-head
+  score matrix (layer x head) with its head TopK, and the offline
+  configuration search (greedy target layers, then greedy draft layers with
+  the target fixed, then the draft/target budget split m), whose objective
+  is the windowed ARR;
 * the blog summary (liuzhao09.github.io), section 2.2 (hybrid aggregation:
   S_Draft over H_d, L_d, Gamma; S_Target over H_t, L_t; one global index
   set), section 2.3 (verification set: protected sink + recent window, draft
@@ -68,6 +73,15 @@ __all__ = [
     "policy_sweep",
     "page_key_bounds",
     "page_scores",
+    "search_objective",
+    "candidate_objectives",
+    "srh_head_scores",
+    "srh_select",
+    "greedy_select",
+    "greedy_target",
+    "greedy_draft",
+    "m_search",
+    "config_search",
     "topk_desc",
     "protected_positions",
     "pages_to_contiguous",
@@ -427,6 +441,154 @@ def policy_sweep(q_window, q_past, K, s_draft, s_target, ks, m_hybrid, n_sink, n
             I, _ = select_verify_set(s_draft, s_target, n, k, m, n_sink, n_window)
             out[P + 2 + r, ki] = arr_window(A, I)
     return out
+
+
+def search_objective(A_layers, I):
+    """Objective of the offline configuration search (blog section 2.4: the
+    windowed ARR, Eq. 2, rather than task accuracy).  Reading taken for a
+    model with several target layers: the global set (blog section 2.2)
+    serves every layer, so the objective is Eq. 2 averaged over the target
+    layers whose attention the set has to recover; with one layer it is
+    Eq. 2 itself.  A_layers: [L][w][n] (each Eq. 1's A of one layer)."""
+    return float(np.mean([arr_window(A, I) for A in A_layers]))
+
+
+def candidate_objectives(A_layers, k, m, n_sink, n_window, base_d=None, units_d=None, base_t=None,
+                         units_t=None, ms=None):
+    """Search objective of the verification set (blog section 2.3) of each
+    candidate configuration c:
+        S_Draft  = base_d + units_d[c]   (a side is absent when neither is given)
+        S_Target = base_t + units_t[c]
+        m        = ms[c] if ms is given, else m.
+    The number of candidates is the length of whichever per-candidate list
+    is given (1 if none).  Returns [C]."""
+    lens = [len(u) for u in (units_d, units_t, ms) if u is not None]
+    C = lens[0] if lens else 1
+    assert all(x == C for x in lens)
+    n = np.asarray(A_layers[0]).shape[1]
+
+    def side(base, units, c):
+        if base is None and units is None:
+            return None
+        v = np.zeros(n)
+        if base is not None:
+            v = v + _f64(base)
+        if units is not None:
+            v = v + _f64(units[c])
+        return v
+
+    out = np.zeros(C)
+    for c in range(C):
+        sd, st = side(base_d, units_d, c), side(base_t, units_t, c)
+        mm = m if ms is None else ms[c]
+        I, _ = select_verify_set(sd, st, n, k, mm, n_sink, n_window)
+        out[c] = search_objective(A_layers, I)
+    return out
+
+
+def srh_head_scores(A_layers, head_prev, k, n_sink, n_window):
+    """Full SRH score matrix of the blog's Fig. 6 (layer x head).  Reading
+    taken: the score of target head (l, h) is the search objective of the
+    target-history set (blog section 2.3 with m = 0) built from that head
+    alone, S_Target = its previous query's attention over the history
+    (translation section 3.2, delta = 1).
+    head_prev: [L_t][H_q][n] per-head probabilities.  Returns [L_t][H_q]."""
+    head_prev = _f64(head_prev)
+    L, H, _ = head_prev.shape
+    flat = candidate_objectives(A_layers, k, 0, n_sink, n_window, units_t=head_prev.reshape(L * H, -1))
+    return flat.reshape(L, H)
+
+
+def srh_select(M, T):
+    """Head TopK of the blog's Fig. 6: the T (layer, head) pairs with the
+    largest SRH score, ties to the lower (layer, head).  Returns the pairs in
+    selection order."""
+    M = _f64(M)
+    L, H = M.shape
+    order = topk_desc(M.ravel(), T)
+    return [(int(i) // H, int(i) % H) for i in order]
+
+
+def greedy_select(objective_of, n_cand, max_units, start=-np.inf):
+    """Greedy forward selection (blog section 2.4, steps 1 and 2): starting
+    from the objective `start` of the empty choice, add the candidate whose
+    addition gives the largest objective; stop after max_units additions or
+    when no remaining candidate improves the objective strictly.  Ties go to
+    the lower candidate index.  objective_of(list of chosen indices) ->
+    float.  Returns (chosen indices in order, objective after each)."""
+    chosen, curve, best = [], [], start
+    while len(chosen) < max_units:
+        top_v, top_c = -np.inf, -1
+        for c in range(n_cand):
+            if c in chosen:
+                continue
+            v = objective_of(chosen + [c])
+            if v > top_v:
+                top_v, top_c = v, c
+        if top_c < 0 or not top_v > best:
+            break
+        chosen.append(top_c)
+        curve.append(top_v)
+        best = top_v
+    return chosen, curve
+
+
+def greedy_target(A_layers, units_t, k, n_sink, n_window, max_units):
+    """Step 1 of the configuration search (blog section 2.4): greedily choose
+    target units (each a set of target heads, given by its S_Target vector)
+    for the target-history set (m = 0); the first unit is always taken."""
+    units_t = _f64(units_t)
+
+    def obj(ch):
+        return candidate_objectives(A_layers, k, 0, n_sink, n_window, base_t=units_t[ch].sum(axis=0))[0]
+
+    return greedy_select(obj, units_t.shape[0], max_units)
+
+
+def greedy_draft(A_layers, s_target, units_d, k, m, n_sink, n_window, max_units):
+    """Step 2 (blog section 2.4): with the target heads fixed, greedily add
+    draft units (each a draft layer, given by its S_Draft vector) to the
+    hybrid set with draft budget m.  The empty choice is the target-history
+    set, so a draft layer is kept only if it raises the objective."""
+    units_d = _f64(units_d)
+    start = candidate_objectives(A_layers, k, 0, n_sink, n_window, base_t=s_target)[0]
+
+    def obj(ch):
+        return candidate_objectives(A_layers, k, m, n_sink, n_window, base_d=units_d[ch].sum(axis=0),
+                                    base_t=s_target)[0]
+
+    return greedy_select(obj, units_d.shape[0], max_units, start=start)
+
+
+def m_search(A_layers, s_draft, s_target, k, ms, n_sink, n_window):
+    """Step 3 (blog section 2.4; the pages tune m with Optuna, here a plain
+    search over the given grid): the objective at every m in ms and the best
+    m (ties: the earlier grid entry).  Returns (values [len(ms)], best m)."""
+    vals = candidate_objectives(A_layers, k, 0, n_sink, n_window, base_d=s_draft, base_t=s_target, ms=list(ms))
+    return vals, int(ms[int(np.argmax(vals))])
+
+
+def config_search(A_layers, head_prev, draft_units, k, m0, ms, n_sink, n_window, T, S, max_draft):
+    """The offline configuration search of blog section 2.4 on one batch
+    element: the SRH score matrix and its head TopK (Fig. 6, T candidates),
+    greedy target heads among them (at most S), greedy draft layers with
+    draft budget m0 (at most max_draft), then the plain m search.
+    head_prev [L_t][H_q][n]; draft_units [L_d][n]."""
+    head_prev = _f64(head_prev)
+    M = srh_head_scores(A_layers, head_prev, k, n_sink, n_window)
+    cand = srh_select(M, T)
+    units_t = np.stack([head_prev[l, h] for (l, h) in cand])
+    ch_t, curve_t = greedy_target(A_layers, units_t, k, n_sink, n_window, S)
+    s_target = units_t[ch_t].sum(axis=0)
+    ch_d, curve_d = greedy_draft(A_layers, s_target, draft_units, k, m0, n_sink, n_window, max_draft)
+    if ch_d:
+        s_draft = _f64(draft_units)[ch_d].sum(axis=0)
+        vals, m_best = m_search(A_layers, s_draft, s_target, k, ms, n_sink, n_window)
+    else:
+        vals, m_best = None, 0
+    return {"M": M, "candidates": cand, "target_choice": ch_t, "target_curve": curve_t,
+            "target_heads": [cand[c] for c in ch_t], "draft_layers": ch_d, "draft_curve": curve_d,
+            "m_values": vals, "m": m_best}
 
 
 def page_key_bounds(K, n, page=16):

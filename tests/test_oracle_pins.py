@@ -579,3 +579,161 @@ def test_page_scores_bound_the_logits_and_match_the_box_corners():
     q2[0, 0, 0] = 5.0                 # a head of group 0 (sees a zero key)
     b0, b1 = oracle.page_key_bounds(K2, 1, 1)
     assert abs(oracle.page_scores(q2, b0, b1)[0] - 2.0 / np.sqrt(d)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Offline configuration search (blog section 2.4, Fig. 6)
+
+def _search_case(seed, L=3, w=3, H=4, Hkv=2, d=8, n=24):
+    """Several target layers: per-layer window attention A_l and per-head
+    previous-query attention, plus a few draft-like score vectors."""
+    rng = np.random.default_rng(seed)
+    A_layers, head_prev = [], []
+    for _ in range(L):
+        K = rng.standard_normal((n, Hkv, d)) * 1.3
+        q = rng.standard_normal((w, H, d)) * 1.3
+        A_layers.append(oracle.window_attention(q, K))
+        qp = q[0] + 0.4 * rng.standard_normal((H, d))
+        head_prev.append(oracle.head_probs(qp[None], K)[:, 0, :])      # [H][n]
+    draft = rng.random((5, n)) ** 3
+    return A_layers, np.stack(head_prev), draft
+
+
+def _top_mass(v, k):
+    """Sum of the k largest entries, by a full sort (independent of topk_desc)."""
+    return float(np.sort(np.asarray(v, dtype=np.float64))[::-1][:k].sum())
+
+
+def test_search_objective_full_budget_and_oracle_unit():
+    """Every layer's A sums to 1 per step, so the whole history scores 1; a
+    target unit equal to the layer-mean Abar, without protected tokens,
+    reproduces the SD oracle of that mean (Eq. 3-4) at every budget."""
+    A_layers, head_prev, draft = _search_case(1)
+    n = A_layers[0].shape[1]
+    Abar = np.mean([A.mean(axis=0) for A in A_layers], axis=0)
+    for k in (1, 5, 11, n):
+        got = oracle.candidate_objectives(A_layers, k, 0, 0, 0, units_t=[Abar, head_prev[0, 0]])
+        assert got[0] == pytest.approx(_top_mass(Abar, k), abs=1e-12)
+        assert got[0] >= got[1] - 1e-12
+    full = oracle.candidate_objectives(A_layers, n, 3, 2, 2, base_d=draft[0], base_t=draft[1])
+    assert full[0] == pytest.approx(1.0, abs=1e-12)
+
+
+def test_search_objective_is_the_layer_mean_and_sides_add():
+    """One layer reproduces Eq. 2 of the set built by select_verify_set; the
+    per-candidate sums base + unit and per-candidate m equal separate calls
+    with the summed vectors."""
+    A_layers, head_prev, draft = _search_case(2)
+    n = A_layers[0].shape[1]
+    k, m = 9, 3
+    I, _ = oracle.select_verify_set(draft[0], draft[1], n, k, m, 1, 2)
+    one = oracle.candidate_objectives(A_layers[:1], k, m, 1, 2, base_d=draft[0], base_t=draft[1])[0]
+    assert one == pytest.approx(float(A_layers[0][:, I].sum(axis=1).mean()), abs=1e-12)
+    got = oracle.candidate_objectives(A_layers, k, m, 1, 2, base_d=draft[0], units_d=draft[2:4], base_t=draft[1])
+    for c in range(2):
+        want = oracle.candidate_objectives(A_layers, k, m, 1, 2, base_d=draft[0] + draft[2 + c], base_t=draft[1])[0]
+        assert got[c] == pytest.approx(want, abs=1e-12)
+    ms = [0, 2, 6]
+    gm = oracle.candidate_objectives(A_layers, k, m, 1, 2, base_d=draft[0], base_t=draft[1], ms=ms)
+    for c, mm in enumerate(ms):
+        assert gm[c] == pytest.approx(
+            oracle.candidate_objectives(A_layers, k, mm, 1, 2, base_d=draft[0], base_t=draft[1])[0], abs=1e-12)
+
+
+def test_srh_matrix_closed_forms_and_head_topk():
+    """A head whose attention is the layer-mean Abar scores the SD oracle's
+    ARR; a head with uniform attention takes the first k positions (ties to
+    the lower position); the head TopK matches a plain sort of the matrix."""
+    A_layers, head_prev, _ = _search_case(3, L=2, H=4)
+    n = A_layers[0].shape[1]
+    k = 6
+    Abar = np.mean([A.mean(axis=0) for A in A_layers], axis=0)
+    hp = head_prev.copy()
+    hp[0, 1] = Abar
+    hp[1, 2] = np.full(n, 1.0 / n)
+    M = oracle.srh_head_scores(A_layers, hp, k, 0, 0)
+    assert M.shape == (2, 4)
+    assert M[0, 1] == pytest.approx(_top_mass(Abar, k), abs=1e-12)
+    assert M[1, 2] == pytest.approx(float(Abar[:k].sum()), abs=1e-12)
+    assert M.max() == pytest.approx(M[0, 1], abs=1e-12)
+    want = sorted(((-M[l, h], l, h) for l in range(2) for h in range(4)))
+    assert oracle.srh_select(M, 4) == [(l, h) for (_, l, h) in want[:4]]
+
+
+def test_greedy_matches_exhaustive_choices():
+    """The first pick is the best single candidate and the second the best
+    completion of it (exhaustive search over all pairs); the objective curve
+    rises strictly; ties go to the lower index."""
+    A_layers, head_prev, draft = _search_case(4)
+    units = head_prev.reshape(-1, head_prev.shape[-1])[:6]
+    k = 7
+
+    def obj(ch):
+        return oracle.candidate_objectives(A_layers, k, 0, 1, 1, base_t=units[list(ch)].sum(axis=0))[0]
+
+    singles = [obj([c]) for c in range(6)]
+    chosen, curve = oracle.greedy_target(A_layers, units, k, 1, 1, max_units=3)
+    assert chosen[0] == int(np.argmax(singles))
+    best2 = max(((obj([chosen[0], c]), -c) for c in range(6) if c != chosen[0]))
+    if len(chosen) > 1:
+        assert chosen[1] == -best2[1] and curve[1] == pytest.approx(best2[0], abs=1e-12)
+    else:
+        assert best2[0] <= curve[0]
+    assert all(b > a for a, b in zip(curve, curve[1:]))
+    # ties: the two best candidates are identical -> the lower index wins
+    Abar = np.mean([A.mean(axis=0) for A in A_layers], axis=0)
+    twin = np.stack([units[0], Abar, Abar])
+    ch, _ = oracle.greedy_target(A_layers, twin, k, 1, 1, max_units=1)
+    assert ch == [1]
+
+
+def test_greedy_stops_at_a_perfect_unit_and_keeps_only_improving_draft_layers():
+    """Once a unit reaches the SD-oracle bound (Eq. 4) nothing can improve on
+    it strictly, so the greedy stops; a draft layer that does not raise the
+    target-history objective is not kept."""
+    A_layers, head_prev, draft = _search_case(5)
+    n = A_layers[0].shape[1]
+    k = 6
+    Abar = np.mean([A.mean(axis=0) for A in A_layers], axis=0)
+    units = np.stack([head_prev[0, 0], Abar, head_prev[1, 1]])
+    chosen, curve = oracle.greedy_target(A_layers, units, k, 0, 0, max_units=3)
+    assert chosen == [1] and curve[0] == pytest.approx(_top_mass(Abar, k), abs=1e-12)
+    # draft side: a draft layer equal to Abar helps the uniform-target set; a
+    # zero-information draft layer (constant) takes the lowest positions
+    flat = np.full(n, 1.0)
+    ch_d, curve_d = oracle.greedy_draft(A_layers, flat, np.stack([flat, Abar]), k, k, 0, 0, max_units=2)
+    assert ch_d == [1]
+    start = oracle.candidate_objectives(A_layers, k, 0, 0, 0, base_t=flat)[0]
+    assert curve_d[0] > start
+    ch_none, _ = oracle.greedy_draft(A_layers, Abar, np.stack([flat]), k, k, 0, 0, max_units=1)
+    assert ch_none == []
+
+
+def test_m_search_is_exhaustive_and_reduces_to_the_tiers():
+    """The m search returns the grid's maximum (earliest on ties); m = 0 is
+    the target-history set and m = k - |P| the draft-lookahead set."""
+    A_layers, head_prev, draft = _search_case(6)
+    k, ns, nw = 10, 1, 2
+    ms = list(range(0, k - ns - nw + 1))
+    vals, best = oracle.m_search(A_layers, draft[0], draft[1], k, ms, ns, nw)
+    assert best == ms[[i for i, v in enumerate(vals) if v == vals.max()][0]]
+    t_only = oracle.candidate_objectives(A_layers, k, 0, ns, nw, base_t=draft[1])[0]
+    d_only = oracle.candidate_objectives(A_layers, k, 0, ns, nw, base_d=draft[0])[0]
+    assert vals[0] == pytest.approx(t_only, abs=1e-12)
+    assert vals[-1] == pytest.approx(d_only, abs=1e-12)
+
+
+def test_config_search_is_consistent():
+    """The composed search: target heads come from the head TopK, the curves
+    rise, and the reported best m reproduces the objective of the final set."""
+    A_layers, head_prev, draft = _search_case(7, L=3, H=4)
+    k = 8
+    r = oracle.config_search(A_layers, head_prev, draft, k, 3, [0, 1, 2, 3, 4, 5], 1, 1, T=6, S=3, max_draft=3)
+    assert len(r["candidates"]) == 6 and set(r["target_heads"]) <= set(r["candidates"])
+    assert all(b > a for a, b in zip(r["target_curve"], r["target_curve"][1:]))
+    assert all(b > a for a, b in zip(r["draft_curve"], r["draft_curve"][1:]))
+    if r["draft_layers"]:
+        s_t = sum(head_prev[l, h] for (l, h) in r["target_heads"])
+        s_d = draft[r["draft_layers"]].sum(axis=0)
+        v = oracle.candidate_objectives(A_layers, k, r["m"], 1, 1, base_d=s_d, base_t=s_t)[0]
+        assert v == pytest.approx(r["m_values"].max(), abs=1e-12)
