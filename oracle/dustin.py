@@ -461,28 +461,40 @@ def candidate_objectives(A_layers, k, m, n_sink, n_window, base_d=None, units_d=
         S_Target = base_t + units_t[c]
         m        = ms[c] if ms is given, else m.
     The number of candidates is the length of whichever per-candidate list
-    is given (1 if none).  Returns [C]."""
+    is given (1 if none).
+
+    One sequence: A_layers [L][w][n], base [n], units [C][n].  A batch of
+    equal-length sequences (the profiling batch of the offline search):
+    A_layers [B][L][w][n], base [B][n], units [C][B][n]; the objective of a
+    configuration is then the mean over the batch of each sequence's.
+    Returns [C]."""
+    A_layers = [_f64(A) for A in A_layers] if np.ndim(A_layers[0]) == 2 else A_layers
+    batch = np.ndim(A_layers[0]) == 3
     lens = [len(u) for u in (units_d, units_t, ms) if u is not None]
     C = lens[0] if lens else 1
     assert all(x == C for x in lens)
-    n = np.asarray(A_layers[0]).shape[1]
+    B = len(A_layers) if batch else 1
+    n = np.asarray(A_layers[0]).shape[-1]
 
-    def side(base, units, c):
+    def side(base, units, c, b):
         if base is None and units is None:
             return None
         v = np.zeros(n)
         if base is not None:
-            v = v + _f64(base)
+            v = v + _f64(base[b] if batch else base)
         if units is not None:
-            v = v + _f64(units[c])
+            v = v + _f64(units[c][b] if batch else units[c])
         return v
 
     out = np.zeros(C)
     for c in range(C):
-        sd, st = side(base_d, units_d, c), side(base_t, units_t, c)
         mm = m if ms is None else ms[c]
-        I, _ = select_verify_set(sd, st, n, k, mm, n_sink, n_window)
-        out[c] = search_objective(A_layers, I)
+        tot = 0.0
+        for b in range(B):
+            sd, st = side(base_d, units_d, c, b), side(base_t, units_t, c, b)
+            I, _ = select_verify_set(sd, st, n, k, mm, n_sink, n_window)
+            tot += search_objective(A_layers[b] if batch else A_layers, I)
+        out[c] = tot / B
     return out
 
 
@@ -492,10 +504,16 @@ def srh_head_scores(A_layers, head_prev, k, n_sink, n_window):
     target-history set (blog section 2.3 with m = 0) built from that head
     alone, S_Target = its previous query's attention over the history
     (translation section 3.2, delta = 1).
-    head_prev: [L_t][H_q][n] per-head probabilities.  Returns [L_t][H_q]."""
+    head_prev: [L_t][H_q][n] per-head probabilities ([B][L_t][H_q][n] for a
+    batch, with A_layers [B][L][w][n]).  Returns [L_t][H_q]."""
     head_prev = _f64(head_prev)
-    L, H, _ = head_prev.shape
-    flat = candidate_objectives(A_layers, k, 0, n_sink, n_window, units_t=head_prev.reshape(L * H, -1))
+    if head_prev.ndim == 4:
+        Bn, L, H, n = head_prev.shape
+        units = head_prev.transpose(1, 2, 0, 3).reshape(L * H, Bn, n)
+    else:
+        L, H, n = head_prev.shape
+        units = head_prev.reshape(L * H, n)
+    flat = candidate_objectives(A_layers, k, 0, n_sink, n_window, units_t=units)
     return flat.reshape(L, H)
 
 
@@ -569,20 +587,26 @@ def m_search(A_layers, s_draft, s_target, k, ms, n_sink, n_window):
 
 
 def config_search(A_layers, head_prev, draft_units, k, m0, ms, n_sink, n_window, T, S, max_draft):
-    """The offline configuration search of blog section 2.4 on one batch
-    element: the SRH score matrix and its head TopK (Fig. 6, T candidates),
-    greedy target heads among them (at most S), greedy draft layers with
-    draft budget m0 (at most max_draft), then the plain m search.
-    head_prev [L_t][H_q][n]; draft_units [L_d][n]."""
+    """The offline configuration search of blog section 2.4: the SRH score
+    matrix and its head TopK (Fig. 6, T candidates), greedy target heads
+    among them (at most S), greedy draft layers with draft budget m0 (at
+    most max_draft), then the plain m search.
+    One sequence: head_prev [L_t][H_q][n], draft_units [L_d][n]; a batch:
+    head_prev [B][L_t][H_q][n], draft_units [L_d][B][n] (A_layers batched
+    likewise)."""
     head_prev = _f64(head_prev)
+    draft_units = _f64(draft_units)
     M = srh_head_scores(A_layers, head_prev, k, n_sink, n_window)
     cand = srh_select(M, T)
-    units_t = np.stack([head_prev[l, h] for (l, h) in cand])
+    if head_prev.ndim == 4:
+        units_t = np.stack([head_prev[:, l, h] for (l, h) in cand])
+    else:
+        units_t = np.stack([head_prev[l, h] for (l, h) in cand])
     ch_t, curve_t = greedy_target(A_layers, units_t, k, n_sink, n_window, S)
     s_target = units_t[ch_t].sum(axis=0)
     ch_d, curve_d = greedy_draft(A_layers, s_target, draft_units, k, m0, n_sink, n_window, max_draft)
     if ch_d:
-        s_draft = _f64(draft_units)[ch_d].sum(axis=0)
+        s_draft = draft_units[ch_d].sum(axis=0)
         vals, m_best = m_search(A_layers, s_draft, s_target, k, ms, n_sink, n_window)
     else:
         vals, m_best = None, 0

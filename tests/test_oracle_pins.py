@@ -737,3 +737,30 @@ def test_config_search_is_consistent():
         s_d = draft[r["draft_layers"]].sum(axis=0)
         v = oracle.candidate_objectives(A_layers, k, r["m"], 1, 1, base_d=s_d, base_t=s_t)[0]
         assert v == pytest.approx(r["m_values"].max(), abs=1e-12)
+
+
+def test_search_batch_is_the_mean_of_its_sequences():
+    """A batch of equal-length sequences scores each configuration by the
+    mean of the sequences' objectives: a batch of one equals the sequence,
+    and a two-sequence batch of the same sequence equals it too, while a
+    batch of two different sequences lies between their values."""
+    A1, hp1, d1 = _search_case(8)
+    A2, hp2, d2 = _search_case(9)
+    k, m = 7, 2
+    one = oracle.candidate_objectives(A1, k, m, 1, 1, base_d=d1[0], units_t=hp1[0])
+    b1 = oracle.candidate_objectives([A1], k, m, 1, 1, base_d=d1[0][None], units_t=hp1[0][:, None])
+    np.testing.assert_allclose(b1, one, rtol=0, atol=1e-12)
+    same = oracle.candidate_objectives([A1, A1], k, m, 1, 1, base_d=np.stack([d1[0], d1[0]]),
+                                       units_t=np.stack([hp1[0], hp1[0]], axis=1))
+    np.testing.assert_allclose(same, one, rtol=0, atol=1e-12)
+    two = oracle.candidate_objectives(A2, k, m, 1, 1, base_d=d2[0], units_t=hp2[0])
+    mix = oracle.candidate_objectives([A1, A2], k, m, 1, 1, base_d=np.stack([d1[0], d2[0]]),
+                                      units_t=np.stack([hp1[0], hp2[0]], axis=1))
+    np.testing.assert_allclose(mix, (one + two) / 2, rtol=0, atol=1e-12)
+    # the batched SRH matrix keeps the (layer, head) layout of the single-sequence one
+    M1 = oracle.srh_head_scores(A1, hp1, k, 1, 1)
+    np.testing.assert_allclose(oracle.srh_head_scores([A1, A1], np.stack([hp1, hp1]), k, 1, 1), M1, rtol=0, atol=1e-12)
+    # the composed search runs on the batch layout
+    r = oracle.config_search([A1, A2], np.stack([hp1, hp2]), np.stack([d1, d2], axis=1), k, 2, [0, 1, 2, 3], 1, 1,
+                             T=4, S=2, max_draft=2)
+    assert r["M"].shape == hp1.shape[:2]
