@@ -520,10 +520,11 @@ def srh_head_scores(A_layers, head_prev, k, n_sink, n_window):
 def srh_select(M, T):
     """Head TopK of the blog's Fig. 6: the T (layer, head) pairs with the
     largest SRH score, ties to the lower (layer, head).  Returns the pairs in
-    selection order."""
+    ascending (layer, head) order, the order in which the greedy step then
+    breaks ties (the sparse SRH matrix is a set; the pages give no order)."""
     M = _f64(M)
     L, H = M.shape
-    order = topk_desc(M.ravel(), T)
+    order = np.sort(topk_desc(M.ravel(), T))
     return [(int(i) // H, int(i) % H) for i in order]
 
 

@@ -657,7 +657,10 @@ def test_srh_matrix_closed_forms_and_head_topk():
     assert M[1, 2] == pytest.approx(float(Abar[:k].sum()), abs=1e-12)
     assert M.max() == pytest.approx(M[0, 1], abs=1e-12)
     want = sorted(((-M[l, h], l, h) for l in range(2) for h in range(4)))
-    assert oracle.srh_select(M, 4) == [(l, h) for (_, l, h) in want[:4]]
+    assert oracle.srh_select(M, 4) == sorted((l, h) for (_, l, h) in want[:4])
+    # ties at the cut go to the lower (layer, head)
+    Mt = np.array([[0.5, 0.7, 0.5, 0.1], [0.5, 0.2, 0.9, 0.5]])
+    assert oracle.srh_select(Mt, 4) == [(0, 0), (0, 1), (0, 2), (1, 2)]
 
 
 def test_greedy_matches_exhaustive_choices():
