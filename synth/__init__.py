@@ -39,7 +39,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Shape", "PRESETS", "preset", "make", "tier_defaults", "spread_heads", "history_trajectory"]
+__all__ = ["Shape", "PRESETS", "preset", "make", "tier_defaults", "spread_heads", "history_trajectory",
+           "SearchInputs", "make_search"]
 
 
 @dataclass(frozen=True)
@@ -117,7 +118,8 @@ def spread_heads(shape):
 
 
 _STREAMS = ["K", "V", "heavy", "dirs", "salience", "q", "drift_q", "proj",
-            "draft_k_noise", "draft_q_noise", "lens", "pages", "trajectory"]
+            "draft_k_noise", "draft_q_noise", "lens", "pages", "trajectory",
+            "search_heavy", "search_layer", "search_rho", "search_draft"]
 
 
 def _gen(master, stream, device):
@@ -345,3 +347,109 @@ def history_trajectory(x: Inputs, deltas):
             out[want[t]] = cur.clone()
     store = x.q.dtype
     return torch.stack(out).to(store).contiguous()
+
+
+@dataclass
+class SearchInputs:
+    """Profiling batch of the offline configuration search: several target
+    layers, each with its own keys, window queries and previous query per
+    head, plus the draft's layers.  Every sequence has length n."""
+    shape: Shape
+    L_t: int
+    seq_lens: torch.Tensor          # [B] int32 (all n)
+    K: torch.Tensor                 # [L_t][B][n][Hkv][d]
+    q: torch.Tensor                 # [L_t][B][w][Hq][d] window queries
+    q_prev: torch.Tensor            # [L_t][B][Hq][d] previous query of every head
+    Kd: torch.Tensor                # [L_d][B][n][Hkv_d][d_d]
+    q_draft: torch.Tensor           # [B][L_d][w][H_d][d_d]
+    rho: torch.Tensor               # [L_t][Hq] retrieval quality of each head's previous query
+    share: torch.Tensor             # [L_t] fraction of the shared salient set a layer attends
+    draft_noise: torch.Tensor       # [L_d] noise level of each draft layer
+
+
+def make_search(shape: Shape, L_t: int, seed=None, device="cpu"):
+    """Synthetic multi-layer profiling data for the configuration search.
+
+    The context has a shared set of salient positions.  Target layer l
+    attends a fraction share[l] of it plus salient positions of its own
+    (keys pushed along one direction per KV head, as in ``make``); its window
+    queries point along that direction.  The previous query of head (l, h)
+    points along it only with weight rho[l][h]: about a quarter of the heads
+    are retrieval-like (rho in [0.8, 1.2]), the rest diffuse (rho in [0,
+    0.4]).  Every draft layer is a random projection of the target layers'
+    summed salient structure (keys: salience times direction; queries: the
+    directions), so its attention weights a position by how many layers
+    attend it, plus noise of the layer's own level: some draft layers are
+    informative and some are not.  Lengths are all n (no padding)."""
+    dev = torch.device(device)
+    master = (shape.seed if seed is None else seed) + 7919 * L_t
+    B, N, Hq, Hkv, d, w = shape.B, shape.n, shape.Hq, shape.Hkv, shape.d, shape.w
+    G = Hq // Hkv
+    store = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+    L_d, H_d, Hkv_d, d_d = shape.L_d, shape.H_d, shape.Hkv_d, shape.d_d
+    G_d = H_d // Hkv_d
+
+    gh = _gen(master, "search_heavy", "cpu")
+    cnt = max(1, math.ceil(shape.heavy_frac * N))
+    shared = [torch.randperm(N, generator=gh)[:cnt] for _ in range(B)]
+    gl = _gen(master, "search_layer", "cpu")
+    share = 0.3 + 0.7 * torch.rand(L_t, generator=gl)
+    grho = _gen(master, "search_rho", "cpu")
+    retr = torch.rand((L_t, Hq), generator=grho) < 0.25
+    rho = torch.where(retr, 0.8 + 0.4 * torch.rand((L_t, Hq), generator=grho), 0.4 * torch.rand((L_t, Hq), generator=grho))
+    gd = _gen(master, "search_draft", dev)
+    draft_noise = 0.2 + 1.3 * torch.rand(L_d, generator=_gen(master, "search_draft", "cpu"))
+    Pm = _randn((L_d, Hkv_d, d_d, d), gd, dev) / math.sqrt(d_d)   # keeps inner products in expectation
+
+    K = torch.empty((L_t, B, N, Hkv, d), dtype=store, device=dev)
+    q = torch.empty((L_t, B, w, Hq, d), dtype=store, device=dev)
+    q_prev = torch.empty((L_t, B, Hq, d), dtype=store, device=dev)
+    Kd = torch.empty((L_d, B, N, Hkv_d, d_d), dtype=store, device=dev)
+    q_draft = torch.empty((B, L_d, w, H_d, d_d), dtype=store, device=dev)
+    kv_of = torch.arange(Hq, device=dev) // G
+    for l in range(L_t):
+        gk = _gen(master * 131 + l, "K", dev)
+        gq = _gen(master * 131 + l, "q", dev)
+        gs = _gen(master * 131 + l, "salience", "cpu")
+        coef = torch.zeros((B, N), dtype=torch.float32)
+        keep = int(round(float(share[l]) * cnt))
+        for b in range(B):
+            coef[b, shared[b][torch.randperm(cnt, generator=gs)[:keep]]] = 3.0
+            coef[b, torch.randperm(N, generator=gs)[:cnt - keep]] = 3.0
+        if shape.sigma > 0:
+            coef += torch.exp(shape.sigma * torch.randn((B, N), generator=gs))
+        coef = coef.to(dev)
+        U = _randn((Hkv, d), gk, dev)
+        U = U / U.norm(dim=-1, keepdim=True)
+        Kl = _randn((B, N, Hkv, d), gk, dev) + coef[:, :, None, None] * U[None, None]
+        zeta = _randn((B, Hq, d), gq, dev)
+        lead = math.sqrt(d) * U[kv_of][None]                              # [1][Hq][d]
+        ql = torch.stack([zeta + lead + (0.2 * _randn((B, Hq, d), gq, dev) if s else 0.0) for s in range(w)], dim=1)
+        r = rho[l].to(dev)[None, :, None]
+        qp = zeta + r * lead + 0.2 * _randn((B, Hq, d), gq, dev)
+        if l == 0:
+            ksig = torch.zeros((B, N, Hkv, d), dtype=torch.float32, device=dev)
+            qsig = torch.zeros((Hq, d), dtype=torch.float32, device=dev)
+        ksig += coef[:, :, None, None] * U[None, None] / math.sqrt(L_t)    # the layers' salient structure
+        qsig += lead[0] / math.sqrt(L_t)
+        K[l] = Kl.to(store)
+        q[l] = ql.to(store)
+        q_prev[l] = qp.to(store)
+        del Kl
+    # draft layers: projections of the layers' summed salient structure, each with its own noise
+    for ld in range(L_d):
+        nz = float(draft_noise[ld])
+        for c in range(Hkv_d):
+            t = (ld * Hkv_d + c) % Hkv
+            Kd[ld, :, :, c, :] = (ksig[:, :, t, :] @ Pm[ld, c].T + nz * _randn((B, N, d_d), gd, dev)).to(store)
+        for h in range(H_d):
+            c = h // G_d
+            t = (ld * Hkv_d + c) % Hkv
+            ht = t * G + ((ld + h) % G)
+            qd = qsig[ht] @ Pm[ld, c].T                                       # [d_d]
+            q_draft[:, ld, :, h, :] = (qd[None, None] + nz * _randn((B, w, d_d), gd, dev)).to(store)
+    del ksig, qsig
+    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    return SearchInputs(shape=shape, L_t=L_t, seq_lens=lens, K=K, q=q, q_prev=q_prev, Kd=Kd, q_draft=q_draft,
+                        rho=rho, share=share, draft_noise=draft_noise)
+

@@ -56,3 +56,23 @@ def test_heavy_hitters_present():
     proj = K @ (x.q[0, 0, 0].double() - 0)  # query carries sqrt(d) u
     top = proj.topk(int(math.ceil(0.02 * 1024))).values.mean()
     assert top > proj.mean() + 3 * math.sqrt(64) * 0.8
+
+
+def test_search_inputs_shapes_determinism_and_structure():
+    """The multi-layer profiling batch: shapes and dtypes, the same bytes for
+    the same seed, finite values (no padding), and retrieval-like heads whose
+    previous query leans on the layer's salient direction more than the rest."""
+    sh = synth.preset("c4").replace(B=2, n=1024, Hq=8, Hkv=2, d=64, L_d=4, H_d=4, Hkv_d=2, d_d=32)
+    a = synth.make_search(sh, 3)
+    b = synth.make_search(sh, 3)
+    assert a.K.shape == (3, 2, 1024, 2, 64) and a.q.shape == (3, 2, 4, 8, 64) and a.q_prev.shape == (3, 2, 8, 64)
+    assert a.Kd.shape == (4, 2, 1024, 2, 32) and a.q_draft.shape == (2, 4, 4, 4, 32)
+    assert a.K.dtype == torch.bfloat16 and int(a.seq_lens.min()) == 1024
+    for t in ("K", "q", "q_prev", "Kd", "q_draft"):
+        assert torch.equal(getattr(a, t), getattr(b, t)), t
+        assert torch.isfinite(getattr(a, t).float()).all(), t
+    # cosine of the previous query with the window query's lead direction grows with rho
+    lead = a.q[:, :, 0].float().mean(dim=1)                     # [L][Hq][d] (offsets average out less, still informative)
+    cos = torch.nn.functional.cosine_similarity(a.q_prev.float().mean(dim=1), lead, dim=-1)
+    hi, lo = cos[a.rho > 0.7].mean(), cos[a.rho < 0.2].mean()
+    assert hi > lo
