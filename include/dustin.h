@@ -21,6 +21,9 @@
  *                                        -> dustin_window_mean, dustin_policy_sweep
  *   and the page-level estimator the pages compare scoring costs with
  *                                        -> dustin_page_bounds, dustin_page_scores
+ *   and the offline configuration search of blog section 2.4
+ *                                        -> dustin_head_scores, dustin_candidate_arr,
+ *                                           dustin_greedy_select
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 5
+#define DUSTIN_ABI_VERSION 6
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -370,6 +373,91 @@ dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const du
                                  void *ws, size_t ws_bytes, dustin_stream_t stream);
 
 size_t dustin_page_scores_workspace_bytes(int32_t B, int32_t H_kv, int32_t head_dim);
+
+/*
+ * Offline configuration search (blog section 2.4 and Fig. 6: a (layer, head)
+ * score matrix with its head TopK, greedy target layers/heads, greedy draft
+ * layers with the target fixed, then the draft/target split m; the
+ * objective is the windowed ARR of translation section 3.1, Eq. 2).  These
+ * calls run on profiling data, not on the verification step.
+ *
+ * Objective of a verification set I of sequence b: Eq. 2 is linear in A, so
+ *   (1/w) sum_s sum_{j in I} A[s][j] = sum_{j in I} abar[b][j]
+ * with abar the window-step mean of A (dustin_window_mean), averaged over the
+ * target layers the set has to serve.  A configuration's objective is the
+ * mean over the profiling batch.
+ */
+
+/*
+ * dustin_head_scores -- per-head S_Target rows: the softmax over the history
+ * of every listed (layer, head) pair's query, not summed,
+ *   out[r][b][j] = softmax_{j < n_b}(scale * q_hist[b][r] . Kt_{L(r)}[b][j][H(r) / G]),
+ * 0 at j >= n_b.  Arguments as for dustin_score's target side (up to 64 rows
+ * over up to 8 distinct layers per call); out [S][B][N_max] float32.
+ */
+dustin_status dustin_head_scores(const dustin_kv *target_layers, int32_t L_t, const void *q_hist,
+                                 const int32_t *sub_heads, int32_t S, int32_t H_t, float scale, float *out,
+                                 void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_head_scores_workspace_bytes(int32_t B, int32_t N_max, int32_t S);
+
+/*
+ * dustin_candidate_arr -- objective of C candidate configurations.  For
+ * candidate c and sequence b the verification set is dustin_topk's (blog
+ * section 2.3) on
+ *   S_Draft  = s_draft[b]  + draft_units[u(c)][b]    (side absent if both NULL)
+ *   S_Target = s_target[b] + target_units[u(c)][b]
+ * with m = m_cand[c] (host, nullable; else m), u(c) = unit_ids[c] (host,
+ * nullable; else c), and
+ *   arr[c][b] = sum_{j in I} abar[b][j],   arr_mean[c] = mean_b arr[c][b].
+ *
+ *  s_draft, s_target       [B][N_max] float32 base vectors, nullable
+ *  draft_units / target_units  [U][B][N_max] float32, at most one side
+ *  seq_lens                [B] device int32
+ *  abar                    [B][N_max] float32
+ *  arr                     out [C][B] float32; arr_mean out [C] or NULL
+ *  ws                      >= dustin_candidate_arr_workspace_bytes(C, B,
+ *                          N_max, k, materialize), materialize = 1 when a
+ *                          side has units and (a base or unit_ids)
+ * Ties follow dustin_topk.  C * B <= 2^24.
+ */
+dustin_status dustin_candidate_arr(const float *s_draft, const float *draft_units, const float *s_target,
+                                   const float *target_units, int32_t U, const int32_t *unit_ids, int32_t C,
+                                   const int32_t *m_cand, const int32_t *seq_lens, int32_t B, int32_t N_max,
+                                   const float *abar, int32_t k, int32_t m, int32_t n_sink, int32_t n_window,
+                                   float *arr, float *arr_mean, void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_candidate_arr_workspace_bytes(int32_t C, int32_t B, int32_t N_max, int32_t k, int32_t materialize);
+
+/*
+ * dustin_greedy_select -- greedy forward selection (blog section 2.4, steps
+ * 1 and 2) over C candidate units of one side:
+ *   side 0 (target): units are S_Target vectors; sets use m = 0 (target
+ *     history); the first unit is always taken; s_target_fixed must be NULL.
+ *   side 1 (draft): units are S_Draft vectors, S_Target = s_target_fixed,
+ *     draft budget m; the empty choice (the target-history set) is the
+ *     objective to beat.
+ * Each round evaluates every remaining candidate (dustin_candidate_arr with
+ * the chosen units' sum as the base) and adds the one with the largest
+ * batch-mean objective (ties: lower candidate index); it stops after
+ * max_units additions or when no candidate improves the objective strictly.
+ *
+ *  units        [U][B][N_max] float32; unit_ids host [C] into them (NULL: 0..C-1)
+ *  chosen       host out [max_units]: candidate indices (into the C list) in order
+ *  curve        host out [max_units]: objective after each addition
+ *  n_chosen     host out
+ *  sum_out      device out [B][N_max]: sum of the chosen units (0 if none)
+ *  ws           >= dustin_greedy_select_workspace_bytes(C, B, N_max, k)
+ * Blocking: the call waits for the stream after every round (it reads the
+ * objectives back), so it cannot be captured into a graph.
+ */
+dustin_status dustin_greedy_select(const float *units, int32_t U, const int32_t *unit_ids, int32_t C, int32_t side,
+                                   const float *s_target_fixed, const int32_t *seq_lens, int32_t B, int32_t N_max,
+                                   const float *abar, int32_t k, int32_t m, int32_t n_sink, int32_t n_window,
+                                   int32_t max_units, int32_t *chosen, float *curve, int32_t *n_chosen,
+                                   float *sum_out, void *ws, size_t ws_bytes, dustin_stream_t stream);
+
+size_t dustin_greedy_select_workspace_bytes(int32_t C, int32_t B, int32_t N_max, int32_t k);
 
 /* Human-readable name of a status code (static storage). */
 const char *dustin_status_string(dustin_status status);

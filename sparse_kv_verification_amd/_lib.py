@@ -27,6 +27,8 @@ EXPORTS = [
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
     "dustin_arr", "dustin_window_mean", "dustin_policy_sweep", "dustin_policy_sweep_workspace_bytes",
     "dustin_page_bounds", "dustin_page_scores", "dustin_page_scores_workspace_bytes",
+    "dustin_head_scores", "dustin_head_scores_workspace_bytes", "dustin_candidate_arr",
+    "dustin_candidate_arr_workspace_bytes", "dustin_greedy_select", "dustin_greedy_select_workspace_bytes",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
 ]
 
@@ -102,6 +104,22 @@ def lib():
         L.dustin_page_scores.argtypes = [vp, i32, i32, kvp, vp, vp, f32, vp, vp, sz, vp]
         L.dustin_page_scores_workspace_bytes.argtypes = [i32, i32, i32]
         L.dustin_page_scores_workspace_bytes.restype = sz
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        L.dustin_head_scores.argtypes = [vp, i32, vp, vp, i32, i32, f32, vp, vp, sz, vp]
+        L.dustin_head_scores.restype = ctypes.c_int
+        L.dustin_head_scores_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dustin_head_scores_workspace_bytes.restype = sz
+        L.dustin_candidate_arr.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, vp, i32, i32, i32, i32,
+                                           vp, vp, vp, sz, vp]
+        L.dustin_candidate_arr.restype = ctypes.c_int
+        L.dustin_candidate_arr_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.dustin_candidate_arr_workspace_bytes.restype = sz
+        L.dustin_greedy_select.argtypes = [vp, i32, vp, i32, i32, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32,
+                                           i32p, f32p, i32p, vp, vp, sz, vp]
+        L.dustin_greedy_select.restype = ctypes.c_int
+        L.dustin_greedy_select_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.dustin_greedy_select_workspace_bytes.restype = sz
         L.dustin_page_scores.restype = ctypes.c_int
         L.dustin_status_string.argtypes = [ctypes.c_int]
         L.dustin_status_string.restype = ctypes.c_char_p
@@ -119,7 +137,13 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a GPU tensor (None for None).  A tensor in host
+    memory is refused here: a kernel dereferencing a host address faults."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError(f"expected a GPU tensor, got one on {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(t=None):
@@ -148,6 +172,9 @@ class KV:
         self.k, self.v, self.seq_lens, self.page_table = k, v, seq_lens, page_table
         if seq_lens is None or seq_lens.dtype != torch.int32:
             raise TypeError("seq_lens must be an int32 tensor")
+        for name, t in (("k", k), ("v", v), ("seq_lens", seq_lens), ("page_table", page_table)):
+            if t is not None and not t.is_cuda:
+                raise TypeError(f"KV: {name} must be a GPU tensor, got one on {t.device}")
         if page_table is None:
             Bk, N, H, D = k.shape
             ps, maxp, npages = 0, 0, 0
@@ -385,3 +412,71 @@ def dustin_page_scores(q, kv: KV, kmin, kmax, scale=0.0, scores=None, ws: Worksp
     _check(lib().dustin_page_scores(_ptr(q), w, Hq, kv.ref, _ptr(kmin), _ptr(kmax), float(scale), _ptr(scores),
                                     _ptr(wsb), wsb.numel(), _stream(q)))
     return scores
+
+
+def _host_i32(vals):
+    if vals is None:
+        return None
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+def dustin_head_scores(target_kvs, q_hist, sub_heads, H_t, scale=0.0, out=None, ws: Workspace | None = None):
+    """Per-(layer, head) S_Target rows [S][B][N_max] float32 (not summed).
+    q_hist: [B][S][d]; sub_heads: S (layer, head) pairs into target_kvs."""
+    d = target_kvs[0].desc
+    S = len(sub_heads)
+    if out is None:
+        out = torch.empty((S, d.B, d.N_max), dtype=torch.float32, device=q_hist.device)
+    heads = (ctypes.c_int32 * (2 * S))(*[x for p in sub_heads for x in p])
+    wsb = _ws("heads", ws, lib().dustin_head_scores_workspace_bytes(d.B, d.N_max, S), q_hist.device)
+    _check(lib().dustin_head_scores(_kv_array(target_kvs), len(target_kvs), _ptr(q_hist), heads, S, int(H_t),
+                                    float(scale), _ptr(out), _ptr(wsb), wsb.numel(), _stream(q_hist)))
+    return out
+
+
+def dustin_candidate_arr(seq_lens, abar, k, m, n_sink, n_window, s_draft=None, draft_units=None, s_target=None,
+                         target_units=None, unit_ids=None, C=None, m_cand=None, arr=None, arr_mean=None,
+                         want_mean=True, ws: Workspace | None = None):
+    """Objective of C candidate configurations: arr [C][B] (and the batch
+    means [C]); units [U][B][N_max] on one side, base vectors [B][N_max]."""
+    B, N = abar.shape
+    units = draft_units if draft_units is not None else target_units
+    U = 0 if units is None else units.shape[0]
+    if C is None:
+        C = len(unit_ids) if unit_ids is not None else (len(m_cand) if m_cand is not None else U or 1)
+    dev = abar.device
+    if arr is None:
+        arr = torch.empty((C, B), dtype=torch.float32, device=dev)
+    if arr_mean is None and want_mean:
+        arr_mean = torch.empty((C,), dtype=torch.float32, device=dev)
+    base = s_draft if draft_units is not None else s_target
+    mat = units is not None and (unit_ids is not None or base is not None)
+    wsb = _ws("cand", ws, lib().dustin_candidate_arr_workspace_bytes(C, B, N, k, int(mat)), dev)
+    _check(lib().dustin_candidate_arr(_ptr(s_draft), _ptr(draft_units), _ptr(s_target), _ptr(target_units), U,
+                                      _host_i32(unit_ids), C, _host_i32(m_cand), _ptr(seq_lens), B, N, _ptr(abar),
+                                      k, m, n_sink, n_window, _ptr(arr), _ptr(arr_mean), _ptr(wsb), wsb.numel(),
+                                      _stream(abar)))
+    return arr, arr_mean
+
+
+def dustin_greedy_select(units, seq_lens, abar, k, m, n_sink, n_window, max_units, side, s_target_fixed=None,
+                         unit_ids=None, sum_out=None, ws: Workspace | None = None):
+    """Greedy forward selection over candidate units of one side (0 target,
+    1 draft).  Returns (chosen candidate indices, objective curve, sum of the
+    chosen units [B][N_max])."""
+    U, B, N = units.shape
+    C = len(unit_ids) if unit_ids is not None else U
+    if sum_out is None:
+        sum_out = torch.empty((B, N), dtype=torch.float32, device=units.device)
+    chosen = (ctypes.c_int32 * max(max_units, 1))()
+    curve = (ctypes.c_float * max(max_units, 1))()
+    n_ch = ctypes.c_int32(0)
+    wsb = _ws("greedy", ws, lib().dustin_greedy_select_workspace_bytes(C, B, N, k), units.device)
+    _check(lib().dustin_greedy_select(_ptr(units), U, _host_i32(unit_ids), C, int(side), _ptr(s_target_fixed),
+                                      _ptr(seq_lens), B, N, _ptr(abar), k, m, n_sink, n_window, max_units, chosen,
+                                      curve, ctypes.byref(n_ch), _ptr(sum_out), _ptr(wsb), wsb.numel(),
+                                      _stream(units)))
+    n = n_ch.value
+    return [chosen[i] for i in range(n)], [curve[i] for i in range(n)], sum_out
+

@@ -12,6 +12,7 @@
 #include "dustin.h"
 #include "common.h"
 #include "internal.h"
+#include <vector>
 
 using namespace dustin;
 
@@ -197,6 +198,51 @@ dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q,
     snprintf(what, sizeof what, "%s launch", name);
     return hip_status(launch_attn(a, p, (hipStream_t)stream), what);
 }
+
+// Target side of the scoring calls: checks the (layer, head) rows and their
+// layers and fills the layer views, row tables, query pointer and scale.
+dustin_status prep_target(const dustin_kv *target_layers, int32_t L_t, const void *q_hist, const int32_t *sub_heads,
+                          int32_t S, int32_t H_t, float scale_target, TargetScoreArgs &a, const dustin_kv *&t0) {
+    CHECK(target_layers != nullptr && L_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: target_layers missing");
+    CHECK(sub_heads != nullptr && q_hist != nullptr, DUSTIN_ERR_INVALID_ARG, "score: sub_heads / q_hist missing");
+    CHECK(S <= kMaxScoreRows, DUSTIN_ERR_UNSUPPORTED, "score: S %d exceeds %d", S, kMaxScoreRows);
+    CHECK(H_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_t must be >= 1");
+    CHECK(L_t <= 64, DUSTIN_ERR_UNSUPPORTED, "score: L_t %d exceeds 64", L_t);
+    int view_of_layer[64];
+    int n_views = 0;
+    int layer_ids[8];
+    for (int l = 0; l < L_t; ++l) view_of_layer[l] = -1;
+    for (int r = 0; r < S; ++r) {
+        const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
+        CHECK(l >= 0 && l < L_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] layer %d out of range", r, l);
+        CHECK(h >= 0 && h < H_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] head %d out of range", r, h);
+        if (view_of_layer[l] < 0) {
+            dustin_status st = check_kv(&target_layers[l], "score target layer", false);
+            if (st != DUSTIN_OK) return st;
+            CHECK(n_views < 8, DUSTIN_ERR_UNSUPPORTED, "score: more than 8 distinct target layers");
+            CHECK(H_t % target_layers[l].H_kv == 0, DUSTIN_ERR_INVALID_ARG,
+                  "score: H_t %d not a multiple of layer %d H_kv", H_t, l);
+            view_of_layer[l] = n_views;
+            layer_ids[n_views++] = l;
+        }
+    }
+    t0 = &target_layers[layer_ids[0]];
+    for (int i = 1; i < n_views; ++i)
+        CHECK(same_geometry(&target_layers[layer_ids[i]], t0), DUSTIN_ERR_INVALID_ARG,
+              "score: scored target layers differ in geometry");
+    for (int i = 0; i < n_views; ++i) a.kv[i] = view_of(&target_layers[layer_ids[i]]);
+    a.n_layers = n_views;
+    a.q_hist = q_hist;
+    a.S = S;
+    for (int r = 0; r < S; ++r) {
+        const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
+        a.row_layer[r] = view_of_layer[l];
+        a.row_kvh[r] = h / (H_t / target_layers[l].H_kv);
+    }
+    a.scale_log2 = resolve_scale(scale_target, a.kv[0].D) * kLog2e;
+    return DUSTIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,34 +427,11 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
                   DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than this build supports");
         }
     }
-    int view_of_layer[64];
-    int n_views = 0;
-    int layer_ids[8];
+    TargetScoreArgs ta{};
     if (do_target) {
-        CHECK(target_layers != nullptr && L_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: target_layers missing");
-        CHECK(sub_heads != nullptr && q_hist != nullptr, DUSTIN_ERR_INVALID_ARG, "score: sub_heads / q_hist missing");
-        CHECK(S <= kMaxScoreRows, DUSTIN_ERR_UNSUPPORTED, "score: S %d exceeds %d", S, kMaxScoreRows);
-        CHECK(H_t >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_t must be >= 1");
-        CHECK(L_t <= 64, DUSTIN_ERR_UNSUPPORTED, "score: L_t %d exceeds 64", L_t);
-        for (int l = 0; l < L_t; ++l) view_of_layer[l] = -1;
-        for (int r = 0; r < S; ++r) {
-            const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
-            CHECK(l >= 0 && l < L_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] layer %d out of range", r, l);
-            CHECK(h >= 0 && h < H_t, DUSTIN_ERR_INVALID_ARG, "score: sub_heads[%d] head %d out of range", r, h);
-            if (view_of_layer[l] < 0) {
-                dustin_status st = check_kv(&target_layers[l], "score target layer", false);
-                if (st != DUSTIN_OK) return st;
-                CHECK(n_views < 8, DUSTIN_ERR_UNSUPPORTED, "score: more than 8 distinct target layers");
-                CHECK(H_t % target_layers[l].H_kv == 0, DUSTIN_ERR_INVALID_ARG,
-                      "score: H_t %d not a multiple of layer %d H_kv", H_t, l);
-                view_of_layer[l] = n_views;
-                layer_ids[n_views++] = l;
-            }
-        }
-        const dustin_kv *t0 = &target_layers[layer_ids[0]];
-        for (int i = 1; i < n_views; ++i)
-            CHECK(same_geometry(&target_layers[layer_ids[i]], t0), DUSTIN_ERR_INVALID_ARG,
-                  "score: scored target layers differ in geometry");
+        const dustin_kv *t0 = nullptr;
+        dustin_status st = prep_target(target_layers, L_t, q_hist, sub_heads, S, H_t, scale_target, ta, t0);
+        if (st != DUSTIN_OK) return st;
         if (ref) {
             CHECK(t0->B == ref->B && t0->N_max == ref->N_max, DUSTIN_ERR_INVALID_ARG,
                   "score: draft and target describe different batches");
@@ -423,23 +446,12 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
     char *wsb = (char *)ws;
     hipStream_t s = (hipStream_t)stream;
     if (do_target) {
-        TargetScoreArgs a{};
-        for (int i = 0; i < n_views; ++i) a.kv[i] = view_of(&target_layers[layer_ids[i]]);
-        a.n_layers = n_views;
-        a.q_hist = q_hist;
-        a.S = S;
-        for (int r = 0; r < S; ++r) {
-            const int l = sub_heads[2 * r], h = sub_heads[2 * r + 1];
-            a.row_layer[r] = view_of_layer[l];
-            a.row_kvh[r] = h / (H_t / target_layers[l].H_kv);
-        }
-        a.scale_log2 = resolve_scale(scale_target, a.kv[0].D) * kLog2e;
-        a.s_target = s_target;
-        a.logit = (float *)(wsb + p.off_tlogit);
-        a.stat = (float *)(wsb + p.off_tstat);
-        a.lse = (float *)(wsb + p.off_tlse);
-        a.nchunk = p.nchunk;
-        hipError_t e = launch_target_score(a, s);
+        ta.s_target = s_target;
+        ta.logit = (float *)(wsb + p.off_tlogit);
+        ta.stat = (float *)(wsb + p.off_tstat);
+        ta.lse = (float *)(wsb + p.off_tlse);
+        ta.nchunk = p.nchunk;
+        hipError_t e = launch_target_score(ta, s);
         if (e != hipSuccess) return hip_status(e, "score target launch");
     }
     if (do_draft) {
@@ -642,3 +654,294 @@ dustin_status dustin_page_scores(const void *q, int32_t w, int32_t H_q, const du
 }
 
 }  // extern "C"
+
+namespace {
+// Candidate-evaluation workspace: the unit index list, the materialised
+// candidate rows (when a side adds units to a base or picks units by index),
+// the index sets and counts of all C * B rows, and the select kernels' flag
+// array when the general select kernel runs (N_max > 131072).
+struct CandLayout {
+    size_t off_ids, off_rows, off_idx, off_cnt, off_flag, bytes;
+};
+
+CandLayout cand_layout(int C, int B, int N_max, int k, bool materialize) {
+    CandLayout L{};
+    const size_t rows = (size_t)C * B;
+    size_t off = 0;
+    L.off_ids = off;
+    off = align_up(off + (size_t)C * sizeof(int32_t), 256);
+    L.off_rows = off;
+    if (materialize) off = align_up(off + rows * N_max * sizeof(float), 256);
+    L.off_idx = off;
+    off = align_up(off + rows * k * sizeof(int32_t), 256);
+    L.off_cnt = off;
+    off = align_up(off + rows * sizeof(int32_t), 256);
+    L.off_flag = off;
+    if ((N_max + 1023) / 1024 > 128) off = align_up(off + rows * N_max, 256);
+    L.bytes = off;
+    return L;
+}
+
+struct CandSide {
+    const float *base, *units;
+};
+
+// Evaluates C candidates (arguments already checked): per side, either a base
+// vector shared by every candidate, units (one per candidate, optionally by
+// index), or both (materialised sums).  m_cand (host, nullable) gives each
+// candidate its own m.
+dustin_status cand_run(CandSide d, CandSide t, int U, const int32_t *unit_ids, int C, const int32_t *m_cand,
+                       const int32_t *seq_lens, int B, int N_max, const float *abar, int k, int m, int n_sink,
+                       int n_window, float *arr, float *arr_mean, char *ws, hipStream_t s) {
+    (void)U;
+    const bool has_units = d.units || t.units;
+    const bool mat = has_units && (unit_ids != nullptr || (d.units ? d.base : t.base) != nullptr);
+    const CandLayout L = cand_layout(C, B, N_max, k, mat);
+    const int32_t *ids_dev = nullptr;
+    if (has_units && unit_ids) {
+        hipError_t e = hipMemcpyAsync(ws + L.off_ids, unit_ids, (size_t)C * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, "candidate ids copy");
+        ids_dev = (const int32_t *)(ws + L.off_ids);
+    }
+    // per side: the pointer the select kernels read and its row modulus
+    const float *pd = nullptr, *pt = nullptr;
+    int md = 0, mt = 0;
+    auto place = [&](CandSide c, const float *&ptr, int &mod) -> hipError_t {
+        if (!c.base && !c.units) return hipSuccess;
+        if (!c.units) {
+            ptr = c.base;
+            mod = B;
+            return hipSuccess;
+        }
+        if (mat) {
+            float *rows = (float *)(ws + L.off_rows);
+            if (ids_dev) {
+                hipError_t e = launch_build_rows(c.base, c.units, ids_dev, C, B, N_max, rows, s);
+                if (e != hipSuccess) return e;
+            } else {
+                // identity ids: candidate c is unit c
+                hipError_t e = hipSuccess;
+                for (int cc = 0; cc < C && e == hipSuccess; ++cc) {
+                    float *dst = rows + (size_t)cc * B * N_max;
+                    e = launch_accumulate(dst, c.base, (int64_t)B * N_max, true, s);
+                    if (e == hipSuccess) e = launch_accumulate(dst, c.units + (size_t)cc * B * N_max, (int64_t)B * N_max, false, s);
+                }
+                if (e != hipSuccess) return e;
+            }
+            ptr = rows;
+        } else {
+            ptr = c.units;   // rows c * B + b are contiguous
+        }
+        mod = 0;
+        return hipSuccess;
+    };
+    hipError_t e = place(d, pd, md);
+    if (e == hipSuccess) e = place(t, pt, mt);
+    if (e != hipSuccess) return hip_status(e, "candidate rows");
+    int32_t *idx = (int32_t *)(ws + L.off_idx);
+    int32_t *cnt = (int32_t *)(ws + L.off_cnt);
+    TopkArgs a{};
+    a.seq_lens = seq_lens;
+    a.N_max = N_max;
+    a.k = k;
+    a.n_sink = n_sink;
+    a.n_window = n_window;
+    a.tier = nullptr;
+    a.flag = (uint8_t *)(ws + L.off_flag);
+    a.len_mod = B;
+    if (!m_cand) {
+        a.s_draft = pd;
+        a.s_target = pt;
+        a.d_mod = md;
+        a.t_mod = mt;
+        a.B = C * B;
+        a.m = m;
+        a.idx = idx;
+        a.count = cnt;
+        e = launch_topk(a, s);
+    } else {
+        for (int c = 0; c < C && e == hipSuccess; ++c) {
+            const size_t off = (size_t)c * B;
+            a.s_draft = pd ? (md ? pd : pd + off * N_max) : nullptr;
+            a.s_target = pt ? (mt ? pt : pt + off * N_max) : nullptr;
+            a.d_mod = md;
+            a.t_mod = mt;
+            a.B = B;
+            a.m = m_cand[c];
+            a.idx = idx + off * k;
+            a.count = cnt + off;
+            a.flag = (uint8_t *)(ws + L.off_flag) + off * N_max;
+            e = launch_topk(a, s);
+        }
+    }
+    if (e == hipSuccess) e = launch_gather_sum(abar, idx, cnt, C * B, B, N_max, k, arr, s);
+    if (e == hipSuccess && arr_mean) e = launch_batch_mean(arr, C, B, arr_mean, s);
+    return hip_status(e, "candidate evaluation");
+}
+
+dustin_status cand_check(const float *s_draft, const float *draft_units, const float *s_target,
+                         const float *target_units, int32_t U, const int32_t *unit_ids, int32_t C,
+                         const int32_t *m_cand, const int32_t *seq_lens, int32_t B, int32_t N_max, const float *abar,
+                         int32_t k, int32_t m, int32_t n_sink, int32_t n_window, const char *name) {
+    CHECK(s_draft || draft_units || s_target || target_units, DUSTIN_ERR_INVALID_ARG,
+          "%s: at least one score side is required", name);
+    CHECK(!(draft_units && target_units), DUSTIN_ERR_INVALID_ARG, "%s: units on one side only", name);
+    CHECK(seq_lens && abar, DUSTIN_ERR_INVALID_ARG, "%s: seq_lens and abar are required", name);
+    CHECK(C >= 1 && B >= 1 && N_max >= 1 && k >= 1, DUSTIN_ERR_INVALID_ARG, "%s: C, B, N_max, k must be >= 1", name);
+    CHECK(m >= 0 && n_sink >= 0 && n_window >= 0 && (int64_t)n_sink + n_window <= k, DUSTIN_ERR_INVALID_ARG,
+          "%s: need m, n_sink, n_window >= 0 and n_sink + n_window <= k", name);
+    CHECK((int64_t)C * B <= (1 << 24) && (int64_t)C * B * N_max <= ((int64_t)1 << 40), DUSTIN_ERR_UNSUPPORTED,
+          "%s: C * B = %lld rows too many", name, (long long)C * B);
+    if (draft_units || target_units) {
+        CHECK(U >= 1, DUSTIN_ERR_INVALID_ARG, "%s: U must be >= 1", name);
+        if (unit_ids) {
+            for (int c = 0; c < C; ++c)
+                CHECK(unit_ids[c] >= 0 && unit_ids[c] < U, DUSTIN_ERR_INVALID_ARG, "%s: unit_ids[%d] = %d out of [0, %d)",
+                      name, c, unit_ids[c], U);
+        } else {
+            CHECK(C <= U, DUSTIN_ERR_INVALID_ARG, "%s: C = %d exceeds U = %d without unit_ids", name, C, U);
+        }
+    }
+    if (m_cand)
+        for (int c = 0; c < C; ++c)
+            CHECK(m_cand[c] >= 0, DUSTIN_ERR_INVALID_ARG, "%s: m_cand[%d] < 0", name, c);
+    return DUSTIN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t dustin_head_scores_workspace_bytes(int32_t B, int32_t N_max, int32_t S) {
+    if (B < 1 || N_max < 1 || S < 1) return 0;
+    return score_plan(B, N_max, 0, 0, 0, S, 1).ws_bytes;
+}
+
+dustin_status dustin_head_scores(const dustin_kv *target_layers, int32_t L_t, const void *q_hist,
+                                 const int32_t *sub_heads, int32_t S, int32_t H_t, float scale, float *out, void *ws,
+                                 size_t ws_bytes, dustin_stream_t stream) {
+    CHECK(S >= 1, DUSTIN_ERR_INVALID_ARG, "head_scores: S must be >= 1");
+    CHECK(out != nullptr, DUSTIN_ERR_INVALID_ARG, "head_scores: out is required");
+    CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "head_scores: scale is not finite");
+    TargetScoreArgs a{};
+    const dustin_kv *t0 = nullptr;
+    dustin_status st = prep_target(target_layers, L_t, q_hist, sub_heads, S, H_t, scale, a, t0);
+    if (st != DUSTIN_OK) return st;
+    const ScorePlan p = score_plan(t0->B, t0->N_max, 0, 0, 0, S, 1);
+    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+          "head_scores: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+    char *wsb = (char *)ws;
+    a.s_target = nullptr;
+    a.rows_out = out;
+    a.logit = (float *)(wsb + p.off_tlogit);
+    a.stat = (float *)(wsb + p.off_tstat);
+    a.lse = (float *)(wsb + p.off_tlse);
+    a.nchunk = p.nchunk;
+    return hip_status(launch_target_score(a, (hipStream_t)stream), "head_scores launch");
+}
+
+size_t dustin_candidate_arr_workspace_bytes(int32_t C, int32_t B, int32_t N_max, int32_t k, int32_t materialize) {
+    if (C < 1 || B < 1 || N_max < 1 || k < 1) return 0;
+    return cand_layout(C, B, N_max, k, materialize != 0).bytes;
+}
+
+dustin_status dustin_candidate_arr(const float *s_draft, const float *draft_units, const float *s_target,
+                                   const float *target_units, int32_t U, const int32_t *unit_ids, int32_t C,
+                                   const int32_t *m_cand, const int32_t *seq_lens, int32_t B, int32_t N_max,
+                                   const float *abar, int32_t k, int32_t m, int32_t n_sink, int32_t n_window,
+                                   float *arr, float *arr_mean, void *ws, size_t ws_bytes, dustin_stream_t stream) {
+    dustin_status st = cand_check(s_draft, draft_units, s_target, target_units, U, unit_ids, C, m_cand, seq_lens, B,
+                                  N_max, abar, k, m, n_sink, n_window, "candidate_arr");
+    if (st != DUSTIN_OK) return st;
+    CHECK(arr != nullptr, DUSTIN_ERR_INVALID_ARG, "candidate_arr: arr is required");
+    const bool has_units = draft_units || target_units;
+    const bool mat = has_units && (unit_ids != nullptr || (draft_units ? s_draft : s_target) != nullptr);
+    const size_t need = cand_layout(C, B, N_max, k, mat).bytes;
+    CHECK(ws != nullptr && ws_bytes >= need, DUSTIN_ERR_INVALID_ARG,
+          "candidate_arr: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    return cand_run({s_draft, draft_units}, {s_target, target_units}, U, unit_ids, C, m_cand, seq_lens, B, N_max, abar,
+                    k, m, n_sink, n_window, arr, arr_mean, (char *)ws, (hipStream_t)stream);
+}
+
+size_t dustin_greedy_select_workspace_bytes(int32_t C, int32_t B, int32_t N_max, int32_t k) {
+    if (C < 1 || B < 1 || N_max < 1 || k < 1) return 0;
+    return align_up(cand_layout(C, B, N_max, k, true).bytes, 256) + align_up((size_t)C * B * sizeof(float), 256) +
+           align_up((size_t)C * sizeof(float), 256);
+}
+
+dustin_status dustin_greedy_select(const float *units, int32_t U, const int32_t *unit_ids, int32_t C, int32_t side,
+                                   const float *s_target_fixed, const int32_t *seq_lens, int32_t B, int32_t N_max,
+                                   const float *abar, int32_t k, int32_t m, int32_t n_sink, int32_t n_window,
+                                   int32_t max_units, int32_t *chosen, float *curve, int32_t *n_chosen,
+                                   float *sum_out, void *ws, size_t ws_bytes, dustin_stream_t stream) {
+    CHECK(side == 0 || side == 1, DUSTIN_ERR_INVALID_ARG, "greedy_select: side must be 0 (target) or 1 (draft)");
+    CHECK(units != nullptr, DUSTIN_ERR_INVALID_ARG, "greedy_select: units are required");
+    CHECK(side == 0 ? s_target_fixed == nullptr : s_target_fixed != nullptr, DUSTIN_ERR_INVALID_ARG,
+          "greedy_select: s_target_fixed is required for the draft side and not taken for the target side");
+    CHECK(max_units >= 0 && chosen && curve && n_chosen && sum_out, DUSTIN_ERR_INVALID_ARG,
+          "greedy_select: max_units >= 0 and the chosen / curve / n_chosen / sum_out outputs are required");
+    dustin_status st = cand_check(nullptr, side ? units : nullptr, s_target_fixed, side ? nullptr : units, U, unit_ids,
+                                  C, nullptr, seq_lens, B, N_max, abar, k, side ? m : 0, n_sink, n_window,
+                                  "greedy_select");
+    if (st != DUSTIN_OK) return st;
+    const size_t cbytes = align_up(cand_layout(C, B, N_max, k, true).bytes, 256);
+    const size_t need = dustin_greedy_select_workspace_bytes(C, B, N_max, k);
+    CHECK(ws != nullptr && ws_bytes >= need, DUSTIN_ERR_INVALID_ARG,
+          "greedy_select: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    float *arr = (float *)(wsb + cbytes);
+    float *mean = (float *)(wsb + cbytes + align_up((size_t)C * B * sizeof(float), 256));
+    std::vector<int32_t> ids(C);
+    for (int c = 0; c < C; ++c) ids[c] = unit_ids ? unit_ids[c] : c;
+    std::vector<float> host(C);
+    std::vector<char> used(C, 0);
+    auto fetch = [&](int n) -> hipError_t {
+        hipError_t e = hipMemcpyAsync(host.data(), mean, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        return e;
+    };
+    const int64_t nel = (int64_t)B * N_max;
+    hipError_t e = launch_accumulate(sum_out, nullptr, nel, true, s);   // the empty choice sums to 0
+    if (e != hipSuccess) return hip_status(e, "greedy_select clear");
+    float best = -__builtin_huge_valf();
+    if (side == 1) {
+        // the target-history set alone is the objective to beat
+        st = cand_run({nullptr, nullptr}, {s_target_fixed, nullptr}, U, nullptr, 1, nullptr, seq_lens, B, N_max, abar,
+                      k, 0, n_sink, n_window, arr, mean, wsb, s);
+        if (st != DUSTIN_OK) return st;
+        if ((e = fetch(1)) != hipSuccess) return hip_status(e, "greedy_select start");
+        best = host[0];
+    }
+    int got = 0;
+    for (int it = 0; it < max_units; ++it) {
+        const float *base = got ? sum_out : nullptr;
+        if (side == 0)
+            st = cand_run({nullptr, nullptr}, {base, units}, U, ids.data(), C, nullptr, seq_lens, B, N_max, abar, k, 0,
+                          n_sink, n_window, arr, mean, wsb, s);
+        else
+            st = cand_run({base, units}, {s_target_fixed, nullptr}, U, ids.data(), C, nullptr, seq_lens, B, N_max, abar,
+                          k, m, n_sink, n_window, arr, mean, wsb, s);
+        if (st != DUSTIN_OK) return st;
+        if ((e = fetch(C)) != hipSuccess) return hip_status(e, "greedy_select fetch");
+        int top = -1;
+        float tv = -__builtin_huge_valf();
+        for (int c = 0; c < C; ++c)
+            if (!used[c] && host[c] > tv) {
+                tv = host[c];
+                top = c;
+            }
+        if (top < 0 || !(tv > best)) break;
+        used[top] = 1;
+        chosen[got] = top;
+        curve[got] = tv;
+        best = tv;
+        e = launch_accumulate(sum_out, units + (size_t)ids[top] * nel, nel, false, s);
+        if (e != hipSuccess) return hip_status(e, "greedy_select accumulate");
+        ++got;
+    }
+    *n_chosen = got;
+    return hip_status(hipStreamSynchronize(s), "greedy_select");
+}
+
+}  // extern "C"
+

@@ -90,6 +90,7 @@ struct TargetScoreArgs {
     int32_t row_kvh[kMaxScoreRows];     // KV head of each row
     float scale_log2;
     float *s_target;                // [B][N_max]
+    float *rows_out;                // [S][B][N_max] per-row probabilities instead of the sum, or NULL
     float *logit;                   // ws
     float *stat;                    // ws
     float *lse;                     // ws
@@ -122,11 +123,22 @@ struct TopkArgs {
     const float *s_draft, *s_target;
     const int32_t *seq_lens;
     int32_t B, N_max, k, m, n_sink, n_window;
+    // row r of a launch reads score row r % d_mod / r % t_mod and length
+    // r % len_mod (0: row r itself), so candidates can share a base vector
+    int32_t d_mod, t_mod, len_mod;
     int32_t *idx, *count;
     int8_t *tier;
     uint8_t *flag;
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- configuration search
+hipError_t launch_build_rows(const float *base, const float *units, const int32_t *ids, int C, int B, int N_max,
+                             float *out, hipStream_t s);
+hipError_t launch_gather_sum(const float *abar, const int32_t *idx, const int32_t *count, int rows, int B, int N_max,
+                             int k, float *arr, hipStream_t s);
+hipError_t launch_batch_mean(const float *arr, int C, int B, float *mean, hipStream_t s);
+hipError_t launch_accumulate(float *dst, const float *src, int64_t n, bool overwrite, hipStream_t s);
 
 // ---------------------------------------------------------------- evaluator
 struct WindowArgs {

@@ -200,6 +200,17 @@ __global__ __launch_bounds__(256) void target_finalize(const float *logit, const
     out[(int64_t)b * N_max + j] = acc;
 }
 
+// Per-row form: out[r][b][j] = exp2(logit[b][r][j] - lse[b][r]) for j < n_b, 0 beyond.
+__global__ __launch_bounds__(256) void target_rows_finalize(const float *logit, const float *lse, float *out,
+                                                            const int32_t *seq_lens, int B, int S, int N_max) {
+    const int b = blockIdx.y, r = blockIdx.z;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= N_max) return;
+    const int nb = min(max(seq_lens[b], 0), N_max);
+    const int64_t row = (int64_t)b * S + r;
+    out[((int64_t)r * B + b) * N_max + j] = (j < nb) ? exp2f(logit[row * N_max + j] - lse[row]) : 0.f;
+}
+
 // ---------------------------------------------------------------------------
 // Draft side, float32 storage: VALU accumulation pass.  One work-group per
 // (sequence, chunk); loops over every unit in order.
@@ -1012,8 +1023,13 @@ static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
     float *lse = a.lse;
     hipLaunchKernelGGL(rows_lse, dim3((k0.B * a.S + 3) / 4), dim3(256), 0, s, a.stat, lse, k0.B * a.S, a.nchunk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(target_finalize, dim3((k0.N_max + 255) / 256, k0.B), dim3(256), 0, s, a.logit, lse,
-                       a.s_target, k0.seq_lens, a.S, k0.N_max);
+    if (a.rows_out) {
+        hipLaunchKernelGGL(target_rows_finalize, dim3((k0.N_max + 255) / 256, k0.B, a.S), dim3(256), 0, s, a.logit,
+                           lse, a.rows_out, k0.seq_lens, k0.B, a.S, k0.N_max);
+    } else {
+        hipLaunchKernelGGL(target_finalize, dim3((k0.N_max + 255) / 256, k0.B), dim3(256), 0, s, a.logit, lse,
+                           a.s_target, k0.seq_lens, a.S, k0.N_max);
+    }
     return hipGetLastError();
 }
 

@@ -132,7 +132,7 @@ __device__ void select_top(const float *sc, uint8_t *flag, int n, int K, int nca
 __global__ __launch_bounds__(TKT) void topk_kernel(TopkArgs a) {
     __shared__ TopkShared sh;
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int n = min(max(a.seq_lens[b], 0), a.N_max);
+    const int n = min(max(a.seq_lens[a.len_mod ? b % a.len_mod : b], 0), a.N_max);
     uint8_t *flag = a.flag + (int64_t)b * a.N_max;
     const int se = min(a.n_sink, n);
     const int wb = max(0, n - a.n_window);
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(TKT) void topk_kernel(TopkArgs a) {
 
     for (int j = tid; j < n; j += TKT) flag[j] = (j < se || j >= wb) ? 1 : 0;
     __syncthreads();
-    if (m_eff > 0) select_top(a.s_draft + (int64_t)b * a.N_max, flag, n, m_eff, rest, 2, sh);
-    if (t_cnt > 0) select_top(a.s_target + (int64_t)b * a.N_max, flag, n, t_cnt, rest - m_eff, 3, sh);
+    if (m_eff > 0) select_top(a.s_draft + (int64_t)(a.d_mod ? b % a.d_mod : b) * a.N_max, flag, n, m_eff, rest, 2, sh);
+    if (t_cnt > 0) select_top(a.s_target + (int64_t)(a.t_mod ? b % a.t_mod : b) * a.N_max, flag, n, t_cnt, rest - m_eff, 3, sh);
 
     int32_t *idx = a.idx + (int64_t)b * a.k;
     int8_t *tier = a.tier ? a.tier + (int64_t)b * a.k : nullptr;
@@ -329,7 +329,7 @@ template <int MW>
 __global__ __launch_bounds__(TKT) void topk_regs_kernel(TopkArgs a) {
     __shared__ TopkShared sh;
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int n = min(max(a.seq_lens[b], 0), a.N_max);
+    const int n = min(max(a.seq_lens[a.len_mod ? b % a.len_mod : b], 0), a.N_max);
     const int se = min(a.n_sink, n);
     const int wb = max(0, n - a.n_window);
     const int np = se + (n - max(wb, se));
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(TKT) void topk_regs_kernel(TopkArgs a) {
         cm[w] = m;
         dsel[w] = tsel[w] = 0;
     }
-    if (m_eff > 0) select_top_regs<MW>(a.s_draft + (int64_t)b * a.N_max, j0, Pl, cm, dsel, m_eff, rest, sh);
+    if (m_eff > 0) select_top_regs<MW>(a.s_draft + (int64_t)(a.d_mod ? b % a.d_mod : b) * a.N_max, j0, Pl, cm, dsel, m_eff, rest, sh);
 #pragma unroll
     for (int w = 0; w < MW; ++w) cm[w] &= ~dsel[w];
-    if (t_cnt > 0) select_top_regs<MW>(a.s_target + (int64_t)b * a.N_max, j0, Pl, cm, tsel, t_cnt, rest - m_eff, sh);
+    if (t_cnt > 0) select_top_regs<MW>(a.s_target + (int64_t)(a.t_mod ? b % a.t_mod : b) * a.N_max, j0, Pl, cm, tsel, t_cnt, rest - m_eff, sh);
 
     // ascending compaction: one prefix count over the lanes' ranges
     int mine = 0;

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.dustin_abi_version() == 5
+    assert L.dustin_abi_version() == 6
     assert L.dustin_status_string(0) == b"DUSTIN_OK"
     assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
 
@@ -202,6 +202,36 @@ def test_page_estimator_argument_errors(L):
     assert f(scale=float("inf")) == INVALID
 
 
+def test_search_argument_errors(L):
+    I32 = ctypes.c_int32
+    ids_bad = (I32 * 2)(0, 5)
+    cand = lambda **k: L.dustin_candidate_arr(k.get("sd"), k.get("du"), k.get("st", FAKE), k.get("tu"), k.get("U", 4),
+                                              k.get("ids"), k.get("C", 2), k.get("mc"), FAKE, 2, 1024, k.get("abar", FAKE),
+                                              k.get("k", 64), 0, k.get("ns", 4), 32, FAKE, None, FAKE, 1 << 40, None)
+    assert cand(st=None) == INVALID                          # no score side at all
+    assert cand(du=FAKE, tu=FAKE) == INVALID                 # units on both sides
+    assert cand(abar=None) == INVALID
+    assert cand(k=0) == INVALID and cand(ns=64) == INVALID   # protected tokens exceed k
+    assert cand(tu=FAKE, ids=ids_bad, U=4) == INVALID        # unit id out of range
+    assert cand(tu=FAKE, U=1, C=2) == INVALID                # C > U without ids
+    assert cand(mc=(I32 * 2)(0, -1)) == INVALID              # negative per-candidate m
+    assert L.dustin_candidate_arr(None, None, FAKE, None, 0, None, 1, None, FAKE, 2, 1024, FAKE, 64, 0, 4, 32, FAKE,
+                                  None, FAKE, 0, None) == INVALID   # workspace too small
+    ch, cu, n = (I32 * 4)(), (ctypes.c_float * 4)(), I32(0)
+    g = lambda **k: L.dustin_greedy_select(k.get("units", FAKE), 4, None, 4, k.get("side", 0), k.get("fixed"), FAKE, 2,
+                                           1024, FAKE, 64, 10, 4, 32, 2, ch, cu, ctypes.byref(n), k.get("out", FAKE),
+                                           FAKE, 1 << 40, None)
+    assert g(side=2) == INVALID and g(units=None) == INVALID and g(out=None) == INVALID
+    assert g(side=1) == INVALID                              # the draft side needs the fixed S_Target
+    assert g(side=0, fixed=FAKE) == INVALID                  # the target side takes none
+    assert L.dustin_greedy_select_workspace_bytes(4, 2, 1024, 64) >= L.dustin_candidate_arr_workspace_bytes(4, 2, 1024, 64, 1)
+    heads = (I32 * 2)(0, 3)
+    assert L.dustin_head_scores(ctypes.byref(kv()), 1, FAKE, heads, 1, 64, 0.0, None, FAKE, 1 << 40, None) == INVALID
+    assert L.dustin_head_scores(ctypes.byref(kv()), 1, FAKE, heads, 0, 64, 0.0, FAKE, FAKE, 1 << 40, None) == INVALID
+    bad = (I32 * 2)(0, 64)
+    assert L.dustin_head_scores(ctypes.byref(kv()), 1, FAKE, bad, 1, 64, 0.0, FAKE, FAKE, 1 << 40, None) == INVALID
+
+
 def test_workspace_sizes_are_shape_only(L):
     # c4 shapes: the attention plan merges partials from several splits
     a = L.dustin_attn_workspace_bytes(16, 4, 64, 8, 128, 2048)
@@ -219,3 +249,15 @@ def test_valid_call_without_device_reports_hip_error(L):
     st = attn(L, desc)
     assert st == HIPERR
     assert L.dustin_last_error() != b""
+
+
+def test_binding_refuses_host_tensors():
+    """A host (CPU) tensor handed to a kernel would be dereferenced as a
+    device address; the binding refuses it before any call."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    lens = torch.full((2,), 8, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        dk.KV(torch.zeros((2, 8, 1, 32), dtype=torch.bfloat16), None, lens)
+    with pytest.raises(TypeError):
+        dk.dustin_window_mean(torch.zeros((2, 3, 8)))
