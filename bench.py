@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-window", action="store_true",
                    help="skip the verification-window step (append + causal verify attention + commit)")
     p.add_argument("--no-sweep", action="store_true", help="skip the policy sweep (ARR of the compared policies)")
+    p.add_argument("--no-search", action="store_true",
+                   help="skip the offline configuration search (SRH matrix, greedy target/draft, m search)")
     p.add_argument("--no-curve", action="store_true",
                    help="skip the estimator-overhead curve (dense, naive, Quest-16, Dustin-T/D/H over context length)")
     p.add_argument("--pmc-probe", action="store_true",
@@ -371,6 +373,8 @@ def main():
         res["policy_sweep"] = policy_sweep(args, sh, x, kvs[0], s_d, s_t, n_sink, n_window, timed)
     if not args.no_curve:
         res["estimator_curve"] = estimator_curve(args, sh, x, cap, timed)
+    if not args.no_search:
+        res["config_search"] = config_search(args, sh)
     if not args.no_window:
         # Last, because it writes the window rows into every layer's cache.
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
@@ -414,6 +418,121 @@ def policy_sweep(args, sh, x, kv, s_d, s_t, n_sink, n_window, timed):
         dt = time.perf_counter() - t0
         out["cpu_oracle_one_sequence_s"] = round(dt, 2)
         out["cpu_oracle_scaled_us"] = round(dt * sh.B * 1e6, 0)
+    return out
+
+
+SEARCH = dict(B=8, n=8192, k=512, T=64, S=8, max_draft=24)
+
+
+def config_search(args, sh):
+    """The offline configuration search (blog section 2.4, Fig. 6) on a
+    synthetic multi-layer profiling batch with the target's full depth
+    (sh.layers layers x H_q heads, every head a candidate) and the draft's
+    layers: per-layer window attention for the objective, per-head S_Target
+    rows, the SRH score matrix and its head TopK (T), greedy target heads
+    (at most S), greedy draft layers, and the m search.  Each phase is timed
+    with a device synchronisation around it (the greedy steps read their
+    objectives back every round)."""
+    import numpy as np
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+    P = SEARCH
+    ssh = sh.replace(B=P["B"], n=P["n"], L_d=sh.L_d)
+    k = P["k"]
+    n_sink, n_window, m0 = synth.tier_defaults(k)
+    ms = list(range(0, k - n_sink - n_window + 1, 8))
+    L, B, N, Hq = sh.layers, ssh.B, ssh.n, sh.Hq
+    t0 = time.perf_counter()
+    x = synth.make_search(ssh, L, device="cuda")
+    torch.cuda.synchronize()
+    log(f"config search: profiling batch generated in {time.perf_counter() - t0:.1f}s "
+        f"({L} target layers x {Hq} heads, {ssh.L_d} draft layers, B={B}, n={N}, k={k})")
+    dev = x.K.device
+    abar_l = torch.empty((L, B, N), dtype=torch.float32, device=dev)
+    units = torch.empty((L * Hq, B, N), dtype=torch.float32, device=dev)
+    d_units = torch.empty((ssh.L_d, B, N), dtype=torch.float32, device=dev)
+    heads = [(0, h) for h in range(Hq)]
+    kvs = [dk.KV(x.K[l], None, x.seq_lens, None) for l in range(L)]
+    dkvs = [dk.KV(x.Kd[l], None, x.seq_lens, None) for l in range(ssh.L_d)]
+    qd = [x.q_draft[:, l:l + 1].contiguous() for l in range(ssh.L_d)]
+    A = torch.empty((B, ssh.w, N), dtype=torch.float32, device=dev)
+    us = {}
+
+    def phase(name, fn):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        us[name] = round((time.perf_counter() - t) * 1e6, 1)
+        return out
+
+    def objective_rows():
+        for l in range(L):
+            dk.dustin_window_attn(x.q[l], kvs[l], A=A)
+            dk.dustin_window_mean(A, Abar=abar_l[l])
+        return dk.dustin_window_mean(abar_l.reshape(1, L, B * N)).reshape(B, N)
+
+    def head_rows():
+        for l in range(L):
+            dk.dustin_head_scores([kvs[l]], x.q_prev[l], heads, Hq, out=units[l * Hq:(l + 1) * Hq])
+
+    def draft_rows():
+        for l in range(ssh.L_d):
+            dk.dustin_score([dkvs[l]], qd[l], [dkvs[l]], None, None, Hq, s_draft=d_units[l], want_target=False)
+
+    for _ in range(2):                     # the second pass is timed (workspaces allocated, code loaded)
+        us = {}
+        abar = phase("objective_attention", objective_rows)
+        phase("head_rows", head_rows)
+        _, M = phase("srh_matrix", lambda: dk.dustin_candidate_arr(x.seq_lens, abar, k, 0, n_sink, n_window,
+                                                                     target_units=units))
+        nM = torch.full((1,), L * Hq, dtype=torch.int32, device=dev)
+        idx, cnt, _ = phase("srh_topk", lambda: dk.dustin_topk(None, M[None].contiguous(), nM, P["T"], 0, 0, 0,
+                                                               want_tier=False))
+        cand = [int(i) for i in idx[0, :int(cnt[0])].cpu()]
+        ch_t, curve_t, s_t = phase("greedy_target", lambda: dk.dustin_greedy_select(
+            units, x.seq_lens, abar, k, 0, n_sink, n_window, P["S"], 0, unit_ids=cand))
+        phase("draft_rows", draft_rows)
+        ch_d, curve_d, s_d = phase("greedy_draft", lambda: dk.dustin_greedy_select(
+            d_units, x.seq_lens, abar, k, m0, n_sink, n_window, P["max_draft"], 1, s_target_fixed=s_t))
+        vals = None
+        if ch_d:
+            _, vals = phase("m_search", lambda: dk.dustin_candidate_arr(x.seq_lens, abar, k, 0, n_sink, n_window,
+                                                                        s_draft=s_d, s_target=s_t, m_cand=ms))
+    us["total"] = round(sum(us.values()), 1)
+    vals = None if vals is None else vals.cpu().numpy()
+    m_best = ms[int(np.argmax(vals))] if vals is not None else 0
+    rho = x.rho.numpy()
+    target_heads = [(cand[c] // Hq, cand[c] % Hq) for c in ch_t]
+    out = {
+        "workload": f"{L} target layers x {Hq} heads (head_dim {sh.d}), {ssh.L_d} draft layers x {ssh.H_d} heads, "
+                    f"profiling batch B={B}, n={N}, k={k}, T={P['T']}, S<={P['S']}, w={ssh.w}",
+        "us": us,
+        "srh_matrix_rho_corr": round(float(np.corrcoef(M.cpu().numpy(), rho.ravel())[0, 1]), 3),
+        "target_heads": target_heads, "target_curve": [round(v, 4) for v in curve_t],
+        "draft_layers": ch_d, "draft_curve": [round(v, 4) for v in curve_d],
+        "m": m_best, "objective": round(float(vals.max()), 4) if vals is not None else None,
+    }
+    log(f"config search {us['total'] / 1e3:.1f} ms ({', '.join(f'{kk} {v / 1e3:.2f}' for kk, v in us.items() if kk != 'total')} ms); "
+        f"heads {target_heads} curve {out['target_curve']}; draft {ch_d} curve {out['draft_curve']}; m {m_best}, "
+        f"objective {out['objective']}")
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+        t = time.perf_counter()
+        Ao = [[oracle.window_attention(f(x.q[l, 0]), f(x.K[l, 0])) for l in range(L)]]
+        hp = np.stack([oracle.head_probs(f(x.q_prev[l, 0])[None], f(x.K[l, 0]))[:, 0] for l in range(L)])[None]
+        du = np.stack([oracle.score_draft(f(x.q_draft[0, l:l + 1]), f(x.Kd[l:l + 1, 0]))[None]
+                       for l in range(ssh.L_d)])
+        oracle.config_search(Ao, hp, du, k, m0, ms, n_sink, n_window, P["T"], P["S"], P["max_draft"])
+        dt = time.perf_counter() - t
+        out["cpu_oracle_one_sequence_s"] = round(dt, 1)
+        out["cpu_oracle_note"] = "the same search on sequence 0 alone (B = 1), fp64 NumPy"
+        log(f"config search: oracle on one sequence {dt:.1f}s")
+    del x, units, d_units, abar_l, kvs, dkvs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return out
 
 
