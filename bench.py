@@ -62,7 +62,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_c4_k2048_traffic.txt")
 TRAFFIC_SOURCES = ["sparse_kv_verification_amd/csrc/attn.hip", "sparse_kv_verification_amd/csrc/common.h",
-                   "sparse_kv_verification_amd/csrc/internal.h"]
+                   "sparse_kv_verification_amd/csrc/attn.h"]
 
 
 def attn_source_digest():

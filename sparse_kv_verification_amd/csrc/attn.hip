@@ -28,8 +28,8 @@
 // A float32 variant (plain VALU arithmetic, 256 lanes per work-group) serves
 // float32 caches with the same split/merge scheme.
 
+#include "attn.h"
 #include "common.h"
-#include "internal.h"
 
 namespace dustin {
 
