@@ -112,6 +112,8 @@ struct WindowLayout {
     size_t off_out, off_lse, bytes;
 };
 
+size_t window_steps_offset() { return align_up((size_t)kAttnCounterSlots * sizeof(int32_t), 256); }
+
 WindowLayout window_layout(int B, int w, int H_q, int H_kv, int D, int N_max, int esz) {
     WindowLayout L{};
     L.plan = attn_plan(B, w, H_q, H_kv, D, N_max, false);
@@ -120,8 +122,19 @@ WindowLayout window_layout(int B, int w, int H_q, int H_kv, int D, int N_max, in
     off = align_up(off + (size_t)B * w * H_q * D * esz, 256);
     L.off_lse = off;
     off = align_up(off + (size_t)B * w * H_q * sizeof(float), 256);
-    L.bytes = off;
+    // the statistics path (window_steps) needs the draft-side scoring
+    // workspace, placed after the arrival-counter region so that region stays
+    // zero for the attention calls that share the workspace
+    const size_t steps = window_steps_offset() + score_plan(B, N_max, 1, H_q, w, 0, H_kv).ws_bytes;
+    L.bytes = off > steps ? off : steps;
     return L;
+}
+
+// The window attention through the statistics passes (one K read for the
+// row normalisers, one for the probabilities, both on MFMA): bfloat16, at
+// most 4 window steps and 64 rows per KV head.
+bool window_steps_apply(const dustin_kv *kv, int w, int H_q) {
+    return kv->dtype == DUSTIN_BF16 && w <= 4 && (int64_t)w * (H_q / kv->H_kv) <= 64;
 }
 
 }  // namespace
@@ -304,6 +317,26 @@ dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q, const du
     CHECK(ws != nullptr && ws_bytes >= L.bytes, DUSTIN_ERR_INVALID_ARG,
           "window_attn: workspace of %zu bytes needed (got %zu)", L.bytes, ws_bytes);
     char *wsb = (char *)ws;
+    if (window_steps_apply(kv, w, H_q)) {
+        DraftScoreArgs da{};
+        da.kv[0] = view_of(kv);
+        da.L_d = 1;
+        da.H_d = H_q;
+        da.gamma = w;
+        da.Hkv_d = kv->H_kv;
+        da.G_d = H_q / kv->H_kv;
+        da.rows = w * da.G_d;
+        da.q_draft = q;
+        da.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
+        const ScorePlan sp = score_plan(kv->B, kv->N_max, 1, H_q, w, 0, kv->H_kv);
+        char *sws = wsb + window_steps_offset();
+        da.stat = (float *)(sws + sp.off_dstat);
+        da.lse = (float *)(sws + sp.off_dlse);
+        da.nchunk = sp.nchunk;
+        da.steps_out = A;
+        da.steps_scale = 1.f / (float)H_q;
+        return hip_status(launch_window_steps(da, (hipStream_t)stream), "window_attn launch");
+    }
     AttnArgs a{};
     a.kv = view_of(kv);
     a.kv.v = a.kv.k;

@@ -57,9 +57,14 @@ struct DraftScoreArgs {
     float *stat;                    // ws
     float *lse;                     // ws
     int32_t nchunk;
+    float *steps_out;               // window form: [B][gamma][N_max] per-step sums times steps_scale
+    float steps_scale;
 };
 
 hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s);
+// Window attention A (Eq. 1) of one layer through the draft passes: bf16,
+// gamma <= 4 window steps, gamma * G <= 64 rows; steps_out / steps_scale set.
+hipError_t launch_window_steps(const DraftScoreArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- select
 struct TopkPlan {

@@ -485,9 +485,15 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
 // chunk); each wave owns 64 positions and loops over every draft unit in a
 // fixed order, the next unit's operands in flight, so S_Draft is summed in
 // registers without atomics.
+//
+// W > 0 is the per-step form used for the window attention A of Eq. (1)
+// (one layer, the window queries as the "draft" rows, which are step-major
+// within a unit): instead of one sum over all rows, lane sums are kept per
+// step (step = row / G_d, at most W steps) and written, times steps_scale
+// (1 / H_q: the head mean), to steps_out [B][gamma][N_max].
 constexpr int kDraftAccChunk = 256;
 
-template <int D, int RB, bool PAGED>
+template <int D, int RB, bool PAGED, int W = 0>
 __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     constexpr int KK = M::KK;
@@ -509,12 +515,27 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         const int rr = qok[rb] ? r : 0;
         qoff[rb] = ((rr / a.G_d) * a.H_d + (rr - (rr / a.G_d) * a.G_d)) * D + (lane >> 4) * 8;
     }
+    // step of each of this lane's result rows (rows past the last are masked
+    // by an infinite normaliser; their step is clamped)
+    int rstep[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb * 16 + (lane >> 4) * 4 + i;
+            rstep[rb][i] = W > 0 ? min(r / a.G_d, W - 1) : 0;
+        }
+    constexpr int NS = W > 0 ? W : 1;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int c = it % nch, b = it / nch;
         const int jb = c * kDraftAccChunk + wave * 64;
         const int nb = sl_len(k0, b);
         const float *lse_b = a.lse + (int64_t)b * U * a.rows;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float acc[4][NS];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int q = 0; q < NS; ++q) acc[st][q] = 0.f;
         // byte offset of this lane's K row in a layer, per subtile (positions
         // past n_b read row 0 of the sequence and are masked)
         int64_t koff[4];
@@ -570,7 +591,9 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
             if (u >= U) return;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {   // one subtile's logits live at a time
-                float t = 0.f;
+                float t[NS];
+#pragma unroll
+                for (int q2 = 0; q2 < NS; ++q2) t[q2] = 0.f;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -578,9 +601,20 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
                     for (int kk = 0; kk < KK; ++kk)
                         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[rb][kk], k[st][kk], sc, 0, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) t += __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
+                        if constexpr (W > 0) {
+#pragma unroll
+                            for (int q2 = 0; q2 < NS; ++q2) t[q2] += (rstep[rb][i] == q2) ? e : 0.f;
+                        } else {
+                            t[0] += e;
+                        }
+                    }
                 }
-                if (jb + st * 16 + (lane & 15) < nb) acc[st] += t;
+                if (jb + st * 16 + (lane & 15) < nb) {
+#pragma unroll
+                    for (int q2 = 0; q2 < NS; ++q2) acc[st][q2] += t[q2];
+                }
             }
         };
         load_k(0, kA);
@@ -591,9 +625,18 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const float v = group4_sum(acc[st]);
             const int j = jb + st * 16 + (lane & 15);
-            if (lane < 16 && j < N) a.s_draft[(int64_t)b * N + j] = v;
+            if constexpr (W > 0) {
+#pragma unroll
+                for (int q2 = 0; q2 < NS; ++q2) {
+                    const float v = group4_sum(acc[st][q2]);
+                    if (lane < 16 && j < N && q2 < a.gamma)
+                        a.steps_out[((int64_t)b * a.gamma + q2) * N + j] = v * a.steps_scale;
+                }
+            } else {
+                const float v = group4_sum(acc[st][0]);
+                if (lane < 16 && j < N) a.s_draft[(int64_t)b * N + j] = v;
+            }
         }
     }
 }
@@ -1149,6 +1192,49 @@ static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     if (k0.page_size != 0) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true>), grid, dim3(256), 0, s, b);
     else hipLaunchKernelGGL((draft_acc_mfma<D, RB, false>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
+}
+
+// Window attention A of Eq. (1) through the draft machinery: statistics pass,
+// row normalisers, then the per-step accumulation (a.gamma <= 4 steps).
+template <int D, int RB>
+static hipError_t window_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
+    const KvView &k0 = a.kv[0];
+    const int U = a.L_d * a.Hkv_d;
+    DraftScoreArgs b = a;
+    b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
+    const int stat_items = k0.B * U * b.nchunk;
+    hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(stat_items < kScoreGroups ? stat_items : kScoreGroups),
+                       dim3(256), 0, s, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nrows = k0.B * U * a.rows;
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
+    const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
+    if (k0.page_size != 0) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true, 4>), grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((draft_acc_mfma<D, RB, false, 4>), grid, dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_steps(const DraftScoreArgs &a, hipStream_t s) {
+    const int RB = (a.rows + 15) / 16;
+    if (a.kv[0].f32 || a.gamma > 4 || RB > 4) return hipErrorInvalidValue;
+#define DUSTIN_WINDOW_CASE(DD)                                 \
+    switch (RB) {                                              \
+        case 1: return window_bf16_impl<DD, 1>(a, s);          \
+        case 2: return window_bf16_impl<DD, 2>(a, s);          \
+        case 3: return window_bf16_impl<DD, 3>(a, s);          \
+        case 4: return window_bf16_impl<DD, 4>(a, s);          \
+    }                                                          \
+    return hipErrorInvalidValue;
+    switch (a.kv[0].D) {
+        case 32: DUSTIN_WINDOW_CASE(32)
+        case 64: DUSTIN_WINDOW_CASE(64)
+        case 128: DUSTIN_WINDOW_CASE(128)
+    }
+#undef DUSTIN_WINDOW_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s) {

@@ -224,8 +224,11 @@ def test_scores_match_oracle(name, over):
 
 
 @pytest.mark.parametrize("name,over", [
-    ("qwen72b", dict(base="c4", B=2, n=3000, L_d=1)),
-    ("paged", dict(base="c5", B=2, n=2000, n_lo=800, L_d=1)),
+    ("qwen72b", dict(base="c4", B=2, n=3000, L_d=1)),                       # 32 rows per KV head
+    ("qwen7b-rows28", dict(base="c2", B=2, n=2600, n_lo=900, L_d=1)),        # 7 rows per step
+    ("d64-one-step", dict(base="c4", B=2, n=2100, Hq=8, Hkv=2, d=64, w=1, L_d=1)),
+    ("paged-one-step", dict(base="c5", B=2, n=2000, n_lo=800, w=1, L_d=1)),
+    ("paged", dict(base="c5", B=2, n=2000, n_lo=800, L_d=1)),                # w = 8: the dense-pass form
     ("tiny-f32", dict(base="c1")),
 ])
 def test_window_attention_and_arr(name, over):
@@ -255,3 +258,28 @@ def test_window_attention_and_arr(name, over):
         sel, arr_orc, Abar_ref = oracle.sd_oracle(Aref, 64)
         g = oi[b, :int(oc[b])].cpu().numpy()
         assert abs(Abar_ref[g].sum() - arr_orc) < 1e-5
+
+
+def test_window_attention_paths_share_a_workspace():
+    """The statistics form (bf16, w <= 4) and the dense-pass form (w = 8, or
+    float32) of the window attention run on one workspace in both orders;
+    the statistics form must leave the attention arrival counters at the
+    workspace's start untouched (zero)."""
+    say("window attention: both forms on one workspace")
+    ws = dk.Workspace()
+    buf = ws.get(1 << 28, torch.device("cuda", torch.cuda.current_device()))   # large enough for all three calls
+    ptr = buf.data_ptr()
+    for base, over in (("c4", dict(B=2, n=1500, L_d=1)), ("c5", dict(B=2, n=1500, n_lo=700, L_d=1)),
+                       ("c4", dict(B=2, n=1500, L_d=1, seed=9))):
+        sh = synth.preset(base).replace(**over)
+        x = synth.make(sh, device=DEV)
+        kv = dk.KV(x.K, None, x.seq_lens, x.page_table)
+        A = dk.dustin_window_attn(x.q, kv, ws=ws)
+        torch.cuda.synchronize()
+        b = 0
+        n = int(x.seq_lens[b])
+        Aref = oracle.window_attention(f64(x.q[b]), oracle_kv(x, "K", b))
+        err = np.abs(f64(A[b, :, :n]) - Aref).max()
+        say(f"  {base} w={sh.w}: max|dA|={err:.2e}")
+        assert err < 1e-5
+        assert ws.buf.data_ptr() == ptr              # the same (never re-zeroed) buffer throughout
