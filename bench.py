@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--no-window", action="store_true",
                    help="skip the verification-window step (append + causal verify attention + commit)")
     p.add_argument("--no-sweep", action="store_true", help="skip the policy sweep (ARR of the compared policies)")
+    p.add_argument("--no-ksweep", action="store_true", help="skip the step at the other budgets k (512, 1024)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the one-layer steps of the other workloads (tiny f32, 7B, 32B, ragged paged)")
     p.add_argument("--no-search", action="store_true",
                    help="skip the offline configuration search (SRH matrix, greedy target/draft, m search)")
     p.add_argument("--no-curve", action="store_true",
@@ -149,8 +152,33 @@ def cpu_baseline(sh, x, k, m, n_sink, n_window, budget_s=20.0):
         info = threadpoolctl.threadpool_info()
         threads = max((i.get("num_threads", 1) for i in info), default=1)
     except Exception:
+        threadpoolctl = None
         threads = os.cpu_count()
     measured = sum(total.values())
+    # sequence 0: score + select + one attention layer with all threads and with one thread, and one
+    # dense (full-cache) layer, stated x layers as an extrapolation
+    n = int(x.seq_lens[0])
+    K, V, Kd = f(x.logical("K", 0)), f(x.logical("V", 0)), f(x.logical("Kd", 0))
+    qd, qh, q = f(x.q_draft[0]), f(x.q_hist[0]), f(x.q[0])
+
+    def one_layer():
+        sd = oracle.score_draft(qd, Kd)
+        st = oracle.score_target(qh, {0: K}, x.sub_heads, sh.Hq)
+        I, _ = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
+        oracle.sparse_attention(q, K, V, I)
+
+    t0 = time.perf_counter()
+    one_layer()
+    t_all = time.perf_counter() - t0
+    t_one = None
+    if threadpoolctl is not None:
+        with threadpoolctl.threadpool_limits(1):
+            t0 = time.perf_counter()
+            one_layer()
+            t_one = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.dense_attention(q, K, V)
+    t_dense = time.perf_counter() - t0
     return {
         "value": measured / done * sh.B * 1e6,
         "unit": "us/step",
@@ -161,6 +189,10 @@ def cpu_baseline(sh, x, k, m, n_sink, n_window, budget_s=20.0):
         "measured_s": {a: round(b, 3) for a, b in total.items()},
         "host_cpu": platform.processor() or platform.machine(),
         "host_cpu_count": os.cpu_count(),
+        "one_sequence_one_layer_s": {"all_threads": round(t_all, 3), "threads": int(threads or 1),
+                                     "one_thread": None if t_one is None else round(t_one, 3)},
+        "dense_layer_one_sequence_s": round(t_dense, 3),
+        "dense_step_extrapolated_s": round(t_dense * sh.layers * sh.B, 1),
     }
 
 
@@ -271,6 +303,28 @@ def main():
         graph_us = timed(g.replay, args.steps)
         log(f"graph step {graph_us:.1f} us")
     step_us = graph_us if graph_us is not None else eager_us
+    # per-step distribution: one event pair around each replay (or eager step)
+    pairs = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        (g.replay if graph_us is not None else step)()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = sorted(a_.elapsed_time(b_) * 1e3 for a_, b_ in pairs)
+    pick = lambda q: ts[min(len(ts) - 1, int(round(q * (len(ts) - 1))))]
+    step_pct = {"p10": round(pick(0.1), 1), "p50": round(pick(0.5), 1), "p90": round(pick(0.9), 1)}
+    log(f"step distribution over {len(ts)} single-step timings: p10 {step_pct['p10']} p50 {step_pct['p50']} "
+        f"p90 {step_pct['p90']} us")
+    # a device-to-device copy of 1 GiB (read + write) as the measured bandwidth reference
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    copy_us = timed(lambda: cdst.copy_(csrc), 5)
+    copy_gbps = 2 * csrc.numel() * 4 / copy_us / 1e3
+    del csrc, cdst
+    log(f"device copy of 1 GiB: {copy_us:.0f} us, {copy_gbps:.0f} GB/s (read + write)")
 
     # component timings (eager, events on the launch stream)
     score_us = timed(score, args.steps)
@@ -346,6 +400,9 @@ def main():
         },
         "step_GBps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_us_distribution": step_pct,
+        "d2d_copy_GBps": round(copy_gbps, 1),
+        "step_frac_of_d2d_copy": round(step_gbps / copy_gbps, 4),
         "step_algorithmic_bytes": bytes_["step"],
         "eager_us_per_step": round(eager_us, 2),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
@@ -371,13 +428,17 @@ def main():
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
     if not args.no_sweep:
         res["policy_sweep"] = policy_sweep(args, sh, x, kvs[0], s_d, s_t, n_sink, n_window, timed)
+    if not args.no_ksweep:
+        res["k_sweep"] = k_sweep(args, sh, x, kvs, dkv, s_d, s_t, cap, timed)
     if not args.no_curve:
         res["estimator_curve"] = estimator_curve(args, sh, x, cap, timed)
     if not args.no_search:
         res["config_search"] = config_search(args, sh)
     if not args.no_window:
-        # Last, because it writes the window rows into every layer's cache.
+        # Last of the c4 legs, because it writes the window rows into every layer's cache.
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
+    if not args.no_configs:
+        res["other_configs"] = other_configs(args, cap, timed)
     print(json.dumps(res), flush=True)
 
 
@@ -418,6 +479,93 @@ def policy_sweep(args, sh, x, kv, s_d, s_t, n_sink, n_window, timed):
         dt = time.perf_counter() - t0
         out["cpu_oracle_one_sequence_s"] = round(dt, 2)
         out["cpu_oracle_scaled_us"] = round(dt * sh.B * 1e6, 0)
+    return out
+
+
+def graph_time(args, fn, cap, timed, reps):
+    """HIP-graph replay time of fn (eager with --no-graph)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    if args.no_graph:
+        return timed(fn, reps)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr, stream=cap):
+            fn()
+    torch.cuda.synchronize()
+    gr.replay()
+    return timed(gr.replay, reps)
+
+
+def k_sweep(args, sh, x, kvs, dkv, s_d, s_t, cap, timed):
+    """The same 80-layer step at the other budgets of the 72B workload."""
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+    out = {}
+    ws_s, ws_k, ws_a = dk.Workspace(), dk.Workspace(), dk.Workspace()
+    for kk in sh.k_sweep:
+        if kk == sh.k:
+            continue
+        ns, nw, mm = synth.tier_defaults(kk)
+        idx = torch.empty((sh.B, kk), dtype=torch.int32, device=x.q.device)
+        cnt = torch.empty((sh.B,), dtype=torch.int32, device=x.q.device)
+        o = torch.empty_like(x.q)
+
+        def step():
+            dk.dustin_score(dkv, x.q_draft, [kvs[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
+            dk.dustin_topk(s_d, s_t, x.seq_lens, kk, mm, ns, nw, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+            for l in range(sh.layers):
+                dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=o, ws=ws_a)
+
+        us = graph_time(args, step, cap, timed, max(2, args.steps // 4))
+        by = algorithmic_bytes(sh, x, kk, cnt, x.sub_heads)["step"]
+        out[str(kk)] = {"us_per_step": round(us, 1), "GBps": round(by / us / 1e3, 1),
+                        "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by}
+        log(f"k={kk}: step {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+    return out
+
+
+def other_configs(args, cap, timed):
+    """One-layer steps (score, select, one attention layer) of the other
+    workloads: tiny float32, 7B-shaped 16k, 32B-shaped 32k, ragged paged."""
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+    out = {}
+    for name in ("c1", "c2", "c3", "c5"):
+        sh = synth.preset(name).replace(layers=1)
+        x = synth.make(sh, device="cuda")
+        k = sh.k
+        ns, nw, mm = synth.tier_defaults(k)
+        kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
+        dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
+        N = kv.desc.N_max
+        s_d = torch.empty((sh.B, N), dtype=torch.float32, device="cuda")
+        s_t = torch.empty_like(s_d)
+        idx = torch.empty((sh.B, k), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((sh.B,), dtype=torch.int32, device="cuda")
+        o = torch.empty_like(x.q)
+        ws_s, ws_k, ws_a = dk.Workspace(), dk.Workspace(), dk.Workspace()
+
+        def step():
+            dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
+            dk.dustin_topk(s_d, s_t, x.seq_lens, k, mm, ns, nw, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+            dk.dustin_sparse_verify_attn(x.q, kv, idx, cnt, out=o, ws=ws_a)
+
+        us = graph_time(args, step, cap, timed, max(3, args.steps // 2))
+        by = algorithmic_bytes(sh, x, k, cnt, x.sub_heads)["step"]
+        out[name] = {"workload": f"{sh.name}: B={sh.B} n={sh.n}{' (ragged, paged)' if sh.n_lo else ''} "
+                                 f"Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d} w={sh.w} k={k} {sh.dtype}, one layer",
+                     "us_per_step": round(us, 1), "GBps": round(by / us / 1e3, 1),
+                     "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by}
+        log(f"{name}: one-layer step {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+        del x, kv, dkv, s_d, s_t
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return out
 
 

@@ -125,7 +125,7 @@ typedef struct dustin_kv {
  * target's most recent query (history distance 1, translation section 3.2).
  *
  *  draft_layers   host [L_d] descriptors (k used; same B, N_max, H_kv,
- *                 head_dim, dtype, paging for all layers)
+ *                 head_dim, dtype, paging for all layers); B <= 1024
  *  q_draft        [B][L_d][gamma][H_d][d_draft], draft dtype
  *  target_layers  host [L_t] descriptors (k used; same B, N_max as draft)
  *  q_hist         [B][S][d_target], target dtype

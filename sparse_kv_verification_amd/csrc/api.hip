@@ -134,7 +134,7 @@ WindowLayout window_layout(int B, int w, int H_q, int H_kv, int D, int N_max, in
 // row normalisers, one for the probabilities, both on MFMA): bfloat16, at
 // most 4 window steps and 64 rows per KV head.
 bool window_steps_apply(const dustin_kv *kv, int w, int H_q) {
-    return kv->dtype == DUSTIN_BF16 && w <= 4 && (int64_t)w * (H_q / kv->H_kv) <= 64;
+    return kv->dtype == DUSTIN_BF16 && w <= 4 && (int64_t)w * (H_q / kv->H_kv) <= 64 && kv->B <= kMaxDraftBatch;
 }
 
 }  // namespace
@@ -441,6 +441,8 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
     if (do_draft) {
         CHECK(draft_layers != nullptr, DUSTIN_ERR_INVALID_ARG, "score: draft_layers is NULL");
         CHECK(L_d <= kMaxDraftLayers, DUSTIN_ERR_UNSUPPORTED, "score: L_d %d exceeds %d", L_d, kMaxDraftLayers);
+        CHECK(draft_layers[0].B <= kMaxDraftBatch, DUSTIN_ERR_UNSUPPORTED, "score: B %d exceeds %d on the draft side",
+              draft_layers[0].B, kMaxDraftBatch);
         for (int l = 0; l < L_d; ++l) {
             dustin_status st = check_kv(&draft_layers[l], "score draft layer", false);
             if (st != DUSTIN_OK) return st;

@@ -17,6 +17,7 @@ hipError_t launch_commit_window(int32_t *seq_lens, const int32_t *accepted, int 
 constexpr int kScoreChunk = 256;    // positions per scoring work-group
 constexpr int kMaxScoreRows = 64;   // scored target rows
 constexpr int kMaxDraftLayers = 32;
+constexpr int kMaxDraftBatch = 1024;  // sequences per call on the draft side
 constexpr int kMaxScoreQoff = 256;   // rows of the float32 draft path
 
 struct ScorePlan {

@@ -169,18 +169,23 @@ __global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, N
 }
 
 // Row log-sum-exp (log2 domain) from the per-chunk statistics.
-// One wave per row.
-__global__ __launch_bounds__(256) void rows_lse(const float *stat, float *lse, int nrows_total, int nchunk) {
+// One wave per row; rows are sequence-major (rows_per_b rows per sequence)
+// and only the chunks holding positions below n_b are read (the statistics
+// passes may leave the others unwritten).
+__global__ __launch_bounds__(256) void rows_lse(const float *stat, float *lse, int nrows_total, int nchunk,
+                                                const int32_t *seq_lens, int rows_per_b, int chunk, int N_max) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nrows_total) return;
+    const int nb = min(max(seq_lens[row / rows_per_b], 0), N_max);
+    const int nv = min(nchunk, (nb + chunk - 1) / chunk);
     const float *st = stat + (int64_t)row * nchunk * 2;
     float mx = kNegInf;
-    for (int c = lane; c < nchunk; c += 64) mx = fmaxf(mx, st[2 * c]);
+    for (int c = lane; c < nv; c += 64) mx = fmaxf(mx, st[2 * c]);
     mx = wave_max(mx);
     const float muse = (mx == kNegInf) ? 0.f : mx;
     float z = 0.f;
-    for (int c = lane; c < nchunk; c += 64) z += st[2 * c + 1] * exp2f(st[2 * c] - muse);
+    for (int c = lane; c < nv; c += 64) z += st[2 * c + 1] * exp2f(st[2 * c] - muse);
     z = wave_sum(z);
     if (lane == 0) lse[row] = (z > 0.f) ? muse + __log2f(z) : __builtin_huge_valf();
 }
@@ -364,23 +369,47 @@ struct DraftMfma {
 // work-group's next item are requested during the last group of the
 // current one, so the stream does not stall between items.
 constexpr int kDraftStatChunk = 4096;
+constexpr int kDraftStatMaxB = kMaxDraftBatch;   // sequences per call of the statistics pass
 
 template <int D, int RB>
 __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     __shared__ float red[4][RB * 16][2];
+    __shared__ int pref[kDraftStatMaxB + 1];  // chunks below n_b of sequences before b
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int U = a.L_d * a.Hkv_d;
     const int nch = a.nchunk;                 // kDraftStatChunk-position chunks
-    const int items = a.kv[0].B * U * nch;
+    const int B = a.kv[0].B;
     constexpr int NG = kDraftStatChunk / 4 / 64;   // 64-position groups per wave
     static_assert(NG % 2 == 0, "groups are folded in pairs");
+    // Items are (b, u, c) over the chunks that hold positions below n_b only
+    // (a ragged batch skips the rest), numbered sequence by sequence: the
+    // prefix of per-sequence chunk counts is built in LDS (B <= 1024, checked
+    // by the launcher).
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
+        pref[bb + 1] = (sl_len(a.kv[0], bb) + kDraftStatChunk - 1) / kDraftStatChunk;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        pref[0] = 0;
+        for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
+    }
+    __syncthreads();
+    const int items = U * pref[B];
     struct Item { int b, u, c, l, kvh, nb, jw; };
     auto decode = [&](int it) {
         Item x;
-        x.c = it % nch;
-        x.u = (it / nch) % U;
-        x.b = it / (nch * U);
+        const int cu = it / U;                // chunk index over all sequences
+        int lo = 0, hi = B - 1;               // the b with pref[b] <= cu < pref[b + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pref[mid] <= cu) lo = mid;
+            else hi = mid - 1;
+        }
+        x.b = lo;
+        const int nbc = pref[lo + 1] - pref[lo];
+        const int r = it - U * pref[lo];      // within the sequence: u-major
+        x.u = r / nbc;
+        x.c = r - x.u * nbc;
         x.l = x.u / a.Hkv_d;
         x.kvh = x.u - x.l * a.Hkv_d;
         x.nb = sl_len(a.kv[x.l], x.b);
@@ -530,6 +559,17 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         const int c = it % nch, b = it / nch;
         const int jb = c * kDraftAccChunk + wave * 64;
         const int nb = sl_len(k0, b);
+        if (jb >= nb) {   // this wave's positions are all past the sequence: zeros, no work
+            const int j = jb + lane;
+            if (j < N) {
+                if constexpr (W > 0) {
+                    for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)b * a.gamma + q2) * N + j] = 0.f;
+                } else {
+                    a.s_draft[(int64_t)b * N + j] = 0.f;
+                }
+            }
+            continue;
+        }
         const float *lse_b = a.lse + (int64_t)b * U * a.rows;
         float acc[4][NS];
 #pragma unroll
@@ -1064,7 +1104,8 @@ static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
     hipError_t e = run_unit_stats(p, k0.B, s);
     if (e != hipSuccess) return e;
     float *lse = a.lse;
-    hipLaunchKernelGGL(rows_lse, dim3((k0.B * a.S + 3) / 4), dim3(256), 0, s, a.stat, lse, k0.B * a.S, a.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((k0.B * a.S + 3) / 4), dim3(256), 0, s, a.stat, lse, k0.B * a.S, a.nchunk,
+                       k0.seq_lens, a.S, CH, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.rows_out) {
         hipLaunchKernelGGL(target_rows_finalize, dim3((k0.N_max + 255) / 256, k0.B, a.S), dim3(256), 0, s, a.logit,
@@ -1132,7 +1173,8 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
     p.N_max = k0.N_max;
     hipError_t e = run_unit_stats(p, k0.B, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rows_lse, dim3((k0.B * row + 3) / 4), dim3(256), 0, s, a.stat, a.lse, k0.B * row, a.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((k0.B * row + 3) / 4), dim3(256), 0, s, a.stat, a.lse, k0.B * row, a.nchunk,
+                       k0.seq_lens, row, CH, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     DraftValuAccParams<D, 8> q{};
     for (int i = 0; i < a.L_d; ++i) q.kv[i] = a.kv[i];
@@ -1162,7 +1204,8 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrows = k0.B * a.L_d * 2 * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
+                       a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int acc_items = k0.B * ((k0.N_max + 1023) / 1024);
     hipLaunchKernelGGL((draft_acc_stream<RB>), dim3(acc_items < kStreamGroups ? acc_items : kStreamGroups),
@@ -1185,7 +1228,8 @@ static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrows = k0.B * U * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
+                       U * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
     const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
@@ -1208,7 +1252,8 @@ static hipError_t window_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrows = k0.B * U * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk);
+    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
+                       U * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
     const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
