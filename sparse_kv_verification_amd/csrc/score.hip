@@ -346,6 +346,27 @@ struct DraftMfma {
         }
     }
 
+    // The same for a paged cache whose four page ids (one per 16-position
+    // subtile, uniform across the wave) are already in registers: no
+    // page-table load on the way to the K rows.
+    static __device__ __forceinline__ void load_k_pg(const KvView &kv, const int (&pg)[4], int c, int j_base, int nb,
+                                                     int lane, bf16x8 (&kf)[4][KK]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int j = j_base + st * 16 + (lane & 15);
+            const bool ok = j < nb && pg[st] >= 0 && pg[st] < kv.num_pages;
+            const char *row = kv.k + ((((int64_t)(ok ? pg[st] : 0) * 16 + (j & 15)) * kv.Hkv + c) * D) * 2;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                if (ok) {
+                    kf[st][kk] = *(const bf16x8 *)(row + (kk * 32 + (lane >> 4) * 8) * 2);
+                } else {
+                    for (int i = 0; i < 8; ++i) kf[st][kk][i] = (__bf16)0.f;
+                }
+            }
+        }
+    }
+
     static __device__ __forceinline__ void logits(const bf16x8 (&qf)[RB][KK], const bf16x8 (&kf)[4][KK],
                                                   f32x4 (&s)[4][RB]) {
 #pragma unroll
@@ -372,7 +393,7 @@ constexpr int kDraftStatChunk = 4096;
 constexpr int kDraftStatMaxB = kMaxDraftBatch;   // sequences per call of the statistics pass
 
 template <int D, int RB>
-__global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
+__global__ __launch_bounds__(256, RB >= 3 ? 1 : 2) void draft_stats_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     __shared__ float red[4][RB * 16][2];
     __shared__ int pref[kDraftStatMaxB + 1];  // chunks below n_b of sequences before b
@@ -418,16 +439,39 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
     };
     int it = blockIdx.x;
     if (it >= items) return;
+    // Paged caches: lane t holds the page id of the wave's t-th 16-position
+    // page (a wave spans kDraftStatChunk / 4 = 1024 positions = 64 pages), so
+    // the K loads of a group need no page-table load first; the next item's
+    // ids are loaded when the current item starts.
+    const bool paged = a.kv[0].page_size != 0;
+    auto load_pg = [&](const Item &x) -> int {
+        if (!paged) return 0;
+        const KvView &kv = a.kv[x.l];
+        const int pgi = (x.jw >> 4) + lane;
+        return pgi < kv.max_pages ? kv.page_table[(int64_t)x.b * kv.max_pages + pgi] : -1;
+    };
+    auto load_kg = [&](const Item &x, int pgl, int gi, bf16x8 (&k)[4][M::KK]) {
+        const int jbase = x.jw + gi * 64;
+        if (paged) {
+            int pg[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) pg[st] = __builtin_amdgcn_readlane(pgl, gi * 4 + st);
+            M::load_k_pg(a.kv[x.l], pg, x.kvh, jbase, x.nb, lane, k);
+        } else {
+            M::load_k(a.kv[x.l], x.b, x.kvh, jbase, x.nb, lane, k);
+        }
+    };
     // two named operand sets keep the double buffer in registers
     bf16x8 qf[RB][M::KK], qn[RB][M::KK];
     bf16x8 kA[4][M::KK], kB[4][M::KK];
     Item cur = decode(it);
+    int pg_cur = load_pg(cur);
     M::load_q(a, cur.b, cur.l, cur.kvh, lane, qf);
-    M::load_k(a.kv[cur.l], cur.b, cur.kvh, cur.jw, cur.nb, lane, kA);
+    load_kg(cur, pg_cur, 0, kA);
     for (; it < items; it += gridDim.x) {
         const int nxt_it = it + gridDim.x;
         const Item nxt = decode(nxt_it < items ? nxt_it : it);
-        const KvView &kv = a.kv[cur.l];
+        const int pg_nxt = load_pg(nxt);
         float mrun[RB][4], zrun[RB][4];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -463,13 +507,13 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
         };
 #pragma unroll 1
         for (int gi = 0; gi < NG; gi += 2) {
-            M::load_k(kv, cur.b, cur.kvh, cur.jw + (gi + 1) * 64, cur.nb, lane, kB);
+            load_kg(cur, pg_cur, gi + 1, kB);
             fold(gi, kA);
             if (gi + 2 < NG) {
-                M::load_k(kv, cur.b, cur.kvh, cur.jw + (gi + 2) * 64, cur.nb, lane, kA);
+                load_kg(cur, pg_cur, gi + 2, kA);
             } else if (nxt_it < items) {   // prefetch the next item's first group
                 M::load_q(a, nxt.b, nxt.l, nxt.kvh, lane, qn);
-                M::load_k(a.kv[nxt.l], nxt.b, nxt.kvh, nxt.jw, nxt.nb, lane, kA);
+                load_kg(nxt, pg_nxt, 0, kA);
             }
             fold(gi + 1, kB);
         }
@@ -507,6 +551,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_mfma(DraftScoreArgs a) {
 #pragma unroll
             for (int kk = 0; kk < M::KK; ++kk) qf[rb][kk] = qn[rb][kk];
         cur = nxt;
+        pg_cur = pg_nxt;
     }
 }
 
@@ -592,11 +637,32 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         bf16x8 qA[RB][KK], qB[RB][KK];
         bf16x8 kA[4][KK], kB[4][KK];
         float lA[RB][4], lB[RB][4];
+        // Paged: the page ids of this wave's 64 positions (4 pages) for every
+        // draft layer, loaded once per item: lane 4 * (l % 16) + s holds page s
+        // of layer l in pgA (l < 16) or pgB (l >= 16).  Loaded layer by layer
+        // (uniform code), so the layer descriptors are never indexed per lane.
+        int pgA = -1, pgB = -1;
+        if constexpr (PAGED) {
+            const int pidx = (jb >> 4) + (lane & 3);
+#pragma unroll 1
+            for (int l = 0; l < a.L_d; ++l) {
+                const KvView &kv = a.kv[l];
+                if ((lane >> 2) == (l & 15)) {
+                    const int v = pidx < kv.max_pages ? kv.page_table[(int64_t)b * kv.max_pages + pidx] : -1;
+                    if (l < 16) pgA = v;
+                    else pgB = v;
+                }
+            }
+        }
         auto load_k = [&](int u, bf16x8 (&k)[4][KK]) {
             u = (u < U) ? u : U - 1;
             const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
             if constexpr (PAGED) {
-                M::load_k(a.kv[l], b, kvh, jb, nb, lane, k);
+                int pg[4];
+                const int src = l < 16 ? pgA : pgB;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) pg[st] = __builtin_amdgcn_readlane(src, (l & 15) * 4 + st);
+                M::load_k_pg(a.kv[l], pg, kvh, jb, nb, lane, k);
             } else {
                 const char *base = a.kv[l].k + (int64_t)kvh * D * 2;
 #pragma unroll
