@@ -70,3 +70,41 @@ def check_set_tieband(gi, gt, oi, ot, sd, st, rel=1e-5):
 
 def oracle_kv(x, name, b):
     return f64(x.logical(name, b))
+
+
+def check_tier_rule(idx_row, tier_row, cnt, sd, st, n, k, m, n_sink, n_window):
+    """Invariants of the verification set (blog section 2.3) on any size,
+    checked directly (not through the oracle): the count, ascending unique
+    positions below n, the protected tier exactly the sinks and the recent
+    window, the draft tier of size min(m, k - |P|, n - |P|) holding the top
+    S_Draft keys (score, then lower position) outside P, and the target tier
+    holding the top S_Target keys of the rest."""
+    idx_row, tier_row = np.asarray(idx_row[:cnt]), np.asarray(tier_row[:cnt])
+    assert cnt == min(k, n)
+    assert (np.diff(idx_row) > 0).all() and (idx_row.size == 0 or (idx_row[0] >= 0 and idx_row[-1] < n))
+    P = set(range(min(n_sink, n))) | set(range(max(0, n - n_window), n))
+    got_p = set(idx_row[tier_row == 0].tolist())
+    assert got_p == P, "protected tier"
+    D = idx_row[tier_row == 1]
+    T = idx_row[tier_row == 2]
+    rest = np.setdiff1d(np.arange(n), np.array(sorted(P), dtype=np.int64))
+    budget = k - len(P)
+    m_eff = 0 if sd is None else (budget if st is None else m)
+    m_eff = max(0, min(m_eff, budget, rest.size))
+    assert D.size == m_eff, "draft tier size"
+    assert T.size == max(0, min(budget - m_eff, rest.size - m_eff)), "target tier size"
+
+    def top_by(score, chosen, pool):
+        """Every chosen position outranks every unchosen one of the pool."""
+        if chosen.size == 0 or chosen.size == pool.size:
+            return
+        others = np.setdiff1d(pool, chosen)
+        worst = min(chosen.tolist(), key=lambda j: (score[j], -j))
+        best = max(others.tolist(), key=lambda j: (score[j], -j))
+        assert (score[worst], -worst) > (score[best], -best), "tier is not the top of its pool"
+
+    if D.size:
+        top_by(sd, D, rest)
+    if T.size:
+        top_by(st, T, np.setdiff1d(rest, D))
+
