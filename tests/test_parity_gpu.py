@@ -146,6 +146,9 @@ SELECT_CASES = [
     (dict(B=2, N=140000, k=1000, m=400, ns=4, nw=32, ties=True), "longer-than-registers"),
     (dict(B=2, N=2500, k=333, m=50, ns=8, nw=8, ties=True, no_draft=True), "no-draft"),
     (dict(B=2, N=2500, k=333, m=50, ns=8, nw=8, ties=True, no_target=True), "no-target"),
+    (dict(B=3, N=65536, k=2048, m=1006, ns=4, nw=32, ties=True), "two-words-ties"),
+    (dict(B=2, N=32768, k=2048, m=1006, ns=4, nw=32, ties=False, equal=True), "all-equal"),
+    (dict(B=2, N=98304, k=4096, m=2030, ns=4, nw=32, ties=False, narrow=True), "narrow-range"),
 ]
 
 
@@ -158,7 +161,13 @@ def test_select_is_bit_exact(cfg, name):
     lens[0] = N
     if B > 2:
         lens[-1] = 0 if name == "ties" else lens[-1]
-    if cfg["ties"]:
+    if cfg.get("equal"):     # one key value: every selection is decided by position alone
+        sd = np.full((B, N), 0.25, dtype=np.float32)
+        st = np.full((B, N), 3.0, dtype=np.float32)
+    elif cfg.get("narrow"):  # keys within one binade, a few patterns apart at the top
+        sd = (1.0 + rng.integers(0, 1 << 12, size=(B, N)) * 2.0 ** -23).astype(np.float32)
+        st = (1.0 + rng.integers(0, 300, size=(B, N)) * 2.0 ** -23).astype(np.float32)
+    elif cfg["ties"]:
         sd = rng.integers(0, 50, size=(B, N)).astype(np.float32) / 7.0
         st = rng.integers(0, 50, size=(B, N)).astype(np.float32) / 3.0
     else:
