@@ -504,6 +504,8 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
         a.stat = (float *)(wsb + p.off_dstat);
         a.lse = (float *)(wsb + p.off_dlse);
         a.nchunk = p.nchunk;
+        a.part = (float *)(wsb + p.off_dpart);
+        a.acc_groups = p.acc_groups;
         hipError_t e = launch_draft_score(a, s);
         if (e != hipSuccess) return hip_status(e, "score draft launch");
     }

@@ -26,6 +26,8 @@ struct ScorePlan {
     size_t off_tlogit, off_tstat, off_tlse;   // [B][S][N_max], [B][S][nchunk][2], [B][S]
     // draft side
     size_t off_dstat, off_dlse;     // [B][L_d][Hkv_d][rows][nchunk][2], [B][L_d][Hkv_d][rows]
+    int acc_groups;                 // layer groups of the streaming accumulation pass
+    size_t off_dpart;               // [acc_groups][B][N_max] partial S_Draft (acc_groups > 1)
     size_t ws_bytes;
 };
 
@@ -60,6 +62,8 @@ struct DraftScoreArgs {
     int32_t nchunk;
     float *steps_out;               // window form: [B][gamma][N_max] per-step sums times steps_scale
     float steps_scale;
+    float *part;                    // ws: [acc_groups][B][N_max] per-layer-group partial sums
+    int32_t acc_groups;             // layer groups of the streaming accumulation (1: no partials)
 };
 
 hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s);

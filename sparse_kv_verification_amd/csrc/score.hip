@@ -987,10 +987,12 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     }
 }
 
-// Accumulation pass, streaming form.  Items (b, 1024-position chunk) walk
-// round robin over the persistent groups (chunks wholly past n_b only write
-// zeros); wave w owns positions w * 256 .. + 255 of the chunk and streams
-// them layer after layer, 8 stages per layer (stages past n_b are skipped).
+// Accumulation pass, streaming form.  Items (b, 1024-position chunk, layer
+// group) walk round robin over the persistent groups (chunks wholly past n_b
+// only write zeros); wave w owns positions w * 256 .. + 255 of the chunk and
+// streams them layer after layer of its group, 8 stages per layer (stages
+// past n_b are skipped).  With one layer group the item writes S_Draft;
+// otherwise it writes its group's partial sum, added up by draft_part_sum.
 // A layer's Q fragments and row normalisers are requested by the previous
 // layer's first stage, unconditionally and into the other of two named
 // register sets, so no register copy waits for a pending load.  Each stage
@@ -1008,9 +1010,13 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
     const int N = k0.N_max;
     const int nch = (N + CHUNK - 1) / CHUNK;
-    const int items = k0.B * nch;
+    const int LG = max(a.acc_groups, 1);
+    const int items = k0.B * nch * LG;
     const int L = a.L_d;
     const int U = L * 2;
+    // layers per group: ceil(L / LG) rounded up to even, so every group is
+    // non-empty and holds an even number of layers (L is even)
+    const int lpg = ((L + LG - 1) / LG + 1) & ~1;
     // per-lane Q offsets, and normaliser offsets: rows rb*16 + (lane >> 4)*4
     // .. + 3 in one 16-byte load (the row count is a multiple of 4); rows past
     // the count read row 0's normalisers and are dropped where the terms are
@@ -1037,20 +1043,22 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     float *acc = accs[wave];
     int slot = 0;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int b = it / nch, c = it - (it / nch) * nch;
+        const int bc = it / LG, g = it - (it / LG) * LG;
+        const int b = bc / nch, c = bc - (bc / nch) * nch;
+        const int l0 = g * lpg, l1 = min(L, l0 + lpg);
         const int nb = sl_len(k0, b);
         const int jw = c * CHUNK + wave * PER_WAVE;
         const int left = nb - jw;
-        const int nst = left <= 0 ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
+        const int nst = (left <= 0 || l0 >= l1) ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
 #pragma unroll
         for (int i = 0; i < PER_WAVE / 64; ++i) acc[lane + 64 * i] = 0.f;
         if (nst > 0) {
             const int64_t seq0 = (int64_t)b * N * 256;
             bf16x8 qA[2][RB][KK], qB[2][RB][KK];
             f32x4 lA[2][RB], lB[2][RB];
-            stream_load_q<RB>(a, b, 0, qo, qA);
-            load_lse(b, 0, lA);
-            stream_issue(a.kv[0].k + seq0, jw, N - 1, lane, ring[wave][slot]);
+            stream_load_q<RB>(a, b, l0, qo, qA);
+            load_lse(b, l0, lA);
+            stream_issue(a.kv[l0].k + seq0, jw, N - 1, lane, ring[wave][slot]);
             auto stage = [&](int s, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB]) {
                 const uint32_t base = lds_addr(ring[wave][slot]);
 #pragma unroll
@@ -1081,12 +1089,12 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                              f32x4 (&lsn)[2][RB]) {
                 // both layers' cache pointers from uniform indices (scalar
                 // loads, outside the vector-load order)
-                const int ln = (l + 1 < L) ? l + 1 : l;
+                const int ln = (l + 1 < l1) ? l + 1 : l;
                 const char *kl = a.kv[l].k + seq0;
                 const char *kn = a.kv[ln].k + seq0;
                 auto next_dma = [&](int s) {   // the DMA after stage s of this layer
                     if (s + 1 < nst) stream_issue(kl, jw + (s + 1) * kStreamPos, N - 1, lane, ring[wave][slot ^ 1]);
-                    else if (l + 1 < L) stream_issue(kn, jw, N - 1, lane, ring[wave][slot ^ 1]);
+                    else if (l + 1 < l1) stream_issue(kn, jw, N - 1, lane, ring[wave][slot ^ 1]);
                 };
                 wait_vmcnt<0>();
                 stream_load_q<RB>(a, b, ln, qo, qn);
@@ -1099,20 +1107,47 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                     stage(s, q, ls);
                 }
             };
-            for (int l = 0; l < L; l += 2) {
+            for (int l = l0; l < l1; l += 2) {
                 layer(l, qA, lA, qB, lB);
                 layer(l + 1, qB, lB, qA, lA);
             }
         }
+        float *out = (LG == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)g * k0.B + b) * N;
 #pragma unroll
         for (int i = 0; i < PER_WAVE / 64; ++i) {
             const int j = jw + lane + 64 * i;
-            if (j < N) a.s_draft[(int64_t)b * N + j] = (j < nb) ? acc[lane + 64 * i] : 0.f;
+            if (j < N) out[j] = (j < nb) ? acc[lane + 64 * i] : 0.f;
         }
     }
 }
 
 // --------------------------------------------------------------- host side
+// Layer groups of the streaming accumulation: with few (sequence, chunk)
+// items (short contexts, small batches) the layers are split into groups of
+// an even number of layers, each group an item of its own with a partial
+// sum, so that about kStreamGroups items fill the persistent grid.  Depends
+// on shapes only, so the workspace size needs no device.
+int draft_acc_groups(int B, int N_max, int L_d) {
+    if (L_d < 4 || L_d % 2 != 0) return 1;
+    const long items = (long)B * ((N_max + 1023) / 1024);
+    long lg = (kStreamGroups + items - 1) / items;
+    if (lg > L_d / 2) lg = L_d / 2;
+    if (lg <= 1) return 1;
+    int lpg = (int)((L_d + lg - 1) / lg);
+    lpg += lpg & 1;
+    return (L_d + lpg - 1) / lpg;
+}
+
+// S_Draft = the layer-group partials summed in group order; positions past
+// n_b are 0 (the partials already hold 0 there).
+__global__ __launch_bounds__(256) void draft_part_sum(const float *part, int groups, int64_t n, float *out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float v = 0.f;
+        for (int g = 0; g < groups; ++g) v += part[(int64_t)g * n + i];
+        out[i] = v;
+    }
+}
+
 ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int Hkv_d) {
     ScorePlan p{};
     p.nchunk = (N_max + CH - 1) / CH;
@@ -1129,6 +1164,9 @@ ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int H
     off = align_up(off + (size_t)B * drows * p.nchunk * 2 * sizeof(float), 256);
     p.off_dlse = off;
     off = align_up(off + (size_t)B * drows * sizeof(float), 256);
+    p.acc_groups = draft_acc_groups(B, N_max, L_d);
+    p.off_dpart = off;
+    if (p.acc_groups > 1) off = align_up(off + (size_t)p.acc_groups * B * N_max * sizeof(float), 256);
     p.ws_bytes = off;
     return p;
 }
@@ -1273,9 +1311,15 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
                        a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int acc_items = k0.B * ((k0.N_max + 1023) / 1024);
+    const int groups = a.acc_groups > 1 ? a.acc_groups : 1;
+    b.acc_groups = groups;
+    const int acc_items = k0.B * ((k0.N_max + 1023) / 1024) * groups;
     hipLaunchKernelGGL((draft_acc_stream<RB>), dim3(acc_items < kStreamGroups ? acc_items : kStreamGroups),
                        dim3(256), 0, s, b);
+    if ((e = hipGetLastError()) != hipSuccess || groups == 1) return e;
+    const int64_t n = (int64_t)k0.B * k0.N_max;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
+    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, groups, n, a.s_draft);
     return hipGetLastError();
 }
 
