@@ -759,21 +759,64 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
 // loads on the way (Q fragments, row normalisers, lengths) complete in order
 // with the DMA, and every stage starts with a full vmcnt wait, so a stage
 // never reads LDS before its own bytes have landed.
-constexpr int kStreamPos = 32;                    // positions per stage
-constexpr int kStreamStage = kStreamPos * 256;    // bytes per stage
-constexpr int kStreamGroups = 512;                // two 4-wave groups per CU
+// Up to two row blocks per KV head: 32-position (8 KiB) stages and two
+// 4-wave groups per CU.  (Three or four row blocks need one group per CU
+// for their registers; with 64-position stages to keep the bytes in flight
+// they ran no faster than the register-staged kernels, which serve them.)
+template <int RB>
+struct StreamGeom {
+    static_assert(RB <= 2, "streaming passes: at most two row blocks");
+    static constexpr int POS = 32;                    // positions per stage
+    static constexpr int STAGE = POS * 256;           // bytes per stage
+    static constexpr int GROUPS = 512;                // persistent work-groups
+};
+constexpr int kStreamGroups = 512;
 
 // DMA of positions j0 .. j0 + 31 of one layer into `stage`; `seq` is the
 // layer's k pointer advanced to the sequence.  Positions past the cache end
 // read the last row (the caller masks them).
+template <int POS>
 __device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast, int lane, uint8_t *stage) {
 #pragma unroll
-    for (int i = 0; i < kStreamStage / 1024; ++i) {
+    for (int i = 0; i < POS / 4; ++i) {
         const int rho = i * 4 + (lane >> 4);
         const int chunk = (lane & 15) ^ (rho & 15);
         const uint32_t j = (uint32_t)min(j0 + rho, jlast);
         dma16_stream(seq + (j * 256u + (uint32_t)chunk * 16u), stage + i * 1024);
     }
+}
+
+// All-zero K row: the source of positions whose page id is out of range
+// (they score as an all-zero key, as in the register-staged kernels).
+__device__ __align__(256) uint8_t g_zero_krow[256] = {0};
+
+// Paged form of stream_issue: stage s of a wave's span, whose POS / 16
+// pages have their ids in lanes (POS / 16) s + 0, 1, .. of `pgv`; `pool` is
+// the layer's k pointer (row r of the pool at r * 256 bytes).
+template <int POS>
+__device__ __forceinline__ void stream_issue_pg(const char *pool, int pgv, int s, int num_pages, int lane,
+                                                uint8_t *stage) {
+    constexpr int NP = POS / 16;
+    int pgs[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) pgs[k] = __builtin_amdgcn_readlane(pgv, NP * s + k);
+#pragma unroll
+    for (int i = 0; i < POS / 4; ++i) {
+        const int rho = i * 4 + (lane >> 4);   // on page i / 4 of the stage
+        const int chunk = (lane & 15) ^ (rho & 15);
+        const int pg = pgs[i >> 2];
+        const char *src = (pg >= 0 && pg < num_pages)
+                              ? pool + (((int64_t)pg * 16 + (rho & 15)) * 256 + chunk * 16)
+                              : (const char *)g_zero_krow + chunk * 16;
+        dma16_stream(src, stage + i * 1024);
+    }
+}
+
+// Page ids of the `npg` pages from position j0 on of sequence b, lane t
+// holding page j0 / 16 + t (-1 past the table).
+__device__ __forceinline__ int stream_load_pg(const KvView &kv, int b, int j0, int npg, int lane) {
+    const int pi = (j0 >> 4) + lane;
+    return (lane < npg && pi < kv.max_pages) ? kv.page_table[(int64_t)b * kv.max_pages + pi] : -1;
 }
 
 // Buffer resource over `bytes` bytes at `base` (loads past the end read 0).
@@ -835,38 +878,69 @@ __device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int l
 // next item's first DMA; items alternate between two named Q sets, so no
 // register copy waits for a pending load.  The cross-wave combine
 // alternates between two LDS buffers, so one barrier per item suffices.
-template <int RB>
+template <int RB, bool PAGED>
 __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     constexpr int KK = 2;
+    constexpr int POS = StreamGeom<RB>::POS;
     constexpr int PER_WAVE = kDraftStatChunk / 4;
-    constexpr int NSTAGE = PER_WAVE / kStreamPos;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][kStreamStage];
+    constexpr int NSTAGE = PER_WAVE / POS;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][StreamGeom<RB>::STAGE];
     __shared__ float red[2][4][2][RB * 16][2];
+    __shared__ int pref[kDraftStatMaxB + 1];   // chunks below n_b of sequences before b
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int U = a.L_d * 2;
     const int nch = a.nchunk;
-    const int items = a.kv[0].B * a.L_d * nch;
+    const int B = a.kv[0].B;
+    // Items are (b, layer, chunk) over the chunks that hold positions below
+    // n_b only, numbered sequence by sequence (B <= kDraftStatMaxB, checked
+    // by the launcher), so a ragged batch spreads evenly over the groups.
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
+        pref[bb + 1] = (sl_len(a.kv[0], bb) + kDraftStatChunk - 1) / kDraftStatChunk;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        pref[0] = 0;
+        for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
+    }
+    __syncthreads();
+    const int items = a.L_d * pref[B];
     struct Item { int b, l, c, nb, jw, nst; const char *seq; int jlast; };
     auto decode = [&](int it) {
         Item x;
-        x.c = it % nch;
-        x.l = (it / nch) % a.L_d;
-        x.b = it / (nch * a.L_d);
+        const int cu = it / a.L_d;             // chunk index over all sequences
+        int lo = 0, hi = B - 1;                // the b with pref[b] <= cu < pref[b + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pref[mid] <= cu) lo = mid;
+            else hi = mid - 1;
+        }
+        x.b = lo;
+        const int nbc = pref[lo + 1] - pref[lo];
+        const int r = it - a.L_d * pref[lo];   // within the sequence: layer-major
+        x.l = r / nbc;
+        x.c = r - x.l * nbc;
         x.nb = sl_len(a.kv[x.l], x.b);
         x.jw = x.c * kDraftStatChunk + wave * PER_WAVE;
         const int left = x.nb - x.jw;
-        x.nst = left <= 0 ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
-        x.seq = a.kv[x.l].k + (int64_t)x.b * a.kv[x.l].N_max * 256;
+        x.nst = left <= 0 ? 0 : min(NSTAGE, (left + POS - 1) / POS);
+        x.seq = PAGED ? a.kv[x.l].k : a.kv[x.l].k + (int64_t)x.b * a.kv[x.l].N_max * 256;
         x.jlast = a.kv[x.l].N_max - 1;
         return x;
     };
     uint32_t qo[RB];
     stream_qoff<RB>(a, lane, qo);
     int slot = 0, par = 0;
-    // One item on Q set q; requests the next item's Q into qn and, when the
-    // next item has stages, its first DMA.
+    // paged caches: the page ids of an item's wave span (64 pages), one per lane
+    auto load_pg = [&](const Item &x) -> int {
+        return PAGED ? stream_load_pg(a.kv[x.l], x.b, x.jw, PER_WAVE / 16, lane) : 0;
+    };
+    auto issue = [&](const Item &x, int pgv, int s, uint8_t *stage) {
+        if constexpr (PAGED) stream_issue_pg<POS>(x.seq, pgv, s, a.kv[x.l].num_pages, lane, stage);
+        else stream_issue<POS>(x.seq, x.jw + s * POS, x.jlast, lane, stage);
+    };
+    // One item on Q set q (page ids pg); requests the next item's Q into qn
+    // (page ids into pgn) and, when the next item has stages, its first DMA.
     auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[2][RB][KK],
-                    bf16x8 (&qn)[2][RB][KK]) {
+                    bf16x8 (&qn)[2][RB][KK], const int &pg, int &pgn) {
         float mrun[2][RB][4], zrun[2][RB][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -878,20 +952,22 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     zrun[h][rb][i] = 0.f;
                 }
         auto next_dma = [&](int s) {   // the DMA after stage s
-            if (s + 1 < cur.nst) stream_issue(cur.seq, cur.jw + (s + 1) * kStreamPos, cur.jlast, lane, ring[wave][slot ^ 1]);
-            else if (has_next && nxt.nst > 0) stream_issue(nxt.seq, nxt.jw, nxt.jlast, lane, ring[wave][slot ^ 1]);
+            if (s + 1 < cur.nst) issue(cur, pg, s + 1, ring[wave][slot ^ 1]);
+            else if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot ^ 1]);
         };
         auto stage = [&](int s) {
             const uint32_t base = lds_addr(ring[wave][slot]);
-            const int j0 = cur.jw + s * kStreamPos;
-            const bool full = j0 + kStreamPos <= cur.nb;
+            const int j0 = cur.jw + s * POS;
+            const bool full = j0 + POS <= cur.nb;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int pr = 0; pr < POS / 32; ++pr) {   // pairs of 16-position subtiles
                 f32x4 sc[2][RB];
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     bf16x8 k[2];
-                    stream_kfrag(base, st, h, lane, k);
+                    stream_kfrag(base, pr * 2 + st, h, lane, k);
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -907,8 +983,8 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         float v0 = sc[0][rb][i] * a.scale_log2, v1 = sc[1][rb][i] * a.scale_log2;
                         if (!full) {
-                            if (j0 + (lane & 15) >= cur.nb) v0 = kNegInf;
-                            if (j0 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
+                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) v0 = kNegInf;
+                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
                         }
                         const float mx = fmaxf(mrun[h][rb][i], fmaxf(v0, v1));
                         const float mu = (mx == kNegInf) ? 0.f : mx;
@@ -921,10 +997,12 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         };
         if (cur.nst == 0) {
             stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
-            if (has_next && nxt.nst > 0) stream_issue(nxt.seq, nxt.jw, nxt.jlast, lane, ring[wave][slot]);
+            pgn = load_pg(nxt);
+            if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot]);
         } else {
             wait_vmcnt<0>();
             stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
+            pgn = load_pg(nxt);
             next_dma(0);
             stage(0);
             for (int s = 1; s < cur.nst; ++s) {
@@ -970,17 +1048,18 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     bf16x8 qA[2][RB][KK], qB[2][RB][KK];
     Item cur = decode(it);
     stream_load_q<RB>(a, cur.b, cur.l, qo, qA);
-    if (cur.nst > 0) stream_issue(cur.seq, cur.jw, cur.jlast, lane, ring[wave][slot]);
+    int pgA = load_pg(cur), pgB = 0;
+    if (cur.nst > 0) issue(cur, pgA, 0, ring[wave][slot]);
     for (;;) {
         int nit = it + gridDim.x;
         Item nxt = decode(nit < items ? nit : it);
-        item(cur, nxt, nit < items, qA, qB);
+        item(cur, nxt, nit < items, qA, qB, pgA, pgB);
         if (nit >= items) break;
         it = nit;
         cur = nxt;
         nit = it + gridDim.x;
         nxt = decode(nit < items ? nit : it);
-        item(cur, nxt, nit < items, qB, qA);
+        item(cur, nxt, nit < items, qB, qA, pgB, pgA);
         if (nit >= items) break;
         it = nit;
         cur = nxt;
@@ -998,20 +1077,38 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
 // register sets, so no register copy waits for a pending load.  Each stage
 // adds sum_{head, row} exp2(logit - lse) for its 32 positions to a
 // wave-private LDS accumulator, in layer order, so S_Draft needs no atomics.
-template <int RB>
+template <int RB, bool PAGED>
 __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     constexpr int KK = 2;
     constexpr int CHUNK = 1024;
+    constexpr int POS = StreamGeom<RB>::POS;
     constexpr int PER_WAVE = CHUNK / 4;
-    constexpr int NSTAGE = PER_WAVE / kStreamPos;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][kStreamStage];
+    constexpr int NSTAGE = PER_WAVE / POS;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][StreamGeom<RB>::STAGE];
     __shared__ float accs[4][PER_WAVE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
     const int N = k0.N_max;
-    const int nch = (N + CHUNK - 1) / CHUNK;
     const int LG = max(a.acc_groups, 1);
-    const int items = k0.B * nch * LG;
+    const int B = k0.B;
+    // Items are (b, chunk, layer group) over the chunks that hold positions
+    // below n_b only, numbered sequence by sequence (B <= kDraftStatMaxB).
+    __shared__ int pref[kDraftStatMaxB + 1];
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x) pref[bb + 1] = (sl_len(k0, bb) + CHUNK - 1) / CHUNK;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        pref[0] = 0;
+        for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
+    }
+    __syncthreads();
+    const int items = pref[B] * LG;
+    if (LG == 1) {   // chunks wholly past n_b: S_Draft = 0 (with layer groups draft_part_sum writes them)
+        for (int bb = 0; bb < B; ++bb) {
+            const int j0 = (pref[bb + 1] - pref[bb]) * CHUNK;
+            for (int j = j0 + blockIdx.x * 256 + (int)threadIdx.x; j < N; j += gridDim.x * 256)
+                a.s_draft[(int64_t)bb * N + j] = 0.f;
+        }
+    }
     const int L = a.L_d;
     const int U = L * 2;
     // layers per group: ceil(L / LG) rounded up to even, so every group is
@@ -1044,25 +1141,40 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     int slot = 0;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int bc = it / LG, g = it - (it / LG) * LG;
-        const int b = bc / nch, c = bc - (bc / nch) * nch;
+        int lo = 0, hi = B - 1;   // the b with pref[b] <= bc < pref[b + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pref[mid] <= bc) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = lo, c = bc - pref[lo];
         const int l0 = g * lpg, l1 = min(L, l0 + lpg);
         const int nb = sl_len(k0, b);
         const int jw = c * CHUNK + wave * PER_WAVE;
         const int left = nb - jw;
-        const int nst = (left <= 0 || l0 >= l1) ? 0 : min(NSTAGE, (left + kStreamPos - 1) / kStreamPos);
+        const int nst = (left <= 0 || l0 >= l1) ? 0 : min(NSTAGE, (left + POS - 1) / POS);
 #pragma unroll
         for (int i = 0; i < PER_WAVE / 64; ++i) acc[lane + 64 * i] = 0.f;
         if (nst > 0) {
-            const int64_t seq0 = (int64_t)b * N * 256;
+            const int64_t seq0 = PAGED ? 0 : (int64_t)b * N * 256;
+            // paged caches: the page ids of the wave's 256 positions (16
+            // pages) in each layer, one per lane, loaded with the layer's Q
+            auto load_pg = [&](int l) -> int { return PAGED ? stream_load_pg(a.kv[l], b, jw, PER_WAVE / 16, lane) : 0; };
+            auto issue = [&](int l, const char *kl, int pgv, int s, uint8_t *stage) {
+                if constexpr (PAGED) stream_issue_pg<POS>(kl, pgv, s, a.kv[l].num_pages, lane, stage);
+                else stream_issue<POS>(kl, jw + s * POS, N - 1, lane, stage);
+            };
             bf16x8 qA[2][RB][KK], qB[2][RB][KK];
             f32x4 lA[2][RB], lB[2][RB];
+            int pA = 0, pB = 0;
             stream_load_q<RB>(a, b, l0, qo, qA);
             load_lse(b, l0, lA);
-            stream_issue(a.kv[l0].k + seq0, jw, N - 1, lane, ring[wave][slot]);
+            pA = load_pg(l0);
+            issue(l0, a.kv[l0].k + seq0, pA, 0, ring[wave][slot]);
             auto stage = [&](int s, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB]) {
                 const uint32_t base = lds_addr(ring[wave][slot]);
 #pragma unroll
-                for (int s16 = 0; s16 < 2; ++s16) {
+                for (int s16 = 0; s16 < POS / 16; ++s16) {
                     float t = 0.f;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
@@ -1081,24 +1193,25 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                         }
                     }
                     t = group4_sum(t);
-                    if (lane < 16) acc[s * kStreamPos + s16 * 16 + lane] += t;
+                    if (lane < 16) acc[s * POS + s16 * 16 + lane] += t;
                 }
                 slot ^= 1;
             };
-            auto layer = [&](int l, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB], bf16x8 (&qn)[2][RB][KK],
-                             f32x4 (&lsn)[2][RB]) {
+            auto layer = [&](int l, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB], const int &pg,
+                             bf16x8 (&qn)[2][RB][KK], f32x4 (&lsn)[2][RB], int &pgn) {
                 // both layers' cache pointers from uniform indices (scalar
                 // loads, outside the vector-load order)
                 const int ln = (l + 1 < l1) ? l + 1 : l;
                 const char *kl = a.kv[l].k + seq0;
                 const char *kn = a.kv[ln].k + seq0;
                 auto next_dma = [&](int s) {   // the DMA after stage s of this layer
-                    if (s + 1 < nst) stream_issue(kl, jw + (s + 1) * kStreamPos, N - 1, lane, ring[wave][slot ^ 1]);
-                    else if (l + 1 < l1) stream_issue(kn, jw, N - 1, lane, ring[wave][slot ^ 1]);
+                    if (s + 1 < nst) issue(l, kl, pg, s + 1, ring[wave][slot ^ 1]);
+                    else if (l + 1 < l1) issue(ln, kn, pgn, 0, ring[wave][slot ^ 1]);
                 };
                 wait_vmcnt<0>();
                 stream_load_q<RB>(a, b, ln, qo, qn);
                 load_lse(b, ln, lsn);
+                pgn = load_pg(ln);
                 next_dma(0);
                 stage(0, q, ls);
                 for (int s = 1; s < nst; ++s) {
@@ -1108,8 +1221,8 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                 }
             };
             for (int l = l0; l < l1; l += 2) {
-                layer(l, qA, lA, qB, lB);
-                layer(l + 1, qB, lB, qA, lA);
+                layer(l, qA, lA, pA, qB, lB, pB);
+                layer(l + 1, qB, lB, pB, qA, lA, pA);
             }
         }
         float *out = (LG == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)g * k0.B + b) * N;
@@ -1139,11 +1252,15 @@ int draft_acc_groups(int B, int N_max, int L_d) {
 }
 
 // S_Draft = the layer-group partials summed in group order; positions past
-// n_b are 0 (the partials already hold 0 there).
-__global__ __launch_bounds__(256) void draft_part_sum(const float *part, int groups, int64_t n, float *out) {
+// n_b are 0 (the partials of chunks wholly past n_b are never written).
+__global__ __launch_bounds__(256) void draft_part_sum(const float *part, int groups, int B, int N,
+                                                      const int32_t *seq_lens, float *out) {
+    const int64_t n = (int64_t)B * N;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int b = (int)(i / N), j = (int)(i - (int64_t)b * N);
         float v = 0.f;
-        for (int g = 0; g < groups; ++g) v += part[(int64_t)g * n + i];
+        if (j < min(max(seq_lens[b], 0), N))
+            for (int g = 0; g < groups; ++g) v += part[(int64_t)g * n + i];
         out[i] = v;
     }
 }
@@ -1295,15 +1412,16 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Streaming passes: contiguous cache, two 64-wide draft KV heads, an even
-// number of draft layers and a row count that is a multiple of four.
-template <int RB>
+// Streaming passes: two 64-wide draft KV heads, an even number of draft
+// layers and a row count that is a multiple of four; contiguous or paged.
+template <int RB, bool PAGED>
 static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     DraftScoreArgs b = a;
     b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
     const int stat_items = k0.B * a.L_d * b.nchunk;
-    hipLaunchKernelGGL((draft_stats_stream<RB>), dim3(stat_items < kStreamGroups ? stat_items : kStreamGroups),
+    constexpr int GROUPS = StreamGeom<RB>::GROUPS;
+    hipLaunchKernelGGL((draft_stats_stream<RB, PAGED>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
                        dim3(256), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1314,12 +1432,13 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const int groups = a.acc_groups > 1 ? a.acc_groups : 1;
     b.acc_groups = groups;
     const int acc_items = k0.B * ((k0.N_max + 1023) / 1024) * groups;
-    hipLaunchKernelGGL((draft_acc_stream<RB>), dim3(acc_items < kStreamGroups ? acc_items : kStreamGroups),
+    hipLaunchKernelGGL((draft_acc_stream<RB, PAGED>), dim3(acc_items < GROUPS ? acc_items : GROUPS),
                        dim3(256), 0, s, b);
     if ((e = hipGetLastError()) != hipSuccess || groups == 1) return e;
     const int64_t n = (int64_t)k0.B * k0.N_max;
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
-    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, groups, n, a.s_draft);
+    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, groups, k0.B, k0.N_max,
+                       k0.seq_lens, a.s_draft);
     return hipGetLastError();
 }
 
@@ -1327,7 +1446,8 @@ template <int D, int RB>
 static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     if constexpr (D == 64 && RB <= 2) {
-        if (a.Hkv_d == 2 && k0.page_size == 0 && a.L_d % 2 == 0 && a.rows % 4 == 0) return draft_stream_impl<RB>(a, s);
+        if (a.Hkv_d == 2 && a.L_d % 2 == 0 && a.rows % 4 == 0)
+            return k0.page_size == 0 ? draft_stream_impl<RB, false>(a, s) : draft_stream_impl<RB, true>(a, s);
     }
     const int U = a.L_d * a.Hkv_d;
     DraftScoreArgs b = a;

@@ -195,6 +195,7 @@ SCORE_CASES = [
     ("qwen72b-packed", dict(base="c4", B=2, n=1700, L_d=2, S=8)),
     ("stream-ragged", dict(base="c2", B=3, n=5000, L_d=4, n_lo=700)),
     ("stream-layer-groups", dict(base="c2", B=2, n=3000, L_d=6, n_lo=1000)),
+    ("stream-paged", dict(base="c5", B=3, n=5000, n_lo=1200, L_d=4, w=4)),
     ("tiny-f32", dict(base="c1")),
 ]
 
