@@ -105,13 +105,25 @@ __global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, N
     constexpr int IPP = 256 / LPI;            // positions per pass
     __shared__ float qs[8][D];
     __shared__ float lg[8][CH];
+    __shared__ int pgs[CH / 16];   // paged caches: the chunk's page ids
 
     const int chunk = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const KvView &kv = p.kv[p.ut.view[u]];
-    const int kvh = p.ut.kvh[u], row0 = p.ut.row0[u], nr = p.ut.nrow[u];
-    const int nb = sl_len(kv, b);
+    const int kvh = p.ut.kvh[u], row0 = p.ut.row0[u], nb = sl_len(kv, b);
+    const int nr = p.ut.nrow[u];
     const int j0 = chunk * CH;
+    // a chunk wholly past n_b has nothing to produce: its statistics and
+    // logits are never read (rows_lse and the finalizers stop at n_b)
+    if (j0 >= nb) return;
+    const bool paged = kv.page_size != 0;
+    // the page ids are loaded once, with Q, so no K load waits for a
+    // page-table load of its own
+    if (paged)
+        for (int i = tid; i < CH / 16; i += 256) {
+            const int pi = (j0 >> 4) + i;
+            pgs[i] = pi < kv.max_pages ? kv.page_table[(int64_t)b * kv.max_pages + pi] : -1;
+        }
 
     for (int e = tid; e < nr * D; e += 256) {
         const int r = e / D, d = e - (e / D) * D;
@@ -125,7 +137,17 @@ __global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, N
         const int j = j0 + pos;
         float x[8];
         const bool ok = j < nb;
-        load_slice<F32>(ok ? krow(kv, b, j, kvh, ESZ) : nullptr, sl, x);
+        const char *row = nullptr;
+        if (ok) {
+            if (paged) {
+                const int pg = pgs[pos >> 4];
+                if (pg >= 0 && pg < kv.num_pages)
+                    row = kv.k + ((((int64_t)pg * 16 + (j & 15)) * kv.Hkv + kvh) * D) * ESZ;
+            } else {
+                row = kv.k + ((((int64_t)b * kv.N_max + j) * kv.Hkv + kvh) * D) * ESZ;
+            }
+        }
+        load_slice<F32>(row, sl, x);
         for (int r = 0; r < nr; ++r) {
             float s = 0.f;
 #pragma unroll
