@@ -597,8 +597,31 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
     const int U = a.L_d * a.Hkv_d;
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
     const int N = k0.N_max;
-    const int nch = (N + kDraftAccChunk - 1) / kDraftAccChunk;
-    const int items = k0.B * nch;
+    const int B = k0.B;
+    // Items are (b, chunk) over the chunks that hold positions below n_b
+    // only, numbered sequence by sequence (B <= kDraftStatMaxB, checked by
+    // the launchers), so a ragged batch spreads evenly over the groups; the
+    // chunks wholly past n_b are zero-filled first.
+    __shared__ int pref[kDraftStatMaxB + 1];
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
+        pref[bb + 1] = (sl_len(k0, bb) + kDraftAccChunk - 1) / kDraftAccChunk;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        pref[0] = 0;
+        for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
+    }
+    __syncthreads();
+    const int items = pref[B];
+    for (int bb = 0; bb < B; ++bb) {
+        const int j0 = (pref[bb + 1] - pref[bb]) * kDraftAccChunk;
+        for (int j = j0 + blockIdx.x * 256 + (int)threadIdx.x; j < N; j += gridDim.x * 256) {
+            if constexpr (W > 0) {
+                for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)bb * a.gamma + q2) * N + j] = 0.f;
+            } else {
+                a.s_draft[(int64_t)bb * N + j] = 0.f;
+            }
+        }
+    }
     // per-lane parts of the Q addresses (row rb*16 + (lane & 15)) and of the
     // normaliser index (rows rb*16 + (lane >> 4)*4 + i); padding rows read
     // row 0 and are masked
@@ -623,7 +646,13 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         }
     constexpr int NS = W > 0 ? W : 1;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int c = it % nch, b = it / nch;
+        int lo = 0, hi = B - 1;   // the b with pref[b] <= it < pref[b + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pref[mid] <= it) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = lo, c = it - pref[lo];
         const int jb = c * kDraftAccChunk + wave * 64;
         const int nb = sl_len(k0, b);
         if (jb >= nb) {   // this wave's positions are all past the sequence: zeros, no work
