@@ -9,12 +9,14 @@
 //
 // One 1024-lane work-group per sequence.  Each TopK is a most-significant-
 // digit radix select on the float bit patterns (scores are non-negative, so
-// the unsigned order of the bits is the numeric order): three passes of
-// 11/11/10-bit digits with the histogram in LDS find the k-th largest key T
-// and how many keys equal to T are needed; one ordered pass then takes every
-// key above T plus the lowest positions among the keys equal to T.  Position
-// j is always handled by lane j mod 1024, so the per-position tier flags need
-// no synchronisation beyond the block barriers.
+// the unsigned order of the bits is the numeric order) that finds the k-th
+// largest key T and how many keys equal to T are needed; every key above T
+// then goes in, plus the lowest positions among the keys equal to T.
+// Sequences up to 131072 positions keep their selections in registers
+// (topk_il_kernel, below); longer ones keep per-position tier flags in the
+// workspace (topk_kernel: three passes of 11/11/10-bit digits with the
+// histogram in LDS; position j is always handled by lane j mod 1024, so the
+// flags need no synchronisation beyond the block barriers).
 
 #include "common.h"
 #include "internal.h"
