@@ -818,11 +818,14 @@ def estimator_curve(args, sh, x, cap, timed):
 
 
 def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):
-    """The step with the draft window in the cache: every layer's window
-    rows appended, score, select, L causal verification attentions over the
-    set plus the window, and the commit.  The histories are w shorter than
-    the generated ones so the window fits behind them; the commit accepts 0
-    tokens so the timed step repeats on the same lengths."""
+    """The step with the draft window in the cache: score, select, L causal
+    verification attentions over the set plus the window, each appending its
+    layer's window rows to the cache in the same launch
+    (dustin_verify_attn_append), and the commit.  The same step with the
+    appends as separate launches (dustin_append_window_kv for every layer,
+    then dustin_verify_attn) is timed beside it.  The histories are w shorter
+    than the generated ones so the window fits behind them; the commit
+    accepts 0 tokens so the timed step repeats on the same lengths."""
     import torch
     import sparse_kv_verification_amd as dk
     dev = x.q.device
@@ -850,20 +853,34 @@ def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):
         for l in range(sh.layers):
             dk.dustin_verify_attn(x.q, kvw[l], idx, cnt, out=out, ws=ws_v)
 
-    def step():
-        append()
+    def verify_fused():
+        for l in range(sh.layers):
+            dk.dustin_verify_attn_append(x.q, kvw[l], k_win, v_win, idx, cnt, out=out, ws=ws_v)
+
+    def select():
         dk.dustin_score(dkw, x.q_draft, [kvw[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
         dk.dustin_topk(s_d, s_t, lens_w, k, m, n_sink, n_window, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+
+    def step():
+        select()
+        verify_fused()
+        dk.dustin_commit_window(lens_w, accepted, sh.w)
+
+    def step_separate():
+        append()
+        select()
         verify()
         dk.dustin_commit_window(lens_w, accepted, sh.w)
 
     for _ in range(max(1, args.warmup)):
+        step_separate()
         step()
     torch.cuda.synchronize()
-    run, per_launch = step, verify
+    fns = (step, verify_fused, step_separate, verify)
+    runs = list(fns)
     graphs = []
     if not args.no_graph:
-        for fn in (step, verify):
+        for fn in fns:
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.stream(cap):
                 with torch.cuda.graph(gr, stream=cap):
@@ -871,18 +888,24 @@ def window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed):
             torch.cuda.synchronize()
             gr.replay()
             graphs.append(gr)
-        run, per_launch = graphs[0].replay, graphs[1].replay
-    step_us = timed(run, args.steps)
-    verify_us = timed(per_launch, args.steps) / sh.layers
+        runs = [gr.replay for gr in graphs]
+    step_us = timed(runs[0], args.steps)
+    fused_us = timed(runs[1], args.steps) / sh.layers
+    step_sep_us = timed(runs[2], args.steps)
+    verify_us = timed(runs[3], args.steps) / sh.layers
     append_us = timed(append, args.steps) / sh.layers
     commit_us = timed(lambda: dk.dustin_commit_window(lens_w, accepted, sh.w), args.steps)
     esz = x.K.element_size()
     rows = int(cnt.sum()) + sh.B * sh.w
     per_layer = rows * sh.Hkv * sh.d * esz * 2 + 2 * x.q.numel() * esz + sh.B * k * 4 + sh.B * 4
-    log(f"window step {step_us:.1f} us; verify attention {verify_us:.2f} us/launch "
-        f"({per_layer / verify_us / 1e3:.0f} GB/s), append {append_us:.2f} us/layer, commit {commit_us:.2f} us")
+    log(f"window step {step_us:.1f} us (appends fused into the attention; {step_sep_us:.1f} us with separate "
+        f"appends); verify attention + append {fused_us:.2f} us/launch, verify attention alone {verify_us:.2f} "
+        f"us/launch ({per_layer / verify_us / 1e3:.0f} GB/s), separate append {append_us:.2f} us/layer, "
+        f"commit {commit_us:.2f} us")
     return {
         "step_us": round(step_us, 2),
+        "step_us_separate_appends": round(step_sep_us, 2),
+        "verify_attn_append_per_launch_us": round(fused_us, 3),
         "verify_attn_per_launch_us": round(verify_us, 3),
         "verify_attn_GBps": round(per_layer / verify_us / 1e3, 1),
         "verify_attn_algorithmic_bytes_per_launch": per_layer,

@@ -13,8 +13,8 @@
  *      K/V rows only                     -> dustin_sparse_verify_attn
  *      (history only) or dustin_verify_attn (history set plus the window's
  *      own rows, causally), with dustin_append_window_kv writing the window
- *      into the cache first and dustin_commit_window keeping the accepted
- *      tokens afterwards
+ *      into the cache first (dustin_verify_attn_append: both in one call)
+ *      and dustin_commit_window keeping the accepted tokens afterwards
  *   plus the evaluator of the translation's section 3.1 (attention recovery
  *   rate):                               -> dustin_window_attn, dustin_arr,
  *   and the policy comparison of its sections 3.2-3.3
@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define DUSTIN_ABI_VERSION 6
+#define DUSTIN_ABI_VERSION 7
 
 typedef enum dustin_status {
     DUSTIN_OK = 0,
@@ -241,6 +241,24 @@ dustin_status dustin_verify_attn(const void *q, int32_t w, int32_t H_q, const du
                                  const int32_t *idx, const int32_t *count, int32_t k, float scale,
                                  void *out, float *lse, void *ws, size_t ws_bytes,
                                  dustin_stream_t stream);
+
+/*
+ * dustin_verify_attn_append -- dustin_append_window_kv followed by
+ * dustin_verify_attn, in one launch for bfloat16 caches (two for float32):
+ * the same cache contents and bitwise the same out / lse as the two calls
+ * in order.  The window's own rows are read from k_win / v_win, and the
+ * first token split of each (sequence, KV head) also writes them into the
+ * cache rows n_b .. n_b + w - 1 (rows at positions >= N_max, or whose page
+ * id is outside [0, num_pages), are neither written nor attended, as in the
+ * separate calls).  Arguments as for dustin_verify_attn, plus k_win /
+ * v_win as for dustin_append_window_kv; same workspace
+ * (dustin_verify_attn_workspace_bytes).  kv->k, kv->v, k_win and v_win must
+ * be 16-byte aligned.
+ */
+dustin_status dustin_verify_attn_append(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                        const void *k_win, const void *v_win, const int32_t *idx,
+                                        const int32_t *count, int32_t k, float scale, void *out, float *lse,
+                                        void *ws, size_t ws_bytes, dustin_stream_t stream);
 
 /* k_or_n: the k passed to the call, or N_max for the dense (idx == NULL) form. */
 size_t dustin_verify_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_kv,

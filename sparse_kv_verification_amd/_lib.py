@@ -22,7 +22,7 @@ EXPORTS = [
     "dustin_score", "dustin_score_workspace_bytes",
     "dustin_topk", "dustin_topk_workspace_bytes",
     "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes",
-    "dustin_verify_attn", "dustin_verify_attn_workspace_bytes",
+    "dustin_verify_attn", "dustin_verify_attn_workspace_bytes", "dustin_verify_attn_append",
     "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
     "dustin_arr", "dustin_window_mean", "dustin_policy_sweep", "dustin_policy_sweep_workspace_bytes",
@@ -80,6 +80,8 @@ def lib():
         L.dustin_attn_workspace_bytes.restype = sz
         L.dustin_verify_attn.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.dustin_verify_attn.restype = ctypes.c_int
+        L.dustin_verify_attn_append.argtypes = [vp, i32, i32, kvp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.dustin_verify_attn_append.restype = ctypes.c_int
         L.dustin_verify_attn_workspace_bytes.argtypes = [i32] * 6
         L.dustin_verify_attn_workspace_bytes.restype = sz
         L.dustin_append_window_kv.argtypes = [kvp, vp, vp, i32, vp]
@@ -256,6 +258,27 @@ def dustin_verify_attn(q, kv: KV, idx=None, count=None, k=None, scale=0.0,
     wsb = _ws("verify", ws, nbytes, q.device)
     _check(lib().dustin_verify_attn(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
                                     _ptr(out), _ptr(lse), _ptr(wsb), wsb.numel(), _stream(q)))
+    return out
+
+
+def dustin_verify_attn_append(q, kv: KV, k_win, v_win, idx=None, count=None, k=None, scale=0.0,
+                              out=None, lse=None, ws: Workspace | None = None):
+    """dustin_append_window_kv(kv, k_win, v_win) then dustin_verify_attn(q,
+    kv, ...) in one call (one launch for a bfloat16 cache): the window's
+    keys / values ([B][w][H_kv][d] each) go into cache rows n_b .. n_b + w - 1
+    and window query s attends the selected history rows and rows
+    n_b .. n_b + s."""
+    B, w, Hq, D = q.shape
+    kk = 0 if idx is None else (k if k is not None else idx.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    d = kv.desc
+    nbytes = lib().dustin_verify_attn_workspace_bytes(d.B, w, Hq, d.H_kv, d.head_dim,
+                                                      kk if idx is not None else d.N_max)
+    wsb = _ws("verify", ws, nbytes, q.device)
+    _check(lib().dustin_verify_attn_append(_ptr(q), w, Hq, kv.ref, _ptr(k_win), _ptr(v_win), _ptr(idx),
+                                           _ptr(count), kk, float(scale), _ptr(out), _ptr(lse), _ptr(wsb),
+                                           wsb.numel(), _stream(q)))
     return out
 
 

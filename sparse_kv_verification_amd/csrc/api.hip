@@ -163,11 +163,12 @@ size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_
 }  // extern "C"
 
 namespace {
-// Shared body of dustin_sparse_verify_attn (causal = 0) and dustin_verify_attn
-// (causal = 1: the w window rows after each history are attended causally).
-dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
-                        const int32_t *idx, const int32_t *count, int32_t k, float scale, void *out, float *lse,
-                        void *ws, size_t ws_bytes, dustin_stream_t stream, int causal) {
+// Checks and kernel arguments shared by dustin_sparse_verify_attn (causal =
+// 0), dustin_verify_attn and dustin_verify_attn_append (causal = 1: the w
+// window rows after each history are attended causally).  No HIP call.
+dustin_status attn_prepare(const char *name, const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                           const int32_t *idx, const int32_t *count, int32_t k, float scale, void *out,
+                           float *lse, void *ws, size_t ws_bytes, int causal, AttnArgs &a, AttnPlan &p) {
     char what[96];
     snprintf(what, sizeof what, "%s kv", name);
     dustin_status st = check_kv(kv, what, true);
@@ -182,11 +183,11 @@ dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q,
     }
     CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "%s: scale is not finite", name);
     const int tokens = (idx ? k : kv->N_max) + (causal ? w : 0);
-    const AttnPlan p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
+    p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
     CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "%s: too many tokens", name);
     CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
           "%s: workspace of %zu bytes needed (got %zu)", name, p.ws_bytes, ws_bytes);
-    AttnArgs a{};
+    a = AttnArgs{};
     a.kv = view_of(kv);
     a.q = q;
     a.w = w;
@@ -208,6 +209,17 @@ dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q,
     a.tps = p.tps;
     a.rpad = p.rpad;
     a.causal = causal;
+    return DUSTIN_OK;
+}
+
+dustin_status attn_call(const char *name, const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                        const int32_t *idx, const int32_t *count, int32_t k, float scale, void *out, float *lse,
+                        void *ws, size_t ws_bytes, dustin_stream_t stream, int causal) {
+    AttnArgs a;
+    AttnPlan p;
+    dustin_status st = attn_prepare(name, q, w, H_q, kv, idx, count, k, scale, out, lse, ws, ws_bytes, causal, a, p);
+    if (st != DUSTIN_OK) return st;
+    char what[96];
     snprintf(what, sizeof what, "%s launch", name);
     return hip_status(launch_attn(a, p, (hipStream_t)stream), what);
 }
@@ -277,6 +289,31 @@ dustin_status dustin_verify_attn(const void *q, int32_t w, int32_t H_q, const du
                                  const int32_t *count, int32_t k, float scale, void *out, float *lse, void *ws,
                                  size_t ws_bytes, dustin_stream_t stream) {
     return attn_call("verify_attn", q, w, H_q, kv, idx, count, k, scale, out, lse, ws, ws_bytes, stream, 1);
+}
+
+dustin_status dustin_verify_attn_append(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                        const void *k_win, const void *v_win, const int32_t *idx,
+                                        const int32_t *count, int32_t k, float scale, void *out, float *lse,
+                                        void *ws, size_t ws_bytes, dustin_stream_t stream) {
+    CHECK(k_win != nullptr && v_win != nullptr, DUSTIN_ERR_INVALID_ARG,
+          "verify_attn_append: k_win and v_win are required");
+    CHECK(kv != nullptr, DUSTIN_ERR_INVALID_ARG, "verify_attn_append: kv is NULL");
+    CHECK(((uintptr_t)kv->k | (uintptr_t)kv->v | (uintptr_t)k_win | (uintptr_t)v_win) % 16 == 0,
+          DUSTIN_ERR_INVALID_ARG, "verify_attn_append: k, v, k_win and v_win must be 16-byte aligned");
+    AttnArgs a;
+    AttnPlan p;
+    dustin_status st = attn_prepare("verify_attn_append", q, w, H_q, kv, idx, count, k, scale, out, lse, ws,
+                                    ws_bytes, 1, a, p);
+    if (st != DUSTIN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (kv->dtype == DUSTIN_F32) {   // float32 caches: the append, then the attention
+        hipError_t e = launch_append_window(a.kv, k_win, v_win, w, s);
+        if (e != hipSuccess) return hip_status(e, "verify_attn_append: append launch");
+    } else {
+        a.k_win = (const char *)k_win;
+        a.v_win = (const char *)v_win;
+    }
+    return hip_status(launch_attn(a, p, s), "verify_attn_append launch");
 }
 
 dustin_status dustin_append_window_kv(const dustin_kv *kv, const void *k_win, const void *v_win, int32_t w,

@@ -60,6 +60,10 @@ struct AttnArgs {
     int32_t *counters;       // [B * Hkv]
     int32_t splits, tps, rpad;
     int32_t causal;          // 1: the w window rows after the history are attended causally
+    // causal form only, or nullptr: the window rows come from these
+    // [B][w][Hkv][D] inputs, and split 0 of each (b, g) also writes them into
+    // the cache (the append and the attention in one launch)
+    const char *k_win, *v_win;
 };
 
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);

@@ -232,6 +232,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         jv[i] = DENSE ? t0 + t : ((t < a.tps && t0 + t < a.k) ? a.idx[(int64_t)b * a.k + t0 + t] : -1);
     }
     const int nb = min(max(nb_raw, 0), a.kv.N_max);
+    // Fused append: split 0 of (b, g) writes head g of the w window rows into
+    // cache positions n_b .. n_b + w - 1 (positions past N_max and pages
+    // outside [0, num_pages) are skipped, as by the separate append).  The
+    // attention itself reads the window rows from k_win / v_win, so no work-
+    // group depends on these stores.
+    if (CAUSAL && a.k_win != nullptr && split == 0) {
+        constexpr int CH16 = D / 8;   // 16-byte chunks of a head row
+        for (int e = tid; e < a.w * 2 * CH16; e += NT) {
+            const int s = e / (2 * CH16), which = (e / CH16) & 1, ch = e - (e / CH16) * CH16;
+            const int pos = nb + s;
+            if (pos >= a.kv.N_max) continue;
+            int64_t row = (int64_t)b * a.kv.N_max + pos;
+            if (a.kv.page_size != 0) {
+                const int pg = a.kv.page_table[(int64_t)b * a.kv.max_pages + (pos >> 4)];
+                if (pg < 0 || pg >= a.kv.num_pages) continue;
+                row = (int64_t)pg * 16 + (pos & 15);
+            }
+            const int64_t src = ((((int64_t)b * a.w + s) * a.kv.Hkv + g) * D) * 2 + ch * 16;
+            const int64_t dst = ((row * a.kv.Hkv + g) * D) * 2 + ch * 16;
+            const char *from = which ? a.v_win : a.k_win;
+            char *to = const_cast<char *>(which ? a.kv.v : a.kv.k);
+            *(u32x4 *)(to + dst) = *(const u32x4 *)(from + src);
+        }
+    }
     // History tokens of the (b, g) token list come first; with CAUSAL the w
     // draft-window rows (cache positions n_b .. n_b + w - 1) follow them.
     const int hist = DENSE ? nb : min(max(cnt_raw, 0), a.k);
@@ -266,8 +290,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
                     if (a.kv.page_size == 0) r = b * a.kv.N_max + pos[i];
                     else if (pg[i] >= 0 && pg[i] < a.kv.num_pages) r = pg[i] * 16 + (pos[i] & 15);
                 }
+                // fused append: a present window row is read from the input,
+                // coded -2 - s for window step s (-1 stays "absent")
+                if (CAUSAL && a.k_win != nullptr && t >= win_lo && r >= 0) r = -2 - (t - win_lo);
                 rows[t] = r;
-                any_bad |= (r < 0);
+                any_bad |= (r == -1);
             }
         }
     }
@@ -307,6 +334,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
                 const size_t off = (size_t)r[ci] * row_stride + head_off + chunk * 16;
                 kp = kbase + off;
                 vp = vbase + off;
+            } else if (CAUSAL && r[ci] <= -2) {   // window row from the fused-append inputs
+                const size_t off = ((((size_t)b * a.w + (-2 - r[ci])) * a.kv.Hkv + g) * D) * 2 + chunk * 16;
+                kp = a.k_win + off;
+                vp = a.v_win + off;
             } else {
                 kp = vp = (const char *)g_zero_row + chunk * 16;
             }
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = tb + (lane >> 4) * 4 + j;
-                if (!(t < ntok && rows[t] >= 0)) st[j] = kNegInf;
+                if (!(t < ntok && rows[t] != -1)) st[j] = kNegInf;
                 if (CAUSAL && t >= win_lo && t - win_lo > sq) st[j] = kNegInf;
             }
         }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.dustin_abi_version() == 6
+    assert L.dustin_abi_version() == 7
     assert L.dustin_status_string(0) == b"DUSTIN_OK"
     assert L.dustin_status_string(2) == b"DUSTIN_ERR_UNSUPPORTED"
 
@@ -141,6 +141,21 @@ def test_verify_window_argument_errors(L):
     assert va(kv(), ws_bytes=need - 1) == INVALID
     assert b"verify_attn" in L.dustin_last_error()
     assert L.dustin_verify_attn_workspace_bytes(2, 0, 64, 8, 128, 2048) == 0
+
+    def vaa(desc, **kw):
+        return L.dustin_verify_attn_append(kw.get("q", FAKE), kw.get("w", 4), kw.get("Hq", 64), ctypes.byref(desc),
+                                           kw.get("kw", FAKE), kw.get("vw", FAKE), kw.get("idx", FAKE),
+                                           kw.get("count", FAKE), kw.get("k", 2048), 0.0, kw.get("out", FAKE), None,
+                                           FAKE, kw.get("ws_bytes", 1 << 40), None)
+    assert vaa(kv(), kw=None) == INVALID and vaa(kv(), vw=None) == INVALID
+    assert vaa(kv(), kw=FAKE + 8) == INVALID                      # not 16-byte aligned
+    assert b"aligned" in L.dustin_last_error()
+    assert vaa(kv(v=None)) == INVALID
+    assert vaa(kv(), w=9) == UNSUPPORTED
+    assert vaa(kv(), count=None) == INVALID
+    assert vaa(kv(), ws_bytes=need - 1) == INVALID
+    assert vaa(kv(dtype=0), out=None) == INVALID                 # float32: every check before the append
+    assert b"verify_attn_append" in L.dustin_last_error()
 
     def ap(desc, kw_=FAKE, vw=FAKE, w=4):
         return L.dustin_append_window_kv(ctypes.byref(desc), kw_, vw, w, None)

@@ -118,9 +118,11 @@ def test_c5_ragged_paged_step():
 
 
 def test_c4_verify_step_with_window():
-    """The headline shape with the window in the cache: append, score,
-    select, then the causal verification attention, on histories shortened
-    by w so the window fits; sampled sequences against the oracle."""
+    """The headline shape with the window: score, select, then the causal
+    verification attention that appends the window rows to the cache in the
+    same launch (as the bench times it), on histories shortened by w so the
+    window fits; sampled sequences against the oracle, and the appended rows
+    checked in the cache."""
     say("full-size c4 verify step with the window")
     sh = synth.preset("c4").replace(layers=1)
     x = synth.make(sh, device=DEV)
@@ -133,15 +135,16 @@ def test_c4_verify_step_with_window():
     kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
     sample = [3, sh.B - 2]
     hist = {b: (oracle_kv(x, "K", b), oracle_kv(x, "V", b)) for b in sample}
-    dk.dustin_append_window_kv(kv, k_win, v_win)
     n_sink, n_window, m = synth.tier_defaults(sh.k)
     dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
     s_d, s_t = dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq)
     idx, cnt, tier = dk.dustin_topk(s_d, s_t, x.seq_lens, sh.k, m, n_sink, n_window)
     lse = torch.empty((sh.B, sh.w, sh.Hq), dtype=torch.float32, device=DEV)
-    out = dk.dustin_verify_attn(x.q, kv, idx, cnt, lse=lse)
+    out = dk.dustin_verify_attn_append(x.q, kv, k_win, v_win, idx, cnt, lse=lse)
     torch.cuda.synchronize()
     for b in sample:
+        n = int(x.seq_lens[b])
+        assert torch.equal(x.K[b, n:n + sh.w], k_win[b]) and torch.equal(x.V[b, n:n + sh.w], v_win[b])
         K, V = hist[b]
         n = int(x.seq_lens[b])
         c = int(cnt[b])

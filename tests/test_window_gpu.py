@@ -235,3 +235,62 @@ def test_verify_edge_cases():
         lerr = np.abs(f64(lse[b]) - L).max()
         say(f"  b={b} n={n} |I|={len(I)} window rows {fit} max|dO|={err:.2e} max|dlse|={lerr:.2e}")
         assert err <= 2e-2 and lerr <= 2e-3
+
+
+FUSED_CASES = CASES + [
+    ("full-history-qwen72b", dict(B=2, n=3000, Hq=64, Hkv=8, k=600, L_d=1), 600, dict(), False),
+    ("full-history-paged", dict(base="c5", B=3, n=3000, n_lo=800, k=500, L_d=1), 500, dict(), False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_append_matches_separate_calls(case):
+    """dustin_verify_attn_append (one launch for bf16) against
+    dustin_append_window_kv + dustin_verify_attn on identical seeded inputs:
+    out, lse and both caches bit-identical (the unused cache rows hold NaN, so
+    the caches are compared as bit patterns); the fused output also against
+    the oracle.  The full-history cases put some windows past N_max."""
+    name, over, k, iopt = case[:4]
+    room = case[4] if len(case) > 4 else True
+    say("fused append + verify", name)
+    sh, x1, k_win, v_win = _setup(name, over, room=room)
+    _, x2, k_win2, v_win2 = _setup(name, over, room=room)
+    assert torch.equal(k_win, k_win2) and torch.equal(v_win, v_win2)
+    f32 = sh.dtype == "f32"
+    kv1 = dk.KV(x1.K, x1.V, x1.seq_lens, x1.page_table)
+    kv2 = dk.KV(x2.K, x2.V, x2.seq_lens, x2.page_table)
+    if k is None:
+        idx = cnt = None
+    else:
+        idx, cnt = make_idx(x1.seq_lens, k, seed=zlib.crc32(name.encode()) % 1000, device=DEV, **iopt)
+    lse1 = torch.empty((sh.B, sh.w, sh.Hq), dtype=torch.float32, device=DEV)
+    lse2 = torch.empty_like(lse1)
+    dk.dustin_append_window_kv(kv1, k_win, v_win)
+    out1 = dk.dustin_verify_attn(x1.q, kv1, idx, cnt, lse=lse1)
+    out2 = dk.dustin_verify_attn_append(x2.q, kv2, k_win, v_win, idx, cnt, lse=lse2)
+    torch.cuda.synchronize()
+    bits = torch.int32 if f32 else torch.int16
+    assert torch.equal(x1.K.view(bits), x2.K.view(bits)), "K cache differs"
+    assert torch.equal(x1.V.view(bits), x2.V.view(bits)), "V cache differs"
+    assert torch.equal(out1.view(bits), out2.view(bits)), "output differs"
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32)), "lse differs"
+    lens = x2.seq_lens.cpu().numpy()
+    for b in range(sh.B):
+        n = int(lens[b])
+        I = np.arange(n) if idx is None else valid_set(idx[b].cpu().numpy(), int(cnt[b]), n)
+        K, V = oracle_kv(x2, "K", b), oracle_kv(x2, "V", b)
+        # window rows present in the cache: positions below N_max whose page
+        # (paged caches) is allocated; they form a prefix of the window
+        nw = 0
+        while nw < sh.w and n + nw < kv2.desc.N_max:
+            if x2.page_table is not None:
+                pg = int(x2.page_table[b, (n + nw) // sh.page_size])
+                if not 0 <= pg < x2.K.shape[0]:
+                    break
+            nw += 1
+        say(f"  b={b} n={n} |I|={len(I)} window rows in the cache {nw}")
+        if len(I) == 0 and nw == 0:
+            continue
+        O, L = oracle.verify_attention(f64(x2.q[b]), K, V, f64(k_win[b, :nw]), f64(v_win[b, :nw]), I)
+        assert np.abs(f64(out2[b]) - O).max() <= (1e-4 if f32 else 2e-2)
+        assert np.abs(f64(lse2[b]) - L).max() <= (1e-5 if f32 else 2e-3)
