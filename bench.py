@@ -371,10 +371,13 @@ def main():
             "us_per_step_attention": dense_us,
             "GBps": bytes_["dense_per_layer"] * sh.layers / dense_us / 1e3,
             "speedup_sparse_step_vs_dense_attention": dense_us / step_us,
+            # the attention alone: the same L layers over the selected rows only
+            "speedup_sparse_attention_vs_dense_attention": dense_us / (attn_launch_us * sh.layers),
         }
         dense["frac"] = dense["GBps"] / HBM_PEAK_GBPS
         log(f"dense attention {dense_us:.1f} us/step ({dense['GBps']:.0f} GB/s), "
-            f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster")
+            f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster, "
+            f"sparse attention alone {dense['speedup_sparse_attention_vs_dense_attention']:.2f}x")
 
     traffic = measured_traffic()
     step_gbps = bytes_["step"] / step_us / 1e3
