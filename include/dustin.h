@@ -69,7 +69,7 @@ extern "C" {
 typedef enum dustin_status {
     DUSTIN_OK = 0,
     DUSTIN_ERR_INVALID_ARG = 1, /* bad shape, null required pointer, small workspace */
-    DUSTIN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    DUSTIN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement */
     DUSTIN_ERR_HIP = 3          /* a HIP runtime call failed; see dustin_last_error() */
 } dustin_status;
 

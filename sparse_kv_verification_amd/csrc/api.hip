@@ -496,7 +496,7 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
         if (ref->dtype == DUSTIN_F32) {
             CHECK(L_d <= 8 && (int64_t)L_d * H_d * gamma <= kMaxScoreQoff &&
                       (int64_t)L_d * Hkv_d * ((gamma * G_d + 7) / 8) <= kMaxScoreRows,
-                  DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than this build supports");
+                  DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than the library supports");
         }
     }
     TargetScoreArgs ta{};
