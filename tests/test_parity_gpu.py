@@ -196,6 +196,7 @@ SCORE_CASES = [
     ("stream-ragged", dict(base="c2", B=3, n=5000, L_d=4, n_lo=700)),
     ("stream-layer-groups", dict(base="c2", B=2, n=3000, L_d=6, n_lo=1000)),
     ("stream-paged", dict(base="c5", B=3, n=5000, n_lo=1200, L_d=4, w=4)),
+    ("stream-many-groups", dict(base="c2", B=1, n=2048, L_d=24)),          # 12 layer groups
     ("tiny-f32", dict(base="c1")),
 ]
 
@@ -232,6 +233,39 @@ def test_scores_match_oracle(name, over):
         assert abs(gt.sum() - len(sub)) < 1e-3 * len(sub)
         assert abs(gd.sum() - sh.L_d * sh.H_d * sh.w) < 1e-3 * sh.L_d * sh.H_d * sh.w
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
+
+
+@pytest.mark.parametrize("w", [4, 8], ids=["streaming-w4", "register-staged-w8"])
+def test_scores_treat_absent_pages_as_zero_keys(w):
+    """Page ids outside [0, num_pages) inside a sequence: both scores treat
+    those positions as all-zero keys (the documented convention), on the
+    streaming draft path (28 rows) and the register-staged one (56 rows).
+    The oracle gets the logical keys with exactly those rows zeroed."""
+    say("scores with absent pages, w", w)
+    sh = synth.preset("c5").replace(B=2, n=3000, n_lo=1200, L_d=2, w=w)
+    x = synth.make(sh, device=DEV)
+    rng = np.random.default_rng(w)
+    pt = x.page_table.clone()
+    gone = {}
+    for b in range(sh.B):
+        npg = (int(x.seq_lens[b]) + 15) // 16
+        gone[b] = rng.choice(npg - 1, 2, replace=False)
+        pt[b, int(gone[b][0])] = -1
+        pt[b, int(gone[b][1])] = x.K.shape[0] + 7          # past num_pages
+    kvs = [dk.KV(x.K, None, x.seq_lens, pt)]
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens, pt) for l in range(sh.L_d)]
+    s_d, s_t = dk.dustin_score(dkv, x.q_draft, kvs, x.q_hist, x.sub_heads, sh.Hq)
+    torch.cuda.synchronize()
+    for b in range(sh.B):
+        n = int(x.seq_lens[b])
+        K, Kd = oracle_kv(x, "K", b).copy(), oracle_kv(x, "Kd", b).copy()
+        for pg in gone[b]:
+            K[pg * 16:(pg + 1) * 16] = 0.0
+            Kd[:, pg * 16:(pg + 1) * 16] = 0.0
+        st = oracle.score_target(f64(x.q_hist[b]), {0: K}, x.sub_heads, sh.Hq)
+        sd = oracle.score_draft(f64(x.q_draft[b]), Kd)
+        np.testing.assert_allclose(f64(s_t[b, :n]), st, rtol=2e-4, atol=1e-12)
+        np.testing.assert_allclose(f64(s_d[b, :n]), sd, rtol=2e-4, atol=1e-12)
 
 
 @pytest.mark.parametrize("name,over", [
