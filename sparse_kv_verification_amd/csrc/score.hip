@@ -814,26 +814,43 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
 // 4-wave groups per CU.  (Three or four row blocks need one group per CU
 // for their registers; with 64-position stages to keep the bytes in flight
 // they ran no faster than the register-staged kernels, which serve them.)
-template <int RB>
+//
+// Three or four row blocks stream one KV head per item instead (HALF): a
+// stage holds the 128-byte head halves of 64 positions, so it is still
+// 8 KiB, the operands of one head fit two groups per CU, and the two heads'
+// accumulation results are partial sums added by draft_part_sum.
+template <int RB, bool HALF = false>
 struct StreamGeom {
-    static_assert(RB <= 2, "streaming passes: at most two row blocks");
-    static constexpr int POS = 32;                    // positions per stage
-    static constexpr int STAGE = POS * 256;           // bytes per stage
+    static_assert(HALF || RB <= 2, "full-row streaming: at most two row blocks");
+    static constexpr int RBY = HALF ? 128 : 256;      // stage bytes per position
+    static constexpr int POS = 8192 / RBY;            // positions per stage
+    static constexpr int STAGE = 8192;                // bytes per stage
+    static constexpr int NH = HALF ? 1 : 2;           // heads per item
     static constexpr int GROUPS = 512;                // persistent work-groups
 };
+
+// 16-byte chunk swizzle of stage row rho: full rows (16 chunks) by the low
+// four bits; half rows (8 chunks, two rows per 256-byte bank span) by bits
+// 1..3, so the 16 positions of a K-operand read hit 16 distinct bank groups.
+template <bool HALF>
+__device__ __forceinline__ int stream_swz(int rho) {
+    return HALF ? ((rho >> 1) & 7) : (rho & 15);
+}
 constexpr int kStreamGroups = 512;
 
 // DMA of positions j0 .. j0 + 31 of one layer into `stage`; `seq` is the
 // layer's k pointer advanced to the sequence.  Positions past the cache end
 // read the last row (the caller masks them).
-template <int POS>
-__device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast, int lane, uint8_t *stage) {
+template <int POS, bool HALF>
+__device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast, int hoff, int lane, uint8_t *stage) {
+    constexpr int CPR = (HALF ? 128 : 256) / 16;   // chunks per stage row
+    constexpr int PPI = 64 / CPR;                  // positions per instruction
 #pragma unroll
-    for (int i = 0; i < POS / 4; ++i) {
-        const int rho = i * 4 + (lane >> 4);
-        const int chunk = (lane & 15) ^ (rho & 15);
+    for (int i = 0; i < 8; ++i) {
+        const int rho = i * PPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ stream_swz<HALF>(rho);
         const uint32_t j = (uint32_t)min(j0 + rho, jlast);
-        dma16_stream(seq + (j * 256u + (uint32_t)chunk * 16u), stage + i * 1024);
+        dma16_stream(seq + (j * 256u + (uint32_t)hoff + (uint32_t)chunk * 16u), stage + i * 1024);
     }
 }
 
@@ -844,20 +861,22 @@ __device__ __align__(256) uint8_t g_zero_krow[256] = {0};
 // Paged form of stream_issue: stage s of a wave's span, whose POS / 16
 // pages have their ids in lanes (POS / 16) s + 0, 1, .. of `pgv`; `pool` is
 // the layer's k pointer (row r of the pool at r * 256 bytes).
-template <int POS>
-__device__ __forceinline__ void stream_issue_pg(const char *pool, int pgv, int s, int num_pages, int lane,
+template <int POS, bool HALF>
+__device__ __forceinline__ void stream_issue_pg(const char *pool, int pgv, int s, int num_pages, int hoff, int lane,
                                                 uint8_t *stage) {
     constexpr int NP = POS / 16;
+    constexpr int CPR = (HALF ? 128 : 256) / 16;
+    constexpr int PPI = 64 / CPR;
     int pgs[NP];
 #pragma unroll
     for (int k = 0; k < NP; ++k) pgs[k] = __builtin_amdgcn_readlane(pgv, NP * s + k);
 #pragma unroll
-    for (int i = 0; i < POS / 4; ++i) {
-        const int rho = i * 4 + (lane >> 4);   // on page i / 4 of the stage
-        const int chunk = (lane & 15) ^ (rho & 15);
-        const int pg = pgs[i >> 2];
+    for (int i = 0; i < 8; ++i) {
+        const int rho = i * PPI + lane / CPR;   // on page rho / 16 of the stage
+        const int chunk = (lane % CPR) ^ stream_swz<HALF>(rho);
+        const int pg = pgs[(i * PPI) >> 4];
         const char *src = (pg >= 0 && pg < num_pages)
-                              ? pool + (((int64_t)pg * 16 + (rho & 15)) * 256 + chunk * 16)
+                              ? pool + (((int64_t)pg * 16 + (rho & 15)) * 256 + hoff + chunk * 16)
                               : (const char *)g_zero_krow + chunk * 16;
         dma16_stream(src, stage + i * 1024);
     }
@@ -890,30 +909,32 @@ __device__ __forceinline__ void stream_qoff(const DraftScoreArgs &a, int lane, u
     }
 }
 
-template <int RB>
-__device__ __forceinline__ void stream_load_q(const DraftScoreArgs &a, int b, int l, const uint32_t (&qo)[RB],
-                                              bf16x8 (&q)[2][RB][2]) {
+// Q fragments of KV heads h0 .. h0 + NH - 1 of (sequence, draft layer).
+template <int RB, int NH>
+__device__ __forceinline__ void stream_load_q(const DraftScoreArgs &a, int b, int l, int h0, const uint32_t (&qo)[RB],
+                                              bf16x8 (&q)[NH][RB][2]) {
     const uint32_t blk = (uint32_t)(a.gamma * a.H_d * 128);
     const __amdgpu_buffer_rsrc_t r = stream_rsrc((const char *)a.q_draft + ((int64_t)b * a.L_d + l) * blk, blk);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 q[h][rb][kk] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, qo[rb] + kk * 64, h * a.G_d * 128, 0));
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, qo[rb] + kk * 64, (h0 + h) * a.G_d * 128, 0));
 }
 
 // K operand (head h, both k-steps) of 16-position subtile `st` of a stage:
 // lane holds position st * 16 + (lane & 15), d slice kk * 32 + (lane >> 4) * 8.
+template <bool HALF>
 __device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int lane, bf16x8 (&k)[2]) {
     const int rho = st * 16 + (lane & 15);
     uint32_t ad[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const int chunk = h * 8 + kk * 4 + (lane >> 4);
-        ad[kk] = base + rho * 256 + ((chunk ^ (rho & 15)) << 4);
+        const int chunk = (HALF ? 0 : h * 8) + kk * 4 + (lane >> 4);
+        ad[kk] = base + rho * (HALF ? 128 : 256) + ((chunk ^ stream_swz<HALF>(rho)) << 4);
     }
     u32x4 raw[2];
     ds_read_b128_n(ad, raw);
@@ -929,14 +950,17 @@ __device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int l
 // next item's first DMA; items alternate between two named Q sets, so no
 // register copy waits for a pending load.  The cross-wave combine
 // alternates between two LDS buffers, so one barrier per item suffices.
-template <int RB, bool PAGED>
+template <int RB, bool PAGED, bool HALF>
 __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     constexpr int KK = 2;
-    constexpr int POS = StreamGeom<RB>::POS;
+    using GM = StreamGeom<RB, HALF>;
+    constexpr int POS = GM::POS;
+    constexpr int NH = GM::NH;                 // heads per item (HALF: one, item.h)
+    constexpr int NHI = HALF ? 2 : 1;          // items per (b, layer, chunk)
     constexpr int PER_WAVE = kDraftStatChunk / 4;
     constexpr int NSTAGE = PER_WAVE / POS;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][StreamGeom<RB>::STAGE];
-    __shared__ float red[2][4][2][RB * 16][2];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][GM::STAGE];
+    __shared__ float red[2][4][NH][RB * 16][2];
     __shared__ int pref[kDraftStatMaxB + 1];   // chunks below n_b of sequences before b
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int U = a.L_d * 2;
@@ -953,11 +977,12 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
     }
     __syncthreads();
-    const int items = a.L_d * pref[B];
-    struct Item { int b, l, c, nb, jw, nst; const char *seq; int jlast; };
+    const int per = a.L_d * NHI;              // items per chunk of a sequence
+    const int items = per * pref[B];
+    struct Item { int b, l, h, c, nb, jw, nst; const char *seq; int jlast; };
     auto decode = [&](int it) {
         Item x;
-        const int cu = it / a.L_d;             // chunk index over all sequences
+        const int cu = it / per;               // chunk index over all sequences
         int lo = 0, hi = B - 1;                // the b with pref[b] <= cu < pref[b + 1]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -966,9 +991,11 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         }
         x.b = lo;
         const int nbc = pref[lo + 1] - pref[lo];
-        const int r = it - a.L_d * pref[lo];   // within the sequence: layer-major
-        x.l = r / nbc;
-        x.c = r - x.l * nbc;
+        const int r = it - per * pref[lo];     // within the sequence: (layer, head)-major
+        const int u = r / nbc;
+        x.c = r - u * nbc;
+        x.l = u / NHI;
+        x.h = u - x.l * NHI;
         x.nb = sl_len(a.kv[x.l], x.b);
         x.jw = x.c * kDraftStatChunk + wave * PER_WAVE;
         const int left = x.nb - x.jw;
@@ -985,16 +1012,16 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         return PAGED ? stream_load_pg(a.kv[x.l], x.b, x.jw, PER_WAVE / 16, lane) : 0;
     };
     auto issue = [&](const Item &x, int pgv, int s, uint8_t *stage) {
-        if constexpr (PAGED) stream_issue_pg<POS>(x.seq, pgv, s, a.kv[x.l].num_pages, lane, stage);
-        else stream_issue<POS>(x.seq, x.jw + s * POS, x.jlast, lane, stage);
+        if constexpr (PAGED) stream_issue_pg<POS, HALF>(x.seq, pgv, s, a.kv[x.l].num_pages, x.h * 128, lane, stage);
+        else stream_issue<POS, HALF>(x.seq, x.jw + s * POS, x.jlast, x.h * 128, lane, stage);
     };
     // One item on Q set q (page ids pg); requests the next item's Q into qn
     // (page ids into pgn) and, when the next item has stages, its first DMA.
-    auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[2][RB][KK],
-                    bf16x8 (&qn)[2][RB][KK], const int &pg, int &pgn) {
-        float mrun[2][RB][4], zrun[2][RB][4];
+    auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[NH][RB][KK],
+                    bf16x8 (&qn)[NH][RB][KK], const int &pg, int &pgn) {
+        float mrun[NH][RB][4], zrun[NH][RB][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -1011,14 +1038,14 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             const int j0 = cur.jw + s * POS;
             const bool full = j0 + POS <= cur.nb;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int pr = 0; pr < POS / 32; ++pr) {   // pairs of 16-position subtiles
                 f32x4 sc[2][RB];
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     bf16x8 k[2];
-                    stream_kfrag(base, pr * 2 + st, h, lane, k);
+                    stream_kfrag<HALF>(base, pr * 2 + st, h, lane, k);
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1047,12 +1074,12 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             slot ^= 1;
         };
         if (cur.nst == 0) {
-            stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
+            stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
             pgn = load_pg(nxt);
             if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot]);
         } else {
             wait_vmcnt<0>();
-            stream_load_q<RB>(a, nxt.b, nxt.l, qo, qn);
+            stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
             pgn = load_pg(nxt);
             next_dma(0);
             stage(0);
@@ -1064,7 +1091,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         }
         // combine the 16 token lanes of each row, then the four waves
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -1079,7 +1106,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     }
                 }
         lds_barrier();   // the next item's requests stay in flight
-        if (threadIdx.x < 2 * a.rows) {
+        if (threadIdx.x < NH * a.rows) {
             const int h = threadIdx.x / a.rows, r = threadIdx.x - h * a.rows;
             float mx = kNegInf;
 #pragma unroll
@@ -1088,7 +1115,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             float z = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) z += red[par][w][h][r][1] * __builtin_amdgcn_exp2f(red[par][w][h][r][0] - mu);
-            float *st = a.stat + ((((int64_t)cur.b * U + cur.l * 2 + h) * a.rows + r) * nch + cur.c) * 2;
+            float *st = a.stat + ((((int64_t)cur.b * U + cur.l * 2 + cur.h + h) * a.rows + r) * nch + cur.c) * 2;
             st[0] = mx;
             st[1] = z;
         }
@@ -1096,9 +1123,9 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     };
     int it = blockIdx.x;
     if (it >= items) return;
-    bf16x8 qA[2][RB][KK], qB[2][RB][KK];
+    bf16x8 qA[NH][RB][KK], qB[NH][RB][KK];
     Item cur = decode(it);
-    stream_load_q<RB>(a, cur.b, cur.l, qo, qA);
+    stream_load_q<RB, NH>(a, cur.b, cur.l, cur.h, qo, qA);
     int pgA = load_pg(cur), pgB = 0;
     if (cur.nst > 0) issue(cur, pgA, 0, ring[wave][slot]);
     for (;;) {
@@ -1128,14 +1155,17 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
 // register sets, so no register copy waits for a pending load.  Each stage
 // adds sum_{head, row} exp2(logit - lse) for its 32 positions to a
 // wave-private LDS accumulator, in layer order, so S_Draft needs no atomics.
-template <int RB, bool PAGED>
+template <int RB, bool PAGED, bool HALF>
 __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     constexpr int KK = 2;
     constexpr int CHUNK = 1024;
-    constexpr int POS = StreamGeom<RB>::POS;
+    using GM = StreamGeom<RB, HALF>;
+    constexpr int POS = GM::POS;
+    constexpr int NH = GM::NH;                 // heads per item (HALF: one)
+    constexpr int NHI = HALF ? 2 : 1;          // items per (b, chunk, layer group)
     constexpr int PER_WAVE = CHUNK / 4;
     constexpr int NSTAGE = PER_WAVE / POS;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][StreamGeom<RB>::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][GM::STAGE];
     __shared__ float accs[4][PER_WAVE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
@@ -1152,8 +1182,9 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
         for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
     }
     __syncthreads();
-    const int items = pref[B] * LG;
-    if (LG == 1) {   // chunks wholly past n_b: S_Draft = 0 (with layer groups draft_part_sum writes them)
+    const int GT = LG * NHI;                   // partial groups: (layer group, head)
+    const int items = pref[B] * GT;
+    if (GT == 1) {   // chunks wholly past n_b: S_Draft = 0 (with layer groups draft_part_sum writes them)
         for (int bb = 0; bb < B; ++bb) {
             const int j0 = (pref[bb + 1] - pref[bb]) * CHUNK;
             for (int j = j0 + blockIdx.x * 256 + (int)threadIdx.x; j < N; j += gridDim.x * 256)
@@ -1179,19 +1210,21 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
         lok[rb] = r4 < a.rows;
         lo[rb] = (uint32_t)(lok[rb] ? r4 : 0) * 4u;
     }
-    auto load_lse = [&](int b, int l, f32x4 (&ls)[2][RB]) {
+    auto load_lse = [&](int b, int l, int h0, f32x4 (&ls)[NH][RB]) {
         const __amdgpu_buffer_rsrc_t lr =
             stream_rsrc(a.lse + ((int64_t)b * U + l * 2) * a.rows, (uint32_t)(2 * a.rows * sizeof(float)));
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                ls[h][rb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, lo[rb], h * a.rows * 4, 0));
+                ls[h][rb] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, lo[rb], (h0 + h) * a.rows * 4, 0));
     };
     float *acc = accs[wave];
     int slot = 0;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int bc = it / LG, g = it - (it / LG) * LG;
+        const int bc = it / GT, gt = it - (it / GT) * GT;
+        const int g = gt / NHI, h0 = gt - (gt / NHI) * NHI;   // layer group, head (HALF)
         int lo = 0, hi = B - 1;   // the b with pref[b] <= bc < pref[b + 1]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -1212,25 +1245,25 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
             // pages) in each layer, one per lane, loaded with the layer's Q
             auto load_pg = [&](int l) -> int { return PAGED ? stream_load_pg(a.kv[l], b, jw, PER_WAVE / 16, lane) : 0; };
             auto issue = [&](int l, const char *kl, int pgv, int s, uint8_t *stage) {
-                if constexpr (PAGED) stream_issue_pg<POS>(kl, pgv, s, a.kv[l].num_pages, lane, stage);
-                else stream_issue<POS>(kl, jw + s * POS, N - 1, lane, stage);
+                if constexpr (PAGED) stream_issue_pg<POS, HALF>(kl, pgv, s, a.kv[l].num_pages, h0 * 128, lane, stage);
+                else stream_issue<POS, HALF>(kl, jw + s * POS, N - 1, h0 * 128, lane, stage);
             };
-            bf16x8 qA[2][RB][KK], qB[2][RB][KK];
-            f32x4 lA[2][RB], lB[2][RB];
+            bf16x8 qA[NH][RB][KK], qB[NH][RB][KK];
+            f32x4 lA[NH][RB], lB[NH][RB];
             int pA = 0, pB = 0;
-            stream_load_q<RB>(a, b, l0, qo, qA);
-            load_lse(b, l0, lA);
+            stream_load_q<RB, NH>(a, b, l0, h0, qo, qA);
+            load_lse(b, l0, h0, lA);
             pA = load_pg(l0);
             issue(l0, a.kv[l0].k + seq0, pA, 0, ring[wave][slot]);
-            auto stage = [&](int s, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB]) {
+            auto stage = [&](int s, const bf16x8 (&q)[NH][RB][KK], const f32x4 (&ls)[NH][RB]) {
                 const uint32_t base = lds_addr(ring[wave][slot]);
 #pragma unroll
                 for (int s16 = 0; s16 < POS / 16; ++s16) {
                     float t = 0.f;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < NH; ++h) {
                         bf16x8 k[2];
-                        stream_kfrag(base, s16, h, lane, k);
+                        stream_kfrag<HALF>(base, s16, h, lane, k);
 #pragma unroll
                         for (int rb = 0; rb < RB; ++rb) {
                             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -1248,8 +1281,8 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                 }
                 slot ^= 1;
             };
-            auto layer = [&](int l, const bf16x8 (&q)[2][RB][KK], const f32x4 (&ls)[2][RB], const int &pg,
-                             bf16x8 (&qn)[2][RB][KK], f32x4 (&lsn)[2][RB], int &pgn) {
+            auto layer = [&](int l, const bf16x8 (&q)[NH][RB][KK], const f32x4 (&ls)[NH][RB], const int &pg,
+                             bf16x8 (&qn)[NH][RB][KK], f32x4 (&lsn)[NH][RB], int &pgn) {
                 // both layers' cache pointers from uniform indices (scalar
                 // loads, outside the vector-load order)
                 const int ln = (l + 1 < l1) ? l + 1 : l;
@@ -1260,8 +1293,8 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                     else if (l + 1 < l1) issue(ln, kn, pgn, 0, ring[wave][slot ^ 1]);
                 };
                 wait_vmcnt<0>();
-                stream_load_q<RB>(a, b, ln, qo, qn);
-                load_lse(b, ln, lsn);
+                stream_load_q<RB, NH>(a, b, ln, h0, qo, qn);
+                load_lse(b, ln, h0, lsn);
                 pgn = load_pg(ln);
                 next_dma(0);
                 stage(0, q, ls);
@@ -1276,7 +1309,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                 layer(l + 1, qB, lB, pB, qA, lA, pA);
             }
         }
-        float *out = (LG == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)g * k0.B + b) * N;
+        float *out = (GT == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)gt * k0.B + b) * N;
 #pragma unroll
         for (int i = 0; i < PER_WAVE / 64; ++i) {
             const int j = jw + lane + 64 * i;
@@ -1334,7 +1367,10 @@ ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int H
     off = align_up(off + (size_t)B * drows * sizeof(float), 256);
     p.acc_groups = draft_acc_groups(B, N_max, L_d);
     p.off_dpart = off;
-    if (p.acc_groups > 1) off = align_up(off + (size_t)p.acc_groups * B * N_max * sizeof(float), 256);
+    // partial sums per (layer group, head): the one-head-per-item form
+    // doubles the groups (its use depends on the draft's head geometry, which
+    // the workspace query does not carry, so the space is always reserved)
+    if (L_d >= 2) off = align_up(off + (size_t)2 * p.acc_groups * B * N_max * sizeof(float), 256);
     p.ws_bytes = off;
     return p;
 }
@@ -1464,15 +1500,17 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
 }
 
 // Streaming passes: two 64-wide draft KV heads, an even number of draft
-// layers and a row count that is a multiple of four; contiguous or paged.
-template <int RB, bool PAGED>
+// layers and a row count that is a multiple of four; contiguous or paged;
+// HALF (three or four row blocks): one KV head per item.
+template <int RB, bool PAGED, bool HALF>
 static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     DraftScoreArgs b = a;
     b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
-    const int stat_items = k0.B * a.L_d * b.nchunk;
-    constexpr int GROUPS = StreamGeom<RB>::GROUPS;
-    hipLaunchKernelGGL((draft_stats_stream<RB, PAGED>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
+    constexpr int NHI = HALF ? 2 : 1;
+    const int stat_items = k0.B * a.L_d * NHI * b.nchunk;
+    constexpr int GROUPS = StreamGeom<RB, HALF>::GROUPS;
+    hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
                        dim3(256), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1480,10 +1518,11 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
                        a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int groups = a.acc_groups > 1 ? a.acc_groups : 1;
-    b.acc_groups = groups;
+    const int lg = a.acc_groups > 1 ? a.acc_groups : 1;
+    b.acc_groups = lg;
+    const int groups = lg * NHI;   // partial sums: (layer group, head)
     const int acc_items = k0.B * ((k0.N_max + 1023) / 1024) * groups;
-    hipLaunchKernelGGL((draft_acc_stream<RB, PAGED>), dim3(acc_items < GROUPS ? acc_items : GROUPS),
+    hipLaunchKernelGGL((draft_acc_stream<RB, PAGED, HALF>), dim3(acc_items < GROUPS ? acc_items : GROUPS),
                        dim3(256), 0, s, b);
     if ((e = hipGetLastError()) != hipSuccess || groups == 1) return e;
     const int64_t n = (int64_t)k0.B * k0.N_max;
@@ -1496,9 +1535,10 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
 template <int D, int RB>
 static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
-    if constexpr (D == 64 && RB <= 2) {
+    if constexpr (D == 64) {
+        constexpr bool HALF = RB >= 3;
         if (a.Hkv_d == 2 && a.L_d % 2 == 0 && a.rows % 4 == 0)
-            return k0.page_size == 0 ? draft_stream_impl<RB, false>(a, s) : draft_stream_impl<RB, true>(a, s);
+            return k0.page_size == 0 ? draft_stream_impl<RB, false, HALF>(a, s) : draft_stream_impl<RB, true, HALF>(a, s);
     }
     const int U = a.L_d * a.Hkv_d;
     DraftScoreArgs b = a;
