@@ -197,6 +197,8 @@ SCORE_CASES = [
     ("stream-layer-groups", dict(base="c2", B=2, n=3000, L_d=6, n_lo=1000)),
     ("stream-paged", dict(base="c5", B=3, n=5000, n_lo=1200, L_d=4, w=4)),
     ("stream-many-groups", dict(base="c2", B=1, n=2048, L_d=24)),          # 12 layer groups
+    ("stream-one-head-rb4", dict(base="c4", B=2, n=3000, L_d=2, w=8)),      # 56 rows: one KV head per item
+    ("stream-one-head-rb3", dict(base="c2", B=2, n=2500, n_lo=900, L_d=4, w=6)),   # 42 rows, ragged
     ("tiny-f32", dict(base="c1")),
 ]
 
@@ -235,11 +237,12 @@ def test_scores_match_oracle(name, over):
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
 
 
-@pytest.mark.parametrize("w", [4, 8], ids=["streaming-w4", "register-staged-w8"])
+@pytest.mark.parametrize("w", [4, 8], ids=["both-heads-per-item-w4", "one-head-per-item-w8"])
 def test_scores_treat_absent_pages_as_zero_keys(w):
     """Page ids outside [0, num_pages) inside a sequence: both scores treat
     those positions as all-zero keys (the documented convention), on the
-    streaming draft path (28 rows) and the register-staged one (56 rows).
+    streaming draft passes with both KV heads per item (28 rows) and with
+    one KV head per item (56 rows).
     The oracle gets the logical keys with exactly those rows zeroed."""
     say("scores with absent pages, w", w)
     sh = synth.preset("c5").replace(B=2, n=3000, n_lo=1200, L_d=2, w=w)
