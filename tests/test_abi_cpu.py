@@ -276,3 +276,24 @@ def test_binding_refuses_host_tensors():
         dk.KV(torch.zeros((2, 8, 1, 32), dtype=torch.bfloat16), None, lens)
     with pytest.raises(TypeError):
         dk.dustin_window_mean(torch.zeros((2, 3, 8)))
+
+
+def test_missing_library_fails_loudly():
+    """No fallback: with the library absent, every entry point raises
+    instead of computing anything elsewhere (run in a fresh interpreter so
+    the already-loaded library of this process is not involved)."""
+    import subprocess
+    import sys
+    code = (
+        "import torch, sparse_kv_verification_amd._lib as L\n"
+        "L.LIB_PATH = '/nonexistent/libdustin.so'\n"
+        "L._lib = None\n"
+        "try:\n"
+        "    L.dustin_topk(torch.zeros(1, 8), torch.zeros(1, 8), torch.full((1,), 8, dtype=torch.int32), 4, 1, 0, 0)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', 'is missing' in str(e))\n"
+        "else:\n"
+        "    print('no error')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert "raised: True" in r.stdout, r.stdout + r.stderr
