@@ -331,6 +331,21 @@ def test_score_head_to_kv_mapping_and_scale():
     expect = np.full(n, 1.0 / n)
     expect[p] += 1.0
     np.testing.assert_allclose(st, expect, rtol=0, atol=1e-14)
+    # S_Target's scale 1/sqrt(d): two keys with raw logits 3 and 1 at d = 4
+    # give p0 = sigmoid((3 - 1) / 2) for a scored head.  Pair (2, 6) is head 6
+    # of layer 2, in KV group 1 (6 // 4; a modulo map gives group 0, whose
+    # keys differ); pair (0, 0) reads layer 0's group 0, whose two keys are
+    # equal (uniform 1/2).  Layer 0's group 1 holds yet other keys, so reading
+    # the wrong layer for either pair moves the result as well.
+    K0 = np.zeros((2, Hkv, d))
+    K0[0, 1, 0] = 5.0
+    K2 = np.zeros((2, Hkv, d))
+    K2[:, 1, 0] = [3.0, 1.0]
+    K2[1, 0, 0] = 9.0
+    qh = np.array([[1.0, 0, 0, 0], [1.0, 0, 0, 0]])
+    st = oracle.score_target(qh, {0: K0, 2: K2}, [(0, 0), (2, 6)], Hq)
+    p0 = 1.0 / (1.0 + math.exp(-1.0))
+    np.testing.assert_allclose(st, [0.5 + p0, 0.5 + 1 - p0], rtol=1e-14)
     # scale 1/sqrt(d_d): two keys with raw logits 2 and 0 -> p0 = sigmoid(2/2)
     qd = np.zeros((1, 1, 4, 4))
     qd[0, 0, :, 0] = 2.0
