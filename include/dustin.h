@@ -41,7 +41,8 @@
  *   [0, num_pages) are treated as absent (never dereferenced).
  * - Workspace: pass at least the byte count the matching *_workspace_bytes()
  *   function returns for the same shape.  dustin_sparse_verify_attn,
- *   dustin_verify_attn, dustin_window_attn and dustin_policy_sweep keep
+ *   dustin_verify_attn, dustin_verify_attn_append, dustin_window_attn and
+ *   dustin_policy_sweep keep
  *   arrival counters in the first 64 KiB of their workspace (one slot per
  *   (sequence, KV head), so B * H_kv <= 16384): that region must be
  *   zero-filled before its first

@@ -810,15 +810,16 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
 // loads on the way (Q fragments, row normalisers, lengths) complete in order
 // with the DMA, and every stage starts with a full vmcnt wait, so a stage
 // never reads LDS before its own bytes have landed.
-// Up to two row blocks per KV head: 32-position (8 KiB) stages and two
-// 4-wave groups per CU.  (Three or four row blocks need one group per CU
-// for their registers; with 64-position stages to keep the bytes in flight
-// they ran no faster than the register-staged kernels, which serve them.)
+// Up to two row blocks per KV head: 32-position (8 KiB) stages of full
+// position rows (both KV heads) and two 4-wave groups per CU.
 //
-// Three or four row blocks stream one KV head per item instead (HALF): a
-// stage holds the 128-byte head halves of 64 positions, so it is still
-// 8 KiB, the operands of one head fit two groups per CU, and the two heads'
-// accumulation results are partial sums added by draft_part_sum.
+// Three or four row blocks stream one KV head per item (HALF): a stage holds
+// the 128-byte head halves of 64 positions, so it is still 8 KiB, the
+// operands of one head fit two groups per CU, and the two heads'
+// accumulation results are partial sums added by draft_part_sum.  (A
+// full-row form at one group per CU, with 64-position stages to keep the
+// bytes in flight, had run no faster than the register-staged kernels,
+// which now serve only the geometries neither streaming form covers.)
 template <int RB, bool HALF = false>
 struct StreamGeom {
     static_assert(HALF || RB <= 2, "full-row streaming: at most two row blocks");
@@ -838,9 +839,10 @@ __device__ __forceinline__ int stream_swz(int rho) {
 }
 constexpr int kStreamGroups = 512;
 
-// DMA of positions j0 .. j0 + 31 of one layer into `stage`; `seq` is the
-// layer's k pointer advanced to the sequence.  Positions past the cache end
-// read the last row (the caller masks them).
+// DMA of the POS positions j0 .. j0 + POS - 1 of one layer into `stage` (32
+// full rows, or 64 head halves when HALF); `seq` is the layer's k pointer
+// advanced to the sequence.  Positions past the cache end read the last row
+// (the caller masks them).
 template <int POS, bool HALF>
 __device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast, int hoff, int lane, uint8_t *stage) {
     constexpr int CPR = (HALF ? 128 : 256) / 16;   // chunks per stage row

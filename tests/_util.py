@@ -38,6 +38,74 @@ def make_idx(seq_lens, k, seed, frac_invalid=0.0, short=0, shuffle=True, device=
     return torch.from_numpy(idx).to(device), torch.from_numpy(cnt).to(device)
 
 
+def assert_scores_close(got, want, what="scores", rel=1e-5, abs_=1e-9):
+    """Score parity bar: |got - want| <= rel * want + abs_ elementwise (fp32
+    accumulation of bf16 products and an fp32 log-sum-exp against fp64)."""
+    got, want = np.asarray(got, dtype=np.float64), np.asarray(want, dtype=np.float64)
+    excess = np.abs(got - want) - (rel * np.abs(want) + abs_)
+    if excess.size and excess.max() > 0:
+        j = int(np.argmax(excess))
+        raise AssertionError(f"{what}: position {j} got {got[j]!r} want {want[j]!r} "
+                             f"(|d| = {abs(got[j] - want[j]):.3e} > {rel:g} * want + {abs_:g}); "
+                             f"{int((excess > 0).sum())} positions outside the bar")
+
+
+def max_rel_err(got, want, floor=1e-6):
+    """Largest |got - want| / want over positions with want >= floor (report only)."""
+    got, want = np.asarray(got, dtype=np.float64), np.asarray(want, dtype=np.float64)
+    sel = want >= floor
+    return float((np.abs(got - want)[sel] / want[sel]).max()) if sel.any() else 0.0
+
+
+def tieband_range(rank, value, k, rel=1e-5):
+    """Range of sum(value[I]) over every size-min(k, n) set I that a TopK of
+    `rank` may return when ties within `rel` (relative) of the k-th largest
+    rank may fall either way: the positions ranked strictly above the band
+    are in every such set, the rest come from the band.  Returns (lo, hi,
+    number of band positions beyond the ones needed)."""
+    rank, value = np.asarray(rank, dtype=np.float64), np.asarray(value, dtype=np.float64)
+    n = rank.size
+    if k >= n:
+        v = float(value.sum())
+        return v, v, 0
+    th = np.sort(rank)[::-1][k - 1]
+    sure = rank > th + rel * abs(th)
+    band = np.abs(rank - th) <= rel * abs(th)
+    need = k - int(sure.sum())
+    bv = np.sort(value[band])
+    base = float(value[sure].sum())
+    return base + float(bv[:need].sum()), base + float(bv[::-1][:need].sum()), int(band.sum()) - need
+
+
+def check_sweep_rows(got, want, A, q_past, K, ks, tol=1e-4):
+    """Policy-sweep rows (oracle.policy_sweep's layout) of one sequence:
+    rows ranked by score vectors both sides share must match the oracle within
+    tol; the SD-oracle and history rows, ranked by attention each side computes
+    itself, must lie within tol of the windowed-ARR range of the sets that the
+    1e-5 tie band allows.  got, want [P + 5][len(ks)]; A the oracle's window
+    attention (Eq. 1), q_past [P][Hq][d].  Returns (entries checked against
+    the oracle's value, entries checked against a tie-band range)."""
+    P = q_past.shape[0]
+    Abar = A.mean(axis=0)
+    rank = [Abar] + [oracle.window_attention(q_past[p][None], K)[0] for p in range(P)]
+    exact = banded = 0
+    for row in range(P + 5):
+        for ki, k in enumerate(ks):
+            v = got[row, ki]
+            assert 0.0 <= v <= 1.0 + 1e-5
+            lo = hi = want[row, ki]
+            spare = 0
+            if row <= P:        # ranked by attention each side computes itself
+                lo, hi, spare = tieband_range(rank[row], Abar, k)
+                assert lo - 1e-12 <= want[row, ki] <= hi + 1e-12
+            if spare:
+                banded += 1
+            else:
+                exact += 1
+            assert lo - tol <= v <= hi + tol, (row, k, v, want[row, ki], lo, hi)
+    return exact, banded
+
+
 def valid_set(idx_row, cnt, n):
     s = idx_row[:cnt]
     return s[(s >= 0) & (s < n)]

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import sparse_kv_verification_amd as dk
-from _util import check_set_tieband, check_tier_rule, f64, oracle_kv, say
+from _util import assert_scores_close, check_set_tieband, check_sweep_rows, check_tier_rule, f64, max_rel_err, oracle_kv, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -51,8 +51,10 @@ def _check(sh, x, k, sample):
         K = oracle_kv(x, "K", b)
         st = oracle.score_target(f64(x.q_hist[b]), {0: K}, x.sub_heads, sh.Hq)
         sd = oracle.score_draft(f64(x.q_draft[b]), oracle_kv(x, "Kd", b))
-        np.testing.assert_allclose(f64(s_t[b, :n]), st, rtol=2e-4, atol=1e-12)
-        np.testing.assert_allclose(f64(s_d[b, :n]), sd, rtol=2e-4, atol=1e-12)
+        assert_scores_close(f64(s_t[b, :n]), st, "S_Target")
+        assert_scores_close(f64(s_d[b, :n]), sd, "S_Draft")
+        say(f"  b={b} max rel|dS_T|={max_rel_err(f64(s_t[b, :n]), st):.2e} "
+            f"rel|dS_D|={max_rel_err(f64(s_d[b, :n]), sd):.2e} (S >= 1e-6)")
         oi, ot = oracle.select_verify_set(sd, st, n, k, m, n_sink, n_window)
         c = int(cnt[b])
         nd = check_set_tieband(idx[b, :c].cpu().numpy(), tier[b, :c].cpu().numpy(), oi, ot, sd, st)
@@ -191,12 +193,6 @@ def test_c4_policy_sweep():
         K = oracle_kv(x, "K", b)
         want = oracle.policy_sweep(f64(x.q[b]), f64(qpast[:, b]), K, f64(sd[b]), f64(st[b]), ks, ms, 4, 32)
         A = oracle.window_attention(f64(x.q[b]), K)
-        rank = [A.mean(axis=0)] + [oracle.window_attention(f64(qpast[p, b])[None], K)[0] for p in range(P)]
-        for row in range(P + 5):
-            for ki, k in enumerate(ks):
-                s = np.sort(rank[row])[::-1] if row <= P else None
-                if s is not None and (s[k - 1] - s[k]) / s[k - 1] < 2e-4:
-                    assert arr[row, ki, b] <= want[0, ki] + 1e-4
-                    continue
-                assert abs(arr[row, ki, b] - want[row, ki]) <= 1e-4, (b, row, k)
-        say(f"  b={b} k=2048: oracle {want[0, -1]:.4f} history {np.round(want[1:P + 1, -1], 4)}")
+        e, t = check_sweep_rows(arr[:, :, b], want, A, f64(qpast[:, b]), K, ks)
+        say(f"  b={b} k=2048: oracle {want[0, -1]:.4f} history {np.round(want[1:P + 1, -1], 4)}; "
+            f"entries with one correct set {e}, with ties inside the 1e-5 band {t}")

@@ -8,8 +8,9 @@ Tolerances (from the benchmark spec and the arithmetic):
   index sets         bit-exact when the oracle's tier rule runs on the GPU's
                      own scores; against the fp64 oracle scores, differences
                      only within 1e-5 relative of a tier threshold
-  scores             relative 2e-4: fp32 accumulation of bf16 products and
-                     an fp32 log-sum-exp over up to 131072 positions
+  scores             |d| <= 1e-5 * S + 1e-9 per position: fp32 accumulation
+                     of bf16 products and an fp32 log-sum-exp over up to
+                     131072 positions, against fp64
   window weights A   abs 1e-5 (each weight <= 1); ARR abs 1e-4
 """
 import zlib
@@ -21,7 +22,7 @@ import torch
 import oracle
 import synth
 import sparse_kv_verification_amd as dk
-from _util import check_set_tieband, f64, make_idx, oracle_kv, say, valid_set
+from _util import assert_scores_close, check_set_tieband, f64, make_idx, max_rel_err, oracle_kv, say, valid_set
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -198,7 +199,10 @@ SCORE_CASES = [
     ("stream-paged", dict(base="c5", B=3, n=5000, n_lo=1200, L_d=4, w=4)),
     ("stream-many-groups", dict(base="c2", B=1, n=2048, L_d=24)),          # 12 layer groups
     ("stream-one-head-rb4", dict(base="c4", B=2, n=3000, L_d=2, w=8)),      # 56 rows: one KV head per item
-    ("stream-one-head-rb3", dict(base="c2", B=2, n=2500, n_lo=900, L_d=4, w=6)),   # 42 rows, ragged
+    # 12 draft heads over 2 KV heads, 6 steps: 36 rows, one KV head per item, ragged
+    ("stream-one-head-rb3", dict(base="c2", B=2, n=2500, n_lo=900, L_d=4, H_d=12, w=6)),
+    # 56 rows, one KV head per item, 8 layers in 4 groups: 8 (group, head) partials
+    ("stream-one-head-groups", dict(base="c4", B=1, n=2048, L_d=8, w=8)),
     ("tiny-f32", dict(base="c1")),
 ]
 
@@ -227,11 +231,11 @@ def test_scores_match_oracle(name, over):
         st = oracle.score_target(f64(q_hist[b]), {0: K}, sub, sh.Hq)
         sd = oracle.score_draft(f64(x.q_draft[b]), oracle_kv(x, "Kd", b))
         gt, gd = f64(s_t[b, :n]), f64(s_d[b, :n])
-        rt = np.abs(gt - st).max() / st.max()
-        rd = np.abs(gd - sd).max() / sd.max()
-        say(f"  b={b} n={n} rel|dS_T|={rt:.2e} rel|dS_D|={rd:.2e} sums {gt.sum():.5f}/{len(sub)} {gd.sum():.4f}/{sh.L_d*sh.H_d*sh.w}")
-        np.testing.assert_allclose(gt, st, rtol=2e-4, atol=1e-12)
-        np.testing.assert_allclose(gd, sd, rtol=2e-4, atol=1e-12)
+        rt, rd = max_rel_err(gt, st), max_rel_err(gd, sd)
+        say(f"  b={b} n={n} max rel|dS_T|={rt:.2e} rel|dS_D|={rd:.2e} (S >= 1e-6) "
+            f"sums {gt.sum():.5f}/{len(sub)} {gd.sum():.4f}/{sh.L_d*sh.H_d*sh.w}")
+        assert_scores_close(gt, st, "S_Target")
+        assert_scores_close(gd, sd, "S_Draft")
         assert abs(gt.sum() - len(sub)) < 1e-3 * len(sub)
         assert abs(gd.sum() - sh.L_d * sh.H_d * sh.w) < 1e-3 * sh.L_d * sh.H_d * sh.w
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
@@ -267,8 +271,8 @@ def test_scores_treat_absent_pages_as_zero_keys(w):
             Kd[:, pg * 16:(pg + 1) * 16] = 0.0
         st = oracle.score_target(f64(x.q_hist[b]), {0: K}, x.sub_heads, sh.Hq)
         sd = oracle.score_draft(f64(x.q_draft[b]), Kd)
-        np.testing.assert_allclose(f64(s_t[b, :n]), st, rtol=2e-4, atol=1e-12)
-        np.testing.assert_allclose(f64(s_d[b, :n]), sd, rtol=2e-4, atol=1e-12)
+        assert_scores_close(f64(s_t[b, :n]), st, "S_Target")
+        assert_scores_close(f64(s_d[b, :n]), sd, "S_Draft")
 
 
 @pytest.mark.parametrize("name,over", [
@@ -302,10 +306,13 @@ def test_window_attention_and_arr(name, over):
         assert (f64(A[b, :, n:]) == 0).all()
         np.testing.assert_allclose(f64(arr_s[b]), oracle.arr_step(Aref, I), atol=1e-4)
         assert abs(float(arr_w[b]) - oracle.arr_window(Aref, I)) < 1e-4
-        # SD oracle: same set as the oracle's TopK on Abar, up to ties in fp32
+        # SD oracle (Eq. 3-4): the GPU's TopK of its own Abar against the
+        # oracle's set, equal except at ties within 1e-5 of the 64-th score
         sel, arr_orc, Abar_ref = oracle.sd_oracle(Aref, 64)
         g = oi[b, :int(oc[b])].cpu().numpy()
+        nd = check_set_tieband(g, np.full(len(g), 2), sel, np.full(len(sel), 2), None, Abar_ref)
         assert abs(Abar_ref[g].sum() - arr_orc) < 1e-5
+        say(f"    SD-oracle set: {len(g)} positions, {nd} differ (tie band)")
 
 
 def test_window_attention_paths_share_a_workspace():

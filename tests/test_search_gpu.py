@@ -3,7 +3,7 @@ per-head S_Target rows, the candidate objective (windowed ARR, Eq. 2, of each
 candidate's verification set, averaged over target layers and the batch),
 greedy target/draft selection and the m search, against the oracle.
 
-Bars: head rows rtol 2e-4 (as S_Target); objectives within 1e-4 (the ARR
+Bars: head rows |d| <= 1e-5 * p + 1e-9 (the S_Target bar); objectives within 1e-4 (the ARR
 bar).  Where the GPU's set inputs are seeded synthetic vectors, they are
 dyadic (multiples of 2^-20 below 1), so base + unit sums are exact in float32
 and both sides select from identical values.  A greedy decision is accepted
@@ -18,7 +18,7 @@ import torch
 import oracle
 import synth
 import sparse_kv_verification_amd as dk
-from _util import f64, say
+from _util import assert_scores_close, f64, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -173,7 +173,7 @@ def test_head_scores_match_oracle():
         torch.cuda.synchronize()
         for b in range(sh.B):
             want = oracle.head_probs(f64(x.q_prev[l, b])[None], f64(x.K[l, b]))[:, 0]     # [Hq][n]
-            np.testing.assert_allclose(f64(rows[:, b]), want, rtol=2e-4, atol=1e-12)
+            assert_scores_close(f64(rows[:, b]), want, f"head rows, layer {l}, b={b}")
 
 
 def _search_gpu(x, sh, k, m0, ms, ns, nw, T, S, max_draft):

@@ -5,10 +5,12 @@ the oracle's policy_sweep on the same seeded inputs.
 
 S_Draft / S_Target are seeded synthetic scores (rounded to float32, the
 precision the GPU selects in), so both sides select those rows from identical
-values.  The oracle and history rows rank positions by attention each side
-computes itself (float32 vs float64): where the oracle's k-th and (k+1)-th
-scores lie within 2e-4 relative, several sets are correct and the entry is
-only checked to be a valid ARR.  Bar: ARR within 1e-4.
+values and must agree within the ARR bar, 1e-4.  The oracle and history rows
+rank positions by attention each side computes itself (float32 vs float64):
+the index-set rule lets positions whose rank score lies within 1e-5 (relative)
+of the k-th score fall either way, so those entries must lie within 1e-4 of
+the range of windowed ARRs that such sets reach (computed exactly from the
+oracle's values); every other entry within 1e-4 of the oracle's value.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ import torch
 import oracle
 import synth
 import sparse_kv_verification_amd as dk
-from _util import f64, oracle_kv, say
+from _util import check_sweep_rows, f64, oracle_kv, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -38,13 +40,6 @@ def _scores(sh, x, kv, seed):
     return sd.contiguous(), st.contiguous()
 
 
-def _boundary_gap(scores, k):
-    s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
-    if k >= s.size:
-        return np.inf
-    return (s[k - 1] - s[k]) / max(s[k - 1], 1e-300)
-
-
 def _check(sh, x, deltas, ks, sample, n_sink=4, n_window=32):
     qpast = synth.history_trajectory(x, deltas)
     kv = dk.KV(x.K, x.V, x.seq_lens, x.page_table)
@@ -56,28 +51,18 @@ def _check(sh, x, deltas, ks, sample, n_sink=4, n_window=32):
     assert torch.equal(arr, arr2), "not deterministic"
     g = arr.cpu().numpy().astype(np.float64)          # [P + 5][nk][B]
     P = len(deltas)
-    checked = skipped = 0
+    exact = banded = 0
     for b in sample:
         n = int(x.seq_lens[b])
         K = oracle_kv(x, "K", b)
         sdb, stb = f64(sd[b, :n]), f64(st[b, :n])
         want = oracle.policy_sweep(f64(x.q[b]), f64(qpast[:, b]), K, sdb, stb, ks, ms, n_sink, n_window)
         A = oracle.window_attention(f64(x.q[b]), K)
-        rank_scores = [A.mean(axis=0)] + [oracle.window_attention(f64(qpast[p, b])[None], K)[0] for p in range(P)]
-        for row in range(P + 5):
-            for ki, k in enumerate(ks):
-                got = g[row, ki, b]
-                assert 0.0 <= got <= 1.0 + 1e-5
-                if row <= P and _boundary_gap(rank_scores[row], k) < 2e-4:
-                    skipped += 1
-                    assert got <= want[0, ki] + 1e-4       # still bounded by the oracle
-                    continue
-                checked += 1
-                assert abs(got - want[row, ki]) <= 1e-4, (b, row, k, got, want[row, ki])
+        e, t = check_sweep_rows(g[:, :, b], want, A, f64(qpast[:, b]), K, ks)
+        exact, banded = exact + e, banded + t
         say(f"  b={b} n={n} oracle {np.round(want[0], 4)} hist {np.round(want[1:P + 1, -1], 4)} "
             f"draft {want[P + 1, -1]:.4f} T/D/H {np.round(want[P + 2:, -1], 4)} (k={ks[-1]})")
-    say(f"  checked {checked}, near-tie entries {skipped}")
-    assert checked >= 0.8 * (checked + skipped)
+    say(f"  entries with one correct set {exact}, with ties inside the 1e-5 band {banded}")
     return g
 
 
@@ -109,4 +94,5 @@ def test_window_mean_matches_definition():
     A = torch.rand((3, 5, 777), generator=g, device=DEV)
     Abar = dk.dustin_window_mean(A)
     torch.cuda.synchronize()
-    np.testing.assert_allclose(f64(Abar), f64(A).mean(axis=1), rtol=1e-6, atol=1e-9)
+    want = np.stack([oracle.sd_oracle(f64(A[b]), 1)[2] for b in range(A.shape[0])])   # Abar of Eq. (3)
+    np.testing.assert_allclose(f64(Abar), want, rtol=1e-6, atol=1e-9)
