@@ -208,6 +208,28 @@ size_t dustin_attn_workspace_bytes(int32_t B, int32_t w, int32_t H_q, int32_t H_
                                    int32_t head_dim, int32_t k_or_n);
 
 /*
+ * dustin_sparse_verify_attn_noalloc -- dustin_sparse_verify_attn for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * results and errors, minus the workspace.  The call allocates nothing.
+ * Its arrival counters and split partials live in a static device array of
+ * DUSTIN_ATTN_SCRATCH_BYTES per GPU (the library's, held from the first
+ * call on that GPU until the process ends), on the current device; `stream`
+ * must belong to it.  A shape whose workspace
+ * (dustin_attn_workspace_bytes) exceeds that size is refused with
+ * DUSTIN_ERR_UNSUPPORTED before any HIP call.  The first call on a device
+ * also enqueues one small kernel on `stream` that zero-fills the counters;
+ * every call leaves them at zero.  All calls on one GPU share the array:
+ * calls that may overlap in time on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.
+ */
+#define DUSTIN_ATTN_SCRATCH_BYTES (32u << 20)
+dustin_status dustin_sparse_verify_attn_noalloc(const void *q, int32_t w, int32_t H_q,
+                                                const dustin_kv *kv, const int32_t *idx,
+                                                const int32_t *count, int32_t k, float scale,
+                                                void *out, float *lse, dustin_stream_t stream);
+
+/*
  * dustin_append_window_kv -- writes the w draft tokens' keys and values into
  * the target cache right after each history, as Stage 2 of the blog's Fig. 5
  * does before verifying them: row n_b + t of sequence b receives

@@ -21,7 +21,7 @@ STATUS = {0: "DUSTIN_OK", 1: "DUSTIN_ERR_INVALID_ARG", 2: "DUSTIN_ERR_UNSUPPORTE
 EXPORTS = [
     "dustin_score", "dustin_score_workspace_bytes",
     "dustin_topk", "dustin_topk_workspace_bytes",
-    "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes",
+    "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes", "dustin_sparse_verify_attn_noalloc",
     "dustin_verify_attn", "dustin_verify_attn_workspace_bytes", "dustin_verify_attn_append",
     "dustin_append_window_kv", "dustin_commit_window",
     "dustin_window_attn", "dustin_window_attn_workspace_bytes",
@@ -76,6 +76,8 @@ def lib():
         L.dustin_topk_workspace_bytes.restype = sz
         L.dustin_sparse_verify_attn.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.dustin_sparse_verify_attn.restype = ctypes.c_int
+        L.dustin_sparse_verify_attn_noalloc.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp]
+        L.dustin_sparse_verify_attn_noalloc.restype = ctypes.c_int
         L.dustin_attn_workspace_bytes.argtypes = [i32] * 6
         L.dustin_attn_workspace_bytes.restype = sz
         L.dustin_verify_attn.argtypes = [vp, i32, i32, kvp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
@@ -240,6 +242,20 @@ def dustin_sparse_verify_attn(q, kv: KV, idx=None, count=None, k=None, scale=0.0
     wsb = _ws("attn", ws, nbytes, q.device)
     _check(lib().dustin_sparse_verify_attn(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
                                            _ptr(out), _ptr(lse), _ptr(wsb), wsb.numel(), _stream(q)))
+    return out
+
+
+def dustin_sparse_verify_attn_noalloc(q, kv: KV, idx=None, count=None, k=None, scale=0.0, out=None, lse=None):
+    """dustin_sparse_verify_attn without a workspace: the library's static
+    per-GPU scratch holds the split state, and the call allocates nothing
+    (pass `out` to keep the binding from allocating it either).  Calls that
+    overlap on one GPU race."""
+    B, w, Hq, D = q.shape
+    kk = 0 if idx is None else (k if k is not None else idx.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().dustin_sparse_verify_attn_noalloc(_ptr(q), w, Hq, kv.ref, _ptr(idx), _ptr(count), kk, float(scale),
+                                                   _ptr(out), _ptr(lse), _stream(q)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dustin.h"
@@ -166,9 +167,19 @@ namespace {
 // Checks and kernel arguments shared by dustin_sparse_verify_attn (causal =
 // 0), dustin_verify_attn and dustin_verify_attn_append (causal = 1: the w
 // window rows after each history are attended causally).  No HIP call.
+// Workspace layout of one attention call: arrival counters at the start,
+// split partials (m, l, O) at the plan's offsets.
+void bind_attn_workspace(AttnArgs &a, const AttnPlan &p, char *wsb) {
+    a.counters = (int32_t *)wsb;
+    a.part_m = (float *)(wsb + p.off_m);
+    a.part_l = (float *)(wsb + p.off_l);
+    a.part_o = (float *)(wsb + p.off_o);
+}
+
 dustin_status attn_prepare(const char *name, const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
                            const int32_t *idx, const int32_t *count, int32_t k, float scale, void *out,
-                           float *lse, void *ws, size_t ws_bytes, int causal, AttnArgs &a, AttnPlan &p) {
+                           float *lse, void *ws, size_t ws_bytes, int causal, AttnArgs &a, AttnPlan &p,
+                           bool own_scratch = false) {
     char what[96];
     snprintf(what, sizeof what, "%s kv", name);
     dustin_status st = check_kv(kv, what, true);
@@ -185,7 +196,9 @@ dustin_status attn_prepare(const char *name, const void *q, int32_t w, int32_t H
     const int tokens = (idx ? k : kv->N_max) + (causal ? w : 0);
     p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
     CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "%s: too many tokens", name);
-    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+    // the allocation-free entry point passes no workspace (own_scratch) and
+    // binds its static scratch afterwards
+    CHECK(own_scratch || (ws != nullptr && ws_bytes >= p.ws_bytes), DUSTIN_ERR_INVALID_ARG,
           "%s: workspace of %zu bytes needed (got %zu)", name, p.ws_bytes, ws_bytes);
     a = AttnArgs{};
     a.kv = view_of(kv);
@@ -200,11 +213,7 @@ dustin_status attn_prepare(const char *name, const void *q, int32_t w, int32_t H
     a.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
     a.out = out;
     a.lse = lse;
-    char *wsb = (char *)ws;
-    a.counters = (int32_t *)wsb;
-    a.part_m = (float *)(wsb + p.off_m);
-    a.part_l = (float *)(wsb + p.off_l);
-    a.part_o = (float *)(wsb + p.off_o);
+    bind_attn_workspace(a, p, (char *)ws);
     a.splits = p.splits;
     a.tps = p.tps;
     a.rpad = p.rpad;
@@ -1019,3 +1028,72 @@ dustin_status dustin_greedy_select(const float *units, int32_t U, const int32_t 
 
 }  // extern "C"
 
+
+// ------------------------------------------- allocation-free attention
+// dustin_sparse_verify_attn_noalloc keeps what the workspace holds for the
+// other entry points (the 64 KiB of arrival counters and the split partials)
+// in one static device array per GPU.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per
+// device, and is kept per device.
+namespace {
+
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[DUSTIN_ATTN_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kScratchDevices];
+
+__global__ __launch_bounds__(256) void scratch_zero_counters(int32_t *c, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) c[i] = 0;
+}
+
+// The scratch's device address on the current device.  The first call on a
+// device looks it up and zero-fills the counter region with a kernel on
+// `s` (every attention launch leaves the counters at zero again, so this is
+// the only clear that is needed).
+dustin_status scratch_on_current_device(hipStream_t s, char **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "sparse_verify_attn_noalloc: hipGetDevice");
+    CHECK(dev >= 0 && dev < kScratchDevices, DUSTIN_ERR_UNSUPPORTED,
+          "sparse_verify_attn_noalloc: device %d outside the %d the scratch table holds", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "sparse_verify_attn_noalloc: hipGetSymbolAddress(scratch)");
+        hipLaunchKernelGGL(scratch_zero_counters, dim3(kAttnCounterSlots / 256), dim3(256), 0, s, (int32_t *)ptr,
+                           kAttnCounterSlots);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return hip_status(e, "sparse_verify_attn_noalloc: clearing the scratch counters");
+        g_scratch_ptr[dev] = (char *)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DUSTIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dustin_status dustin_sparse_verify_attn_noalloc(const void *q, int32_t w, int32_t H_q, const dustin_kv *kv,
+                                                const int32_t *idx, const int32_t *count, int32_t k, float scale,
+                                                void *out, float *lse, dustin_stream_t stream) {
+    static const char *name = "sparse_verify_attn_noalloc";
+    AttnArgs a;
+    AttnPlan p;
+    dustin_status st =
+        attn_prepare(name, q, w, H_q, kv, idx, count, k, scale, out, lse, nullptr, 0, 0, a, p, true);
+    if (st != DUSTIN_OK) return st;
+    CHECK(p.ws_bytes <= (size_t)DUSTIN_ATTN_SCRATCH_BYTES, DUSTIN_ERR_UNSUPPORTED,
+          "%s: this shape needs %zu bytes of scratch, the static scratch holds %zu "
+          "(dustin_sparse_verify_attn takes a workspace of any size)",
+          name, p.ws_bytes, (size_t)DUSTIN_ATTN_SCRATCH_BYTES);
+    char *base = nullptr;
+    if ((st = scratch_on_current_device((hipStream_t)stream, &base)) != DUSTIN_OK) return st;
+    bind_attn_workspace(a, p, base);
+    return hip_status(launch_attn(a, p, (hipStream_t)stream), "sparse_verify_attn_noalloc launch");
+}
+
+}  // extern "C"

@@ -257,6 +257,25 @@ def test_workspace_sizes_are_shape_only(L):
     assert L.dustin_topk_workspace_bytes(16, 32768, 2048) >= 16 * 32768
 
 
+def test_noalloc_attention_limits(L):
+    """The allocation-free attention checks its arguments like the workspace
+    form and refuses, on the host, a shape whose split state exceeds its
+    static scratch (the dense form over 131072 positions at B = 64)."""
+    def call(desc, **kw):
+        a = dict(q=FAKE, w=4, Hq=64, idx=FAKE, count=FAKE, k=2048, out=FAKE)
+        a.update(kw)
+        return L.dustin_sparse_verify_attn_noalloc(a["q"], a["w"], a["Hq"], ctypes.byref(desc), a["idx"],
+                                                   a["count"], a["k"], 0.0, a["out"], None, None)
+    assert call(kv(k=None)) == INVALID
+    assert call(kv(), out=None) == INVALID
+    assert call(kv(), Hq=60) == INVALID
+    big = kv(B=64, N_max=131072)
+    assert L.dustin_attn_workspace_bytes(64, 4, 64, 8, 128, 131072) > (32 << 20)
+    assert call(big, idx=None, count=None, k=0) == UNSUPPORTED
+    assert b"scratch" in L.dustin_last_error()
+    assert L.dustin_attn_workspace_bytes(16, 4, 64, 8, 128, 2048) <= (32 << 20)   # the headline shape fits
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
 def test_valid_call_without_device_reports_hip_error(L):
     # Validation passes; the first HIP call then fails because there is no device.
@@ -264,6 +283,9 @@ def test_valid_call_without_device_reports_hip_error(L):
     st = attn(L, desc)
     assert st == HIPERR
     assert L.dustin_last_error() != b""
+    st = L.dustin_sparse_verify_attn_noalloc(FAKE, 4, 64, ctypes.byref(desc), FAKE, FAKE, 2048, 0.0, FAKE, None,
+                                             None)
+    assert st == HIPERR
 
 
 def test_binding_refuses_host_tensors():
