@@ -195,7 +195,7 @@ dustin_status attn_prepare(const char *name, const void *q, int32_t w, int32_t H
     CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "%s: scale is not finite", name);
     const int tokens = (idx ? k : kv->N_max) + (causal ? w : 0);
     p = attn_plan(kv->B, w, H_q, kv->H_kv, kv->head_dim, tokens, kv->dtype == DUSTIN_F32);
-    CHECK((int64_t)p.tps * p.splits >= tokens, DUSTIN_ERR_UNSUPPORTED, "%s: too many tokens", name);
+    CHECK((int64_t)p.tps * p.splits >= tokens && p.splits < 32768, DUSTIN_ERR_UNSUPPORTED, "%s: too many tokens", name);
     // the allocation-free entry point passes no workspace (own_scratch) and
     // binds its static scratch afterwards
     CHECK(own_scratch || (ws != nullptr && ws_bytes >= p.ws_bytes), DUSTIN_ERR_INVALID_ARG,

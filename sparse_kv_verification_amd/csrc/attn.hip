@@ -496,12 +496,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         return;
     }
 
-    // Split partials (row-major m, l, O per split).  A split that, when its
-    // token loop ended, found every other split of (b, g) already published merges
-    // at once: its own partial comes from registers, so it neither waits for
-    // its stores nor arrives.  Otherwise it publishes, waits for its stores,
-    // and arrives; the last split to arrive merges.  Exactly one split
-    // merges, always in split order, so the output does not depend on which.
+    // Split partials (m, l per row; O in thread order).  A split that, when
+    // its token loop ended, found every other split of (b, g) already
+    // published merges at once: its own partial comes from registers, so it
+    // neither waits for its stores nor arrives.  Otherwise it publishes,
+    // waits for its stores, and arrives; the last split to arrive merges.
+    // Exactly one split merges, always in split order, so the output does
+    // not depend on which.
+    // The O partial is stored in thread order (chunk c of thread tid at
+    // float4 index c * NT + tid): every wave store covers 1 KiB of whole
+    // lines, and the merging split reads the other splits' values for its
+    // own slice at the same offsets.  (A row-major layout made each lane's
+    // 16-byte write-through store land in a line of its own.)
     const size_t pb0 = (size_t)bg * a.splits * a.rpad;   // partial rows of split 0 of (b, g)
     {
         const size_t pb = pb0 + (size_t)split * a.rpad;
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         }
         const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb * D, (uint32_t)(a.rpad * D * sizeof(float)));
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) st_coherent4(po, (uint32_t)((r * D + d0 + 4 * c) * 4), acc[c]);
+        for (int c = 0; c < E / 4; ++c) st_coherent4(po, (uint32_t)((c * NT + tid) * 16), acc[c]);
     }
     if (tid == 0) s_flag = (seen == a.splits - 1);
     lds_barrier();   // the partial stores stay in flight
@@ -523,35 +529,50 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         __syncthreads();
         if (!s_flag) return;
     }
-    // merge: each lane folds its (row, E columns) slice over the splits
+    // merge: each lane folds its (row, E columns) slice over the splits, in
+    // split order; the partials of up to MB splits are loaded together
+    // before any is folded, so a batch costs one memory round trip.
     {
         const uint32_t nml = (uint32_t)(a.splits * a.rpad * sizeof(float));
         const __amdgpu_buffer_rsrc_t pm = coherent_rsrc(a.part_m + pb0, nml);
         const __amdgpu_buffer_rsrc_t pl = coherent_rsrc(a.part_l + pb0, nml);
         const __amdgpu_buffer_rsrc_t po = coherent_rsrc(a.part_o + pb0 * D, nml * D);
+        constexpr int MB = 4;
         float Mt = kNegInf, Lt = 0.f;
         f32x4 at[E / 4];
 #pragma unroll
         for (int c = 0; c < E / 4; ++c) at[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < a.splits; ++s2) {
-            float ms = M, ls = L;
-            f32x4 v[E / 4];
+        for (int s0 = 0; s0 < a.splits; s0 += MB) {
+            float msb[MB], lsb[MB];
+            f32x4 vb[MB][E / 4];
 #pragma unroll
-            for (int c = 0; c < E / 4; ++c) v[c] = acc[c];
-            if (s2 != split) {
-                const uint32_t o = (uint32_t)(s2 * a.rpad + r);
-                ms = ld_coherent(pm, o * 4u);
-                ls = ld_coherent(pl, o * 4u);
+            for (int q = 0; q < MB; ++q) {
+                const int s2 = s0 + q;
+                msb[q] = M;
+                lsb[q] = L;
 #pragma unroll
-                for (int c = 0; c < E / 4; ++c) v[c] = ld_coherent4(po, (o * D + d0 + 4 * c) * 4u);
+                for (int c = 0; c < E / 4; ++c) vb[q][c] = acc[c];
+                if (s2 < a.splits && s2 != split) {
+                    const uint32_t o = (uint32_t)(s2 * a.rpad + r);
+                    msb[q] = ld_coherent(pm, o * 4u);
+                    lsb[q] = ld_coherent(pl, o * 4u);
+                    const uint32_t ob = (uint32_t)(s2 * a.rpad * D) * 4u;
+#pragma unroll
+                    for (int c = 0; c < E / 4; ++c) vb[q][c] = ld_coherent4(po, ob + (uint32_t)((c * NT + tid) * 16));
+                }
             }
-            const float Mn = fmaxf(Mt, ms);
-            const float mu = (Mn == kNegInf) ? 0.f : Mn;
-            const float so = exp2f(Mt - mu), sn = exp2f(ms - mu);
-            Lt = Lt * so + ls * sn;
 #pragma unroll
-            for (int c = 0; c < E / 4; ++c) at[c] = at[c] * so + v[c] * sn;
-            Mt = Mn;
+            for (int q = 0; q < MB; ++q) {
+                if (s0 + q >= a.splits) break;
+                const float ms = msb[q], ls = lsb[q];
+                const float Mn = fmaxf(Mt, ms);
+                const float mu = (Mn == kNegInf) ? 0.f : Mn;
+                const float so = exp2f(Mt - mu), sn = exp2f(ms - mu);
+                Lt = Lt * so + ls * sn;
+#pragma unroll
+                for (int c = 0; c < E / 4; ++c) at[c] = at[c] * so + vb[q][c] * sn;
+                Mt = Mn;
+            }
         }
         if (r < a.R) {
             const int sq = r / a.G, gh = r - (r / a.G) * a.G;
