@@ -257,6 +257,21 @@ def test_workspace_sizes_are_shape_only(L):
     assert L.dustin_topk_workspace_bytes(16, 32768, 2048) >= 16 * 32768
 
 
+def test_bf16_attention_refuses_head_dim_32(L):
+    """bf16 attention serves head_dim 64 and 128 only (float32 serves 32 too):
+    refused on the host with DUSTIN_ERR_UNSUPPORTED, by every attention entry point."""
+    d32 = kv(head_dim=32, dtype=1)
+    assert attn(L, d32) == UNSUPPORTED
+    assert b"head_dim 64 or 128" in L.dustin_last_error()
+    assert L.dustin_verify_attn(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE, None, FAKE, 1 << 40,
+                                None) == UNSUPPORTED
+    assert L.dustin_sparse_verify_attn_noalloc(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE, None,
+                                               None) == UNSUPPORTED
+    # the same geometry in float32 passes validation (then needs a device)
+    if not torch.cuda.is_available():
+        assert attn(L, kv(head_dim=32, dtype=0)) == HIPERR
+
+
 def test_noalloc_attention_limits(L):
     """The allocation-free attention checks its arguments like the workspace
     form and refuses, on the host, a shape whose split state exceeds its
