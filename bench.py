@@ -55,6 +55,8 @@ def parse():
                    help="skip the one-layer steps of the other workloads (tiny f32, 7B, 32B, ragged paged)")
     p.add_argument("--no-search", action="store_true",
                    help="skip the offline configuration search (SRH matrix, greedy target/draft, m search)")
+    p.add_argument("--no-srh", action="store_true",
+                   help="skip the step restricted to the searched draft layers and target heads (Dustin-H, blog Fig. 6)")
     p.add_argument("--no-curve", action="store_true",
                    help="skip the estimator-overhead curve (dense, naive, Quest-16, Dustin-T/D/H over context length)")
     p.add_argument("--pmc-probe", action="store_true",
@@ -435,8 +437,11 @@ def main():
         res["k_sweep"] = k_sweep(args, sh, x, kvs, dkv, s_d, s_t, cap, timed)
     if not args.no_curve:
         res["estimator_curve"] = estimator_curve(args, sh, x, cap, timed)
+    search = None
     if not args.no_search:
-        res["config_search"] = config_search(args, sh)
+        res["config_search"] = search = config_search(args, sh)
+    if not args.no_srh:
+        res["srh_restricted_step"] = srh_step(args, sh, x, kvs, dkv, cap, timed, search)
     if not args.no_window:
         # Last of the c4 legs, because it writes the window rows into every layer's cache.
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
@@ -524,11 +529,97 @@ def k_sweep(args, sh, x, kvs, dkv, s_d, s_t, cap, timed):
             for l in range(sh.layers):
                 dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=o, ws=ws_a)
 
+        def attn_layers():
+            for l in range(sh.layers):
+                dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=o, ws=ws_a)
+
         us = graph_time(args, step, cap, timed, max(2, args.steps // 4))
-        by = algorithmic_bytes(sh, x, kk, cnt, x.sub_heads)["step"]
+        a_us = graph_time(args, attn_layers, cap, timed, max(2, args.steps // 4)) / sh.layers
+        bys = algorithmic_bytes(sh, x, kk, cnt, x.sub_heads)
+        by, ab = bys["step"], bys["attn_per_layer"]
         out[str(kk)] = {"us_per_step": round(us, 1), "GBps": round(by / us / 1e3, 1),
-                        "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by}
-        log(f"k={kk}: step {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+                        "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by,
+                        "attention_us_per_launch": round(a_us, 2),
+                        "attention_GBps": round(ab / a_us / 1e3, 1),
+                        "attention_frac_of_hbm_peak": round(ab / a_us / 1e3 / HBM_PEAK_GBPS, 4),
+                        "attention_algorithmic_bytes_per_launch": ab}
+        log(f"k={kk}: step {us:.1f} us, {by / us / 1e3:.0f} GB/s; attention {a_us:.2f} us/launch "
+            f"({ab / a_us / 1e3:.0f} GB/s, {ab / a_us / 1e3 / HBM_PEAK_GBPS:.3f} of peak)")
+    return out
+
+
+# The configuration the offline search picks on the synthetic profiling
+# batch (its last measured result), used when the search leg is skipped.
+SRH_DEFAULT = {"draft_layers": [0, 6, 12, 18, 23], "target_heads": [(10 * g, 8 * g) for g in range(8)]}
+
+
+def srh_step(args, sh, x, kvs, dkv, cap, timed, search):
+    """Dustin-H restricted to a searched configuration (blog section 2.4,
+    Fig. 6: only the searched target heads and draft layers are scored; the
+    efficiency figures of blog section 3, Fig. 8, are for that restricted
+    estimator): the step with S_Draft over the searched draft layers and
+    S_Target over the searched target heads (in their own layers), then the
+    same select and L attention layers.  The headline step scores every
+    draft layer and head, as the task defines S_Draft; this is an extra,
+    labelled measurement.  Also the restricted score alone against dense
+    full-cache attention of every layer (one point of the estimator curve)."""
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+    cfg = SRH_DEFAULT if not search else {"draft_layers": search["draft_layers"],
+                                          "target_heads": [tuple(p) for p in search["target_heads"]]}
+    dl = [int(l) for l in cfg["draft_layers"]]
+    th = [(int(l), int(h)) for l, h in cfg["target_heads"]]
+    t_layers = sorted({l for l, _ in th})
+    sub = [(t_layers.index(l), h) for l, h in th]
+    tk = [kvs[l] for l in t_layers]
+    qd = x.q_draft[:, dl].contiguous() if dl else None
+    dsub = [dkv[l] for l in dl]
+    qh = x.q[:, -1][:, [h for _, h in th]].contiguous()      # the scored heads' most recent queries
+    k = sh.k
+    ns, nw, mm = synth.tier_defaults(k)
+    s_d = torch.empty((sh.B, sh.n), dtype=torch.float32, device=x.q.device)
+    s_t = torch.empty_like(s_d)
+    idx = torch.empty((sh.B, k), dtype=torch.int32, device=x.q.device)
+    cnt = torch.empty((sh.B,), dtype=torch.int32, device=x.q.device)
+    o = torch.empty_like(x.q)
+    ws_s, ws_k, ws_a, ws_d = dk.Workspace(), dk.Workspace(), dk.Workspace(), dk.Workspace()
+
+    def score():
+        dk.dustin_score(dsub, qd, tk, qh, sub, sh.Hq, s_draft=s_d if dl else None, s_target=s_t, ws=ws_s,
+                        want_draft=bool(dl))
+
+    def step():
+        score()
+        dk.dustin_topk(s_d if dl else None, s_t, x.seq_lens, k, mm, ns, nw, idx=idx, count=cnt, want_tier=False,
+                       ws=ws_k)
+        for l in range(sh.layers):
+            dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=o, ws=ws_a)
+
+    def dense():
+        for l in range(sh.layers):
+            dk.dustin_sparse_verify_attn(x.q, kvs[l], None, None, out=o, ws=ws_d)
+
+    reps = max(2, args.steps // 4)
+    us = graph_time(args, step, cap, timed, reps)
+    score_us = graph_time(args, score, cap, timed, reps)
+    dense_us = None if args.no_dense else graph_time(args, dense, cap, timed, 2)
+    # global layer ids for the byte count (U = distinct (layer, KV head) pairs)
+    by = algorithmic_bytes(sh.replace(L_d=len(dl)), x, k, cnt, th)
+    out = {"source": "config_search leg" if search else "default (search leg skipped)",
+           "draft_layers": dl, "target_heads": [list(p) for p in th], "m": mm,
+           "us_per_step": round(us, 1), "score_us": round(score_us, 1),
+           "step_GBps": round(by["step"] / us / 1e3, 1),
+           "step_frac_of_hbm_peak": round(by["step"] / us / 1e3 / HBM_PEAK_GBPS, 4),
+           "algorithmic_bytes": by["step"]}
+    if dense_us is not None:
+        out["dense_attention_us"] = round(dense_us, 1)
+        out["speedup_vs_dense_attention"] = round(dense_us / us, 2)
+        out["score_normalized_by_dense"] = round(score_us / dense_us, 5)
+    log(f"SRH-restricted Dustin-H ({len(dl)} draft layers, {len(th)} target heads over {len(t_layers)} layers): "
+        f"step {us:.1f} us ({out['step_frac_of_hbm_peak']:.3f} of peak), score {score_us:.1f} us" +
+        ("" if dense_us is None else f", {out['speedup_vs_dense_attention']:.2f}x faster than dense, score = "
+                                      f"1/{1 / out['score_normalized_by_dense']:.0f} of dense"))
     return out
 
 

@@ -1196,7 +1196,8 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     const int L = a.L_d;
     const int U = L * 2;
     // layers per group: ceil(L / LG) rounded up to even, so every group is
-    // non-empty and holds an even number of layers (L is even)
+    // non-empty (with several groups L is even and so is every group; one
+    // group takes all L layers, odd or even)
     const int lpg = ((L + LG - 1) / LG + 1) & ~1;
     // per-lane Q offsets, and normaliser offsets: rows rb*16 + (lane >> 4)*4
     // .. + 3 in one 16-byte load (the row count is a multiple of 4); rows past
@@ -1308,7 +1309,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
             };
             for (int l = l0; l < l1; l += 2) {
                 layer(l, qA, lA, pA, qB, lB, pB);
-                layer(l + 1, qB, lB, pB, qA, lA, pA);
+                if (l + 1 < l1) layer(l + 1, qB, lB, pB, qA, lA, pA);
             }
         }
         float *out = (GT == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)gt * k0.B + b) * N;
@@ -1501,9 +1502,9 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Streaming passes: two 64-wide draft KV heads, an even number of draft
-// layers and a row count that is a multiple of four; contiguous or paged;
-// HALF (three or four row blocks): one KV head per item.
+// Streaming passes: two 64-wide draft KV heads and a row count that is a
+// multiple of four; contiguous or paged; HALF (three or four row blocks):
+// one KV head per item.
 template <int RB, bool PAGED, bool HALF>
 static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
@@ -1539,7 +1540,7 @@ static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     if constexpr (D == 64) {
         constexpr bool HALF = RB >= 3;
-        if (a.Hkv_d == 2 && a.L_d % 2 == 0 && a.rows % 4 == 0)
+        if (a.Hkv_d == 2 && a.rows % 4 == 0)
             return k0.page_size == 0 ? draft_stream_impl<RB, false, HALF>(a, s) : draft_stream_impl<RB, true, HALF>(a, s);
     }
     const int U = a.L_d * a.Hkv_d;

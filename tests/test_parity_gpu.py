@@ -203,6 +203,8 @@ SCORE_CASES = [
     ("stream-one-head-rb3", dict(base="c2", B=2, n=2500, n_lo=900, L_d=4, H_d=12, w=6)),
     # 56 rows, one KV head per item, 8 layers in 4 groups: 8 (group, head) partials
     ("stream-one-head-groups", dict(base="c4", B=1, n=2048, L_d=8, w=8)),
+    ("stream-odd-layers", dict(base="c2", B=2, n=3000, n_lo=1100, L_d=5)),     # 28 rows, five layers
+    ("stream-one-head-odd-layers", dict(base="c4", B=2, n=2500, L_d=3, w=8)),  # 56 rows, three layers
     ("tiny-f32", dict(base="c1")),
 ]
 
@@ -239,6 +241,37 @@ def test_scores_match_oracle(name, over):
         assert abs(gt.sum() - len(sub)) < 1e-3 * len(sub)
         assert abs(gd.sum() - sh.L_d * sh.H_d * sh.w) < 1e-3 * sh.L_d * sh.H_d * sh.w
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
+
+
+def test_scores_on_searched_subsets():
+    """Dustin-H restricted to a searched configuration (blog section 2.4,
+    Fig. 6; section 3 Fig. 8): S_Draft over a subset of the draft layers (not
+    contiguous, in the caller's order) and S_Target over heads that sit in
+    three different target layers, each layer its own cache.  The oracle
+    scores the same subsets from the same layers."""
+    say("scores on a draft-layer subset and target heads over three layers")
+    sh = synth.preset("c4").replace(B=2, n=3000, L_d=6)
+    x = synth.make(sh, device=DEV)
+    layers = [1, 4, 5, 2, 0]                     # the searched draft layers, in the caller's order
+    qd = x.q_draft[:, layers].contiguous()
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens) for l in layers]
+    # three target layers: the generated cache and two position-rotated copies of it
+    Kt = [x.K, torch.roll(x.K, 7, dims=1).contiguous(), torch.roll(x.K, -123, dims=1).contiguous()]
+    kvs = [dk.KV(K, None, x.seq_lens) for K in Kt]
+    sub = [(2, 9), (0, 40), (1, 17), (2, 63), (1, 0)]    # (layer, head): heads of KV groups 1, 5, 2, 7, 0
+    qh = x.q[:, -1][:, [h for _, h in sub]].contiguous()
+    s_d, s_t = dk.dustin_score(dkv, qd, kvs, qh, sub, sh.Hq)
+    torch.cuda.synchronize()
+    for b in range(sh.B):
+        n = int(x.seq_lens[b])
+        Ko = {l: f64(Kt[l][b, :n]) for l in range(3)}
+        st = oracle.score_target(f64(qh[b]), Ko, sub, sh.Hq)
+        sd = oracle.score_draft(f64(qd[b]), f64(x.Kd[layers, b, :n]))
+        say(f"  b={b} n={n} max rel|dS_T|={max_rel_err(f64(s_t[b, :n]), st):.2e} "
+            f"rel|dS_D|={max_rel_err(f64(s_d[b, :n]), sd):.2e}")
+        assert_scores_close(f64(s_t[b, :n]), st, "S_Target")
+        assert_scores_close(f64(s_d[b, :n]), sd, "S_Draft")
+        assert abs(float(s_d[b, :n].double().sum()) - len(layers) * sh.H_d * sh.w) < 1e-3 * len(layers) * sh.H_d * sh.w
 
 
 @pytest.mark.parametrize("w", [4, 8], ids=["both-heads-per-item-w4", "one-head-per-item-w8"])
