@@ -133,28 +133,74 @@ __global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, N
     __syncthreads();
 
     const int grp = tid / LPI, sl = tid - (tid / LPI) * LPI;
-    for (int pos = grp; pos < CH; pos += IPP) {
-        const int j = j0 + pos;
-        float x[8];
-        const bool ok = j < nb;
-        const char *row = nullptr;
-        if (ok) {
-            if (paged) {
-                const int pg = pgs[pos >> 4];
-                if (pg >= 0 && pg < kv.num_pages)
-                    row = kv.k + ((((int64_t)pg * 16 + (j & 15)) * kv.Hkv + kvh) * D) * ESZ;
-            } else {
-                row = kv.k + ((((int64_t)b * kv.N_max + j) * kv.Hkv + kvh) * D) * ESZ;
-            }
+    // This lane's slice of every query row, in registers (the dot products
+    // then read no LDS), and the dot product's sum over the LPI lanes of a
+    // position with DPP row rotations when a position is one 16-lane row.
+    float qr[8][EPL];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) qr[r][i] = r < nr ? qs[r][sl * EPL + i] : 0.f;
+    auto lane_sum = [&](float v) {
+        if constexpr (LPI == 16) {
+            return lane16_sum(v);
+        } else if constexpr (LPI == 32) {
+            v = lane16_sum(v);
+            return v + __shfl_xor(v, 16, 64);
+        } else {
+#pragma unroll
+            for (int o = LPI / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+            return v;
         }
-        load_slice<F32>(row, sl, x);
-        for (int r = 0; r < nr; ++r) {
-            float s = 0.f;
+    };
+    // All of a lane's slice loads of a batch are issued before any is used.
+    constexpr int NP = CH / IPP;              // positions per lane group
+    constexpr int NB = NP < 8 ? NP : 8;       // positions per batch
+    static_assert(NP % NB == 0, "batches");
+#pragma unroll 1
+    for (int t0 = 0; t0 < NP; t0 += NB) {
+        u32x4 raw[NB];
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) s += qs[r][sl * EPL + i] * x[i];
+        for (int t = 0; t < NB; ++t) {
+            const int pos = grp + (t0 + t) * IPP;
+            const int j = j0 + pos;
+            const char *row = nullptr;
+            if (j < nb) {
+                if (paged) {
+                    const int pg = pgs[pos >> 4];
+                    if (pg >= 0 && pg < kv.num_pages)
+                        row = kv.k + ((((int64_t)pg * 16 + (j & 15)) * kv.Hkv + kvh) * D) * ESZ;
+                } else {
+                    row = kv.k + ((((int64_t)b * kv.N_max + j) * kv.Hkv + kvh) * D) * ESZ;
+                }
+            }
+            raw[t] = row ? ld_stream16(row + sl * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int o = LPI / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-            if (sl == 0) lg[r][pos] = ok ? s * p.scale_log2 : kNegInf;
+        for (int t = 0; t < NB; ++t) {
+            const int pos = grp + (t0 + t) * IPP;
+            const bool ok = j0 + pos < nb;
+            float x[8];
+            if constexpr (F32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(raw[t][i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[2 * i] = __uint_as_float(raw[t][i] << 16);
+                    x[2 * i + 1] = __uint_as_float(raw[t][i] & 0xffff0000u);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r < nr) {
+                    float sdot = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPL; ++i) sdot += qr[r][i] * x[i];
+                    sdot = lane_sum(sdot);
+                    if (sl == 0) lg[r][pos] = ok ? sdot * p.scale_log2 : kNegInf;
+                }
+            }
         }
     }
     __syncthreads();
