@@ -55,6 +55,8 @@ def parse():
                    help="skip the one-layer steps of the other workloads (tiny f32, 7B, 32B, ragged paged)")
     p.add_argument("--no-search", action="store_true",
                    help="skip the offline configuration search (SRH matrix, greedy target/draft, m search)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the achievable-rate probes (streaming read, K/V row gather, last-level-cache re-read)")
     p.add_argument("--no-srh", action="store_true",
                    help="skip the step restricted to the searched draft layers and target heads (Dustin-H, blog Fig. 6)")
     p.add_argument("--no-curve", action="store_true",
@@ -381,6 +383,7 @@ def main():
             f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster, "
             f"sparse attention alone {dense['speedup_sparse_attention_vs_dense_attention']:.2f}x")
 
+    ceil = None if args.no_ceilings else ceilings(args, sh, x, idx, cnt, timed)
     traffic = measured_traffic()
     step_gbps = bytes_["step"] / step_us / 1e3
     attn_gbps = bytes_["attn_per_layer"] / attn_launch_us / 1e3
@@ -425,7 +428,12 @@ def main():
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes_per_launch": bytes_["attn_per_layer"],
+            # the same bytes gathered by a kernel that does nothing else
+            # (dustin_probe_gather_rows): the rate this access pattern reaches
+            "achievable_GBps": None if ceil is None else ceil["gather_kv_rows_GBps"],
+            "frac_of_achievable": None if ceil is None else round(attn_gbps / ceil["gather_kv_rows_GBps"], 4),
         },
+        "ceilings": ceil,
         "dense_baseline": dense,
     }
     if not args.no_cpu_baseline:
@@ -452,6 +460,77 @@ def main():
 
 SWEEP_DELTAS = (1, 4, 16, 64)
 SWEEP_KS = (128, 256, 512, 1024, 2048)
+
+
+def ceilings(args, sh, x, idx, cnt, timed):
+    """Achievable HBM rates on this part, measured with the library's
+    measurement kernels (dustin_probe_*): a streaming read of 4 GiB with the
+    nontemporal and the default cache policy (each after 4 GiB of other
+    reads, so nothing is cached), the gather of the step's K/V rows (the
+    rows the attention reads for the current index set: 256-byte head rows
+    of K and V, the attention's work split) and a 128 MiB re-read that the
+    256 MiB last-level cache (MALL) could serve, cold and warm."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    dev = x.q.device
+    out = {}
+    big = torch.empty(1 << 30, dtype=torch.int32, device=dev)           # 4 GiB
+    other = torch.empty_like(big)
+    big.fill_(1)
+    other.fill_(2)
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+    reps = 3
+
+    def once(fn, flush=True):
+        ts = []
+        for _ in range(reps):
+            if flush:
+                dk.dustin_probe_stream_read(other, True, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(ts)[reps // 2]
+
+    nb = big.numel() * 4
+    for nt in (True, False):
+        us = once(lambda: dk.dustin_probe_stream_read(big, nt, sink))
+        out["stream_read_" + ("nontemporal" if nt else "default") + "_GBps"] = round(nb / us / 1e3, 1)
+    # the attention's gather: row (b, j, g) of K (and V) for every selected j
+    B, N, Hkv = sh.B, x.K.shape[1], sh.Hkv
+    sel = idx.long()
+    valid = torch.arange(idx.shape[1], device=dev)[None, :] < cnt[:, None].long()
+    jj = torch.where(valid, sel, torch.zeros_like(sel))
+    rows = ((torch.arange(B, device=dev)[:, None, None] * N + jj[:, None, :]) * Hkv
+            + torch.arange(Hkv, device=dev)[None, :, None])                # [B][Hkv][k]
+    rows = rows.to(torch.int32).reshape(-1).contiguous()
+    us = once(lambda: dk.dustin_probe_gather_rows(x.K, rows, 256, 256, base2=x.V))
+    gb = rows.numel() * 256 * 2
+    out["gather_kv_rows_GBps"] = round(gb / us / 1e3, 1)
+    out["gather_kv_rows_us"] = round(us, 2)
+    out["gather_kv_rows_bytes"] = gb
+    # MALL: a 128 MiB buffer read cold, then again at once (warm)
+    small = big[: (128 << 20) // 4]
+    cold, warm = [], []
+    for _ in range(reps):
+        dk.dustin_probe_stream_read(other, True, sink)
+        for lst in (cold, warm):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dk.dustin_probe_stream_read(small, True, sink)
+            e1.record()
+            e1.synchronize()
+            lst.append(e0.elapsed_time(e1) * 1e3)
+    mb = small.numel() * 4
+    out["mall_128MiB_cold_GBps"] = round(mb / sorted(cold)[reps // 2] / 1e3, 1)
+    out["mall_128MiB_warm_GBps"] = round(mb / sorted(warm)[reps // 2] / 1e3, 1)
+    del big, other
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("ceilings: " + ", ".join(f"{k} {v}" for k, v in out.items()))
+    return out
 
 
 def policy_sweep(args, sh, x, kv, s_d, s_t, n_sink, n_window, timed):

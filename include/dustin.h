@@ -502,6 +502,37 @@ dustin_status dustin_greedy_select(const float *units, int32_t U, const int32_t 
 
 size_t dustin_greedy_select_workspace_bytes(int32_t C, int32_t B, int32_t N_max, int32_t k);
 
+/*
+ * Measurement kernels.  They compute nothing of the method: they give the
+ * achievable HBM rates that the step's kernels are compared with, beside
+ * the 8 TB/s peak of the part.
+ *
+ * dustin_probe_stream_read -- reads every 16-byte piece of `buf` once
+ * (grid-stride, 2048 work-groups of 256 lanes, four loads in flight per
+ * lane), with the nontemporal cache policy of the scoring passes
+ * (nontemporal != 0) or the default policy.
+ *  buf   device, `bytes` bytes (a positive multiple of 16)
+ *  sink  device [2048] uint32; written only in the impossible case that the
+ *        folded data equals a marker (it keeps the loads from being dropped)
+ *
+ * dustin_probe_gather_rows -- gathers rows[0 .. n_rows) (row numbers,
+ * clamped to [0, buf_rows)) of `row_bytes` bytes each, at row r of base
+ * (byte r * row_stride) and, when base2 is not NULL, at the same row of
+ * base2, into LDS with global->LDS DMA: the access pattern of the
+ * verification attention's K/V gather (256 work-groups of 8 waves, a
+ * four-stage 32 KiB ring each, no arithmetic).  Work-group g takes the
+ * rows g * ceil(n_rows / 256) .. in list order.
+ *  row_bytes   64, 128, 256 or 512; row_stride >= row_bytes, a multiple of 16
+ *  n_rows      1 .. 256 * 4096
+ * Both return DUSTIN_ERR_INVALID_ARG for the conditions above, checked on
+ * the host before any HIP call.
+ */
+dustin_status dustin_probe_stream_read(const void *buf, size_t bytes, int32_t nontemporal, uint32_t *sink,
+                                       dustin_stream_t stream);
+dustin_status dustin_probe_gather_rows(const void *base, const void *base2, int64_t row_stride, int64_t buf_rows,
+                                       const int32_t *rows, int64_t n_rows, int32_t row_bytes,
+                                       dustin_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *dustin_status_string(dustin_status status);
 

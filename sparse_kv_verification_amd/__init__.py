@@ -12,6 +12,6 @@ from ._lib import (  # noqa: F401
     dustin_page_bounds, dustin_page_scores, dustin_policy_sweep, dustin_topk, dustin_verify_attn,
     dustin_verify_attn_append,
     dustin_window_attn, dustin_window_mean, dustin_head_scores, dustin_candidate_arr, dustin_greedy_select,
-    POLICY_NAMES,
+    POLICY_NAMES, dustin_probe_stream_read, dustin_probe_gather_rows,
     EXPORTS, LIB_PATH,
 )

@@ -29,6 +29,7 @@ EXPORTS = [
     "dustin_page_bounds", "dustin_page_scores", "dustin_page_scores_workspace_bytes",
     "dustin_head_scores", "dustin_head_scores_workspace_bytes", "dustin_candidate_arr",
     "dustin_candidate_arr_workspace_bytes", "dustin_greedy_select", "dustin_greedy_select_workspace_bytes",
+    "dustin_probe_stream_read", "dustin_probe_gather_rows",
     "dustin_status_string", "dustin_last_error", "dustin_abi_version",
 ]
 
@@ -125,6 +126,11 @@ def lib():
         L.dustin_greedy_select_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.dustin_greedy_select_workspace_bytes.restype = sz
         L.dustin_page_scores.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.dustin_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+        L.dustin_probe_stream_read.restype = ctypes.c_int
+        L.dustin_probe_gather_rows.argtypes = [vp, vp, i64, i64, vp, i64, i32, vp]
+        L.dustin_probe_gather_rows.restype = ctypes.c_int
         L.dustin_status_string.argtypes = [ctypes.c_int]
         L.dustin_status_string.restype = ctypes.c_char_p
         L.dustin_last_error.argtypes = []
@@ -519,3 +525,19 @@ def dustin_greedy_select(units, seq_lens, abar, k, m, n_sink, n_window, max_unit
     n = n_ch.value
     return [chosen[i] for i in range(n)], [curve[i] for i in range(n)], sum_out
 
+
+def dustin_probe_stream_read(buf, nontemporal=True, sink=None):
+    """Measurement kernel: read every byte of `buf` once (returns sink)."""
+    if sink is None:
+        sink = torch.zeros(2048, dtype=torch.int32, device=buf.device)
+    _check(lib().dustin_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
+                                          _ptr(sink), _stream(buf)))
+    return sink
+
+
+def dustin_probe_gather_rows(base, rows, row_bytes, row_stride, base2=None):
+    """Measurement kernel: gather rows[i] (row numbers) of `row_bytes` bytes
+    at `row_stride` from base (and base2) into LDS, as the attention does."""
+    buf_rows = (base.numel() * base.element_size() - row_bytes) // row_stride + 1
+    _check(lib().dustin_probe_gather_rows(_ptr(base), _ptr(base2), int(row_stride), int(buf_rows), _ptr(rows),
+                                          rows.numel(), int(row_bytes), _stream(base)))

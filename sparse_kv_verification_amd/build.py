@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdustin.so")
-SOURCES = ["attn.hip", "score.hip", "select.hip", "eval.hip", "window.hip", "pages.hip", "search.hip", "api.hip"]
+SOURCES = ["attn.hip", "score.hip", "select.hip", "eval.hip", "window.hip", "pages.hip", "search.hip", "probe.hip",
+           "api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -1029,6 +1029,36 @@ dustin_status dustin_greedy_select(const float *units, int32_t U, const int32_t 
 }  // extern "C"
 
 
+// ------------------------------------------- measurement kernels
+extern "C" {
+
+dustin_status dustin_probe_stream_read(const void *buf, size_t bytes, int32_t nontemporal, uint32_t *sink,
+                                       dustin_stream_t stream) {
+    CHECK(buf != nullptr && sink != nullptr, DUSTIN_ERR_INVALID_ARG, "probe_stream_read: buf and sink are required");
+    CHECK(bytes >= 16 && bytes % 16 == 0, DUSTIN_ERR_INVALID_ARG,
+          "probe_stream_read: bytes must be a positive multiple of 16 (got %zu)", bytes);
+    return hip_status(launch_probe_stream_read(buf, bytes, nontemporal != 0, sink, 2048, (hipStream_t)stream),
+                      "probe_stream_read launch");
+}
+
+dustin_status dustin_probe_gather_rows(const void *base, const void *base2, int64_t row_stride, int64_t buf_rows,
+                                       const int32_t *rows, int64_t n_rows, int32_t row_bytes,
+                                       dustin_stream_t stream) {
+    CHECK(base != nullptr && rows != nullptr, DUSTIN_ERR_INVALID_ARG, "probe_gather_rows: base and rows are required");
+    CHECK(row_bytes == 64 || row_bytes == 128 || row_bytes == 256 || row_bytes == 512, DUSTIN_ERR_INVALID_ARG,
+          "probe_gather_rows: row_bytes %d not one of 64, 128, 256, 512", row_bytes);
+    CHECK(row_stride >= row_bytes && row_stride % 16 == 0, DUSTIN_ERR_INVALID_ARG,
+          "probe_gather_rows: row_stride %lld must be >= row_bytes and a multiple of 16", (long long)row_stride);
+    CHECK(buf_rows >= 1, DUSTIN_ERR_INVALID_ARG, "probe_gather_rows: buf_rows must be >= 1");
+    CHECK(n_rows >= 1 && n_rows <= 256LL * 4096, DUSTIN_ERR_INVALID_ARG,
+          "probe_gather_rows: n_rows %lld outside 1 .. %lld", (long long)n_rows, 256LL * 4096);
+    return hip_status(launch_probe_gather_rows(base, base2, row_stride, buf_rows, rows, n_rows, row_bytes, 256,
+                                               (hipStream_t)stream),
+                      "probe_gather_rows launch");
+}
+
+}  // extern "C"
+
 // ------------------------------------------- allocation-free attention
 // dustin_sparse_verify_attn_noalloc keeps what the workspace holds for the
 // other entry points (the 64 KiB of arrival counters and the split partials)

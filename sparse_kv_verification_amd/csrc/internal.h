@@ -99,6 +99,12 @@ hipError_t launch_gather_sum(const float *abar, const int32_t *idx, const int32_
 hipError_t launch_batch_mean(const float *arr, int C, int B, float *mean, hipStream_t s);
 hipError_t launch_accumulate(float *dst, const float *src, int64_t n, bool overwrite, hipStream_t s);
 
+// measurement kernels (probe.hip)
+hipError_t launch_probe_stream_read(const void *p, size_t bytes, bool nontemporal, uint32_t *sink, int blocks,
+                                    hipStream_t s);
+hipError_t launch_probe_gather_rows(const void *base, const void *base2, int64_t row_stride, int64_t buf_rows,
+                                    const int32_t *rows, int64_t n_rows, int32_t row_bytes, int blocks, hipStream_t s);
+
 // ---------------------------------------------------------------- evaluator
 struct WindowArgs {
     KvView kv;

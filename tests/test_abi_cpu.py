@@ -272,6 +272,22 @@ def test_bf16_attention_refuses_head_dim_32(L):
         assert attn(L, kv(head_dim=32, dtype=0)) == HIPERR
 
 
+def test_probe_argument_errors(L):
+    """The measurement kernels check their arguments on the host."""
+    assert L.dustin_probe_stream_read(None, 4096, 1, FAKE, None) == INVALID
+    assert L.dustin_probe_stream_read(FAKE, 4096, 1, None, None) == INVALID
+    assert L.dustin_probe_stream_read(FAKE, 4100, 1, FAKE, None) == INVALID
+    assert L.dustin_probe_stream_read(FAKE, 0, 1, FAKE, None) == INVALID
+    g = L.dustin_probe_gather_rows
+    assert g(FAKE, None, 256, 100, FAKE, 10, 96, None) == INVALID          # row size
+    assert g(FAKE, None, 128, 100, FAKE, 10, 256, None) == INVALID         # stride below the row
+    assert g(FAKE, None, 264, 100, FAKE, 10, 256, None) == INVALID         # stride not a multiple of 16
+    assert g(FAKE, None, 256, 100, FAKE, 0, 256, None) == INVALID          # no rows
+    assert g(FAKE, None, 256, 100, FAKE, 256 * 4096 + 1, 256, None) == INVALID
+    assert g(FAKE, None, 256, 0, FAKE, 10, 256, None) == INVALID
+    assert g(None, None, 256, 100, FAKE, 10, 256, None) == INVALID
+
+
 def test_noalloc_attention_limits(L):
     """The allocation-free attention checks its arguments like the workspace
     form and refuses, on the host, a shape whose split state exceeds its
