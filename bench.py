@@ -38,6 +38,12 @@ def log(*a):
 
 def parse():
     p = argparse.ArgumentParser()
+    p.add_argument("--attn-timeline-child", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--timeline-v-offset", type=int, default=0,
+                   help="attention timeline with every V buffer placed this many bytes (multiple of 256) past an "
+                        "allocation boundary, K left aligned")
+    p.add_argument("--no-timeline", action="store_true",
+                   help="skip the attention phase timeline (phase-trace build of the library, in a child process)")
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
@@ -200,8 +206,127 @@ def cpu_baseline(sh, x, k, m, n_sink, n_window, budget_s=20.0):
     }
 
 
+TRACE_LIB = os.path.join(ROOT, "sparse_kv_verification_amd", "libdustin_trace.so")
+TIMELINE_PHASES = ["entry", "rows_ready", "first_tile", "loop_end", "partial_stored", "handshake", "exit"]
+
+
+def attn_timeline_child(args):
+    """Run in a child process with DUSTIN_LIBRARY = the phase-trace build:
+    the step's score and select on the generated inputs, then 80 attention
+    launches over 16 distinct layer buffers replayed from a HIP graph, and
+    the per-work-group phase stamps of the last replay, summarised.  Prints
+    one JSON line."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    import sparse_kv_verification_amd as dk
+    dev = torch.device("cuda:0")
+    sh = synth.preset(args.config)
+    x = synth.make(sh, device=dev)
+    NL, L = 16, 80
+    Ks = [x.K] + [x.K.clone() for _ in range(NL - 1)]
+    off = args.timeline_v_offset
+    assert off >= 0 and off % 256 == 0, "--timeline-v-offset takes a multiple of 256 bytes"
+    if off:
+        Vs = []
+        for _ in range(NL):
+            flat = torch.empty(x.V.numel() + off // 2, dtype=x.V.dtype, device=dev)
+            v = flat[off // 2:].view(x.V.shape)
+            v.copy_(x.V)
+            Vs.append(v)
+    else:
+        Vs = [x.V] + [x.V.clone() for _ in range(NL - 1)]
+    kvs = [dk.KV(Ks[l], Vs[l], x.seq_lens, x.page_table) for l in range(NL)]
+    dkv = [dk.KV(x.Kd[l], None, x.seq_lens, x.page_table) for l in range(sh.L_d)]
+    n_sink, n_window, m = synth.tier_defaults(sh.k)
+    s_d, s_t = dk.dustin_score(dkv, x.q_draft, [kvs[0]], x.q_hist, x.sub_heads, sh.Hq)
+    idx, cnt, _ = dk.dustin_topk(s_d, s_t, x.seq_lens, sh.k, m, n_sink, n_window, want_tier=False)
+    out = torch.empty_like(x.q)
+    ws = dk.Workspace()
+    lib = dk.lib()
+    lib.dustin_trace_attn_restart.restype = None
+    lib.dustin_trace_attn_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+
+    def layers():
+        for l in range(L):
+            dk.dustin_sparse_verify_attn(x.q, kvs[l % NL], idx, cnt, out=out, ws=ws)
+
+    layers()
+    torch.cuda.synchronize()
+    lib.dustin_trace_attn_restart()            # the captured launches take rows 0..79
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            layers()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    e1.synchronize()
+    buf = np.zeros((80, 1024, 8), dtype=np.uint64)
+    rc = lib.dustin_trace_attn_read(buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes)
+    assert rc == 0, f"dustin_trace_attn_read: hipError {rc}"
+    nwg = int((buf[0, :, 0] > 0).sum())        # the array starts zeroed: recorded groups are nonzero
+    st = buf[:, :nwg, :].astype(np.int64)
+    start = st[:, :, 0].min(axis=1)
+    rel = (st[:, :, :7] - start[:, None, None]) / 100.0      # us since the launch's first work-group began
+    ok = st[:, :, :7] > 0
+    res = {"workload": f"{sh.name}: B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d} w={sh.w} k={sh.k}, "
+                       f"{L} launches over {NL} layer buffers, graph replay",
+           "v_offset_bytes": off,
+           "work_groups_per_launch": nwg, "us_per_launch": round(e0.elapsed_time(e1) * 1e3 / L, 2),
+           "launch_span_us_p50": round(float(np.median((st[:, :, 6].max(axis=1) - start) / 100.0)), 2),
+           "gap_between_launches_us_p50": round(float(np.median((start[1:] - st[:-1, :, 6].max(axis=1)) / 100.0)), 2),
+           "phases_us_since_launch_start_p0_p50_p90_p100": {}}
+    for i, nm in enumerate(TIMELINE_PHASES):
+        v = rel[:, :, i][ok[:, :, i]]
+        if v.size:
+            res["phases_us_since_launch_start_p0_p50_p90_p100"][nm] = [
+                round(float(np.percentile(v, q)), 2) for q in (0, 50, 90, 100)]
+    loop = np.where(ok[:, :, 2] & ok[:, :, 3], rel[:, :, 3] - rel[:, :, 2], np.nan)   # a split with no tile: none
+    wg = np.arange(nwg)
+    splits = nwg // (sh.B * sh.Hkv)
+    head = (wg // splits) % sh.Hkv
+    xcc = (st[:, :, 7] >> 8) & 0xF
+    res["token_loop_us_by_kv_head"] = {int(h): round(float(np.nanmean(loop[:, head == h])), 2)
+                                       for h in range(sh.Hkv)}
+    res["token_loop_us_by_xcd"] = {int(c): round(float(np.nanmean(loop[xcc == c])), 2)
+                                   for c in range(8) if (xcc == c).any()}
+    res["paths"] = {["one split", "merged at once", "merged after arriving last", "published only"][int(p)]:
+                    int(((st[:, :, 7] & 0xFF) == p).sum()) for p in np.unique(st[:, :, 7] & 0xFF)}
+    print(json.dumps(res), flush=True)
+
+
+def attn_timeline(args):
+    """The attention phase timeline from the phase-trace build, in a child
+    process (the trace build exports the same entry points)."""
+    import subprocess
+    if not os.path.exists(TRACE_LIB):
+        log("attention timeline skipped: no phase-trace build (python -m sparse_kv_verification_amd.build --trace)")
+        return None
+    env = dict(os.environ, DUSTIN_LIBRARY=TRACE_LIB)
+    r = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), "--attn-timeline-child", "--config",
+                        args.config], capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        log("attention timeline failed: " + (r.stderr or "")[-2000:])
+        return None
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    ph = res["phases_us_since_launch_start_p0_p50_p90_p100"]
+    log(f"attention timeline (phase-trace build, {res['us_per_launch']} us/launch): " +
+        ", ".join(f"{k} p50 {v[1]} max {v[3]}" for k, v in ph.items()) +
+        f"; token loop by KV head {res['token_loop_us_by_kv_head']}")
+    return res
+
+
 def main():
     args = parse()
+    if args.attn_timeline_child:
+        return attn_timeline_child(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -383,7 +508,7 @@ def main():
             f"sparse step is {dense['speedup_sparse_step_vs_dense_attention']:.2f}x faster, "
             f"sparse attention alone {dense['speedup_sparse_attention_vs_dense_attention']:.2f}x")
 
-    ceil = None if args.no_ceilings else ceilings(args, sh, x, idx, cnt, timed)
+    ceil = None if args.no_ceilings else ceilings(args, sh, x, Ks, Vs, idx, cnt, cap, timed)
     traffic = measured_traffic()
     step_gbps = bytes_["step"] / step_us / 1e3
     attn_gbps = bytes_["attn_per_layer"] / attn_launch_us / 1e3
@@ -455,6 +580,8 @@ def main():
         res["verification_window"] = window_step(args, sh, x, Ks, Vs, k, m, n_sink, n_window, cap, timed)
     if not args.no_configs:
         res["other_configs"] = other_configs(args, cap, timed)
+    if not args.no_timeline and args.config == "c4":
+        res["attention_timeline"] = attn_timeline(args)
     print(json.dumps(res), flush=True)
 
 
@@ -462,14 +589,16 @@ SWEEP_DELTAS = (1, 4, 16, 64)
 SWEEP_KS = (128, 256, 512, 1024, 2048)
 
 
-def ceilings(args, sh, x, idx, cnt, timed):
+def ceilings(args, sh, x, Ks, Vs, idx, cnt, cap, timed):
     """Achievable HBM rates on this part, measured with the library's
     measurement kernels (dustin_probe_*): a streaming read of 4 GiB with the
     nontemporal and the default cache policy (each after 4 GiB of other
     reads, so nothing is cached), the gather of the step's K/V rows (the
     rows the attention reads for the current index set: 256-byte head rows
-    of K and V, the attention's work split) and a 128 MiB re-read that the
-    256 MiB last-level cache (MALL) could serve, cold and warm."""
+    of K and V, the attention's work split), timed like the attention (one
+    launch per layer buffer, L launches replayed from a HIP graph), and a
+    128 MiB re-read that the 256 MiB last-level cache (MALL) could serve,
+    cold and warm, with either policy."""
     import torch
     import sparse_kv_verification_amd as dk
     dev = x.q.device
@@ -506,26 +635,37 @@ def ceilings(args, sh, x, idx, cnt, timed):
     rows = ((torch.arange(B, device=dev)[:, None, None] * N + jj[:, None, :]) * Hkv
             + torch.arange(Hkv, device=dev)[None, :, None])                # [B][Hkv][k]
     rows = rows.to(torch.int32).reshape(-1).contiguous()
-    us = once(lambda: dk.dustin_probe_gather_rows(x.K, rows, 256, 256, base2=x.V))
+    def gather_layers():
+        for l in range(len(Ks)):
+            dk.dustin_probe_gather_rows(Ks[l], rows, 256, 256, base2=Vs[l])
+
+    us = graph_time(args, gather_layers, cap, timed, max(2, args.steps // 4)) / len(Ks)
     gb = rows.numel() * 256 * 2
     out["gather_kv_rows_GBps"] = round(gb / us / 1e3, 1)
     out["gather_kv_rows_us"] = round(us, 2)
     out["gather_kv_rows_bytes"] = gb
-    # MALL: a 128 MiB buffer read cold, then again at once (warm)
-    small = big[: (128 << 20) // 4]
-    cold, warm = [], []
-    for _ in range(reps):
-        dk.dustin_probe_stream_read(other, True, sink)
-        for lst in (cold, warm):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            dk.dustin_probe_stream_read(small, True, sink)
-            e1.record()
-            e1.synchronize()
-            lst.append(e0.elapsed_time(e1) * 1e3)
-    mb = small.numel() * 4
-    out["mall_128MiB_cold_GBps"] = round(mb / sorted(cold)[reps // 2] / 1e3, 1)
-    out["mall_128MiB_warm_GBps"] = round(mb / sorted(warm)[reps // 2] / 1e3, 1)
+    # MALL: 128 MiB reads, four back-to-back under one pair of events: cold
+    # = four distinct 128 MiB regions after 4 GiB of other reads; warm = one
+    # region read four times after an untimed read of it
+    mb = 128 << 20
+    regions = [big[i * (mb // 4):(i + 1) * (mb // 4)] for i in range(4)]
+    for nt in (True, False):
+        cold, warm = [], []
+        for _ in range(reps):
+            for lst, bufs in ((cold, regions), (warm, [regions[0]] * 4)):
+                dk.dustin_probe_stream_read(other, True, sink)
+                if lst is warm:
+                    dk.dustin_probe_stream_read(regions[0], nt, sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for r in bufs:
+                    dk.dustin_probe_stream_read(r, nt, sink)
+                e1.record()
+                e1.synchronize()
+                lst.append(e0.elapsed_time(e1) * 1e3)
+        pol = "nontemporal" if nt else "default"
+        out[f"mall_128MiB_cold_{pol}_GBps"] = round(4 * mb / sorted(cold)[reps // 2] / 1e3, 1)
+        out[f"mall_128MiB_warm_{pol}_GBps"] = round(4 * mb / sorted(warm)[reps // 2] / 1e3, 1)
     del big, other
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -724,18 +864,31 @@ def other_configs(args, cap, timed):
         o = torch.empty_like(x.q)
         ws_s, ws_k, ws_a = dk.Workspace(), dk.Workspace(), dk.Workspace()
 
-        def step():
+        def score():
             dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s)
+
+        def select():
             dk.dustin_topk(s_d, s_t, x.seq_lens, k, mm, ns, nw, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+
+        def attn():
             dk.dustin_sparse_verify_attn(x.q, kv, idx, cnt, out=o, ws=ws_a)
 
-        us = graph_time(args, step, cap, timed, max(3, args.steps // 2))
+        def step():
+            score()
+            select()
+            attn()
+
+        reps = max(3, args.steps // 2)
+        us = graph_time(args, step, cap, timed, reps)
+        parts = {nm: round(graph_time(args, fn, cap, timed, reps), 1)
+                 for nm, fn in (("score", score), ("select", select), ("attention", attn))}
         by = algorithmic_bytes(sh, x, k, cnt, x.sub_heads)["step"]
         out[name] = {"workload": f"{sh.name}: B={sh.B} n={sh.n}{' (ragged, paged)' if sh.n_lo else ''} "
                                  f"Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d} w={sh.w} k={k} {sh.dtype}, one layer",
                      "us_per_step": round(us, 1), "GBps": round(by / us / 1e3, 1),
-                     "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by}
-        log(f"{name}: one-layer step {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+                     "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by,
+                     "components_us": parts}
+        log(f"{name}: one-layer step {us:.1f} us, {by / us / 1e3:.0f} GB/s; parts {parts}")
         del x, kv, dkv, s_d, s_t
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -12,7 +12,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdustin.so")
+# DUSTIN_LIBRARY selects another build of the same library (the phase-trace
+# build, libdustin_trace.so); by default the in-tree libdustin.so.
+LIB_PATH = os.environ.get("DUSTIN_LIBRARY") or os.path.join(_HERE, "libdustin.so")
 
 DUSTIN_F32 = 0
 DUSTIN_BF16 = 1

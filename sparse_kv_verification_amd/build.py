@@ -35,9 +35,9 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -47,19 +47,27 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile every source and link libdustin.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+TRACE_LIB = os.path.join(HERE, "libdustin_trace.so")
+
+
+def build(verbose=False, trace=False):
+    """Compile every source and link libdustin.so; returns its path.  With
+    trace=True, the phase-trace build instead (libdustin_trace.so: the same
+    sources with DUSTIN_ATTN_TRACE, see include/dustin_trace.h)."""
+    build_dir = BUILD + ("_trace" if trace else "")
+    lib = TRACE_LIB if trace else LIB
+    extra = ("-DDUSTIN_ATTN_TRACE",) if trace else ()
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

@@ -64,6 +64,7 @@ struct AttnArgs {
     // [B][w][Hkv][D] inputs, and split 0 of each (b, g) also writes them into
     // the cache (the append and the attention in one launch)
     const char *k_win, *v_win;
+    int32_t trace_slot;      // phase-trace builds only: which trace row this launch fills
 };
 
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);

@@ -33,6 +33,40 @@
 
 namespace dustin {
 
+// Phase trace (builds with DUSTIN_ATTN_TRACE only; the library proper has
+// none of it): thread 0 of every work-group of the bf16 kernel records the
+// 100 MHz real-time counter at kernel entry, when the row table is ready,
+// when the first tile has landed, at the end of the token loop, after the
+// split partial is stored, after the split handshake and at exit, plus the
+// path it took (0 one split, 1 merged at once, 2 merged after arriving last,
+// 3 published only) and the XCD it ran on.  Launch l fills row l mod
+// kTraceLaunches of g_attn_trace.
+#ifdef DUSTIN_ATTN_TRACE
+constexpr int kTraceLaunches = 80, kTraceGroups = 1024;
+__device__ unsigned long long g_attn_trace[kTraceLaunches][kTraceGroups][8];
+__device__ __forceinline__ unsigned long long trace_clock() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ unsigned trace_xcc() {
+    unsigned v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v;
+}
+#define ATTN_TRACE_DECL unsigned long long trace_t[7] = {trace_clock(), 0, 0, 0, 0, 0, 0}
+#define ATTN_TRACE(i) (trace_t[i] = trace_clock())
+#define ATTN_TRACE_DUMP(path)                                                                        \
+    do {                                                                                             \
+        if (threadIdx.x == 0 && blockIdx.x < kTraceGroups) {                                         \
+            unsigned long long *o_ = g_attn_trace[a.trace_slot % kTraceLaunches][blockIdx.x];        \
+            for (int i_ = 0; i_ < 6; ++i_) o_[i_] = trace_t[i_];                                     \
+            o_[6] = trace_clock();                                                                   \
+            o_[7] = (unsigned long long)(path) | ((unsigned long long)trace_xcc() << 8);             \
+        }                                                                                            \
+    } while (0)
+#else
+#define ATTN_TRACE_DECL
+#define ATTN_TRACE(i)
+#define ATTN_TRACE_DUMP(path)
+#endif
+
 // All-zero stand-in for absent rows (masked tokens still go through the DMA
 // so that every lane of every tile has a defined, finite source).
 __device__ __align__(256) uint8_t g_zero_row[1024] = {0};
@@ -194,6 +228,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     __shared__ int s_flag;
     extern __shared__ int rows[];   // [a.tps] physical rows, sized at launch
 
+    ATTN_TRACE_DECL;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rbw = wave % RB, th = wave / RB;
     const int split = blockIdx.x % a.splits;
@@ -304,6 +339,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     wait_vmcnt<0>();
     lds_barrier();
     const bool all_rows_valid = (s_flag == 0);
+    ATTN_TRACE(1);
 
     f32x4 o[DT];
 #pragma unroll
@@ -424,6 +460,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         // own DMA of tile i done (tiles issued after it may stay in flight)
         wait_tile<NBUF - 2, 2 * NIW>(min(ntiles - 1 - i, NBUF - 2));
         lds_barrier();   // tile i visible to all waves; buffer (i-1) free
+        if (i == 0) ATTN_TRACE(2);
         {
             const int nxt = i + NBUF - 1;
             if (nxt < ntiles) issue(nxt, nxt % NBUF);
@@ -431,6 +468,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int sub = th; sub < T / 16; sub += NTH) compute_sub(i, i % NBUF, sub);
     }
 
+    ATTN_TRACE(3);
     lsum = group4_sum(lsum);
     // Ring no longer read (every tile's DMA has been waited for): reuse it for
     // the share fold.  LDS-only barriers from here on, so the split
@@ -493,6 +531,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             }
             if (a.lse && th == 0 && lane < 16) a.lse[hrow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
         }
+        ATTN_TRACE_DUMP(0);
         return;
     }
 
@@ -519,7 +558,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < E / 4; ++c) st_coherent4(po, (uint32_t)((c * NT + tid) * 16), acc[c]);
     }
-    if (tid == 0) s_flag = (seen == a.splits - 1);
+    ATTN_TRACE(4);
+    const bool merged_at_once = (seen == a.splits - 1);
+    if (tid == 0) s_flag = merged_at_once;
     lds_barrier();   // the partial stores stay in flight
     if (!s_flag) {
         wait_all_mem();
@@ -527,8 +568,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         if (tid == 0)
             s_flag = __hip_atomic_fetch_add(&a.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
         __syncthreads();
-        if (!s_flag) return;
+        if (!s_flag) {
+            ATTN_TRACE(5);
+            ATTN_TRACE_DUMP(3);
+            return;
+        }
     }
+    ATTN_TRACE(5);
     // merge: each lane folds its (row, E columns) slice over the splits, in
     // split order; the partials of up to MB splits are loaded together
     // before any is folded, so a batch costs one memory round trip.
@@ -587,6 +633,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
             if (a.lse && th == 0 && lane < 16) a.lse[hrow] = (Lt > 0.f) ? (Mt + __log2f(Lt)) * kLn2 : kNegInf;
         }
     }
+    ATTN_TRACE_DUMP(merged_at_once ? 1 : 2);
     if (tid == 0) a.counters[bg] = 0;
 }
 
@@ -804,7 +851,15 @@ static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+#ifdef DUSTIN_ATTN_TRACE
+static int g_trace_launches = 0;
+#endif
+
+hipError_t launch_attn(const AttnArgs &a_in, const AttnPlan &p, hipStream_t s) {
+    AttnArgs a = a_in;
+#ifdef DUSTIN_ATTN_TRACE
+    a.trace_slot = g_trace_launches++;
+#endif
     const dim3 grid((unsigned)((size_t)a.kv.B * a.kv.Hkv * p.splits));
     if (a.kv.f32) {
         switch (a.kv.D) {
@@ -834,3 +889,12 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
 }
 
 }  // namespace dustin
+
+#ifdef DUSTIN_ATTN_TRACE
+// Trace access of the phase-trace build (declared in include/dustin_trace.h).
+extern "C" int dustin_trace_attn_read(void *host_dst, size_t bytes) {
+    if (bytes < sizeof(dustin::g_attn_trace)) return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(dustin::g_attn_trace), sizeof(dustin::g_attn_trace));
+}
+extern "C" void dustin_trace_attn_restart(void) { dustin::g_trace_launches = 0; }
+#endif
