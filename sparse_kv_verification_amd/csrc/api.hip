@@ -760,7 +760,7 @@ CandLayout cand_layout(int C, int B, int N_max, int k, bool materialize) {
     L.off_cnt = off;
     off = align_up(off + rows * sizeof(int32_t), 256);
     L.off_flag = off;
-    if ((N_max + 1023) / 1024 > 128) off = align_up(off + rows * N_max, 256);
+    off = align_up(off + topk_plan((int)rows, N_max, k).ws_bytes, 256);   // shared by the candidates' launches
     L.bytes = off;
     return L;
 }
@@ -853,7 +853,7 @@ dustin_status cand_run(CandSide d, CandSide t, int U, const int32_t *unit_ids, i
             a.m = m_cand[c];
             a.idx = idx + off * k;
             a.count = cnt + off;
-            a.flag = (uint8_t *)(ws + L.off_flag) + off * N_max;
+            a.flag = (uint8_t *)(ws + L.off_flag);   // launches in stream order share the select workspace
             e = launch_topk(a, s);
         }
     }

@@ -503,19 +503,540 @@ __global__ __launch_bounds__(TKT) void topk_il_kernel(TopkArgs a) {
     if (tid == 0) a.count[b] = cnt;
 }
 
+// ----------------------------------------------------------------------------
+// Chunked variant for long rows (kMwMinN <= N_max <= kMwMaxN): a sequence is
+// cut into chunks of 4096 positions, one 256-lane work-group per chunk, so a
+// long row's radix passes run on many CUs instead of one.  Lane t of chunk c
+// owns the positions j = 4096 c + 256 i + t, rows i = 0 .. 15 (each key load
+// of a wave reads 64 consecutive floats); position order inside a chunk is
+// row-major, as in the register-resident kernel.
+//
+// The passes are separate launches (the order of the stream is the only
+// synchronisation between them):
+//   mw_begin     tier flags of the sinks and the recent window; per-chunk
+//                [min, max] of the first selection's candidate keys
+//   mw_pass x3   histogram of the candidate keys inside the current window
+//                (2048 bins, digit (key - lo) >> s, as in the register-
+//                resident kernel), written per chunk; the work-group that
+//                arrives last sums the chunks' histograms, finds the bin of
+//                the remaining-th largest key and narrows the window
+//   mw_mark      keys above the window, or, when the window ended as one
+//                value, the lowest positions holding it: the ties before a
+//                chunk are the other chunks' counts in the last pass's bin;
+//                then the next selection's per-chunk [min, max] or the
+//                chunk's kept count
+//   mw_compact   ascending positions, each chunk at the prefix of the kept
+//                counts of the chunks before it
+// Three passes always suffice: the first window spans < 2^32 patterns, so
+// s <= 21, then s <= 10, then s = 0.  A pass whose search has ended returns
+// at once.  Data read across work-groups of one launch (the histograms, the
+// arrival counter) goes through device-coherent accesses.
+
+constexpr int MWT = 256;                   // lanes per chunk work-group
+constexpr int MWW = MWT / 64;              // waves
+constexpr int MWR = 16;                    // positions per lane
+constexpr int MWC = MWT * MWR;             // positions per chunk
+constexpr int kMwBins = 2048;
+constexpr int kMwMaxChunks = 64;
+constexpr int kMwMinN = 32768 + 1;         // shorter rows: the register-resident kernel
+constexpr int kMwMaxN = kMwMaxChunks * MWC;
+
+struct MwState {
+    uint32_t lo, hi;       // the window of key patterns still open
+    int32_t remaining;     // keys still to take from the window
+    int32_t exact;         // every key of the window is taken
+    int32_t fin;           // the search has ended
+    int32_t tie_bin;       // last pass's bin of the threshold value (ranking of ties)
+    int32_t pad[2];
+};
+
+struct MwPtrs {
+    uint32_t *flag;        // [B][C][MWT] 2-bit tier codes of the lane's 16 rows
+    uint32_t *mm;          // [B][C][2] per-chunk min / max candidate pattern
+    int32_t *kept;         // [B][C] kept positions per chunk
+    uint32_t *hist;        // [B][C][kMwBins] per-chunk histogram of the current pass
+    MwState *state;        // [B][2] per selection (0 draft, 1 target)
+    int32_t *ctr;          // [B] arrival counter of the current pass
+    int C;
+};
+
+struct MwLayout {
+    size_t off_flag, off_mm, off_kept, off_hist, off_state, off_ctr, bytes;
+    int C;
+};
+
+MwLayout mw_layout(int B, int N_max) {
+    MwLayout L{};
+    L.C = (N_max + MWC - 1) / MWC;
+    const size_t BC = (size_t)B * L.C;
+    size_t off = 0;
+    L.off_flag = off;
+    off = align_up(off + BC * MWT * 4, 256);
+    L.off_mm = off;
+    off = align_up(off + BC * 2 * 4, 256);
+    L.off_kept = off;
+    off = align_up(off + BC * 4, 256);
+    L.off_hist = off;
+    off = align_up(off + BC * kMwBins * 4, 256);
+    L.off_state = off;
+    off = align_up(off + (size_t)B * 2 * sizeof(MwState), 256);
+    L.off_ctr = off;
+    off = align_up(off + (size_t)B * 4, 256);
+    L.bytes = off;
+    return L;
+}
+
+// Tier sizes of sequence b (the same arithmetic as the kernels above).
+struct MwTiers {
+    int n, se, wb, rest, m_eff, t_cnt;
+};
+__device__ __forceinline__ MwTiers mw_tiers(const TopkArgs &a, int b) {
+    MwTiers T;
+    T.n = min(max(a.seq_lens[a.len_mod ? b % a.len_mod : b], 0), a.N_max);
+    T.se = min(a.n_sink, T.n);
+    T.wb = max(0, T.n - a.n_window);
+    const int np = T.se + (T.n - max(T.wb, T.se));
+    const int budget = a.k - np;
+    T.rest = T.n - np;
+    int m_eff = a.s_draft ? (a.s_target ? a.m : budget) : 0;
+    T.m_eff = max(0, min(m_eff, min(budget, T.rest)));
+    T.t_cnt = max(0, min(budget - T.m_eff, T.rest - T.m_eff));
+    return T;
+}
+// Selection `sel` of sequence b: its score row, K and candidate count.
+__device__ __forceinline__ const float *mw_row(const TopkArgs &a, int b, int sel) {
+    return sel == 0 ? a.s_draft + (int64_t)(a.d_mod ? b % a.d_mod : b) * a.N_max
+                    : a.s_target + (int64_t)(a.t_mod ? b % a.t_mod : b) * a.N_max;
+}
+__device__ __forceinline__ void mw_sel(const MwTiers &T, int sel, int &K, int &ncand) {
+    K = sel == 0 ? T.m_eff : T.t_cnt;
+    ncand = sel == 0 ? T.rest : T.rest - T.m_eff;
+}
+
+__device__ __forceinline__ uint32_t ld_coherent_u32(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent_u32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct MwShared {
+    unsigned hist[kMwBins];
+    int wave_tot[MWW];
+    uint32_t red_lo[MWW], red_hi[MWW];
+    int rowcnt[MWR * MWW];
+    int flag;
+    uint32_t b_lo, b_hi;
+    int b_rem, b_digit, b_above, b_inbin;
+};
+
+// Block-wide min and max (every lane gets them).
+__device__ __forceinline__ void mw_minmax(uint32_t &lo, uint32_t &hi, MwShared &sh) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    }
+    if (lane == 0) {
+        sh.red_lo[wave] = lo;
+        sh.red_hi[wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < MWW; ++w) {
+        lo = min(lo, sh.red_lo[w]);
+        hi = max(hi, sh.red_hi[w]);
+    }
+    __syncthreads();
+}
+
+// Block-wide exclusive prefix of v in lane order, plus the total.
+__device__ __forceinline__ int mw_prefix(int v, int &total, MwShared &sh) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) sh.wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < MWW; ++w) {
+        const int c = sh.wave_tot[w];
+        before += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + incl - v;
+}
+
+// Rank the lane's set bits of `m` (bit i = row i) in the chunk's position
+// order, calling f(i, rank) for each; returns the chunk's total.
+template <class F>
+__device__ __forceinline__ int mw_rank(uint32_t m, MwShared &sh, F &&f) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) {
+        const unsigned long long bal = __ballot((m >> i) & 1u);
+        if (lane == 0) sh.rowcnt[i * MWW + wave] = __popcll(bal);
+    }
+    __syncthreads();
+    // exclusive prefix over the 64 (row, wave) counts in (row, wave) order
+    int total = 0;
+    if (wave == 0) {
+        const int v = sh.rowcnt[lane];
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += u;
+        }
+        sh.rowcnt[lane] = incl - v;
+        if (lane == 63) sh.wave_tot[0] = incl;
+    }
+    __syncthreads();
+    total = sh.wave_tot[0];
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) {
+        const bool mine = (m >> i) & 1u;
+        const unsigned long long bal = __ballot(mine);
+        if (mine) f(i, sh.rowcnt[i * MWW + wave] + __popcll(bal & lt));
+    }
+    __syncthreads();
+    return total;
+}
+
+// Sum over the lanes of the block (every lane gets it).
+__device__ __forceinline__ int mw_sum(int v, MwShared &sh) {
+    int total;
+    (void)mw_prefix(v, total, sh);
+    return total;
+}
+
+// Candidate keys of rows `cand` of this lane: per-chunk min and max, stored
+// by lane 0.
+__device__ __forceinline__ void mw_store_minmax(const float *row, uint32_t cand, int j0, MwShared &sh, uint32_t *mm) {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i)
+        if ((cand >> i) & 1u) {
+            const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+    mw_minmax(lo, hi, sh);
+    if (threadIdx.x == 0) {
+        st_coherent_u32(mm, lo);
+        st_coherent_u32(mm + 1, hi);
+    }
+}
+
+// Rows of this lane whose position is below n.
+__device__ __forceinline__ uint32_t mw_valid(int j0, int n) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) v |= (uint32_t)(j0 + i * MWT < n) << i;
+    return v;
+}
+// Rows whose 2-bit tier code is 0 (not kept so far).
+__device__ __forceinline__ uint32_t mw_free(uint32_t fw) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) v |= (uint32_t)(((fw >> (2 * i)) & 3u) == 0u) << i;
+    return v;
+}
+
+__global__ __launch_bounds__(MWT) void mw_begin(TopkArgs a, MwPtrs p) {
+    __shared__ MwShared sh;
+    const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
+    const MwTiers T = mw_tiers(a, b);
+    const int j0 = c * MWC + t;
+    const uint32_t valid = mw_valid(j0, T.n);
+    uint32_t fw = 0, prot = 0;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) {
+        const int j = j0 + i * MWT;
+        prot |= (uint32_t)(((valid >> i) & 1u) && (j < T.se || j >= T.wb)) << i;
+    }
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) fw |= ((prot >> i) & 1u) << (2 * i);
+    p.flag[((size_t)b * p.C + c) * MWT + t] = fw;
+    const int sel = a.s_draft ? 0 : 1;   // the first selection of the call
+    int K, ncand;
+    mw_sel(T, sel, K, ncand);
+    if (K > 0 && K < ncand) mw_store_minmax(mw_row(a, b, sel), valid & ~prot, j0, sh, p.mm + ((size_t)b * p.C + c) * 2);
+    if (c == 0 && t == 0) __hip_atomic_store(&p.ctr[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int SEL>
+__global__ __launch_bounds__(MWT) void mw_pass(TopkArgs a, MwPtrs p, int pass) {
+    __shared__ MwShared sh;
+    const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const MwTiers T = mw_tiers(a, b);
+    int K, ncand;
+    mw_sel(T, SEL, K, ncand);
+    if (K <= 0 || K >= ncand) return;   // the same for every chunk of the sequence
+    MwState *st = p.state + (size_t)b * 2 + SEL;
+    uint32_t lo, hi;
+    int remaining;
+    if (pass == 0) {
+        lo = 0xffffffffu;
+        hi = 0u;
+        if (t < p.C) {
+            lo = ld_coherent_u32(p.mm + ((size_t)b * p.C + t) * 2);
+            hi = ld_coherent_u32(p.mm + ((size_t)b * p.C + t) * 2 + 1);
+        }
+        mw_minmax(lo, hi, sh);
+        remaining = K;
+    } else {
+        if (t == 0) {
+            sh.flag = (int)ld_coherent_u32((const uint32_t *)&st->fin);
+            sh.b_lo = ld_coherent_u32(&st->lo);
+            sh.b_hi = ld_coherent_u32(&st->hi);
+            sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
+        }
+        __syncthreads();
+        if (sh.flag) return;
+        lo = sh.b_lo;
+        hi = sh.b_hi;
+        remaining = sh.b_rem;
+    }
+    const uint32_t r = hi - lo;
+    const int bl = r ? 32 - __clz((int)r) : 0;
+    const int s = max(0, bl - 11);
+    for (int i = t; i < kMwBins; i += MWT) sh.hist[i] = 0;
+    __syncthreads();
+    const int j0 = c * MWC + t;
+    const uint32_t cand = mw_valid(j0, T.n) & mw_free(p.flag[((size_t)b * p.C + c) * MWT + t]);
+    const float *row = mw_row(a, b, SEL);
+#pragma unroll
+    for (int i = 0; i < MWR; ++i)
+        if ((cand >> i) & 1u) {
+            const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
+            if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key - lo) >> s], 1u);
+        }
+    __syncthreads();
+    // this chunk's histogram, written through (8 consecutive bins per lane)
+    uint32_t *hrow = p.hist + ((size_t)b * p.C + c) * kMwBins;
+    const __amdgpu_buffer_rsrc_t hr = coherent_rsrc(hrow, kMwBins * 4);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4 *)&sh.hist[8 * t + 4 * q], hr,
+                                               (uint32_t)((8 * t + 4 * q) * 4), 0, kCachePolicySc1);
+    wait_all_mem();
+    __syncthreads();
+    if (t == 0) sh.flag = __hip_atomic_fetch_add(&p.ctr[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.C - 1;
+    __syncthreads();
+    if (!sh.flag) return;
+    // last to arrive: sum the chunks' histograms (lane t: bins 8t .. 8t + 7)
+    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const __amdgpu_buffer_rsrc_t hall =
+        coherent_rsrc(p.hist + (size_t)b * p.C * kMwBins, (uint32_t)(p.C * kMwBins * 4));
+    // eight chunks' loads in flight before any is added (loads past the
+    // last chunk fall outside the resource and read 0)
+    for (int c0 = 0; c0 < p.C; c0 += 8) {
+        u32x4 u[8][2];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                u[q][h2] = __builtin_amdgcn_raw_buffer_load_b128(
+                    hall, (uint32_t)(((c0 + q) * kMwBins + 8 * t + 4 * h2) * 4), 0, kCachePolicySc1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[e] += u[q][0][e];
+                h[4 + e] += u[q][1][e];
+            }
+    }
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) local += (int)h[q];
+    // keys in the bins of the lanes above this one (higher bins = larger keys)
+    int incl = local;   // inclusive suffix sum within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(incl, o, 64);
+        if (lane + o < 64) incl += v;
+    }
+    if (lane == 0) sh.wave_tot[wave] = incl;
+    __syncthreads();
+    int above = incl - local;
+#pragma unroll
+    for (int w = 0; w < MWW; ++w) above += (w > wave) ? sh.wave_tot[w] : 0;
+    if (above < remaining && remaining <= above + local) {
+        int acc = above;
+#pragma unroll
+        for (int q = 7; q >= 0; --q) {
+            const int cq = (int)h[q];
+            if (acc < remaining && remaining <= acc + cq) {
+                sh.b_digit = 8 * t + q;
+                sh.b_above = acc;
+                sh.b_inbin = cq;
+            }
+            acc += cq;
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        const int rem = remaining - sh.b_above;
+        const uint32_t nlo = lo + ((uint32_t)sh.b_digit << s);
+        const uint32_t nhi = min(hi, nlo + ((1u << s) - 1u));
+        const int exact = rem == sh.b_inbin;
+        st_coherent_u32(&st->lo, nlo);
+        st_coherent_u32(&st->hi, nhi);
+        st_coherent_u32((uint32_t *)&st->remaining, (uint32_t)rem);
+        st_coherent_u32((uint32_t *)&st->exact, (uint32_t)exact);
+        st_coherent_u32((uint32_t *)&st->fin, (uint32_t)(exact || s == 0));
+        st_coherent_u32((uint32_t *)&st->tie_bin, (uint32_t)sh.b_digit);
+        __hip_atomic_store(&p.ctr[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Mark the selection SEL in the chunk's tier codes; then either the per-chunk
+// [min, max] of the target candidates (next_mm) or the chunk's kept count.
+template <int SEL>
+__global__ __launch_bounds__(MWT) void mw_mark(TopkArgs a, MwPtrs p, int next_mm, int count) {
+    __shared__ MwShared sh;
+    const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
+    const MwTiers T = mw_tiers(a, b);
+    int K, ncand;
+    mw_sel(T, SEL, K, ncand);
+    const int j0 = c * MWC + t;
+    const uint32_t valid = mw_valid(j0, T.n);
+    uint32_t *fwp = p.flag + ((size_t)b * p.C + c) * MWT + t;
+    uint32_t fw = *fwp;
+    const uint32_t cand = valid & mw_free(fw);
+    uint32_t sel = 0;
+    if (K > 0 && K >= ncand) {
+        sel = cand;
+    } else if (K > 0) {
+        const MwState *st = p.state + (size_t)b * 2 + SEL;
+        if (t == 0) {
+            sh.b_lo = ld_coherent_u32(&st->lo);
+            sh.b_hi = ld_coherent_u32(&st->hi);
+            sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
+            sh.b_above = (int)ld_coherent_u32((const uint32_t *)&st->exact);
+            sh.b_digit = (int)ld_coherent_u32((const uint32_t *)&st->tie_bin);
+        }
+        __syncthreads();
+        const uint32_t lo = sh.b_lo, hi = sh.b_hi;
+        const int exact = sh.b_above, tie_bin = sh.b_digit, remaining = sh.b_rem;
+        const float *row = mw_row(a, b, SEL);
+        uint32_t tie = 0;
+#pragma unroll
+        for (int i = 0; i < MWR; ++i)
+            if ((cand >> i) & 1u) {
+                const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
+                sel |= (uint32_t)(key > hi || (exact && key >= lo)) << i;
+                tie |= (uint32_t)(!exact && key == lo) << i;
+            }
+        if (!exact) {
+            // ties in the chunks before this one: their counts in the last
+            // pass's bin of the threshold value
+            int before = 0;
+            if (t < c)
+                before = (int)ld_coherent_u32(p.hist + ((size_t)b * p.C + t) * kMwBins + tie_bin);
+            before = mw_sum(before, sh);
+            const int need = remaining - before;
+            mw_rank(tie, sh, [&](int i, int rank) {
+                if (rank < need) sel |= 1u << i;
+            });
+        }
+    }
+    const uint32_t code = SEL == 0 ? 2u : 3u;
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) fw |= (((sel >> i) & 1u) * code) << (2 * i);
+    *fwp = fw;
+    if (next_mm) {
+        int Kt, nct;
+        mw_sel(T, 1, Kt, nct);
+        if (Kt > 0 && Kt < nct)
+            mw_store_minmax(mw_row(a, b, 1), valid & mw_free(fw), j0, sh, p.mm + ((size_t)b * p.C + c) * 2);
+    }
+    if (count) {
+        const int kept = mw_sum(__popc(valid & ~mw_free(fw)), sh);
+        if (t == 0) st_coherent_u32((uint32_t *)&p.kept[(size_t)b * p.C + c], (uint32_t)kept);
+    }
+}
+
+__global__ __launch_bounds__(MWT) void mw_compact(TopkArgs a, MwPtrs p) {
+    __shared__ MwShared sh;
+    const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
+    const MwTiers T = mw_tiers(a, b);
+    const int j0 = c * MWC + t;
+    const uint32_t valid = mw_valid(j0, T.n);
+    const uint32_t fw = p.flag[((size_t)b * p.C + c) * MWT + t];
+    const uint32_t keep = valid & ~mw_free(fw);
+    const int kc = (t < p.C) ? (int)ld_coherent_u32((const uint32_t *)&p.kept[(size_t)b * p.C + t]) : 0;
+    int total;
+    const int ex = mw_prefix(kc, total, sh);   // lane c holds the kept positions before chunk c
+    if (t == c) sh.b_above = ex;
+    __syncthreads();
+    const int before = sh.b_above;
+    int32_t *idx = a.idx + (int64_t)b * a.k;
+    int8_t *tier = a.tier ? a.tier + (int64_t)b * a.k : nullptr;
+    mw_rank(keep, sh, [&](int i, int rank) {
+        const int pos = before + rank;
+        if (pos < a.k) {
+            idx[pos] = j0 + i * MWT;
+            if (tier) tier[pos] = (int8_t)(((fw >> (2 * i)) & 3u) - 1u);
+        }
+    });
+    const int cnt = min(total, a.k);
+    for (int q = cnt + c * MWT + t; q < a.k; q += p.C * MWT) {
+        idx[q] = -1;
+        if (tier) tier[q] = -1;
+    }
+    if (c == 0 && t == 0) a.count[b] = cnt;
+}
+
+static hipError_t launch_topk_mw(const TopkArgs &a, hipStream_t s) {
+    const MwLayout L = mw_layout(a.B, a.N_max);
+    char *ws = (char *)a.flag;
+    MwPtrs p{};
+    p.flag = (uint32_t *)(ws + L.off_flag);
+    p.mm = (uint32_t *)(ws + L.off_mm);
+    p.kept = (int32_t *)(ws + L.off_kept);
+    p.hist = (uint32_t *)(ws + L.off_hist);
+    p.state = (MwState *)(ws + L.off_state);
+    p.ctr = (int32_t *)(ws + L.off_ctr);
+    p.C = L.C;
+    const dim3 grid((unsigned)(a.B * L.C)), block(MWT);
+    hipLaunchKernelGGL(mw_begin, grid, block, 0, s, a, p);
+    if (a.s_draft) {
+        for (int pass = 0; pass < 3; ++pass) hipLaunchKernelGGL(mw_pass<0>, grid, block, 0, s, a, p, pass);
+        hipLaunchKernelGGL(mw_mark<0>, grid, block, 0, s, a, p, a.s_target ? 1 : 0, a.s_target ? 0 : 1);
+    }
+    if (a.s_target) {
+        for (int pass = 0; pass < 3; ++pass) hipLaunchKernelGGL(mw_pass<1>, grid, block, 0, s, a, p, pass);
+        hipLaunchKernelGGL(mw_mark<1>, grid, block, 0, s, a, p, 0, 1);
+    }
+    hipLaunchKernelGGL(mw_compact, grid, block, 0, s, a, p);
+    return hipGetLastError();
+}
+
 TopkPlan topk_plan(int B, int N_max, int k) {
     (void)k;
     TopkPlan p{};
     p.off_flag = 0;
-    p.ws_bytes = align_up((size_t)B * N_max, 256);
+    if (N_max < kMwMinN) p.ws_bytes = 256;                          // register-resident: no workspace
+    else if (N_max <= kMwMaxN) p.ws_bytes = mw_layout(B, N_max).bytes;
+    else p.ws_bytes = align_up((size_t)B * N_max, 256);
     return p;
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     const int P = (a.N_max + TKT - 1) / TKT;   // positions per lane
+    if (a.N_max >= kMwMinN && a.N_max <= kMwMaxN) return launch_topk_mw(a, s);
     if (P <= 32) hipLaunchKernelGGL(topk_il_kernel<1>, dim3(a.B), dim3(TKT), 0, s, a);
-    else if (P <= 64) hipLaunchKernelGGL(topk_il_kernel<2>, dim3(a.B), dim3(TKT), 0, s, a);
-    else if (P <= 128) hipLaunchKernelGGL(topk_il_kernel<4>, dim3(a.B), dim3(TKT), 0, s, a);
     else hipLaunchKernelGGL(topk_kernel, dim3(a.B), dim3(TKT), 0, s, a);
     return hipGetLastError();
 }

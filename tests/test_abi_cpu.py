@@ -254,7 +254,12 @@ def test_workspace_sizes_are_shape_only(L):
     assert 0 < a < b
     assert L.dustin_attn_workspace_bytes(0, 4, 64, 8, 128, 2048) == 0
     assert L.dustin_score_workspace_bytes(16, 32768, 24, 14, 4, 8) > 16 * 8 * 32768 * 4
-    assert L.dustin_topk_workspace_bytes(16, 32768, 2048) >= 16 * 32768
+    # rows up to 32768 positions: register-resident select, no workspace beyond the minimum;
+    # 32769 .. 262144: per-chunk histograms (4096-position chunks, 2048 bins of 4 bytes);
+    # longer: one tier byte per position
+    assert L.dustin_topk_workspace_bytes(16, 32768, 2048) == 256
+    assert L.dustin_topk_workspace_bytes(8, 131072, 4096) >= 8 * 32 * 2048 * 4
+    assert L.dustin_topk_workspace_bytes(2, 300000, 4096) >= 2 * 300000
 
 
 def test_bf16_attention_refuses_head_dim_32(L):

@@ -150,6 +150,14 @@ SELECT_CASES = [
     (dict(B=3, N=65536, k=2048, m=1006, ns=4, nw=32, ties=True), "two-words-ties"),
     (dict(B=2, N=32768, k=2048, m=1006, ns=4, nw=32, ties=False, equal=True), "all-equal"),
     (dict(B=2, N=98304, k=4096, m=2030, ns=4, nw=32, ties=False, narrow=True), "narrow-range"),
+    # rows of 32769 .. 262144 positions go through the chunked (multi-work-group) select
+    (dict(B=3, N=50000, k=1500, m=600, ns=4, nw=32, ties=True, empty_last=True), "chunked-ties-empty"),
+    (dict(B=2, N=65536, k=2048, m=1006, ns=4, nw=32, ties=False, equal=True), "chunked-all-equal"),
+    (dict(B=2, N=70000, k=900, m=50, ns=8, nw=8, ties=True, no_draft=True), "chunked-no-draft"),
+    (dict(B=2, N=70000, k=900, m=50, ns=8, nw=8, ties=True, no_target=True), "chunked-no-target"),
+    (dict(B=2, N=40000, k=50000, m=100, ns=4, nw=32, ties=True), "chunked-k>=n"),
+    (dict(B=2, N=262144, k=8192, m=4000, ns=4, nw=32, ties=True), "chunked-max"),
+    (dict(B=2, N=300000, k=4096, m=2000, ns=4, nw=32, ties=True), "beyond-chunked"),
 ]
 
 
@@ -161,7 +169,7 @@ def test_select_is_bit_exact(cfg, name):
     lens = rng.integers(max(1, N // 3), N + 1, size=B).astype(np.int32)
     lens[0] = N
     if B > 2:
-        lens[-1] = 0 if name == "ties" else lens[-1]
+        lens[-1] = 0 if (name == "ties" or cfg.get("empty_last")) else lens[-1]
     if cfg.get("equal"):     # one key value: every selection is decided by position alone
         sd = np.full((B, N), 0.25, dtype=np.float32)
         st = np.full((B, N), 3.0, dtype=np.float32)
