@@ -1192,6 +1192,30 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     }
 }
 
+// Layer groups of the streaming accumulation, chosen on the device from the
+// actual chunk count (sum over sequences of ceil(n_b / 1024)): the count g <=
+// cap (several groups: an even number of layers each) whose items (chunks x
+// g x heads per item) take the fewest rounds of the persistent grid,
+// weighted by the layers an item streams plus an eighth of a layer of fixed
+// cost per item; ties to fewer groups.  The accumulation kernel and
+// draft_part_sum evaluate it on the same arguments.
+__device__ __forceinline__ int acc_layer_groups(int chunks, int nhi, int L, int cap, int grid) {
+    int best = 1;
+    long long best_cost = -1;
+    for (int lg = 1; lg <= cap; ++lg) {
+        int lpg = (L + lg - 1) / lg;
+        if (lg > 1) lpg += lpg & 1;
+        if ((L + lpg - 1) / lpg != lg) continue;   // not a count that even groups reach
+        const long long items = (long long)chunks * lg * nhi;
+        const long long cost = ((items + grid - 1) / grid) * (8LL * lpg + 1);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = lg;
+        }
+    }
+    return best;
+}
+
 // Accumulation pass, streaming form.  Items (b, 1024-position chunk, layer
 // group) walk round robin over the persistent groups (chunks wholly past n_b
 // only write zeros); wave w owns positions w * 256 .. + 255 of the chunk and
@@ -1218,7 +1242,6 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
     const int N = k0.N_max;
-    const int LG = max(a.acc_groups, 1);
     const int B = k0.B;
     // Items are (b, chunk, layer group) over the chunks that hold positions
     // below n_b only, numbered sequence by sequence (B <= kDraftStatMaxB).
@@ -1230,6 +1253,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
         for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
     }
     __syncthreads();
+    const int LG = acc_layer_groups(pref[B], NHI, a.L_d, max(a.acc_groups, 1), gridDim.x);
     const int GT = LG * NHI;                   // partial groups: (layer group, head)
     const int items = pref[B] * GT;
     if (GT == 1) {   // chunks wholly past n_b: S_Draft = 0 (with layer groups draft_part_sum writes them)
@@ -1368,26 +1392,28 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
 }
 
 // --------------------------------------------------------------- host side
-// Layer groups of the streaming accumulation: with few (sequence, chunk)
-// items (short contexts, small batches) the layers are split into groups of
-// an even number of layers, each group an item of its own with a partial
-// sum, so that about kStreamGroups items fill the persistent grid.  Depends
-// on shapes only, so the workspace size needs no device.
+// Most layer groups the streaming accumulation may split a chunk's layers
+// into (the device picks the count from the actual lengths, at most this):
+// enough that items at full lengths would fill the persistent grid about 16
+// times, at most L_d / 2 groups of two layers.  Depends on shapes only, so
+// the workspace size needs no device.
 int draft_acc_groups(int B, int N_max, int L_d) {
     if (L_d < 4 || L_d % 2 != 0) return 1;
     const long items = (long)B * ((N_max + 1023) / 1024);
-    long lg = (kStreamGroups + items - 1) / items;
+    long lg = (16L * kStreamGroups + items - 1) / items;
     if (lg > L_d / 2) lg = L_d / 2;
-    if (lg <= 1) return 1;
-    int lpg = (int)((L_d + lg - 1) / lg);
-    lpg += lpg & 1;
-    return (L_d + lpg - 1) / lpg;
+    return lg <= 1 ? 1 : (int)lg;
 }
 
-// S_Draft = the layer-group partials summed in group order; positions past
-// n_b are 0 (the partials of chunks wholly past n_b are never written).
-__global__ __launch_bounds__(256) void draft_part_sum(const float *part, int groups, int B, int N,
-                                                      const int32_t *seq_lens, float *out) {
+// S_Draft = the partials (layer group, head) summed in group order; positions
+// past n_b are 0 (the partials of chunks wholly past n_b are never written).
+// With one partial the accumulation kernel has written S_Draft itself.
+__global__ __launch_bounds__(256) void draft_part_sum(const float *part, int nhi, int cap, int L, int grid, int B,
+                                                      int N, const int32_t *seq_lens, float *out) {
+    int chunks = 0;
+    for (int bb = 0; bb < B; ++bb) chunks += (min(max(seq_lens[bb], 0), N) + 1023) / 1024;
+    const int groups = acc_layer_groups(chunks, nhi, L, cap, grid) * nhi;
+    if (groups == 1) return;
     const int64_t n = (int64_t)B * N;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         const int b = (int)(i / N), j = (int)(i - (int64_t)b * N);
@@ -1419,7 +1445,7 @@ ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int H
     // partial sums per (layer group, head): the one-head-per-item form
     // doubles the groups (its use depends on the draft's head geometry, which
     // the workspace query does not carry, so the space is always reserved)
-    if (L_d >= 2) off = align_up(off + (size_t)2 * p.acc_groups * B * N_max * sizeof(float), 256);
+    if (L_d >= 1) off = align_up(off + (size_t)2 * p.acc_groups * B * N_max * sizeof(float), 256);
     p.ws_bytes = off;
     return p;
 }
@@ -1567,17 +1593,16 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
                        a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int lg = a.acc_groups > 1 ? a.acc_groups : 1;
-    b.acc_groups = lg;
-    const int groups = lg * NHI;   // partial sums: (layer group, head)
-    const int acc_items = k0.B * ((k0.N_max + 1023) / 1024) * groups;
-    hipLaunchKernelGGL((draft_acc_stream<RB, PAGED, HALF>), dim3(acc_items < GROUPS ? acc_items : GROUPS),
-                       dim3(256), 0, s, b);
-    if ((e = hipGetLastError()) != hipSuccess || groups == 1) return e;
+    const int cap = a.acc_groups > 1 ? a.acc_groups : 1;   // the device picks <= cap layer groups
+    b.acc_groups = cap;
+    const long acc_items = (long)k0.B * ((k0.N_max + 1023) / 1024) * cap * NHI;   // at full lengths
+    const int grid = acc_items < GROUPS ? (int)acc_items : GROUPS;
+    hipLaunchKernelGGL((draft_acc_stream<RB, PAGED, HALF>), dim3(grid), dim3(256), 0, s, b);
+    if ((e = hipGetLastError()) != hipSuccess || cap * NHI == 1) return e;
     const int64_t n = (int64_t)k0.B * k0.N_max;
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
-    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, groups, k0.B, k0.N_max,
-                       k0.seq_lens, a.s_draft);
+    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, NHI, cap, a.L_d, grid, k0.B,
+                       k0.N_max, k0.seq_lens, a.s_draft);
     return hipGetLastError();
 }
 
