@@ -67,6 +67,8 @@ __all__ = [
     "arr_window",
     "sd_oracle",
     "score_target",
+    "draft_row_lse",
+    "score_draft_given_lse",
     "score_draft",
     "select_verify_set",
     "history_policy",
@@ -340,6 +342,53 @@ def score_draft(q_draft, K_draft, scale=None):
             c = _kv_head_of(h, H_d, Hkv_d)
             logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)  # [Gamma][n]
             out += softmax(logits, axis=-1).sum(axis=0)
+    return out
+
+
+def draft_row_lse(q_draft, K_draft, scale=None):
+    """Row normalisers of the softmaxes that S_Draft sums (blog section 2.2):
+    for draft layer l, draft step g and draft head h,
+        lse[l, g, h] = ln sum_j exp(scale_d * q_draft[l,g,h] . K_draft[l][j][c(h)]),
+    j over the history positions, c(h) = floor(h / G_d).  These are what the
+    draft model's own attention over the history computes for the same
+    queries.  Returns [L_d][Gamma][H_d] (float64); -inf for an empty history.
+    """
+    q_draft = _f64(q_draft)
+    L_d, Gamma, H_d, d_d = q_draft.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_d)
+    out = np.full((L_d, Gamma, H_d), -np.inf)
+    for l in range(L_d):
+        K = _f64(K_draft[l])
+        if K.shape[0] == 0:
+            continue
+        for h in range(H_d):
+            c = _kv_head_of(h, H_d, K.shape[1])
+            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]
+            m = logits.max(axis=-1, keepdims=True)
+            out[l, :, h] = (m + np.log(np.exp(logits - m).sum(axis=-1, keepdims=True)))[:, 0]
+    return out
+
+
+def score_draft_given_lse(q_draft, K_draft, lse, scale=None):
+    """S_Draft with the row normalisers supplied (blog section 2.2; the
+    normalisers are the draft attention's, see draft_row_lse):
+        S_D[j] = sum_{l,g,h} exp(scale_d * q_draft[l,g,h] . K_draft[l][j][c(h)] - lse[l,g,h]).
+    With lse = draft_row_lse(q_draft, K_draft) this is score_draft.
+    """
+    q_draft = _f64(q_draft)
+    lse = _f64(lse)
+    L_d, Gamma, H_d, d_d = q_draft.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_d)
+    n = np.asarray(K_draft[0]).shape[0]
+    out = np.zeros(n)
+    for l in range(L_d):
+        K = _f64(K_draft[l])
+        for h in range(H_d):
+            c = _kv_head_of(h, H_d, K.shape[1])
+            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]
+            out += np.exp(logits - lse[l, :, h][:, None]).sum(axis=0)
     return out
 
 

@@ -31,7 +31,8 @@ MUTATIONS = [
     ("score_target: modulo head map",
      [("g = _kv_head_of(h, Hq, K.shape[1])", "g = h % K.shape[1]")]),
     ("score_draft: no 1/sqrt(d_d) scale",
-     [("logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)", "logits = q_draft[l, :, h, :] @ K[:, c, :].T")]),
+     [("logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)  # [Gamma][n]\n            out += softmax(",
+       "logits = q_draft[l, :, h, :] @ K[:, c, :].T  # [Gamma][n]\n            out += softmax(")]),
     ("score_draft: first draft step only (dropped Gamma sum)",
      [("out += softmax(logits, axis=-1).sum(axis=0)", "out += softmax(logits, axis=-1)[0]")]),
     ("score_draft: softmax over the draft steps instead of the history",
@@ -112,6 +113,23 @@ MUTATIONS = [
       ("blk = K[p * page:min(n, (p + 1) * page)]", "blk = K[p * page:(p + 1) * page]")]),
     ("page_scores: upper face only",
      [("np.maximum(kmin[:, g, :] * qq, kmax[:, g, :] * qq)", "(kmax[:, g, :] * qq)")]),
+    ("draft_row_lse: no 1/sqrt(d_d) scale",
+     [("            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            m = logits.max",
+       "            logits = (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            m = logits.max")]),
+    ("draft_row_lse: modulo head map",
+     [("            c = _kv_head_of(h, H_d, K.shape[1])\n            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            m = logits.max",
+       "            c = h % K.shape[1]\n            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            m = logits.max")]),
+    ("score_draft_given_lse: no 1/sqrt(d_d) scale",
+     [("            logits = scale * (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            out += np.exp(",
+       "            logits = (q_draft[l, :, h, :] @ K[:, c, :].T)   # [Gamma][n]\n            out += np.exp(")]),
+    ("draft_row_lse: max left out of the log-sum-exp",
+     [("out[l, :, h] = (m + np.log(np.exp(logits - m)", "out[l, :, h] = (np.log(np.exp(logits - m)")]),
+    ("score_draft_given_lse: normaliser of step 0 for every step",
+     [("out += np.exp(logits - lse[l, :, h][:, None]).sum(axis=0)",
+       "out += np.exp(logits - lse[l, 0, h]).sum(axis=0)")]),
+    ("score_draft_given_lse: normaliser added instead of subtracted",
+     [("out += np.exp(logits - lse[l, :, h][:, None]).sum(axis=0)",
+       "out += np.exp(logits + lse[l, :, h][:, None]).sum(axis=0)")]),
     ("pages_to_contiguous: page table ignored",
      [("rows = [pool[int(page_row[p])] for p in range(n_pages)]", "rows = [pool[p] for p in range(n_pages)]")]),
 ]

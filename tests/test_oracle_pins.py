@@ -364,6 +364,50 @@ def test_score_head_to_kv_mapping_and_scale():
     np.testing.assert_allclose(sd, np.array([1, 1, 1]) + np.array([0, 0, 1.0]), atol=1e-14)
 
 
+def test_draft_row_lse_closed_forms():
+    # All-zero keys: every logit is 0, so lse = ln n for every (layer, step, head).
+    n = 37
+    qd = np.random.default_rng(13).normal(size=(2, 3, 4, 8))
+    np.testing.assert_allclose(oracle.draft_row_lse(qd, np.zeros((2, n, 2, 8))), math.log(n), rtol=1e-14)
+    # One key per (layer, KV head) with raw logit x, n - 1 zero logits:
+    # lse = ln(exp(x * scale) + n - 1), scale 1/sqrt(d_d) = 1/2 at d_d = 4.
+    # Draft heads 0, 1 read KV head 0 and heads 2, 3 KV head 1 (G_d = 2); the
+    # two layers hold their keys at different strengths.
+    n = 5
+    qd = np.zeros((2, 1, 4, 4))
+    qd[:, 0, :, 0] = 1.0
+    Kd = np.zeros((2, n, 2, 4))
+    Kd[0, 3, 0, 0] = 6.0      # layer 0, KV head 0: x = 6  -> scaled 3
+    Kd[0, 1, 1, 0] = 2.0      # layer 0, KV head 1: x = 2  -> scaled 1
+    Kd[1, 0, 1, 0] = 8.0      # layer 1, KV head 1: x = 8  -> scaled 4; KV head 0 all zero
+    lse = oracle.draft_row_lse(qd, Kd)
+    e = lambda x: math.log(math.exp(x) + n - 1)
+    np.testing.assert_allclose(lse[0, 0], [e(3), e(3), e(1), e(1)], rtol=1e-14)
+    np.testing.assert_allclose(lse[1, 0], [math.log(n), math.log(n), e(4), e(4)], rtol=1e-14)
+    # empty history: -inf
+    assert np.isneginf(oracle.draft_row_lse(qd, np.zeros((2, 0, 2, 4)))).all()
+
+
+def test_score_draft_given_lse():
+    # With lse = ln n on all-zero keys every row contributes 1/n per position.
+    n = 9
+    qd = np.random.default_rng(14).normal(size=(2, 3, 4, 8))
+    Kz = np.zeros((2, n, 2, 8))
+    np.testing.assert_allclose(oracle.score_draft_given_lse(qd, Kz, np.full((2, 3, 4), math.log(n))),
+                               2 * 3 * 4 / n, rtol=1e-14)
+    # Each row's terms scale by exp(-delta) when its normaliser grows by delta:
+    # raising one row's lse by ln 2 removes half of that row's mass (1/2 in total).
+    rng = np.random.default_rng(15)
+    qd = rng.normal(size=(2, 2, 4, 8))
+    Kd = rng.normal(size=(2, 23, 2, 8))
+    lse = oracle.draft_row_lse(qd, Kd)
+    full = oracle.score_draft_given_lse(qd, Kd, lse)
+    assert abs(full.sum() - 2 * 2 * 4) < 1e-12
+    lse2 = lse.copy()
+    lse2[1, 0, 3] += math.log(2.0)
+    assert abs(oracle.score_draft_given_lse(qd, Kd, lse2).sum() - (2 * 2 * 4 - 0.5)) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # Paged layout
 # --------------------------------------------------------------------------
