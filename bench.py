@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--timeline-v-offset", type=int, default=0,
                    help="attention timeline with every V buffer placed this many bytes (multiple of 256) past an "
                         "allocation boundary, K left aligned")
+    p.add_argument("--no-lse", action="store_true",
+                   help="skip the labelled step with caller-supplied draft row normalisers")
     p.add_argument("--no-timeline", action="store_true",
                    help="skip the attention phase timeline (phase-trace build of the library, in a child process)")
     p.add_argument("--gpus", type=int, default=1)
@@ -561,6 +563,9 @@ def main():
         "ceilings": ceil,
         "dense_baseline": dense,
     }
+    if not args.no_lse:
+        res["supplied_draft_normalisers"] = supplied_lse_step(args, sh, x, kvs, dkv, k, m, n_sink, n_window, cap,
+                                                              timed, bytes_)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
@@ -583,6 +588,48 @@ def main():
     if not args.no_timeline and args.config == "c4":
         res["attention_timeline"] = attn_timeline(args)
     print(json.dumps(res), flush=True)
+
+
+def supplied_lse_step(args, sh, x, kvs, dkv, k, m, n_sink, n_window, cap, timed, bytes_):
+    """Labelled extra line, never the headline: the step when the caller
+    supplies the draft softmaxes' row normalisers (the draft model's own
+    attention over the history computes them while drafting), so S_Draft
+    reads the draft keys once.  The normalisers come from
+    dustin_draft_row_lse, untimed here (it stands in for the draft model's
+    attention output); its own time is reported beside."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    dev = x.q.device
+    lse = dk.dustin_draft_row_lse(dkv, x.q_draft)
+    s_d = torch.empty((sh.B, kvs[0].desc.N_max), dtype=torch.float32, device=dev)
+    s_t = torch.empty_like(s_d)
+    idx = torch.empty((sh.B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((sh.B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(x.q)
+    ws_s, ws_k, ws_a, ws_l = dk.Workspace(), dk.Workspace(), dk.Workspace(), dk.Workspace()
+
+    def score():
+        dk.dustin_score(dkv, x.q_draft, [kvs[0]], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t, ws=ws_s,
+                        draft_lse=lse)
+
+    def step():
+        score()
+        dk.dustin_topk(s_d, s_t, x.seq_lens, k, m, n_sink, n_window, idx=idx, count=cnt, want_tier=False, ws=ws_k)
+        for l in range(sh.layers):
+            dk.dustin_sparse_verify_attn(x.q, kvs[l], idx, cnt, out=out, ws=ws_a)
+
+    reps = max(3, args.steps // 2)
+    step_us = graph_time(args, step, cap, timed, reps)
+    score_us = graph_time(args, score, cap, timed, reps)
+    lse_us = graph_time(args, lambda: dk.dustin_draft_row_lse(dkv, x.q_draft, out=lse, ws=ws_l), cap, timed, reps)
+    by = bytes_["step"]
+    res = {"label": "not the headline: draft row normalisers supplied by the caller",
+           "us_per_step": round(step_us, 1), "score_us": round(score_us, 1),
+           "step_GBps": round(by / step_us / 1e3, 1), "step_frac_of_hbm_peak": round(by / step_us / 1e3 / HBM_PEAK_GBPS, 4),
+           "draft_row_lse_query_us": round(lse_us, 1)}
+    log(f"supplied draft normalisers (labelled line): step {step_us:.1f} us, score {score_us:.1f} us "
+        f"(the normaliser query itself {lse_us:.1f} us)")
+    return res
 
 
 SWEEP_DELTAS = (1, 4, 16, 64)

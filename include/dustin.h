@@ -133,6 +133,14 @@ typedef struct dustin_kv {
  *  sub_heads      host [S][2] (layer, head) pairs, 0 <= layer < L_t,
  *                 0 <= head < H_t
  *  scale_*        softmax scale; 0 means 1/sqrt(head_dim)
+ *  draft_lse      nullable, device [B][L_d][gamma][H_d] float32: the row
+ *                 normalisers ln sum_{j < n_b} exp(scale_draft * q . k_j) of
+ *                 the draft softmaxes above (what the draft model's own
+ *                 attention over the history computes for these queries;
+ *                 dustin_draft_row_lse gives the same values).  When given,
+ *                 S_Draft reads the draft keys once, using these normalisers
+ *                 as they are, instead of twice; -inf (or any non-finite
+ *                 value) marks an empty row
  *  s_draft        [B][N_max] float32 out, 0 at j >= n_b; NULL or L_d == 0
  *                 skips the draft side
  *  s_target       [B][N_max] float32 out; NULL or S == 0 skips it
@@ -145,11 +153,25 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d,
                            const void *q_hist, const int32_t *sub_heads,
                            int32_t S, int32_t H_t,
                            float scale_draft, float scale_target,
+                           const float *draft_lse,
                            float *s_draft, float *s_target,
                            void *ws, size_t ws_bytes, dustin_stream_t stream);
 
 size_t dustin_score_workspace_bytes(int32_t B, int32_t N_max, int32_t L_d,
                                     int32_t H_d, int32_t gamma, int32_t S);
+
+/*
+ * dustin_draft_row_lse -- the row normalisers of S_Draft's softmaxes (blog
+ * section 2.2): lse_out[b][l][g][h] = ln sum_{j < n_b} exp(scale_draft *
+ * q_draft[b][l][g][h] . Kd_l[b][j][h / G_d]), -inf for an empty history.
+ * Arguments and workspace as for dustin_score's draft side (workspace size
+ * dustin_score_workspace_bytes(B, N_max, L_d, H_d, gamma, 0)); lse_out is
+ * device [B][L_d][gamma][H_d] float32.  One read of the draft keys.
+ */
+dustin_status dustin_draft_row_lse(const dustin_kv *draft_layers, int32_t L_d,
+                                   const void *q_draft, int32_t H_d, int32_t gamma,
+                                   float scale_draft, float *lse_out,
+                                   void *ws, size_t ws_bytes, dustin_stream_t stream);
 
 /*
  * dustin_topk -- the per-sequence verification set I_verify (blog section

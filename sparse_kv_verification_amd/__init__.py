@@ -7,7 +7,8 @@ include/dustin.h); this package only marshals torch tensors into it.
 """
 from ._lib import (  # noqa: F401
     KV, DustinError, DustinKV, Workspace, lib,
-    dustin_append_window_kv, dustin_arr, dustin_commit_window, dustin_score, dustin_sparse_verify_attn,
+    dustin_append_window_kv, dustin_arr, dustin_commit_window, dustin_score, dustin_draft_row_lse,
+    dustin_sparse_verify_attn,
     dustin_sparse_verify_attn_noalloc,
     dustin_page_bounds, dustin_page_scores, dustin_policy_sweep, dustin_topk, dustin_verify_attn,
     dustin_verify_attn_append,

@@ -21,7 +21,7 @@ DUSTIN_BF16 = 1
 STATUS = {0: "DUSTIN_OK", 1: "DUSTIN_ERR_INVALID_ARG", 2: "DUSTIN_ERR_UNSUPPORTED", 3: "DUSTIN_ERR_HIP"}
 
 EXPORTS = [
-    "dustin_score", "dustin_score_workspace_bytes",
+    "dustin_score", "dustin_score_workspace_bytes", "dustin_draft_row_lse",
     "dustin_topk", "dustin_topk_workspace_bytes",
     "dustin_sparse_verify_attn", "dustin_attn_workspace_bytes", "dustin_sparse_verify_attn_noalloc",
     "dustin_verify_attn", "dustin_verify_attn_workspace_bytes", "dustin_verify_attn_append",
@@ -69,7 +69,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         kvp = ctypes.POINTER(DustinKV)
-        L.dustin_score.argtypes = [kvp, i32, vp, i32, i32, kvp, i32, vp, vp, i32, i32, f32, f32, vp, vp, vp, sz, vp]
+        L.dustin_score.argtypes = [kvp, i32, vp, i32, i32, kvp, i32, vp, vp, i32, i32, f32, f32, vp, vp, vp, vp, sz,
+                                   vp]
+        L.dustin_draft_row_lse.argtypes = [kvp, i32, vp, i32, i32, f32, vp, vp, sz, vp]
+        L.dustin_draft_row_lse.restype = ctypes.c_int
         L.dustin_score.restype = ctypes.c_int
         L.dustin_score_workspace_bytes.argtypes = [i32] * 6
         L.dustin_score_workspace_bytes.restype = sz
@@ -322,10 +325,12 @@ def dustin_commit_window(seq_lens, accepted, w):
 
 def dustin_score(draft_kvs, q_draft, target_kvs, q_hist, sub_heads, H_t, s_draft=None, s_target=None,
                  scale_draft=0.0, scale_target=0.0, ws: Workspace | None = None, want_draft=True,
-                 want_target=True):
+                 want_target=True, draft_lse=None):
     """Hybrid importance vectors S_Draft, S_Target ([B][N_max] float32 each).
     q_draft: [B][L_d][gamma][H_d][d_d]; q_hist: [B][S][d]; sub_heads: S
-    (layer, head) pairs into target_kvs."""
+    (layer, head) pairs into target_kvs.  draft_lse (optional, float32
+    [B][L_d][gamma][H_d] on the device): the draft softmaxes' row normalisers
+    (natural log), used as given: S_Draft then reads the draft keys once."""
     ref = (draft_kvs or target_kvs)[0]
     B, N = ref.desc.B, ref.desc.N_max
     dev = (q_draft if q_draft is not None else q_hist).device
@@ -340,6 +345,10 @@ def dustin_score(draft_kvs, q_draft, target_kvs, q_hist, sub_heads, H_t, s_draft
     if S and s_target is None:
         s_target = torch.empty((B, N), dtype=torch.float32, device=dev)
     heads = (ctypes.c_int32 * (2 * max(S, 1)))(*[x for p in (sub_heads or [])[:S] for x in p])
+    if L_d and draft_lse is not None:
+        if not (draft_lse.is_cuda and draft_lse.dtype == torch.float32 and draft_lse.is_contiguous()
+                and tuple(draft_lse.shape) == (B, L_d, gamma, H_d)):
+            raise TypeError(f"draft_lse must be a contiguous float32 GPU tensor of shape {(B, L_d, gamma, H_d)}")
     darr = _kv_array(draft_kvs) if L_d else None
     tarr = _kv_array(target_kvs) if S else None
     nbytes = lib().dustin_score_workspace_bytes(B, N, L_d, H_d, gamma, S)
@@ -347,9 +356,25 @@ def dustin_score(draft_kvs, q_draft, target_kvs, q_hist, sub_heads, H_t, s_draft
     _check(lib().dustin_score(darr, L_d, _ptr(q_draft) if L_d else None, H_d, gamma,
                               tarr, len(target_kvs) if S else 0, _ptr(q_hist) if S else None,
                               heads if S else None, S, int(H_t), float(scale_draft), float(scale_target),
+                              _ptr(draft_lse) if (L_d and draft_lse is not None) else None,
                               _ptr(s_draft) if L_d else None, _ptr(s_target) if S else None,
                               _ptr(wsb), wsb.numel(), _stream(wsb)))
     return s_draft, s_target
+
+
+def dustin_draft_row_lse(draft_kvs, q_draft, scale_draft=0.0, out=None, ws: Workspace | None = None):
+    """Row normalisers of S_Draft's softmaxes: float32 [B][L_d][gamma][H_d],
+    ln sum_{j < n_b} exp(scale * q . k_j) (-inf for an empty history)."""
+    B, N = draft_kvs[0].desc.B, draft_kvs[0].desc.N_max
+    _, L_d, gamma, H_d, _ = q_draft.shape
+    assert L_d == len(draft_kvs), "q_draft layer count differs from draft_kvs"
+    if out is None:
+        out = torch.empty((B, L_d, gamma, H_d), dtype=torch.float32, device=q_draft.device)
+    nbytes = lib().dustin_score_workspace_bytes(B, N, L_d, H_d, gamma, 0)
+    wsb = _ws("score", ws, nbytes, q_draft.device)
+    _check(lib().dustin_draft_row_lse(_kv_array(draft_kvs), L_d, _ptr(q_draft), H_d, gamma, float(scale_draft),
+                                      _ptr(out), _ptr(wsb), wsb.numel(), _stream(wsb)))
+    return out
 
 
 def dustin_topk(s_draft, s_target, seq_lens, k, m, n_sink, n_window, idx=None, count=None, tier=None,

@@ -471,11 +471,66 @@ size_t dustin_score_workspace_bytes(int32_t B, int32_t N_max, int32_t L_d, int32
     return score_plan(B, N_max, L_d, H_d, gamma, S, 1).ws_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+// Checks of the draft side of a scoring call; sets the draft KV head count
+// and the query heads per KV head.
+dustin_status prep_draft(const dustin_kv *draft_layers, int32_t L_d, const void *q_draft, int32_t H_d, int32_t gamma,
+                         int &Hkv_d, int &G_d) {
+    CHECK(draft_layers != nullptr, DUSTIN_ERR_INVALID_ARG, "score: draft_layers is NULL");
+    CHECK(L_d <= kMaxDraftLayers, DUSTIN_ERR_UNSUPPORTED, "score: L_d %d exceeds %d", L_d, kMaxDraftLayers);
+    CHECK(draft_layers[0].B <= kMaxDraftBatch, DUSTIN_ERR_UNSUPPORTED, "score: B %d exceeds %d on the draft side",
+          draft_layers[0].B, kMaxDraftBatch);
+    for (int l = 0; l < L_d; ++l) {
+        dustin_status st = check_kv(&draft_layers[l], "score draft layer", false);
+        if (st != DUSTIN_OK) return st;
+        CHECK(same_geometry(&draft_layers[l], &draft_layers[0]), DUSTIN_ERR_INVALID_ARG,
+              "score: draft layer %d differs in geometry from layer 0", l);
+    }
+    const dustin_kv *ref = &draft_layers[0];
+    CHECK(q_draft != nullptr, DUSTIN_ERR_INVALID_ARG, "score: q_draft is NULL");
+    CHECK(H_d >= 1 && gamma >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_d and gamma must be >= 1");
+    Hkv_d = ref->H_kv;
+    CHECK(H_d % Hkv_d == 0, DUSTIN_ERR_INVALID_ARG, "score: H_d %d not a multiple of draft H_kv %d", H_d, Hkv_d);
+    G_d = H_d / Hkv_d;
+    CHECK(gamma * G_d <= 64, DUSTIN_ERR_UNSUPPORTED, "score: gamma * G_d = %d exceeds 64", gamma * G_d);
+    if (ref->dtype == DUSTIN_F32) {
+        CHECK(L_d <= 8 && (int64_t)L_d * H_d * gamma <= kMaxScoreQoff &&
+                  (int64_t)L_d * Hkv_d * ((gamma * G_d + 7) / 8) <= kMaxScoreRows,
+              DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than the library supports");
+    }
+    return ok();
+}
+
+DraftScoreArgs draft_args(const dustin_kv *draft_layers, int32_t L_d, const void *q_draft, int32_t H_d,
+                          int32_t gamma, int Hkv_d, int G_d, float scale_draft, const ScorePlan &p, char *wsb) {
+    DraftScoreArgs a{};
+    for (int l = 0; l < L_d; ++l) a.kv[l] = view_of(&draft_layers[l]);
+    a.L_d = L_d;
+    a.H_d = H_d;
+    a.gamma = gamma;
+    a.Hkv_d = Hkv_d;
+    a.G_d = G_d;
+    a.rows = gamma * G_d;
+    a.q_draft = q_draft;
+    a.scale_log2 = resolve_scale(scale_draft, a.kv[0].D) * kLog2e;
+    a.stat = (float *)(wsb + p.off_dstat);
+    a.lse = (float *)(wsb + p.off_dlse);
+    a.nchunk = p.nchunk;
+    a.part = (float *)(wsb + p.off_dpart);
+    a.acc_groups = p.acc_groups;
+    return a;
+}
+}  // namespace
+
+extern "C" {
+
 dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const void *q_draft, int32_t H_d,
                            int32_t gamma, const dustin_kv *target_layers, int32_t L_t, const void *q_hist,
                            const int32_t *sub_heads, int32_t S, int32_t H_t, float scale_draft,
-                           float scale_target, float *s_draft, float *s_target, void *ws, size_t ws_bytes,
-                           dustin_stream_t stream) {
+                           float scale_target, const float *draft_lse, float *s_draft, float *s_target, void *ws,
+                           size_t ws_bytes, dustin_stream_t stream) {
     const bool do_draft = s_draft != nullptr && L_d > 0;
     const bool do_target = s_target != nullptr && S > 0;
     CHECK(L_d >= 0 && S >= 0 && L_t >= 0, DUSTIN_ERR_INVALID_ARG, "score: negative count");
@@ -485,28 +540,9 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
     int Hkv_d = 1;
     int G_d = 1;
     if (do_draft) {
-        CHECK(draft_layers != nullptr, DUSTIN_ERR_INVALID_ARG, "score: draft_layers is NULL");
-        CHECK(L_d <= kMaxDraftLayers, DUSTIN_ERR_UNSUPPORTED, "score: L_d %d exceeds %d", L_d, kMaxDraftLayers);
-        CHECK(draft_layers[0].B <= kMaxDraftBatch, DUSTIN_ERR_UNSUPPORTED, "score: B %d exceeds %d on the draft side",
-              draft_layers[0].B, kMaxDraftBatch);
-        for (int l = 0; l < L_d; ++l) {
-            dustin_status st = check_kv(&draft_layers[l], "score draft layer", false);
-            if (st != DUSTIN_OK) return st;
-            CHECK(same_geometry(&draft_layers[l], &draft_layers[0]), DUSTIN_ERR_INVALID_ARG,
-                  "score: draft layer %d differs in geometry from layer 0", l);
-        }
+        dustin_status st = prep_draft(draft_layers, L_d, q_draft, H_d, gamma, Hkv_d, G_d);
+        if (st != DUSTIN_OK) return st;
         ref = &draft_layers[0];
-        CHECK(q_draft != nullptr, DUSTIN_ERR_INVALID_ARG, "score: q_draft is NULL");
-        CHECK(H_d >= 1 && gamma >= 1, DUSTIN_ERR_INVALID_ARG, "score: H_d and gamma must be >= 1");
-        Hkv_d = ref->H_kv;
-        CHECK(H_d % Hkv_d == 0, DUSTIN_ERR_INVALID_ARG, "score: H_d %d not a multiple of draft H_kv %d", H_d, Hkv_d);
-        G_d = H_d / Hkv_d;
-        CHECK(gamma * G_d <= 64, DUSTIN_ERR_UNSUPPORTED, "score: gamma * G_d = %d exceeds 64", gamma * G_d);
-        if (ref->dtype == DUSTIN_F32) {
-            CHECK(L_d <= 8 && (int64_t)L_d * H_d * gamma <= kMaxScoreQoff &&
-                      (int64_t)L_d * Hkv_d * ((gamma * G_d + 7) / 8) <= kMaxScoreRows,
-                  DUSTIN_ERR_UNSUPPORTED, "score: float32 draft larger than the library supports");
-        }
     }
     TargetScoreArgs ta{};
     if (do_target) {
@@ -536,26 +572,31 @@ dustin_status dustin_score(const dustin_kv *draft_layers, int32_t L_d, const voi
         if (e != hipSuccess) return hip_status(e, "score target launch");
     }
     if (do_draft) {
-        DraftScoreArgs a{};
-        for (int l = 0; l < L_d; ++l) a.kv[l] = view_of(&draft_layers[l]);
-        a.L_d = L_d;
-        a.H_d = H_d;
-        a.gamma = gamma;
-        a.Hkv_d = Hkv_d;
-        a.G_d = G_d;
-        a.rows = gamma * G_d;
-        a.q_draft = q_draft;
-        a.scale_log2 = resolve_scale(scale_draft, a.kv[0].D) * kLog2e;
+        DraftScoreArgs a = draft_args(draft_layers, L_d, q_draft, H_d, gamma, Hkv_d, G_d, scale_draft, p, wsb);
         a.s_draft = s_draft;
-        a.stat = (float *)(wsb + p.off_dstat);
-        a.lse = (float *)(wsb + p.off_dlse);
-        a.nchunk = p.nchunk;
-        a.part = (float *)(wsb + p.off_dpart);
-        a.acc_groups = p.acc_groups;
+        a.lse_in = draft_lse;
         hipError_t e = launch_draft_score(a, s);
         if (e != hipSuccess) return hip_status(e, "score draft launch");
     }
     return ok();
+}
+
+dustin_status dustin_draft_row_lse(const dustin_kv *draft_layers, int32_t L_d, const void *q_draft, int32_t H_d,
+                                   int32_t gamma, float scale_draft, float *lse_out, void *ws, size_t ws_bytes,
+                                   dustin_stream_t stream) {
+    CHECK(L_d >= 1, DUSTIN_ERR_INVALID_ARG, "draft_row_lse: L_d must be >= 1");
+    CHECK(lse_out != nullptr, DUSTIN_ERR_INVALID_ARG, "draft_row_lse: lse_out is NULL");
+    CHECK(std::isfinite(scale_draft), DUSTIN_ERR_INVALID_ARG, "draft_row_lse: scale is not finite");
+    int Hkv_d = 1, G_d = 1;
+    dustin_status st = prep_draft(draft_layers, L_d, q_draft, H_d, gamma, Hkv_d, G_d);
+    if (st != DUSTIN_OK) return st;
+    const dustin_kv *ref = &draft_layers[0];
+    const ScorePlan p = score_plan(ref->B, ref->N_max, L_d, H_d, gamma, 0, Hkv_d);
+    CHECK(ws != nullptr && ws_bytes >= p.ws_bytes, DUSTIN_ERR_INVALID_ARG,
+          "draft_row_lse: workspace of %zu bytes needed (got %zu)", p.ws_bytes, ws_bytes);
+    DraftScoreArgs a = draft_args(draft_layers, L_d, q_draft, H_d, gamma, Hkv_d, G_d, scale_draft, p, (char *)ws);
+    a.lse_out = lse_out;
+    return hip_status(launch_draft_score(a, (hipStream_t)stream), "draft_row_lse launch");
 }
 
 }  // extern "C"

@@ -64,6 +64,12 @@ struct DraftScoreArgs {
     float steps_scale;
     float *part;                    // ws: [acc_groups][B][N_max] per-layer-group partial sums
     int32_t acc_groups;             // layer groups of the streaming accumulation (1: no partials)
+    // supplied row normalisers, natural log, [B][L_d][gamma][H_d] (nullable):
+    // taken instead of the statistics pass
+    const float *lse_in;
+    // row-normaliser query (nullable): the normalisers are written here in the
+    // layout of lse_in and nothing is accumulated
+    float *lse_out;
 };
 
 hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s);

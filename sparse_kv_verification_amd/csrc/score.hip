@@ -258,6 +258,33 @@ __global__ __launch_bounds__(256) void rows_lse(const float *stat, float *lse, i
     if (lane == 0) lse[row] = (z > 0.f) ? muse + __log2f(z) : __builtin_huge_valf();
 }
 
+// Row normalisers between the caller's layout ([B][L_d][gamma][H_d], natural
+// log) and the draft passes' ([B][L_d * Hkv_d][rows], log2, row r = step *
+// G_d + head mod G_d of KV head head / G_d).  An empty row is -inf outside and
+// +inf inside (its terms are exp2(logit - inf) = 0); other non-finite inputs
+// are taken as empty rows.
+__device__ __forceinline__ int64_t draft_lse_slot(int64_t i, int L_d, int gamma, int H_d, int Hkv_d, int G_d) {
+    const int h = (int)(i % H_d);
+    const int64_t t = i / H_d;
+    const int g = (int)(t % gamma);
+    const int64_t bl = t / gamma;   // b * L_d + l
+    return (bl * Hkv_d + h / G_d) * (int64_t)(gamma * G_d) + g * G_d + h % G_d;
+}
+__global__ __launch_bounds__(256) void draft_lse_import(const float *in, float *lse, int64_t n, int L_d, int gamma,
+                                                        int H_d, int Hkv_d, int G_d) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float v = in[i];
+        lse[draft_lse_slot(i, L_d, gamma, H_d, Hkv_d, G_d)] = __builtin_isfinite(v) ? v * kLog2e : __builtin_huge_valf();
+    }
+}
+__global__ __launch_bounds__(256) void draft_lse_export(const float *lse, float *out, int64_t n, int L_d, int gamma,
+                                                        int H_d, int Hkv_d, int G_d) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float v = lse[draft_lse_slot(i, L_d, gamma, H_d, Hkv_d, G_d)];
+        out[i] = __builtin_isfinite(v) ? v * kLn2 : kNegInf;
+    }
+}
+
 // S_Target[b][j] = sum_r exp2(logit[r][j] - lse[r]).
 __global__ __launch_bounds__(256) void target_finalize(const float *logit, const float *lse, float *out,
                                                        const int32_t *seq_lens, int S, int N_max) {
@@ -1450,6 +1477,23 @@ ScorePlan score_plan(int B, int N_max, int L_d, int H_d, int gamma, int S, int H
     return p;
 }
 
+// Supplied normalisers into the passes' layout.
+static hipError_t import_draft_lse(const DraftScoreArgs &a, int B, hipStream_t s) {
+    const int64_t n = (int64_t)B * a.L_d * a.gamma * a.H_d;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(draft_lse_import, dim3((unsigned)blocks), dim3(256), 0, s, a.lse_in, a.lse, n, a.L_d, a.gamma,
+                       a.H_d, a.Hkv_d, a.G_d);
+    return hipGetLastError();
+}
+// Row-normaliser query: the passes' normalisers out in the caller's layout.
+static hipError_t export_draft_lse(const DraftScoreArgs &a, int B, hipStream_t s) {
+    const int64_t n = (int64_t)B * a.L_d * a.gamma * a.H_d;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(draft_lse_export, dim3((unsigned)blocks), dim3(256), 0, s, a.lse, a.lse_out, n, a.L_d, a.gamma,
+                       a.H_d, a.Hkv_d, a.G_d);
+    return hipGetLastError();
+}
+
 template <bool F32, int D, int NV>
 static hipError_t run_unit_stats(const ValuStatsParams<F32, D, NV> &p, int B, hipStream_t s) {
     dim3 grid(p.nchunk, p.ut.n_units, B);
@@ -1554,11 +1598,16 @@ static hipError_t draft_f32_impl(const DraftScoreArgs &a, hipStream_t s) {
     p.logit = nullptr;
     p.nchunk = a.nchunk;
     p.N_max = k0.N_max;
-    hipError_t e = run_unit_stats(p, k0.B, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rows_lse, dim3((k0.B * row + 3) / 4), dim3(256), 0, s, a.stat, a.lse, k0.B * row, a.nchunk,
-                       k0.seq_lens, row, CH, k0.N_max);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e;
+    if (a.lse_in) {
+        if ((e = import_draft_lse(a, k0.B, s)) != hipSuccess) return e;
+    } else {
+        if ((e = run_unit_stats(p, k0.B, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL(rows_lse, dim3((k0.B * row + 3) / 4), dim3(256), 0, s, a.stat, a.lse, k0.B * row, a.nchunk,
+                           k0.seq_lens, row, CH, k0.N_max);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.lse_out) return export_draft_lse(a, k0.B, s);
     DraftValuAccParams<D, 8> q{};
     for (int i = 0; i < a.L_d; ++i) q.kv[i] = a.kv[i];
     q.ut = ut;
@@ -1585,14 +1634,19 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     constexpr int NHI = HALF ? 2 : 1;
     const int stat_items = k0.B * a.L_d * NHI * b.nchunk;
     constexpr int GROUPS = StreamGeom<RB, HALF>::GROUPS;
-    hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
-                       dim3(256), 0, s, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nrows = k0.B * a.L_d * 2 * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
-                       a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e;
+    if (a.lse_in) {
+        if ((e = import_draft_lse(a, k0.B, s)) != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
+                           dim3(256), 0, s, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int nrows = k0.B * a.L_d * 2 * a.rows;
+        hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk,
+                           k0.seq_lens, a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.lse_out) return export_draft_lse(a, k0.B, s);
     const int cap = a.acc_groups > 1 ? a.acc_groups : 1;   // the device picks <= cap layer groups
     b.acc_groups = cap;
     const long acc_items = (long)k0.B * ((k0.N_max + 1023) / 1024) * cap * NHI;   // at full lengths
@@ -1618,14 +1672,19 @@ static hipError_t draft_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     DraftScoreArgs b = a;
     b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
     const int stat_items = k0.B * U * b.nchunk;
-    hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(stat_items < kScoreGroups ? stat_items : kScoreGroups),
-                       dim3(256), 0, s, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nrows = k0.B * U * a.rows;
-    hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk, k0.seq_lens,
-                       U * a.rows, kDraftStatChunk, k0.N_max);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e;
+    if (a.lse_in) {
+        if ((e = import_draft_lse(a, k0.B, s)) != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((draft_stats_mfma<D, RB>), dim3(stat_items < kScoreGroups ? stat_items : kScoreGroups),
+                           dim3(256), 0, s, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int nrows = k0.B * U * a.rows;
+        hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk,
+                           k0.seq_lens, U * a.rows, kDraftStatChunk, k0.N_max);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.lse_out) return export_draft_lse(a, k0.B, s);
     const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
     const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
     if (k0.page_size != 0) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true>), grid, dim3(256), 0, s, b);

@@ -100,7 +100,8 @@ def test_score_argument_errors(L):
         return L.dustin_score(kw.get("d", d), kw.get("L_d", 2), kw.get("qd", FAKE), kw.get("H_d", 14),
                               kw.get("gamma", 4), kw.get("t", t), kw.get("L_t", 1), kw.get("qh", FAKE),
                               kw.get("heads", heads), kw.get("S", 2), kw.get("H_t", 64), 0.0, 0.0,
-                              kw.get("sd", FAKE), kw.get("st", FAKE), FAKE, kw.get("ws", 1 << 40), None)
+                              kw.get("lse", None), kw.get("sd", FAKE), kw.get("st", FAKE), FAKE,
+                              kw.get("ws", 1 << 40), None)
     assert f(qd=None) == INVALID
     assert f(H_d=13) == INVALID                                   # not a multiple of draft H_kv
     assert f(gamma=20) == UNSUPPORTED                             # gamma * G_d = 140 > 64
@@ -114,6 +115,17 @@ def test_score_argument_errors(L):
     assert f(ws=10) == INVALID
     # nothing requested: a no-op that succeeds without touching the GPU
     assert f(sd=None, st=None) == 0
+    # the row-normaliser query checks the draft side the same way
+    def g(**kw):
+        return L.dustin_draft_row_lse(kw.get("d", d), kw.get("L_d", 2), kw.get("qd", FAKE), kw.get("H_d", 14),
+                                      kw.get("gamma", 4), 0.0, kw.get("out", FAKE), FAKE, kw.get("ws", 1 << 40), None)
+    assert g(out=None) == INVALID
+    assert g(L_d=0) == INVALID
+    assert g(qd=None) == INVALID
+    assert g(H_d=13) == INVALID
+    assert g(gamma=20) == UNSUPPORTED
+    assert g(d=bad) == INVALID
+    assert g(ws=10) == INVALID
 
 
 def test_arr_and_window_argument_errors(L):

@@ -15,6 +15,8 @@ Tolerances (from the benchmark spec and the arithmetic):
 """
 import zlib
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -249,6 +251,62 @@ def test_scores_match_oracle(name, over):
         assert abs(gt.sum() - len(sub)) < 1e-3 * len(sub)
         assert abs(gd.sum() - sh.L_d * sh.H_d * sh.w) < 1e-3 * sh.L_d * sh.H_d * sh.w
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
+
+
+LSE_CASES = [
+    ("stream-ragged-empty", dict(base="c2", B=3, n=3000, L_d=3, n_lo=900), True),   # last sequence empty
+    ("stream-one-head-paged", dict(base="c5", B=2, n=3000, n_lo=1200, L_d=2, w=8), False),
+    ("stream-layer-groups", dict(base="c2", B=1, n=2048, L_d=24), False),
+    ("mfma-one-kv-head", dict(base="c2", B=2, n=2100, L_d=2, Hkv_d=1, H_d=8), False),
+    ("tiny-f32", dict(base="c1"), False),
+]
+
+
+@pytest.mark.parametrize("name,over,empty_last", LSE_CASES, ids=[c[0] for c in LSE_CASES])
+def test_draft_row_lse_and_supplied_normalisers(name, over, empty_last):
+    """The row normalisers of S_Draft's softmaxes (dustin_draft_row_lse)
+    against the oracle's, and S_Draft computed from normalisers the caller
+    supplies (one read of the draft keys) against the oracle's S_Draft given
+    the same normalisers: the oracle's own, then the same with one row's
+    raised by ln 2 in each sequence (that row's terms halve)."""
+    say("draft row normalisers", name)
+    over = dict(over)
+    base = over.pop("base")
+    sh = synth.preset(base).replace(**over)
+    x = synth.make(sh, device=DEV)
+    lens = x.seq_lens.clone()
+    if empty_last:
+        lens[-1] = 0
+    dkv = [dk.KV(x.Kd[l], None, lens, x.page_table) for l in range(sh.L_d)]
+    lse = dk.dustin_draft_row_lse(dkv, x.q_draft)
+    torch.cuda.synchronize()
+    lse_ref = np.empty((sh.B, sh.L_d, sh.w, sh.H_d))
+    for b in range(sh.B):
+        n = int(lens[b])
+        Kd = oracle_kv(x, "Kd", b)[:, :n] if n else np.zeros((sh.L_d, 0, sh.Hkv_d, sh.d_d))
+        lse_ref[b] = oracle.draft_row_lse(f64(x.q_draft[b]), Kd)
+    got = f64(lse)
+    fin = np.isfinite(lse_ref)
+    assert (np.isneginf(got) == ~fin).all(), "empty rows must read -inf"
+    err = np.abs(got[fin] - lse_ref[fin]).max()
+    say(f"  max |d lse| = {err:.2e}")
+    assert err <= 2e-5 + 2e-6 * np.abs(lse_ref[fin]).max()
+    shifted = lse_ref.copy()
+    for b in range(sh.B):
+        shifted[b, sh.L_d - 1, 0, sh.H_d - 1] += math.log(2.0)
+    for given in (lse_ref, shifted):
+        given32 = given.astype(np.float32)
+        s_d, _ = dk.dustin_score(dkv, x.q_draft, [], None, None, sh.Hq, want_target=False,
+                                 draft_lse=torch.from_numpy(given32).to(DEV))
+        torch.cuda.synchronize()
+        for b in range(sh.B):
+            n = int(lens[b])
+            assert (f64(s_d[b, n:]) == 0).all()
+            if n == 0:
+                continue
+            ref = oracle.score_draft_given_lse(f64(x.q_draft[b]), oracle_kv(x, "Kd", b)[:, :n], given32[b].astype(np.float64))
+            say(f"  b={b} n={n} max rel|dS_D| = {max_rel_err(f64(s_d[b, :n]), ref):.2e}")
+            assert_scores_close(f64(s_d[b, :n]), ref, "S_Draft from supplied normalisers")
 
 
 def test_scores_on_searched_subsets():
