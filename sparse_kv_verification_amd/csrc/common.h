@@ -19,6 +19,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFltMax = 3.40282347e+38f;   // largest finite float
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);

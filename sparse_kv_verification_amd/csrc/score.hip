@@ -1094,6 +1094,15 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     // (page ids into pgn) and, when the next item has stages, its first DMA.
     auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[NH][RB][KK],
                     bf16x8 (&qn)[NH][RB][KK], const int &pg, int &pgn) {
+        // Per lane and row: zrun = sum of exp2(v - mrun) over the lane's
+        // positions so far.  Up to two row blocks (LAZY), mrun is a reference
+        // at least every such v that moves only when a logit passes it, and
+        // then to that logit + 16: most pairs of logits cost two exp2 and no
+        // rescale, terms stay <= 1, and the reference is finite (-FLT_MAX
+        // until the row's first valid position).  With more row blocks the
+        // registers do not leave room for that form, and mrun is the running
+        // maximum (three exp2 per pair).
+        constexpr bool LAZY = RB <= 2;
         float mrun[NH][RB][4], zrun[NH][RB][4];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -1101,7 +1110,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    mrun[h][rb][i] = kNegInf;
+                    mrun[h][rb][i] = LAZY ? -kFltMax : kNegInf;
                     zrun[h][rb][i] = 0.f;
                 }
         auto next_dma = [&](int s) {   // the DMA after stage s
@@ -1130,21 +1139,61 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                         sc[st][rb] = acc;
                     }
                 }
+                const float sl = a.scale_log2;
+                if constexpr (!LAZY) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float v0 = sc[0][rb][i] * sl, v1 = sc[1][rb][i] * sl;
+                            if (!full) {
+                                if (j0 + pr * 32 + (lane & 15) >= cur.nb) v0 = kNegInf;
+                                if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
+                            }
+                            const float mx = fmaxf(mrun[h][rb][i], fmaxf(v0, v1));
+                            const float mu = (mx == kNegInf) ? 0.f : mx;
+                            zrun[h][rb][i] = zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu) +
+                                             __builtin_amdgcn_exp2f(v0 - mu) + __builtin_amdgcn_exp2f(v1 - mu);
+                            mrun[h][rb][i] = mx;
+                        }
+                    continue;
+                }
+                // d = v - mrun for both logits; a positive d passes the
+                // reference.  The products sc stay as they are: while a row's
+                // reference is still -FLT_MAX, d has lost v to rounding, so a
+                // moved reference is computed from sc and d again from it.
+                float d[2][RB][4];
+                bool pass_ref = false;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float v0 = sc[0][rb][i] * a.scale_log2, v1 = sc[1][rb][i] * a.scale_log2;
                         if (!full) {
-                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) v0 = kNegInf;
-                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
+                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) sc[0][rb][i] = kNegInf;
+                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) sc[1][rb][i] = kNegInf;
                         }
-                        const float mx = fmaxf(mrun[h][rb][i], fmaxf(v0, v1));
-                        const float mu = (mx == kNegInf) ? 0.f : mx;
-                        zrun[h][rb][i] = zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu) +
-                                         __builtin_amdgcn_exp2f(v0 - mu) + __builtin_amdgcn_exp2f(v1 - mu);
-                        mrun[h][rb][i] = mx;
+                        d[0][rb][i] = __builtin_fmaf(sc[0][rb][i], sl, -mrun[h][rb][i]);
+                        d[1][rb][i] = __builtin_fmaf(sc[1][rb][i], sl, -mrun[h][rb][i]);
+                        pass_ref |= fmaxf(d[0][rb][i], d[1][rb][i]) > 0.f;
                     }
+                if (__ballot(pass_ref)) {   // rare after a row's first positions
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float pv = fmaxf(sc[0][rb][i], sc[1][rb][i]) * sl;
+                            const float rn = pv > mrun[h][rb][i] ? pv + 16.f : mrun[h][rb][i];
+                            zrun[h][rb][i] *= __builtin_amdgcn_exp2f(mrun[h][rb][i] - rn);
+                            mrun[h][rb][i] = rn;
+                            d[0][rb][i] = __builtin_fmaf(sc[0][rb][i], sl, -rn);
+                            d[1][rb][i] = __builtin_fmaf(sc[1][rb][i], sl, -rn);
+                        }
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        zrun[h][rb][i] += __builtin_amdgcn_exp2f(d[0][rb][i]) + __builtin_amdgcn_exp2f(d[1][rb][i]);
             }
             slot ^= 1;
         };
@@ -1171,12 +1220,14 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    // a row with no valid position has a zero sum (its
+                    // reference -inf, or -FLT_MAX in the lazy form): (-inf, 0)
                     const float mx = lane16_max(mrun[h][rb][i]);
                     const float mu = (mx == kNegInf) ? 0.f : mx;
                     const float z = lane16_sum(zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu));
                     if ((lane & 15) == 0) {
                         const int r = rb * 16 + (lane >> 4) * 4 + i;
-                        red[par][wave][h][r][0] = mx;
+                        red[par][wave][h][r][0] = z > 0.f ? mx : kNegInf;
                         red[par][wave][h][r][1] = z;
                     }
                 }
