@@ -236,6 +236,132 @@ __global__ __launch_bounds__(256) void unit_stats_valu(ValuStatsParams<F32, D, N
     }
 }
 
+// Target statistics, whole-row form: when the scored rows of one layer use
+// every one of its KV heads (each KV head one unit of <= 8 rows), all of the
+// layer's key bytes are needed, so a work-group streams whole position rows
+// ([H_kv][128] bf16, contiguous) once instead of each head's 256-byte slices
+// at the row stride in separate work-groups.  Lane t of a position's
+// H_kv * 16 lanes holds 16 bytes of head (t / 16); a head's dot products are
+// summed over its 16 lanes with DPP rotations.  Same outputs as
+// unit_stats_valu: per-chunk (max, sum of exp2) per row, and the logits.
+struct RowStatsParams {
+    KvView kv;
+    const char *q;                   // [B][S][128] bf16
+    int32_t S;
+    int32_t unit_of_head[16];        // unit index of each KV head
+    int32_t row0[16], nrow[16];      // per unit
+    float scale_log2;
+    float *stat;                     // [B][S][nchunk][2]
+    float *logit;                    // [B][S][N_max]
+    int32_t nchunk, N_max;
+};
+
+template <int NR>   // rows per unit at most (1, 2, 4 or 8)
+__global__ __launch_bounds__(256) void unit_stats_rows(RowStatsParams p) {
+    constexpr int D = 128, EPL = 8;
+    constexpr int NB = NR <= 2 ? 16 : 8;   // loads in flight per lane
+    extern __shared__ float lg[];    // [S][CH]
+    __shared__ int pgs[CH / 16];
+    const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const KvView &kv = p.kv;
+    const int nb = sl_len(kv, b);
+    const int j0 = chunk * CH;
+    if (j0 >= nb) return;   // statistics and logits past n_b are never read
+    const int LPP = kv.Hkv * 16;     // lanes per position (<= 256, a power of two)
+    const int PPI = 256 / LPP;       // positions per load instruction
+    const int g = (tid % LPP) >> 4, sl = tid & 15, pq = tid / LPP;
+    const bool paged = kv.page_size != 0;
+    if (paged)
+        for (int i = tid; i < CH / 16; i += 256) {
+            const int pi = (j0 >> 4) + i;
+            pgs[i] = pi < kv.max_pages ? kv.page_table[(int64_t)b * kv.max_pages + pi] : -1;
+        }
+    const int u = p.unit_of_head[g];
+    const int r0 = p.row0[u], nr = p.nrow[u];
+    float qr[NR][EPL];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+        if (r < nr) raw = *(const u32x4 *)(p.q + (((int64_t)b * p.S + r0 + r) * D + sl * EPL) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qr[r][2 * i] = __uint_as_float(raw[i] << 16);
+            qr[r][2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+        }
+    }
+    __syncthreads();   // page ids in LDS
+    const int64_t rowb = (int64_t)kv.Hkv * D * 2;   // bytes per position row
+    const int NP = CH / PPI;                          // positions per lane
+    for (int t0 = 0; t0 < NP; t0 += NB) {
+        u32x4 raw[NB];
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            const int pos = pq + (t0 + t) * PPI;
+            const int j = j0 + pos;
+            const char *row = nullptr;
+            if (t0 + t < NP && j < nb) {
+                if (paged) {
+                    const int pg = pgs[pos >> 4];
+                    if (pg >= 0 && pg < kv.num_pages) row = kv.k + ((int64_t)pg * 16 + (j & 15)) * rowb;
+                } else {
+                    row = kv.k + ((int64_t)b * kv.N_max + j) * rowb;
+                }
+            }
+            raw[t] = row ? ld_stream16(row + (g * 16 + sl) * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            if (t0 + t >= NP) break;
+            const int pos = pq + (t0 + t) * PPI;
+            const bool ok = j0 + pos < nb;
+            float x[EPL];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(raw[t][i] << 16);
+                x[2 * i + 1] = __uint_as_float(raw[t][i] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (r < nr) {   // the same for the 16 lanes of a head
+                    float sdot = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPL; ++i) sdot += qr[r][i] * x[i];
+                    sdot = lane16_sum(sdot);
+                    if (sl == 0) lg[(r0 + r) * CH + pos] = ok ? sdot * p.scale_log2 : kNegInf;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int r = wave; r < p.S; r += 4) {
+        float v[CH / 64];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) {
+            v[i] = lg[r * CH + lane + 64 * i];
+            mx = fmaxf(mx, v[i]);
+        }
+        mx = wave_max(mx);
+        const float muse = (mx == kNegInf) ? 0.f : mx;
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) z += exp2f(v[i] - muse);
+        z = wave_sum(z);
+        if (lane == 0) {
+            float *st = p.stat + (((int64_t)b * p.S + r) * p.nchunk + chunk) * 2;
+            st[0] = mx;
+            st[1] = z;
+        }
+        float *lp = p.logit + ((int64_t)b * p.S + r) * p.N_max + j0;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) {
+            const int pos = lane + 64 * i;
+            if (j0 + pos < p.N_max) lp[pos] = v[i];
+        }
+    }
+}
+
 // Row log-sum-exp (log2 domain) from the per-chunk statistics.
 // One wave per row; rows are sequence-major (rows_per_b rows per sequence)
 // and only the chunks holding positions below n_b are read (the statistics
@@ -1579,7 +1705,43 @@ static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
     p.logit = a.logit;
     p.nchunk = a.nchunk;
     p.N_max = k0.N_max;
-    hipError_t e = run_unit_stats(p, k0.B, s);
+    // whole-row form: bf16, head_dim 128, one layer, every KV head exactly one unit
+    bool rows_form = !F32 && D == 128 && a.n_layers == 1 && ut.n_units == k0.Hkv && k0.Hkv <= 16 &&
+                     (k0.Hkv & (k0.Hkv - 1)) == 0;
+    int unit_of_head[16];
+    for (int h = 0; h < 16; ++h) unit_of_head[h] = -1;
+    for (int u = 0; rows_form && u < ut.n_units; ++u) {
+        if (unit_of_head[ut.kvh[u]] >= 0) rows_form = false;
+        else unit_of_head[ut.kvh[u]] = u;
+    }
+    hipError_t e;
+    if (rows_form) {
+        RowStatsParams q{};
+        q.kv = k0;
+        q.q = (const char *)a.q_hist;
+        q.S = a.S;
+        for (int h = 0; h < 16; ++h) q.unit_of_head[h] = unit_of_head[h] < 0 ? 0 : unit_of_head[h];
+        for (int u = 0; u < ut.n_units; ++u) {
+            q.row0[u] = ut.row0[u];
+            q.nrow[u] = ut.nrow[u];
+        }
+        q.scale_log2 = a.scale_log2;
+        q.stat = a.stat;
+        q.logit = a.logit;
+        q.nchunk = a.nchunk;
+        q.N_max = k0.N_max;
+        int nr_max = 1;
+        for (int u = 0; u < ut.n_units; ++u) nr_max = ut.nrow[u] > nr_max ? ut.nrow[u] : nr_max;
+        const dim3 grid(a.nchunk, k0.B);
+        const size_t lds = (size_t)a.S * CH * sizeof(float);
+        if (nr_max == 1) hipLaunchKernelGGL(unit_stats_rows<1>, grid, dim3(256), lds, s, q);
+        else if (nr_max == 2) hipLaunchKernelGGL(unit_stats_rows<2>, grid, dim3(256), lds, s, q);
+        else if (nr_max <= 4) hipLaunchKernelGGL(unit_stats_rows<4>, grid, dim3(256), lds, s, q);
+        else hipLaunchKernelGGL(unit_stats_rows<8>, grid, dim3(256), lds, s, q);
+        e = hipGetLastError();
+    } else {
+        e = run_unit_stats(p, k0.B, s);
+    }
     if (e != hipSuccess) return e;
     float *lse = a.lse;
     hipLaunchKernelGGL(rows_lse, dim3((k0.B * a.S + 3) / 4), dim3(256), 0, s, a.stat, lse, k0.B * a.S, a.nchunk,

@@ -253,6 +253,35 @@ def test_scores_match_oracle(name, over):
         assert (f64(s_t[b, n:]) == 0).all() and (f64(s_d[b, n:]) == 0).all()
 
 
+@pytest.mark.parametrize("layout,paged", [("two-rows-per-kv-head", False), ("two-rows-per-kv-head", True),
+                                           ("split-units", False)],
+                         ids=["rows-2-per-head", "rows-2-per-head-paged", "units-not-one-per-head"])
+def test_target_scores_whole_row_form(layout, paged):
+    """S_Target when the scored rows of one layer use every KV head (the
+    whole-row statistics pass) with two rows per KV head, contiguous and
+    paged; and with rows of one KV head that are not adjacent (two units for
+    that head: the per-unit pass).  The oracle scores the same pairs."""
+    say("target scores", layout, "paged" if paged else "contiguous")
+    sh = synth.preset("c5" if paged else "c2").replace(B=2, n=3000, n_lo=1100, L_d=1, Hq=28, Hkv=4, S=8)
+    x = synth.make(sh, device=DEV)
+    G = sh.Hq // sh.Hkv
+    if layout == "two-rows-per-kv-head":
+        heads = [0, 1, G, G + 3, 2 * G + 1, 2 * G + 6, 3 * G, 3 * G + 2]
+    else:
+        heads = [0, G, 1, 2 * G, 3 * G, 2 * G + 1, 3 * G + 4, G + 5]
+    sub = [(0, h) for h in heads]
+    qh = x.q[:, -1][:, heads].contiguous()
+    kvs = [dk.KV(x.K, None, x.seq_lens, x.page_table)]
+    _, s_t = dk.dustin_score([], None, kvs, qh, sub, sh.Hq, want_draft=False)
+    torch.cuda.synchronize()
+    for b in range(sh.B):
+        n = int(x.seq_lens[b])
+        st = oracle.score_target(f64(qh[b]), {0: oracle_kv(x, "K", b)}, sub, sh.Hq)
+        say(f"  b={b} n={n} max rel|dS_T|={max_rel_err(f64(s_t[b, :n]), st):.2e}")
+        assert_scores_close(f64(s_t[b, :n]), st, "S_Target")
+        assert (f64(s_t[b, n:]) == 0).all()
+
+
 LSE_CASES = [
     ("stream-ragged-empty", dict(base="c2", B=3, n=3000, L_d=3, n_lo=900), True),   # last sequence empty
     ("stream-one-head-paged", dict(base="c5", B=2, n=3000, n_lo=1200, L_d=2, w=8), False),
