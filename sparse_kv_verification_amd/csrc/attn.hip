@@ -236,35 +236,51 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int b = bg / a.kv.Hkv, g = bg - (bg / a.kv.Hkv) * a.kv.Hkv;
 
     // Every load of the prologue is independent of the others, so they are
-    // all in flight together: sequence length, count, Q and the split's
-    // index entries (read up to the k bound; the count masks them after).
+    // all in flight together: sequence length and count (scalar), then Q and
+    // the split's index entries, with no branch between them: padding rows
+    // of Q read row 0 and are zeroed once the loads have landed, and index
+    // entries are read through a buffer resource bounded at the row's k
+    // entries (entries past the split are masked after).
     const int nb_raw = a.kv.seq_lens[b];
     const int cnt_raw = DENSE ? 0 : a.count[b];
     const int t0 = split * a.tps;
 
     if (tid == 0) s_flag = 0;
     // Q^T operand fragments of this wave's row block: lane holds row
-    // rbw*16 + (lane & 15), d slice kk*32 + (lane >> 4) * 8.  Issued first so
-    // they overlap the index loads below.
+    // rbw*16 + (lane & 15), d slice kk*32 + (lane >> 4) * 8.
     const int qrow = rbw * 16 + (lane & 15);
     bf16x8 qf[KK];
+    {
+        const int qr = qrow < a.R ? qrow : 0;
+        const int sq = qr / a.G, gh = qr - (qr / a.G) * a.G;
+        const uint16_t *qp = (const uint16_t *)a.q +
+            (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D + (lane >> 4) * 8;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        if (qrow < a.R) {
-            const int sq = qrow / a.G, gh = qrow - (qrow / a.G) * a.G;
-            const uint16_t *qp = (const uint16_t *)a.q +
-                (((size_t)b * a.w + sq) * a.Hq + (size_t)g * a.G + gh) * D + kk * 32 + (lane >> 4) * 8;
-            qf[kk] = *(const bf16x8 *)qp;
-        } else {
-            for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.f;
-        }
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8 *)(qp + kk * 32);
     }
     constexpr int PER = kAttnMaxTps / NT;
     int jv[PER];
+    if constexpr (DENSE) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int t = tid + NT * i;
-        jv[i] = DENSE ? t0 + t : ((t < a.tps && t0 + t < a.k) ? a.idx[(int64_t)b * a.k + t0 + t] : -1);
+        for (int i = 0; i < PER; ++i) jv[i] = t0 + tid + NT * i;
+    } else {
+        const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.idx) + (int64_t)b * a.k, (short)0, a.k * 4, 0x00020000);
+        // all PER entries are requested (entries past the row's k read 0)
+        // before any is masked, so the loads are in flight together
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            jv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, (uint32_t)(t0 + tid + NT * i) * 4u, 0, 0);
+        // every loaded value is used here, unconditionally: otherwise the
+        // compiler sinks a load into the branch of its mask and waits for it
+        // there, after the others
+#pragma unroll
+        for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(jv[i]));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = tid + NT * i;
+            jv[i] = (t < a.tps && t0 + t < a.k) ? jv[i] : -1;
+        }
     }
     const int nb = min(max(nb_raw, 0), a.kv.N_max);
     // Fused append: split 0 of (b, g) writes head g of the w window rows into
@@ -299,7 +315,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     const int win_lo = hist - t0;   // local index of the first window token
     lds_barrier();   // s_flag cleared; the loads stay in flight
     bool any_bad = false;
-    {   // physical row of every token of the split
+    if (!CAUSAL && a.kv.page_size == 0) {
+        // contiguous history-only rows: arithmetic only, no branch per entry
+        const int rb0 = b * a.kv.N_max;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (NT * i < a.tps) {   // the same for every lane
+                const int t = tid + NT * i;
+                const bool ok = jv[i] >= 0 && jv[i] < nb;
+                if (t < a.tps) rows[t] = ok ? rb0 + jv[i] : -1;
+                any_bad |= t < ntok && !ok;
+            }
+        }
+    } else {   // physical row of every token of the split
         int pos[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -337,6 +365,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     // Q fragments and index loads have landed (nothing else is in flight
     // yet), so no wait on them is left for the compiler to place in the loop.
     wait_vmcnt<0>();
+    if (qrow >= a.R) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.f;
+    }
     lds_barrier();
     const bool all_rows_valid = (s_flag == 0);
     ATTN_TRACE(1);
