@@ -1614,8 +1614,17 @@ int draft_acc_groups(int B, int N_max, int L_d) {
 // With one partial the accumulation kernel has written S_Draft itself.
 __global__ __launch_bounds__(256) void draft_part_sum(const float *part, int nhi, int cap, int L, int grid, int B,
                                                       int N, const int32_t *seq_lens, float *out) {
-    int chunks = 0;
-    for (int bb = 0; bb < B; ++bb) chunks += (min(max(seq_lens[bb], 0), N) + 1023) / 1024;
+    // the chunk count, with the lengths loaded in parallel (one load per
+    // lane, then a block sum): a serial loop over B put B dependent loads in
+    // front of the common case, one group, where nothing is left to do
+    __shared__ int s_part[4];
+    int c = 0;
+    for (int bb = threadIdx.x; bb < B; bb += 256) c += (min(max(seq_lens[bb], 0), N) + 1023) / 1024;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = c;
+    __syncthreads();
+    const int chunks = s_part[0] + s_part[1] + s_part[2] + s_part[3];
     const int groups = acc_layer_groups(chunks, nhi, L, cap, grid) * nhi;
     if (groups == 1) return;
     const int64_t n = (int64_t)B * N;
