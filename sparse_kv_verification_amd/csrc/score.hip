@@ -1228,7 +1228,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         // until the row's first valid position).  With more row blocks the
         // registers do not leave room for that form, and mrun is the running
         // maximum (three exp2 per pair).
-        constexpr bool LAZY = RB <= 2;
+        constexpr bool LAZY = true;
         float mrun[NH][RB][4], zrun[NH][RB][4];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -1284,42 +1284,62 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                         }
                     continue;
                 }
-                // d = v - mrun for both logits; a positive d passes the
-                // reference.  The products sc stay as they are: while a row's
-                // reference is still -FLT_MAX, d has lost v to rounding, so a
-                // moved reference is computed from sc and d again from it.
-                float d[2][RB][4];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!full) {
+                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) sc[0][rb][i] = kNegInf;
+                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) sc[1][rb][i] = kNegInf;
+                        }
+                if (s == 0 && pr == 0) {
+                    // The item's first pair sets each row's reference from
+                    // its own logits.  A lane whose first pair is masked has
+                    // no valid position in the item at all (positions only
+                    // grow), so a reference left at -FLT_MAX only ever meets
+                    // masked logits: d = -inf, and it never moves.
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v0 = sc[0][rb][i] * sl, v1 = sc[1][rb][i] * sl;
+                            const float pv = fmaxf(v0, v1);
+                            const float rn = pv > kNegInf ? pv + 16.f : -kFltMax;
+                            mrun[h][rb][i] = rn;
+                            zrun[h][rb][i] = __builtin_amdgcn_exp2f(v0 - rn) + __builtin_amdgcn_exp2f(v1 - rn);
+                        }
+                    continue;
+                }
+                // d = v - mrun for both logits, in place; a positive d passes
+                // the reference
                 bool pass_ref = false;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (!full) {
-                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) sc[0][rb][i] = kNegInf;
-                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) sc[1][rb][i] = kNegInf;
-                        }
-                        d[0][rb][i] = __builtin_fmaf(sc[0][rb][i], sl, -mrun[h][rb][i]);
-                        d[1][rb][i] = __builtin_fmaf(sc[1][rb][i], sl, -mrun[h][rb][i]);
-                        pass_ref |= fmaxf(d[0][rb][i], d[1][rb][i]) > 0.f;
+                        sc[0][rb][i] = __builtin_fmaf(sc[0][rb][i], sl, -mrun[h][rb][i]);
+                        sc[1][rb][i] = __builtin_fmaf(sc[1][rb][i], sl, -mrun[h][rb][i]);
+                        pass_ref |= (sc[0][rb][i] > 0.f) | (sc[1][rb][i] > 0.f);
                     }
                 if (__ballot(pass_ref)) {   // rare after a row's first positions
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float pv = fmaxf(sc[0][rb][i], sc[1][rb][i]) * sl;
-                            const float rn = pv > mrun[h][rb][i] ? pv + 16.f : mrun[h][rb][i];
-                            zrun[h][rb][i] *= __builtin_amdgcn_exp2f(mrun[h][rb][i] - rn);
-                            mrun[h][rb][i] = rn;
-                            d[0][rb][i] = __builtin_fmaf(sc[0][rb][i], sl, -rn);
-                            d[1][rb][i] = __builtin_fmaf(sc[1][rb][i], sl, -rn);
+                            // the reference moves to the larger logit + 16
+                            const float dm = fmaxf(sc[0][rb][i], sc[1][rb][i]);
+                            const float up = dm > 0.f ? dm + 16.f : 0.f;
+                            zrun[h][rb][i] *= __builtin_amdgcn_exp2f(-up);
+                            mrun[h][rb][i] += up;
+                            sc[0][rb][i] -= up;
+                            sc[1][rb][i] -= up;
                         }
                 }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        zrun[h][rb][i] += __builtin_amdgcn_exp2f(d[0][rb][i]) + __builtin_amdgcn_exp2f(d[1][rb][i]);
+                        zrun[h][rb][i] += __builtin_amdgcn_exp2f(sc[0][rb][i]) + __builtin_amdgcn_exp2f(sc[1][rb][i]);
             }
             slot ^= 1;
         };
