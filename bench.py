@@ -935,7 +935,23 @@ def other_configs(args, cap, timed):
                      "us_per_step": round(us, 1), "GBps": round(by / us / 1e3, 1),
                      "frac_of_hbm_peak": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": by,
                      "components_us": parts}
-        log(f"{name}: one-layer step {us:.1f} us, {by / us / 1e3:.0f} GB/s; parts {parts}")
+        if not args.no_lse and sh.dtype == "bf16":
+            # labelled, not the line above: the same step with the draft row
+            # normalisers supplied (one read of draft K)
+            lse = dk.dustin_draft_row_lse(dkv, x.q_draft)
+
+            def step_lse():
+                dk.dustin_score(dkv, x.q_draft, [kv], x.q_hist, x.sub_heads, sh.Hq, s_draft=s_d, s_target=s_t,
+                                ws=ws_s, draft_lse=lse)
+                select()
+                attn()
+
+            us_l = graph_time(args, step_lse, cap, timed, reps)
+            out[name]["supplied_draft_normalisers"] = {
+                "us_per_step": round(us_l, 1), "frac_of_hbm_peak": round(by / us_l / 1e3 / HBM_PEAK_GBPS, 4)}
+        log(f"{name}: one-layer step {us:.1f} us, {by / us / 1e3:.0f} GB/s; parts {parts}"
+            + (f"; with supplied draft normalisers {out[name]['supplied_draft_normalisers']['us_per_step']} us"
+               if "supplied_draft_normalisers" in out[name] else ""))
         del x, kv, dkv, s_d, s_t
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
