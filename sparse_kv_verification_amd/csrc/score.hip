@@ -362,6 +362,165 @@ __global__ __launch_bounds__(256) void unit_stats_rows(RowStatsParams p) {
     }
 }
 
+// The whole-row form on the matrix cores, for units of five to eight rows
+// (every head of a layer scored: the all-heads estimator, the per-head rows
+// of the configuration search), where the VALU form's 16-lane sum per row
+// and position bounds it.  A work-group takes the heads [z * HPG, (z + 1) *
+// HPG) of its chunk (HPG = Hkv when the chunks alone fill the chip); wave w
+// takes HPW of them and every subtile (HPG >= 4), or one head and every
+// wph-th subtile (HPG < 4, wph = 4 / HPG).  The logits of one head's 16
+// positions are one MFMA chain: A = the unit's query rows (padded to 16),
+// B = the 16 key rows, d contracted in four 32-wide steps.  Key rows of
+// positions past n_b or in absent pages are zero (logit 0, then masked past
+// n_b), as in the VALU form.  The logits go to LDS, slot (local head, row)
+// with a row stride of CH + 4 floats (the four lane groups of an MFMA
+// result land in different banks), then one wave per slot writes the
+// chunk statistics and the logit row, as the VALU form does.
+constexpr int kRowsMfmaLdsStride = CH + 4;
+
+template <int HPW>
+__global__ __launch_bounds__(256, 2) void unit_stats_rows_mfma(RowStatsParams p, int HPG, int wph) {
+    constexpr int D = 128, KK = 4, NSUB = CH / 16;
+    extern __shared__ float lg[];    // [HPG][8][kRowsMfmaLdsStride]
+    __shared__ int pgs[NSUB];
+    const int chunk = blockIdx.x, b = blockIdx.y, hz = blockIdx.z, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const KvView &kv = p.kv;
+    const int nb = sl_len(kv, b);
+    const int j0 = chunk * CH;
+    if (j0 >= nb) return;   // statistics and logits past n_b are never read
+    const bool paged = kv.page_size != 0;
+    if (paged && tid < NSUB) {
+        const int pi = (j0 >> 4) + tid;
+        pgs[tid] = pi < kv.max_pages ? kv.page_table[(int64_t)b * kv.max_pages + pi] : -1;
+    }
+    const int hl0 = (wave / wph) * HPW;   // first local head of this wave
+    const int sub0 = wave % wph;          // first subtile; then every wph-th
+    // Q fragments of this wave's heads (row lane & 15 of the head's unit,
+    // d slice kk * 32 + (lane >> 4) * 8); padding rows are zero.
+    bf16x8 qf[HPW][KK];
+    int rbase[HPW], nrow[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        const int u = p.unit_of_head[hz * HPG + hl0 + hh];
+        rbase[hh] = p.row0[u];
+        nrow[hh] = p.nrow[u];
+        const int r = lane & 15;
+        const bool ok = r < nrow[hh];
+        const char *qp = p.q + (((int64_t)b * p.S + rbase[hh] + (ok ? r : 0)) * D + (lane >> 4) * 8) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 v = *(const u32x4 *)(qp + kk * 64);
+            qf[hh][kk] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    __syncthreads();   // page ids in LDS
+    const int64_t rowb = (int64_t)kv.Hkv * D * 2;   // bytes per position row
+    const int gph = NSUB / wph / 4;                   // groups of 4 subtiles per head
+    const int items = HPW * gph;
+    // Key fragments of item `it` (local head it % HPW, subtile group
+    // it / HPW: a wave's heads are read together, position by position);
+    // every load of an item is issued; positions past n_b and absent pages
+    // read row 0 and are zeroed after.
+    auto load = [&](int it, u32x4 (&k)[4][KK], uint32_t &okm) {
+        if (it >= items) return;   // wave-uniform
+        const int hh = it % HPW, g = it / HPW;
+        const int h = hz * HPG + hl0 + hh;
+        okm = 0;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int sub = sub0 + (g * 4 + st) * wph;
+            const int j = j0 + sub * 16 + (lane & 15);
+            int64_t r = -1;
+            if (paged) {
+                const int pg = pgs[sub];
+                if (j < nb && pg >= 0 && pg < kv.num_pages) r = (int64_t)pg * 16 + (j & 15);
+            } else if (j < nb) {
+                r = (int64_t)b * kv.N_max + j;
+            }
+            okm |= (r >= 0 ? 1u : 0u) << st;
+            const char *row = kv.k + (r >= 0 ? r : 0) * rowb + (int64_t)h * D * 2 + (lane >> 4) * 16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) k[st][kk] = *(const u32x4 *)(row + kk * 64);
+        }
+    };
+    auto fold = [&](int it, const u32x4 (&k)[4][KK], uint32_t okm) {
+        if (it >= items) return;
+        const int hh = it % HPW, g = it / HPW;
+        bf16x8 qc[KK];
+        int rb0 = 0, nr = 0;
+#pragma unroll
+        for (int c = 0; c < HPW; ++c)
+            if (c == hh) {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) qc[kk] = qf[c][kk];
+                rb0 = c;
+                nr = nrow[c];
+            }
+        float *slot = lg + ((hl0 + rb0) * 8) * kRowsMfmaLdsStride;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int sub = sub0 + (g * 4 + st) * wph;
+            const int pos = sub * 16 + (lane & 15);
+            const bool ok = (okm >> st) & 1u;
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const u32x4 kv4 = ok ? k[st][kk] : u32x4{0u, 0u, 0u, 0u};
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qc[kk], __builtin_bit_cast(bf16x8, kv4), sc, 0, 0, 0);
+            }
+            const bool live = j0 + pos < nb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 4) * 4 + i;
+                if (r < nr) slot[r * kRowsMfmaLdsStride + pos] = live ? sc[i] * p.scale_log2 : kNegInf;
+            }
+        }
+    };
+    u32x4 kA[4][KK], kB[4][KK];
+    uint32_t okA = 0, okB = 0;
+    load(0, kA, okA);
+    for (int it = 0; it < items; it += 2) {
+        load(it + 1, kB, okB);
+        fold(it, kA, okA);
+        load(it + 2, kA, okA);
+        fold(it + 1, kB, okB);
+    }
+    __syncthreads();
+    // one wave per (local head, row) slot
+    for (int sidx = wave; sidx < HPG * 8; sidx += 4) {
+        const int hl = sidx >> 3, rr = sidx & 7;
+        const int u = p.unit_of_head[hz * HPG + hl];
+        if (rr >= p.nrow[u]) continue;
+        const int r = p.row0[u] + rr;
+        const float *src = lg + sidx * kRowsMfmaLdsStride;
+        float v[CH / 64];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) {
+            v[i] = src[lane + 64 * i];
+            mx = fmaxf(mx, v[i]);
+        }
+        mx = wave_max(mx);
+        const float muse = (mx == kNegInf) ? 0.f : mx;
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) z += exp2f(v[i] - muse);
+        z = wave_sum(z);
+        if (lane == 0) {
+            float *st = p.stat + (((int64_t)b * p.S + r) * p.nchunk + chunk) * 2;
+            st[0] = mx;
+            st[1] = z;
+        }
+        float *lp = p.logit + ((int64_t)b * p.S + r) * p.N_max + j0;
+#pragma unroll
+        for (int i = 0; i < CH / 64; ++i) {
+            const int pos = lane + 64 * i;
+            if (j0 + pos < p.N_max) lp[pos] = v[i];
+        }
+    }
+}
+
 // Row log-sum-exp (log2 domain) from the per-chunk statistics.
 // One wave per row; rows are sequence-major (rows_per_b rows per sequence)
 // and only the chunks holding positions below n_b are read (the statistics
@@ -412,29 +571,68 @@ __global__ __launch_bounds__(256) void draft_lse_export(const float *lse, float 
 }
 
 // S_Target[b][j] = sum_r exp2(logit[r][j] - lse[r]).
+// V4: four positions per lane (N_max % 4 == 0, so every logit row is
+// 16-byte aligned); rows are summed in order either way.
+template <bool V4>
 __global__ __launch_bounds__(256) void target_finalize(const float *logit, const float *lse, float *out,
                                                        const int32_t *seq_lens, int S, int N_max) {
     const int b = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= N_max) return;
     const int nb = min(max(seq_lens[b], 0), N_max);
-    float acc = 0.f;
-    if (j < nb) {
-        for (int r = 0; r < S; ++r)
-            acc += exp2f(logit[((int64_t)b * S + r) * N_max + j] - lse[(int64_t)b * S + r]);
+    if constexpr (V4) {
+        const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+        if (j >= N_max) return;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (j < nb) {
+            const float *lg = logit + (int64_t)b * S * N_max + j;
+            const float *ls = lse + (int64_t)b * S;
+#pragma unroll 8
+            for (int r = 0; r < S; ++r) {
+                const f32x4 v = *(const f32x4 *)(lg + (int64_t)r * N_max);
+                const float m = ls[r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += exp2f(v[i] - m);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (j + i >= nb) acc[i] = 0.f;
+        }
+        *(f32x4 *)(out + (int64_t)b * N_max + j) = acc;
+    } else {
+        const int j = blockIdx.x * 256 + threadIdx.x;
+        if (j >= N_max) return;
+        float acc = 0.f;
+        if (j < nb) {
+            for (int r = 0; r < S; ++r)
+                acc += exp2f(logit[((int64_t)b * S + r) * N_max + j] - lse[(int64_t)b * S + r]);
+        }
+        out[(int64_t)b * N_max + j] = acc;
     }
-    out[(int64_t)b * N_max + j] = acc;
 }
 
-// Per-row form: out[r][b][j] = exp2(logit[b][r][j] - lse[b][r]) for j < n_b, 0 beyond.
+// Per-row form: out[r][b][j] = exp2(logit[b][r][j] - lse[b][r]) for j < n_b, 0 beyond
+// (V4: four positions per lane, N_max % 4 == 0).
+template <bool V4>
 __global__ __launch_bounds__(256) void target_rows_finalize(const float *logit, const float *lse, float *out,
                                                             const int32_t *seq_lens, int B, int S, int N_max) {
     const int b = blockIdx.y, r = blockIdx.z;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= N_max) return;
     const int nb = min(max(seq_lens[b], 0), N_max);
     const int64_t row = (int64_t)b * S + r;
-    out[((int64_t)r * B + b) * N_max + j] = (j < nb) ? exp2f(logit[row * N_max + j] - lse[row]) : 0.f;
+    if constexpr (V4) {
+        const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+        if (j >= N_max) return;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j < nb) {
+            const f32x4 x = *(const f32x4 *)(logit + row * N_max + j);
+            const float m = lse[row];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (j + i < nb) ? exp2f(x[i] - m) : 0.f;
+        }
+        *(f32x4 *)(out + ((int64_t)r * B + b) * N_max + j) = v;
+    } else {
+        const int j = blockIdx.x * 256 + threadIdx.x;
+        if (j >= N_max) return;
+        out[((int64_t)r * B + b) * N_max + j] = (j < nb) ? exp2f(logit[row * N_max + j] - lse[row]) : 0.f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1761,12 +1959,26 @@ static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
         q.N_max = k0.N_max;
         int nr_max = 1;
         for (int u = 0; u < ut.n_units; ++u) nr_max = ut.nrow[u] > nr_max ? ut.nrow[u] : nr_max;
-        const dim3 grid(a.nchunk, k0.B);
-        const size_t lds = (size_t)a.S * CH * sizeof(float);
-        if (nr_max == 1) hipLaunchKernelGGL(unit_stats_rows<1>, grid, dim3(256), lds, s, q);
-        else if (nr_max == 2) hipLaunchKernelGGL(unit_stats_rows<2>, grid, dim3(256), lds, s, q);
-        else if (nr_max <= 4) hipLaunchKernelGGL(unit_stats_rows<4>, grid, dim3(256), lds, s, q);
-        else hipLaunchKernelGGL(unit_stats_rows<8>, grid, dim3(256), lds, s, q);
+        if (nr_max > 4) {
+            // matrix-core form: split the KV heads over work-groups until the
+            // chunks fill the chip four times over (or one head per group)
+            const int Hkv = k0.Hkv;
+            int hsplit = 1;
+            while (hsplit < Hkv && (int64_t)a.nchunk * k0.B * hsplit < 4 * 256) hsplit *= 2;
+            while (Hkv / hsplit > 8) hsplit *= 2;   // at most 8 heads (64 KiB of logits) per group
+            const int HPG = Hkv / hsplit;
+            const int wph = HPG >= 4 ? 1 : 4 / HPG;
+            const dim3 grid(a.nchunk, k0.B, hsplit);
+            const size_t lds = (size_t)HPG * 8 * kRowsMfmaLdsStride * sizeof(float);
+            if (HPG >= 8) hipLaunchKernelGGL(unit_stats_rows_mfma<2>, grid, dim3(256), lds, s, q, HPG, wph);
+            else hipLaunchKernelGGL(unit_stats_rows_mfma<1>, grid, dim3(256), lds, s, q, HPG, wph);
+        } else {
+            const dim3 grid(a.nchunk, k0.B);
+            const size_t lds = (size_t)a.S * CH * sizeof(float);
+            if (nr_max == 1) hipLaunchKernelGGL(unit_stats_rows<1>, grid, dim3(256), lds, s, q);
+            else if (nr_max == 2) hipLaunchKernelGGL(unit_stats_rows<2>, grid, dim3(256), lds, s, q);
+            else hipLaunchKernelGGL(unit_stats_rows<4>, grid, dim3(256), lds, s, q);
+        }
         e = hipGetLastError();
     } else {
         e = run_unit_stats(p, k0.B, s);
@@ -1777,11 +1989,19 @@ static hipError_t target_impl(const TargetScoreArgs &a, hipStream_t s) {
                        k0.seq_lens, a.S, CH, k0.N_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.rows_out) {
-        hipLaunchKernelGGL(target_rows_finalize, dim3((k0.N_max + 255) / 256, k0.B, a.S), dim3(256), 0, s, a.logit,
-                           lse, a.rows_out, k0.seq_lens, k0.B, a.S, k0.N_max);
+        if (k0.N_max % 4 == 0 && ((uintptr_t)a.rows_out | (uintptr_t)a.logit) % 16 == 0)
+            hipLaunchKernelGGL(target_rows_finalize<true>, dim3((k0.N_max / 4 + 255) / 256, k0.B, a.S), dim3(256), 0,
+                               s, a.logit, lse, a.rows_out, k0.seq_lens, k0.B, a.S, k0.N_max);
+        else
+            hipLaunchKernelGGL(target_rows_finalize<false>, dim3((k0.N_max + 255) / 256, k0.B, a.S), dim3(256), 0, s,
+                               a.logit, lse, a.rows_out, k0.seq_lens, k0.B, a.S, k0.N_max);
     } else {
-        hipLaunchKernelGGL(target_finalize, dim3((k0.N_max + 255) / 256, k0.B), dim3(256), 0, s, a.logit, lse,
-                           a.s_target, k0.seq_lens, a.S, k0.N_max);
+        if (k0.N_max % 4 == 0 && ((uintptr_t)a.s_target | (uintptr_t)a.logit) % 16 == 0)
+            hipLaunchKernelGGL(target_finalize<true>, dim3((k0.N_max / 4 + 255) / 256, k0.B), dim3(256), 0, s,
+                               a.logit, lse, a.s_target, k0.seq_lens, a.S, k0.N_max);
+        else
+            hipLaunchKernelGGL(target_finalize<false>, dim3((k0.N_max + 255) / 256, k0.B), dim3(256), 0, s, a.logit,
+                               lse, a.s_target, k0.seq_lens, a.S, k0.N_max);
     }
     return hipGetLastError();
 }

@@ -282,6 +282,56 @@ def test_target_scores_whole_row_form(layout, paged):
         assert (f64(s_t[b, n:]) == 0).all()
 
 
+# Every head of a layer scored (five to eight rows per KV head: the matrix-
+# core whole-row pass).  The shapes pick how the KV heads are split over
+# work-groups: one head per group with four waves sharing its subtiles (few
+# chunks), two heads, four heads, all eight heads per group (two per wave).
+ALL_HEADS_CASES = [
+    ("g7-hkv4-one-head-per-group", dict(base="c2", B=2, n=3000, n_lo=1100), None, False),
+    ("g8-paged-ragged-empty", dict(base="c5", B=3, n=2600, n_lo=700), None, True),
+    ("g8-two-heads-per-group", dict(base="c4", B=2, n=40000), None, False),
+    ("g8-four-heads-per-group", dict(base="c4", B=4, n=40000), [0, 3], False),
+    ("g8-eight-heads-per-group", dict(base="c4", B=8, n=32768), [1, 6], False),
+]
+
+
+@pytest.mark.parametrize("name,over,check,empty_last", ALL_HEADS_CASES, ids=[c[0] for c in ALL_HEADS_CASES])
+def test_target_scores_all_heads(name, over, check, empty_last):
+    """S_Target over every head of one layer, and the per-head softmax rows
+    (dustin_head_scores), against the oracle on the same heads: contiguous
+    and paged caches, ragged lengths that end inside a chunk, an empty
+    sequence, and each split of the KV heads over work-groups."""
+    say("all-heads target scores", name)
+    over = dict(over)
+    sh = synth.preset(over.pop("base")).replace(L_d=1, **over)
+    x = synth.make(sh, device=DEV)
+    lens = x.seq_lens.clone()
+    if empty_last:
+        lens[-1] = 0
+    heads = [(0, h) for h in range(sh.Hq)]
+    qh = x.q[:, -1].contiguous()
+    kvs = [dk.KV(x.K, None, lens, x.page_table)]
+    _, s_t = dk.dustin_score([], None, kvs, qh, heads, sh.Hq, want_draft=False)
+    rows = dk.dustin_head_scores(kvs, qh, heads, sh.Hq)
+    _, s_t2 = dk.dustin_score([], None, kvs, qh, heads, sh.Hq, want_draft=False)
+    torch.cuda.synchronize()
+    assert torch.equal(s_t, s_t2), "not deterministic"
+    for b in (check if check is not None else range(sh.B)):
+        n = int(lens[b])
+        if n == 0:
+            assert (f64(s_t[b]) == 0).all() and (f64(rows[:, b]) == 0).all()
+            continue
+        K = oracle_kv(x, "K", b)[:n]
+        st = oracle.score_target(f64(qh[b]), {0: K}, heads, sh.Hq)
+        hp = oracle.head_probs(f64(qh[b])[None], K)[:, 0]
+        say(f"  b={b} n={n} max rel|dS_T|={max_rel_err(f64(s_t[b, :n]), st):.2e} "
+            f"rows {max_rel_err(f64(rows[:, b, :n]).ravel(), hp.ravel()):.2e}")
+        assert_scores_close(f64(s_t[b, :n]), st, "S_Target")
+        assert_scores_close(f64(rows[:, b, :n]).ravel(), hp.ravel(), "head rows")
+        assert (f64(s_t[b, n:]) == 0).all() and (f64(rows[:, b, n:]) == 0).all()
+        assert abs(f64(s_t[b, :n]).sum() - sh.Hq) < 1e-3 * sh.Hq
+
+
 LSE_CASES = [
     ("stream-ragged-empty", dict(base="c2", B=3, n=3000, L_d=3, n_lo=900), True),   # last sequence empty
     ("stream-one-head-paged", dict(base="c5", B=2, n=3000, n_lo=1200, L_d=2, w=8), False),
