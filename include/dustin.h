@@ -332,6 +332,11 @@ dustin_status dustin_commit_window(int32_t *seq_lens, const int32_t *accepted, i
  *
  *  q   [B][w][H_q][head_dim], kv dtype
  *  A   out [B][w][N_max] float32, 0 at j >= n_b
+ *
+ * w <= 16.  bfloat16 caches (B <= 1024): G = H_q / H_kv <= 64; the window is
+ * processed in slices of min(4, 64 / G) steps, two reads of K per slice.
+ * float32 caches: w * G <= 64 (the attention kernel's limit).  Anything else
+ * returns DUSTIN_ERR_UNSUPPORTED.
  */
 dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q,
                                  const dustin_kv *kv, float scale, float *A,

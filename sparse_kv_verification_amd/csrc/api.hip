@@ -132,10 +132,13 @@ WindowLayout window_layout(int B, int w, int H_q, int H_kv, int D, int N_max, in
 }
 
 // The window attention through the statistics passes (one K read for the
-// row normalisers, one for the probabilities, both on MFMA): bfloat16, at
-// most 4 window steps and 64 rows per KV head.
-bool window_steps_apply(const dustin_kv *kv, int w, int H_q) {
-    return kv->dtype == DUSTIN_BF16 && w <= 4 && (int64_t)w * (H_q / kv->H_kv) <= 64 && kv->B <= kMaxDraftBatch;
+// row normalisers, one for the probabilities, both on MFMA), bfloat16: the
+// window steps per pass are at most four (per-step lane sums) and at most 64
+// rows per KV head; 0 when the form does not apply.
+int window_steps_group(const dustin_kv *kv, int w, int H_q) {
+    const int G = H_q / kv->H_kv;
+    if (kv->dtype != DUSTIN_BF16 || kv->B > kMaxDraftBatch || G > 64) return 0;
+    return std::min(std::min(w, 4), 64 / G);
 }
 
 }  // namespace
@@ -354,8 +357,14 @@ dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q, const du
                                  void *ws, size_t ws_bytes, dustin_stream_t stream) {
     dustin_status st = check_kv(kv, "window_attn kv", false);
     if (st != DUSTIN_OK) return st;
-    if ((st = check_attn_shape(kv, w, H_q, "window_attn")) != DUSTIN_OK) return st;
+    CHECK(w >= 1 && H_q >= 1, DUSTIN_ERR_INVALID_ARG, "window_attn: w and H_q must be >= 1");
+    CHECK(H_q % kv->H_kv == 0, DUSTIN_ERR_INVALID_ARG, "window_attn: H_q %d not a multiple of H_kv %d", H_q,
+          kv->H_kv);
     CHECK(w <= 16, DUSTIN_ERR_UNSUPPORTED, "window_attn: w %d exceeds 16", w);
+    // the statistics form takes the window in slices; the dense-pass form
+    // (float32) has the attention kernel's limits
+    if (!window_steps_group(kv, w, H_q) && (st = check_attn_shape(kv, w, H_q, "window_attn")) != DUSTIN_OK)
+        return st;
     CHECK(q != nullptr && A != nullptr, DUSTIN_ERR_INVALID_ARG, "window_attn: q and A are required");
     CHECK(std::isfinite(scale), DUSTIN_ERR_INVALID_ARG, "window_attn: scale is not finite");
     // The dense pass needs V only for its (discarded) output; K stands in.
@@ -363,25 +372,35 @@ dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q, const du
     CHECK(ws != nullptr && ws_bytes >= L.bytes, DUSTIN_ERR_INVALID_ARG,
           "window_attn: workspace of %zu bytes needed (got %zu)", L.bytes, ws_bytes);
     char *wsb = (char *)ws;
-    if (window_steps_apply(kv, w, H_q)) {
-        DraftScoreArgs da{};
-        da.kv[0] = view_of(kv);
-        da.L_d = 1;
-        da.H_d = H_q;
-        da.gamma = w;
-        da.Hkv_d = kv->H_kv;
-        da.G_d = H_q / kv->H_kv;
-        da.rows = w * da.G_d;
-        da.q_draft = q;
-        da.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
-        const ScorePlan sp = score_plan(kv->B, kv->N_max, 1, H_q, w, 0, kv->H_kv);
-        char *sws = wsb + window_steps_offset();
-        da.stat = (float *)(sws + sp.off_dstat);
-        da.lse = (float *)(sws + sp.off_dlse);
-        da.nchunk = sp.nchunk;
-        da.steps_out = A;
-        da.steps_scale = 1.f / (float)H_q;
-        return hip_status(launch_window_steps(da, (hipStream_t)stream), "window_attn launch");
+    if (const int wg = window_steps_group(kv, w, H_q)) {
+        // the window in slices of wg steps, each one pass of the draft
+        // machinery over the layer (two K reads per slice)
+        const size_t esz = 2;
+        for (int s0 = 0; s0 < w; s0 += wg) {
+            const int g = std::min(wg, w - s0);
+            DraftScoreArgs da{};
+            da.kv[0] = view_of(kv);
+            da.L_d = 1;
+            da.H_d = H_q;
+            da.gamma = g;
+            da.Hkv_d = kv->H_kv;
+            da.G_d = H_q / kv->H_kv;
+            da.rows = g * da.G_d;
+            da.q_draft = (const char *)q + (size_t)s0 * H_q * kv->head_dim * esz;
+            da.q_bstride = (int64_t)w * H_q * kv->head_dim;
+            da.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
+            const ScorePlan sp = score_plan(kv->B, kv->N_max, 1, H_q, g, 0, kv->H_kv);
+            char *sws = wsb + window_steps_offset();
+            da.stat = (float *)(sws + sp.off_dstat);
+            da.lse = (float *)(sws + sp.off_dlse);
+            da.nchunk = sp.nchunk;
+            da.steps_out = A + (size_t)s0 * kv->N_max;
+            da.steps_bstride = w;
+            da.steps_scale = 1.f / (float)H_q;
+            const hipError_t e = launch_window_steps(da, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_status(e, "window_attn launch");
+        }
+        return DUSTIN_OK;
     }
     AttnArgs a{};
     a.kv = view_of(kv);

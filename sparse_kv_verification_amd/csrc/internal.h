@@ -62,6 +62,11 @@ struct DraftScoreArgs {
     int32_t nchunk;
     float *steps_out;               // window form: [B][gamma][N_max] per-step sums times steps_scale
     float steps_scale;
+    // window form on a slice of the window steps: elements of q_draft per
+    // sequence (0: L_d * gamma * H_d * d_d) and rows of steps_out per
+    // sequence (0: gamma)
+    int64_t q_bstride;
+    int32_t steps_bstride;
     float *part;                    // ws: [acc_groups][B][N_max] per-layer-group partial sums
     int32_t acc_groups;             // layer groups of the streaming accumulation (1: no partials)
     // supplied row normalisers, natural log, [B][L_d][gamma][H_d] (nullable):
@@ -74,7 +79,8 @@ struct DraftScoreArgs {
 
 hipError_t launch_draft_score(const DraftScoreArgs &a, hipStream_t s);
 // Window attention A (Eq. 1) of one layer through the draft passes: bf16,
-// gamma <= 4 window steps, gamma * G <= 64 rows; steps_out / steps_scale set.
+// gamma <= 4 window steps, gamma * G <= 64 rows; steps_out / steps_scale set
+// (and q_bstride / steps_bstride for a slice of a longer window).
 hipError_t launch_window_steps(const DraftScoreArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- select

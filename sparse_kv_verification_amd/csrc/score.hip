@@ -722,8 +722,9 @@ struct DraftMfma {
             const bool ok = r < a.rows;
             const int rr = ok ? r : 0;
             const int gs = rr / a.G_d, hh = rr - (rr / a.G_d) * a.G_d;
-            const uint16_t *qp = (const uint16_t *)a.q_draft +
-                ((((int64_t)b * a.L_d + l) * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + (lane >> 4) * 8;
+            const int64_t qbs = a.q_bstride ? a.q_bstride : (int64_t)a.L_d * a.gamma * a.H_d * D;
+            const uint16_t *qp = (const uint16_t *)a.q_draft + (int64_t)b * qbs +
+                (((int64_t)l * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + (lane >> 4) * 8;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const u32x4 v = *(const u32x4 *)(qp + kk * 32);
@@ -995,6 +996,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
     const int N = k0.N_max;
     const int B = k0.B;
+    const int64_t sbs = a.steps_bstride ? a.steps_bstride : a.gamma;   // steps_out rows per sequence
     // Items are (b, chunk) over the chunks that hold positions below n_b
     // only, numbered sequence by sequence (B <= kDraftStatMaxB, checked by
     // the launchers), so a ragged batch spreads evenly over the groups; the
@@ -1013,7 +1015,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         const int j0 = (pref[bb + 1] - pref[bb]) * kDraftAccChunk;
         for (int j = j0 + blockIdx.x * 256 + (int)threadIdx.x; j < N; j += gridDim.x * 256) {
             if constexpr (W > 0) {
-                for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)bb * a.gamma + q2) * N + j] = 0.f;
+                for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)bb * sbs + q2) * N + j] = 0.f;
             } else {
                 a.s_draft[(int64_t)bb * N + j] = 0.f;
             }
@@ -1056,7 +1058,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
             const int j = jb + lane;
             if (j < N) {
                 if constexpr (W > 0) {
-                    for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)b * a.gamma + q2) * N + j] = 0.f;
+                    for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)b * sbs + q2) * N + j] = 0.f;
                 } else {
                     a.s_draft[(int64_t)b * N + j] = 0.f;
                 }
@@ -1122,8 +1124,9 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
         auto load_ql = [&](int u, bf16x8 (&q)[RB][KK], float (&ls)[RB][4]) {
             u = (u < U) ? u : U - 1;
             const int l = u / a.Hkv_d, kvh = u - (u / a.Hkv_d) * a.Hkv_d;
-            const uint16_t *qb = (const uint16_t *)a.q_draft +
-                ((((int64_t)b * a.L_d + l) * a.gamma) * a.H_d + kvh * a.G_d) * D;
+            const int64_t qbs = a.q_bstride ? a.q_bstride : (int64_t)a.L_d * a.gamma * a.H_d * D;
+            const uint16_t *qb = (const uint16_t *)a.q_draft + (int64_t)b * qbs +
+                (((int64_t)l * a.gamma) * a.H_d + kvh * a.G_d) * D;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -1185,7 +1188,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_mfma(DraftScoreArgs a) {
                 for (int q2 = 0; q2 < NS; ++q2) {
                     const float v = group4_sum(acc[st][q2]);
                     if (lane < 16 && j < N && q2 < a.gamma)
-                        a.steps_out[((int64_t)b * a.gamma + q2) * N + j] = v * a.steps_scale;
+                        a.steps_out[((int64_t)b * sbs + q2) * N + j] = v * a.steps_scale;
                 }
             } else {
                 const float v = group4_sum(acc[st][0]);

@@ -136,6 +136,13 @@ def test_arr_and_window_argument_errors(L):
     assert L.dustin_window_attn(FAKE, 17, 8, ctypes.byref(desc), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
     assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, None, FAKE, 1 << 40, None) == INVALID
     assert L.dustin_window_attn(FAKE, 4, 64, ctypes.byref(desc), 0.0, FAKE, FAKE, 16, None) == INVALID
+    # bfloat16 takes long windows in slices (at most 64 rows per KV head per slice), float32 does not
+    assert L.dustin_window_attn(FAKE, 4, 60, ctypes.byref(desc), 0.0, FAKE, FAKE, 1 << 40, None) == INVALID
+    h2 = kv(H_kv=1)
+    assert L.dustin_window_attn(FAKE, 2, 65, ctypes.byref(h2), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    f32 = kv(dtype=0)
+    assert L.dustin_window_attn(FAKE, 16, 64, ctypes.byref(f32), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert L.dustin_window_attn(FAKE, 9, 64, ctypes.byref(f32), 0.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
 
 
 def test_verify_window_argument_errors(L):

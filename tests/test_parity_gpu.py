@@ -458,8 +458,12 @@ def test_scores_treat_absent_pages_as_zero_keys(w):
     ("qwen7b-rows28", dict(base="c2", B=2, n=2600, n_lo=900, L_d=1)),        # 7 rows per step
     ("d64-one-step", dict(base="c4", B=2, n=2100, Hq=8, Hkv=2, d=64, w=1, L_d=1)),
     ("paged-one-step", dict(base="c5", B=2, n=2000, n_lo=800, w=1, L_d=1)),
-    ("paged", dict(base="c5", B=2, n=2000, n_lo=800, L_d=1)),                # w = 8: the dense-pass form
-    ("tiny-f32", dict(base="c1")),
+    ("paged", dict(base="c5", B=2, n=2000, n_lo=800, L_d=1)),                # w = 8: two slices of 4 steps
+    ("w6-slices-4-2", dict(base="c4", B=2, n=2300, w=6, L_d=1)),
+    ("w5-g16", dict(base="c4", B=2, n=2200, Hq=64, Hkv=4, w=5, L_d=1)),      # 64 rows per slice of 4
+    ("w3-g32-d64", dict(base="c4", B=2, n=1900, Hq=64, Hkv=2, d=64, w=3, L_d=1)),   # slices of 2 steps
+    ("w16-g7", dict(base="c2", B=1, n=2000, w=16, L_d=1)),                   # four slices
+    ("tiny-f32", dict(base="c1")),                                           # float32: the dense-pass form
 ])
 def test_window_attention_and_arr(name, over):
     say("window attention + ARR", name)
@@ -494,15 +498,16 @@ def test_window_attention_and_arr(name, over):
 
 
 def test_window_attention_paths_share_a_workspace():
-    """The statistics form (bf16, w <= 4) and the dense-pass form (w = 8, or
-    float32) of the window attention run on one workspace in both orders;
-    the statistics form must leave the attention arrival counters at the
-    workspace's start untouched (zero)."""
+    """The statistics form (bf16; w = 8 in two slices) and the dense-pass
+    form (float32) of the window attention run on one workspace in both
+    orders; the statistics form must leave the attention arrival counters at
+    the workspace's start untouched (zero)."""
     say("window attention: both forms on one workspace")
     ws = dk.Workspace()
     buf = ws.get(1 << 28, torch.device("cuda", torch.cuda.current_device()))   # large enough for all three calls
     ptr = buf.data_ptr()
-    for base, over in (("c4", dict(B=2, n=1500, L_d=1)), ("c5", dict(B=2, n=1500, n_lo=700, L_d=1)),
+    for base, over in (("c4", dict(B=2, n=1500, L_d=1)), ("c1", dict(n=1500)),
+                       ("c5", dict(B=2, n=1500, n_lo=700, L_d=1)), ("c1", dict(n=1300, seed=9)),
                        ("c4", dict(B=2, n=1500, L_d=1, seed=9))):
         sh = synth.preset(base).replace(**over)
         x = synth.make(sh, device=DEV)
