@@ -813,7 +813,7 @@ constexpr int kDraftStatChunk = 4096;
 constexpr int kDraftStatMaxB = kMaxDraftBatch;   // sequences per call of the statistics pass
 
 template <int D, int RB>
-__global__ __launch_bounds__(256, RB >= 3 ? 1 : 2) void draft_stats_mfma(DraftScoreArgs a) {
+__global__ __launch_bounds__(256, (RB >= 3 || (D == 128 && RB >= 2)) ? 1 : 2) void draft_stats_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     __shared__ float red[4][RB * 16][2];
     __shared__ int pref[kDraftStatMaxB + 1];  // chunks below n_b of sequences before b
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(256, RB >= 3 ? 1 : 2) void draft_stats_mfma(DraftSc
 constexpr int kDraftAccChunk = 256;
 
 template <int D, int RB, bool PAGED, int W = 0>
-__global__ __launch_bounds__(256, (W > 0 && D == 128 && RB >= 2) ? 1 : 2) void draft_acc_mfma(DraftScoreArgs a) {
+__global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     constexpr int KK = M::KK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

@@ -215,6 +215,10 @@ SCORE_CASES = [
     ("stream-one-head-groups", dict(base="c4", B=1, n=2048, L_d=8, w=8)),
     ("stream-odd-layers", dict(base="c2", B=2, n=3000, n_lo=1100, L_d=5)),     # 28 rows, five layers
     ("stream-one-head-odd-layers", dict(base="c4", B=2, n=2500, L_d=3, w=8)),  # 56 rows, three layers
+    # draft head_dim 128: the register-staged passes at two, three and four row blocks
+    ("mfma-d128-rb2", dict(base="c2", B=2, n=2300, n_lo=800, L_d=2, d_d=128)),
+    ("mfma-d128-rb3", dict(base="c2", B=2, n=2000, L_d=3, d_d=128, H_d=12, w=6)),
+    ("mfma-d128-rb4-paged", dict(base="c5", B=2, n=2600, n_lo=900, L_d=2, d_d=128)),
     ("tiny-f32", dict(base="c1")),
 ]
 
