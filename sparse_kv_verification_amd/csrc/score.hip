@@ -23,6 +23,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace dustin {
 
 constexpr int CH = kScoreChunk;
@@ -1391,15 +1393,18 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             if (pref[mid] <= cu) lo = mid;
             else hi = mid - 1;
         }
-        x.b = lo;
-        const int nbc = pref[lo + 1] - pref[lo];
-        const int r = it - per * pref[lo];     // within the sequence: (layer, head)-major
+        // every field is the same across the wave: readfirstlane makes that
+        // visible to the compiler, so tests on them are scalar branches
+        // (the LDS reads above otherwise make them look per-lane)
+        x.b = __builtin_amdgcn_readfirstlane(lo);
+        const int nbc = __builtin_amdgcn_readfirstlane(pref[lo + 1] - pref[lo]);
+        const int r = it - per * __builtin_amdgcn_readfirstlane(pref[lo]);   // within the sequence: (layer, head)-major
         const int u = r / nbc;
         x.c = r - u * nbc;
         x.l = u / NHI;
         x.h = u - x.l * NHI;
-        x.nb = sl_len(a.kv[x.l], x.b);
-        x.jw = x.c * kDraftStatChunk + wave * PER_WAVE;
+        x.nb = __builtin_amdgcn_readfirstlane(sl_len(a.kv[x.l], x.b));
+        x.jw = x.c * kDraftStatChunk + __builtin_amdgcn_readfirstlane(wave) * PER_WAVE;
         const int left = x.nb - x.jw;
         x.nst = left <= 0 ? 0 : min(NSTAGE, (left + POS - 1) / POS);
         x.seq = PAGED ? a.kv[x.l].k : a.kv[x.l].k + (int64_t)x.b * a.kv[x.l].N_max * 256;
@@ -1444,7 +1449,10 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             if (s + 1 < cur.nst) issue(cur, pg, s + 1, ring[wave][slot ^ 1]);
             else if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot ^ 1]);
         };
-        auto stage = [&](int s) {
+        // FIRST: the item's first stage (its first pair sets the references);
+        // a compile-time flag, so the other stages carry no trace of that path
+        auto stage = [&](int s, auto first) {
+            constexpr bool FIRST = decltype(first)::value;
             const uint32_t base = lds_addr(ring[wave][slot]);
             const int j0 = cur.jw + s * POS;
             const bool full = j0 + POS <= cur.nb;
@@ -1493,7 +1501,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                             if (j0 + pr * 32 + (lane & 15) >= cur.nb) sc[0][rb][i] = kNegInf;
                             if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) sc[1][rb][i] = kNegInf;
                         }
-                if (s == 0 && pr == 0) {
+                if (FIRST && pr == 0) {
                     // The item's first pair sets each row's reference from
                     // its own logits.  A lane whose first pair is masked has
                     // no valid position in the item at all (positions only
@@ -1553,11 +1561,11 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
             pgn = load_pg(nxt);
             next_dma(0);
-            stage(0);
+            stage(0, std::true_type{});
             for (int s = 1; s < cur.nst; ++s) {
                 wait_vmcnt<0>();
                 next_dma(s);
-                stage(s);
+                stage(s, std::false_type{});
             }
         }
         // combine the 16 token lanes of each row, then the four waves
