@@ -141,6 +141,49 @@ int window_steps_group(const dustin_kv *kv, int w, int H_q) {
     return std::min(std::min(w, 4), 64 / G);
 }
 
+// The statistics form over w window steps whose queries sit at
+// q + b * q_bstride + s * q_sstride (elements, [H_q][head_dim] each) and whose
+// weights go to A + (b * a_bstride + s * a_sstride) * N_max, in slices of
+// window_steps_group steps on the workspace's statistics region.  The
+// caller has checked that the form applies; a step stride too large for the
+// kernels' 32-bit query offsets returns DUSTIN_ERR_UNSUPPORTED.
+dustin_status window_steps_run(const void *q, int64_t q_bstride, int64_t q_sstride, int w, int H_q,
+                               const dustin_kv *kv, float scale, float *A, int64_t a_bstride, int64_t a_sstride,
+                               char *wsb, hipStream_t stream) {
+    const int wg = window_steps_group(kv, w, H_q);
+    CHECK(wg > 0, DUSTIN_ERR_UNSUPPORTED, "window_attn: the statistics form does not apply");
+    CHECK((int64_t)(wg - 1) * q_sstride + (int64_t)H_q * kv->head_dim < ((int64_t)1 << 29), DUSTIN_ERR_UNSUPPORTED,
+          "window_attn: query step stride %lld too large", (long long)q_sstride);
+    const size_t esz = 2;
+    for (int s0 = 0; s0 < w; s0 += wg) {
+        const int g = std::min(wg, w - s0);
+        DraftScoreArgs da{};
+        da.kv[0] = view_of(kv);
+        da.L_d = 1;
+        da.H_d = H_q;
+        da.gamma = g;
+        da.Hkv_d = kv->H_kv;
+        da.G_d = H_q / kv->H_kv;
+        da.rows = g * da.G_d;
+        da.q_draft = (const char *)q + (size_t)s0 * q_sstride * esz;
+        da.q_bstride = q_bstride;
+        da.q_sstride = q_sstride;
+        da.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
+        const ScorePlan sp = score_plan(kv->B, kv->N_max, 1, H_q, g, 0, kv->H_kv);
+        char *sws = wsb + window_steps_offset();
+        da.stat = (float *)(sws + sp.off_dstat);
+        da.lse = (float *)(sws + sp.off_dlse);
+        da.nchunk = sp.nchunk;
+        da.steps_out = A + (size_t)s0 * a_sstride * kv->N_max;
+        da.steps_bstride = (int32_t)a_bstride;
+        da.steps_sstride = (int32_t)a_sstride;
+        da.steps_scale = 1.f / (float)H_q;
+        const hipError_t e = launch_window_steps(da, stream);
+        if (e != hipSuccess) return hip_status(e, "window_attn launch");
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,35 +415,10 @@ dustin_status dustin_window_attn(const void *q, int32_t w, int32_t H_q, const du
     CHECK(ws != nullptr && ws_bytes >= L.bytes, DUSTIN_ERR_INVALID_ARG,
           "window_attn: workspace of %zu bytes needed (got %zu)", L.bytes, ws_bytes);
     char *wsb = (char *)ws;
-    if (const int wg = window_steps_group(kv, w, H_q)) {
-        // the window in slices of wg steps, each one pass of the draft
-        // machinery over the layer (two K reads per slice)
-        const size_t esz = 2;
-        for (int s0 = 0; s0 < w; s0 += wg) {
-            const int g = std::min(wg, w - s0);
-            DraftScoreArgs da{};
-            da.kv[0] = view_of(kv);
-            da.L_d = 1;
-            da.H_d = H_q;
-            da.gamma = g;
-            da.Hkv_d = kv->H_kv;
-            da.G_d = H_q / kv->H_kv;
-            da.rows = g * da.G_d;
-            da.q_draft = (const char *)q + (size_t)s0 * H_q * kv->head_dim * esz;
-            da.q_bstride = (int64_t)w * H_q * kv->head_dim;
-            da.scale_log2 = resolve_scale(scale, kv->head_dim) * kLog2e;
-            const ScorePlan sp = score_plan(kv->B, kv->N_max, 1, H_q, g, 0, kv->H_kv);
-            char *sws = wsb + window_steps_offset();
-            da.stat = (float *)(sws + sp.off_dstat);
-            da.lse = (float *)(sws + sp.off_dlse);
-            da.nchunk = sp.nchunk;
-            da.steps_out = A + (size_t)s0 * kv->N_max;
-            da.steps_bstride = w;
-            da.steps_scale = 1.f / (float)H_q;
-            const hipError_t e = launch_window_steps(da, (hipStream_t)stream);
-            if (e != hipSuccess) return hip_status(e, "window_attn launch");
-        }
-        return DUSTIN_OK;
+    if (window_steps_group(kv, w, H_q)) {
+        // [B][w][H_q][head_dim] queries, [B][w][N_max] weights
+        const int64_t qs = (int64_t)H_q * kv->head_dim;
+        return window_steps_run(q, w * qs, qs, w, H_q, kv, scale, A, w, 1, wsb, (hipStream_t)stream);
     }
     AttnArgs a{};
     a.kv = view_of(kv);
@@ -632,7 +650,9 @@ struct SweepLayout {
 SweepLayout sweep_layout(int B, int w, int P, int H_q, int H_kv, int D, int N, int k_max) {
     SweepLayout L{};
     const size_t a1 = window_layout(B, w, H_q, H_kv, D, N, 4).bytes;
-    const size_t a2 = window_layout(B, 1, H_q, H_kv, D, N, 4).bytes;
+    // the past queries: one step each (dense-pass form) or slices of up to
+    // four steps (statistics form)
+    const size_t a2 = window_layout(B, std::min(std::max(P, 1), 4), H_q, H_kv, D, N, 4).bytes;
     L.attn_bytes = a1 > a2 ? a1 : a2;
     size_t off = align_up(L.attn_bytes, 256);
     L.off_awin = off;
@@ -713,13 +733,21 @@ dustin_status dustin_policy_sweep(const void *q_window, int32_t w, const void *q
         const hipError_t e = launch_window_mean(Awin, B, w, N, Abar, (hipStream_t)stream);
         if (e != hipSuccess) return hip_status(e, "policy_sweep window mean");
     }
-    // A_{i-delta,.} of each past query (a one-step window each)
+    // A_{i-delta,.} of each past query: the past queries [n_past][B][H_q][d]
+    // are the steps of one window (step-major), so the statistics form reads
+    // K twice per four of them; otherwise one one-step window each
     const size_t esz = kv->dtype == DUSTIN_F32 ? 4 : 2;
     const size_t qstride = (size_t)B * H_q * kv->head_dim * esz;
-    for (int p = 0; p < n_past; ++p)
-        if ((st = dustin_window_attn((const char *)q_past + p * qstride, 1, H_q, kv, scale, Apast + (size_t)p * B * N,
-                                     wsb, L.attn_bytes, stream)) != DUSTIN_OK)
+    if (n_past > 0 && window_steps_group(kv, n_past, H_q)) {
+        if ((st = window_steps_run(q_past, (int64_t)H_q * kv->head_dim, (int64_t)B * H_q * kv->head_dim, n_past, H_q,
+                                   kv, scale, Apast, 1, B, wsb, (hipStream_t)stream)) != DUSTIN_OK)
             return st;
+    } else {
+        for (int p = 0; p < n_past; ++p)
+            if ((st = dustin_window_attn((const char *)q_past + p * qstride, 1, H_q, kv, scale,
+                                         Apast + (size_t)p * B * N, wsb, L.attn_bytes, stream)) != DUSTIN_OK)
+                return st;
+    }
     auto eval = [&](const float *sd, const float *stg, int k, int m, int ns, int nw, int row, int ki) {
         dustin_status e = dustin_topk(sd, stg, kv->seq_lens, B, N, k, m, ns, nw, idx, cnt, nullptr, tws, tbytes, stream);
         if (e != DUSTIN_OK) return e;

@@ -62,11 +62,12 @@ struct DraftScoreArgs {
     int32_t nchunk;
     float *steps_out;               // window form: [B][gamma][N_max] per-step sums times steps_scale
     float steps_scale;
-    // window form on a slice of the window steps: elements of q_draft per
-    // sequence (0: L_d * gamma * H_d * d_d) and rows of steps_out per
-    // sequence (0: gamma)
-    int64_t q_bstride;
-    int32_t steps_bstride;
+    // window form on a slice of the window steps, or on steps stored step-
+    // major: elements of q_draft per sequence (0: L_d * gamma * H_d * d_d)
+    // and between consecutive steps (0: H_d * d_d); rows of steps_out per
+    // sequence (0: gamma) and between consecutive steps (0: 1)
+    int64_t q_bstride, q_sstride;
+    int32_t steps_bstride, steps_sstride;
     float *part;                    // ws: [acc_groups][B][N_max] per-layer-group partial sums
     int32_t acc_groups;             // layer groups of the streaming accumulation (1: no partials)
     // supplied row normalisers, natural log, [B][L_d][gamma][H_d] (nullable):

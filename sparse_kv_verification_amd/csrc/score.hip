@@ -725,8 +725,9 @@ struct DraftMfma {
             const int rr = ok ? r : 0;
             const int gs = rr / a.G_d, hh = rr - (rr / a.G_d) * a.G_d;
             const int64_t qbs = a.q_bstride ? a.q_bstride : (int64_t)a.L_d * a.gamma * a.H_d * D;
-            const uint16_t *qp = (const uint16_t *)a.q_draft + (int64_t)b * qbs +
-                (((int64_t)l * a.gamma + gs) * a.H_d + c * a.G_d + hh) * D + (lane >> 4) * 8;
+            const int64_t qss = a.q_sstride ? a.q_sstride : (int64_t)a.H_d * D;
+            const uint16_t *qp = (const uint16_t *)a.q_draft + (int64_t)b * qbs + gs * qss +
+                ((int64_t)l * a.gamma * a.H_d + c * a.G_d + hh) * D + (lane >> 4) * 8;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const u32x4 v = *(const u32x4 *)(qp + kk * 32);
@@ -999,6 +1000,7 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
     const int N = k0.N_max;
     const int B = k0.B;
     const int64_t sbs = a.steps_bstride ? a.steps_bstride : a.gamma;   // steps_out rows per sequence
+    const int64_t sss = a.steps_sstride ? a.steps_sstride : 1;         // and between steps
     // Items are (b, chunk) over the chunks that hold positions below n_b
     // only, numbered sequence by sequence (B <= kDraftStatMaxB, checked by
     // the launchers), so a ragged batch spreads evenly over the groups; the
@@ -1017,7 +1019,7 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
         const int j0 = (pref[bb + 1] - pref[bb]) * kDraftAccChunk;
         for (int j = j0 + blockIdx.x * 256 + (int)threadIdx.x; j < N; j += gridDim.x * 256) {
             if constexpr (W > 0) {
-                for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)bb * sbs + q2) * N + j] = 0.f;
+                for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)bb * sbs + q2 * sss) * N + j] = 0.f;
             } else {
                 a.s_draft[(int64_t)bb * N + j] = 0.f;
             }
@@ -1033,7 +1035,8 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
         const int r = rb * 16 + (lane & 15);
         qok[rb] = r < a.rows;
         const int rr = qok[rb] ? r : 0;
-        qoff[rb] = ((rr / a.G_d) * a.H_d + (rr - (rr / a.G_d) * a.G_d)) * D + (lane >> 4) * 8;
+        const int qss = a.q_sstride ? (int)a.q_sstride : a.H_d * D;   // < 2^31 / 4 (checked on the host)
+        qoff[rb] = (rr / a.G_d) * qss + (rr - (rr / a.G_d) * a.G_d) * D + (lane >> 4) * 8;
     }
     // step of each of this lane's result rows (rows past the last are masked
     // by an infinite normaliser; their step is clamped)
@@ -1060,7 +1063,7 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
             const int j = jb + lane;
             if (j < N) {
                 if constexpr (W > 0) {
-                    for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)b * sbs + q2) * N + j] = 0.f;
+                    for (int q2 = 0; q2 < a.gamma; ++q2) a.steps_out[((int64_t)b * sbs + q2 * sss) * N + j] = 0.f;
                 } else {
                     a.s_draft[(int64_t)b * N + j] = 0.f;
                 }
@@ -1190,7 +1193,7 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
                 for (int q2 = 0; q2 < NS; ++q2) {
                     const float v = group4_sum(acc[st][q2]);
                     if (lane < 16 && j < N && q2 < a.gamma)
-                        a.steps_out[((int64_t)b * sbs + q2) * N + j] = v * a.steps_scale;
+                        a.steps_out[((int64_t)b * sbs + q2 * sss) * N + j] = v * a.steps_scale;
                 }
             } else {
                 const float v = group4_sum(acc[st][0]);
