@@ -987,11 +987,14 @@ __global__ __launch_bounds__(256, (RB >= 3 || (D == 128 && RB >= 2)) ? 1 : 2) vo
 // (one layer, the window queries as the "draft" rows, which are step-major
 // within a unit): instead of one sum over all rows, lane sums are kept per
 // step (step = row / G_d, at most W steps) and written, times steps_scale
-// (1 / H_q: the head mean), to steps_out [B][gamma][N_max].
+// (1 / H_q: the head mean), to steps_out [B][gamma][N_max].  SA (G_d a
+// multiple of 4): the four rows a lane holds per row block, rows
+// rb * 16 + (lane >> 4) * 4 + i, share one step, so their four terms are
+// summed before the one per-step select.
 constexpr int kDraftAccChunk = 256;
 
-template <int D, int RB, bool PAGED, int W = 0>
-__global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_mfma(DraftScoreArgs a) {
+template <int D, int RB, bool PAGED, int W = 0, bool SA = false>
+__global__ __launch_bounds__(256, ((D == 128 && RB >= 2) || (W > 0 && RB >= 4)) ? 1 : 2) void draft_acc_mfma(DraftScoreArgs a) {
     using M = DraftMfma<D, RB>;
     constexpr int KK = M::KK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1162,14 +1165,22 @@ __global__ __launch_bounds__(256, (D == 128 && RB >= 2) ? 1 : 2) void draft_acc_
 #pragma unroll
                     for (int kk = 0; kk < KK; ++kk)
                         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[rb][kk], k[st][kk], sc, 0, 0, 0);
+                    if constexpr (W > 0 && SA) {
+                        float e4 = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
-                        if constexpr (W > 0) {
+                        for (int i = 0; i < 4; ++i) e4 += __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
 #pragma unroll
-                            for (int q2 = 0; q2 < NS; ++q2) t[q2] += (rstep[rb][i] == q2) ? e : 0.f;
-                        } else {
-                            t[0] += e;
+                        for (int q2 = 0; q2 < NS; ++q2) t[q2] += (rstep[rb][0] == q2) ? e4 : 0.f;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = __builtin_amdgcn_exp2f(sc[i] * a.scale_log2 - ls[rb][i]);
+                            if constexpr (W > 0) {
+#pragma unroll
+                                for (int q2 = 0; q2 < NS; ++q2) t[q2] += (rstep[rb][i] == q2) ? e : 0.f;
+                            } else {
+                                t[0] += e;
+                            }
                         }
                     }
                 }
@@ -2187,8 +2198,14 @@ static hipError_t window_bf16_impl(const DraftScoreArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int acc_items = k0.B * ((k0.N_max + kDraftAccChunk - 1) / kDraftAccChunk);
     const dim3 grid(acc_items < kScoreGroups ? acc_items : kScoreGroups);
-    if (k0.page_size != 0) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true, 4>), grid, dim3(256), 0, s, b);
-    else hipLaunchKernelGGL((draft_acc_mfma<D, RB, false, 4>), grid, dim3(256), 0, s, b);
+    const bool sa = a.G_d % 4 == 0;
+    if (k0.page_size != 0) {
+        if (sa) hipLaunchKernelGGL((draft_acc_mfma<D, RB, true, 4, true>), grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL((draft_acc_mfma<D, RB, true, 4, false>), grid, dim3(256), 0, s, b);
+    } else {
+        if (sa) hipLaunchKernelGGL((draft_acc_mfma<D, RB, false, 4, true>), grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL((draft_acc_mfma<D, RB, false, 4, false>), grid, dim3(256), 0, s, b);
+    }
     return hipGetLastError();
 }
 
