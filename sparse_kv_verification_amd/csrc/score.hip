@@ -1368,14 +1368,16 @@ __device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int l
 // next item's first DMA; items alternate between two named Q sets, so no
 // register copy waits for a pending load.  The cross-wave combine
 // alternates between two LDS buffers, so one barrier per item suffices.
-template <int RB, bool PAGED, bool HALF>
+template <int RB, bool PAGED, bool HALF, int CHUNK = kDraftStatChunk>
 __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
+    // a paged wave span's page ids are one per lane: at most 64 pages
+    static_assert(!PAGED || CHUNK / 4 / 16 <= 64, "paged items of at most 4096 positions");
     constexpr int KK = 2;
     using GM = StreamGeom<RB, HALF>;
     constexpr int POS = GM::POS;
     constexpr int NH = GM::NH;                 // heads per item (HALF: one, item.h)
     constexpr int NHI = HALF ? 2 : 1;          // items per (b, layer, chunk)
-    constexpr int PER_WAVE = kDraftStatChunk / 4;
+    constexpr int PER_WAVE = CHUNK / 4;
     constexpr int NSTAGE = PER_WAVE / POS;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][GM::STAGE];
     __shared__ float red[2][4][NH][RB * 16][2];
@@ -1388,7 +1390,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     // n_b only, numbered sequence by sequence (B <= kDraftStatMaxB, checked
     // by the launcher), so a ragged batch spreads evenly over the groups.
     for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
-        pref[bb + 1] = (sl_len(a.kv[0], bb) + kDraftStatChunk - 1) / kDraftStatChunk;
+        pref[bb + 1] = (sl_len(a.kv[0], bb) + CHUNK - 1) / CHUNK;
     __syncthreads();
     if (threadIdx.x == 0) {
         pref[0] = 0;
@@ -1418,7 +1420,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         x.l = u / NHI;
         x.h = u - x.l * NHI;
         x.nb = __builtin_amdgcn_readfirstlane(sl_len(a.kv[x.l], x.b));
-        x.jw = x.c * kDraftStatChunk + __builtin_amdgcn_readfirstlane(wave) * PER_WAVE;
+        x.jw = x.c * CHUNK + __builtin_amdgcn_readfirstlane(wave) * PER_WAVE;
         const int left = x.nb - x.jw;
         x.nst = left <= 0 ? 0 : min(NSTAGE, (left + POS - 1) / POS);
         x.seq = PAGED ? a.kv[x.l].k : a.kv[x.l].k + (int64_t)x.b * a.kv[x.l].N_max * 256;
@@ -2117,20 +2119,33 @@ template <int RB, bool PAGED, bool HALF>
 static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const KvView &k0 = a.kv[0];
     DraftScoreArgs b = a;
-    b.nchunk = (k0.N_max + kDraftStatChunk - 1) / kDraftStatChunk;
     constexpr int NHI = HALF ? 2 : 1;
-    const int stat_items = k0.B * a.L_d * NHI * b.nchunk;
     constexpr int GROUPS = StreamGeom<RB, HALF>::GROUPS;
+    // Statistics items of twice the positions halve the per-item combine
+    // when there are still at least two per persistent group (contiguous
+    // caches: a paged wave span holds one page id per lane).  Measured at
+    // c4: 504 -> 490 us; at c2 (B = 4, 16k) the larger items underfill the
+    // chip, so the rule keeps 4096 there.
+    constexpr int CH2 = 2 * kDraftStatChunk;
+    const bool big = !PAGED && (long)k0.B * a.L_d * NHI * ((k0.N_max + CH2 - 1) / CH2) >= 2L * GROUPS;
+    const int chunk = big ? CH2 : kDraftStatChunk;
+    b.nchunk = (k0.N_max + chunk - 1) / chunk;
+    const int stat_items = k0.B * a.L_d * NHI * b.nchunk;
     hipError_t e;
     if (a.lse_in) {
         if ((e = import_draft_lse(a, k0.B, s)) != hipSuccess) return e;
     } else {
-        hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), dim3(stat_items < GROUPS ? stat_items : GROUPS),
-                           dim3(256), 0, s, b);
+        const dim3 grid(stat_items < GROUPS ? stat_items : GROUPS);
+        if constexpr (!PAGED) {
+            if (big) hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF, CH2>), grid, dim3(256), 0, s, b);
+            else hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), grid, dim3(256), 0, s, b);
+        } else {
+            hipLaunchKernelGGL((draft_stats_stream<RB, PAGED, HALF>), grid, dim3(256), 0, s, b);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int nrows = k0.B * a.L_d * 2 * a.rows;
         hipLaunchKernelGGL(rows_lse, dim3((nrows + 3) / 4), dim3(256), 0, s, b.stat, b.lse, nrows, b.nchunk,
-                           k0.seq_lens, a.L_d * 2 * a.rows, kDraftStatChunk, k0.N_max);
+                           k0.seq_lens, a.L_d * 2 * a.rows, chunk, k0.N_max);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.lse_out) return export_draft_lse(a, k0.B, s);
