@@ -1215,8 +1215,9 @@ __global__ __launch_bounds__(256, ((D == 128 && RB >= 2) || (W > 0 && RB >= 4)) 
 }
 
 // ---------------------------------------------------------------------------
-// Draft side, streaming form for contiguous bfloat16 drafts with two 64-wide
-// KV heads, where a draft layer's position row is 256 bytes ([2][64] bf16).
+// Draft side, streaming form for bfloat16 drafts (contiguous or paged) with
+// two 64-wide KV heads, where a draft layer's position row is 256 bytes
+// ([2][64] bf16).
 // Every wave streams its own positions through a private two-stage LDS ring:
 // a stage is 32 positions of one layer (8 KiB) fetched with the nontemporal
 // global->LDS DMA (each row is read once per pass), while the wave computes
@@ -1443,14 +1444,11 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[NH][RB][KK],
                     bf16x8 (&qn)[NH][RB][KK], const int &pg, int &pgn) {
         // Per lane and row: zrun = sum of exp2(v - mrun) over the lane's
-        // positions so far.  Up to two row blocks (LAZY), mrun is a reference
-        // at least every such v that moves only when a logit passes it, and
-        // then to that logit + 16: most pairs of logits cost two exp2 and no
-        // rescale, terms stay <= 1, and the reference is finite (-FLT_MAX
-        // until the row's first valid position).  With more row blocks the
-        // registers do not leave room for that form, and mrun is the running
-        // maximum (three exp2 per pair).
-        constexpr bool LAZY = true;
+        // positions so far, where mrun is a reference at least every such v
+        // that moves only when a logit passes it, and then to that logit + 16:
+        // most pairs of logits cost two exp2 and no rescale, terms stay <= 1,
+        // and the reference is finite (-FLT_MAX for a lane with no valid
+        // position in the item).
         float mrun[NH][RB][4], zrun[NH][RB][4];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -1458,7 +1456,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    mrun[h][rb][i] = LAZY ? -kFltMax : kNegInf;
+                    mrun[h][rb][i] = -kFltMax;
                     zrun[h][rb][i] = 0.f;
                 }
         auto next_dma = [&](int s) {   // the DMA after stage s
@@ -1491,24 +1489,6 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     }
                 }
                 const float sl = a.scale_log2;
-                if constexpr (!LAZY) {
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float v0 = sc[0][rb][i] * sl, v1 = sc[1][rb][i] * sl;
-                            if (!full) {
-                                if (j0 + pr * 32 + (lane & 15) >= cur.nb) v0 = kNegInf;
-                                if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) v1 = kNegInf;
-                            }
-                            const float mx = fmaxf(mrun[h][rb][i], fmaxf(v0, v1));
-                            const float mu = (mx == kNegInf) ? 0.f : mx;
-                            zrun[h][rb][i] = zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu) +
-                                             __builtin_amdgcn_exp2f(v0 - mu) + __builtin_amdgcn_exp2f(v1 - mu);
-                            mrun[h][rb][i] = mx;
-                        }
-                    continue;
-                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -1592,7 +1572,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     // a row with no valid position has a zero sum (its
-                    // reference -inf, or -FLT_MAX in the lazy form): (-inf, 0)
+                    // reference left at -FLT_MAX): reported as (-inf, 0)
                     const float mx = lane16_max(mrun[h][rb][i]);
                     const float mu = (mx == kNegInf) ? 0.f : mx;
                     const float z = lane16_sum(zrun[h][rb][i] * __builtin_amdgcn_exp2f(mrun[h][rb][i] - mu));
