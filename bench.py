@@ -71,7 +71,10 @@ def parse():
                    help="skip the estimator-overhead curve (dense, naive, Quest-16, Dustin-T/D/H over context length)")
     p.add_argument("--pmc-probe", action="store_true",
                    help="for counter collection: one warm step, a 1 GiB float32 copy (the calibration "
-                        "kernel of known size), then one more step; prints no JSON")
+                        "kernel of known size), then one more step and one window attention of w = 4 and of "
+                        "w = 8 on layer 0; prints no JSON")
+    p.add_argument("--no-evaluator", action="store_true",
+                   help="skip the window-attention timings of the evaluator (w = 4 and w = 8 on the c4 cache)")
     return p.parse_args()
 
 
@@ -399,6 +402,11 @@ def main():
         log("pmc probe: one step")
         step()
         torch.cuda.synchronize()
+        log("pmc probe: window attention, w = 4 and w = 8")
+        q8 = torch.cat([x.q, x.q.flip(1)], dim=1).contiguous()
+        dk.dustin_window_attn(x.q, kvs[0])
+        dk.dustin_window_attn(q8, kvs[0])
+        torch.cuda.synchronize()
         log("pmc probe done")
         return
     bytes_ = algorithmic_bytes(sh, x, k, cnt, x.sub_heads)
@@ -569,6 +577,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(sh, x, k, m, n_sink, n_window)
+    if not args.no_evaluator:
+        res["evaluator"] = evaluator(args, sh, x, kvs[0], cap, timed)
     if not args.no_sweep:
         res["policy_sweep"] = policy_sweep(args, sh, x, kvs[0], s_d, s_t, n_sink, n_window, timed)
     if not args.no_ksweep:
@@ -717,6 +727,29 @@ def ceilings(args, sh, x, Ks, Vs, idx, cnt, cap, timed):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     log("ceilings: " + ", ".join(f"{k} {v}" for k, v in out.items()))
+    return out
+
+
+def evaluator(args, sh, x, kv, cap, timed):
+    """Window attention A (Eq. 1) of one layer, as the evaluator, the policy
+    sweep and the configuration search call it: w = 4 (the window's queries)
+    and w = 8 (the window and its reverse, two slices of four steps), graph
+    replayed.  Two passes read K (row normalisers, then probabilities), so
+    the rate is given on twice the K bytes."""
+    import torch
+    import sparse_kv_verification_amd as dk
+    q8 = torch.cat([x.q, x.q.flip(1)], dim=1).contiguous()
+    kbytes = int(x.seq_lens.sum()) * sh.Hkv * sh.d * x.K.element_size()
+    out = {}
+    for w, q in ((sh.w, x.q), (2 * sh.w, q8)):
+        A = torch.empty((sh.B, w, kv.desc.N_max), dtype=torch.float32, device=x.q.device)
+        ws = dk.Workspace()
+        fn = lambda: dk.dustin_window_attn(q, kv, A=A, ws=ws)
+        us = graph_time(args, fn, cap, timed, max(3, args.steps // 2))
+        out[f"w{w}"] = {"us": round(us, 1), "k_reads": 2 * ((w + 3) // 4),
+                        "GBps_on_k_reads": round(2 * ((w + 3) // 4) * kbytes / us / 1e3, 1)}
+    log("evaluator window attention: " + ", ".join(f"{k_} {v['us']:.0f} us ({v['GBps_on_k_reads']:.0f} GB/s over "
+                                                   f"{v['k_reads']} K reads)" for k_, v in out.items()))
     return out
 
 
