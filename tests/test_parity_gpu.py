@@ -467,6 +467,7 @@ def test_scores_treat_absent_pages_as_zero_keys(w):
     ("w5-g16", dict(base="c4", B=2, n=2200, Hq=64, Hkv=4, w=5, L_d=1)),      # 64 rows per slice of 4
     ("w3-g32-d64", dict(base="c4", B=2, n=1900, Hq=64, Hkv=2, d=64, w=3, L_d=1)),   # slices of 2 steps
     ("w16-g7", dict(base="c2", B=1, n=2000, w=16, L_d=1)),                   # four slices
+    ("d32-bf16", dict(base="c4", B=2, n=2000, Hq=8, Hkv=2, d=32, L_d=1)),    # head_dim 32
     ("tiny-f32", dict(base="c1")),                                           # float32: the dense-pass form
 ])
 def test_window_attention_and_arr(name, over):
