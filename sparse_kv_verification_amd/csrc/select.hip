@@ -267,28 +267,37 @@ __device__ __forceinline__ uint32_t row_bits(int w, int r0, int r1) {
 // work-group (count per (row, wave), block prefix, then the ballot offset),
 // calling f(w, bit, rank) for each set bit.  Rows from `nrows` on must hold
 // no set bit.  Every lane must call it.
+// The 16 waves of the work-group share one CU, so the per-row loops are kept
+// free of branches and LDS round trips: a word's 32 row counts are gathered
+// into lanes 0..31 (a select per row) and stored with one instruction, and after
+// the scan the 32 prefixes come back with one LDS read and readlane.
 template <int MW, class F>
 __device__ __forceinline__ int rank_rows(const uint32_t (&m)[MW], int nrows, TopkIlShared &sh, F &&f) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    (void)nrows;   // rows from nrows on hold no set bit: they count zero
 #pragma unroll
-    for (int w = 0; w < MW; ++w)
-#pragma unroll 1
+    for (int w = 0; w < MW; ++w) {
+        int cnt = 0;   // lane r < 32: set bits of row w * 32 + r in this wave
+#pragma unroll
         for (int bit = 0; bit < 32; ++bit) {
-            const int row = w * 32 + bit;
-            const unsigned long long bal = (row < nrows) ? __ballot((m[w] >> bit) & 1u) : 0ull;
-            if (lane == 0) sh.rowcnt[row * TKW + wave] = __popcll(bal);
+            // every lane takes part in the ballot; only lane `bit` keeps its count
+            const int pc = (int)__popcll(__ballot((m[w] >> bit) & 1u));
+            cnt = (lane == bit) ? pc : cnt;
         }
+        if (lane < 32) sh.rowcnt[(w * 32 + lane) * TKW + wave] = cnt;
+    }
     __syncthreads();
     const int total = block_scan_array(sh.rowcnt, 32 * MW * TKW, sh.wave_tot);
     const unsigned long long lt = (1ull << lane) - 1ull;
 #pragma unroll
     for (int w = 0; w < MW; ++w) {
-        if (w * 32 >= nrows) break;
-#pragma unroll 1
+        if (__ballot(m[w] != 0u) == 0ull) continue;   // no lane of the wave has a set bit in this word
+        const int pre = sh.rowcnt[(w * 32 + (lane & 31)) * TKW + wave];   // lane r: prefix of row w * 32 + r
+#pragma unroll
         for (int bit = 0; bit < 32; ++bit) {
             const bool mine = (m[w] >> bit) & 1u;
             const unsigned long long bal = __ballot(mine);
-            if (mine) f(w, bit, sh.rowcnt[(w * 32 + bit) * TKW + wave] + __popcll(bal & lt));
+            if (mine) f(w, bit, __builtin_amdgcn_readlane(pre, bit) + __popcll(bal & lt));
         }
     }
     __syncthreads();   // rowcnt may be reused
