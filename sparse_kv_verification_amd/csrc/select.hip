@@ -363,19 +363,15 @@ __device__ void select_top_il(const float *sc, int n, const uint32_t (&cm)[MW], 
     }
     int remaining = K;    // keys still to take from the window
     bool exact = false;   // every key of the window is taken
-    unsigned *hflat = &sh.hist[0][0];
     unsigned *hc = sh.hist[wave % kIlHistCopies];
+    // The histogram is zero on entry (cleared at the kernel's start, and
+    // every pass's scan zeroes the counters it reads), so a pass needs no
+    // clear of its own; the barrier after the scan orders those zeroes
+    // before the next pass's atomics.
     for (int pass = 0; pass < 4; ++pass) {   // the window shrinks to one value within three passes
         const uint32_t r = hi - lo;
         const int bl = r ? 32 - __clz((int)r) : 0;
         const int s = max(0, bl - 11);
-        for (int i = tid; i < kIlHistCopies * 2048; i += TKT) hflat[i] = 0;
-        if (tid == 0) {
-            sh.digit = 0;
-            sh.above = 0;
-            sh.inbin = 0;
-        }
-        __syncthreads();
         each_word([&](int w, const uint32_t (&kw)[32]) {
 #pragma unroll
             for (int bit = 0; bit < 32; ++bit) {
@@ -393,6 +389,15 @@ __device__ void select_top_il(const float *sc, int n, const uint32_t (&cm)[MW], 
                 const uint2 h = *(const uint2 *)&sh.hist[c][b0];
                 c0 += (int)h.x;
                 c1 += (int)h.y;
+            }
+#pragma unroll
+            for (int c = 0; c < kIlHistCopies; ++c) *(uint2 *)&sh.hist[c][b0] = uint2{0u, 0u};
+            // every lane read the previous pass's result before the
+            // histogram barrier above, so it can be reset here
+            if (tid == 0) {
+                sh.digit = 0;
+                sh.above = 0;
+                sh.inbin = 0;
             }
             const int local = c0 + c1;
             int incl = local;   // inclusive suffix sum over lanes >= lane
@@ -419,7 +424,6 @@ __device__ void select_top_il(const float *sc, int n, const uint32_t (&cm)[MW], 
         const int inbin = sh.inbin;
         lo += (uint32_t)sh.digit << s;
         hi = min(hi, lo + ((1u << s) - 1u));
-        __syncthreads();   // every lane has read digit / above / inbin before the next pass resets them
         if (remaining == inbin) {
             exact = true;
             break;
@@ -462,6 +466,14 @@ template <int MW>
 __global__ __launch_bounds__(TKT) void topk_il_kernel(TopkArgs a) {
     __shared__ TopkIlShared sh;
     const int b = blockIdx.x, tid = threadIdx.x;
+    // the radix passes expect a zero histogram (each pass leaves it zero);
+    // the barrier inside the first selection orders this before any atomic
+    for (int i = tid; i < kIlHistCopies * 2048; i += TKT) (&sh.hist[0][0])[i] = 0u;
+    if (tid == 0) {
+        sh.digit = 0;
+        sh.above = 0;
+        sh.inbin = 0;
+    }
     const int n = min(max(a.seq_lens[a.len_mod ? b % a.len_mod : b], 0), a.N_max);
     const int se = min(a.n_sink, n);
     const int wb = max(0, n - a.n_window);
