@@ -168,6 +168,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(lds_void_t *)p;
 }
 
+// 32-bit LDS reads that have completed when they return.  Inline assembly:
+// the compiler cannot always tell a C++ read of LDS apart from the target of
+// a pending global->LDS DMA, and then puts a wait for every outstanding
+// vector-memory request in front of it, which empties a streaming ring.
+__device__ __forceinline__ int lds_read_i32(const void *p) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+__device__ __forceinline__ float lds_read_f32(const void *p) {
+    float v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+
 // Transposed LDS reads (ds_read_b64_tr_b16) of the V operand of the PV
 // product, issued as one block that also waits for their completion.  Within
 // each 16-lane group, lane i receives element (i mod 4) of the 8-byte rows

@@ -1218,34 +1218,55 @@ __global__ __launch_bounds__(256, ((D == 128 && RB >= 2) || (W > 0 && RB >= 4)) 
 // Draft side, streaming form for bfloat16 drafts (contiguous or paged) with
 // two 64-wide KV heads, where a draft layer's position row is 256 bytes
 // ([2][64] bf16).
-// Every wave streams its own positions through a private two-stage LDS ring:
-// a stage is 32 positions of one layer (8 KiB) fetched with the nontemporal
-// global->LDS DMA (each row is read once per pass), while the wave computes
-// on the other stage.  The sixteen 16-byte chunks of a position row are
-// stored XOR-swizzled by the position's low four bits, so a K-operand read
-// (16 positions, one chunk each) touches 16 distinct bank groups.  Register
-// loads on the way (Q fragments, row normalisers, lengths) complete in order
-// with the DMA, and every stage starts with a full vmcnt wait, so a stage
-// never reads LDS before its own bytes have landed.
-// Up to two row blocks per KV head: 32-position (8 KiB) stages of full
-// position rows (both KV heads) and two 4-wave groups per CU.
+// Every wave streams its own positions through a private 16 KiB LDS ring of
+// stages of one layer, fetched with the nontemporal global->LDS DMA (each
+// row is read once per pass), while it computes on an earlier stage.  The
+// sixteen 16-byte chunks of a position row are stored XOR-swizzled by the
+// position's low four bits, so a K-operand read (16 positions, one chunk
+// each) touches 16 distinct bank groups.  Register loads on the way (Q
+// fragments, row normalisers, lengths) complete in order with the DMA, and
+// every stage starts with a vmcnt wait that leaves only later stages in
+// flight, so a stage never reads LDS before its own bytes have landed.
+// Up to two row blocks per KV head: two 8 KiB stages of 32 full position
+// rows (both KV heads, one stage in flight while the other is computed) and
+// two 4-wave groups per CU.
 //
-// Three or four row blocks stream one KV head per item (HALF): a stage holds
-// the 128-byte head halves of 64 positions, so it is still 8 KiB, the
-// operands of one head fit two groups per CU, and the two heads'
-// accumulation results are partial sums added by draft_part_sum.  (A
-// full-row form at one group per CU, with 64-position stages to keep the
-// bytes in flight, had run no faster than the register-staged kernels,
-// which now serve only the geometries neither streaming form covers.)
-template <int RB, bool HALF = false>
+// Three or four row blocks stream one KV head per item (HALF): stages hold
+// 128-byte head halves, the operands of one head fit two groups per CU, and
+// the two heads' accumulation results are partial sums added by
+// draft_part_sum.  The statistics pass over half rows (DEEP) splits its ring
+// into four 4 KiB stages of 32 positions, three in flight while one is
+// computed; the accumulation pass keeps two 8 KiB stages of 64 positions,
+// which measured faster there.  (A full-row form at one group per CU, with
+// 64-position stages to keep the bytes in flight, had run no faster than the
+// register-staged kernels, which now serve only the geometries neither
+// streaming form covers.)
+template <int RB, bool HALF = false, bool DEEP = false>
 struct StreamGeom {
     static_assert(HALF || RB <= 2, "full-row streaming: at most two row blocks");
+    static_assert(!DEEP || HALF, "four-stage rings: half rows only");
     static constexpr int RBY = HALF ? 128 : 256;      // stage bytes per position
-    static constexpr int POS = 8192 / RBY;            // positions per stage
-    static constexpr int STAGE = 8192;                // bytes per stage
+    static constexpr int STAGE = DEEP ? 4096 : 8192;  // bytes per stage
+    static constexpr int NSLOT = 16384 / STAGE;       // stages in a wave's ring
+    static constexpr int POS = STAGE / RBY;           // positions per stage
+    static constexpr int NI = STAGE / 1024;           // DMA instructions per stage
     static constexpr int NH = HALF ? 1 : 2;           // heads per item
     static constexpr int GROUPS = 512;                // persistent work-groups
 };
+
+// Wait until the stage about to be computed has landed, while the `ahead`
+// stages issued after it (NI instructions each; ahead < A) stay in flight.
+// Vector-memory loads complete in issue order, and any other request issued
+// after that stage only makes the wait longer.
+template <int A, int NI>
+__device__ __forceinline__ void stream_wait(int ahead) {
+    if constexpr (A <= 1) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= A - 1) wait_vmcnt<(A - 1) * NI>();
+        else stream_wait<A - 1, NI>(ahead);
+    }
+}
 
 // 16-byte chunk swizzle of stage row rho: full rows (16 chunks) by the low
 // four bits; half rows (8 chunks, two rows per 256-byte bank span) by bits
@@ -1257,7 +1278,7 @@ __device__ __forceinline__ int stream_swz(int rho) {
 constexpr int kStreamGroups = 512;
 
 // DMA of the POS positions j0 .. j0 + POS - 1 of one layer into `stage` (32
-// full rows, or 64 head halves when HALF); `seq` is the layer's k pointer
+// full rows, or 32 or 64 head halves when HALF); `seq` is the layer's k pointer
 // advanced to the sequence.  Positions past the cache end read the last row
 // (the caller masks them).
 template <int POS, bool HALF>
@@ -1265,7 +1286,7 @@ __device__ __forceinline__ void stream_issue(const char *seq, int j0, int jlast,
     constexpr int CPR = (HALF ? 128 : 256) / 16;   // chunks per stage row
     constexpr int PPI = 64 / CPR;                  // positions per instruction
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < POS / PPI; ++i) {
         const int rho = i * PPI + lane / CPR;
         const int chunk = (lane % CPR) ^ stream_swz<HALF>(rho);
         const uint32_t j = (uint32_t)min(j0 + rho, jlast);
@@ -1290,7 +1311,7 @@ __device__ __forceinline__ void stream_issue_pg(const char *pool, int pgv, int s
 #pragma unroll
     for (int k = 0; k < NP; ++k) pgs[k] = __builtin_amdgcn_readlane(pgv, NP * s + k);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < POS / PPI; ++i) {
         const int rho = i * PPI + lane / CPR;   // on page rho / 16 of the stage
         const int chunk = (lane % CPR) ^ stream_swz<HALF>(rho);
         const int pg = pgs[(i * PPI) >> 4];
@@ -1332,6 +1353,11 @@ __device__ __forceinline__ void stream_qoff(const DraftScoreArgs &a, int lane, u
 template <int RB, int NH>
 __device__ __forceinline__ void stream_load_q(const DraftScoreArgs &a, int b, int l, int h0, const uint32_t (&qo)[RB],
                                               bf16x8 (&q)[NH][RB][2]) {
+    // (b, l, h0) are wave-uniform; saying so keeps the buffer resource in
+    // scalar registers (otherwise each load becomes a per-lane loop)
+    b = __builtin_amdgcn_readfirstlane(b);
+    l = __builtin_amdgcn_readfirstlane(l);
+    h0 = __builtin_amdgcn_readfirstlane(h0);
     const uint32_t blk = (uint32_t)(a.gamma * a.H_d * 128);
     const __amdgpu_buffer_rsrc_t r = stream_rsrc((const char *)a.q_draft + ((int64_t)b * a.L_d + l) * blk, blk);
 #pragma unroll
@@ -1374,15 +1400,18 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     // a paged wave span's page ids are one per lane: at most 64 pages
     static_assert(!PAGED || CHUNK / 4 / 16 <= 64, "paged items of at most 4096 positions");
     constexpr int KK = 2;
-    using GM = StreamGeom<RB, HALF>;
+    using GM = StreamGeom<RB, HALF, HALF>;
     constexpr int POS = GM::POS;
     constexpr int NH = GM::NH;                 // heads per item (HALF: one, item.h)
     constexpr int NHI = HALF ? 2 : 1;          // items per (b, layer, chunk)
     constexpr int PER_WAVE = CHUNK / 4;
     constexpr int NSTAGE = PER_WAVE / POS;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][GM::STAGE];
+    constexpr int NSL = GM::NSLOT;
+    constexpr int AHEAD = NSL - 1;             // stages in flight beyond the one computed
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][NSL][GM::STAGE];
     __shared__ float red[2][4][NH][RB * 16][2];
     __shared__ int pref[kDraftStatMaxB + 1];   // chunks below n_b of sequences before b
+    __shared__ int slen[kDraftStatMaxB];       // n_b (every draft layer has layer 0's lengths)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int U = a.L_d * 2;
     const int nch = a.nchunk;
@@ -1390,8 +1419,11 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     // Items are (b, layer, chunk) over the chunks that hold positions below
     // n_b only, numbered sequence by sequence (B <= kDraftStatMaxB, checked
     // by the launcher), so a ragged batch spreads evenly over the groups.
-    for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
-        pref[bb + 1] = (sl_len(a.kv[0], bb) + CHUNK - 1) / CHUNK;
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x) {
+        const int n = sl_len(a.kv[0], bb);
+        slen[bb] = n;
+        pref[bb + 1] = (n + CHUNK - 1) / CHUNK;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         pref[0] = 0;
@@ -1399,7 +1431,7 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     }
     __syncthreads();
     const int per = a.L_d * NHI;              // items per chunk of a sequence
-    const int items = per * pref[B];
+    const int items = per * __builtin_amdgcn_readfirstlane(pref[B]);
     struct Item { int b, l, h, c, nb, jw, nst; const char *seq; int jlast; };
     auto decode = [&](int it) {
         Item x;
@@ -1407,20 +1439,23 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         int lo = 0, hi = B - 1;                // the b with pref[b] <= cu < pref[b + 1]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (pref[mid] <= cu) lo = mid;
+            if (lds_read_i32(&pref[mid]) <= cu) lo = mid;
             else hi = mid - 1;
         }
         // every field is the same across the wave: readfirstlane makes that
         // visible to the compiler, so tests on them are scalar branches
         // (the LDS reads above otherwise make them look per-lane)
         x.b = __builtin_amdgcn_readfirstlane(lo);
-        const int nbc = __builtin_amdgcn_readfirstlane(pref[lo + 1] - pref[lo]);
-        const int r = it - per * __builtin_amdgcn_readfirstlane(pref[lo]);   // within the sequence: (layer, head)-major
+        const int p0 = __builtin_amdgcn_readfirstlane(lds_read_i32(&pref[lo]));
+        const int nbc = __builtin_amdgcn_readfirstlane(lds_read_i32(&pref[lo + 1])) - p0;
+        const int r = it - per * p0;   // within the sequence: (layer, head)-major
         const int u = r / nbc;
         x.c = r - u * nbc;
         x.l = u / NHI;
         x.h = u - x.l * NHI;
-        x.nb = __builtin_amdgcn_readfirstlane(sl_len(a.kv[x.l], x.b));
+        // from LDS: a global load here would be waited for together with
+        // every stage already in flight
+        x.nb = __builtin_amdgcn_readfirstlane(lds_read_i32(&slen[x.b]));
         x.jw = x.c * CHUNK + __builtin_amdgcn_readfirstlane(wave) * PER_WAVE;
         const int left = x.nb - x.jw;
         x.nst = left <= 0 ? 0 : min(NSTAGE, (left + POS - 1) / POS);
@@ -1430,19 +1465,22 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     };
     uint32_t qo[RB];
     stream_qoff<RB>(a, lane, qo);
-    int slot = 0, par = 0;
+    int slot = 0, islot = 0, par = 0;   // ring slots of the next stage to compute / to issue
     // paged caches: the page ids of an item's wave span (64 pages), one per lane
     auto load_pg = [&](const Item &x) -> int {
         return PAGED ? stream_load_pg(a.kv[x.l], x.b, x.jw, PER_WAVE / 16, lane) : 0;
     };
-    auto issue = [&](const Item &x, int pgv, int s, uint8_t *stage) {
+    auto issue = [&](const Item &x, int pgv, int s, uint8_t *stage) __attribute__((always_inline)) {
         if constexpr (PAGED) stream_issue_pg<POS, HALF>(x.seq, pgv, s, a.kv[x.l].num_pages, x.h * 128, lane, stage);
         else stream_issue<POS, HALF>(x.seq, x.jw + s * POS, x.jlast, x.h * 128, lane, stage);
     };
-    // One item on Q set q (page ids pg); requests the next item's Q into qn
-    // (page ids into pgn) and, when the next item has stages, its first DMA.
+    // One item on Q set q (page ids pg), `ci` of whose stages were issued
+    // before it began; requests the next item's Q into qn (page ids into
+    // pgn) and keeps AHEAD stages in flight, running on into the next item's
+    // first stages.  Returns how many of those it issued.
     auto item = [&](const Item &cur, const Item &nxt, bool has_next, const bf16x8 (&q)[NH][RB][KK],
-                    bf16x8 (&qn)[NH][RB][KK], const int &pg, int &pgn) {
+                    bf16x8 (&qn)[NH][RB][KK], const int &pg, int &pgn, int ci) -> int {
+        ci = __builtin_amdgcn_readfirstlane(ci);
         // Per lane and row: zrun = sum of exp2(v - mrun) over the lane's
         // positions so far, where mrun is a reference at least every such v
         // that moves only when a logit passes it, and then to that logit + 16:
@@ -1459,9 +1497,21 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     mrun[h][rb][i] = -kFltMax;
                     zrun[h][rb][i] = 0.f;
                 }
-        auto next_dma = [&](int s) {   // the DMA after stage s
-            if (s + 1 < cur.nst) issue(cur, pg, s + 1, ring[wave][slot ^ 1]);
-            else if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot ^ 1]);
+        const int nn = has_next ? nxt.nst : 0;
+        int ni = 0;   // stages of the next item issued
+        // top up to AHEAD stages in flight after stage s (s = -1: none computed yet)
+        auto top_up = [&](int s) __attribute__((always_inline)) {
+            // (the counters move by arithmetic: incrementing one of two
+            // through a selected reference had put both in scratch memory)
+            while ((ci - 1 - s) + ni < AHEAD) {
+                const bool own = ci < cur.nst;
+                if (!own && ni >= nn) break;
+                if (own) issue(cur, pg, ci, ring[wave][islot]);
+                else issue(nxt, pgn, ni, ring[wave][islot]);
+                ci += own ? 1 : 0;
+                ni += own ? 0 : 1;
+                islot = (islot + 1) & (NSL - 1);
+            }
         };
         // FIRST: the item's first stage (its first pair sets the references);
         // a compile-time flag, so the other stages carry no trace of that path
@@ -1489,14 +1539,19 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     }
                 }
                 const float sl = a.scale_log2;
+                // one wave-uniform test per pair (written inside the element
+                // loops it became sixteen branches on every stage)
+                if (!full) {
+                    const bool out0 = j0 + pr * 32 + (lane & 15) >= cur.nb;
+                    const bool out1 = j0 + pr * 32 + 16 + (lane & 15) >= cur.nb;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!full) {
-                            if (j0 + pr * 32 + (lane & 15) >= cur.nb) sc[0][rb][i] = kNegInf;
-                            if (j0 + pr * 32 + 16 + (lane & 15) >= cur.nb) sc[1][rb][i] = kNegInf;
+                        for (int i = 0; i < 4; ++i) {
+                            sc[0][rb][i] = out0 ? kNegInf : sc[0][rb][i];
+                            sc[1][rb][i] = out1 ? kNegInf : sc[1][rb][i];
                         }
+                }
                 if (FIRST && pr == 0) {
                     // The item's first pair sets each row's reference from
                     // its own logits.  A lane whose first pair is masked has
@@ -1546,22 +1601,63 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
                     for (int i = 0; i < 4; ++i)
                         zrun[h][rb][i] += __builtin_amdgcn_exp2f(sc[0][rb][i]) + __builtin_amdgcn_exp2f(sc[1][rb][i]);
             }
-            slot ^= 1;
+            slot = (slot + 1) & (NSL - 1);
         };
+        // The next item's page ids are requested before its Q fragments, so
+        // the waits that follow cover them.  Steady case (a full ring on
+        // entry and at least AHEAD + 2 stages): stages 0 and 1 each issue one
+        // of this item's stages unconditionally, so at least 2 * NI requests
+        // follow those loads before the counted waits of the last AHEAD
+        // stages, which issue the next item's first stages and need its page
+        // ids; the compiler can then see the loads complete without draining
+        // the ring.  Other items settle the loads with one full wait.
+        // (the loads sit on one path: loads in two branches became a
+        // select of the two results, which waits for them)
+        if (cur.nst > 0) stream_wait<AHEAD, GM::NI>(ci - 1);
+        pgn = load_pg(nxt);
+        stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
         if (cur.nst == 0) {
-            stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
-            pgn = load_pg(nxt);
-            if (has_next && nxt.nst > 0) issue(nxt, pgn, 0, ring[wave][slot]);
-        } else {
             wait_vmcnt<0>();
-            stream_load_q<RB, NH>(a, nxt.b, nxt.l, nxt.h, qo, qn);
-            pgn = load_pg(nxt);
-            next_dma(0);
-            stage(0, std::true_type{});
-            for (int s = 1; s < cur.nst; ++s) {
+            top_up(-1);
+        } else {
+            const bool steady = ci == AHEAD && cur.nst >= AHEAD + 2;
+            if (steady) {
+                issue(cur, pg, ci++, ring[wave][islot]);
+                islot = (islot + 1) & (NSL - 1);
+                stage(0, std::true_type{});
+                // at least one pass (cur.nst >= AHEAD + 2): written so, the
+                // compiler sees two stages issued after the loads above on
+                // every path and needs no wait of its own for them
+                int s = 1;
+                do {
+                    wait_vmcnt<(AHEAD - 1) * GM::NI>();
+                    issue(cur, pg, ci++, ring[wave][islot]);
+                    islot = (islot + 1) & (NSL - 1);
+                    stage(s, std::false_type{});
+                } while (++s < cur.nst - AHEAD);
+                // The last AHEAD stages each issue one of the next item's
+                // first stages.  Unrolled: a loop here that reads the page ids
+                // loaded outside it and issues DMA whose results it never
+                // reads made the compiler drain every request before it.
+#pragma unroll
+                for (int t = 0; t < AHEAD; ++t) {
+                    stream_wait<AHEAD, GM::NI>(AHEAD - 1 - t + min(t, nn));
+                    if (t < nn) {
+                        issue(nxt, pgn, t, ring[wave][islot]);
+                        islot = (islot + 1) & (NSL - 1);
+                    }
+                    stage(cur.nst - AHEAD + t, std::false_type{});
+                }
+                ni = min(AHEAD, nn);
+            } else {
                 wait_vmcnt<0>();
-                next_dma(s);
-                stage(s, std::false_type{});
+                top_up(0);
+                stage(0, std::true_type{});
+                for (int s = 1; s < cur.nst; ++s) {
+                    stream_wait<AHEAD, GM::NI>(ci - 1 - s + ni);
+                    top_up(s);
+                    stage(s, std::false_type{});
+                }
             }
         }
         // combine the 16 token lanes of each row, then the four waves
@@ -1585,18 +1681,25 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
         lds_barrier();   // the next item's requests stay in flight
         if (threadIdx.x < NH * a.rows) {
             const int h = threadIdx.x / a.rows, r = threadIdx.x - h * a.rows;
+            float rm[4], rz[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                rm[w] = lds_read_f32(&red[par][w][h][r][0]);
+                rz[w] = lds_read_f32(&red[par][w][h][r][1]);
+            }
             float mx = kNegInf;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[par][w][h][r][0]);
+            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, rm[w]);
             const float mu = (mx == kNegInf) ? 0.f : mx;
             float z = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) z += red[par][w][h][r][1] * __builtin_amdgcn_exp2f(red[par][w][h][r][0] - mu);
+            for (int w = 0; w < 4; ++w) z += rz[w] * __builtin_amdgcn_exp2f(rm[w] - mu);
             float *st = a.stat + ((((int64_t)cur.b * U + cur.l * 2 + cur.h + h) * a.rows + r) * nch + cur.c) * 2;
             st[0] = mx;
             st[1] = z;
         }
         par ^= 1;
+        return ni;
     };
     int it = blockIdx.x;
     if (it >= items) return;
@@ -1604,17 +1707,21 @@ __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     Item cur = decode(it);
     stream_load_q<RB, NH>(a, cur.b, cur.l, cur.h, qo, qA);
     int pgA = load_pg(cur), pgB = 0;
-    if (cur.nst > 0) issue(cur, pgA, 0, ring[wave][slot]);
+    int ci = 0;   // stages of the current item already issued
+    for (; ci < cur.nst && ci < AHEAD; ++ci) {
+        issue(cur, pgA, ci, ring[wave][islot]);
+        islot = (islot + 1) & (NSL - 1);
+    }
     for (;;) {
         int nit = it + gridDim.x;
         Item nxt = decode(nit < items ? nit : it);
-        item(cur, nxt, nit < items, qA, qB, pgA, pgB);
+        ci = item(cur, nxt, nit < items, qA, qB, pgA, pgB, ci);
         if (nit >= items) break;
         it = nit;
         cur = nxt;
         nit = it + gridDim.x;
         nxt = decode(nit < items ? nit : it);
-        item(cur, nxt, nit < items, qB, qA, pgB, pgA);
+        ci = item(cur, nxt, nit < items, qB, qA, pgB, pgA, ci);
         if (nit >= items) break;
         it = nit;
         cur = nxt;
@@ -1666,7 +1773,9 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
     constexpr int NHI = HALF ? 2 : 1;          // items per (b, chunk, layer group)
     constexpr int PER_WAVE = CHUNK / 4;
     constexpr int NSTAGE = PER_WAVE / POS;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][GM::STAGE];
+    constexpr int NSL = GM::NSLOT;
+    constexpr int AHEAD = NSL - 1;             // stages in flight beyond the one computed
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][NSL][GM::STAGE];
     __shared__ float accs[4][PER_WAVE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const KvView &k0 = a.kv[0];   // every draft layer has this geometry (checked on the host)
@@ -1682,9 +1791,10 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
         for (int bb = 0; bb < B; ++bb) pref[bb + 1] += pref[bb];
     }
     __syncthreads();
-    const int LG = acc_layer_groups(pref[B], NHI, a.L_d, max(a.acc_groups, 1), gridDim.x);
+    const int nchunks = __builtin_amdgcn_readfirstlane(pref[B]);   // uniform: the item loop is scalar
+    const int LG = acc_layer_groups(nchunks, NHI, a.L_d, max(a.acc_groups, 1), gridDim.x);
     const int GT = LG * NHI;                   // partial groups: (layer group, head)
-    const int items = pref[B] * GT;
+    const int items = nchunks * GT;
     if (GT == 1) {   // chunks wholly past n_b: S_Draft = 0 (with layer groups draft_part_sum writes them)
         for (int bb = 0; bb < B; ++bb) {
             const int j0 = (pref[bb + 1] - pref[bb]) * CHUNK;
@@ -1723,7 +1833,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, lo[rb], (h0 + h) * a.rows * 4, 0));
     };
     float *acc = accs[wave];
-    int slot = 0;
+    int slot = 0, islot = 0;   // ring slots of the next stage to compute / to issue
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int bc = it / GT, gt = it - (it / GT) * GT;
         const int g = gt / NHI, h0 = gt - (gt / NHI) * NHI;   // layer group, head (HALF)
@@ -1733,10 +1843,13 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
             if (pref[mid] <= bc) lo = mid;
             else hi = mid - 1;
         }
-        const int b = lo, c = bc - pref[lo];
+        // every item field is wave-uniform: readfirstlane makes that visible,
+        // so the stage loops and the counted waits are scalar branches
+        const int b = __builtin_amdgcn_readfirstlane(lo);
+        const int c = __builtin_amdgcn_readfirstlane(bc - pref[lo]);
         const int l0 = g * lpg, l1 = min(L, l0 + lpg);
-        const int nb = sl_len(k0, b);
-        const int jw = c * CHUNK + wave * PER_WAVE;
+        const int nb = __builtin_amdgcn_readfirstlane(sl_len(k0, b));
+        const int jw = c * CHUNK + __builtin_amdgcn_readfirstlane(wave) * PER_WAVE;
         const int left = nb - jw;
         const int nst = (left <= 0 || l0 >= l1) ? 0 : min(NSTAGE, (left + POS - 1) / POS);
 #pragma unroll
@@ -1746,7 +1859,7 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
             // paged caches: the page ids of the wave's 256 positions (16
             // pages) in each layer, one per lane, loaded with the layer's Q
             auto load_pg = [&](int l) -> int { return PAGED ? stream_load_pg(a.kv[l], b, jw, PER_WAVE / 16, lane) : 0; };
-            auto issue = [&](int l, const char *kl, int pgv, int s, uint8_t *stage) {
+            auto issue = [&](int l, const char *kl, int pgv, int s, uint8_t *stage) __attribute__((always_inline)) {
                 if constexpr (PAGED) stream_issue_pg<POS, HALF>(kl, pgv, s, a.kv[l].num_pages, h0 * 128, lane, stage);
                 else stream_issue<POS, HALF>(kl, jw + s * POS, N - 1, h0 * 128, lane, stage);
             };
@@ -1756,7 +1869,11 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
             stream_load_q<RB, NH>(a, b, l0, h0, qo, qA);
             load_lse(b, l0, h0, lA);
             pA = load_pg(l0);
-            issue(l0, a.kv[l0].k + seq0, pA, 0, ring[wave][slot]);
+            int ci = 0;   // stages of the current layer already issued
+            for (; ci < nst && ci < AHEAD; ++ci) {
+                issue(l0, a.kv[l0].k + seq0, pA, ci, ring[wave][islot]);
+                islot = (islot + 1) & (NSL - 1);
+            }
             auto stage = [&](int s, const bf16x8 (&q)[NH][RB][KK], const f32x4 (&ls)[NH][RB]) {
                 const uint32_t base = lds_addr(ring[wave][slot]);
 #pragma unroll
@@ -1781,35 +1898,84 @@ __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
                     t = group4_sum(t);
                     if (lane < 16) acc[s * POS + s16 * 16 + lane] += t;
                 }
-                slot ^= 1;
+                slot = (slot + 1) & (NSL - 1);
             };
+            // One layer, `ci` of whose stages were issued before it began;
+            // keeps AHEAD stages in flight, running on into the next layer of
+            // the group, and returns how many of its stages it issued.
             auto layer = [&](int l, const bf16x8 (&q)[NH][RB][KK], const f32x4 (&ls)[NH][RB], const int &pg,
-                             bf16x8 (&qn)[NH][RB][KK], f32x4 (&lsn)[NH][RB], int &pgn) {
+                             bf16x8 (&qn)[NH][RB][KK], f32x4 (&lsn)[NH][RB], int &pgn, int ci) -> int {
+                ci = __builtin_amdgcn_readfirstlane(ci);
                 // both layers' cache pointers from uniform indices (scalar
                 // loads, outside the vector-load order)
                 const int ln = (l + 1 < l1) ? l + 1 : l;
+                const int nn = (l + 1 < l1) ? nst : 0;
                 const char *kl = a.kv[l].k + seq0;
                 const char *kn = a.kv[ln].k + seq0;
-                auto next_dma = [&](int s) {   // the DMA after stage s of this layer
-                    if (s + 1 < nst) issue(l, kl, pg, s + 1, ring[wave][slot ^ 1]);
-                    else if (l + 1 < l1) issue(ln, kn, pgn, 0, ring[wave][slot ^ 1]);
+                int ni = 0;   // stages of the next layer issued
+                auto top_up = [&](int s) __attribute__((always_inline)) {
+                    while ((ci - 1 - s) + ni < AHEAD) {
+                        const bool own = ci < nst;
+                        if (!own && ni >= nn) break;
+                        if (own) issue(l, kl, pg, ci, ring[wave][islot]);
+                        else issue(ln, kn, pgn, ni, ring[wave][islot]);
+                        ci += own ? 1 : 0;
+                        ni += own ? 0 : 1;
+                        islot = (islot + 1) & (NSL - 1);
+                    }
                 };
-                wait_vmcnt<0>();
+                // As in the statistics pass: the next layer's page ids ahead
+                // of its Q and normalisers; in the steady case stages 0 and 1
+                // issue this layer's stages unconditionally, so the counted
+                // waits of the last AHEAD stages cover those loads.
+                const bool steady = ci == AHEAD && nst >= AHEAD + 2;
+                stream_wait<AHEAD, GM::NI>(ci - 1);
+                pgn = load_pg(ln);
                 stream_load_q<RB, NH>(a, b, ln, h0, qo, qn);
                 load_lse(b, ln, h0, lsn);
-                pgn = load_pg(ln);
-                next_dma(0);
-                stage(0, q, ls);
-                for (int s = 1; s < nst; ++s) {
+                if (steady) {
+                    issue(l, kl, pg, ci++, ring[wave][islot]);
+                    islot = (islot + 1) & (NSL - 1);
+                    stage(0, q, ls);
+                    int s = 1;   // at least one pass (see the statistics pass)
+                    do {
+                        wait_vmcnt<(AHEAD - 1) * GM::NI>();
+                        issue(l, kl, pg, ci++, ring[wave][islot]);
+                        islot = (islot + 1) & (NSL - 1);
+                        stage(s, q, ls);
+                    } while (++s < nst - AHEAD);
+                    // the last AHEAD stages, unrolled (see the statistics pass)
+#pragma unroll
+                    for (int t = 0; t < AHEAD; ++t) {
+                        stream_wait<AHEAD, GM::NI>(AHEAD - 1 - t + min(t, nn));
+                        if (t < nn) {
+                            issue(ln, kn, pgn, t, ring[wave][islot]);
+                            islot = (islot + 1) & (NSL - 1);
+                        }
+                        stage(nst - AHEAD + t, q, ls);
+                    }
+                    ni = min(AHEAD, nn);
+                } else {
                     wait_vmcnt<0>();
-                    next_dma(s);
-                    stage(s, q, ls);
+                    top_up(0);
+                    stage(0, q, ls);
+                    for (int s = 1; s < nst; ++s) {
+                        stream_wait<AHEAD, GM::NI>(ci - 1 - s + ni);
+                        top_up(s);
+                        stage(s, q, ls);
+                    }
                 }
+                return ni;
             };
-            for (int l = l0; l < l1; l += 2) {
-                layer(l, qA, lA, pA, qB, lB, pB);
-                if (l + 1 < l1) layer(l + 1, qB, lB, pB, qA, lA, pA);
+            // layer pairs with both calls unconditional (a conditional second
+            // call made the compiler merge the two Q sets with selects, which
+            // wait for the loads), then an odd last layer
+            int l = l0;
+            for (; l + 1 < l1; l += 2) {
+                ci = layer(l, qA, lA, pA, qB, lB, pB, ci);
+                ci = layer(l + 1, qB, lB, pB, qA, lA, pA, ci);
             }
+            if (l < l1) layer(l, qA, lA, pA, qB, lB, pB, ci);
         }
         float *out = (GT == 1) ? a.s_draft + (int64_t)b * N : a.part + ((int64_t)gt * k0.B + b) * N;
 #pragma unroll
