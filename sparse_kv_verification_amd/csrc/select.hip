@@ -558,6 +558,12 @@ constexpr int MWW = MWT / 64;              // waves
 constexpr int MWR = 16;                    // positions per lane
 constexpr int MWC = MWT * MWR;             // positions per chunk
 constexpr int kMwBins = 2048;
+// A chunk's histogram in global memory holds 16-bit counts (a chunk has
+// MWC = 4096 positions), two bins per word, so the work-group that sums the
+// chunks' histograms reads a lane's eight bins of one chunk with one 16-byte
+// load and keeps every chunk's load in flight at once.
+constexpr int kMwHistWords = kMwBins / 2;
+static_assert(MWC < 65536, "16-bit chunk histogram counts");
 constexpr int kMwMaxChunks = 64;
 constexpr int kMwMinN = 32768 + 1;         // shorter rows: the register-resident kernel
 constexpr int kMwMaxN = kMwMaxChunks * MWC;
@@ -575,7 +581,7 @@ struct MwPtrs {
     uint32_t *flag;        // [B][C][MWT] 2-bit tier codes of the lane's 16 rows
     uint32_t *mm;          // [B][C][2] per-chunk min / max candidate pattern
     int32_t *kept;         // [B][C] kept positions per chunk
-    uint32_t *hist;        // [B][C][kMwBins] per-chunk histogram of the current pass
+    uint32_t *hist;        // [B][C][kMwHistWords] per-chunk histogram of the current pass (16-bit bins)
     MwState *state;        // [B][2] per selection (0 draft, 1 target)
     int32_t *ctr;          // [B] arrival counter of the current pass
     int C;
@@ -843,13 +849,16 @@ __global__ __launch_bounds__(MWT) void mw_pass(TopkArgs a, MwPtrs p, int pass) {
             if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key - lo) >> s], 1u);
         }
     __syncthreads();
-    // this chunk's histogram, written through (8 consecutive bins per lane)
-    uint32_t *hrow = p.hist + ((size_t)b * p.C + c) * kMwBins;
-    const __amdgpu_buffer_rsrc_t hr = coherent_rsrc(hrow, kMwBins * 4);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4 *)&sh.hist[8 * t + 4 * q], hr,
-                                               (uint32_t)((8 * t + 4 * q) * 4), 0, kCachePolicySc1);
+    // this chunk's histogram, written through: lane t packs bins 8t .. 8t + 7
+    // into one 16-byte store
+    uint32_t *hrow = p.hist + ((size_t)b * p.C + c) * kMwHistWords;
+    const __amdgpu_buffer_rsrc_t hr = coherent_rsrc(hrow, kMwHistWords * 4);
+    {
+        const u32x4 lo4 = *(const u32x4 *)&sh.hist[8 * t], hi4 = *(const u32x4 *)&sh.hist[8 * t + 4];
+        const u32x4 pk = {lo4[0] | (lo4[1] << 16), lo4[2] | (lo4[3] << 16), hi4[0] | (hi4[1] << 16),
+                          hi4[2] | (hi4[3] << 16)};
+        __builtin_amdgcn_raw_buffer_store_b128(pk, hr, (uint32_t)(16 * t), 0, kCachePolicySc1);
+    }
     wait_all_mem();
     __syncthreads();
     if (t == 0) sh.flag = __hip_atomic_fetch_add(&p.ctr[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.C - 1;
@@ -858,23 +867,22 @@ __global__ __launch_bounds__(MWT) void mw_pass(TopkArgs a, MwPtrs p, int pass) {
     // last to arrive: sum the chunks' histograms (lane t: bins 8t .. 8t + 7)
     uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const __amdgpu_buffer_rsrc_t hall =
-        coherent_rsrc(p.hist + (size_t)b * p.C * kMwBins, (uint32_t)(p.C * kMwBins * 4));
-    // eight chunks' loads in flight before any is added (loads past the
-    // last chunk fall outside the resource and read 0)
-    for (int c0 = 0; c0 < p.C; c0 += 8) {
-        u32x4 u[8][2];
+        coherent_rsrc(p.hist + (size_t)b * p.C * kMwHistWords, (uint32_t)(p.C * kMwHistWords * 4));
+    // 32 chunks' loads in flight before any is added, one round for up to
+    // 131072 positions (loads past the last chunk fall outside the resource
+    // and read 0)
+    for (int c0 = 0; c0 < p.C; c0 += 32) {
+        u32x4 u[32];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 32; ++q)
+            u[q] = __builtin_amdgcn_raw_buffer_load_b128(hall, (uint32_t)(((c0 + q) * kMwHistWords + 4 * t) * 4), 0,
+                                                         kCachePolicySc1);
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                u[q][h2] = __builtin_amdgcn_raw_buffer_load_b128(
-                    hall, (uint32_t)(((c0 + q) * kMwBins + 8 * t + 4 * h2) * 4), 0, kCachePolicySc1);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 32; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                h[e] += u[q][0][e];
-                h[4 + e] += u[q][1][e];
+                h[2 * e] += u[q][e] & 0xffffu;
+                h[2 * e + 1] += u[q][e] >> 16;
             }
     }
     int local = 0;
@@ -963,8 +971,11 @@ __global__ __launch_bounds__(MWT) void mw_mark(TopkArgs a, MwPtrs p, int next_mm
             // ties in the chunks before this one: their counts in the last
             // pass's bin of the threshold value
             int before = 0;
-            if (t < c)
-                before = (int)ld_coherent_u32(p.hist + ((size_t)b * p.C + t) * kMwBins + tie_bin);
+            if (t < c) {
+                const uint32_t w2 =
+                    ld_coherent_u32(p.hist + ((size_t)b * p.C + t) * kMwHistWords + (tie_bin >> 1));
+                before = (int)((tie_bin & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+            }
             before = mw_sum(before, sh);
             const int need = remaining - before;
             mw_rank(tie, sh, [&](int i, int rank) {
