@@ -2004,7 +2004,7 @@ int draft_acc_groups(int B, int N_max, int L_d) {
 // past n_b are 0 (the partials of chunks wholly past n_b are never written).
 // With one partial the accumulation kernel has written S_Draft itself.
 __global__ __launch_bounds__(256) void draft_part_sum(const float *part, int nhi, int cap, int L, int grid, int B,
-                                                      int N, const int32_t *seq_lens, float *out) {
+                                                      int N, const int32_t *seq_lens, float *out, bool vec) {
     // the chunk count, with the lengths loaded in parallel (one load per
     // lane, then a block sum): a serial loop over B put B dependent loads in
     // front of the common case, one group, where nothing is left to do
@@ -2018,13 +2018,38 @@ __global__ __launch_bounds__(256) void draft_part_sum(const float *part, int nhi
     const int chunks = s_part[0] + s_part[1] + s_part[2] + s_part[3];
     const int groups = acc_layer_groups(chunks, nhi, L, cap, grid) * nhi;
     if (groups == 1) return;
+    // row b = blockIdx.y; with vec, four positions per lane in 16-byte
+    // accesses (N % 4 == 0, out and part 16-byte aligned: checked by the
+    // launcher)
     const int64_t n = (int64_t)B * N;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int b = (int)(i / N), j = (int)(i - (int64_t)b * N);
-        float v = 0.f;
-        if (j < min(max(seq_lens[b], 0), N))
-            for (int g = 0; g < groups; ++g) v += part[(int64_t)g * n + i];
-        out[i] = v;
+    const int b = blockIdx.y;
+    const int nb = __builtin_amdgcn_readfirstlane(min(max(seq_lens[b], 0), N));
+    const float *pr = part + (int64_t)b * N;
+    float *orow = out + (int64_t)b * N;
+    if (vec) {
+        for (int j = (blockIdx.x * 256 + threadIdx.x) * 4; j < N; j += gridDim.x * 1024) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (j < nb) {
+                for (int g = 0; g < groups; ++g) {
+                    const f32x4 u = *(const f32x4 *)(pr + (int64_t)g * n + j);
+                    v[0] += u[0];
+                    v[1] += u[1];
+                    v[2] += u[2];
+                    v[3] += u[3];
+                }
+#pragma unroll
+                for (int e = 1; e < 4; ++e)   // a row that ends inside these four
+                    if (j + e >= nb) v[e] = 0.f;
+            }
+            *(f32x4 *)(orow + j) = v;
+        }
+    } else {
+        for (int j = blockIdx.x * 256 + threadIdx.x; j < N; j += gridDim.x * 256) {
+            float v = 0.f;
+            if (j < nb)
+                for (int g = 0; g < groups; ++g) v += pr[(int64_t)g * n + j];
+            orow[j] = v;
+        }
     }
 }
 
@@ -2301,10 +2326,11 @@ static hipError_t draft_stream_impl(const DraftScoreArgs &a, hipStream_t s) {
     const int grid = acc_items < GROUPS ? (int)acc_items : GROUPS;
     hipLaunchKernelGGL((draft_acc_stream<RB, PAGED, HALF>), dim3(grid), dim3(256), 0, s, b);
     if ((e = hipGetLastError()) != hipSuccess || cap * NHI == 1) return e;
-    const int64_t n = (int64_t)k0.B * k0.N_max;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
-    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)blocks), dim3(256), 0, s, a.part, NHI, cap, a.L_d, grid, k0.B,
-                       k0.N_max, k0.seq_lens, a.s_draft);
+    const bool vec = k0.N_max % 4 == 0 && (uintptr_t)a.s_draft % 16 == 0 && (uintptr_t)a.part % 16 == 0;
+    const int per_block = vec ? 1024 : 256;   // positions of a row per work-group and round
+    const int bx = std::min((k0.N_max + per_block - 1) / per_block, 256);
+    hipLaunchKernelGGL(draft_part_sum, dim3((unsigned)bx, (unsigned)k0.B), dim3(256), 0, s, a.part, NHI, cap, a.L_d,
+                       grid, k0.B, k0.N_max, k0.seq_lens, a.s_draft, vec);
     return hipGetLastError();
 }
 
