@@ -261,7 +261,9 @@ struct RowStatsParams {
 template <int NR>   // rows per unit at most (1, 2, 4 or 8)
 __global__ __launch_bounds__(256) void unit_stats_rows(RowStatsParams p) {
     constexpr int D = 128, EPL = 8;
-    constexpr int NB = NR <= 2 ? 16 : 8;   // loads in flight per lane
+    // loads in flight per lane: 8 (16, with fewer waves per SIMD, measured 2%
+    // slower, 24 5% slower, 4 3% slower on the paged c5 cache)
+    constexpr int NB = 8;
     extern __shared__ float lg[];    // [S][CH]
     __shared__ int pgs[CH / 16];
     const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -532,9 +534,35 @@ __global__ __launch_bounds__(256) void rows_lse(const float *stat, float *lse, i
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nrows_total) return;
+    const float *st = stat + (int64_t)row * nchunk * 2;
+    constexpr int MAXP = 8;   // (max, sum) pairs per lane held in registers
+    if (nchunk <= 64 * MAXP) {
+        // every pair of the row is requested together with the length (the
+        // ones past n_b are in bounds and then ignored): one round trip
+        float2 v[MAXP];
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int c = lane + 64 * i;
+            v[i] = c < nchunk ? *(const float2 *)(st + 2 * c) : float2{kNegInf, 0.f};
+        }
+        const int nb = min(max(seq_lens[row / rows_per_b], 0), N_max);
+        const int nv = min(nchunk, (nb + chunk - 1) / chunk);
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i)
+            if (lane + 64 * i < nv) mx = fmaxf(mx, v[i].x);
+        mx = wave_max(mx);
+        const float muse = (mx == kNegInf) ? 0.f : mx;
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i)
+            if (lane + 64 * i < nv) z += v[i].y * exp2f(v[i].x - muse);
+        z = wave_sum(z);
+        if (lane == 0) lse[row] = (z > 0.f) ? muse + __log2f(z) : __builtin_huge_valf();
+        return;
+    }
     const int nb = min(max(seq_lens[row / rows_per_b], 0), N_max);
     const int nv = min(nchunk, (nb + chunk - 1) / chunk);
-    const float *st = stat + (int64_t)row * nchunk * 2;
     float mx = kNegInf;
     for (int c = lane; c < nv; c += 64) mx = fmaxf(mx, st[2 * c]);
     mx = wave_max(mx);
