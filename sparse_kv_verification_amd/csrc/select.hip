@@ -745,16 +745,27 @@ __device__ __forceinline__ int mw_sum(int v, MwShared &sh) {
     return total;
 }
 
+// The lane's 16 keys of score row `row` (nullptr: none), requested for every
+// position below N_max whether or not it turns out to be a candidate, so the
+// loads wait for no other result (the length, the tier codes, the window).
+__device__ __forceinline__ void mw_load_keys(const float *row, int j0, int N_max, uint32_t (&key)[MWR]) {
+#pragma unroll
+    for (int i = 0; i < MWR; ++i) {
+        const int j = j0 + i * MWT;
+        key[i] = (row != nullptr && j < N_max) ? __float_as_uint(row[j]) : 0u;
+    }
+}
+
 // Candidate keys of rows `cand` of this lane: per-chunk min and max, stored
 // by lane 0.
-__device__ __forceinline__ void mw_store_minmax(const float *row, uint32_t cand, int j0, MwShared &sh, uint32_t *mm) {
+__device__ __forceinline__ void mw_store_minmax(const uint32_t (&key)[MWR], uint32_t cand, MwShared &sh,
+                                                uint32_t *mm) {
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
     for (int i = 0; i < MWR; ++i)
         if ((cand >> i) & 1u) {
-            const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
-            lo = min(lo, key);
-            hi = max(hi, key);
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
         }
     mw_minmax(lo, hi, sh);
     if (threadIdx.x == 0) {
@@ -781,8 +792,11 @@ __device__ __forceinline__ uint32_t mw_free(uint32_t fw) {
 __global__ __launch_bounds__(MWT) void mw_begin(TopkArgs a, MwPtrs p) {
     __shared__ MwShared sh;
     const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
-    const MwTiers T = mw_tiers(a, b);
     const int j0 = c * MWC + t;
+    const int sel = a.s_draft ? 0 : 1;   // the first selection of the call
+    uint32_t key[MWR];                   // requested together with the length
+    mw_load_keys((a.s_draft || a.s_target) ? mw_row(a, b, sel) : nullptr, j0, a.N_max, key);
+    const MwTiers T = mw_tiers(a, b);
     const uint32_t valid = mw_valid(j0, T.n);
     uint32_t fw = 0, prot = 0;
 #pragma unroll
@@ -793,10 +807,9 @@ __global__ __launch_bounds__(MWT) void mw_begin(TopkArgs a, MwPtrs p) {
 #pragma unroll
     for (int i = 0; i < MWR; ++i) fw |= ((prot >> i) & 1u) << (2 * i);
     p.flag[((size_t)b * p.C + c) * MWT + t] = fw;
-    const int sel = a.s_draft ? 0 : 1;   // the first selection of the call
     int K, ncand;
     mw_sel(T, sel, K, ncand);
-    if (K > 0 && K < ncand) mw_store_minmax(mw_row(a, b, sel), valid & ~prot, j0, sh, p.mm + ((size_t)b * p.C + c) * 2);
+    if (K > 0 && K < ncand) mw_store_minmax(key, valid & ~prot, sh, p.mm + ((size_t)b * p.C + c) * 2);
     if (c == 0 && t == 0) __hip_atomic_store(&p.ctr[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -805,29 +818,35 @@ __global__ __launch_bounds__(MWT) void mw_pass(TopkArgs a, MwPtrs p, int pass) {
     __shared__ MwShared sh;
     const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
-    const MwTiers T = mw_tiers(a, b);
-    int K, ncand;
-    mw_sel(T, SEL, K, ncand);
-    if (K <= 0 || K >= ncand) return;   // the same for every chunk of the sequence
+    // Every load of the pass is requested before any result is used: the
+    // keys, the tier codes, the chunks' [min, max] or the window, and the
+    // length (one round trip instead of a chain of them).
+    const int j0 = c * MWC + t;
+    uint32_t key[MWR];
+    mw_load_keys(mw_row(a, b, SEL), j0, a.N_max, key);
+    const uint32_t fw = p.flag[((size_t)b * p.C + c) * MWT + t];
     MwState *st = p.state + (size_t)b * 2 + SEL;
-    uint32_t lo, hi;
-    int remaining;
+    uint32_t lo = 0xffffffffu, hi = 0u;
     if (pass == 0) {
-        lo = 0xffffffffu;
-        hi = 0u;
         if (t < p.C) {
             lo = ld_coherent_u32(p.mm + ((size_t)b * p.C + t) * 2);
             hi = ld_coherent_u32(p.mm + ((size_t)b * p.C + t) * 2 + 1);
         }
+    } else if (t == 0) {
+        sh.flag = (int)ld_coherent_u32((const uint32_t *)&st->fin);
+        sh.b_lo = ld_coherent_u32(&st->lo);
+        sh.b_hi = ld_coherent_u32(&st->hi);
+        sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
+    }
+    const MwTiers T = mw_tiers(a, b);
+    int K, ncand;
+    mw_sel(T, SEL, K, ncand);
+    if (K <= 0 || K >= ncand) return;   // the same for every chunk of the sequence
+    int remaining;
+    if (pass == 0) {
         mw_minmax(lo, hi, sh);
         remaining = K;
     } else {
-        if (t == 0) {
-            sh.flag = (int)ld_coherent_u32((const uint32_t *)&st->fin);
-            sh.b_lo = ld_coherent_u32(&st->lo);
-            sh.b_hi = ld_coherent_u32(&st->hi);
-            sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
-        }
         __syncthreads();
         if (sh.flag) return;
         lo = sh.b_lo;
@@ -839,15 +858,11 @@ __global__ __launch_bounds__(MWT) void mw_pass(TopkArgs a, MwPtrs p, int pass) {
     const int s = max(0, bl - 11);
     for (int i = t; i < kMwBins; i += MWT) sh.hist[i] = 0;
     __syncthreads();
-    const int j0 = c * MWC + t;
-    const uint32_t cand = mw_valid(j0, T.n) & mw_free(p.flag[((size_t)b * p.C + c) * MWT + t]);
-    const float *row = mw_row(a, b, SEL);
+    const uint32_t cand = mw_valid(j0, T.n) & mw_free(fw);
 #pragma unroll
     for (int i = 0; i < MWR; ++i)
-        if ((cand >> i) & 1u) {
-            const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
-            if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key - lo) >> s], 1u);
-        }
+        if ((cand >> i) & 1u)
+            if (key[i] >= lo && key[i] <= hi) atomicAdd(&sh.hist[(key[i] - lo) >> s], 1u);
     __syncthreads();
     // this chunk's histogram, written through: lane t packs bins 8t .. 8t + 7
     // into one 16-byte store
@@ -935,37 +950,40 @@ template <int SEL>
 __global__ __launch_bounds__(MWT) void mw_mark(TopkArgs a, MwPtrs p, int next_mm, int count) {
     __shared__ MwShared sh;
     const int b = blockIdx.x / p.C, c = blockIdx.x - (blockIdx.x / p.C) * p.C, t = threadIdx.x;
+    // requests first (keys of this selection and, for the next one's
+    // [min, max], of the target row; tier codes; the window), then the length
+    const int j0 = c * MWC + t;
+    uint32_t key[MWR], tkey[MWR];
+    mw_load_keys(mw_row(a, b, SEL), j0, a.N_max, key);
+    mw_load_keys(next_mm ? mw_row(a, b, 1) : nullptr, j0, a.N_max, tkey);
+    uint32_t *fwp = p.flag + ((size_t)b * p.C + c) * MWT + t;
+    uint32_t fw = *fwp;
+    const MwState *st = p.state + (size_t)b * 2 + SEL;
+    if (t == 0) {
+        sh.b_lo = ld_coherent_u32(&st->lo);
+        sh.b_hi = ld_coherent_u32(&st->hi);
+        sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
+        sh.b_above = (int)ld_coherent_u32((const uint32_t *)&st->exact);
+        sh.b_digit = (int)ld_coherent_u32((const uint32_t *)&st->tie_bin);
+    }
     const MwTiers T = mw_tiers(a, b);
     int K, ncand;
     mw_sel(T, SEL, K, ncand);
-    const int j0 = c * MWC + t;
     const uint32_t valid = mw_valid(j0, T.n);
-    uint32_t *fwp = p.flag + ((size_t)b * p.C + c) * MWT + t;
-    uint32_t fw = *fwp;
     const uint32_t cand = valid & mw_free(fw);
     uint32_t sel = 0;
     if (K > 0 && K >= ncand) {
         sel = cand;
     } else if (K > 0) {
-        const MwState *st = p.state + (size_t)b * 2 + SEL;
-        if (t == 0) {
-            sh.b_lo = ld_coherent_u32(&st->lo);
-            sh.b_hi = ld_coherent_u32(&st->hi);
-            sh.b_rem = (int)ld_coherent_u32((const uint32_t *)&st->remaining);
-            sh.b_above = (int)ld_coherent_u32((const uint32_t *)&st->exact);
-            sh.b_digit = (int)ld_coherent_u32((const uint32_t *)&st->tie_bin);
-        }
         __syncthreads();
         const uint32_t lo = sh.b_lo, hi = sh.b_hi;
         const int exact = sh.b_above, tie_bin = sh.b_digit, remaining = sh.b_rem;
-        const float *row = mw_row(a, b, SEL);
         uint32_t tie = 0;
 #pragma unroll
         for (int i = 0; i < MWR; ++i)
             if ((cand >> i) & 1u) {
-                const uint32_t key = __float_as_uint(row[j0 + i * MWT]);
-                sel |= (uint32_t)(key > hi || (exact && key >= lo)) << i;
-                tie |= (uint32_t)(!exact && key == lo) << i;
+                sel |= (uint32_t)(key[i] > hi || (exact && key[i] >= lo)) << i;
+                tie |= (uint32_t)(!exact && key[i] == lo) << i;
             }
         if (!exact) {
             // ties in the chunks before this one: their counts in the last
@@ -990,8 +1008,7 @@ __global__ __launch_bounds__(MWT) void mw_mark(TopkArgs a, MwPtrs p, int next_mm
     if (next_mm) {
         int Kt, nct;
         mw_sel(T, 1, Kt, nct);
-        if (Kt > 0 && Kt < nct)
-            mw_store_minmax(mw_row(a, b, 1), valid & mw_free(fw), j0, sh, p.mm + ((size_t)b * p.C + c) * 2);
+        if (Kt > 0 && Kt < nct) mw_store_minmax(tkey, valid & mw_free(fw), sh, p.mm + ((size_t)b * p.C + c) * 2);
     }
     if (count) {
         const int kept = mw_sum(__popc(valid & ~mw_free(fw)), sh);
