@@ -219,6 +219,9 @@ SCORE_CASES = [
     ("mfma-d128-rb2", dict(base="c2", B=2, n=2300, n_lo=800, L_d=2, d_d=128)),
     ("mfma-d128-rb3", dict(base="c2", B=2, n=2000, L_d=3, d_d=128, H_d=12, w=6)),
     ("mfma-d128-rb4-paged", dict(base="c5", B=2, n=2600, n_lo=900, L_d=2, d_d=128)),
+    # 140000 positions: 547 target chunks of 256, past the 512 per-chunk pairs
+    # the row normaliser holds in registers (its loop form)
+    ("long-row-normaliser-loop", dict(base="c2", B=1, n=140000, L_d=1)),
     ("tiny-f32", dict(base="c1")),
 ]
 
