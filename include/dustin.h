@@ -217,9 +217,9 @@ size_t dustin_topk_workspace_bytes(int32_t B, int32_t N_max, int32_t k);
  *  scale 0 means 1/sqrt(head_dim)
  *  out   [B][w][H_q][head_dim], kv dtype; an empty set gives 0
  *  lse   nullable [B][w][H_q] float32; an empty set gives -inf
- * Requires w * (H_q / H_kv) <= 64.  A bfloat16 cache needs head_dim 64 or
- * 128 (DUSTIN_ERR_UNSUPPORTED for 32, which only float32 caches serve here);
- * the same holds for every attention entry point below.
+ * Requires w * (H_q / H_kv) <= 64.  head_dim 32, 64 or 128 in either dtype
+ * (bfloat16 head_dim 32 pads up to 32 query rows per KV head); the same
+ * holds for every attention entry point below.
  */
 dustin_status dustin_sparse_verify_attn(const void *q, int32_t w, int32_t H_q,
                                         const dustin_kv *kv, const int32_t *idx,

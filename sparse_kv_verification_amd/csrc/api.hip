@@ -101,8 +101,7 @@ dustin_status check_attn_shape(const dustin_kv *kv, int w, int H_q, const char *
     CHECK(w >= 1 && H_q >= 1, DUSTIN_ERR_INVALID_ARG, "%s: w and H_q must be >= 1", what);
     CHECK(H_q % kv->H_kv == 0, DUSTIN_ERR_INVALID_ARG, "%s: H_q %d not a multiple of H_kv %d", what, H_q, kv->H_kv);
     CHECK(w * (H_q / kv->H_kv) <= 64, DUSTIN_ERR_UNSUPPORTED, "%s: w * G = %d exceeds 64", what, w * (H_q / kv->H_kv));
-    CHECK(kv->dtype == DUSTIN_F32 || kv->head_dim >= 64, DUSTIN_ERR_UNSUPPORTED,
-          "%s: bf16 attention needs head_dim 64 or 128", what);
+
     CHECK((int64_t)kv->B * kv->H_kv <= kAttnCounterSlots, DUSTIN_ERR_UNSUPPORTED,
           "%s: B * H_kv = %lld exceeds %d", what, (long long)kv->B * kv->H_kv, kAttnCounterSlots);
     return DUSTIN_OK;

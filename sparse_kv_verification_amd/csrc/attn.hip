@@ -83,12 +83,16 @@ __device__ __forceinline__ int phys_row(const KvView &kv, int b, int j) {
 // 16-byte-chunk swizzle of row r of a tile.  D = 128: a bijection on the low
 // four bits (16 rows at one chunk -> 16 distinct chunk slots; four
 // consecutive rows -> four distinct chunk pairs).  D = 64: two rows share a
-// 64-bank span, so the swizzle acts on r >> 1.
+// 64-bank span, so the swizzle acts on r >> 1.  D = 32: four rows of four
+// chunks share a span; rows r and r + 4k take chunk slots c ^ k, so 16
+// consecutive rows at one chunk fill the 16 bank groups of four spans.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) {
         const int x = r & 15;
         return ((x << 1) | (x >> 3)) & 15;
+    } else if constexpr (D == 32) {
+        return (r >> 2) & 3;
     } else {
         const int x = (r >> 1) & 7;
         return ((x << 1) | (x >> 2)) & 7;
@@ -199,7 +203,10 @@ __device__ __forceinline__ void wait_tile(int ahead) {
 
 template <int D, int RB, int NW>
 struct AttnGeom {
-    static constexpr int T = (16 * NW / RB > kAttnTile) ? 16 * NW / RB : kAttnTile;   // tokens per tile
+    // tokens per tile: at least kAttnTile, 16 per token share of a row block,
+    // and one DMA instruction (64 lanes x 16 bytes) per wave for K and for V
+    static constexpr int T0 = (16 * NW / RB > kAttnTile) ? 16 * NW / RB : kAttnTile;
+    static constexpr int T = (NW * (512 / D) > T0) ? NW * (512 / D) : T0;
     static constexpr int STAGE = 2 * T * D * 2;                                        // K + V bytes per tile
     static constexpr int NBUF = (kAttnRingBytes / STAGE < 8) ? kAttnRingBytes / STAGE : 8;
 };
@@ -827,6 +834,9 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
     p.rows = w * G;
     p.rb = (p.rows + 15) / 16;
     if (p.rb == 3) p.rb = 4;   // the bf16 kernel splits its waves over 1, 2 or 4 row blocks
+    // head_dim 32: the share fold gives each wave at least 16 columns, so at
+    // most two token shares per row block: pad one row block to two
+    if (D == 32 && p.rb == 1) p.rb = 2;
     p.rpad = p.rb * 16;
     const long groups = (long)B * Hkv;
     const int tok = tokens > 0 ? tokens : 1;
@@ -867,8 +877,9 @@ AttnPlan attn_plan(int B, int w, int Hq, int Hkv, int D, int tokens, bool f32) {
 template <int D, int RB>
 static hipError_t launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
     // 8 waves (two per SIMD hide the MFMA / LDS latency of the tile loop)
-    // unless a tile would then hold fewer DMA instructions than waves.
-    constexpr int NW = (D == 64 && RB == 4) ? 4 : (RB == 1 ? 4 : 8);
+    // unless a tile would then hold fewer DMA instructions than waves
+    // (head_dim 32: a 64-token tile is four DMA instructions per K or V).
+    constexpr int NW = (D == 32 || (D == 64 && RB == 4)) ? 4 : (RB == 1 ? 4 : 8);
     const size_t dyn = (size_t)a.tps * sizeof(int);
     if (a.causal) {
         if (a.idx)
@@ -916,6 +927,11 @@ hipError_t launch_attn(const AttnArgs &a_in, const AttnPlan &p, hipStream_t s) {
             case 2: return launch_bf16<64, 2>(a, grid, s);
             case 3: return launch_bf16<64, 4>(a, grid, s);
             case 4: return launch_bf16<64, 4>(a, grid, s);
+        }
+    } else if (a.kv.D == 32) {   // at least two row blocks (attn_plan)
+        switch (p.rb) {
+            case 2: return launch_bf16<32, 2>(a, grid, s);
+            case 4: return launch_bf16<32, 4>(a, grid, s);
         }
     }
     return hipErrorInvalidValue;

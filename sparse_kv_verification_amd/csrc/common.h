@@ -303,6 +303,14 @@ __device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[4], u32x4 (&v
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 }
+__device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[1], u32x4 (&v)[1]) {
+    asm volatile(
+        "ds_read_b128 %0, %1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0])
+        : "v"(a[0])
+        : "memory");
+}
 __device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[2], u32x4 (&v)[2]) {
     asm volatile(
         "ds_read_b128 %0, %2\n\t"
@@ -313,11 +321,22 @@ __device__ __forceinline__ void ds_read_b128_n(const uint32_t (&a)[2], u32x4 (&v
         : "memory");
 }
 
+__device__ __forceinline__ void ds_read_tr16_n2(const uint32_t (&a)[2], s16x4 (&v)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void ds_read_tr16_n(const uint32_t (&a)[N], s16x4 (&v)[N]) {
-    static_assert(N == 8 || N == 4, "d tiles");
+    static_assert(N == 8 || N == 4 || N == 2, "d tiles");
     if constexpr (N == 8) ds_read_tr16_n8(a, v);
-    else ds_read_tr16_n4(a, v);
+    else if constexpr (N == 4) ds_read_tr16_n4(a, v);
+    else ds_read_tr16_n2(a, v);
 }
 
 // Dispatch on the number of d tiles.

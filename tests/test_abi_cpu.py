@@ -59,7 +59,6 @@ def test_attention_argument_errors(L):
     assert attn(L, kv(), out=None) == INVALID
     assert attn(L, kv(dtype=7)) == UNSUPPORTED
     assert attn(L, kv(head_dim=96)) == UNSUPPORTED
-    assert attn(L, kv(dtype=1, head_dim=32)) == UNSUPPORTED          # bf16 MFMA path needs 64/128
     assert attn(L, kv(), Hq=60) == INVALID                            # not a multiple of H_kv
     assert attn(L, kv(), w=9) == UNSUPPORTED                          # w * G = 72 > 64
     assert attn(L, kv(), k=0) == INVALID
@@ -281,19 +280,21 @@ def test_workspace_sizes_are_shape_only(L):
     assert L.dustin_topk_workspace_bytes(2, 300000, 4096) >= 2 * 300000
 
 
-def test_bf16_attention_refuses_head_dim_32(L):
-    """bf16 attention serves head_dim 64 and 128 only (float32 serves 32 too):
-    refused on the host with DUSTIN_ERR_UNSUPPORTED, by every attention entry point."""
-    d32 = kv(head_dim=32, dtype=1)
-    assert attn(L, d32) == UNSUPPORTED
-    assert b"head_dim 64 or 128" in L.dustin_last_error()
-    assert L.dustin_verify_attn(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE, None, FAKE, 1 << 40,
-                                None) == UNSUPPORTED
-    assert L.dustin_sparse_verify_attn_noalloc(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE, None,
-                                               None) == UNSUPPORTED
-    # the same geometry in float32 passes validation (then needs a device)
+def test_attention_head_dims(L):
+    """Every attention entry point serves head_dim 32, 64 and 128 in bfloat16
+    and float32 (validation passes, then a device is needed); other head dims
+    are refused on the host with DUSTIN_ERR_UNSUPPORTED."""
     if not torch.cuda.is_available():
-        assert attn(L, kv(head_dim=32, dtype=0)) == HIPERR
+        for d in (32, 64, 128):
+            for dt in (0, 1):
+                assert attn(L, kv(head_dim=d, dtype=dt)) == HIPERR, (d, dt)
+        d32 = kv(head_dim=32, dtype=1)
+        assert L.dustin_verify_attn(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE, None, FAKE,
+                                    1 << 40, None) == HIPERR
+        assert L.dustin_sparse_verify_attn_noalloc(FAKE, 4, 64, ctypes.byref(d32), FAKE, FAKE, 2048, 0.0, FAKE,
+                                                   None, None) == HIPERR
+    assert attn(L, kv(head_dim=48, dtype=1)) == UNSUPPORTED
+    assert b"head_dim" in L.dustin_last_error()
 
 
 def test_probe_argument_errors(L):

@@ -41,6 +41,9 @@ ATTN_CASES = [
     ("qwen7b-rows28-tail", dict(B=3, n=2333, Hq=28, Hkv=4, k=517, L_d=1), 517, dict(shuffle=False)),
     ("paged-ragged-rows64", dict(base="c5", B=3, n=4000, n_lo=700, k=700, L_d=1), 700, dict(frac_invalid=0.02)),
     ("d64-rows16", dict(B=2, n=2000, Hq=8, Hkv=2, d=64, k=257, L_d=1), 257, dict()),
+    # head_dim 32: 16 rows padded to two row blocks; 64 rows in four
+    ("d32-rows16", dict(B=2, n=2000, Hq=8, Hkv=2, d=32, k=257, L_d=1), 257, dict(frac_invalid=0.05)),
+    ("d32-rows64", dict(B=2, n=2600, Hq=32, Hkv=2, d=32, k=700, L_d=1), 700, dict(short=5)),
     ("k1", dict(B=2, n=500, Hq=64, Hkv=8, k=1, L_d=1), 1, dict()),
     ("tiny-f32", dict(base="c1"), 128, dict()),
 ]
@@ -79,6 +82,7 @@ def test_sparse_attention_matches_oracle(name, over, k, iopt):
 @pytest.mark.parametrize("name,over", [
     ("dense-qwen72b", dict(B=2, n=4100, Hq=64, Hkv=8, L_d=1)),
     ("dense-paged", dict(base="c5", B=2, n=3000, n_lo=900, L_d=1)),
+    ("dense-d32", dict(B=2, n=2100, Hq=16, Hkv=4, d=32, L_d=1)),
     ("dense-f32", dict(base="c1")),
 ])
 def test_dense_attention_matches_oracle(name, over):

@@ -95,6 +95,8 @@ CASES = [
     ("qwen7b-rows28-tail", dict(B=3, n=2333, Hq=28, Hkv=4, k=517, L_d=1), 517, dict(shuffle=False)),
     ("paged-ragged-rows64", dict(base="c5", B=3, n=4000, n_lo=700, k=700, L_d=1), 700, dict(frac_invalid=0.02)),
     ("d64-rows16", dict(B=2, n=2000, Hq=8, Hkv=2, d=64, k=257, L_d=1), 257, dict()),
+    ("d32-rows16", dict(B=2, n=2000, Hq=8, Hkv=2, d=32, k=257, L_d=1), 257, dict()),
+    ("d32-dense-rows32", dict(B=2, n=120, Hq=16, Hkv=2, d=32, L_d=1), None, dict()),   # short: the mask matters
     ("w1-rows8", dict(B=2, n=3000, Hq=64, Hkv=8, w=1, k=200, L_d=1), 200, dict()),
     ("dense-qwen72b", dict(B=2, n=4100, Hq=64, Hkv=8, L_d=1), None, dict()),
     ("dense-paged", dict(base="c5", B=2, n=3000, n_lo=900, L_d=1), None, dict()),
