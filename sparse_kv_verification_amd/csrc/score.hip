@@ -1418,11 +1418,12 @@ __device__ __forceinline__ void stream_kfrag(uint32_t base, int st, int h, int l
 // Statistics pass, streaming form.  Items (b, layer, 4096-position chunk)
 // walk round robin over the persistent groups; wave w streams positions
 // w * 1024 .. + 1023 of the chunk (stages past n_b are skipped) keeping
-// per-lane running (max, sum of exp2) pairs for both KV heads.  An item's
-// first stage requests the next item's Q fragments and its last stage the
-// next item's first DMA; items alternate between two named Q sets, so no
-// register copy waits for a pending load.  The cross-wave combine
-// alternates between two LDS buffers, so one barrier per item suffices.
+// per-lane running (max, sum of exp2) pairs for its KV heads.  An item's
+// first stage requests the next item's page ids and Q fragments, and its
+// last stages issue the next item's first DMA stages, so the ring stays as
+// full across items as inside one; items alternate between two named Q
+// sets.  The cross-wave combine alternates between two LDS buffers, so one
+// barrier per item suffices.
 template <int RB, bool PAGED, bool HALF, int CHUNK = kDraftStatChunk>
 __global__ __launch_bounds__(256, 2) void draft_stats_stream(DraftScoreArgs a) {
     // a paged wave span's page ids are one per lane: at most 64 pages
@@ -1783,13 +1784,13 @@ __device__ __forceinline__ int acc_layer_groups(int chunks, int nhi, int L, int 
 // Accumulation pass, streaming form.  Items (b, 1024-position chunk, layer
 // group) walk round robin over the persistent groups (chunks wholly past n_b
 // only write zeros); wave w owns positions w * 256 .. + 255 of the chunk and
-// streams them layer after layer of its group, 8 stages per layer (stages
-// past n_b are skipped).  With one layer group the item writes S_Draft;
-// otherwise it writes its group's partial sum, added up by draft_part_sum.
-// A layer's Q fragments and row normalisers are requested by the previous
-// layer's first stage, unconditionally and into the other of two named
-// register sets, so no register copy waits for a pending load.  Each stage
-// adds sum_{head, row} exp2(logit - lse) for its 32 positions to a
+// streams them layer after layer of its group, 8 stages per layer of full
+// rows or 4 of half rows (stages past n_b are skipped).  With one layer
+// group the item writes S_Draft; otherwise it writes its group's partial
+// sum, added up by draft_part_sum.  A layer's page ids, Q fragments and row
+// normalisers are requested by the previous layer's first stage,
+// unconditionally and into the other of two named register sets.  Each
+// stage adds sum_{head, row} exp2(logit - lse) for its positions to a
 // wave-private LDS accumulator, in layer order, so S_Draft needs no atomics.
 template <int RB, bool PAGED, bool HALF>
 __global__ __launch_bounds__(256, 2) void draft_acc_stream(DraftScoreArgs a) {
